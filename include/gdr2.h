@@ -1,0 +1,133 @@
+/*
+ * gdr2.h -- C ABI of libgdr2, the Gated Delta Rule-2 operator for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operator (Gated DeltaNet-2 pages, "The Gated Delta Rule-2 State
+ * Update", Eq. 10 and Steps 1-5): per head, with a dk x dv state S,
+ *
+ *     S_t = (I - k_t (b_t * k_t)^T) Diag(alpha_t) S_{t-1} + k_t (w_t * v_t)^T
+ *     o_t = S_t^T q_t,            alpha_t = exp(log_alpha_t)   (Eq. 12)
+ *
+ * alpha_t (dk) is a channel-wise decay on the key axis, b_t (dk) a
+ * channel-wise erase gate on the key axis and w_t (dv) a channel-wise write
+ * gate on the value axis.  The output reads the updated state and there is no
+ * query scaling.  The gates are not clamped: b may lie in [0, 2] (the pages'
+ * negative-eigenvalue variant, gate parameterisation after Eq. 11).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor arguments are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or retains them.
+ *   - Token tensors are contiguous [B, T, H, D] (D fastest); the state is
+ *     contiguous fp32 [N, H, dk, dv] (row i = key channel, dv fastest).
+ *   - Every base pointer must be 16-byte aligned (else GDR2_E_ALIGN).
+ *   - dk and dv must each be 32, 64 or 128 (else GDR2_E_UNSUPPORTED).
+ *   - in_dtype (GDR2_F32 or GDR2_BF16) is the storage type of q, k, v, b, w
+ *     and o; log_alpha has its own storage type.  The decay is always summed
+ *     in fp32 (pages, Appendix D.1).
+ *   - Calls are stream ordered and asynchronous: they enqueue kernels on
+ *     `stream` (a hipStream_t; NULL is the null stream) and return without
+ *     synchronising.  They are reentrant; the library has no global mutable
+ *     state besides a thread-local error string.
+ *   - Every argument error is detected on the host before any device call:
+ *     nothing is written, the status is returned and gdr2_last_error()
+ *     describes it.  A failed launch returns GDR2_E_LAUNCH.
+ *   - Device-side contract violations are undefined results, not errors:
+ *     cu_seqlens that is not non-decreasing from 0 to T, NaN/Inf inputs,
+ *     o aliasing an input.  Out-of-range cu_seqlens entries are clamped to
+ *     [0, T] so that no access leaves the caller's buffers.
+ */
+#ifndef GDR2_H
+#define GDR2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GDR2_F32 = 0, GDR2_BF16 = 1 } gdr2_dtype;
+
+typedef enum {
+    GDR2_OK = 0,
+    GDR2_E_NULL = 1,        /* a required pointer is NULL */
+    GDR2_E_SHAPE = 2,       /* a size is negative, zero where it must not be, or inconsistent */
+    GDR2_E_DTYPE = 3,       /* unknown dtype code */
+    GDR2_E_ALIGN = 4,       /* a base pointer is not 16-byte aligned */
+    GDR2_E_UNSUPPORTED = 5, /* dk or dv outside {32, 64, 128} */
+    GDR2_E_WORKSPACE = 6,   /* workspace missing or smaller than required */
+    GDR2_E_LAUNCH = 7       /* the HIP runtime refused a launch */
+} gdr2_status;
+
+/*
+ * Bytes of device workspace gdr2_chunk_fwd needs for these sizes (0 means the
+ * workspace pointer may be NULL).  Returns 0 for arguments gdr2_chunk_fwd
+ * would reject.
+ */
+size_t gdr2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs,
+                                      gdr2_dtype in_dtype);
+
+/*
+ * Chunkwise forward over whole sequences (pages, "Chunkwise Parallel Training
+ * via WY Representation": Step 1 decay normalisation, Step 2 WY form, Step 3
+ * state and output equations, Eqs. 20-24; packed variable-length batches per
+ * Appendix C.6).  The chunk size is internal; the result does not depend on
+ * it beyond rounding.
+ *
+ *   q, k, log_alpha, b : [B, T, H, dk]      v, w : [B, T, H, dv]
+ *   S0  : fp32 [N, H, dk, dv] initial state per sequence, or NULL for zeros.
+ *   o   : [B, T, H, dv] in in_dtype (written for every token of every sequence;
+ *         with cu_seqlens, tokens outside [cu[0], cu[N]) are not written).
+ *   S_T : fp32 [N, H, dk, dv] state after each sequence's last token, or NULL.
+ *         S_T may alias S0 exactly (each state is read before it is written).
+ *   cu_seqlens : NULL, in which case N = B and every batch row is one sequence
+ *         of T tokens; or device int32 [num_seqs + 1] token offsets of packed
+ *         sequences inside the single row (requires B == 1, N = num_seqs).
+ *         A zero-length sequence gets S_T = S0.
+ *   workspace : device scratch of at least gdr2_chunk_fwd_workspace_bytes().
+ *
+ * Precision: the cumulative log-decay, the WY solve's diagonal blocks, every
+ * accumulation and the state are fp32.  With in_dtype = GDR2_F32 every
+ * matrix product takes fp32 operands.  With GDR2_BF16 the products take
+ * 16-bit operands: bf16 for the decay-normalised chunk matrix, a bf16 hi/lo
+ * pair for the causal score matrix, and fp16 for the bounded state-pass
+ * operands.  The per-channel log-decay summed over any 32 consecutive tokens
+ * of a chunk must stay above -80 (the decay normalisation is centred inside
+ * each 64-token chunk); stronger decay gives undefined results.
+ */
+gdr2_status gdr2_chunk_fwd(const void *q, const void *k, const void *v,
+                           const void *log_alpha, const void *b, const void *w,
+                           const float *S0, void *o, float *S_T,
+                           const int32_t *cu_seqlens, int num_seqs,
+                           int B, int T, int H, int dk, int dv,
+                           gdr2_dtype in_dtype, gdr2_dtype log_alpha_dtype,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One recurrent decode step for N independent sequences (pages, Appendix C.5:
+ * forward-only recurrent kernel with an fp32 state, Eq. 10 applied to one
+ * token).  The state is read once and written once.
+ *
+ *   q, k, log_alpha, b : [N, H, dk]      v, w : [N, H, dv]
+ *   S : fp32 [N, H, dk, dv], updated in place.
+ *   o : [N, H, dv] in in_dtype; must not alias S or an input.
+ */
+gdr2_status gdr2_decode_step(const void *q, const void *k, const void *v,
+                             const void *log_alpha, const void *b, const void *w,
+                             float *S, void *o, int N, int H, int dk, int dv,
+                             gdr2_dtype in_dtype, gdr2_dtype log_alpha_dtype, void *stream);
+
+/* Static description of a status code. */
+const char *gdr2_status_string(gdr2_status s);
+
+/* Thread-local detail of the last non-OK status returned on this thread. */
+const char *gdr2_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int gdr2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR2_H */

@@ -1,0 +1,198 @@
+"""Python binding of libgdr2: the Gated Delta Rule-2 operator on MI355X.
+
+Argument marshalling only.  Every step of the operator runs in the HIP kernels
+of ``libgdr2.so`` (built by :mod:`linear_attention_sequence_gdr_amd.build`);
+there is no CPU or PyTorch fallback, and calling in without the library raises
+:class:`LibraryMissing`.  PyTorch supplies device memory and the stream.
+
+Functions carry the C names (include/gdr2.h):
+
+* :func:`gdr2_chunk_fwd` -- chunkwise forward over whole (optionally packed)
+  sequences, returns ``(o, S_T)``.
+* :func:`gdr2_decode_step` -- one token for N sequences, updates ``S`` in place,
+  returns ``o``.
+* :func:`gdr2_chunk_fwd_workspace_bytes`, :func:`gdr2_status_string`,
+  :func:`gdr2_last_error`, :func:`gdr2_version`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["gdr2_chunk_fwd", "gdr2_decode_step", "gdr2_chunk_fwd_workspace_bytes",
+           "gdr2_status_string", "gdr2_last_error", "gdr2_version", "Gdr2Error",
+           "LibraryMissing", "library", "library_path", "GDR2_F32", "GDR2_BF16", "EXPORTS"]
+
+GDR2_F32, GDR2_BF16 = 0, 1
+STATUS = {0: "GDR2_OK", 1: "GDR2_E_NULL", 2: "GDR2_E_SHAPE", 3: "GDR2_E_DTYPE",
+          4: "GDR2_E_ALIGN", 5: "GDR2_E_UNSUPPORTED", 6: "GDR2_E_WORKSPACE", 7: "GDR2_E_LAUNCH"}
+EXPORTS = ("gdr2_chunk_fwd_workspace_bytes", "gdr2_chunk_fwd", "gdr2_decode_step",
+           "gdr2_status_string", "gdr2_last_error", "gdr2_version")
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libgdr2.so")
+_lib = None
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+class Gdr2Error(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+
+
+def library():
+    """Load libgdr2.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise LibraryMissing(
+                f"{library_path} is not built; run `python -m linear_attention_sequence_gdr_amd.build`")
+        lib = ctypes.CDLL(library_path)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        lib.gdr2_chunk_fwd_workspace_bytes.argtypes = [i32] * 7
+        lib.gdr2_chunk_fwd_workspace_bytes.restype = sz
+        lib.gdr2_chunk_fwd.argtypes = [vp] * 10 + [i32] * 6 + [i32, i32, vp, sz, vp]
+        lib.gdr2_chunk_fwd.restype = i32
+        lib.gdr2_decode_step.argtypes = [vp] * 8 + [i32] * 6 + [vp]
+        lib.gdr2_decode_step.restype = i32
+        lib.gdr2_status_string.argtypes = [i32]
+        lib.gdr2_status_string.restype = ctypes.c_char_p
+        lib.gdr2_last_error.argtypes = []
+        lib.gdr2_last_error.restype = ctypes.c_char_p
+        lib.gdr2_version.argtypes = []
+        lib.gdr2_version.restype = i32
+        _lib = lib
+    return _lib
+
+
+def gdr2_status_string(status: int) -> str:
+    return library().gdr2_status_string(int(status)).decode()
+
+
+def gdr2_last_error() -> str:
+    return library().gdr2_last_error().decode()
+
+
+def gdr2_version() -> int:
+    return int(library().gdr2_version())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDR2_BF16
+    if t.dtype == torch.float32:
+        return GDR2_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, device) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(status: int):
+    if status != 0:
+        raise Gdr2Error(status, gdr2_last_error())
+
+
+def gdr2_chunk_fwd_workspace_bytes(B: int, T: int, H: int, dk: int, dv: int, num_seqs: int,
+                                   in_dtype: int) -> int:
+    return int(library().gdr2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, num_seqs, in_dtype))
+
+
+def gdr2_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
+                   b: torch.Tensor, w: torch.Tensor, S0: Optional[torch.Tensor] = None,
+                   cu_seqlens: Optional[torch.Tensor] = None, *, o: Optional[torch.Tensor] = None,
+                   S_T: Optional[torch.Tensor] = None, want_state: bool = True,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+    """Chunkwise forward.  q, k, log_alpha, b: [B, T, H, dk]; v, w: [B, T, H, dv];
+    S0: fp32 [N, H, dk, dv] or None; cu_seqlens: int32 [N+1] (B == 1) or None.
+    ``o``/``S_T``/``workspace`` may be passed to avoid allocation.  Returns
+    ``(o, S_T)`` (S_T is None when ``want_state`` is False and none is given)."""
+    lib = library()
+    dev = q.device
+    Bsz, T, H, dk = q.shape
+    dv = v.shape[-1]
+    in_dt = _dtype_code(q)
+    N = Bsz if cu_seqlens is None else cu_seqlens.numel() - 1
+    if o is None:
+        o = torch.empty((Bsz, T, H, dv), dtype=q.dtype, device=dev)
+    if S_T is None and want_state:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    ws_bytes = 0
+    if cu_seqlens is not None:
+        ws_bytes = gdr2_chunk_fwd_workspace_bytes(Bsz, T, H, dk, dv, N, in_dt)
+        if workspace is None and ws_bytes:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    for name, t, want in (("k", k, q.dtype), ("v", v, q.dtype), ("b", b, q.dtype), ("w", w, q.dtype),
+                          ("o", o, q.dtype)):
+        if t.dtype != want:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {want}")
+    for name, t in (("k", k), ("log_alpha", log_alpha), ("b", b)):
+        if tuple(t.shape) != (Bsz, T, H, dk):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(Bsz, T, H, dk)}")
+    for name, t in (("w", w), ("o", o)):
+        if tuple(t.shape) != (Bsz, T, H, dv):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(Bsz, T, H, dv)}")
+    for name, t in (("S0", S0), ("S_T", S_T)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (N, H, dk, dv)):
+            raise ValueError(f"{name} must be fp32 {(N, H, dk, dv)}")
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    st = lib.gdr2_chunk_fwd(
+        _ptr(q, "q", dev), _ptr(k, "k", dev), _ptr(v, "v", dev), _ptr(log_alpha, "log_alpha", dev),
+        _ptr(b, "b", dev), _ptr(w, "w", dev), _ptr(S0, "S0", dev), _ptr(o, "o", dev),
+        _ptr(S_T, "S_T", dev), _ptr(cu_seqlens, "cu_seqlens", dev), N if cu_seqlens is not None else 0,
+        Bsz, T, H, dk, dv, in_dt, _dtype_code(log_alpha), _ptr(workspace, "workspace", dev),
+        ws_bytes, _stream(stream, dev))
+    _check(st)
+    return o, S_T
+
+
+def gdr2_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
+                     b: torch.Tensor, w: torch.Tensor, S: torch.Tensor, *,
+                     o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decode step.  q, k, log_alpha, b: [N, H, dk]; v, w: [N, H, dv];
+    S: fp32 [N, H, dk, dv] updated in place.  Returns o [N, H, dv]."""
+    lib = library()
+    dev = q.device
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    for name, t, shp in (("k", k, (N, H, dk)), ("log_alpha", log_alpha, (N, H, dk)),
+                         ("b", b, (N, H, dk)), ("v", v, (N, H, dv)), ("w", w, (N, H, dv)),
+                         ("o", o, (N, H, dv)), ("S", S, (N, H, dk, dv))):
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    if S.dtype != torch.float32:
+        raise TypeError("S must be fp32")
+    st = lib.gdr2_decode_step(
+        _ptr(q, "q", dev), _ptr(k, "k", dev), _ptr(v, "v", dev), _ptr(log_alpha, "log_alpha", dev),
+        _ptr(b, "b", dev), _ptr(w, "w", dev), _ptr(S, "S", dev), _ptr(o, "o", dev),
+        N, H, dk, dv, _dtype_code(q), _dtype_code(log_alpha), _stream(stream, dev))
+    _check(st)
+    return o

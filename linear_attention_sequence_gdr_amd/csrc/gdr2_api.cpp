@@ -1,0 +1,147 @@
+// gdr2_api.cpp -- the C ABI of libgdr2 (declared in include/gdr2.h).
+//
+// Every argument is validated on the host before any HIP call, so a rejected
+// call touches no device memory and needs no GPU.  Valid calls enqueue their
+// kernels on the caller's stream and return without synchronising.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "gdr2.h"
+#include "gdr2_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gdr2_status fail(gdr2_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
+bool dtype_ok(int t) { return t == GDR2_F32 || t == GDR2_BF16; }
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+extern "C" {
+
+const char* gdr2_status_string(gdr2_status s) {
+  switch (s) {
+    case GDR2_OK: return "ok";
+    case GDR2_E_NULL: return "a required pointer is NULL";
+    case GDR2_E_SHAPE: return "invalid or inconsistent sizes";
+    case GDR2_E_DTYPE: return "unknown dtype code";
+    case GDR2_E_ALIGN: return "a base pointer is not 16-byte aligned";
+    case GDR2_E_UNSUPPORTED: return "unsupported head dimension";
+    case GDR2_E_WORKSPACE: return "workspace missing or too small";
+    case GDR2_E_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+const char* gdr2_last_error(void) { return g_err; }
+
+int gdr2_version(void) { return 100; }
+
+size_t gdr2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs,
+                                      gdr2_dtype in_dtype) {
+  if (B <= 0 || T < 0 || H <= 0 || !dim_ok(dk) || !dim_ok(dv) || num_seqs < 0 ||
+      !dtype_ok(in_dtype))
+    return 0;
+  const size_t s = gdr2::schedule_bytes(num_seqs);
+  return s ? align256(s) : 0;
+}
+
+gdr2_status gdr2_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                           const void* b, const void* w, const float* S0, void* o, float* S_T,
+                           const int32_t* cu_seqlens, int num_seqs, int B, int T, int H, int dk,
+                           int dv, gdr2_dtype in_dtype, gdr2_dtype log_alpha_dtype,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !log_alpha || !b || !w || !o)
+    return fail(GDR2_E_NULL, "gdr2_chunk_fwd: q, k, v, log_alpha, b, w and o must be non-NULL");
+  if (!dtype_ok(in_dtype) || !dtype_ok(log_alpha_dtype))
+    return fail(GDR2_E_DTYPE, "gdr2_chunk_fwd: dtype codes %d/%d are not GDR2_F32 or GDR2_BF16",
+                (int)in_dtype, (int)log_alpha_dtype);
+  if (B <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0)
+    return fail(GDR2_E_SHAPE, "gdr2_chunk_fwd: need B >= 1, T >= 0, H >= 1, dk, dv >= 1 (got B=%d T=%d H=%d dk=%d dv=%d)",
+                B, T, H, dk, dv);
+  if (!dim_ok(dk) || !dim_ok(dv))
+    return fail(GDR2_E_UNSUPPORTED, "gdr2_chunk_fwd: dk=%d dv=%d; each must be 32, 64 or 128", dk, dv);
+  const bool bf16 = in_dtype == GDR2_BF16;
+  if (!gdr2::chunk_supported(dk, dv, bf16))
+    return fail(GDR2_E_UNSUPPORTED, "gdr2_chunk_fwd: fp32 inputs support dk of 32 or 64 (got dk=%d)", dk);
+  int N = B;
+  if (cu_seqlens) {
+    if (B != 1)
+      return fail(GDR2_E_SHAPE, "gdr2_chunk_fwd: packed sequences (cu_seqlens) need B == 1, got B=%d", B);
+    if (num_seqs < 1)
+      return fail(GDR2_E_SHAPE, "gdr2_chunk_fwd: num_seqs must be >= 1 with cu_seqlens, got %d", num_seqs);
+    N = num_seqs;
+  }
+  if ((long long)N * H > (1LL << 26))
+    return fail(GDR2_E_SHAPE, "gdr2_chunk_fwd: N*H = %lld (sequence, head) pairs is too many", (long long)N * H);
+  const void* ptrs[] = {q, k, v, log_alpha, b, w, o, S0, S_T, cu_seqlens, workspace};
+  const char* names[] = {"q", "k", "v", "log_alpha", "b", "w", "o", "S0", "S_T", "cu_seqlens", "workspace"};
+  for (int i = 0; i < 11; ++i)
+    if (ptrs[i] && !aligned16(ptrs[i]))
+      return fail(GDR2_E_ALIGN, "gdr2_chunk_fwd: %s is not 16-byte aligned", names[i]);
+  const size_t need = cu_seqlens ? gdr2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, in_dtype) : 0;
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(GDR2_E_WORKSPACE, "gdr2_chunk_fwd: workspace of %zu bytes needed, got %zu%s", need,
+                workspace_bytes, workspace ? "" : " (NULL)");
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* order = need ? static_cast<int32_t*>(workspace) : nullptr;
+  if (order) {
+    const hipError_t e = gdr2::launch_schedule(cu_seqlens, N, T, order, st);
+    if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "gdr2_chunk_fwd: schedule launch: %s", hipGetErrorString(e));
+  }
+  gdr2::ChunkArgs a;
+  a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.b = b; a.w = w;
+  a.S0 = S0; a.o = o; a.ST = S_T; a.cu = cu_seqlens; a.order = order;
+  a.N = N; a.T = T; a.H = H; a.DV = dv;
+  a.la_bf16 = log_alpha_dtype == GDR2_BF16;
+  const hipError_t e = gdr2::launch_chunk(a, dk, dv, bf16, st);
+  if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "gdr2_chunk_fwd: launch: %s", hipGetErrorString(e));
+  return GDR2_OK;
+}
+
+gdr2_status gdr2_decode_step(const void* q, const void* k, const void* v, const void* log_alpha,
+                             const void* b, const void* w, float* S, void* o, int N, int H, int dk,
+                             int dv, gdr2_dtype in_dtype, gdr2_dtype log_alpha_dtype, void* stream) {
+  if (!q || !k || !v || !log_alpha || !b || !w || !S || !o)
+    return fail(GDR2_E_NULL, "gdr2_decode_step: q, k, v, log_alpha, b, w, S and o must be non-NULL");
+  if (!dtype_ok(in_dtype) || !dtype_ok(log_alpha_dtype))
+    return fail(GDR2_E_DTYPE, "gdr2_decode_step: dtype codes %d/%d are not GDR2_F32 or GDR2_BF16",
+                (int)in_dtype, (int)log_alpha_dtype);
+  if (N < 0 || H <= 0 || dk <= 0 || dv <= 0)
+    return fail(GDR2_E_SHAPE, "gdr2_decode_step: need N >= 0, H >= 1, dk, dv >= 1 (got N=%d H=%d dk=%d dv=%d)",
+                N, H, dk, dv);
+  if (!dim_ok(dk) || !dim_ok(dv))
+    return fail(GDR2_E_UNSUPPORTED, "gdr2_decode_step: dk=%d dv=%d; each must be 32, 64 or 128", dk, dv);
+  if ((long long)N * H > 0x7fffffffLL)
+    return fail(GDR2_E_SHAPE, "gdr2_decode_step: N*H = %lld is too many", (long long)N * H);
+  const void* ptrs[] = {q, k, v, log_alpha, b, w, S, o};
+  const char* names[] = {"q", "k", "v", "log_alpha", "b", "w", "S", "o"};
+  for (int i = 0; i < 8; ++i)
+    if (!aligned16(ptrs[i]))
+      return fail(GDR2_E_ALIGN, "gdr2_decode_step: %s is not 16-byte aligned", names[i]);
+  gdr2::DecodeArgs a;
+  a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.b = b; a.w = w;
+  a.S = S; a.o = o; a.N = N; a.H = H;
+  a.la_bf16 = log_alpha_dtype == GDR2_BF16;
+  const hipError_t e = gdr2::launch_decode(a, dk, dv, in_dtype == GDR2_BF16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "gdr2_decode_step: launch: %s", hipGetErrorString(e));
+  return GDR2_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,162 @@
+// gdr2_device.h -- device-side helpers shared by the libgdr2 kernels (gfx950).
+//
+// Storage conversions for bf16, the CDNA4 MFMA wrappers and their lane layouts.
+// MFMA 16x16 tiles (one 64-lane wavefront): lane l = 16*g + m (m = l & 15,
+// g = l >> 4).  The A operand lane holds row m of A and a group of K elements
+// picked by g; the B operand lane holds column m of B and the same K group.
+// The accumulator lane holds C[4*g + q][m] for q = 0..3 ("C layout").  Both
+// operands are always fetched with the same K grouping, so the contraction
+// covers every K index exactly once whatever order the hardware uses inside a
+// group.  A C-layout tile converted to 16-bit is therefore directly the B
+// operand of a K = 16 product that contracts over the tile's rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr2 {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// ---- bf16 storage <-> fp32 ----------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Round to nearest even; NaN stays NaN (quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Load 8 consecutive elements (16-byte aligned for bf16, 32-byte for fp32) as fp32.
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* base, size_t idx, float out[8]) {
+  if constexpr (BF16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+    const float4 a = p[0], b = p[1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void load4(const void* base, size_t idx, float out[4]) {
+  if constexpr (BF16) {
+    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
+    out[0] = __uint_as_float(u.x << 16);
+    out[1] = __uint_as_float(u.x & 0xffff0000u);
+    out[2] = __uint_as_float(u.y << 16);
+    out[3] = __uint_as_float(u.y & 0xffff0000u);
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load1(const void* base, size_t idx) {
+  if constexpr (BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[idx]);
+  else return static_cast<const float*>(base)[idx];
+}
+
+// Store 4 consecutive fp32 values in the storage type (8- or 16-byte aligned).
+template <bool BF16>
+__device__ __forceinline__ void store4(void* base, size_t idx, const float v[4]) {
+  if constexpr (BF16) {
+    uint2 u;
+    u.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+    u.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) = u;
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(base) + idx) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+// ---- MFMA wrappers ---------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mma32(const bf16x8& a, const bf16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma32(const f16x8& a, const f16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(const f16x4& a, const f16x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+// fp32: a K = 16 block as four K = 4 instructions; lane group g supplies K
+// index 4*g + q to instruction q, for A and B alike.
+__device__ __forceinline__ f32x4 mma16(const float4& a, const float4& b, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, c, 0, 0, 0);
+  return c;
+}
+
+template <typename E> struct Vec;
+template <> struct Vec<__bf16> { typedef bf16x8 v8; };
+template <> struct Vec<_Float16> { typedef f16x8 v8; typedef f16x4 v4; };
+template <> struct Vec<float> { typedef float4 v4; };
+
+// Accumulator chains never mix MFMA shapes: a 16x16x16 step whose C input is
+// the result of a 16x16x32 step has returned wrong values in the first two
+// accumulator registers, timing-dependently, so the K = 32 helper below and
+// the K = 16 helper that follows are only ever chained with themselves (or
+// started from a VALU-written accumulator).
+//
+// acc += A[16 x K] * B[K x 16], both operands K-contiguous in LDS: A row m at
+// A + m*lda, B column n at Bt + n*ldb (i.e. B stored transposed).
+template <typename E, int K>
+__device__ __forceinline__ f32x4 mma_lds(f32x4 acc, const E* A, int lda, const E* Bt, int ldb) {
+  const int m = lane_id() & 15, g = lane_id() >> 4;
+  const E* a = A + m * lda;
+  const E* b = Bt + m * ldb;
+  if constexpr (sizeof(E) == 2) {
+    static_assert(K % 32 == 0, "16-bit operands: K must be a multiple of 32");
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 32)
+      acc = mma32(*reinterpret_cast<const typename Vec<E>::v8*>(a + k0 + 8 * g),
+                  *reinterpret_cast<const typename Vec<E>::v8*>(b + k0 + 8 * g), acc);
+  } else {
+    static_assert(K % 16 == 0, "K must be a multiple of 16");
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 16)
+      acc = mma16(*reinterpret_cast<const float4*>(a + k0 + 4 * g),
+                  *reinterpret_cast<const float4*>(b + k0 + 4 * g), acc);
+  }
+  return acc;
+}
+
+// Same, with a K extent known only at run time (a multiple of 16, at most KMAX).
+template <typename E, int KMAX>
+__device__ __forceinline__ f32x4 mma_lds_k16(f32x4 acc, const E* A, int lda, const E* Bt, int ldb,
+                                             int K) {
+  const int m = lane_id() & 15, g = lane_id() >> 4;
+  const E* a = A + m * lda;
+  const E* b = Bt + m * ldb;
+  typedef typename Vec<E>::v4 V4;
+#pragma unroll
+  for (int k0 = 0; k0 < KMAX; k0 += 16)
+    if (k0 < K)
+      acc = mma16(*reinterpret_cast<const V4*>(a + k0 + 4 * g),
+                  *reinterpret_cast<const V4*>(b + k0 + 4 * g), acc);
+  return acc;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace gdr2

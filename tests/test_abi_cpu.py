@@ -1,0 +1,107 @@
+"""C-ABI contract of libgdr2 on the CPU: the library loads with no GPU present,
+exports every entry point include/gdr2.h declares, and rejects bad arguments on
+the host before any device call (no compute call is made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import linear_attention_sequence_gdr_amd as G
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr2.h")
+A = 0x10000            # a 16-byte aligned fake device address (never dereferenced)
+MIS = 0x10008          # misaligned
+
+pytestmark = pytest.mark.skipif(not os.path.exists(G.library_path), reason="libgdr2.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr2_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_and_exports_agree():
+    decl = declared_functions()
+    assert set(decl) == set(G.EXPORTS), decl
+    out = subprocess.run(["nm", "-D", "--defined-only", G.library_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (gdr2_[a-z_0-9]+)$", out, flags=re.M))
+    missing = set(decl) - exported
+    assert not missing, f"declared but not exported: {missing}"
+    lib = G.library()
+    for name in decl:
+        assert hasattr(lib, name)
+
+
+def test_version_and_strings():
+    assert G.gdr2_version() >= 100
+    for s in range(8):
+        assert G.gdr2_status_string(s)
+
+
+def fwd(**kw):
+    args = dict(q=A, k=A, v=A, la=A, b=A, w=A, S0=None, o=A, ST=None, cu=None, ns=0, B=2, T=100,
+                H=4, dk=128, dv=128, dt=G.GDR2_BF16, ldt=G.GDR2_BF16, ws=None, wsb=0, stream=None)
+    args.update(kw)
+    return G.library().gdr2_chunk_fwd(*args.values())
+
+
+def dec(**kw):
+    args = dict(q=A, k=A, v=A, la=A, b=A, w=A, S=A, o=A, N=8, H=4, dk=128, dv=128,
+                dt=G.GDR2_F32, ldt=G.GDR2_F32, stream=None)
+    args.update(kw)
+    return G.library().gdr2_decode_step(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(la=None), 1),
+    (dict(dt=7), 3), (dict(ldt=-1), 3),
+    (dict(B=0), 2), (dict(T=-1), 2), (dict(H=0), 2), (dict(dk=0), 2),
+    (dict(dk=48), 5), (dict(dv=256), 5), (dict(dt=G.GDR2_F32, dk=128), 5),
+    (dict(cu=A, ns=3), 2), (dict(cu=A, B=1, ns=0), 2),
+    (dict(q=MIS), 4), (dict(S0=MIS), 4), (dict(cu=MIS, B=1, ns=3), 4),
+    (dict(cu=A, B=1, ns=3), 6), (dict(cu=A, B=1, ns=3, ws=A, wsb=8), 6),
+])
+def test_chunk_fwd_rejects(kw, status):
+    assert fwd(**kw) == status
+    assert G.gdr2_last_error().startswith("gdr2_chunk_fwd")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(S=None), 1), (dict(q=None), 1), (dict(dt=5), 3), (dict(N=-1), 2), (dict(H=0), 2),
+    (dict(dk=16), 5), (dict(o=MIS), 4), (dict(S=MIS), 4),
+])
+def test_decode_rejects(kw, status):
+    assert dec(**kw) == status
+    assert G.gdr2_last_error().startswith("gdr2_decode_step")
+
+
+def test_workspace_query():
+    q = G.gdr2_chunk_fwd_workspace_bytes
+    assert q(1, 100, 16, 128, 128, 0, G.GDR2_BF16) == 0
+    assert q(1, 100, 16, 128, 128, 1, G.GDR2_BF16) == 0
+    assert q(1, 100, 16, 128, 128, 64, G.GDR2_BF16) == 256
+    assert q(1, 100, 16, 128, 128, 100, G.GDR2_BF16) == 512
+    assert q(1, 100, 16, 48, 128, 64, G.GDR2_BF16) == 0
+    assert q(0, 100, 16, 128, 128, 64, G.GDR2_BF16) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    x = torch.zeros(1, 8, 2, 32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        G.gdr2_chunk_fwd(x, x, x, x, x, x, o=torch.zeros(1, 8, 2, 32), S_T=torch.zeros(1, 2, 32, 32))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        y = torch.zeros(4, 2, 32)
+        G.gdr2_decode_step(y, y, y, y, y, y, torch.zeros(4, 2, 32, 32), o=torch.zeros(4, 2, 32))
+
+
+def test_binding_has_no_fallback(monkeypatch):
+    monkeypatch.setattr(G, "library_path", "/nonexistent/libgdr2.so")
+    monkeypatch.setattr(G, "_lib", None)
+    with pytest.raises(G.LibraryMissing):
+        G.library()

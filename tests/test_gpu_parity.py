@@ -1,0 +1,252 @@
+"""GPU path vs the fp64 oracle on the same seeded inputs (needs an MI355X).
+
+Every call goes through the C ABI (the ctypes binding).  Small cases span
+several 64-token chunks, ragged tails, packed sequences with zero and one
+token, all supported head sizes and both value-block widths; the full-size
+workloads run in the launch configuration the benchmark times and are checked
+on sampled (sequence, head) pairs that the oracle computes one by one.
+
+Tolerances: fp32 path max relative error <= 1e-4 on o and S_T; bf16 path
+max-abs error / RMS <= 2e-2 on S_T and on o beyond o's own bf16 storage
+rounding (tests/metrics.py).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdr2_inputs as I
+import oracle
+from tests import metrics as M
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+TOL_F32 = 1e-4
+TOL_BF16 = 2e-2
+
+
+def G():
+    import linear_attention_sequence_gdr_amd as g
+    return g
+
+
+def dev(x):
+    return None if x is None else x.cuda()
+
+
+def run_fwd(wl, **kw):
+    o, ST = G().gdr2_chunk_fwd(dev(wl.q), dev(wl.k), dev(wl.v), dev(wl.log_alpha), dev(wl.b),
+                               dev(wl.w), dev(wl.S0), dev(wl.cu_seqlens), **kw)
+    torch.cuda.synchronize()
+    return o.cpu(), ST.cpu()
+
+
+def oracle_fwd(wl, mask=None):
+    cu = None
+    if wl.cu_seqlens is not None:
+        cu = wl.cu_seqlens.numpy()
+    return oracle.fwd(wl.q, wl.k, wl.v, wl.log_alpha, wl.b, wl.w, S0=wl.S0, cu_seqlens=cu,
+                      mask=mask)
+
+
+def check(o, ST, ro, rS, bf16, what=""):
+    if bf16:
+        eo, es = M.bf16_excess(o, ro), M.rms_err(ST, rS)
+        assert eo <= TOL_BF16 and es <= TOL_BF16, f"{what}: o excess {eo:.3e}, S_T {es:.3e}"
+    else:
+        eo, es = M.max_rel(o, ro), M.max_rel(ST, rS)
+        assert eo <= TOL_F32 and es <= TOL_F32, f"{what}: o {eo:.3e}, S_T {es:.3e}"
+    return eo, es
+
+
+# ---- fp32 path: the tiny workload and its collapses --------------------------------
+
+@pytest.mark.parametrize("variant", ["none", "kda", "gdn"])
+def test_cfg0_fp32(variant):
+    wl = I.config(0, variant=variant)
+    o, ST = run_fwd(wl)
+    ro, rS = oracle_fwd(wl)
+    check(o, ST, ro, rS, False, wl.name)
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 32), (64, 32), (32, 128), (64, 64)])
+def test_fp32_shapes_ragged(dk, dv):
+    wl = I.make_forward(2, 203, 3, dk, dv, dtype=torch.float32, decay_shift=0.0, s0_std=0.1,
+                        seed=11)
+    o, ST = run_fwd(wl)
+    ro, rS = oracle_fwd(wl)
+    check(o, ST, ro, rS, False, f"fp32 dk={dk} dv={dv}")
+
+
+# ---- bf16 path --------------------------------------------------------------------
+
+@pytest.mark.parametrize("dk,dv,H", [(128, 128, 4), (128, 128, 64), (64, 128, 4), (32, 64, 8),
+                                     (128, 32, 4)])
+def test_bf16_shapes_ragged(dk, dv, H):
+    # H=4 uses 16-channel value blocks, H=64 the 32-channel ones
+    wl = I.make_forward(2, 333, H, dk, dv, dtype=torch.bfloat16, decay_shift=-2.0, s0_std=0.1,
+                        seed=12)
+    o, ST = run_fwd(wl)
+    ro, rS = oracle_fwd(wl)
+    check(o, ST, ro, rS, True, f"bf16 dk={dk} dv={dv} H={H}")
+
+
+def test_bf16_negative_eigenvalues_fp32_decay():
+    wl = I.make_forward(1, 700, 4, 128, 128, dtype=torch.bfloat16, la_dtype=torch.float32,
+                        decay_shift=-4.0, erase_scale=2.0, s0_std=0.1, seed=13)
+    o, ST = run_fwd(wl)
+    ro, rS = oracle_fwd(wl)
+    check(o, ST, ro, rS, True, "b in [0,2], fp32 log_alpha")
+
+
+def test_bf16_varlen_edges():
+    lens = [1, 63, 64, 65, 0, 130, 7, 200]
+    wl = I.make_forward(1, sum(lens), 4, 128, 128, dtype=torch.bfloat16, decay_shift=-2.0,
+                        s0_std=0.1, seqlens=lens, seed=14)
+    o, ST = run_fwd(wl)
+    ro, rS = oracle_fwd(wl)
+    check(o, ST, ro, rS, True, "varlen edges")
+    # zero-length sequence: S_T = S0 exactly
+    assert torch.equal(ST[4], wl.S0[4])
+
+
+def test_varlen_equals_separate_calls():
+    lens = [70, 5, 129]
+    wl = I.make_forward(1, sum(lens), 2, 64, 64, dtype=torch.bfloat16, decay_shift=-2.0,
+                        s0_std=0.1, seqlens=lens, seed=15)
+    o, ST = run_fwd(wl)
+    cu = wl.cu_seqlens.tolist()
+    for n in range(3):
+        sl = slice(cu[n], cu[n + 1])
+        part = I.Workload("part", *(x[:, sl].contiguous() for x in
+                                    (wl.q, wl.k, wl.v, wl.log_alpha, wl.b, wl.w)),
+                          wl.S0[n:n + 1].contiguous(), None, 0)
+        op, Sp = run_fwd(part)
+        assert torch.equal(op, o[:, sl]) and torch.equal(Sp[0], ST[n])
+
+
+def test_split_resume():
+    wl = I.make_forward(1, 256, 4, 128, 128, dtype=torch.bfloat16, decay_shift=-2.0, s0_std=0.1,
+                        seed=16)
+    o, ST = run_fwd(wl)
+    a = I.Workload("a", *(x[:, :128].contiguous() for x in (wl.q, wl.k, wl.v, wl.log_alpha,
+                                                            wl.b, wl.w)), wl.S0, None, 0)
+    oa, Sa = run_fwd(a)
+    b = I.Workload("b", *(x[:, 128:].contiguous() for x in (wl.q, wl.k, wl.v, wl.log_alpha,
+                                                            wl.b, wl.w)), Sa, None, 0)
+    ob, Sb = run_fwd(b)
+    # chunk boundaries coincide, so the two runs do the same arithmetic
+    assert torch.equal(torch.cat([oa, ob], 1), o) and torch.equal(Sb, ST)
+
+
+def test_deterministic():
+    wl = I.make_forward(2, 300, 8, 128, 128, dtype=torch.bfloat16, s0_std=0.1, seed=17)
+    o1, S1 = run_fwd(wl)
+    o2, S2 = run_fwd(wl)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_state_aliasing_in_place():
+    wl = I.make_forward(1, 150, 2, 64, 64, dtype=torch.bfloat16, s0_std=0.1, seed=18)
+    o, ST = run_fwd(wl)
+    S = dev(wl.S0).clone()
+    G().gdr2_chunk_fwd(dev(wl.q), dev(wl.k), dev(wl.v), dev(wl.log_alpha), dev(wl.b), dev(wl.w),
+                       S, None, S_T=S)
+    torch.cuda.synchronize()
+    assert torch.equal(S.cpu(), ST)
+
+
+# ---- the full-size workloads, sampled ------------------------------------------------
+
+def sampled_mask(N, H, picks):
+    m = np.zeros((N, H), bool)
+    for n, h in picks:
+        m[n, h] = True
+    return m
+
+
+@pytest.mark.parametrize("index,picks", [
+    (1, [(0, 0), (1, 7), (2, 15), (3, 3)]),
+    (3, [(0, 0), (0, 11)]),
+])
+def test_full_workload_sampled(index, picks):
+    wl = I.config(index)
+    o, ST = run_fwd(wl)
+    mask = sampled_mask(wl.num_seqs, wl.H, picks)
+    ro, rS = oracle_fwd(wl, mask)
+    for n, h in picks:
+        check(o[n, :, h], ST[n, h], ro[n, :, h], rS[n, h], True, f"{wl.name} seq {n} head {h}")
+    assert torch.isfinite(o.float()).all() and torch.isfinite(ST).all()
+
+
+def test_varlen_workload_sampled():
+    wl = I.config(4)
+    o, ST = run_fwd(wl)
+    cu = wl.cu_seqlens.tolist()
+    lens = np.diff(cu)
+    picks = [(int(np.argmax(lens)), 5), (int(np.argmin(lens)), 0), (17, 9), (40, 15)]
+    mask = sampled_mask(wl.num_seqs, wl.H, picks)
+    ro, rS = oracle_fwd(wl, mask)
+    for n, h in picks:
+        sl = slice(cu[n], cu[n + 1])
+        check(o[0, sl, h], ST[n, h], ro[0, sl, h], rS[n, h], True, f"cfg4 seq {n} head {h}")
+    assert torch.isfinite(o.float()).all() and torch.isfinite(ST).all()
+
+
+# ---- decode -------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dk,dv,dtype", [(128, 128, torch.float32), (32, 64, torch.float32),
+                                         (64, 32, torch.bfloat16), (128, 128, torch.bfloat16)])
+def test_decode_small(dk, dv, dtype):
+    N, H = 5, 3
+    S = I.decode_state(N, H, dk, dv, seed=21)
+    Sd = S.cuda()
+    Sr = S.double().numpy()
+    for step in range(6):
+        x = I.decode_step_inputs(step, N, H, dk, dv, dtype=dtype, seed=21)
+        o = G().gdr2_decode_step(*(t.cuda() for t in x), Sd)
+        ro, Sr = oracle.decode(*x, Sr)
+        torch.cuda.synchronize()
+        tol = 1e-4 if dtype == torch.float32 else 1e-2
+        assert M.max_rel(o, ro) <= tol, f"step {step} o {M.max_rel(o, ro):.3e}"
+        assert M.max_rel(Sd, Sr) <= 1e-4, f"step {step} S {M.max_rel(Sd, Sr):.3e}"
+
+
+def test_decode_workload_512_steps_sampled():
+    """Config 2: 256 sequences x 16 heads, 512 in-place steps on the GPU; the oracle
+    follows 8 sequences and the state and that step's output are compared every
+    64 steps."""
+    S = I.decode_state()
+    Sd = S.cuda()
+    seqs = [0, 37, 101, 128, 199, 200, 254, 255]
+    Sr = S[seqs].double().numpy()
+    for step in range(I.DECODE_STEPS):
+        x = I.decode_step_inputs(step)
+        o = G().gdr2_decode_step(*(t.cuda() for t in x), Sd)
+        ro, Sr = oracle.decode(*(t[seqs] for t in x), Sr)
+        if (step + 1) % 64 == 0:
+            torch.cuda.synchronize()
+            eo = M.max_rel(o[seqs], ro)
+            es = M.max_rel(Sd[seqs], Sr)
+            assert eo <= TOL_F32 and es <= TOL_F32, f"step {step}: o {eo:.3e} S {es:.3e}"
+
+
+def test_repeated_launches_identical():
+    """Regression: the output tile once summed a K=32 and a K=16 MFMA chain in one
+    accumulator, which corrupted two of its four registers on some launches.
+    Twelve launches into NaN-filled outputs must all equal the first, bit for bit,
+    and the first must meet the tolerance."""
+    wl = I.make_forward(2, 333, 64, 128, 128, dtype=torch.bfloat16, decay_shift=-2.0, s0_std=0.1,
+                        seed=12)
+    args = [dev(x) for x in (wl.q, wl.k, wl.v, wl.log_alpha, wl.b, wl.w, wl.S0)]
+    first = None
+    for rep in range(12):
+        o = torch.full((2, 333, 64, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+        _, ST = G().gdr2_chunk_fwd(*args, o=o)
+        torch.cuda.synchronize()
+        if first is None:
+            first = (o.cpu(), ST.cpu())
+            ro, rS = oracle_fwd(wl)
+            check(first[0], first[1], ro, rS, True, "repeat launch 0")
+        else:
+            assert torch.equal(o.cpu(), first[0]) and torch.equal(ST.cpu(), first[1]), f"launch {rep}"
