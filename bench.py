@@ -1,0 +1,207 @@
+"""Benchmark of the Gated Delta Rule-2 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps D] [--no-cpu]
+
+A step is one gdr2_chunk_fwd over the training-shape workload (B=4, T=4096,
+H=16, dk=dv=128, bf16 inputs, fp32 state, S0 = 0): inputs are resident in HBM
+before timing starts, W untimed steps run first, then exactly K steps are timed
+back to back with HIP events on the launch stream.  The same run also times D
+decode steps (256 sequences x 16 heads, fp32 state updated in place) and the
+fp64 oracle on a bounded sample of the forward workload on the host cores.
+
+Prints one JSON line: tokens/s of the forward (whole job), its TFLOP/s and the
+HBM roofline of the forward kernel, the decode HBM GB/s with its own roofline,
+and the CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_chunk_fwd_b4_t4096_h16_d128.json")
+
+
+def fwd_algorithmic(B, T, H, dk, dv, in_bytes=2, C=64):
+    """Algorithmic bytes and flops of one forward (no S0 read, S_T written).
+
+    Bytes: q, k, log_alpha, b (dk each) and v, w (dv each) read once, o written
+    once, S_T written once.  Flops per 64-token chunk and head: T and A_qk
+    (triangular), Y and U (triangular), A_qk R, and the three state products
+    Q_g S, Y S, K_tail^T R.
+    """
+    tok = B * T * H
+    byts = tok * (4 * dk + 2 * dv) * in_bytes + tok * dv * in_bytes + B * H * dk * dv * 4
+    per_chunk = (C * (C - 1) * dk + C * (C + 1) * dk + C * (C - 1) * (dk + dv)
+                 + C * (C + 1) * dv + 6 * C * dk * dv)
+    flops = per_chunk * tok / C
+    return byts, flops
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_attention_sequence_gdr_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(launch_bytes_alg):
+    """HBM bytes per launch measured by rocprofv3 counters (committed under
+    profiles/), only when they were taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def time_events(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps     # ms per step
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The fp64 oracle as it stands, on a sample of whole (sequence, head) chains
+    of the forward workload, using every host core it is allowed."""
+    import numpy as np
+    import oracle
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    N, H = wl.B, wl.H
+    # probe one chain to size the sample to the budget
+    m = np.zeros((N, H), bool)
+    m[0, 0] = True
+    q, k, v, g, b, w = (oracle.f64(x[:1]) for x in (wl.q, wl.k, wl.v, wl.log_alpha, wl.b, wl.w))
+    t0 = time.perf_counter()
+    oracle.fwd(q, k, v, g, b, w, mask=m[:1], nthreads=1)
+    t1 = time.perf_counter() - t0
+    pairs = int(max(1, min(N * H, cores * max(1, budget_s // max(t1, 1e-3)))))
+    pairs = max(min(pairs, N * H), 1)
+    m = np.zeros(N * H, bool)
+    m[:pairs] = True
+    m = m.reshape(N, H)
+    nseq = int(np.ceil(pairs / H))
+    q, k, v, g, b, w = (oracle.f64(x[:nseq]) for x in (wl.q, wl.k, wl.v, wl.log_alpha, wl.b, wl.w))
+    used = min(cores, pairs)
+    t0 = time.perf_counter()
+    oracle.fwd(q, k, v, g, b, w, mask=m[:nseq], nthreads=used)
+    dt = time.perf_counter() - t0
+    head_tokens = pairs * wl.T
+    return {"value": head_tokens / H / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{pairs} of {N * H} (sequence, head) chains x {wl.T} tokens, fp64 "
+                      f"token-by-token, {dt:.1f} s; tokens/s counts a token once per {H} heads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=100)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the Gated Delta Rule-2 path here has no multi-GPU "
+              "mode (sequences and heads shard with no exchange; see DESIGN.md). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gdr2_inputs as I
+    import linear_attention_sequence_gdr_amd as G
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    G.library()
+
+    # ---- forward: B4 T4096 H16 d128 bf16 ------------------------------------------------
+    wl = I.config(1)
+    B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
+    ins = [x.to(dev) for x in (wl.q, wl.k, wl.v, wl.log_alpha, wl.b, wl.w)]
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    ST = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    fwd = lambda: G.gdr2_chunk_fwd(*ins, None, None, o=o, S_T=ST)
+    ms = time_events(fwd, args.steps, args.warmup, torch)
+    byts, flops = fwd_algorithmic(B, T, H, dk, dv)
+    tokens = B * T
+    gbs = byts / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    traffic = load_traffic(byts)
+
+    # ---- decode: 256 sequences x 16 heads, fp32 state ---------------------------------
+    S = I.decode_state().to(dev)
+    pool = [[t.to(dev) for t in I.decode_step_inputs(s)] for s in range(8)]
+    od = torch.empty((I.DECODE_N, I.DECODE_H, I.DECODE_D), dtype=torch.float32, device=dev)
+    it = [0]
+
+    def dec():
+        x = pool[it[0] % len(pool)]
+        it[0] += 1
+        G.gdr2_decode_step(*x, S, o=od)
+    dms = time_events(dec, args.decode_steps, 5, torch)
+    Nd, Hd, D = I.DECODE_N, I.DECODE_H, I.DECODE_D
+    dbytes = Nd * Hd * (2 * D * D * 4 + 6 * D * 4 + D * 4)
+    dgbs = dbytes / (dms * 1e-3) / 1e9
+    del S, pool
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl)
+
+    line = {
+        "metric": "GDR-2 fwd tokens/s + TFLOP/s (H16,d128,T4K); decode HBM GB/s",
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gdr2_chunk_fwd B4 T4096 H16 dk=dv=128, bf16 q/k/v/b/w/log_alpha, "
+                               "fp32 state, S0=0, chunk 64",
+                   "global_batch": B, "seq_len": T, "heads": H, "dk": dk, "dv": dv},
+        "fwd_tflops": tflops,
+        "fwd_tflops_frac_of_bf16_peak": tflops / BF16_PEAK_TFLOPS,
+        "fwd_alg_bytes": byts,
+        "fwd_alg_flops": flops,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": traffic},
+        "decode": {"workload": "gdr2_decode_step N256 H16 dk=dv=128 fp32 state in place",
+                   "steps": args.decode_steps, "us_per_step": dms * 1e3, "alg_bytes": dbytes,
+                   "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS,
+                                "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS}},
+        "cpu_baseline": cpu,
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

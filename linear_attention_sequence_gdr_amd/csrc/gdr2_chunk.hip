@@ -1,40 +1,46 @@
 // gdr2_chunk.hip -- chunkwise forward of the Gated Delta Rule-2 operator on
 // gfx950 (Gated DeltaNet-2 pages, "Chunkwise Parallel Training via WY
-// Representation", Steps 1-3, Eqs. 20-24, and the row recurrences of
-// Appendix A.4; packed sequences per Appendix C.6).
+// Representation", Steps 1-3, Eqs. 20-24; packed sequences per Appendix C.6).
 //
 // One workgroup (256 threads, 4 wavefronts) owns one (sequence, head, block
 // of DVB value channels) and walks the sequence's 64-token chunks in order.
 // The value channels of the state are independent of each other (every
-// key-side quantity is shared and column j of S, U, R, O depends only on
+// key-side quantity is shared, and column j of S, U, R, O depends only on
 // column j of S0 and Z), so splitting dv across workgroups needs no exchange.
-// Every workgroup recomputes the key-side chunk quantities; the workgroups of
-// one (sequence, head) are placed on the same XCD so the repeated key-side
+// Each workgroup recomputes the key-side chunk quantities; the workgroups of
+// one (sequence, head) are placed on the same XCD so their repeated key-side
 // reads hit that XCD's L2.  Nothing is written to HBM but o and S_T.
 //
-// Per chunk (G = fp32 cumulative log-decay from the chunk start, m = row 31):
-//   L   load q, k, g, b, v, w; G by a fp32 scan; centred decay factors
-//       e1 = exp(G - G_m), e2 = exp(G_m - G) so that no factor exceeds the
-//       decay over half a chunk;  E' = e1*b*k, K' = e2*k, Q' = e1*q  and the
-//       un-centred E = gamma*b*k, Q_g = gamma*q, K_tail = (gamma_C/gamma)*k,
-//       Z = w*v  (Step 1, Eq. 20).
-//   P   T = tril(E' K'^T, -1) and A_qk = tril(Q' K'^T, 0) on MFMA (the
-//       centring cancels in every product; Step 2 and the A_qk of Eq. 24).
-//   S   A = (I + T)^-1 applied to [E | Z]: the four 16x16 diagonal blocks are
-//       inverted by fp32 forward substitution, then a block forward
-//       substitution X_a = A_aa (RHS_a - sum_{b<a} T_ab X_b) gives Y = A E and
-//       U = A Z without forming the off-diagonal blocks of A.
-//   R   R = U - Y S                      (chunk-local residual)
-//   O   O = Q_g S + A_qk R               (Eq. 24)
+// Per chunk, with G the fp32 cumulative log-decay from the chunk start (kept
+// in log2 units) and m = row 31 of the chunk:
+//   L   the raw q, k, g, b, v, w of the chunk come from registers filled
+//       during the previous chunk, and the next chunk's loads are issued.
+//       G by a DPP scan; centred decay factors e1 = 2^(G - G_m) and
+//       e2 = 2^(G_m - G), so no factor exceeds the decay over half a chunk;
+//       E' = e1*b*k, K' = e2*k, Q' = e1*q, and the un-centred E = gamma*b*k,
+//       Q_g = gamma*q, K_tail = (gamma_C/gamma)*k, Z = w*v (Step 1, Eq. 20).
+//       Each thread owns 4 consecutive rows, so the transposed copies E^T,
+//       K_tail^T and Z^T are written as 8-byte vectors.
+//   P   T^T = K' E'^T and A_qk^T = K' Q'^T on MFMA (the centring cancels in
+//       every product; Step 2 and the A_qk of Eq. 24).  Computing the
+//       transposes lets each lane store 4 adjacent entries of a row.
+//   S   A = (I + T)^-1: the four 16x16 diagonal blocks by fp32 forward
+//       substitution, then the off-diagonal blocks by the block recurrence
+//       A_ab = A_aa (-sum_{b<=c<a} T_ac A_cb).
+//   Y   Y^T = E^T A^T and U = A Z as plain MFMA products (U stays in the
+//       registers of the wavefront that turns it into R).
+//   R   R = U - Y S                       (chunk-local residual)
+//   O   O = Q_g S + A_qk R                (Eq. 24)
 //       S <- Diag(gamma_C) S + K_tail^T R (Eq. 23)
 // The state stays in fp32 MFMA accumulators for the whole sequence.
 //
 // Operand precision: with fp32 inputs every product is fp32 MFMA.  With bf16
 // inputs T uses bf16 operands, A_qk a bf16 hi/lo split (three products), and
-// every state-pass operand (Y, U-side R, Q_g, K_tail, A_qk, S) is fp16: these
+// every state-pass operand (A, Y, Z, R, Q_g, K_tail, A_qk, S) is fp16: these
 // are bounded by |q|, |k|, |b k| and the state, and fp16 keeps 3 more mantissa
 // bits than bf16, which the output needs because Q_g S and A_qk Y S nearly
-// cancel.  Accumulation is always fp32.
+// cancel.  Accumulation is always fp32.  Every MFMA accumulator chain uses a
+// single instruction shape (see gdr2_device.h).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -47,43 +53,52 @@ namespace gdr2 {
 constexpr int CH = 64;   // chunk length
 constexpr int NT = 256;  // threads per workgroup
 constexpr int NW = 4;    // wavefronts per workgroup
+constexpr float LOG2E = 1.4426950408889634f;
 
 template <int DK, int DVB, bool F32>
 struct ChunkCfg {
   typedef typename std::conditional<F32, float, __bf16>::type KT;    // T / A_qk operands
   typedef typename std::conditional<F32, float, _Float16>::type ST;  // state-pass operands
   typedef typename std::conditional<F32, float4, f16x4>::type SV4;
-  static constexpr int PAD = F32 ? 4 : 8;      // row padding (elements) against bank conflicts
-  static constexpr int LDK = DK + PAD;         // rows of [64][DK]
-  static constexpr int LDC = CH + PAD;         // rows of [*][64]
-  static constexpr int LDA = 16 + PAD;         // rows of the 16x16 diagonal inverses
-  static constexpr int LDZ = DVB + 4;          // rows of fp32 [64][DVB]
-  static constexpr int NKT = F32 ? 3 : 5;      // E', K'(hi,lo), Q'(hi,lo)
-  static constexpr size_t SZK = (size_t)CH * LDK * sizeof(KT);
-  static constexpr size_t SZS = (size_t)CH * LDK * sizeof(ST);
+  static constexpr int PAD = F32 ? 4 : 8;  // row padding (elements) against bank conflicts
+  static constexpr int LDK = DK + PAD;     // rows of [64][DK] and [DVB][DK]
+  static constexpr int LDC = CH + PAD;     // rows of [*][64]
+  static constexpr size_t SK = sizeof(KT), SS = sizeof(ST);
+  // region X, phase P set: E', K'hi, (K'lo), Q'hi, (Q'lo)  [64][LDK] KT
+  static constexpr int NKT = F32 ? 3 : 5;
+  static constexpr size_t SZK = (size_t)CH * LDK * SK;
   static constexpr size_t XP = NKT * SZK;
-  static constexpr size_t XR = 3 * SZS + (size_t)DK * LDC * sizeof(ST);
+  // region X after phase P: E^T, K_tail^T [DK][LDC]; Q_g, -Y [64][LDK]  (ST)
+  static constexpr size_t O_EHT = 0;
+  static constexpr size_t O_KTT = O_EHT + (size_t)DK * LDC * SS;
+  static constexpr size_t O_QG = O_KTT + (size_t)DK * LDC * SS;
+  static constexpr size_t O_YN = O_QG + (size_t)CH * LDK * SS;
+  static constexpr size_t XR = O_YN + (size_t)CH * LDK * SS;
   static constexpr size_t X = ((XP > XR ? XP : XR) + 15) / 16 * 16;
-  // byte offsets
-  static constexpr size_t O_TD = X;                                        // fp32 [4][16][16]
-  static constexpr size_t O_TN = O_TD + 4 * 16 * 16 * 4;                   // ST [64][LDC]  (-T)
-  static constexpr size_t O_AD = O_TN + (size_t)CH * LDC * sizeof(ST);     // ST [4][16][LDA]
-  static constexpr size_t O_AQK = O_AD + (size_t)4 * 16 * LDA * sizeof(ST);  // ST [64][LDC]
-  static constexpr size_t O_Z = O_AQK + (size_t)CH * LDC * sizeof(ST);     // fp32 [64][LDZ]
-  static constexpr size_t O_U = O_Z + (size_t)CH * LDZ * 4;                // fp32 [64][LDZ]
-  static constexpr size_t O_RT = O_U + (size_t)CH * LDZ * 4;               // ST [DVB][LDC]
-  static constexpr size_t O_S = O_RT + (size_t)DVB * LDC * sizeof(ST);     // ST [2][DVB][LDK]
-  static constexpr size_t O_GC = O_S + (size_t)2 * DVB * LDK * sizeof(ST); // fp32 [DK]
+  static constexpr size_t O_TD = X;                                 // fp32 [4][16][16] diag T
+  static constexpr size_t O_TN = O_TD + 4 * 16 * 16 * 4;            // ST [64][LDC]  -T
+  static constexpr size_t O_A = O_TN + (size_t)CH * LDC * SS;       // ST [64][LDC]  A
+  static constexpr size_t O_AQK = O_A + (size_t)CH * LDC * SS;      // ST [64][LDC]  A_qk
+  static constexpr size_t O_ZT = O_AQK + (size_t)CH * LDC * SS;     // ST [DVB][LDC] Z^T
+  static constexpr size_t O_RT = O_ZT + (size_t)DVB * LDC * SS;     // ST [DVB][LDC] R^T
+  static constexpr size_t O_S = O_RT + (size_t)DVB * LDC * SS;      // ST [2][DVB][LDK] S^T
+  static constexpr size_t O_GC = O_S + (size_t)2 * DVB * LDK * SS;  // fp32 [DK] gamma_C
   static constexpr size_t BYTES = O_GC + (size_t)DK * 4;
   static_assert(BYTES <= 160 * 1024, "LDS budget exceeded");
-  // phase-L thread mapping: RPT consecutive rows x 8 columns per thread
+  // phase-L mapping: thread = (column group cg of 8 key channels, row group rg
+  // of RPT consecutive rows); the RG row groups of a column group are
+  // consecutive lanes of one wavefront.
   static constexpr int CG = DK / 8, RG = NT / CG, RPT = CH / RG;
-  static_assert(RG >= 1 && RG <= 64 && CH % RG == 0, "bad phase-L mapping");
-  // v/w mapping
-  static constexpr int EPT = CH * DVB / NT, TPR = DVB / EPT;
-  static_assert(EPT == 4 || EPT == 8, "bad v/w mapping");
-  static constexpr int NSTILE = (DK / 16) * (DVB / 16);  // state tiles
-  static constexpr int NSU = (NSTILE + NW - 1) / NW;     // state tiles per wave
+  static_assert(RG >= 16 && RG <= 64 && CH % RG == 0, "bad phase-L mapping");
+  // v/w mapping: 4 consecutive rows x CPT value channels per thread
+  static constexpr int CPT = DVB / 16;
+  static_assert(CPT == 1 || CPT == 2, "DVB must be 16 or 32");
+  static constexpr int NSTILE = (DK / 16) * (DVB / 16);  // 16x16 state tiles
+  static constexpr int NSU = (NSTILE + NW - 1) / NW;     // state tiles per wavefront
+  static constexpr int NJT = DVB / 16;                   // value column tiles
+  static constexpr int ESZ = F32 ? 4 : 2;                // bytes per stored input element
+  static constexpr int KW = F32 ? 8 : 4;                 // dwords per 8 key elements
+  static constexpr int VB = CPT * ESZ;                   // bytes per row of v/w per thread
 };
 
 template <typename T> __device__ __forceinline__ T cvt(float x) { return (T)x; }
@@ -95,55 +110,173 @@ template <> __device__ __forceinline__ f16x4 cvt4<f16x4>(f32x4 a) {
 template <> __device__ __forceinline__ float4 cvt4<float4>(f32x4 a) {
   return make_float4(a[0], a[1], a[2], a[3]);
 }
+// 2^x on the hardware exponential unit (about 1 ulp).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Write 8 consecutive fp32 values as the KT type (16 B for bf16, 32 B for fp32).
-template <typename KT>
-__device__ __forceinline__ void st8(KT* dst, const float v[8]) {
-  if constexpr (std::is_same<KT, float>::value) {
+template <typename V4> __device__ __forceinline__ V4 neg_cvt4(f32x4 a) {
+  return cvt4<V4>(f32x4{-a[0], -a[1], -a[2], -a[3]});
+}
+
+// Four consecutive ST values from LDS, or gathered from a C-layout column.
+template <typename ST, typename SV4>
+__device__ __forceinline__ SV4 gather4(const ST* p, int stride) {
+  SV4 r;
+  if constexpr (std::is_same<ST, float>::value) {
+    r = make_float4(p[0], p[stride], p[2 * stride], p[3 * stride]);
+  } else {
+    r = f16x4{p[0], p[stride], p[2 * stride], p[3 * stride]};
+  }
+  return r;
+}
+
+// Write 8 consecutive fp32 values as E (16 B for 16-bit types, 32 B for fp32).
+template <typename E>
+__device__ __forceinline__ void st8(E* dst, const float v[8]) {
+  if constexpr (std::is_same<E, float>::value) {
     reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
     reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
   } else {
-    typedef __attribute__((ext_vector_type(8))) KT V8;
+    typedef __attribute__((ext_vector_type(8))) E V8;
     V8 x;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = (KT)v[i];
+    for (int i = 0; i < 8; ++i) x[i] = (E)v[i];
     *reinterpret_cast<V8*>(dst) = x;
   }
 }
 
-// The (a, b) block coordinates of the 10 lower-triangular 16x16 tiles of a
-// 64x64 chunk matrix.
+// Write N (1, 2 or 4) consecutive values as E.
+template <typename E, int N>
+__device__ __forceinline__ void stn(E* dst, const float* v) {
+  if constexpr (N == 4) {
+    if constexpr (std::is_same<E, float>::value) *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+    else *reinterpret_cast<f16x4*>(dst) = f16x4{(E)v[0], (E)v[1], (E)v[2], (E)v[3]};
+  } else if constexpr (N == 2) {
+    if constexpr (std::is_same<E, float>::value) *reinterpret_cast<float2*>(dst) = make_float2(v[0], v[1]);
+    else *reinterpret_cast<f16x2*>(dst) = f16x2{(E)v[0], (E)v[1]};
+  } else {
+    dst[0] = (E)v[0];
+  }
+}
+
+__device__ __forceinline__ float dpp_shr(float v, int n) {
+  int r;
+  switch (n) {
+    case 1: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, true); break;
+    case 2: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xf, 0xf, true); break;
+    case 4: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xf, 0xf, true); break;
+    default: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xf, 0xf, true); break;
+  }
+  return __builtin_bit_cast(float, r);
+}
+
+// Inclusive prefix sum over groups of RG consecutive lanes (RG = 16, 32, 64):
+// a DPP scan inside each 16-lane row (row_shr 1, 2, 4, 8), then row carries.
+template <int RG>
+__device__ __forceinline__ float seg_scan(float x) {
+  x += dpp_shr(x, 1);
+  x += dpp_shr(x, 2);
+  x += dpp_shr(x, 4);
+  x += dpp_shr(x, 8);
+  if constexpr (RG >= 32) {
+    const float c = __shfl(x, (lane_id() & ~31) + 15);
+    if (lane_id() & 16) x += c;
+  }
+  if constexpr (RG == 64) {
+    const float c = __shfl(x, 31);
+    if (lane_id() & 32) x += c;
+  }
+  return x;
+}
+
+// The (a, b) block coordinates (b <= a) of the 10 lower-triangular 16x16
+// tiles of a 64x64 chunk matrix.
 __device__ __forceinline__ void tri_tile(int t, int& a, int& b) {
   a = (t >= 1) + (t >= 3) + (t >= 6);
   b = t - (a * (a + 1)) / 2;
 }
 
-template <int DK, int DVB, bool F32>
+template <int N>
+__device__ __forceinline__ void ldw(uint32_t (&dst)[N], const void* p) {
+  if constexpr (N == 8) {
+    const uint4* s = static_cast<const uint4*>(p);
+    const uint4 a = s[0], c = s[1];
+    dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
+    dst[4] = c.x; dst[5] = c.y; dst[6] = c.z; dst[7] = c.w;
+  } else if constexpr (N == 4) {
+    const uint4 a = *static_cast<const uint4*>(p);
+    dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
+  } else if constexpr (N == 2) {
+    const uint2 a = *static_cast<const uint2*>(p);
+    dst[0] = a.x; dst[1] = a.y;
+  } else {
+    dst[0] = *static_cast<const uint32_t*>(p);
+  }
+}
+
+// 8 stored key elements (bf16 pairs or fp32) to fp32.
+template <bool F32, int KW>
+__device__ __forceinline__ void unpack8(const uint32_t (&w)[KW], float out[8]) {
+  if constexpr (F32) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = __uint_as_float(w[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+}
+
+// Off-diagonal blocks of column block B of A = (I + T)^-1 by the block
+// recurrence A_aB = A_aa (-sum_{B<=c<a} T_ac A_cB); Tn holds -T and the
+// diagonal blocks of A are already in Am.
+template <int B, typename ST, typename SV4, int LDC>
+__device__ __forceinline__ void wy_column(const ST* Tn, ST* Am) {
+  const int m = lane_id() & 15, g4 = lane_id() >> 4;
+  SV4 xb[4];
+  xb[B] = gather4<ST, SV4>(Am + (16 * B + 4 * g4) * LDC + 16 * B + m, LDC);
+#pragma unroll
+  for (int a = B + 1; a < 4; ++a) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int c = B; c < a; ++c)
+      acc = mma16(*reinterpret_cast<const SV4*>(Tn + (16 * a + m) * LDC + 16 * c + 4 * g4), xb[c], acc);
+    const SV4 wvec = cvt4<SV4>(acc);
+    const f32x4 xa =
+        mma16(*reinterpret_cast<const SV4*>(Am + (16 * a + m) * LDC + 16 * a + 4 * g4), wvec, zero4());
+    xb[a] = cvt4<SV4>(xa);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Am[(16 * a + 4 * g4 + q) * LDC + 16 * B + m] = cvt<ST>(xa[q]);
+  }
+}
+
+template <int DK, int DVB, bool F32, bool LA16>
 __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs p) {
   typedef ChunkCfg<DK, DVB, F32> Cfg;
   typedef typename Cfg::KT KT;
   typedef typename Cfg::ST ST;
   typedef typename Cfg::SV4 SV4;
   constexpr bool BF16 = !F32;
-  constexpr int LDK = Cfg::LDK, LDC = Cfg::LDC, LDA = Cfg::LDA, LDZ = Cfg::LDZ;
-  constexpr int RPT = Cfg::RPT, RG = Cfg::RG;
+  constexpr int LDK = Cfg::LDK, LDC = Cfg::LDC;
+  constexpr int RPT = Cfg::RPT, RG = Cfg::RG, CPT = Cfg::CPT, NJT = Cfg::NJT;
+  constexpr int ESZ = Cfg::ESZ, KW = Cfg::KW;
 
   extern __shared__ __align__(16) unsigned char smem[];
   KT* Ep = reinterpret_cast<KT*>(smem);
   KT* Kh = reinterpret_cast<KT*>(smem + Cfg::SZK);
-  KT* Kl = reinterpret_cast<KT*>(smem + 2 * Cfg::SZK);      // bf16 path only
+  KT* Kl = reinterpret_cast<KT*>(smem + 2 * Cfg::SZK);  // bf16 path only
   KT* Qh = reinterpret_cast<KT*>(smem + (F32 ? 2 : 3) * Cfg::SZK);
-  KT* Ql = reinterpret_cast<KT*>(smem + 4 * Cfg::SZK);      // bf16 path only
-  ST* Eh = reinterpret_cast<ST*>(smem);                      // after phase P
-  ST* Qg = reinterpret_cast<ST*>(smem + Cfg::SZS);
-  ST* Yn = reinterpret_cast<ST*>(smem + 2 * Cfg::SZS);
-  ST* KtT = reinterpret_cast<ST*>(smem + 3 * Cfg::SZS);
+  KT* Ql = reinterpret_cast<KT*>(smem + 4 * Cfg::SZK);  // bf16 path only
+  ST* EhT = reinterpret_cast<ST*>(smem + Cfg::O_EHT);
+  ST* KtT = reinterpret_cast<ST*>(smem + Cfg::O_KTT);
+  ST* Qg = reinterpret_cast<ST*>(smem + Cfg::O_QG);
+  ST* Yn = reinterpret_cast<ST*>(smem + Cfg::O_YN);
   float* Td = reinterpret_cast<float*>(smem + Cfg::O_TD);
   ST* Tn = reinterpret_cast<ST*>(smem + Cfg::O_TN);
-  ST* Ad = reinterpret_cast<ST*>(smem + Cfg::O_AD);
+  ST* Am = reinterpret_cast<ST*>(smem + Cfg::O_A);
   ST* Aqk = reinterpret_cast<ST*>(smem + Cfg::O_AQK);
-  float* Zf = reinterpret_cast<float*>(smem + Cfg::O_Z);
-  float* Uf = reinterpret_cast<float*>(smem + Cfg::O_U);
+  ST* ZT = reinterpret_cast<ST*>(smem + Cfg::O_ZT);
   ST* RT = reinterpret_cast<ST*>(smem + Cfg::O_RT);
   ST* Sbuf = reinterpret_cast<ST*>(smem + Cfg::O_S);
   float* gC = reinterpret_cast<float*>(smem + Cfg::O_GC);
@@ -175,6 +308,13 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs p) {
   const size_t nh = (size_t)n * H + h;
   const int jbase = jb * DVB;
 
+  // the strictly upper blocks of A and A_qk stay zero for the whole sequence;
+  // the products below run over them instead of switching instruction shape
+  for (int e = tid; e < CH * LDC; e += NT) {
+    Am[e] = cvt<ST>(0.f);
+    Aqk[e] = cvt<ST>(0.f);
+  }
+
   // ---- state: fp32 accumulators in C layout -------------------------------------------
   f32x4 Sacc[Cfg::NSU];
 #pragma unroll
@@ -198,73 +338,123 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs p) {
       *reinterpret_cast<SV4*>(Scur + (16 * jt + m) * LDK + 16 * ib + 4 * g4) = cvt4<SV4>(Sacc[u]);
     }
   }
+
+  // phase-L coordinates: rows r0 .. r0+RPT-1, key channels 8*cg .. 8*cg+7
+  const int cg = tid / RG, rg = tid % RG, r0 = rg * RPT;
+  // v/w coordinates: rows 4*vq .. 4*vq+3, value channels CPT*vc ..
+  const int vc = tid % 16, vq = tid / 16;
+
+  // raw inputs of the chunk in flight (registers)
+  uint32_t rq[RPT][KW], rk[RPT][KW], rb[RPT][KW], rgd[RPT][LA16 ? 4 : 8];
+  uint32_t rv[4], rw[4];
+  auto fetch = [&](int c) {
+    const long long ctok = tok0 + (long long)c * CH;
+    const int clen = min(CH, len - c * CH);
+#pragma unroll
+    for (int pr = 0; pr < RPT; ++pr) {
+      const int r = r0 + pr;
+      if (r < clen) {
+        const size_t idx = ((size_t)(ctok + r) * H + h) * DK + 8 * cg;
+        ldw(rq[pr], static_cast<const char*>(p.q) + idx * ESZ);
+        ldw(rk[pr], static_cast<const char*>(p.k) + idx * ESZ);
+        ldw(rb[pr], static_cast<const char*>(p.b) + idx * ESZ);
+        // raw words only: expanding bf16 here would wait for the load
+        ldw(rgd[pr], static_cast<const char*>(p.la) + idx * (LA16 ? 2 : 4));
+      } else {
+#pragma unroll
+        for (int i = 0; i < KW; ++i) rq[pr][i] = rk[pr][i] = rb[pr][i] = 0u;
+#pragma unroll
+        for (int i = 0; i < (LA16 ? 4 : 8); ++i) rgd[pr][i] = 0u;
+      }
+    }
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) {
+      const int r = 4 * vq + pr;
+      rv[pr] = rw[pr] = 0u;
+      if (r < clen) {
+        const size_t idx = ((size_t)(ctok + r) * H + h) * DV + jbase + CPT * vc;
+        if constexpr (Cfg::VB == 4) {
+          rv[pr] = *reinterpret_cast<const uint32_t*>(static_cast<const char*>(p.v) + idx * ESZ);
+          rw[pr] = *reinterpret_cast<const uint32_t*>(static_cast<const char*>(p.w) + idx * ESZ);
+        } else if constexpr (Cfg::VB == 2) {
+          rv[pr] = static_cast<const uint16_t*>(p.v)[idx];
+          rw[pr] = static_cast<const uint16_t*>(p.w)[idx];
+        }
+      }
+    }
+  };
+  // fp32 inputs with 32-channel blocks would need 8 bytes of v/w per row
+  static_assert(Cfg::VB <= 4, "v/w fetch covers at most 4 bytes per row");
+
+  const int nchunks = (len + CH - 1) / CH;
+  if (nchunks > 0) fetch(0);
   __syncthreads();
 
-  const int cg = tid / RG, rg = tid % RG;
-  const int nchunks = (len + CH - 1) / CH;
   for (int c = 0; c < nchunks; ++c) {
     const long long ctok = tok0 + (long long)c * CH;
     const int clen = min(CH, len - c * CH);
 
-    // ================= phase L: loads, decay scan, operand tiles =================
+    // ================= phase L: decay scan and operand tiles ====================
     float eh[RPT][8], qg[RPT][8], kt[RPT][8];
     {
       float G[RPT][8], kv[RPT][8], qv[RPT][8], bv[RPT][8];
+      float z[4][CPT];
 #pragma unroll
       for (int pr = 0; pr < RPT; ++pr) {
-        const int r = rg * RPT + pr;
-        if (r < clen) {
-          const size_t idx = ((size_t)(ctok + r) * H + h) * DK + 8 * cg;
-          load8<BF16>(p.q, idx, qv[pr]);
-          load8<BF16>(p.k, idx, kv[pr]);
-          load8<BF16>(p.b, idx, bv[pr]);
-          if (p.la_bf16) load8<true>(p.la, idx, G[pr]);
-          else load8<false>(p.la, idx, G[pr]);
-        } else {
+        unpack8<F32>(rq[pr], qv[pr]);
+        unpack8<F32>(rk[pr], kv[pr]);
+        unpack8<F32>(rb[pr], bv[pr]);
+        unpack8<!LA16>(rgd[pr], G[pr]);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) qv[pr][i] = kv[pr][i] = bv[pr][i] = G[pr][i] = 0.f;
+        for (int i = 0; i < 8; ++i) G[pr][i] *= LOG2E;
+      }
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr) {
+        if constexpr (F32) {
+          z[pr][0] = __uint_as_float(rv[pr]) * __uint_as_float(rw[pr]);
+        } else if constexpr (CPT == 2) {
+          z[pr][0] = __uint_as_float(rv[pr] << 16) * __uint_as_float(rw[pr] << 16);
+          z[pr][1] = __uint_as_float(rv[pr] & 0xffff0000u) * __uint_as_float(rw[pr] & 0xffff0000u);
+        } else {
+          z[pr][0] = __uint_as_float(rv[pr] << 16) * __uint_as_float(rw[pr] << 16);
         }
       }
-      // fp32 cumulative log-decay over the chunk: serial inside the thread,
-      // then an exclusive scan of thread totals across the RG row groups.
+      // The raw registers are free: start the next chunk's loads now.  This
+      // chunk's loads (issued a chunk ago) are waited for explicitly first;
+      // otherwise the in-order memory counter makes the first use of their
+      // registers wait for the new loads as well.
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+      if (c + 1 < nchunks) fetch(c + 1);
+
+      // fp32 cumulative log2-decay over the chunk: serial inside the thread,
+      // then a scan of thread totals across the RG row groups
 #pragma unroll
       for (int pr = 1; pr < RPT; ++pr)
 #pragma unroll
         for (int i = 0; i < 8; ++i) G[pr][i] += G[pr - 1][i];
-      float Gm[8], GC[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float tot = G[RPT - 1][i];
-        float incl = tot;
-#pragma unroll
-        for (int off = 1; off < RG; off <<= 1) {
-          const float y = __shfl_up(incl, off, RG);
-          if (rg >= off) incl += y;
-        }
-        const float excl = incl - tot;
-#pragma unroll
-        for (int pr = 0; pr < RPT; ++pr) G[pr][i] += excl;
-        Gm[i] = __shfl(G[(CH / 2 - 1) % RPT][i], (CH / 2 - 1) / RPT, RG);
-        GC[i] = __shfl(G[RPT - 1][i], RG - 1, RG);
-      }
       float egm[8], egcm[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        egm[i] = F32 ? expf(Gm[i]) : __expf(Gm[i]);
-        egcm[i] = F32 ? expf(GC[i] - Gm[i]) : __expf(GC[i] - Gm[i]);
-      }
-      if (rg == 0) {
+        const float tot = G[RPT - 1][i];
+        const float excl = seg_scan<RG>(tot) - tot;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) gC[8 * cg + i] = F32 ? expf(GC[i]) : __expf(GC[i]);
+        for (int pr = 0; pr < RPT; ++pr) G[pr][i] += excl;
+        const float gm = __shfl(G[(CH / 2 - 1) % RPT][i], (CH / 2 - 1) / RPT, RG);
+        const float gc = __shfl(G[RPT - 1][i], RG - 1, RG);
+        egm[i] = exp2_fast(gm);
+        egcm[i] = exp2_fast(gc - gm);
+        if (rg == 0) gC[8 * cg + i] = exp2_fast(gc);
+#pragma unroll
+        for (int pr = 0; pr < RPT; ++pr) G[pr][i] -= gm;  // centred: G - G_m
       }
 #pragma unroll
       for (int pr = 0; pr < RPT; ++pr) {
-        const int r = rg * RPT + pr;
+        const int r = r0 + pr;
         float ep[8], kh[8], kl[8], qh[8], ql[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float e1 = F32 ? expf(G[pr][i] - Gm[i]) : __expf(G[pr][i] - Gm[i]);
-          const float e2 = F32 ? expf(Gm[i] - G[pr][i]) : __expf(Gm[i] - G[pr][i]);
+          const float e1 = exp2_fast(G[pr][i]);
+          const float e2 = exp2_fast(-G[pr][i]);
           const float bk = bv[pr][i] * kv[pr][i];
           ep[i] = e1 * bk;
           const float kb = e2 * kv[pr][i];
@@ -278,153 +468,137 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs p) {
             qh[i] = (float)(__bf16)qp;
             ql[i] = qp - qh[i];
           }
-          const float gam = e1 * egm[i];
-          eh[pr][i] = gam * bk;
-          qg[pr][i] = gam * qv[pr][i];
-          kt[pr][i] = e2 * egcm[i] * kv[pr][i];
+          eh[pr][i] = ep[i] * egm[i];
+          qg[pr][i] = qp * egm[i];
+          kt[pr][i] = kb * egcm[i];
         }
         st8<KT>(Ep + r * LDK + 8 * cg, ep);
         st8<KT>(Kh + r * LDK + 8 * cg, kh);
         st8<KT>(Qh + r * LDK + 8 * cg, qh);
-        if constexpr (!F32) {
+        if constexpr (BF16) {
           st8<KT>(Kl + r * LDK + 8 * cg, kl);
           st8<KT>(Ql + r * LDK + 8 * cg, ql);
         }
       }
-      // Z = w * v for this value block (fp32, exact for bf16 inputs)
-      {
-        constexpr int EPT = Cfg::EPT, TPR = Cfg::TPR;
-        const int r = tid / TPR, j0 = (tid % TPR) * EPT;
-        float vv[8], ww[8];
-        if (r < clen) {
-          const size_t idx = ((size_t)(ctok + r) * H + h) * DV + jbase + j0;
-          if constexpr (EPT == 8) {
-            load8<BF16>(p.v, idx, vv);
-            load8<BF16>(p.w, idx, ww);
-          } else {
-            load4<BF16>(p.v, idx, vv);
-            load4<BF16>(p.w, idx, ww);
-          }
-        } else {
+      // Z^T: 4 consecutive rows of each owned value channel
 #pragma unroll
-          for (int i = 0; i < EPT; ++i) vv[i] = ww[i] = 0.f;
-        }
-#pragma unroll
-        for (int i = 0; i < EPT; i += 4)
-          *reinterpret_cast<float4*>(Zf + r * LDZ + j0 + i) =
-              make_float4(ww[i] * vv[i], ww[i + 1] * vv[i + 1], ww[i + 2] * vv[i + 2],
-                          ww[i + 3] * vv[i + 3]);
+      for (int e = 0; e < CPT; ++e) {
+        const float zz[4] = {z[0][e], z[1][e], z[2][e], z[3][e]};
+        stn<ST, 4>(ZT + (CPT * vc + e) * LDC + 4 * vq, zz);
       }
     }
     __syncthreads();
 
-    // ================= phase P: T and A_qk on MFMA =================================
-    for (int ti = wv; ti < 10; ti += NW) {
-      int a, bb;
-      tri_tile(ti, a, bb);
-      f32x4 accT = mma_lds<KT, DK>(zero4(), Ep + 16 * a * LDK, LDK, Kh + 16 * bb * LDK, LDK);
-      f32x4 accA = mma_lds<KT, DK>(zero4(), Qh + 16 * a * LDK, LDK, Kh + 16 * bb * LDK, LDK);
-      if constexpr (!F32) {
-        accA = mma_lds<KT, DK>(accA, Qh + 16 * a * LDK, LDK, Kl + 16 * bb * LDK, LDK);
-        accA = mma_lds<KT, DK>(accA, Ql + 16 * a * LDK, LDK, Kh + 16 * bb * LDK, LDK);
-      }
+    // ================= phase P: T^T and A_qk^T on MFMA ==========================
+    {
+      // A_qk tiles wv, wv+4, wv+8; T tiles: wave 0 {8}, 1 {9}, 2 {0..3}, 3 {4..7}
+      for (int ti = wv; ti < 10; ti += NW) {
+        int a, b;
+        tri_tile(ti, a, b);
+        f32x4 acc = mma_lds<KT, DK>(zero4(), Kh + 16 * b * LDK, LDK, Qh + 16 * a * LDK, LDK);
+        if constexpr (BF16) {
+          acc = mma_lds<KT, DK>(acc, Kh + 16 * b * LDK, LDK, Ql + 16 * a * LDK, LDK);
+          acc = mma_lds<KT, DK>(acc, Kl + 16 * b * LDK, LDK, Qh + 16 * a * LDK, LDK);
+        }
+        // lane holds A_qk[16a + m][16b + 4*g4 + q]
+        if (a == b) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int rl = 4 * g4 + q;                 // row inside the 16-block
-        const int r = 16 * a + rl, s = 16 * bb + m;
-        if (a == bb) {
-          Td[(a * 16 + rl) * 16 + m] = (m < rl) ? accT[q] : 0.f;
-          Aqk[r * LDC + s] = cvt<ST>((m <= rl) ? accA[q] : 0.f);
+          for (int q = 0; q < 4; ++q) acc[q] = (4 * g4 + q <= m) ? acc[q] : 0.f;
+        }
+        *reinterpret_cast<SV4*>(Aqk + (16 * a + m) * LDC + 16 * b + 4 * g4) = cvt4<SV4>(acc);
+      }
+      const int t0 = wv == 0 ? 8 : wv == 1 ? 9 : wv == 2 ? 0 : 4;
+      const int tn = wv < 2 ? 1 : 4;
+      for (int ti = t0; ti < t0 + tn; ++ti) {
+        int a, b;
+        tri_tile(ti, a, b);
+        f32x4 acc = mma_lds<KT, DK>(zero4(), Kh + 16 * b * LDK, LDK, Ep + 16 * a * LDK, LDK);
+        // lane holds T[16a + m][16b + 4*g4 + q]
+        if (a == b) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[q] = (4 * g4 + q < m) ? acc[q] : 0.f;
+          *reinterpret_cast<float4*>(Td + (a * 16 + m) * 16 + 4 * g4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         } else {
-          Tn[r * LDC + s] = cvt<ST>(-accT[q]);
-          Aqk[r * LDC + s] = cvt<ST>(accA[q]);
+          *reinterpret_cast<SV4*>(Tn + (16 * a + m) * LDC + 16 * b + 4 * g4) = neg_cvt4<SV4>(acc);
         }
       }
     }
     __syncthreads();
 
-    // ======= phase S(i): diagonal inverses; late operand tiles into region X =======
-#pragma unroll
-    for (int pr = 0; pr < RPT; ++pr) {
-      const int r = rg * RPT + pr;
+    // ==== phase S(i): diagonal inverses; state-pass tiles into region X ===========
+    {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        Eh[r * LDK + 8 * cg + i] = cvt<ST>(eh[pr][i]);
-        Qg[r * LDK + 8 * cg + i] = cvt<ST>(qg[pr][i]);
-        KtT[(8 * cg + i) * LDC + r] = cvt<ST>(kt[pr][i]);
-      }
-    }
-    if (lane < 16) {
-      // column `lane` of (I + T_aa)^-1 by forward substitution, fp32
-      const int a = wv;
-      const float* Ta = Td + a * 256;
-      float xs[16];
+        float col[RPT], col2[RPT];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = (r == lane) ? 1.f : 0.f;
-#pragma unroll
-        for (int s = 0; s < r; ++s) acc = fmaf(-Ta[r * 16 + s], xs[s], acc);
-        xs[r] = acc;
+        for (int pr = 0; pr < RPT; ++pr) {
+          col[pr] = eh[pr][i];
+          col2[pr] = kt[pr][i];
+        }
+        stn<ST, RPT>(EhT + (8 * cg + i) * LDC + r0, col);
+        stn<ST, RPT>(KtT + (8 * cg + i) * LDC + r0, col2);
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) Ad[(a * 16 + r) * LDA + lane] = cvt<ST>(xs[r]);
+      for (int pr = 0; pr < RPT; ++pr) st8<ST>(Qg + (r0 + pr) * LDK + 8 * cg, qg[pr]);
+      if (wv == 0) {
+        // lane 16a + c: column c of (I + T_aa)^-1, fp32 forward substitution
+        const int a = lane >> 4, cc = lane & 15;
+        const float* Ta = Td + a * 256;
+        float xs[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float acc = (r == cc) ? 1.f : 0.f;
+#pragma unroll
+          for (int s = 0; s < r; ++s) acc = fmaf(-Ta[r * 16 + s], xs[s], acc);
+          xs[r] = acc;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Am[(16 * a + r) * LDC + 16 * a + cc] = cvt<ST>(xs[r]);
+      }
     }
     __syncthreads();
 
-    // ===== phase S(ii): block forward substitution for Y = A E and U = A Z ==========
+    // ==== phase S(ii): off-diagonal blocks of A ===================================
+    if (wv == 3) wy_column<0, ST, SV4, LDC>(Tn, Am);
+    else if (wv == 2) wy_column<1, ST, SV4, LDC>(Tn, Am);
+    else if (wv == 1) wy_column<2, ST, SV4, LDC>(Tn, Am);
+    __syncthreads();
+
+    // ==== phase Y: Y^T = E^T A^T (stored as -Y), U = A Z (kept) ===================
+    f32x4 Ureg[NJT];
     {
-      constexpr int NCTY = DK / 16, NCT = DK / 16 + DVB / 16;
-      for (int ct = wv; ct < NCT; ct += NW) {
-        const bool isY = ct < NCTY;
-        const int col = isY ? 16 * ct + m : 16 * (ct - NCTY) + m;
-        SV4 xh[4];
+      for (int ib = wv; ib < DK / 16; ib += NW) {
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           f32x4 acc;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = 16 * a + 4 * g4 + q;
-            acc[q] = isY ? (float)Eh[r * LDK + col] : Zf[r * LDZ + col];
-          }
-#pragma unroll
-          for (int b = 0; b < a; ++b)
-            acc = mma16(*reinterpret_cast<const SV4*>(Tn + (16 * a + m) * LDC + 16 * b + 4 * g4),
-                        xh[b], acc);
-          const SV4 wvec = cvt4<SV4>(acc);
-          const f32x4 xa =
-              mma16(*reinterpret_cast<const SV4*>(Ad + (16 * a + m) * LDA + 4 * g4), wvec, zero4());
-          xh[a] = cvt4<SV4>(xa);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = 16 * a + 4 * g4 + q;
-            if (isY) Yn[r * LDK + col] = cvt<ST>(-xa[q]);
-            else Uf[r * LDZ + col] = xa[q];
-          }
+          if (a < 2) acc = mma_lds<ST, 32>(zero4(), EhT + 16 * ib * LDC, LDC, Am + 16 * a * LDC, LDC);
+          else acc = mma_lds<ST, 64>(zero4(), EhT + 16 * ib * LDC, LDC, Am + 16 * a * LDC, LDC);
+          // lane holds Y[16a + m][16ib + 4*g4 + q]
+          *reinterpret_cast<SV4*>(Yn + (16 * a + m) * LDK + 16 * ib + 4 * g4) = neg_cvt4<SV4>(acc);
         }
       }
-    }
-    __syncthreads();
-
-    // ================= phase R: R = U - Y S =========================================
-    for (int t = wv; t < 4 * (DVB / 16); t += NW) {
-      const int a = t & 3, jt = t >> 2;
-      f32x4 acc;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = Uf[(16 * a + 4 * g4 + q) * LDZ + 16 * jt + m];
-      acc = mma_lds<ST, DK>(acc, Yn + 16 * a * LDK, LDK, Scur + 16 * jt * LDK, LDK);
-      *reinterpret_cast<SV4*>(RT + (16 * jt + m) * LDC + 16 * a + 4 * g4) = cvt4<SV4>(acc);
+      for (int jt = 0; jt < NJT; ++jt)
+        Ureg[jt] = mma_lds<ST, CH>(zero4(), Am + 16 * wv * LDC, LDC, ZT + 16 * jt * LDC, LDC);
     }
     __syncthreads();
 
-    // ========== phase O: O^T = S^T Q_g^T + R^T A_qk^T ;  state update ===============
-    for (int t = wv; t < 4 * (DVB / 16); t += NW) {
-      const int a = t & 3, jt = t >> 2;
-      // two accumulators: a K=16 MFMA must not extend a K=32 MFMA chain
-      f32x4 acc = mma_lds<ST, DK>(zero4(), Scur + 16 * jt * LDK, LDK, Qg + 16 * a * LDK, LDK);
-      const f32x4 acc2 =
-          mma_lds_k16<ST, CH>(zero4(), RT + 16 * jt * LDC, LDC, Aqk + 16 * a * LDC, LDC, 16 * (a + 1));
-      acc += acc2;
-      const int r = 16 * a + m;
+    // ================= phase R: R = U - Y S =======================================
+#pragma unroll
+    for (int jt = 0; jt < NJT; ++jt) {
+      const f32x4 acc = mma_lds<ST, DK>(Ureg[jt], Yn + 16 * wv * LDK, LDK, Scur + 16 * jt * LDK, LDK);
+      // lane holds R[16wv + 4*g4 + q][16jt + m]
+      *reinterpret_cast<SV4*>(RT + (16 * jt + m) * LDC + 16 * wv + 4 * g4) = cvt4<SV4>(acc);
+    }
+    __syncthreads();
+
+    // ======= phase O: O^T = S^T Q_g^T + R^T A_qk^T ;  state update ==================
+#pragma unroll
+    for (int jt = 0; jt < NJT; ++jt) {
+      f32x4 acc = mma_lds<ST, DK>(zero4(), Scur + 16 * jt * LDK, LDK, Qg + 16 * wv * LDK, LDK);
+      acc = mma_lds<ST, CH>(acc, RT + 16 * jt * LDC, LDC, Aqk + 16 * wv * LDC, LDC);
+      // lane holds O[16wv + m][16jt + 4*g4 + q]
+      const int r = 16 * wv + m;
       if (r < clen) {
         const float vals[4] = {acc[0], acc[1], acc[2], acc[3]};
         store4<BF16>(p.o, ((size_t)(ctok + r) * H + h) * DV + jbase + 16 * jt + 4 * g4, vals);
@@ -436,8 +610,11 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs p) {
       if (t < Cfg::NSTILE) {
         const int ib = t % (DK / 16), jt = t / (DK / 16);
         f32x4 acc = Sacc[u];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] *= gC[16 * ib + 4 * g4 + q];
+        const float4 gc4 = *reinterpret_cast<const float4*>(gC + 16 * ib + 4 * g4);
+        acc[0] *= gc4.x;
+        acc[1] *= gc4.y;
+        acc[2] *= gc4.z;
+        acc[3] *= gc4.w;
         acc = mma_lds<ST, CH>(acc, KtT + 16 * ib * LDC, LDC, RT + 16 * jt * LDC, LDC);
         Sacc[u] = acc;
         *reinterpret_cast<SV4*>(Snext + (16 * jt + m) * LDK + 16 * ib + 4 * g4) = cvt4<SV4>(acc);
@@ -465,8 +642,8 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs p) {
 
 // ---- host-side dispatch -------------------------------------------------------------
 
-template <int DK, int DVB, bool F32>
-static hipError_t launch_variant(const ChunkArgs& a, hipStream_t stream) {
+template <int DK, int DVB, bool F32, bool LA16>
+static hipError_t launch_variant1(const ChunkArgs& a, hipStream_t stream) {
   typedef ChunkCfg<DK, DVB, F32> Cfg;
   const int NB = a.DV / DVB;
   const long long pairs = (long long)a.N * a.H;
@@ -480,14 +657,20 @@ static hipError_t launch_variant(const ChunkArgs& a, hipStream_t stream) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64 || !attr_set[dev]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_fwd_kernel<DK, DVB, F32>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_fwd_kernel<DK, DVB, F32, LA16>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::BYTES);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < 64) attr_set[dev] = true;
   }
-  hipLaunchKernelGGL((chunk_fwd_kernel<DK, DVB, F32>), dim3((unsigned)grid), dim3(NT), Cfg::BYTES,
+  hipLaunchKernelGGL((chunk_fwd_kernel<DK, DVB, F32, LA16>), dim3((unsigned)grid), dim3(NT), Cfg::BYTES,
                      stream, a);
   return hipGetLastError();
+}
+
+template <int DK, int DVB, bool F32>
+static hipError_t launch_variant(const ChunkArgs& a, hipStream_t stream) {
+  return a.la_bf16 ? launch_variant1<DK, DVB, F32, true>(a, stream)
+                   : launch_variant1<DK, DVB, F32, false>(a, stream);
 }
 
 bool chunk_supported(int dk, int dv, bool bf16) {
