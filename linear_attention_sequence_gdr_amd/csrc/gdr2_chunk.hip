@@ -2,7 +2,7 @@
 // gfx950 (Gated DeltaNet-2 pages, "Chunkwise Parallel Training via WY
 // Representation", Steps 1-3, Eqs. 20-24; packed sequences per Appendix C.6).
 //
-// One workgroup (256 threads, 4 wavefronts) owns one (sequence, head, block
+// One workgroup (512 threads, 8 wavefronts) owns one (sequence, head, block
 // of DVB value channels) and walks the sequence's 64-token chunks in order.
 // The value channels of the state are independent of each other (every
 // key-side quantity is shared, and column j of S, U, R, O depends only on
@@ -19,8 +19,8 @@
 //       e2 = 2^(G_m - G), so no factor exceeds the decay over half a chunk;
 //       E' = e1*b*k, K' = e2*k, Q' = e1*q, and the un-centred E = gamma*b*k,
 //       Q_g = gamma*q, K_tail = (gamma_C/gamma)*k, Z = w*v (Step 1, Eq. 20).
-//       Each thread owns 4 consecutive rows, so the transposed copies E^T,
-//       K_tail^T and Z^T are written as 8-byte vectors.
+//       Each thread owns consecutive rows, so the transposed copies E^T,
+//       K_tail^T and Z^T are written as vectors.
 //   P   T^T = K' E'^T and A_qk^T = K' Q'^T on MFMA (the centring cancels in
 //       every product; Step 2 and the A_qk of Eq. 24).  Computing the
 //       transposes lets each lane store 4 adjacent entries of a row.
@@ -51,8 +51,8 @@
 namespace gdr2 {
 
 constexpr int CH = 64;   // chunk length
-constexpr int NT = 256;  // threads per workgroup
-constexpr int NW = 4;    // wavefronts per workgroup
+constexpr int NT = 512;  // threads per workgroup
+constexpr int NW = 8;    // wavefronts per workgroup (two per SIMD)
 constexpr float LOG2E = 1.4426950408889634f;
 
 template <int DK, int DVB, bool F32>
@@ -75,7 +75,7 @@ struct ChunkCfg {
   static constexpr size_t O_YN = O_QG + (size_t)CH * LDK * SS;
   static constexpr size_t XR = O_YN + (size_t)CH * LDK * SS;
   static constexpr size_t X = ((XP > XR ? XP : XR) + 15) / 16 * 16;
-  static constexpr size_t O_TD = X;                                 // fp32 [4][16][16] diag T
+  static constexpr size_t O_TD = X;                                 // fp32 [4][16][16] diag T^T
   static constexpr size_t O_TN = O_TD + 4 * 16 * 16 * 4;            // ST [64][LDC]  -T
   static constexpr size_t O_A = O_TN + (size_t)CH * LDC * SS;       // ST [64][LDC]  A
   static constexpr size_t O_AQK = O_A + (size_t)CH * LDC * SS;      // ST [64][LDC]  A_qk
@@ -85,20 +85,19 @@ struct ChunkCfg {
   static constexpr size_t O_GC = O_S + (size_t)2 * DVB * LDK * SS;  // fp32 [DK] gamma_C
   static constexpr size_t BYTES = O_GC + (size_t)DK * 4;
   static_assert(BYTES <= 160 * 1024, "LDS budget exceeded");
-  // phase-L mapping: thread = (column group cg of 8 key channels, row group rg
-  // of RPT consecutive rows); the RG row groups of a column group are
+  // phase-L mapping: thread = (column group cg of EPC key channels, row group
+  // rg of RPT consecutive rows); the RG row groups of a column group are
   // consecutive lanes of one wavefront.
-  static constexpr int CG = DK / 8, RG = NT / CG, RPT = CH / RG;
+  static constexpr int EPC = 4, CG = DK / EPC, RG = NT / CG, RPT = CH / RG;
   static_assert(RG >= 16 && RG <= 64 && CH % RG == 0, "bad phase-L mapping");
-  // v/w mapping: 4 consecutive rows x CPT value channels per thread
-  static constexpr int CPT = DVB / 16;
-  static_assert(CPT == 1 || CPT == 2, "DVB must be 16 or 32");
+  // v/w mapping: thread = (value channel vc, row group vq of VR consecutive rows)
+  static constexpr int VR = CH * DVB / NT;
+  static_assert(VR == 2 || VR == 4, "DVB must be 16 or 32");
   static constexpr int NSTILE = (DK / 16) * (DVB / 16);  // 16x16 state tiles
   static constexpr int NSU = (NSTILE + NW - 1) / NW;     // state tiles per wavefront
   static constexpr int NJT = DVB / 16;                   // value column tiles
   static constexpr int ESZ = F32 ? 4 : 2;                // bytes per stored input element
-  static constexpr int KW = F32 ? 8 : 4;                 // dwords per 8 key elements
-  static constexpr int VB = CPT * ESZ;                   // bytes per row of v/w per thread
+  static constexpr int KW = F32 ? 4 : 2;                 // dwords per EPC key elements
 };
 
 template <typename T> __device__ __forceinline__ T cvt(float x) { return (T)x; }
@@ -169,6 +168,18 @@ __device__ __forceinline__ float dpp_shr(float v, int n) {
   return __builtin_bit_cast(float, r);
 }
 
+// Broadcast lane k of each group of four lanes (DPP quad_perm).
+__device__ __forceinline__ float quad_bcast(float v, int k) {
+  int r;
+  switch (k) {
+    case 0: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x00, 0xf, 0xf, false); break;
+    case 1: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x55, 0xf, 0xf, false); break;
+    case 2: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xaa, 0xf, 0xf, false); break;
+    default: r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xff, 0xf, 0xf, false); break;
+  }
+  return __builtin_bit_cast(float, r);
+}
+
 // Inclusive prefix sum over groups of RG consecutive lanes (RG = 16, 32, 64):
 // a DPP scan inside each 16-lane row (row_shr 1, 2, 4, 8), then row carries.
 template <int RG>
@@ -228,6 +239,57 @@ __device__ __forceinline__ void unpack8(const uint32_t (&w)[KW], float out[8]) {
   }
 }
 
+// Round to the nearest bf16 value, returned as fp32 (hardware conversion).
+__device__ __forceinline__ float bf16_round(float x) { return (float)(__bf16)x; }
+
+// Write 4 consecutive fp32 values as E (8 B for 16-bit types, 16 B for fp32).
+template <typename E>
+__device__ __forceinline__ void st4(E* dst, const float v[4]) {
+  if constexpr (std::is_same<E, float>::value) {
+    *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    typedef __attribute__((ext_vector_type(4))) E V4;
+    *reinterpret_cast<V4*>(dst) = V4{(E)v[0], (E)v[1], (E)v[2], (E)v[3]};
+  }
+}
+
+// 4 stored key elements (bf16 pairs in 2 words, or 4 fp32 words) to fp32.
+template <bool F32, int NWD>
+__device__ __forceinline__ void unpack4(const uint32_t (&w)[NWD], float out[4]) {
+  if constexpr (F32) {
+    static_assert(NWD == 4, "fp32: 4 words");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(w[i]);
+  } else {
+    static_assert(NWD == 2, "bf16: 2 words");
+    out[0] = __uint_as_float(w[0] << 16);
+    out[1] = __uint_as_float(w[0] & 0xffff0000u);
+    out[2] = __uint_as_float(w[1] << 16);
+    out[3] = __uint_as_float(w[1] & 0xffff0000u);
+  }
+}
+
+// A raw buffer resource over [base, base + bytes): loads outside read as 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// N consecutive words through a buffer resource.
+template <int N>
+__device__ __forceinline__ void bld(uint32_t (&dst)[N], __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef __attribute__((ext_vector_type(2))) unsigned int u2;
+  typedef __attribute__((ext_vector_type(4))) unsigned int u4;
+  if constexpr (N == 4) {
+    const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+  } else if constexpr (N == 2) {
+    const u2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    dst[0] = v.x; dst[1] = v.y;
+  } else {
+    dst[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+  }
+}
+
 // Off-diagonal blocks of column block B of A = (I + T)^-1 by the block
 // recurrence A_aB = A_aa (-sum_{B<=c<a} T_ac A_cB); Tn holds -T and the
 // diagonal blocks of A are already in Am.
@@ -258,9 +320,9 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs p) {
   typedef typename Cfg::ST ST;
   typedef typename Cfg::SV4 SV4;
   constexpr bool BF16 = !F32;
-  constexpr int LDK = Cfg::LDK, LDC = Cfg::LDC;
-  constexpr int RPT = Cfg::RPT, RG = Cfg::RG, CPT = Cfg::CPT, NJT = Cfg::NJT;
-  constexpr int ESZ = Cfg::ESZ, KW = Cfg::KW;
+  constexpr int LDK = Cfg::LDK, LDC = Cfg::LDC, EPC = Cfg::EPC;
+  constexpr int RPT = Cfg::RPT, RG = Cfg::RG, VR = Cfg::VR, NJT = Cfg::NJT;
+  constexpr int ESZ = Cfg::ESZ, KW = Cfg::KW, LW = LA16 ? 2 : 4;
 
   extern __shared__ __align__(16) unsigned char smem[];
   KT* Ep = reinterpret_cast<KT*>(smem);
@@ -272,7 +334,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs p) {
   ST* KtT = reinterpret_cast<ST*>(smem + Cfg::O_KTT);
   ST* Qg = reinterpret_cast<ST*>(smem + Cfg::O_QG);
   ST* Yn = reinterpret_cast<ST*>(smem + Cfg::O_YN);
-  float* Td = reinterpret_cast<float*>(smem + Cfg::O_TD);
+  float* Tdt = reinterpret_cast<float*>(smem + Cfg::O_TD);
   ST* Tn = reinterpret_cast<ST*>(smem + Cfg::O_TN);
   ST* Am = reinterpret_cast<ST*>(smem + Cfg::O_A);
   ST* Aqk = reinterpret_cast<ST*>(smem + Cfg::O_AQK);
@@ -339,52 +401,65 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs p) {
     }
   }
 
-  // phase-L coordinates: rows r0 .. r0+RPT-1, key channels 8*cg .. 8*cg+7
+  // phase-L coordinates: rows r0 .. r0+RPT-1, key channels EPC*cg ..
   const int cg = tid / RG, rg = tid % RG, r0 = rg * RPT;
-  // v/w coordinates: rows 4*vq .. 4*vq+3, value channels CPT*vc ..
-  const int vc = tid % 16, vq = tid / 16;
+  // v/w coordinates: value channel vc, rows VR*vq .. VR*vq+VR-1
+  const int vc = tid % DVB, vq = tid / DVB;
+  // byte offsets of this thread's elements inside a chunk (a chunk spans 64
+  // token rows, so 32 bits suffice); the chunk base itself is uniform
+  const size_t krow = (size_t)H * DK, vrow = (size_t)H * DV;
+  uint32_t koff[RPT], goff[RPT], voff[VR];
+#pragma unroll
+  for (int pr = 0; pr < RPT; ++pr) {
+    koff[pr] = (uint32_t)(((r0 + pr) * krow + EPC * cg) * ESZ);
+    goff[pr] = (uint32_t)(((r0 + pr) * krow + EPC * cg) * (LA16 ? 2 : 4));
+  }
+#pragma unroll
+  for (int pr = 0; pr < VR; ++pr) voff[pr] = (uint32_t)(((VR * vq + pr) * vrow + vc) * ESZ);
 
   // raw inputs of the chunk in flight (registers)
-  uint32_t rq[RPT][KW], rk[RPT][KW], rb[RPT][KW], rgd[RPT][LA16 ? 4 : 8];
-  uint32_t rv[4], rw[4];
+  uint32_t rq[RPT][KW], rk[RPT][KW], rb[RPT][KW], rgd[RPT][LW];
+  uint32_t rv[VR], rw[VR];
+  // Buffer loads against a per-chunk resource whose range ends at the last
+  // valid token row: rows past a ragged end read as zero without branches
+  // and nothing outside the caller's tensors is touched.
   auto fetch = [&](int c) {
-    const long long ctok = tok0 + (long long)c * CH;
     const int clen = min(CH, len - c * CH);
+    const size_t crow = (size_t)tok0 + (size_t)c * CH;
+    const size_t kel = crow * krow + (size_t)h * DK, vel = crow * vrow + (size_t)h * DV + jbase;
+    const int kbytes = (int)(clen * krow * ESZ), gbytes = (int)(clen * krow * (LA16 ? 2 : 4));
+    const int vbytes = (int)(clen * vrow * ESZ);
+    const auto rsq = make_rsrc(static_cast<const char*>(p.q) + kel * ESZ, kbytes);
+    const auto rsk = make_rsrc(static_cast<const char*>(p.k) + kel * ESZ, kbytes);
+    const auto rsb = make_rsrc(static_cast<const char*>(p.b) + kel * ESZ, kbytes);
+    const auto rsg = make_rsrc(static_cast<const char*>(p.la) + kel * (LA16 ? 2 : 4), gbytes);
+    const auto rsv = make_rsrc(static_cast<const char*>(p.v) + vel * ESZ, vbytes);
+    const auto rsw = make_rsrc(static_cast<const char*>(p.w) + vel * ESZ, vbytes);
 #pragma unroll
     for (int pr = 0; pr < RPT; ++pr) {
-      const int r = r0 + pr;
-      if (r < clen) {
-        const size_t idx = ((size_t)(ctok + r) * H + h) * DK + 8 * cg;
-        ldw(rq[pr], static_cast<const char*>(p.q) + idx * ESZ);
-        ldw(rk[pr], static_cast<const char*>(p.k) + idx * ESZ);
-        ldw(rb[pr], static_cast<const char*>(p.b) + idx * ESZ);
-        // raw words only: expanding bf16 here would wait for the load
-        ldw(rgd[pr], static_cast<const char*>(p.la) + idx * (LA16 ? 2 : 4));
-      } else {
-#pragma unroll
-        for (int i = 0; i < KW; ++i) rq[pr][i] = rk[pr][i] = rb[pr][i] = 0u;
-#pragma unroll
-        for (int i = 0; i < (LA16 ? 4 : 8); ++i) rgd[pr][i] = 0u;
-      }
+      bld(rq[pr], rsq, koff[pr]);
+      bld(rk[pr], rsk, koff[pr]);
+      bld(rb[pr], rsb, koff[pr]);
+      // raw words only: expanding bf16 here would wait for the load
+      bld(rgd[pr], rsg, goff[pr]);
     }
 #pragma unroll
-    for (int pr = 0; pr < 4; ++pr) {
-      const int r = 4 * vq + pr;
-      rv[pr] = rw[pr] = 0u;
-      if (r < clen) {
-        const size_t idx = ((size_t)(ctok + r) * H + h) * DV + jbase + CPT * vc;
-        if constexpr (Cfg::VB == 4) {
-          rv[pr] = *reinterpret_cast<const uint32_t*>(static_cast<const char*>(p.v) + idx * ESZ);
-          rw[pr] = *reinterpret_cast<const uint32_t*>(static_cast<const char*>(p.w) + idx * ESZ);
-        } else if constexpr (Cfg::VB == 2) {
-          rv[pr] = static_cast<const uint16_t*>(p.v)[idx];
-          rw[pr] = static_cast<const uint16_t*>(p.w)[idx];
-        }
+    for (int pr = 0; pr < VR; ++pr) {
+      if constexpr (F32) {
+        rv[pr] = __builtin_amdgcn_raw_buffer_load_b32(rsv, voff[pr], 0, 0);
+        rw[pr] = __builtin_amdgcn_raw_buffer_load_b32(rsw, voff[pr], 0, 0);
+      } else {
+        rv[pr] = __builtin_amdgcn_raw_buffer_load_b16(rsv, voff[pr], 0, 0);
+        rw[pr] = __builtin_amdgcn_raw_buffer_load_b16(rsw, voff[pr], 0, 0);
       }
     }
   };
-  // fp32 inputs with 32-channel blocks would need 8 bytes of v/w per row
-  static_assert(Cfg::VB <= 4, "v/w fetch covers at most 4 bytes per row");
+
+  // the output tile of a chunk is stored during the next chunk, after its
+  // prefetch is issued, so that waiting for one never waits for the other
+  bool o_pending = false;
+  size_t o_idx = 0;
+  float o_val[4] = {0.f, 0.f, 0.f, 0.f};
 
   const int nchunks = (len + CH - 1) / CH;
   if (nchunks > 0) fetch(0);
@@ -395,29 +470,24 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs p) {
     const int clen = min(CH, len - c * CH);
 
     // ================= phase L: decay scan and operand tiles ====================
-    float eh[RPT][8], qg[RPT][8], kt[RPT][8];
+    // E, Q_g, K_tail rows kept packed (16-bit on the bf16 path) until phase S
+    SV4 eh[RPT], qg[RPT], kt[RPT];
     {
-      float G[RPT][8], kv[RPT][8], qv[RPT][8], bv[RPT][8];
-      float z[4][CPT];
+      float G[RPT][EPC], kv[RPT][EPC], qv[RPT][EPC], bv[RPT][EPC];
+      float z[VR];
 #pragma unroll
       for (int pr = 0; pr < RPT; ++pr) {
-        unpack8<F32>(rq[pr], qv[pr]);
-        unpack8<F32>(rk[pr], kv[pr]);
-        unpack8<F32>(rb[pr], bv[pr]);
-        unpack8<!LA16>(rgd[pr], G[pr]);
+        unpack4<F32>(rq[pr], qv[pr]);
+        unpack4<F32>(rk[pr], kv[pr]);
+        unpack4<F32>(rb[pr], bv[pr]);
+        unpack4<!LA16>(rgd[pr], G[pr]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) G[pr][i] *= LOG2E;
+        for (int i = 0; i < EPC; ++i) G[pr][i] *= LOG2E;
       }
 #pragma unroll
-      for (int pr = 0; pr < 4; ++pr) {
-        if constexpr (F32) {
-          z[pr][0] = __uint_as_float(rv[pr]) * __uint_as_float(rw[pr]);
-        } else if constexpr (CPT == 2) {
-          z[pr][0] = __uint_as_float(rv[pr] << 16) * __uint_as_float(rw[pr] << 16);
-          z[pr][1] = __uint_as_float(rv[pr] & 0xffff0000u) * __uint_as_float(rw[pr] & 0xffff0000u);
-        } else {
-          z[pr][0] = __uint_as_float(rv[pr] << 16) * __uint_as_float(rw[pr] << 16);
-        }
+      for (int pr = 0; pr < VR; ++pr) {
+        if constexpr (F32) z[pr] = __uint_as_float(rv[pr]) * __uint_as_float(rw[pr]);
+        else z[pr] = __uint_as_float(rv[pr] << 16) * __uint_as_float(rw[pr] << 16);
       }
       // The raw registers are free: start the next chunk's loads now.  This
       // chunk's loads (issued a chunk ago) are waited for explicitly first;
@@ -425,16 +495,18 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs p) {
       // registers wait for the new loads as well.
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
       if (c + 1 < nchunks) fetch(c + 1);
+      if (o_pending) store4<BF16>(p.o, o_idx, o_val);
+      o_pending = false;
 
       // fp32 cumulative log2-decay over the chunk: serial inside the thread,
       // then a scan of thread totals across the RG row groups
 #pragma unroll
       for (int pr = 1; pr < RPT; ++pr)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) G[pr][i] += G[pr - 1][i];
-      float egm[8], egcm[8];
+        for (int i = 0; i < EPC; ++i) G[pr][i] += G[pr - 1][i];
+      float egm[EPC], egcm[EPC];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < EPC; ++i) {
         const float tot = G[RPT - 1][i];
         const float excl = seg_scan<RG>(tot) - tot;
 #pragma unroll
@@ -443,56 +515,56 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs p) {
         const float gc = __shfl(G[RPT - 1][i], RG - 1, RG);
         egm[i] = exp2_fast(gm);
         egcm[i] = exp2_fast(gc - gm);
-        if (rg == 0) gC[8 * cg + i] = exp2_fast(gc);
+        if (rg == 0) gC[EPC * cg + i] = exp2_fast(gc);
 #pragma unroll
         for (int pr = 0; pr < RPT; ++pr) G[pr][i] -= gm;  // centred: G - G_m
       }
 #pragma unroll
       for (int pr = 0; pr < RPT; ++pr) {
         const int r = r0 + pr;
-        float ep[8], kh[8], kl[8], qh[8], ql[8];
+        float ep[EPC], kh[EPC], kl[EPC], qh[EPC], ql[EPC];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < EPC; ++i) {
           const float e1 = exp2_fast(G[pr][i]);
           const float e2 = exp2_fast(-G[pr][i]);
           const float bk = bv[pr][i] * kv[pr][i];
           ep[i] = e1 * bk;
-          const float kb = e2 * kv[pr][i];
+          const float kbv = e2 * kv[pr][i];
           const float qp = e1 * qv[pr][i];
           if constexpr (F32) {
-            kh[i] = kb;
+            kh[i] = kbv;
             qh[i] = qp;
           } else {
-            kh[i] = (float)(__bf16)kb;
-            kl[i] = kb - kh[i];
-            qh[i] = (float)(__bf16)qp;
+            kh[i] = bf16_round(kbv);
+            kl[i] = kbv - kh[i];
+            qh[i] = bf16_round(qp);
             ql[i] = qp - qh[i];
           }
-          eh[pr][i] = ep[i] * egm[i];
-          qg[pr][i] = qp * egm[i];
-          kt[pr][i] = kb * egcm[i];
+          eh[pr][i] = cvt<ST>(ep[i] * egm[i]);
+          qg[pr][i] = cvt<ST>(qp * egm[i]);
+          kt[pr][i] = cvt<ST>(kbv * egcm[i]);
         }
-        st8<KT>(Ep + r * LDK + 8 * cg, ep);
-        st8<KT>(Kh + r * LDK + 8 * cg, kh);
-        st8<KT>(Qh + r * LDK + 8 * cg, qh);
+        st4<KT>(Ep + r * LDK + EPC * cg, ep);
+        st4<KT>(Kh + r * LDK + EPC * cg, kh);
+        st4<KT>(Qh + r * LDK + EPC * cg, qh);
         if constexpr (BF16) {
-          st8<KT>(Kl + r * LDK + 8 * cg, kl);
-          st8<KT>(Ql + r * LDK + 8 * cg, ql);
+          st4<KT>(Kl + r * LDK + EPC * cg, kl);
+          st4<KT>(Ql + r * LDK + EPC * cg, ql);
         }
       }
-      // Z^T: 4 consecutive rows of each owned value channel
-#pragma unroll
-      for (int e = 0; e < CPT; ++e) {
-        const float zz[4] = {z[0][e], z[1][e], z[2][e], z[3][e]};
-        stn<ST, 4>(ZT + (CPT * vc + e) * LDC + 4 * vq, zz);
-      }
+      // Z^T: VR consecutive rows of the owned value channel
+      stn<ST, VR>(ZT + vc * LDC + VR * vq, z);
     }
     __syncthreads();
 
     // ================= phase P: T^T and A_qk^T on MFMA ==========================
+    // tile t goes to wave t (and tiles 8, 9 to waves 0, 2); one wave forms
+    // both T and A_qk of its tile so the K' operand is read once per K step
     {
-      // A_qk tiles wv, wv+4, wv+8; T tiles: wave 0 {8}, 1 {9}, 2 {0..3}, 3 {4..7}
-      for (int ti = wv; ti < 10; ti += NW) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int ti = k == 0 ? wv : (wv == 0 ? 8 : wv == 2 ? 9 : -1);
+        if (ti < 0) break;
         int a, b;
         tri_tile(ti, a, b);
         f32x4 acc = mma_lds<KT, DK>(zero4(), Kh + 16 * b * LDK, LDK, Qh + 16 * a * LDK, LDK);
@@ -500,27 +572,18 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs p) {
           acc = mma_lds<KT, DK>(acc, Kh + 16 * b * LDK, LDK, Ql + 16 * a * LDK, LDK);
           acc = mma_lds<KT, DK>(acc, Kl + 16 * b * LDK, LDK, Qh + 16 * a * LDK, LDK);
         }
-        // lane holds A_qk[16a + m][16b + 4*g4 + q]
+        f32x4 acct = mma_lds<KT, DK>(zero4(), Kh + 16 * b * LDK, LDK, Ep + 16 * a * LDK, LDK);
+        // lanes hold A_qk[16a + m][16b + 4*g4 + q] and T[16a + m][16b + 4*g4 + q]
         if (a == b) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) acc[q] = (4 * g4 + q <= m) ? acc[q] : 0.f;
+          // diagonal blocks of T transposed, fp32: Tdt[a][s][r] = T[r][s], s < r
+#pragma unroll
+          for (int q = 0; q < 4; ++q) Tdt[(a * 16 + 4 * g4 + q) * 16 + m] = (4 * g4 + q < m) ? acct[q] : 0.f;
+        } else {
+          *reinterpret_cast<SV4*>(Tn + (16 * a + m) * LDC + 16 * b + 4 * g4) = neg_cvt4<SV4>(acct);
         }
         *reinterpret_cast<SV4*>(Aqk + (16 * a + m) * LDC + 16 * b + 4 * g4) = cvt4<SV4>(acc);
-      }
-      const int t0 = wv == 0 ? 8 : wv == 1 ? 9 : wv == 2 ? 0 : 4;
-      const int tn = wv < 2 ? 1 : 4;
-      for (int ti = t0; ti < t0 + tn; ++ti) {
-        int a, b;
-        tri_tile(ti, a, b);
-        f32x4 acc = mma_lds<KT, DK>(zero4(), Kh + 16 * b * LDK, LDK, Ep + 16 * a * LDK, LDK);
-        // lane holds T[16a + m][16b + 4*g4 + q]
-        if (a == b) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[q] = (4 * g4 + q < m) ? acc[q] : 0.f;
-          *reinterpret_cast<float4*>(Td + (a * 16 + m) * 16 + 4 * g4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        } else {
-          *reinterpret_cast<SV4*>(Tn + (16 * a + m) * LDC + 16 * b + 4 * g4) = neg_cvt4<SV4>(acc);
-        }
       }
     }
     __syncthreads();
@@ -528,32 +591,39 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs p) {
     // ==== phase S(i): diagonal inverses; state-pass tiles into region X ===========
     {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < EPC; ++i) {
         float col[RPT], col2[RPT];
 #pragma unroll
         for (int pr = 0; pr < RPT; ++pr) {
-          col[pr] = eh[pr][i];
-          col2[pr] = kt[pr][i];
+          col[pr] = (float)eh[pr][i];
+          col2[pr] = (float)kt[pr][i];
         }
-        stn<ST, RPT>(EhT + (8 * cg + i) * LDC + r0, col);
-        stn<ST, RPT>(KtT + (8 * cg + i) * LDC + r0, col2);
+        stn<ST, RPT>(EhT + (EPC * cg + i) * LDC + r0, col);
+        stn<ST, RPT>(KtT + (EPC * cg + i) * LDC + r0, col2);
       }
 #pragma unroll
-      for (int pr = 0; pr < RPT; ++pr) st8<ST>(Qg + (r0 + pr) * LDK + 8 * cg, qg[pr]);
-      if (wv == 0) {
-        // lane 16a + c: column c of (I + T_aa)^-1, fp32 forward substitution
-        const int a = lane >> 4, cc = lane & 15;
-        const float* Ta = Td + a * 256;
-        float xs[16];
+      for (int pr = 0; pr < RPT; ++pr) *reinterpret_cast<SV4*>(Qg + (r0 + pr) * LDK + EPC * cg) = qg[pr];
+      if (wv < 4) {
+        // wave a inverts I + T_aa: lane 4*cc + part holds rows 4*part .. 4*part+3
+        // of column cc and runs a right-looking fp32 forward substitution over
+        // the columns s of T_aa; row s of column cc is broadcast in its quad
+        const int a = wv, cc = lane >> 2, part = lane & 3;
+        const float4* Tc = reinterpret_cast<const float4*>(Tdt + a * 256);
+        float xs[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float acc = (r == cc) ? 1.f : 0.f;
+        for (int j = 0; j < 4; ++j) xs[j] = (4 * part + j == cc) ? 1.f : 0.f;
 #pragma unroll
-          for (int s = 0; s < r; ++s) acc = fmaf(-Ta[r * 16 + s], xs[s], acc);
-          xs[r] = acc;
+        for (int s = 0; s < 15; ++s) {
+          const float4 col = Tc[s * 4 + part];
+          const float xv = quad_bcast(xs[s & 3], s >> 2);
+          // T[r][s] is zero for r <= s, so finished rows are left unchanged
+          xs[0] = fmaf(-col.x, xv, xs[0]);
+          xs[1] = fmaf(-col.y, xv, xs[1]);
+          xs[2] = fmaf(-col.z, xv, xs[2]);
+          xs[3] = fmaf(-col.w, xv, xs[3]);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) Am[(16 * a + r) * LDC + 16 * a + cc] = cvt<ST>(xs[r]);
+        for (int j = 0; j < 4; ++j) Am[(16 * a + 4 * part + j) * LDC + 16 * a + cc] = cvt<ST>(xs[j]);
       }
     }
     __syncthreads();
@@ -565,9 +635,11 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs p) {
     __syncthreads();
 
     // ==== phase Y: Y^T = E^T A^T (stored as -Y), U = A Z (kept) ===================
-    f32x4 Ureg[NJT];
+    const int ua = wv & 3, ujt = wv >> 2;  // this wave's (row block, value tile)
+    f32x4 Ureg = zero4();
     {
-      for (int ib = wv; ib < DK / 16; ib += NW) {
+      if (wv < DK / 16) {
+        const int ib = wv;
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           f32x4 acc;
@@ -577,31 +649,29 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs p) {
           *reinterpret_cast<SV4*>(Yn + (16 * a + m) * LDK + 16 * ib + 4 * g4) = neg_cvt4<SV4>(acc);
         }
       }
-#pragma unroll
-      for (int jt = 0; jt < NJT; ++jt)
-        Ureg[jt] = mma_lds<ST, CH>(zero4(), Am + 16 * wv * LDC, LDC, ZT + 16 * jt * LDC, LDC);
+      if (ujt < NJT) Ureg = mma_lds<ST, CH>(zero4(), Am + 16 * ua * LDC, LDC, ZT + 16 * ujt * LDC, LDC);
     }
     __syncthreads();
 
     // ================= phase R: R = U - Y S =======================================
-#pragma unroll
-    for (int jt = 0; jt < NJT; ++jt) {
-      const f32x4 acc = mma_lds<ST, DK>(Ureg[jt], Yn + 16 * wv * LDK, LDK, Scur + 16 * jt * LDK, LDK);
-      // lane holds R[16wv + 4*g4 + q][16jt + m]
-      *reinterpret_cast<SV4*>(RT + (16 * jt + m) * LDC + 16 * wv + 4 * g4) = cvt4<SV4>(acc);
+    if (ujt < NJT) {
+      const f32x4 acc = mma_lds<ST, DK>(Ureg, Yn + 16 * ua * LDK, LDK, Scur + 16 * ujt * LDK, LDK);
+      // lane holds R[16ua + 4*g4 + q][16ujt + m]
+      *reinterpret_cast<SV4*>(RT + (16 * ujt + m) * LDC + 16 * ua + 4 * g4) = cvt4<SV4>(acc);
     }
     __syncthreads();
 
     // ======= phase O: O^T = S^T Q_g^T + R^T A_qk^T ;  state update ==================
-#pragma unroll
-    for (int jt = 0; jt < NJT; ++jt) {
-      f32x4 acc = mma_lds<ST, DK>(zero4(), Scur + 16 * jt * LDK, LDK, Qg + 16 * wv * LDK, LDK);
-      acc = mma_lds<ST, CH>(acc, RT + 16 * jt * LDC, LDC, Aqk + 16 * wv * LDC, LDC);
-      // lane holds O[16wv + m][16jt + 4*g4 + q]
-      const int r = 16 * wv + m;
+    if (ujt < NJT) {
+      f32x4 acc = mma_lds<ST, DK>(zero4(), Scur + 16 * ujt * LDK, LDK, Qg + 16 * ua * LDK, LDK);
+      acc = mma_lds<ST, CH>(acc, RT + 16 * ujt * LDC, LDC, Aqk + 16 * ua * LDC, LDC);
+      // lane holds O[16ua + m][16ujt + 4*g4 + q]
+      const int r = 16 * ua + m;
       if (r < clen) {
-        const float vals[4] = {acc[0], acc[1], acc[2], acc[3]};
-        store4<BF16>(p.o, ((size_t)(ctok + r) * H + h) * DV + jbase + 16 * jt + 4 * g4, vals);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o_val[q] = acc[q];
+        o_idx = ((size_t)(ctok + r) * H + h) * DV + jbase + 16 * ujt + 4 * g4;
+        o_pending = true;
       }
     }
 #pragma unroll
@@ -626,6 +696,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs p) {
     Snext = tmp;
   }
 
+  if (o_pending) store4<BF16>(p.o, o_idx, o_val);
   if (p.ST) {
 #pragma unroll
     for (int u = 0; u < Cfg::NSU; ++u) {
