@@ -55,9 +55,10 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(launch_bytes_alg):
-    """HBM bytes per launch measured by rocprofv3 counters (committed under
-    profiles/), only when they were taken on the current kernel sources."""
+def load_traffic(kernel_key):
+    """HBM bytes per launch of one kernel, from the rocprofv3 counter runs
+    committed under profiles/, only when they were taken on the current
+    kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -65,7 +66,47 @@ def load_traffic(launch_bytes_alg):
         return None
     if t.get("source_hash") != source_hash():
         return None
-    return t.get("bytes_per_launch")
+    k = t.get("kernels", {}).get(kernel_key)
+    return None if k is None else k["fetch_bytes"] + k["write_bytes"]
+
+
+def _counter_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def write_traffic(fetch_csv, write_csv, copy_mib, command):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch) into HBM bytes per launch for every libgdr2 kernel.  Each counter
+    is scaled by what it reads for the calibration copy (torch.neg over
+    copy_mib MiB of fp32: copy_mib MiB read and copy_mib MiB written)."""
+    known = copy_mib * 1024 * 1024
+    out = {"source_hash": source_hash(), "command": command, "kernels": {}, "calibration": {}}
+    per = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _counter_rows(path) if r.get("Counter_Name") == counter]
+        calib = [float(r["Counter_Value"]) * 1024 for r in rows if "neg" in r["Kernel_Name"]]
+        if not calib:
+            raise SystemExit(f"{path}: no calibration copy dispatch found")
+        factor = max(calib) / known
+        out["calibration"][counter] = {"copy_bytes": known, "counter_bytes": max(calib),
+                                       "factor": factor}
+        for r in rows:
+            name = r["Kernel_Name"]
+            if "gdr2::" not in name:
+                continue
+            key = name.split("gdr2::", 1)[1].split("<", 1)[0].split("(", 1)[0]
+            per.setdefault(key, {}).setdefault(counter, []).append(
+                float(r["Counter_Value"]) * 1024 / factor)
+    for key, d in per.items():
+        f, w = d.get("FETCH_SIZE", [0.0]), d.get("WRITE_SIZE", [0.0])
+        out["kernels"][key] = {"fetch_bytes": sum(f) / len(f), "write_bytes": sum(w) / len(w),
+                               "dispatches": len(f)}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fo:
+        json.dump(out, fo, indent=1)
+    print(json.dumps(out))
 
 
 def time_events(fn, steps, warmup, torch):
@@ -82,11 +123,14 @@ def time_events(fn, steps, warmup, torch):
 
 
 def cpu_baseline(wl, budget_s=12.0):
-    """The fp64 oracle as it stands, on a sample of whole (sequence, head) chains
-    of the forward workload, using every host core it is allowed."""
+    """The fp64 oracle as it stands, on whole (sequence, head) chains of the
+    forward workload, using every host core it is allowed.  The sample is as
+    many chains as fit the budget on the cores; when all of them fit, the
+    whole workload is repeated until the budget is spent."""
     import numpy as np
     import oracle
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    cores = min(cores, oracle.max_threads())  # read before the probe sets the thread count
     N, H = wl.B, wl.H
     # probe one chain to size the sample to the budget
     m = np.zeros((N, H), bool)
@@ -96,20 +140,23 @@ def cpu_baseline(wl, budget_s=12.0):
     oracle.fwd(q, k, v, g, b, w, mask=m[:1], nthreads=1)
     t1 = time.perf_counter() - t0
     pairs = int(max(1, min(N * H, cores * max(1, budget_s // max(t1, 1e-3)))))
-    pairs = max(min(pairs, N * H), 1)
     m = np.zeros(N * H, bool)
     m[:pairs] = True
     m = m.reshape(N, H)
     nseq = int(np.ceil(pairs / H))
     q, k, v, g, b, w = (oracle.f64(x[:nseq]) for x in (wl.q, wl.k, wl.v, wl.log_alpha, wl.b, wl.w))
     used = min(cores, pairs)
+    reps, dt = 0, 0.0
     t0 = time.perf_counter()
-    oracle.fwd(q, k, v, g, b, w, mask=m[:nseq], nthreads=used)
-    dt = time.perf_counter() - t0
-    head_tokens = pairs * wl.T
+    while reps == 0 or dt < budget_s:
+        oracle.fwd(q, k, v, g, b, w, mask=m[:nseq], nthreads=used)
+        reps += 1
+        dt = time.perf_counter() - t0
+    head_tokens = reps * pairs * wl.T
     return {"value": head_tokens / H / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": f"{pairs} of {N * H} (sequence, head) chains x {wl.T} tokens, fp64 "
-                      f"token-by-token, {dt:.1f} s; tokens/s counts a token once per {H} heads"}
+            "sample": f"{reps} x {pairs} of {N * H} (sequence, head) chains x {wl.T} tokens, fp64 "
+                      f"token-by-token, {dt:.1f} s on {used} threads; tokens/s counts a token "
+                      f"once per {H} heads"}
 
 
 def main():
@@ -119,7 +166,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run a plain copy of MIB MiB (for counter calibration)")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="host only: write the per-kernel HBM traffic table from two "
+                         "rocprofv3 --pmc counter_collection.csv files")
+    ap.add_argument("--traffic-command", default="",
+                    help="the command that produced the counter files (recorded)")
     args = ap.parse_args()
+    if args.traffic:
+        write_traffic(args.traffic[0], args.traffic[1], args.calibrate_copy, args.traffic_command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the Gated Delta Rule-2 path here has no multi-GPU "
               "mode (sequences and heads shard with no exchange; see DESIGN.md). Use --gpus 1.",
@@ -148,7 +205,7 @@ def main():
     tokens = B * T
     gbs = byts / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
-    traffic = load_traffic(byts)
+    traffic = load_traffic("chunk_fwd_kernel")
 
     # ---- decode: 256 sequences x 16 heads, fp32 state ---------------------------------
     S = I.decode_state().to(dev)
@@ -165,6 +222,15 @@ def main():
     dbytes = Nd * Hd * (2 * D * D * 4 + 6 * D * 4 + D * 4)
     dgbs = dbytes / (dms * 1e-3) / 1e9
     del S, pool
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * 1024 * 1024 // 4
+        src_t = torch.randn(n, device=dev)
+        dst_t = torch.empty_like(src_t)
+        for _ in range(3):
+            torch.neg(src_t, out=dst_t)
+        torch.cuda.synchronize()
+        del src_t, dst_t
 
     cpu = None
     if not args.no_cpu:
@@ -196,7 +262,8 @@ def main():
         "decode": {"workload": "gdr2_decode_step N256 H16 dk=dv=128 fp32 state in place",
                    "steps": args.decode_steps, "us_per_step": dms * 1e3, "alg_bytes": dbytes,
                    "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS,
-                                "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS}},
+                                "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
+                                "traffic": load_traffic("decode_kernel")}},
         "cpu_baseline": cpu,
         "source_hash": source_hash(),
     }
