@@ -199,7 +199,9 @@ def main():
     o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
     ST = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
-    fwd = lambda: G.gdr2_chunk_fwd(*ins, None, None, o=o, S_T=ST)
+    ws = torch.empty(max(1, G.gdr2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, 0, G.GDR2_BF16)),
+                     dtype=torch.uint8, device=dev)
+    fwd = lambda: G.gdr2_chunk_fwd(*ins, None, None, o=o, S_T=ST, workspace=ws)
     ms = time_events(fwd, args.steps, args.warmup, torch)
     byts, flops = fwd_algorithmic(B, T, H, dk, dv)
     tokens = B * T

@@ -140,11 +140,10 @@ def gdr2_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha:
         o = torch.empty((Bsz, T, H, dv), dtype=q.dtype, device=dev)
     if S_T is None and want_state:
         S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
-    ws_bytes = 0
-    if cu_seqlens is not None:
-        ws_bytes = gdr2_chunk_fwd_workspace_bytes(Bsz, T, H, dk, dv, N, in_dt)
-        if workspace is None and ws_bytes:
-            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_bytes = gdr2_chunk_fwd_workspace_bytes(Bsz, T, H, dk, dv,
+                                              N if cu_seqlens is not None else 0, in_dt)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     if workspace is not None:
         ws_bytes = workspace.numel() * workspace.element_size()
     for name, t, want in (("k", k, q.dtype), ("v", v, q.dtype), ("b", b, q.dtype), ("w", w, q.dtype),

@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdr2.so")
-SOURCES = ["gdr2_api.cpp", "gdr2_chunk.hip", "gdr2_decode.hip", "gdr2_schedule.hip"]
+SOURCES = ["gdr2_api.cpp", "gdr2_chunk.hip", "gdr2_intra.hip", "gdr2_state.hip", "gdr2_decode.hip",
+           "gdr2_schedule.hip"]
 ARCH = os.environ.get("GDR2_OFFLOAD_ARCH", "gfx950")
 
 

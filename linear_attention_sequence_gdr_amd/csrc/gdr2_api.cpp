@@ -30,6 +30,34 @@ bool dtype_ok(int t) { return t == GDR2_F32 || t == GDR2_BF16; }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Workspace of the two-pass forward (16-bit inputs): for packed sequences the
+// longest-first order, the chunk base per sequence and the chunk table, then
+// one record per (chunk, head).  Packed sequences add at most one partial
+// chunk each, so ceil(T/64) + N chunks bound the record count.
+struct Layout {
+  size_t order, cbase, tab, rec, total;
+  long long cap;  // chunks with a record
+};
+Layout two_pass_layout(int B, int T, int H, int dk, int dv, int num_seqs) {
+  Layout l{};
+  const long long nc = ((long long)T + 63) / 64;
+  size_t off = 0;
+  if (num_seqs > 0) {
+    l.cap = nc + num_seqs;
+    l.order = off;
+    off += align256(gdr2::schedule_bytes(num_seqs));
+    l.cbase = off;
+    off += align256(sizeof(int32_t) * ((size_t)num_seqs + 1));
+    l.tab = off;
+    off += align256(2 * sizeof(int32_t) * (size_t)l.cap);
+  } else {
+    l.cap = (long long)B * nc;
+  }
+  l.rec = off;
+  l.total = off + (size_t)l.cap * (size_t)H * gdr2::record_bytes(dk, dv);
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -57,8 +85,12 @@ size_t gdr2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
   if (B <= 0 || T < 0 || H <= 0 || !dim_ok(dk) || !dim_ok(dv) || num_seqs < 0 ||
       !dtype_ok(in_dtype))
     return 0;
-  const size_t s = gdr2::schedule_bytes(num_seqs);
-  return s ? align256(s) : 0;
+  if (in_dtype == GDR2_F32) {
+    const size_t s = gdr2::schedule_bytes(num_seqs);
+    return s ? align256(s) : 0;
+  }
+  const Layout l = two_pass_layout(B, T, H, dk, dv, num_seqs);
+  return l.total;
 }
 
 gdr2_status gdr2_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
@@ -94,23 +126,65 @@ gdr2_status gdr2_chunk_fwd(const void* q, const void* k, const void* v, const vo
   for (int i = 0; i < 11; ++i)
     if (ptrs[i] && !aligned16(ptrs[i]))
       return fail(GDR2_E_ALIGN, "gdr2_chunk_fwd: %s is not 16-byte aligned", names[i]);
-  const size_t need = cu_seqlens ? gdr2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, in_dtype) : 0;
+  const int ns = cu_seqlens ? N : 0;
+  if (bf16 && two_pass_layout(B, T, H, dk, dv, ns).cap * H > 0x7fffffffLL)
+    return fail(GDR2_E_SHAPE, "gdr2_chunk_fwd: %lld (chunk, head) items exceed 2^31 - 1",
+                two_pass_layout(B, T, H, dk, dv, ns).cap * H);
+  const size_t need = gdr2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, ns, in_dtype);
   if (need && (!workspace || workspace_bytes < need))
     return fail(GDR2_E_WORKSPACE, "gdr2_chunk_fwd: workspace of %zu bytes needed, got %zu%s", need,
                 workspace_bytes, workspace ? "" : " (NULL)");
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  int32_t* order = need ? static_cast<int32_t*>(workspace) : nullptr;
-  if (order) {
-    const hipError_t e = gdr2::launch_schedule(cu_seqlens, N, T, order, st);
-    if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "gdr2_chunk_fwd: schedule launch: %s", hipGetErrorString(e));
+  char* ws = static_cast<char*>(workspace);
+  if (!bf16) {
+    // fp32 inputs: single fused kernel per (sequence, head, value block)
+    int32_t* order = need ? reinterpret_cast<int32_t*>(ws) : nullptr;
+    if (order) {
+      const hipError_t e = gdr2::launch_schedule(cu_seqlens, N, T, order, st);
+      if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "gdr2_chunk_fwd: schedule launch: %s", hipGetErrorString(e));
+    }
+    gdr2::ChunkArgs a;
+    a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.b = b; a.w = w;
+    a.S0 = S0; a.o = o; a.ST = S_T; a.cu = cu_seqlens; a.order = order;
+    a.N = N; a.T = T; a.H = H; a.DV = dv;
+    a.la_bf16 = log_alpha_dtype == GDR2_BF16;
+    const hipError_t e = gdr2::launch_chunk(a, dk, dv, bf16, st);
+    if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "gdr2_chunk_fwd: launch: %s", hipGetErrorString(e));
+    return GDR2_OK;
   }
-  gdr2::ChunkArgs a;
-  a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.b = b; a.w = w;
-  a.S0 = S0; a.o = o; a.ST = S_T; a.cu = cu_seqlens; a.order = order;
-  a.N = N; a.T = T; a.H = H; a.DV = dv;
-  a.la_bf16 = log_alpha_dtype == GDR2_BF16;
-  const hipError_t e = gdr2::launch_chunk(a, dk, dv, bf16, st);
+
+  // 16-bit inputs: intra-chunk pass over all (chunk, head) items, then the state pass
+  const Layout l = two_pass_layout(B, T, H, dk, dv, ns);
+  int32_t* order = nullptr;
+  int32_t* cbase = nullptr;
+  int32_t* tab = nullptr;
+  if (cu_seqlens) {
+    cbase = reinterpret_cast<int32_t*>(ws + l.cbase);
+    tab = reinterpret_cast<int32_t*>(ws + l.tab);
+    if (gdr2::schedule_bytes(N)) {
+      order = reinterpret_cast<int32_t*>(ws + l.order);
+      const hipError_t e = gdr2::launch_schedule(cu_seqlens, N, T, order, st);
+      if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "gdr2_chunk_fwd: schedule launch: %s", hipGetErrorString(e));
+    }
+    const hipError_t e = gdr2::launch_chunk_table(cu_seqlens, N, T, (int)l.cap, cbase, tab, st);
+    if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "gdr2_chunk_fwd: chunk table launch: %s", hipGetErrorString(e));
+  }
+  gdr2::IntraArgs ia;
+  ia.q = q; ia.k = k; ia.v = v; ia.la = log_alpha; ia.b = b; ia.w = w;
+  ia.rec = ws + l.rec;
+  ia.tab = tab;
+  ia.total = cu_seqlens ? cbase + N : nullptr;
+  ia.nc = (T + 63) / 64;
+  ia.chunks = (int)l.cap;
+  ia.T = T; ia.H = H;
+  ia.la_bf16 = log_alpha_dtype == GDR2_BF16;
+  gdr2::StateArgs sa;
+  sa.rec = ws + l.rec;
+  sa.S0 = S0; sa.o = o; sa.ST = S_T; sa.cu = cu_seqlens; sa.order = order; sa.cbase = cbase;
+  sa.cap = (int)l.cap;
+  sa.N = N; sa.T = T; sa.H = H; sa.DV = dv;
+  const hipError_t e = gdr2::launch_two_pass(ia, sa, dk, dv, st);
   if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "gdr2_chunk_fwd: launch: %s", hipGetErrorString(e));
   return GDR2_OK;
 }

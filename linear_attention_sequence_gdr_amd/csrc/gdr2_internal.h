@@ -27,6 +27,61 @@ struct ChunkArgs {
   int la_bf16;
 };
 
+// ---- two-pass chunkwise forward (16-bit inputs) ------------------------------------
+//
+// The intra-chunk pass writes one record per (chunk, head); the state pass
+// reads them in chunk order.  Record r = chunk_index * H + head.  Every matrix
+// in a record is fp16 and stored as MFMA operand fragments: 64 lanes x 16 B
+// (8 halves) for the A/B operands of a 16x16x32 product, 64 lanes x 8 B (4
+// halves) for an accumulator-layout tile.  Lane l = 16*g + m.
+//   YN [a][kb]  (a < 4, kb < DK/32)  lane: -Y[16a+m][32kb+4g+j], -Y[16a+m][32kb+16+4g+j]  (j < 4)
+//   QG [a][kb]                       lane:  Qg[16a+m][...same columns...]
+//   KT [ib][p]  (ib < DK/16, p < 2)  lane:  Kt[32p+4g+j][16ib+m], Kt[32p+16+4g+j][16ib+m]
+//   AQK (a, p), p <= a/2 (6 tiles)   lane:  Aqk[16a+m][32p+4g+j], Aqk[16a+m][32p+16+4g+j]
+//   GC          fp32 [DK]                   gamma_C per key channel
+//   U  [jt][a]  (jt < DV/16)         lane:  U[16a+4g+q][16jt+m]  (q < 4, accumulator layout)
+// Everything before U is shared by all value channels; U is last so that a
+// block of value channels reads one contiguous range of it.
+template <int DK, int DV>
+struct Rec {
+  static constexpr int NKB = DK / 32, NIB = DK / 16, NJT = DV / 16;
+  static constexpr size_t FRAG = 1024, TILE = 512;
+  static constexpr size_t YN = 0;
+  static constexpr size_t QG = YN + 4 * NKB * FRAG;
+  static constexpr size_t KT = QG + 4 * NKB * FRAG;
+  static constexpr size_t AQK = KT + NIB * 2 * FRAG;
+  static constexpr size_t GC = AQK + 6 * FRAG;
+  static constexpr size_t U = GC + DK * 4;
+  static constexpr size_t BYTES = U + NJT * 4 * TILE;
+};
+size_t record_bytes(int dk, int dv);
+
+// Packed-sequence tables for the two-pass forward: cbase[n] = index of the
+// first chunk of sequence n (cbase[N] = total chunks), tab[2c], tab[2c+1] =
+// first token row and length of chunk c.
+struct IntraArgs {
+  const void *q, *k, *v, *la, *b, *w;
+  char* rec;
+  const int32_t* tab;     // packed sequences: per chunk (row, length); else nullptr
+  const int32_t* total;   // packed sequences: device total chunk count; else nullptr
+  int nc;                 // chunks per sequence (equal-length sequences)
+  int chunks;             // total chunks (equal-length) or an upper bound (packed)
+  int T, H;
+  int la_bf16;
+};
+struct StateArgs {
+  const char* rec;
+  const float* S0;
+  void* o;
+  float* ST;
+  const int32_t* cu;      // device [N+1] or nullptr
+  const int32_t* order;   // longest-first schedule or nullptr
+  const int32_t* cbase;   // packed sequences: first chunk per sequence; else nullptr
+  int cap;                // records available (chunks); chunks past it are skipped
+  int N, T, H, DV;
+};
+hipError_t launch_two_pass(const IntraArgs& ia, const StateArgs& sa, int dk, int dv, hipStream_t stream);
+
 hipError_t launch_decode(const DecodeArgs& a, int dk, int dv, bool bf16, hipStream_t stream);
 
 // Returns hipErrorInvalidValue when no kernel variant exists for the sizes.
@@ -37,5 +92,9 @@ bool chunk_supported(int dk, int dv, bool bf16);
 // into `order` (device int32 [N]) from cu_seqlens.  `scratch` holds N int32.
 hipError_t launch_schedule(const int32_t* cu, int N, int T, int32_t* order, hipStream_t stream);
 size_t schedule_bytes(int N);
+// cbase (int32 [N+1]) and tab (int32 [2 * chunks]) of packed sequences.
+hipError_t launch_chunk_table(const int32_t* cu, int N, int T, int cap, int32_t* cbase, int32_t* tab,
+                              hipStream_t stream);
+constexpr int SCHED_MAX = 4096;  // sequences the longest-first sort handles
 
 }  // namespace gdr2

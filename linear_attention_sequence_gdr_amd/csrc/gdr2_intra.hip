@@ -1,0 +1,452 @@
+// gdr2_intra.hip -- intra-chunk pass of the two-pass chunkwise forward of the
+// Gated Delta Rule-2 operator, 16-bit inputs (Gated DeltaNet-2 pages,
+// "Chunkwise Parallel Training via WY Representation", Step 1 decay
+// normalisation and Step 2 WY representation, Eqs. 20-22).
+//
+// Everything in a chunk that does not depend on the incoming state is
+// computed here, for all chunks of all sequences and heads at once: one
+// (chunk, head) item per workgroup iteration, in a persistent grid that
+// prefetches the next item's raw inputs into registers while it works on the
+// current one.  Per item, with G the fp32 cumulative log-decay from the chunk
+// start (log2 units) and m = row 31 of the chunk:
+//   L  G by a DPP scan; centred factors e1 = 2^(G - G_m), e2 = 2^(G_m - G) so
+//      that no factor exceeds the decay over half a chunk; E' = e1*b*k,
+//      K' = e2*k, Q' = e1*q (bf16, hi/lo for K' and Q'), the un-centred
+//      E = gamma*b*k, Q_g = gamma*q, K_tail = (gamma_C/gamma)*k and Z = w*v.
+//   P  T^T = K' E'^T and A_qk^T = K' Q'^T on MFMA (the centring cancels in
+//      every product).
+//   S  A = (I + T)^-1: fp32 forward substitution on the four 16x16 diagonal
+//      blocks, then the block recurrence for the off-diagonal blocks.
+//   Y  Y = A E and U = A Z on MFMA, written straight from the accumulators
+//      into the record together with Q_g, K_tail^T, A_qk and gamma_C (record
+//      layout in gdr2_internal.h).
+// The state pass (gdr2_state.hip) then needs only three small products per
+// chunk and value tile.
+#include <hip/hip_runtime.h>
+
+#include "gdr2_chunk_common.h"
+#include "gdr2_internal.h"
+
+namespace gdr2 {
+
+namespace {
+
+constexpr int NT = 512;  // threads per workgroup
+constexpr int NW = 8;    // wavefronts per workgroup
+
+template <int DK, int DV>
+struct IntraCfg {
+  typedef __bf16 KT;    // T / A_qk operands
+  typedef _Float16 ST;  // record and state-pass operands
+  static constexpr int PAD = 8;
+  static constexpr int LDK = DK + PAD;  // rows of [64][DK]
+  static constexpr int LDC = CH + PAD;  // rows of [*][64]
+  // region X, phase P set: E', K'hi, K'lo, Q'hi, Q'lo  [64][LDK] bf16
+  static constexpr size_t SZK = (size_t)CH * LDK * 2;
+  static constexpr size_t XP = 5 * SZK;
+  // region X after phase P: E^T, K_tail^T [DK][LDC]; Q_g [64][LDK]  (fp16)
+  static constexpr size_t O_EHT = 0;
+  static constexpr size_t O_KTT = O_EHT + (size_t)DK * LDC * 2;
+  static constexpr size_t O_QG = O_KTT + (size_t)DK * LDC * 2;
+  static constexpr size_t XR = O_QG + (size_t)CH * LDK * 2;
+  static constexpr size_t X = ((XP > XR ? XP : XR) + 15) / 16 * 16;
+  static constexpr size_t O_TD = X;                                // fp32 [4][16][16] diag T^T
+  static constexpr size_t O_TN = O_TD + 4 * 16 * 16 * 4;           // [64][LDC] -T
+  static constexpr size_t O_A = O_TN + (size_t)CH * LDC * 2;       // [64][LDC] A
+  static constexpr size_t O_AQK = O_A + (size_t)CH * LDC * 2;      // [64][LDC] A_qk
+  static constexpr size_t O_ZT = O_AQK + (size_t)CH * LDC * 2;     // [DV][LDC] Z^T
+  static constexpr size_t O_GC = O_ZT + (size_t)DV * LDC * 2;      // fp32 [DK] gamma_C
+  static constexpr size_t BYTES = O_GC + (size_t)DK * 4;
+  static_assert(BYTES <= 160 * 1024, "LDS budget exceeded");
+  // key-side mapping: thread = (column group cg of EPC channels, row group rg
+  // of RPT consecutive rows); the RG row groups of a column group are
+  // consecutive lanes of one wavefront
+  static constexpr int EPC = 4, CG = DK / EPC, RG = NT / CG, RPT = CH / RG;
+  static_assert(RG >= 16 && RG <= 64 && CH % RG == 0, "bad key-side mapping");
+  // value-side mapping: units of VE consecutive channels of one row
+  static constexpr int VPT = CH * DV / NT;          // elements per thread
+  static constexpr int VE = VPT < 8 ? VPT : 8;      // elements per unit (one load)
+  static constexpr int NVU = VPT / VE;              // units per thread
+  static constexpr int UPR = DV / VE;               // units per row
+  static_assert(VE == 4 || VE == 8, "bad value-side mapping");
+};
+
+}  // namespace
+
+template <int DK, int DV, bool LA16>
+__global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
+  typedef IntraCfg<DK, DV> Cfg;
+  typedef Rec<DK, DV> R;
+  typedef __bf16 KT;
+  typedef _Float16 ST;
+  typedef f16x4 SV4;
+  constexpr int LDK = Cfg::LDK, LDC = Cfg::LDC, EPC = Cfg::EPC;
+  constexpr int RPT = Cfg::RPT, RG = Cfg::RG, LW = LA16 ? 2 : 4;
+  constexpr int VE = Cfg::VE, NVU = Cfg::NVU, UPR = Cfg::UPR;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  KT* Ep = reinterpret_cast<KT*>(smem);
+  KT* Kh = reinterpret_cast<KT*>(smem + Cfg::SZK);
+  KT* Kl = reinterpret_cast<KT*>(smem + 2 * Cfg::SZK);
+  KT* Qh = reinterpret_cast<KT*>(smem + 3 * Cfg::SZK);
+  KT* Ql = reinterpret_cast<KT*>(smem + 4 * Cfg::SZK);
+  ST* EhT = reinterpret_cast<ST*>(smem + Cfg::O_EHT);
+  ST* KtT = reinterpret_cast<ST*>(smem + Cfg::O_KTT);
+  ST* Qg = reinterpret_cast<ST*>(smem + Cfg::O_QG);
+  float* Tdt = reinterpret_cast<float*>(smem + Cfg::O_TD);
+  ST* Tn = reinterpret_cast<ST*>(smem + Cfg::O_TN);
+  ST* Am = reinterpret_cast<ST*>(smem + Cfg::O_A);
+  ST* Aqk = reinterpret_cast<ST*>(smem + Cfg::O_AQK);
+  ST* ZT = reinterpret_cast<ST*>(smem + Cfg::O_ZT);
+  float* gC = reinterpret_cast<float*>(smem + Cfg::O_GC);
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int m = lane & 15, g4 = lane >> 4;
+  const int H = p.H;
+  const int items = (p.total ? *p.total : p.chunks) * H;
+  if ((int)blockIdx.x >= items) return;
+
+  // the strictly upper blocks of A and A_qk stay zero; the products run over them
+  for (int e = tid; e < CH * LDC; e += NT) {
+    Am[e] = (ST)0.f;
+    Aqk[e] = (ST)0.f;
+  }
+
+  // item -> first token row, valid rows, head
+  auto locate = [&](int it, long long& row0, int& clen, int& h) {
+    const int ci = it / H;
+    h = it - ci * H;
+    if (p.tab) {
+      row0 = p.tab[2 * ci];
+      clen = p.tab[2 * ci + 1];
+    } else {
+      const int n = ci / p.nc, c = ci - n * p.nc;
+      row0 = (long long)n * p.T + (long long)c * CH;
+      clen = min(CH, p.T - c * CH);
+    }
+  };
+
+  const int cg = tid / RG, rg = tid % RG, r0 = rg * RPT;
+  const size_t krow = (size_t)H * DK, vrow = (size_t)H * DV;
+  uint32_t koff[RPT], goff[RPT], voff[NVU];
+  int vr[NVU], vc0[NVU];
+#pragma unroll
+  for (int pr = 0; pr < RPT; ++pr) {
+    koff[pr] = (uint32_t)(((r0 + pr) * krow + EPC * cg) * 2);
+    goff[pr] = (uint32_t)(((r0 + pr) * krow + EPC * cg) * (LA16 ? 2 : 4));
+  }
+#pragma unroll
+  for (int i = 0; i < NVU; ++i) {
+    const int u = tid + NT * i;
+    vr[i] = u / UPR;
+    vc0[i] = VE * (u % UPR);
+    voff[i] = (uint32_t)((vr[i] * vrow + vc0[i]) * 2);
+  }
+
+  uint32_t rq[RPT][2], rk[RPT][2], rb[RPT][2], rgd[RPT][LW];
+  uint32_t rv[NVU][VE / 2], rw[NVU][VE / 2];
+  // Range-limited buffer loads: rows past the chunk's last valid token read
+  // as zero and nothing outside the caller's tensors is touched.
+  auto fetch = [&](long long row0, int clen, int h) {
+    const size_t kel = (size_t)row0 * krow + (size_t)h * DK, vel = (size_t)row0 * vrow + (size_t)h * DV;
+    const int kbytes = (int)(clen * krow * 2), gbytes = (int)(clen * krow * (LA16 ? 2 : 4));
+    const int vbytes = (int)(clen * vrow * 2);
+    const auto rsq = make_rsrc(static_cast<const char*>(p.q) + kel * 2, kbytes);
+    const auto rsk = make_rsrc(static_cast<const char*>(p.k) + kel * 2, kbytes);
+    const auto rsb = make_rsrc(static_cast<const char*>(p.b) + kel * 2, kbytes);
+    const auto rsg = make_rsrc(static_cast<const char*>(p.la) + kel * (LA16 ? 2 : 4), gbytes);
+    const auto rsv = make_rsrc(static_cast<const char*>(p.v) + vel * 2, vbytes);
+    const auto rsw = make_rsrc(static_cast<const char*>(p.w) + vel * 2, vbytes);
+#pragma unroll
+    for (int pr = 0; pr < RPT; ++pr) {
+      bld(rq[pr], rsq, koff[pr]);
+      bld(rk[pr], rsk, koff[pr]);
+      bld(rb[pr], rsb, koff[pr]);
+      bld(rgd[pr], rsg, goff[pr]);  // raw words: expanding bf16 here would wait for the load
+    }
+#pragma unroll
+    for (int i = 0; i < NVU; ++i) {
+      bld(rv[i], rsv, voff[i]);
+      bld(rw[i], rsw, voff[i]);
+    }
+  };
+
+  long long row0;
+  int clen, h;
+  locate(blockIdx.x, row0, clen, h);
+  fetch(row0, clen, h);
+  __syncthreads();
+
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int itn = it + gridDim.x;
+    long long nrow0 = 0;
+    int nclen = 0, nh = 0;
+    if (itn < items) locate(itn, nrow0, nclen, nh);
+
+    // ================= phase L: decay scan and operand tiles ====================
+    SV4 eh[RPT], qg[RPT], kt[RPT];
+    {
+      float G[RPT][EPC], kv[RPT][EPC], qv[RPT][EPC], bv[RPT][EPC];
+      float z[NVU][VE];
+#pragma unroll
+      for (int pr = 0; pr < RPT; ++pr) {
+        unpack4<false>(rq[pr], qv[pr]);
+        unpack4<false>(rk[pr], kv[pr]);
+        unpack4<false>(rb[pr], bv[pr]);
+        unpack4<!LA16>(rgd[pr], G[pr]);
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) G[pr][i] *= LOG2E;
+      }
+#pragma unroll
+      for (int i = 0; i < NVU; ++i)
+#pragma unroll
+        for (int j = 0; j < VE / 2; ++j) {
+          z[i][2 * j] = __uint_as_float(rv[i][j] << 16) * __uint_as_float(rw[i][j] << 16);
+          z[i][2 * j + 1] = __uint_as_float(rv[i][j] & 0xffff0000u) * __uint_as_float(rw[i][j] & 0xffff0000u);
+        }
+      // The raw registers are free: start the next item's loads.  The loads
+      // of this item are waited for explicitly first, so that the first use
+      // of their registers does not also wait for the new ones.
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+      if (itn < items) fetch(nrow0, nclen, nh);
+
+      // fp32 cumulative log2-decay: serial inside the thread, then a scan of
+      // the thread totals across the RG row groups of the column group
+#pragma unroll
+      for (int pr = 1; pr < RPT; ++pr)
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) G[pr][i] += G[pr - 1][i];
+      float egm[EPC], egcm[EPC];
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) {
+        const float tot = G[RPT - 1][i];
+        const float excl = seg_scan<RG>(tot) - tot;
+#pragma unroll
+        for (int pr = 0; pr < RPT; ++pr) G[pr][i] += excl;
+        const float gm = __shfl(G[(CH / 2 - 1) % RPT][i], (CH / 2 - 1) / RPT, RG);
+        const float gc = __shfl(G[RPT - 1][i], RG - 1, RG);
+        egm[i] = exp2_fast(gm);
+        egcm[i] = exp2_fast(gc - gm);
+        if (rg == 0) gC[EPC * cg + i] = exp2_fast(gc);
+#pragma unroll
+        for (int pr = 0; pr < RPT; ++pr) G[pr][i] -= gm;  // centred: G - G_m
+      }
+#pragma unroll
+      for (int pr = 0; pr < RPT; ++pr) {
+        const int r = r0 + pr;
+        float ep[EPC], kh[EPC], kl[EPC], qh[EPC], ql[EPC];
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) {
+          const float e1 = exp2_fast(G[pr][i]);
+          const float e2 = exp2_fast(-G[pr][i]);
+          ep[i] = e1 * (bv[pr][i] * kv[pr][i]);
+          const float kbv = e2 * kv[pr][i];
+          const float qp = e1 * qv[pr][i];
+          kh[i] = bf16_round(kbv);
+          kl[i] = kbv - kh[i];
+          qh[i] = bf16_round(qp);
+          ql[i] = qp - qh[i];
+          eh[pr][i] = (ST)(ep[i] * egm[i]);
+          qg[pr][i] = (ST)(qp * egm[i]);
+          kt[pr][i] = (ST)(kbv * egcm[i]);
+        }
+        st4<KT>(Ep + r * LDK + EPC * cg, ep);
+        st4<KT>(Kh + r * LDK + EPC * cg, kh);
+        st4<KT>(Kl + r * LDK + EPC * cg, kl);
+        st4<KT>(Qh + r * LDK + EPC * cg, qh);
+        st4<KT>(Ql + r * LDK + EPC * cg, ql);
+      }
+      // Z^T: each unit is VE channels of one row
+#pragma unroll
+      for (int i = 0; i < NVU; ++i)
+#pragma unroll
+        for (int j = 0; j < VE; ++j) ZT[(vc0[i] + j) * LDC + vr[i]] = (ST)z[i][j];
+    }
+    __syncthreads();
+
+    // ================= phase P: T^T and A_qk^T on MFMA ==========================
+    // tile t goes to wave t (tiles 8, 9 to waves 0, 2); one wave forms both T
+    // and A_qk of its tile so the K' operand is read once per K step
+    {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int ti = k == 0 ? wv : (wv == 0 ? 8 : wv == 2 ? 9 : -1);
+        if (ti < 0) break;
+        int a, b;
+        tri_tile(ti, a, b);
+        f32x4 acc = mma_lds<KT, DK>(zero4(), Kh + 16 * b * LDK, LDK, Qh + 16 * a * LDK, LDK);
+        acc = mma_lds<KT, DK>(acc, Kh + 16 * b * LDK, LDK, Ql + 16 * a * LDK, LDK);
+        acc = mma_lds<KT, DK>(acc, Kl + 16 * b * LDK, LDK, Qh + 16 * a * LDK, LDK);
+        const f32x4 acct = mma_lds<KT, DK>(zero4(), Kh + 16 * b * LDK, LDK, Ep + 16 * a * LDK, LDK);
+        // lanes hold A_qk[16a + m][16b + 4*g4 + q] and T[16a + m][16b + 4*g4 + q]
+        if (a == b) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[q] = (4 * g4 + q <= m) ? acc[q] : 0.f;
+          // diagonal blocks of T transposed, fp32: Tdt[a][s][r] = T[r][s], s < r
+#pragma unroll
+          for (int q = 0; q < 4; ++q) Tdt[(a * 16 + 4 * g4 + q) * 16 + m] = (4 * g4 + q < m) ? acct[q] : 0.f;
+        } else {
+          *reinterpret_cast<SV4*>(Tn + (16 * a + m) * LDC + 16 * b + 4 * g4) = neg_cvt4<SV4>(acct);
+        }
+        *reinterpret_cast<SV4*>(Aqk + (16 * a + m) * LDC + 16 * b + 4 * g4) = cvt4<SV4>(acc);
+      }
+    }
+    __syncthreads();
+
+    // ==== phase S(i): diagonal inverses; record operands into region X ===========
+    {
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) {
+        float col[RPT], col2[RPT];
+#pragma unroll
+        for (int pr = 0; pr < RPT; ++pr) {
+          col[pr] = (float)eh[pr][i];
+          col2[pr] = (float)kt[pr][i];
+        }
+        stn<ST, RPT>(EhT + (EPC * cg + i) * LDC + r0, col);
+        stn<ST, RPT>(KtT + (EPC * cg + i) * LDC + r0, col2);
+      }
+#pragma unroll
+      for (int pr = 0; pr < RPT; ++pr) *reinterpret_cast<SV4*>(Qg + (r0 + pr) * LDK + EPC * cg) = qg[pr];
+      if (wv < 4) {
+        // wave a inverts I + T_aa: lane 4*cc + part holds rows 4*part .. 4*part+3
+        // of column cc and runs a right-looking fp32 forward substitution over
+        // the columns s of T_aa; row s of column cc is broadcast in its quad
+        const int a = wv, cc = lane >> 2, part = lane & 3;
+        const float4* Tc = reinterpret_cast<const float4*>(Tdt + a * 256);
+        float xs[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xs[j] = (4 * part + j == cc) ? 1.f : 0.f;
+#pragma unroll
+        for (int s = 0; s < 15; ++s) {
+          const float4 col = Tc[s * 4 + part];
+          const float xv = quad_bcast(xs[s & 3], s >> 2);
+          // T[r][s] is zero for r <= s, so finished rows are left unchanged
+          xs[0] = fmaf(-col.x, xv, xs[0]);
+          xs[1] = fmaf(-col.y, xv, xs[1]);
+          xs[2] = fmaf(-col.z, xv, xs[2]);
+          xs[3] = fmaf(-col.w, xv, xs[3]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Am[(16 * a + 4 * part + j) * LDC + 16 * a + cc] = (ST)xs[j];
+      }
+    }
+    __syncthreads();
+
+    // ==== phase S(ii): off-diagonal blocks of A; record copies of Q_g, K_tail, A_qk ==
+    char* rec = p.rec + (size_t)it * R::BYTES;
+    if (wv == 3) wy_column<0, ST, SV4, LDC>(Tn, Am);
+    else if (wv == 2) wy_column<1, ST, SV4, LDC>(Tn, Am);
+    else if (wv == 1) wy_column<2, ST, SV4, LDC>(Tn, Am);
+    else {
+      // waves 0, 4..7: fragments whose sources are complete after phase S(i)
+      constexpr int NQG = 4 * R::NKB, NKT = 2 * R::NIB, NF = NQG + NKT + 6;
+      const int w5 = wv == 0 ? 0 : wv - 3;  // 0..4
+      for (int f = w5; f < NF; f += 5) {
+        const ST* src;
+        char* dst;
+        if (f < NQG) {
+          const int a = f / R::NKB, kb = f % R::NKB;
+          src = Qg + (16 * a + m) * LDK + 32 * kb + 4 * g4;
+          dst = rec + R::QG + (size_t)f * R::FRAG;
+        } else if (f < NQG + NKT) {
+          const int ff = f - NQG, ib = ff >> 1, pp = ff & 1;
+          src = KtT + (16 * ib + m) * LDC + 32 * pp + 4 * g4;
+          dst = rec + R::KT + (size_t)ff * R::FRAG;
+        } else {
+          const int ff = f - NQG - NKT;
+          const int a = ff < 2 ? ff : 2 + ((ff - 2) >> 1), pp = ff < 2 ? 0 : ((ff - 2) & 1);
+          src = Aqk + (16 * a + m) * LDC + 32 * pp + 4 * g4;
+          dst = rec + R::AQK + (size_t)ff * R::FRAG;
+        }
+        const SV4 lo = *reinterpret_cast<const SV4*>(src);
+        const SV4 hi = *reinterpret_cast<const SV4*>(src + 16);
+        *reinterpret_cast<f16x8*>(dst + lane * 16) =
+            f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      if (wv == 0 && lane < DK / 4)
+        *reinterpret_cast<float4*>(rec + R::GC + lane * 16) = *reinterpret_cast<const float4*>(gC + 4 * lane);
+    }
+    __syncthreads();
+
+    // ==== phase Y: -Y and U into the record ======================================
+    {
+      // -Y fragments (a, kb): wave -> kb = wv / 2 and row blocks {wv & 1, 3 - (wv & 1)}
+      const int kb = wv >> 1;
+      if (kb < R::NKB) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int a = s == 0 ? (wv & 1) : 3 - (wv & 1);
+          f32x4 y0, y1;
+          if (a < 2) {
+            y0 = mma_lds<ST, 32>(zero4(), EhT + 32 * kb * LDC, LDC, Am + 16 * a * LDC, LDC);
+            y1 = mma_lds<ST, 32>(zero4(), EhT + (32 * kb + 16) * LDC, LDC, Am + 16 * a * LDC, LDC);
+          } else {
+            y0 = mma_lds<ST, 64>(zero4(), EhT + 32 * kb * LDC, LDC, Am + 16 * a * LDC, LDC);
+            y1 = mma_lds<ST, 64>(zero4(), EhT + (32 * kb + 16) * LDC, LDC, Am + 16 * a * LDC, LDC);
+          }
+          // lane holds Y[16a + m][32kb + 4*g4 + q] (y0) and Y[16a + m][32kb + 16 + 4*g4 + q] (y1)
+          *reinterpret_cast<f16x8*>(rec + R::YN + ((size_t)(a * R::NKB + kb) * 64 + lane) * 16) =
+              f16x8{(ST)-y0[0], (ST)-y0[1], (ST)-y0[2], (ST)-y0[3],
+                    (ST)-y1[0], (ST)-y1[1], (ST)-y1[2], (ST)-y1[3]};
+        }
+      }
+      // U tiles (jt, a)
+      for (int t = wv; t < 4 * R::NJT; t += NW) {
+        const int a = t / R::NJT, jt = t % R::NJT;
+        f32x4 u;
+        if (a < 2) u = mma_lds<ST, 32>(zero4(), Am + 16 * a * LDC, LDC, ZT + 16 * jt * LDC, LDC);
+        else u = mma_lds<ST, 64>(zero4(), Am + 16 * a * LDC, LDC, ZT + 16 * jt * LDC, LDC);
+        // lane holds U[16a + 4*g4 + q][16jt + m]
+        *reinterpret_cast<SV4*>(rec + R::U + ((size_t)(jt * 4 + a) * 64 + lane) * 8) = cvt4<SV4>(u);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+size_t record_bytes(int dk, int dv) {
+#define GDR2_REC(DK, DV) \
+  if (dk == DK && dv == DV) return Rec<DK, DV>::BYTES;
+  GDR2_REC(32, 32) GDR2_REC(32, 64) GDR2_REC(32, 128)
+  GDR2_REC(64, 32) GDR2_REC(64, 64) GDR2_REC(64, 128)
+  GDR2_REC(128, 32) GDR2_REC(128, 64) GDR2_REC(128, 128)
+#undef GDR2_REC
+  return 0;
+}
+
+template <int DK, int DV, bool LA16>
+static hipError_t launch_intra1(const IntraArgs& a, hipStream_t stream) {
+  typedef IntraCfg<DK, DV> Cfg;
+  const long long items = (long long)a.chunks * a.H;
+  if (items <= 0) return hipSuccess;
+  static bool attr_set[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64 || !attr_set[dev]) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&intra_kernel<DK, DV, LA16>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::BYTES);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) attr_set[dev] = true;
+  }
+  int cus = 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const long long grid = items < cus ? items : cus;  // persistent: one workgroup per CU
+  hipLaunchKernelGGL((intra_kernel<DK, DV, LA16>), dim3((unsigned)grid), dim3(NT), Cfg::BYTES, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_intra(const IntraArgs& a, int dk, int dv, hipStream_t stream) {
+#define GDR2_INTRA(DK, DV)                                                                  \
+  if (dk == DK && dv == DV)                                                                 \
+    return a.la_bf16 ? launch_intra1<DK, DV, true>(a, stream) : launch_intra1<DK, DV, false>(a, stream);
+  GDR2_INTRA(32, 32) GDR2_INTRA(32, 64) GDR2_INTRA(32, 128)
+  GDR2_INTRA(64, 32) GDR2_INTRA(64, 64) GDR2_INTRA(64, 128)
+  GDR2_INTRA(128, 32) GDR2_INTRA(128, 64) GDR2_INTRA(128, 128)
+#undef GDR2_INTRA
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdr2

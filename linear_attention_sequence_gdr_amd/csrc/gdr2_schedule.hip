@@ -12,8 +12,6 @@
 
 namespace gdr2 {
 
-constexpr int SCHED_MAX = 4096;  // sequences sorted in one workgroup
-
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* cu, int N, int T,
                                                        int32_t* order) {
   __shared__ unsigned long long key[SCHED_MAX];
@@ -48,6 +46,62 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* cu, int N
     }
   }
   for (int i = threadIdx.x; i < N; i += blockDim.x) order[i] = (int32_t)(key[i] & 0xffffffffu);
+}
+
+// Chunk table of packed sequences for the two-pass forward: cbase[n] is the
+// index of sequence n's first 64-token chunk (an exclusive prefix sum of the
+// chunk counts, one block of 1024 sequences at a time with a running carry),
+// cbase[N] the number of chunks, clamped to the capacity `cap` of the table
+// and of the record buffer; tab[2c], tab[2c+1] are chunk c's first token row
+// and length.  Entries at or past `cap` are never written (only inputs that
+// break the cu_seqlens contract can reach them).
+__global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* cu, int N, int T, int cap,
+                                                          int32_t* cbase, int32_t* tab) {
+  __shared__ int part[1024];
+  __shared__ int carry_s;
+  const int t = threadIdx.x;
+  if (t == 0) carry_s = 0;
+  __syncthreads();
+  for (int base = 0; base < N; base += 1024) {
+    const int n = base + t;
+    int s = 0, len = 0;
+    if (n < N) {
+      s = cu[n];
+      int e = cu[n + 1];
+      s = s < 0 ? 0 : (s > T ? T : s);
+      e = e < s ? s : (e > T ? T : e);
+      len = e - s;
+    }
+    const int nc = (len + 63) / 64;
+    part[t] = nc;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+      const int v = t >= d ? part[t - d] : 0;
+      __syncthreads();
+      part[t] += v;
+      __syncthreads();
+    }
+    const long long carry = carry_s;
+    const long long first = carry + part[t] - nc;
+    if (n < N) {
+      cbase[n] = (int32_t)(first < cap ? first : cap);
+      for (int c = 0; c < nc && first + c < cap; ++c) {
+        tab[2 * (first + c)] = s + 64 * c;
+        tab[2 * (first + c) + 1] = min(64, len - 64 * c);
+      }
+    }
+    __syncthreads();
+    if (t == 1023) carry_s = (int)min(carry + part[1023], (long long)cap);
+    __syncthreads();
+  }
+  if (t == 0) cbase[N] = carry_s;
+}
+
+hipError_t launch_chunk_table(const int32_t* cu, int N, int T, int cap, int32_t* cbase, int32_t* tab,
+                              hipStream_t stream) {
+  if (N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, stream, cu, N, T, cap, cbase, tab);
+  return hipGetLastError();
 }
 
 size_t schedule_bytes(int N) { return N <= 1 || N > SCHED_MAX ? 0 : (size_t)N * sizeof(int32_t); }

@@ -83,10 +83,25 @@ def test_decode_rejects(kw, status):
 
 def test_workspace_query():
     q = G.gdr2_chunk_fwd_workspace_bytes
-    assert q(1, 100, 16, 128, 128, 0, G.GDR2_BF16) == 0
-    assert q(1, 100, 16, 128, 128, 1, G.GDR2_BF16) == 0
-    assert q(1, 100, 16, 128, 128, 64, G.GDR2_BF16) == 256
-    assert q(1, 100, 16, 128, 128, 100, G.GDR2_BF16) == 512
+    a256 = lambda x: (x + 255) // 256 * 256
+    # fp32 inputs: only the longest-first order of more than one packed sequence
+    assert q(1, 100, 16, 64, 64, 0, G.GDR2_F32) == 0
+    assert q(1, 100, 16, 64, 64, 1, G.GDR2_F32) == 0
+    assert q(1, 100, 16, 64, 64, 64, G.GDR2_F32) == 256
+    assert q(1, 100, 16, 64, 64, 100, G.GDR2_F32) == 512
+    # 16-bit inputs: one record per (chunk, head), plus the packed-sequence tables
+    # record of the intra-chunk pass (include/gdr2.h): fp16 fragments -Y and Q_g
+    # (4*dk/32 KiB each), K_tail (2*dk/16 KiB), A_qk (6 KiB), U (dv/16*4 tiles of
+    # 512 B) and fp32 gamma_C (4*dk B)
+    def rec_bytes(dk, dv):
+        return 2 * 4 * (dk // 32) * 1024 + 2 * (dk // 16) * 1024 + 6 * 1024 + (dv // 16) * 4 * 512 + 4 * dk
+    rec = rec_bytes(128, 128)
+    assert q(4, 4096, 16, 128, 128, 0, G.GDR2_BF16) == 4 * 64 * 16 * rec
+    assert q(1, 100, 16, 128, 128, 0, G.GDR2_BF16) == 2 * 16 * rec
+    cap = 2 + 64
+    assert q(1, 100, 16, 128, 128, 64, G.GDR2_BF16) == \
+        a256(64 * 4) + a256(65 * 4) + a256(cap * 8) + cap * 16 * rec
+    assert q(2, 64, 3, 32, 64, 0, G.GDR2_BF16) == 2 * 1 * 3 * rec_bytes(32, 64)
     assert q(1, 100, 16, 48, 128, 64, G.GDR2_BF16) == 0
     assert q(0, 100, 16, 128, 128, 64, G.GDR2_BF16) == 0
 
