@@ -31,10 +31,10 @@ namespace gdr2 {
 
 namespace {
 
-template <int DK, int DV, int NWV>
+template <int DK, int DV, int NWV, int NP>
 struct StateCfg {
   typedef Rec<DK, DV> R;
-  static constexpr int NTH = 64 * NWV;
+  static constexpr int NTH = 64 * (NWV + NP);
   static constexpr int DVB = 16 * NWV;                       // value channels per workgroup
   static constexpr size_t O_GC = R::GC;                      // shared part: record [0, R::U)
   static constexpr size_t O_U = R::U;                        // then this block's U tiles
@@ -59,10 +59,11 @@ __device__ __forceinline__ f16x8 join8(const f32x4& a, const f32x4& b) {
 
 }  // namespace
 
-// One workgroup per CU (LDS-bound), so each wavefront may use a whole SIMD's registers.
-template <int DK, int DV, int NWV>
-__global__ __launch_bounds__(64 * NWV, 1) void state_kernel(StateArgs p) {
-  typedef StateCfg<DK, DV, NWV> Cfg;
+// NWV compute wavefronts and NP producer wavefronts; one workgroup per CU
+// (LDS-bound), so each wavefront may use a whole SIMD's registers.
+template <int DK, int DV, int NWV, int NP>
+__global__ __launch_bounds__(64 * (NWV + NP), 1) void state_kernel(StateArgs p) {
+  typedef StateCfg<DK, DV, NWV, NP> Cfg;
   typedef Rec<DK, DV> R;
   constexpr int NKB = R::NKB, NIB = R::NIB, NCP = Cfg::NCP;
 
@@ -98,14 +99,16 @@ __global__ __launch_bounds__(64 * NWV, 1) void state_kernel(StateArgs p) {
   int nch = (len + CH - 1) / CH;
   if (cb + nch > p.cap) nch = max(0, p.cap - cb);  // only inputs that break the cu_seqlens contract
   const size_t nh = (size_t)n * H + h;
-  const int col0 = Cfg::DVB * jb + 16 * wv;  // this wavefront's first value channel
+  const bool producer = wv >= NWV;
+  const int col0 = Cfg::DVB * jb + 16 * (producer ? 0 : wv);  // this wavefront's first value channel
+  const size_t olane = ((size_t)m * H + h) * DV + col0 + 4 * g4;  // output element of row m of a chunk
 
   // ---- state: fp32 accumulators, tile ib holds S[16ib + 4*g4 + q][col0 + m] -------
   f32x4 S[NIB];
 #pragma unroll
   for (int ib = 0; ib < NIB; ++ib) {
     S[ib] = zero4();
-    if (p.S0) {
+    if (p.S0 && !producer) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) S[ib][q] = p.S0[(nh * DK + 16 * ib + 4 * g4 + q) * DV + col0 + m];
     }
@@ -119,12 +122,16 @@ __global__ __launch_bounds__(64 * NWV, 1) void state_kernel(StateArgs p) {
   constexpr int RUNS = (NCP + 63) / 64;
   constexpr int NSH = (int)(R::U / 16);  // shared pieces
   const size_t uoff = (size_t)jb * NWV * 4 * R::TILE;  // this block's U tiles inside the record's U
+  // The producer wavefronts copy chunk c's record into stage buffer `buf`; a
+  // wavefront issues its memory instructions in order, so keeping the copies
+  // off the compute wavefronts lets both proceed at once.
+  constexpr int KPW = (RUNS + NP - 1) / NP;  // runs per producer wavefront
   auto stage_async = [&](int c, int buf) {
     const char* rec = p.rec + ((size_t)(cb + c) * H + h) * R::BYTES;
     unsigned char* dst = smem + (size_t)buf * Cfg::STAGE;
 #pragma unroll
-    for (int k = 0; k < (RUNS + NWV - 1) / NWV; ++k) {
-      const int run = k * NWV + wv;  // uniform across the wavefront
+    for (int k = 0; k < KPW; ++k) {
+      const int run = k * NP + (wv - NWV);  // uniform across the wavefront
       const int xp = run * 64 + lane;
       const char* src = rec + (size_t)xp * 16 + (xp < NSH ? 0 : uoff);
       if (run < RUNS - 1 || (run == RUNS - 1 && (NCP % 64 == 0 || xp < NCP)))
@@ -132,27 +139,21 @@ __global__ __launch_bounds__(64 * NWV, 1) void state_kernel(StateArgs p) {
     }
   };
 
-  if (nch > 0) stage_async(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wavefront's pieces have landed
+  if (producer && nch > 0) {
+    stage_async(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wavefront's pieces have landed
+  }
   __syncthreads();
 
   for (int c = 0; c < nch; ++c) {
-    const unsigned char* L = smem + (size_t)(c & 1) * Cfg::STAGE;
-    // U and gamma_C are read before the next chunk's loads are issued: the
-    // compiler cannot tell that those loads target the other buffer and
-    // would otherwise wait for them before these reads
-    f32x4 Rt[4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const f16x4 u = *reinterpret_cast<const f16x4*>(L + Cfg::O_U + ((size_t)(wv * 4 + a) * 64 + lane) * 8);
-      Rt[a] = f32x4{(float)u[0], (float)u[1], (float)u[2], (float)u[3]};
+    if (producer) {
+      // the other buffer was last read in chunk c - 1, which every wavefront has left
+      if (c + 1 < nch) stage_async(c + 1, (c + 1) & 1);
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next chunk's pieces have landed
+      __syncthreads();
+      continue;
     }
-    float4 gcr[NIB];
-#pragma unroll
-    for (int ib = 0; ib < NIB; ++ib)
-      gcr[ib] = *reinterpret_cast<const float4*>(L + Cfg::O_GC + (size_t)(16 * ib + 4 * g4) * 4);
-    // the other buffer was last read in chunk c - 1, which every wavefront has left
-    if (c + 1 < nch) stage_async(c + 1, (c + 1) & 1);
+    const unsigned char* L = smem + (size_t)(c & 1) * Cfg::STAGE;
     const int clen = min(CH, len - c * CH);
 
     // 16-bit state operand: fragment kb = tiles 2kb, 2kb+1 (dk rows 32kb + ...)
@@ -160,39 +161,41 @@ __global__ __launch_bounds__(64 * NWV, 1) void state_kernel(StateArgs p) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) sf[kb] = join8(S[2 * kb], S[2 * kb + 1]);
 
-    // ---- R = U + (-Y) S: tile a holds R[16a + 4*g4 + q][col0 + m] ----
+    // ---- R = U + (-Y) S and the state part of O^T, S^T Q_g^T (independent
+    // of R), as eight interleaved accumulator chains.  Rt[a] holds
+    // R[16a + 4*g4 + q][col0 + m]; O[a] holds O[16a + m][col0 + 4*g4 + q]. ----
+    f32x4 Rt[4], O[4];
     {
-      f16x8 yf[4][NKB];
+      f16x8 yf[4][NKB], qf[4][NKB];
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb) {
           yf[a][kb] = *reinterpret_cast<const f16x8*>(L + R::YN + ((size_t)(a * NKB + kb) * 64 + lane) * 16);
+          qf[a][kb] = *reinterpret_cast<const f16x8*>(L + R::QG + ((size_t)(a * NKB + kb) * 64 + lane) * 16);
+        }
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f16x4 u = *reinterpret_cast<const f16x4*>(L + Cfg::O_U + ((size_t)(wv * 4 + a) * 64 + lane) * 8);
+        Rt[a] = f32x4{(float)u[0], (float)u[1], (float)u[2], (float)u[3]};
+        O[a] = zero4();
+      }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int a = 0; a < 4; ++a) Rt[a] = mma32(yf[a][kb], sf[kb], Rt[a]);
+        for (int a = 0; a < 4; ++a) {
+          Rt[a] = mma32(yf[a][kb], sf[kb], Rt[a]);
+          O[a] = mma32(sf[kb], qf[a][kb], O[a]);
+        }
     }
     const f16x8 rf[2] = {join8(Rt[0], Rt[1]), join8(Rt[2], Rt[3])};
 
-    // ---- O^T = S^T Q_g^T + R^T A_qk^T: tile a holds O[16a + m][col0 + 4*g4 + q] ----
+    // ---- O^T += R^T A_qk^T, then the output tile in bf16 ----
     {
-      f16x8 qf[4][NKB], af[6];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          qf[a][kb] = *reinterpret_cast<const f16x8*>(L + R::QG + ((size_t)(a * NKB + kb) * 64 + lane) * 16);
+      f16x8 af[6];
 #pragma unroll
       for (int f = 0; f < 6; ++f)
         af[f] = *reinterpret_cast<const f16x8*>(L + R::AQK + ((size_t)f * 64 + lane) * 16);
-      f32x4 O[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) O[a] = zero4();
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) O[a] = mma32(sf[kb], qf[a][kb], O[a]);
       // A_qk tile (a, p) exists for p <= a / 2; index a for a < 2, 2a - 2 + p above
       O[0] = mma32(rf[0], af[0], O[0]);
       O[1] = mma32(rf[0], af[1], O[1]);
@@ -200,15 +203,12 @@ __global__ __launch_bounds__(64 * NWV, 1) void state_kernel(StateArgs p) {
       O[3] = mma32(rf[0], af[4], O[3]);
       O[2] = mma32(rf[1], af[3], O[2]);
       O[3] = mma32(rf[1], af[5], O[3]);
+      __bf16* orow = static_cast<__bf16*>(p.o) + ((size_t)(tok0 + (long long)c * CH) * H) * DV + olane;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int r = 16 * a + m;
-        if (r < clen) {
-          const size_t oi = ((size_t)(tok0 + (long long)c * CH + r) * H + h) * DV + col0 + 4 * g4;
-          *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.o) + oi) =
+      for (int a = 0; a < 4; ++a)
+        if (16 * a + m < clen)
+          *reinterpret_cast<bf16x4*>(orow + (size_t)16 * a * H * DV) =
               bf16x4{(__bf16)O[a][0], (__bf16)O[a][1], (__bf16)O[a][2], (__bf16)O[a][3]};
-        }
-      }
     }
 
     // ---- S <- Diag(gamma_C) S + K_tail^T R ----
@@ -221,10 +221,11 @@ __global__ __launch_bounds__(64 * NWV, 1) void state_kernel(StateArgs p) {
           kf[ib][pp] = *reinterpret_cast<const f16x8*>(L + R::KT + ((size_t)(ib * 2 + pp) * 64 + lane) * 16);
 #pragma unroll
       for (int ib = 0; ib < NIB; ++ib) {
-        S[ib][0] *= gcr[ib].x;
-        S[ib][1] *= gcr[ib].y;
-        S[ib][2] *= gcr[ib].z;
-        S[ib][3] *= gcr[ib].w;
+        const float4 gc = *reinterpret_cast<const float4*>(L + Cfg::O_GC + (size_t)(16 * ib + 4 * g4) * 4);
+        S[ib][0] *= gc.x;
+        S[ib][1] *= gc.y;
+        S[ib][2] *= gc.z;
+        S[ib][3] *= gc.w;
       }
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp)
@@ -232,11 +233,10 @@ __global__ __launch_bounds__(64 * NWV, 1) void state_kernel(StateArgs p) {
         for (int ib = 0; ib < NIB; ++ib) S[ib] = mma32(kf[ib][pp], rf[pp], S[ib]);
     }
 
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next chunk's pieces have landed
     __syncthreads();
   }
 
-  if (p.ST) {
+  if (p.ST && !producer) {
 #pragma unroll
     for (int ib = 0; ib < NIB; ++ib)
 #pragma unroll
@@ -246,9 +246,9 @@ __global__ __launch_bounds__(64 * NWV, 1) void state_kernel(StateArgs p) {
 
 hipError_t launch_intra(const IntraArgs& a, int dk, int dv, hipStream_t stream);
 
-template <int DK, int DV, int NWV>
+template <int DK, int DV, int NWV, int NP>
 static hipError_t launch_state1(const StateArgs& a, hipStream_t stream) {
-  typedef StateCfg<DK, DV, NWV> Cfg;
+  typedef StateCfg<DK, DV, NWV, NP> Cfg;
   constexpr int NB = DV / Cfg::DVB;
   const long long pairs = (long long)a.N * a.H;
   const long long grid = (pairs + 7) / 8 * 8 * NB;
@@ -259,20 +259,20 @@ static hipError_t launch_state1(const StateArgs& a, hipStream_t stream) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64 || !attr_set[dev]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&state_kernel<DK, DV, NWV>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&state_kernel<DK, DV, NWV, NP>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::BYTES);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < 64) attr_set[dev] = true;
   }
-  hipLaunchKernelGGL((state_kernel<DK, DV, NWV>), dim3((unsigned)grid), dim3(64 * NWV), Cfg::BYTES,
+  hipLaunchKernelGGL((state_kernel<DK, DV, NWV, NP>), dim3((unsigned)grid), dim3(Cfg::NTH), Cfg::BYTES,
                      stream, a);
   return hipGetLastError();
 }
 
 template <int DK, int DV>
 static hipError_t launch_state_dv(const StateArgs& a, hipStream_t stream) {
-  // two wavefronts (32 value channels) per workgroup
-  return launch_state1<DK, DV, 2>(a, stream);
+  // two compute wavefronts (32 value channels) and four producers per workgroup
+  return launch_state1<DK, DV, 2, 4>(a, stream);
 }
 
 hipError_t launch_two_pass(const IntraArgs& ia, const StateArgs& sa, int dk, int dv, hipStream_t stream) {
