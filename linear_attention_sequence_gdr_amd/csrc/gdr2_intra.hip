@@ -54,8 +54,9 @@ struct IntraCfg {
   static constexpr size_t O_TN = O_TD + 4 * 16 * 16 * 4;           // [64][LDC] -T
   static constexpr size_t O_A = O_TN + (size_t)CH * LDC * 2;       // [64][LDC] A
   static constexpr size_t O_AQK = O_A + (size_t)CH * LDC * 2;      // [64][LDC] A_qk
-  static constexpr size_t O_ZT = O_AQK + (size_t)CH * LDC * 2;     // [DV][LDC] Z^T
-  static constexpr size_t O_GC = O_ZT + (size_t)DV * LDC * 2;      // fp32 [DK] gamma_C
+  static constexpr int LDZ = DV + PAD;                             // rows of Z
+  static constexpr size_t O_Z = O_AQK + (size_t)CH * LDC * 2;      // [64][LDZ] Z (row major)
+  static constexpr size_t O_GC = O_Z + (size_t)CH * LDZ * 2;       // fp32 [DK] gamma_C
   static constexpr size_t BYTES = O_GC + (size_t)DK * 4;
   static_assert(BYTES <= 160 * 1024, "LDS budget exceeded");
   // key-side mapping: thread = (column group cg of EPC channels, row group rg
@@ -70,6 +71,16 @@ struct IntraCfg {
   static constexpr int UPR = DV / VE;               // units per row
   static_assert(VE == 4 || VE == 8, "bad value-side mapping");
 };
+
+// Transposing LDS read of 16-bit data: within each 16-lane group, lane t
+// receives element t, t + 16, t + 32 and t + 48 of the 64 elements that the
+// group's lanes address (4 consecutive elements per lane, in lane order).
+__device__ __forceinline__ f16x4 lds_tr16(const _Float16* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(__attribute__((address_space(3))) void*)p);
+  return __builtin_bit_cast(f16x4, v);
+}
 
 }  // namespace
 
@@ -97,7 +108,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
   ST* Tn = reinterpret_cast<ST*>(smem + Cfg::O_TN);
   ST* Am = reinterpret_cast<ST*>(smem + Cfg::O_A);
   ST* Aqk = reinterpret_cast<ST*>(smem + Cfg::O_AQK);
-  ST* ZT = reinterpret_cast<ST*>(smem + Cfg::O_ZT);
+  ST* Zr = reinterpret_cast<ST*>(smem + Cfg::O_Z);
   float* gC = reinterpret_cast<float*>(smem + Cfg::O_GC);
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -147,34 +158,46 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
   uint32_t rv[NVU][VE / 2], rw[NVU][VE / 2];
   // Range-limited buffer loads: rows past the chunk's last valid token read
   // as zero and nothing outside the caller's tensors is touched.
-  auto fetch = [&](long long row0, int clen, int h) {
+  // batch 0: q, k; batch 1: b, log_alpha; batch 2: v, w.  Issuing a whole
+  // item at once stalls the issuing wavefronts until the CU's memory pipeline
+  // drains, so the batches go out in different phases of the current item.
+  auto fetch = [&](long long row0, int clen, int h, int batch) {
     const size_t kel = (size_t)row0 * krow + (size_t)h * DK, vel = (size_t)row0 * vrow + (size_t)h * DV;
     const int kbytes = (int)(clen * krow * 2), gbytes = (int)(clen * krow * (LA16 ? 2 : 4));
     const int vbytes = (int)(clen * vrow * 2);
-    const auto rsq = make_rsrc(static_cast<const char*>(p.q) + kel * 2, kbytes);
-    const auto rsk = make_rsrc(static_cast<const char*>(p.k) + kel * 2, kbytes);
-    const auto rsb = make_rsrc(static_cast<const char*>(p.b) + kel * 2, kbytes);
-    const auto rsg = make_rsrc(static_cast<const char*>(p.la) + kel * (LA16 ? 2 : 4), gbytes);
-    const auto rsv = make_rsrc(static_cast<const char*>(p.v) + vel * 2, vbytes);
-    const auto rsw = make_rsrc(static_cast<const char*>(p.w) + vel * 2, vbytes);
+    if (batch == 0) {
+      const auto rsq = make_rsrc(static_cast<const char*>(p.q) + kel * 2, kbytes);
+      const auto rsk = make_rsrc(static_cast<const char*>(p.k) + kel * 2, kbytes);
 #pragma unroll
-    for (int pr = 0; pr < RPT; ++pr) {
-      bld(rq[pr], rsq, koff[pr]);
-      bld(rk[pr], rsk, koff[pr]);
-      bld(rb[pr], rsb, koff[pr]);
-      bld(rgd[pr], rsg, goff[pr]);  // raw words: expanding bf16 here would wait for the load
-    }
+      for (int pr = 0; pr < RPT; ++pr) {
+        bld(rq[pr], rsq, koff[pr]);
+        bld(rk[pr], rsk, koff[pr]);
+      }
+    } else if (batch == 1) {
+      const auto rsb = make_rsrc(static_cast<const char*>(p.b) + kel * 2, kbytes);
+      const auto rsg = make_rsrc(static_cast<const char*>(p.la) + kel * (LA16 ? 2 : 4), gbytes);
 #pragma unroll
-    for (int i = 0; i < NVU; ++i) {
-      bld(rv[i], rsv, voff[i]);
-      bld(rw[i], rsw, voff[i]);
+      for (int pr = 0; pr < RPT; ++pr) {
+        bld(rb[pr], rsb, koff[pr]);
+        bld(rgd[pr], rsg, goff[pr]);  // raw words: expanding bf16 here would wait for the load
+      }
+    } else {
+      const auto rsv = make_rsrc(static_cast<const char*>(p.v) + vel * 2, vbytes);
+      const auto rsw = make_rsrc(static_cast<const char*>(p.w) + vel * 2, vbytes);
+#pragma unroll
+      for (int i = 0; i < NVU; ++i) {
+        bld(rv[i], rsv, voff[i]);
+        bld(rw[i], rsw, voff[i]);
+      }
     }
   };
 
   long long row0;
   int clen, h;
   locate(blockIdx.x, row0, clen, h);
-  fetch(row0, clen, h);
+  fetch(row0, clen, h, 0);
+  fetch(row0, clen, h, 1);
+  fetch(row0, clen, h, 2);
   __syncthreads();
 
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
@@ -204,11 +227,12 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
           z[i][2 * j] = __uint_as_float(rv[i][j] << 16) * __uint_as_float(rw[i][j] << 16);
           z[i][2 * j + 1] = __uint_as_float(rv[i][j] & 0xffff0000u) * __uint_as_float(rw[i][j] & 0xffff0000u);
         }
-      // The raw registers are free: start the next item's loads.  The loads
-      // of this item are waited for explicitly first, so that the first use
-      // of their registers does not also wait for the new ones.
+      // The raw registers are free: the next item's loads go out in three
+      // batches from here on.  The loads of this item are waited for
+      // explicitly first, so that the first use of their registers does not
+      // also wait for the new ones.
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-      if (itn < items) fetch(nrow0, nclen, nh);
+      if (itn < items) fetch(nrow0, nclen, nh, 0);
 
       // fp32 cumulative log2-decay: serial inside the thread, then a scan of
       // the thread totals across the RG row groups of the column group
@@ -256,17 +280,19 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
         st4<KT>(Qh + r * LDK + EPC * cg, qh);
         st4<KT>(Ql + r * LDK + EPC * cg, ql);
       }
-      // Z^T: each unit is VE channels of one row
+      // Z row major: each unit is VE consecutive channels of one row
 #pragma unroll
-      for (int i = 0; i < NVU; ++i)
-#pragma unroll
-        for (int j = 0; j < VE; ++j) ZT[(vc0[i] + j) * LDC + vr[i]] = (ST)z[i][j];
+      for (int i = 0; i < NVU; ++i) {
+        if constexpr (VE == 8) st8<ST>(Zr + vr[i] * Cfg::LDZ + vc0[i], z[i]);
+        else st4<ST>(Zr + vr[i] * Cfg::LDZ + vc0[i], z[i]);
+      }
     }
     __syncthreads();
 
     // ================= phase P: T^T and A_qk^T on MFMA ==========================
     // tile t goes to wave t (tiles 8, 9 to waves 0, 2); one wave forms both T
     // and A_qk of its tile so the K' operand is read once per K step
+    if (itn < items) fetch(nrow0, nclen, nh, 1);
     {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
@@ -294,6 +320,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
     __syncthreads();
 
     // ==== phase S(i): diagonal inverses; record operands into region X ===========
+    if (itn < items) fetch(nrow0, nclen, nh, 2);
     {
 #pragma unroll
       for (int i = 0; i < EPC; ++i) {
@@ -391,12 +418,26 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
                     (ST)-y1[0], (ST)-y1[1], (ST)-y1[2], (ST)-y1[3]};
         }
       }
-      // U tiles (jt, a)
+      // U tiles (jt, a): U = A Z over tokens.  K position 8*g4 + j of a 32-token
+      // step p is token 32p + 4*g4 + j (j < 4) or 32p + 16 + 4*g4 + j - 4; the
+      // A operand reads those columns of row 16a + m of A, and the Z operand
+      // comes from row-major Z through the LDS transpose read (lane s of a
+      // 16-lane group points at 4 channels of one token row; lane m then holds
+      // channel m of 4 consecutive token rows)
       for (int t = wv; t < 4 * R::NJT; t += NW) {
         const int a = t / R::NJT, jt = t % R::NJT;
-        f32x4 u;
-        if (a < 2) u = mma_lds<ST, 32>(zero4(), Am + 16 * a * LDC, LDC, ZT + 16 * jt * LDC, LDC);
-        else u = mma_lds<ST, 64>(zero4(), Am + 16 * a * LDC, LDC, ZT + 16 * jt * LDC, LDC);
+        f32x4 u = zero4();
+        const int s = m;  // source lane inside the 16-lane group
+        for (int pp = 0; pp <= (a >> 1); ++pp) {
+          const ST* arow = Am + (16 * a + m) * LDC + 32 * pp + 4 * g4;
+          const f16x4 a0 = *reinterpret_cast<const f16x4*>(arow);
+          const f16x4 a1 = *reinterpret_cast<const f16x4*>(arow + 16);
+          const ST* z0 = Zr + (32 * pp + 4 * g4 + (s >> 2)) * Cfg::LDZ + 16 * jt + 4 * (s & 3);
+          const f16x4 b0 = lds_tr16(z0);
+          const f16x4 b1 = lds_tr16(z0 + 16 * Cfg::LDZ);
+          u = mma32(f16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]},
+                    f16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]}, u);
+        }
         // lane holds U[16a + 4*g4 + q][16jt + m]
         *reinterpret_cast<SV4*>(rec + R::U + ((size_t)(jt * 4 + a) * 64 + lane) * 8) = cvt4<SV4>(u);
       }
