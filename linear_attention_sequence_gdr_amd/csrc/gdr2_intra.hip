@@ -158,46 +158,35 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
   uint32_t rv[NVU][VE / 2], rw[NVU][VE / 2];
   // Range-limited buffer loads: rows past the chunk's last valid token read
   // as zero and nothing outside the caller's tensors is touched.
-  // batch 0: q, k; batch 1: b, log_alpha; batch 2: v, w.  Issuing a whole
-  // item at once stalls the issuing wavefronts until the CU's memory pipeline
-  // drains, so the batches go out in different phases of the current item.
+  // One input tensor per batch (q, k, b, log_alpha, v, w).  A CU keeps only
+  // a limited amount of memory traffic in flight, and issuing a whole item at
+  // once stalls the issuing wavefronts until it drains, so the batches go out
+  // at six points of the current item (two in phase L, then one at the start
+  // of each later phase).
   auto fetch = [&](long long row0, int clen, int h, int batch) {
     const size_t kel = (size_t)row0 * krow + (size_t)h * DK, vel = (size_t)row0 * vrow + (size_t)h * DV;
     const int kbytes = (int)(clen * krow * 2), gbytes = (int)(clen * krow * (LA16 ? 2 : 4));
     const int vbytes = (int)(clen * vrow * 2);
-    if (batch == 0) {
-      const auto rsq = make_rsrc(static_cast<const char*>(p.q) + kel * 2, kbytes);
-      const auto rsk = make_rsrc(static_cast<const char*>(p.k) + kel * 2, kbytes);
+    if (batch <= 2) {
+      const void* src = batch == 0 ? p.q : batch == 1 ? p.k : p.b;
+      const auto rs = make_rsrc(static_cast<const char*>(src) + kel * 2, kbytes);
 #pragma unroll
-      for (int pr = 0; pr < RPT; ++pr) {
-        bld(rq[pr], rsq, koff[pr]);
-        bld(rk[pr], rsk, koff[pr]);
-      }
-    } else if (batch == 1) {
-      const auto rsb = make_rsrc(static_cast<const char*>(p.b) + kel * 2, kbytes);
+      for (int pr = 0; pr < RPT; ++pr) bld(batch == 0 ? rq[pr] : batch == 1 ? rk[pr] : rb[pr], rs, koff[pr]);
+    } else if (batch == 3) {
       const auto rsg = make_rsrc(static_cast<const char*>(p.la) + kel * (LA16 ? 2 : 4), gbytes);
 #pragma unroll
-      for (int pr = 0; pr < RPT; ++pr) {
-        bld(rb[pr], rsb, koff[pr]);
-        bld(rgd[pr], rsg, goff[pr]);  // raw words: expanding bf16 here would wait for the load
-      }
+      for (int pr = 0; pr < RPT; ++pr) bld(rgd[pr], rsg, goff[pr]);  // raw words: expanding bf16 here would wait
     } else {
-      const auto rsv = make_rsrc(static_cast<const char*>(p.v) + vel * 2, vbytes);
-      const auto rsw = make_rsrc(static_cast<const char*>(p.w) + vel * 2, vbytes);
+      const auto rs = make_rsrc(static_cast<const char*>(batch == 4 ? p.v : p.w) + vel * 2, vbytes);
 #pragma unroll
-      for (int i = 0; i < NVU; ++i) {
-        bld(rv[i], rsv, voff[i]);
-        bld(rw[i], rsw, voff[i]);
-      }
+      for (int i = 0; i < NVU; ++i) bld(batch == 4 ? rv[i] : rw[i], rs, voff[i]);
     }
   };
 
   long long row0;
   int clen, h;
   locate(blockIdx.x, row0, clen, h);
-  fetch(row0, clen, h, 0);
-  fetch(row0, clen, h, 1);
-  fetch(row0, clen, h, 2);
+  for (int b = 0; b < 6; ++b) fetch(row0, clen, h, b);
   __syncthreads();
 
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
@@ -227,7 +216,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
           z[i][2 * j] = __uint_as_float(rv[i][j] << 16) * __uint_as_float(rw[i][j] << 16);
           z[i][2 * j + 1] = __uint_as_float(rv[i][j] & 0xffff0000u) * __uint_as_float(rw[i][j] & 0xffff0000u);
         }
-      // The raw registers are free: the next item's loads go out in three
+      // The raw registers are free: the next item's loads go out in six
       // batches from here on.  The loads of this item are waited for
       // explicitly first, so that the first use of their registers does not
       // also wait for the new ones.
@@ -280,6 +269,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
         st4<KT>(Qh + r * LDK + EPC * cg, qh);
         st4<KT>(Ql + r * LDK + EPC * cg, ql);
       }
+      if (itn < items) fetch(nrow0, nclen, nh, 1);
       // Z row major: each unit is VE consecutive channels of one row
 #pragma unroll
       for (int i = 0; i < NVU; ++i) {
@@ -292,7 +282,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
     // ================= phase P: T^T and A_qk^T on MFMA ==========================
     // tile t goes to wave t (tiles 8, 9 to waves 0, 2); one wave forms both T
     // and A_qk of its tile so the K' operand is read once per K step
-    if (itn < items) fetch(nrow0, nclen, nh, 1);
+    if (itn < items) fetch(nrow0, nclen, nh, 2);
     {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
@@ -320,7 +310,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
     __syncthreads();
 
     // ==== phase S(i): diagonal inverses; record operands into region X ===========
-    if (itn < items) fetch(nrow0, nclen, nh, 2);
+    if (itn < items) fetch(nrow0, nclen, nh, 3);
     {
 #pragma unroll
       for (int i = 0; i < EPC; ++i) {
@@ -362,6 +352,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
 
     // ==== phase S(ii): off-diagonal blocks of A; record copies of Q_g, K_tail, A_qk ==
     char* rec = p.rec + (size_t)it * R::BYTES;
+    if (itn < items) fetch(nrow0, nclen, nh, 4);
     if (wv == 3) wy_column<0, ST, SV4, LDC>(Tn, Am);
     else if (wv == 2) wy_column<1, ST, SV4, LDC>(Tn, Am);
     else if (wv == 1) wy_column<2, ST, SV4, LDC>(Tn, Am);
@@ -397,6 +388,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
     __syncthreads();
 
     // ==== phase Y: -Y and U into the record ======================================
+    if (itn < items) fetch(nrow0, nclen, nh, 5);
     {
       // -Y fragments (a, kb): wave -> kb = wv / 2 and row blocks {wv & 1, 3 - (wv & 1)}
       const int kb = wv >> 1;
