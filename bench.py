@@ -55,10 +55,10 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_key):
-    """HBM bytes per launch of one kernel, from the rocprofv3 counter runs
-    committed under profiles/, only when they were taken on the current
-    kernel sources."""
+def load_traffic(*kernel_keys):
+    """HBM bytes per launch of one kernel (summed over several kernels that
+    one call launches), from the rocprofv3 counter runs committed under
+    profiles/, only when they were taken on the current kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -66,8 +66,13 @@ def load_traffic(kernel_key):
         return None
     if t.get("source_hash") != source_hash():
         return None
-    k = t.get("kernels", {}).get(kernel_key)
-    return None if k is None else k["fetch_bytes"] + k["write_bytes"]
+    total = 0.0
+    for key in kernel_keys:
+        k = t.get("kernels", {}).get(key)
+        if k is None:
+            return None
+        total += k["fetch_bytes"] + k["write_bytes"]
+    return total
 
 
 def _counter_rows(path):
@@ -207,7 +212,8 @@ def main():
     tokens = B * T
     gbs = byts / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
-    traffic = load_traffic("chunk_fwd_kernel")
+    # one gdr2_chunk_fwd call = the intra-chunk pass + the state pass
+    traffic = load_traffic("intra_kernel", "state_kernel")
 
     # ---- decode: 256 sequences x 16 heads, fp32 state ---------------------------------
     S = I.decode_state().to(dev)
@@ -260,7 +266,9 @@ def main():
         "fwd_alg_flops": flops,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": traffic},
+                     "traffic": traffic,
+                     "kernel": "gdr2_chunk_fwd call (intra_kernel + state_kernel), "
+                               "algorithmic 1792 B per head-token"},
         "decode": {"workload": "gdr2_decode_step N256 H16 dk=dv=128 fp32 state in place",
                    "steps": args.decode_steps, "us_per_step": dms * 1e3, "alg_bytes": dbytes,
                    "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS,

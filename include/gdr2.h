@@ -61,8 +61,18 @@ typedef enum {
 
 /*
  * Bytes of device workspace gdr2_chunk_fwd needs for these sizes (0 means the
- * workspace pointer may be NULL).  Returns 0 for arguments gdr2_chunk_fwd
- * would reject.
+ * workspace pointer may be NULL).  num_seqs is the value passed to
+ * gdr2_chunk_fwd: the number of packed sequences with cu_seqlens, 0 without.
+ * Returns 0 for arguments gdr2_chunk_fwd would reject.
+ *
+ * With in_dtype = GDR2_BF16 the forward runs in two passes and the workspace
+ * holds one record per (64-token chunk, head) of the intra-chunk results the
+ * state pass consumes: 2*4*(dk/32) KiB + 2*(dk/16) KiB + 6 KiB + (dv/16)*2 KiB
+ * + 4*dk bytes each (70.5 KiB at dk = dv = 128), for B*ceil(T/64) chunks, or
+ * ceil(T/64) + num_seqs chunks with packed sequences plus small tables.  With
+ * GDR2_F32 only packed calls with more than one sequence need workspace (their
+ * longest-first order).  The workspace is scratch: its contents on entry do
+ * not matter and are not meaningful on return.
  */
 size_t gdr2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs,
                                       gdr2_dtype in_dtype);
@@ -86,12 +96,18 @@ size_t gdr2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  *         A zero-length sequence gets S_T = S0.
  *   workspace : device scratch of at least gdr2_chunk_fwd_workspace_bytes().
  *
+ * Execution: with GDR2_BF16, an intra-chunk kernel handles every (chunk,
+ * head) in parallel (decay scan, chunk matrix, WY inverse and its products)
+ * and writes a record per chunk to the workspace; a state kernel then walks
+ * each sequence's chunks in order.  With GDR2_F32 one kernel walks the chunks
+ * and does both.
+ *
  * Precision: the cumulative log-decay, the WY solve's diagonal blocks, every
  * accumulation and the state are fp32.  With in_dtype = GDR2_F32 every
  * matrix product takes fp32 operands.  With GDR2_BF16 the products take
  * 16-bit operands: bf16 for the decay-normalised chunk matrix, a bf16 hi/lo
  * pair for the causal score matrix, and fp16 for the bounded state-pass
- * operands.  The per-channel log-decay summed over any 32 consecutive tokens
+ * operands (stored in that form in the workspace records).  The per-channel log-decay summed over any 32 consecutive tokens
  * of a chunk must stay above -80 (the decay normalisation is centred inside
  * each 64-token chunk); stronger decay gives undefined results.
  */

@@ -78,7 +78,7 @@ const char* gdr2_status_string(gdr2_status s) {
 
 const char* gdr2_last_error(void) { return g_err; }
 
-int gdr2_version(void) { return 100; }
+int gdr2_version(void) { return 200; }
 
 size_t gdr2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs,
                                       gdr2_dtype in_dtype) {
