@@ -17,9 +17,10 @@
 //      every product).
 //   S  A = (I + T)^-1: fp32 forward substitution on the four 16x16 diagonal
 //      blocks, then the block recurrence for the off-diagonal blocks.
-//   Y  Y = A E and U = A Z on MFMA, written straight from the accumulators
-//      into the record together with Q_g, K_tail^T, A_qk and gamma_C (record
-//      layout in gdr2_internal.h).
+//   Y  Y = A E and U = A Z on MFMA.
+// The record (layout in gdr2_internal.h) gets gamma_C in phase L, A_qk in
+// phase P straight from the accumulators, Q_g and K_tail through LDS in phase
+// S, and -Y and U from the accumulators in phase Y.
 // The state pass (gdr2_state.hip) then needs only three small products per
 // chunk and value tile.
 #include <hip/hip_runtime.h>
@@ -53,11 +54,9 @@ struct IntraCfg {
   static constexpr size_t O_TD = X;                                // fp32 [4][16][16] diag T^T
   static constexpr size_t O_TN = O_TD + 4 * 16 * 16 * 4;           // [64][LDC] -T
   static constexpr size_t O_A = O_TN + (size_t)CH * LDC * 2;       // [64][LDC] A
-  static constexpr size_t O_AQK = O_A + (size_t)CH * LDC * 2;      // [64][LDC] A_qk
   static constexpr int LDZ = DV + PAD;                             // rows of Z
-  static constexpr size_t O_Z = O_AQK + (size_t)CH * LDC * 2;      // [64][LDZ] Z (row major)
-  static constexpr size_t O_GC = O_Z + (size_t)CH * LDZ * 2;       // fp32 [DK] gamma_C
-  static constexpr size_t BYTES = O_GC + (size_t)DK * 4;
+  static constexpr size_t O_Z = O_A + (size_t)CH * LDC * 2;        // [64][LDZ] Z (row major)
+  static constexpr size_t BYTES = O_Z + (size_t)CH * LDZ * 2;
   static_assert(BYTES <= 160 * 1024, "LDS budget exceeded");
   // key-side mapping: thread = (column group cg of EPC channels, row group rg
   // of RPT consecutive rows); the RG row groups of a column group are
@@ -107,9 +106,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
   float* Tdt = reinterpret_cast<float*>(smem + Cfg::O_TD);
   ST* Tn = reinterpret_cast<ST*>(smem + Cfg::O_TN);
   ST* Am = reinterpret_cast<ST*>(smem + Cfg::O_A);
-  ST* Aqk = reinterpret_cast<ST*>(smem + Cfg::O_AQK);
   ST* Zr = reinterpret_cast<ST*>(smem + Cfg::O_Z);
-  float* gC = reinterpret_cast<float*>(smem + Cfg::O_GC);
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int m = lane & 15, g4 = lane >> 4;
@@ -117,11 +114,8 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
   const int items = (p.total ? *p.total : p.chunks) * H;
   if ((int)blockIdx.x >= items) return;
 
-  // the strictly upper blocks of A and A_qk stay zero; the products run over them
-  for (int e = tid; e < CH * LDC; e += NT) {
-    Am[e] = (ST)0.f;
-    Aqk[e] = (ST)0.f;
-  }
+  // the strictly upper blocks of A stay zero; the products run over them
+  for (int e = tid; e < CH * LDC; e += NT) Am[e] = (ST)0.f;
 
   // item -> first token row, valid rows, head
   auto locate = [&](int it, long long& row0, int& clen, int& h) {
@@ -194,6 +188,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
     long long nrow0 = 0;
     int nclen = 0, nh = 0;
     if (itn < items) locate(itn, nrow0, nclen, nh);
+    char* rec = p.rec + (size_t)it * R::BYTES;
 
     // ================= phase L: decay scan and operand tiles ====================
     SV4 eh[RPT], qg[RPT], kt[RPT];
@@ -240,7 +235,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
         const float gc = __shfl(G[RPT - 1][i], RG - 1, RG);
         egm[i] = exp2_fast(gm);
         egcm[i] = exp2_fast(gc - gm);
-        if (rg == 0) gC[EPC * cg + i] = exp2_fast(gc);
+        if (rg == 0) reinterpret_cast<float*>(rec + R::GC)[EPC * cg + i] = exp2_fast(gc);
 #pragma unroll
         for (int pr = 0; pr < RPT; ++pr) G[pr][i] -= gm;  // centred: G - G_m
       }
@@ -304,12 +299,19 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
         } else {
           *reinterpret_cast<SV4*>(Tn + (16 * a + m) * LDC + 16 * b + 4 * g4) = neg_cvt4<SV4>(acct);
         }
-        *reinterpret_cast<SV4*>(Aqk + (16 * a + m) * LDC + 16 * b + 4 * g4) = cvt4<SV4>(acc);
+        // A_qk fragment (a, p = b/2) half b&1, lane (m, g4); the upper halves of
+        // fragments (0, 0) and (2, 1) are zero
+        {
+          const int f = a < 2 ? a : 2 * a - 2 + (b >> 1);
+          char* dst = rec + R::AQK + ((size_t)f * 64 + lane) * 16;
+          *reinterpret_cast<SV4*>(dst + 8 * (b & 1)) = cvt4<SV4>(acc);
+          if (a == b && (a & 1) == 0) *reinterpret_cast<SV4*>(dst + 8) = SV4{(ST)0.f, (ST)0.f, (ST)0.f, (ST)0.f};
+        }
       }
     }
     __syncthreads();
 
-    // ==== phase S(i): diagonal inverses; record operands into region X ===========
+    // ==== phase S(i): diagonal inverses; E^T, K_tail^T, Q_g into region X ==========
     if (itn < items) fetch(nrow0, nclen, nh, 3);
     {
 #pragma unroll
@@ -350,15 +352,15 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
     }
     __syncthreads();
 
-    // ==== phase S(ii): off-diagonal blocks of A; record copies of Q_g, K_tail, A_qk ==
-    char* rec = p.rec + (size_t)it * R::BYTES;
+    // ==== phase S(ii): off-diagonal blocks of A ===================================
     if (itn < items) fetch(nrow0, nclen, nh, 4);
     if (wv == 3) wy_column<0, ST, SV4, LDC>(Tn, Am);
     else if (wv == 2) wy_column<1, ST, SV4, LDC>(Tn, Am);
     else if (wv == 1) wy_column<2, ST, SV4, LDC>(Tn, Am);
     else {
-      // waves 0, 4..7: fragments whose sources are complete after phase S(i)
-      constexpr int NQG = 4 * R::NKB, NKT = 2 * R::NIB, NF = NQG + NKT + 6;
+      // waves 0, 4..7 copy the Q_g and K_tail fragments, complete since phase
+      // S(i), while the others solve (16-byte pieces, 1 KiB per instruction)
+      constexpr int NQG = 4 * R::NKB, NF = NQG + 2 * R::NIB;
       const int w5 = wv == 0 ? 0 : wv - 3;  // 0..4
       for (int f = w5; f < NF; f += 5) {
         const ST* src;
@@ -367,23 +369,16 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
           const int a = f / R::NKB, kb = f % R::NKB;
           src = Qg + (16 * a + m) * LDK + 32 * kb + 4 * g4;
           dst = rec + R::QG + (size_t)f * R::FRAG;
-        } else if (f < NQG + NKT) {
+        } else {
           const int ff = f - NQG, ib = ff >> 1, pp = ff & 1;
           src = KtT + (16 * ib + m) * LDC + 32 * pp + 4 * g4;
           dst = rec + R::KT + (size_t)ff * R::FRAG;
-        } else {
-          const int ff = f - NQG - NKT;
-          const int a = ff < 2 ? ff : 2 + ((ff - 2) >> 1), pp = ff < 2 ? 0 : ((ff - 2) & 1);
-          src = Aqk + (16 * a + m) * LDC + 32 * pp + 4 * g4;
-          dst = rec + R::AQK + (size_t)ff * R::FRAG;
         }
         const SV4 lo = *reinterpret_cast<const SV4*>(src);
         const SV4 hi = *reinterpret_cast<const SV4*>(src + 16);
         *reinterpret_cast<f16x8*>(dst + lane * 16) =
             f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-      if (wv == 0 && lane < DK / 4)
-        *reinterpret_cast<float4*>(rec + R::GC + lane * 16) = *reinterpret_cast<const float4*>(gC + 4 * lane);
     }
     __syncthreads();
 
