@@ -117,13 +117,18 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
   // the strictly upper blocks of A stay zero; the products run over them
   for (int e = tid; e < CH * LDC; e += NT) Am[e] = (ST)0.f;
 
-  // item -> first token row, valid rows, head
+  // item -> first token row, valid rows, head.  The values are uniform across
+  // the workgroup; reading them through readfirstlane keeps them in scalar
+  // registers, so the buffer descriptors built from them need no per-lane loop.
   auto locate = [&](int it, long long& row0, int& clen, int& h) {
     const int ci = it / H;
     h = it - ci * H;
+    int r, l;
     if (p.tab) {
-      row0 = p.tab[2 * ci];
-      clen = p.tab[2 * ci + 1];
+      r = p.tab[2 * ci];
+      l = p.tab[2 * ci + 1];
+      row0 = __builtin_amdgcn_readfirstlane(r);
+      clen = __builtin_amdgcn_readfirstlane(l);
     } else {
       const int n = ci / p.nc, c = ci - n * p.nc;
       row0 = (long long)n * p.T + (long long)c * CH;
@@ -333,12 +338,16 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
         // the columns s of T_aa; row s of column cc is broadcast in its quad
         const int a = wv, cc = lane >> 2, part = lane & 3;
         const float4* Tc = reinterpret_cast<const float4*>(Tdt + a * 256);
+        // all 15 column pieces first, so the substitution chain waits on no LDS read
+        float4 tcol[15];
+#pragma unroll
+        for (int s = 0; s < 15; ++s) tcol[s] = Tc[s * 4 + part];
         float xs[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) xs[j] = (4 * part + j == cc) ? 1.f : 0.f;
 #pragma unroll
         for (int s = 0; s < 15; ++s) {
-          const float4 col = Tc[s * 4 + part];
+          const float4 col = tcol[s];
           const float xv = quad_bcast(xs[s & 3], s >> 2);
           // T[r][s] is zero for r <= s, so finished rows are left unchanged
           xs[0] = fmaf(-col.x, xv, xs[0]);
