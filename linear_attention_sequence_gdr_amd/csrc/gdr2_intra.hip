@@ -290,10 +290,24 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
         if (ti < 0) break;
         int a, b;
         tri_tile(ti, a, b);
-        f32x4 acc = mma_lds<KT, DK>(zero4(), Kh + 16 * b * LDK, LDK, Qh + 16 * a * LDK, LDK);
-        acc = mma_lds<KT, DK>(acc, Kh + 16 * b * LDK, LDK, Ql + 16 * a * LDK, LDK);
-        acc = mma_lds<KT, DK>(acc, Kl + 16 * b * LDK, LDK, Qh + 16 * a * LDK, LDK);
-        const f32x4 acct = mma_lds<KT, DK>(zero4(), Kh + 16 * b * LDK, LDK, Ep + 16 * a * LDK, LDK);
+        // each operand fragment is read from LDS once per K step and feeds the
+        // three hi/lo products of A_qk and the product of T
+        f32x4 acc = zero4(), acct = zero4();
+        {
+          const int ob = (16 * b + m) * LDK + 8 * g4, oa = (16 * a + m) * LDK + 8 * g4;
+#pragma unroll
+          for (int k0 = 0; k0 < DK; k0 += 32) {
+            const bf16x8 kh = *reinterpret_cast<const bf16x8*>(Kh + ob + k0);
+            const bf16x8 kl = *reinterpret_cast<const bf16x8*>(Kl + ob + k0);
+            const bf16x8 qh = *reinterpret_cast<const bf16x8*>(Qh + oa + k0);
+            const bf16x8 ql = *reinterpret_cast<const bf16x8*>(Ql + oa + k0);
+            const bf16x8 ep = *reinterpret_cast<const bf16x8*>(Ep + oa + k0);
+            acc = mma32(kh, qh, acc);
+            acct = mma32(kh, ep, acct);
+            acc = mma32(kh, ql, acc);
+            acc = mma32(kl, qh, acc);
+          }
+        }
         // lanes hold A_qk[16a + m][16b + 4*g4 + q] and T[16a + m][16b + 4*g4 + q]
         if (a == b) {
 #pragma unroll
