@@ -271,7 +271,14 @@ static hipError_t launch_state1(const StateArgs& a, hipStream_t stream) {
 
 template <int DK, int DV>
 static hipError_t launch_state_dv(const StateArgs& a, hipStream_t stream) {
-  // two compute wavefronts (32 value channels) and four producers per workgroup
+  // Two compute wavefronts (32 value channels) and four producers per
+  // workgroup; with too few (sequence, head) chains to cover the CUs that
+  // way, blocks of 16 channels double the number of workgroups.
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if ((long long)a.N * a.H * (DV / 32) < cus) return launch_state1<DK, DV, 1, 4>(a, stream);
   return launch_state1<DK, DV, 2, 4>(a, stream);
 }
 

@@ -38,7 +38,7 @@ def run_fwd(wl, **kw):
     o, ST = G().gdr2_chunk_fwd(dev(wl.q), dev(wl.k), dev(wl.v), dev(wl.log_alpha), dev(wl.b),
                                dev(wl.w), dev(wl.S0), dev(wl.cu_seqlens), **kw)
     torch.cuda.synchronize()
-    return o.cpu(), ST.cpu()
+    return o.cpu(), None if ST is None else ST.cpu()
 
 
 def oracle_fwd(wl, mask=None):
@@ -108,6 +108,30 @@ def test_bf16_varlen_edges():
     check(o, ST, ro, rS, True, "varlen edges")
     # zero-length sequence: S_T = S0 exactly
     assert torch.equal(ST[4], wl.S0[4])
+
+
+def test_bf16_many_packed_sequences():
+    """More sequences than the longest-first sort handles (4096): the state pass
+    runs them in index order and the chunk table's prefix sum carries across
+    several blocks of 1024 sequences."""
+    gen = np.random.default_rng(20)
+    lens = [int(x) for x in gen.choice([0, 1, 2, 3, 65], size=4200, p=[0.1, 0.3, 0.3, 0.25, 0.05])]
+    wl = I.make_forward(1, sum(lens), 2, 32, 32, dtype=torch.bfloat16, decay_shift=-2.0,
+                        s0_std=0.1, seqlens=lens, seed=19)
+    o, ST = run_fwd(wl)
+    ro, rS = oracle_fwd(wl)
+    check(o, ST, ro, rS, True, "4200 packed sequences")
+    zero = [n for n, L in enumerate(lens) if L == 0]
+    assert torch.equal(ST[zero], wl.S0[zero])
+
+
+def test_bf16_without_final_state():
+    wl = I.make_forward(2, 150, 3, 64, 128, dtype=torch.bfloat16, decay_shift=-2.0, s0_std=0.1,
+                        seed=22)
+    o, ST = run_fwd(wl, want_state=False)
+    assert ST is None
+    ro, rS = oracle_fwd(wl)
+    assert M.bf16_excess(o, ro) <= TOL_BF16
 
 
 def test_varlen_equals_separate_calls():
