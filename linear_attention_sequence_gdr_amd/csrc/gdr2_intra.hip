@@ -136,6 +136,17 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
     }
   };
 
+  // processing order -> record index.  With equal-length sequences the items
+  // go last chunk first, so the records the state pass reads first are the
+  // most recently written ones (still in the last-level cache when the state
+  // pass starts); packed sequences keep the record order.
+  auto order = [&](int it) -> int {
+    if (p.tab) return it;
+    const int pairs = p.chunks / p.nc * H, step = it / pairs, rem = it - step * pairs;
+    const int n = rem / H, hh = rem - n * H;
+    return ((n * p.nc) + (p.nc - 1 - step)) * H + hh;
+  };
+
   const int cg = tid / RG, rg = tid % RG, r0 = rg * RPT;
   const size_t krow = (size_t)H * DK, vrow = (size_t)H * DV;
   uint32_t koff[RPT], goff[RPT], voff[NVU];
@@ -184,7 +195,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
 
   long long row0;
   int clen, h;
-  locate(blockIdx.x, row0, clen, h);
+  locate(order(blockIdx.x), row0, clen, h);
   for (int b = 0; b < 6; ++b) fetch(row0, clen, h, b);
   __syncthreads();
 
@@ -192,8 +203,8 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
     const int itn = it + gridDim.x;
     long long nrow0 = 0;
     int nclen = 0, nh = 0;
-    if (itn < items) locate(itn, nrow0, nclen, nh);
-    char* rec = p.rec + (size_t)it * R::BYTES;
+    if (itn < items) locate(order(itn), nrow0, nclen, nh);
+    char* rec = p.rec + (size_t)order(it) * R::BYTES;
 
     // ================= phase L: decay scan and operand tiles ====================
     SV4 eh[RPT], qg[RPT], kt[RPT];
