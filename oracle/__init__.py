@@ -8,6 +8,8 @@ with the GPU library.
   (``gdr2_oracle.c``; Gated DeltaNet-2 pages, Steps 1-5 and Eq. 10).
 * :mod:`oracle.chunk_ref` -- the pages' chunkwise WY algorithm in fp64 numpy,
   used to pin the recurrence (the two must agree to rounding).
+* :mod:`oracle.epilogue` -- the block's output epilogue, RMSNorm then a SiLU
+  output gate, in fp64 numpy (pages, "Big-Picture Architecture" item 6).
 
 Inputs are the *stored* tensors (bf16 or fp32), converted exactly to fp64, so
 the comparison measures the kernel's arithmetic and not input quantisation.
