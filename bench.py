@@ -7,7 +7,10 @@ H=16, dk=dv=128, bf16 inputs, fp32 state, S0 = 0): inputs are resident in HBM
 before timing starts, W untimed steps run first, then exactly K steps are timed
 back to back with HIP events on the launch stream.  The same run also times D
 decode steps (256 sequences x 16 heads, fp32 state updated in place) and the
-fp64 oracle on a bounded sample of the forward workload on the host cores.
+fp64 oracle on a bounded sample of the forward workload on the host cores,
+and, outside the step, the block's output epilogue (gdr2_norm_gate over the
+forward's o) and the decode step with that epilogue fused
+(gdr2_decode_step_norm_gate).
 
 Prints one JSON line: tokens/s of the forward (whole job), its TFLOP/s and the
 HBM roofline of the forward kernel, the decode HBM GB/s with its own roofline,
@@ -229,7 +232,30 @@ def main():
     Nd, Hd, D = I.DECODE_N, I.DECODE_H, I.DECODE_D
     dbytes = Nd * Hd * (2 * D * D * 4 + 6 * D * 4 + D * 4)
     dgbs = dbytes / (dms * 1e-3) / 1e9
+
+    # the same decode step with the output epilogue fused into its store
+    zd = torch.randn((Nd, Hd, D), generator=torch.Generator("cpu").manual_seed(5)).to(dev)
+    nwd = torch.ones(D, dtype=torch.float32, device=dev)
+
+    def dec_gated():
+        x = pool[it[0] % len(pool)]
+        it[0] += 1
+        G.gdr2_decode_step_norm_gate(*x, S, zd, nwd, 1e-6, y=od)
+    gms = time_events(dec_gated, args.decode_steps, 5, torch)
+    gbytes = dbytes + Nd * Hd * D * 4 + D * 4
+    ggbs = gbytes / (gms * 1e-3) / 1e9
     del S, pool
+
+    # ---- output epilogue over the forward's o: RMSNorm per head + SiLU gate ----------
+    _, z_epi, w_epi = I.epilogue_inputs((B, T, H, dv), seed=6)
+    z_epi, w_epi = z_epi.to(dev), w_epi.to(dev)
+    y_epi = torch.empty_like(o)
+    fwd()
+    epi = lambda: G.gdr2_norm_gate(o, z_epi, w_epi, 1e-6, dv, y=y_epi)
+    ems = time_events(epi, args.steps, args.warmup, torch)
+    ebytes = 3 * o.numel() * o.element_size() + dv * 4
+    egbs = ebytes / (ems * 1e-3) / 1e9
+    del z_epi, y_epi
 
     if args.calibrate_copy:
         n = args.calibrate_copy * 1024 * 1024 // 4
@@ -273,7 +299,19 @@ def main():
                    "steps": args.decode_steps, "us_per_step": dms * 1e3, "alg_bytes": dbytes,
                    "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
-                                "traffic": load_traffic("decode_kernel")}},
+                                "traffic": load_traffic("decode_kernel")},
+                   "norm_gate_fused": {
+                       "entry": "gdr2_decode_step_norm_gate (RMSNorm over dv + SiLU gate in the store)",
+                       "us_per_step": gms * 1e3, "alg_bytes": gbytes,
+                       "roofline": {"bound": "hbm", "achieved": ggbs, "peak": HBM_PEAK_GBS,
+                                    "unit": "GB/s", "frac": ggbs / HBM_PEAK_GBS,
+                                    "traffic": load_traffic("decode_norm_gate_kernel")}}},
+        "epilogue": {"workload": "gdr2_norm_gate over the forward's o [B4 T4096 H16 128] bf16, "
+                                 "RMSNorm per head (group 128) x weight x silu(z), into y",
+                     "steps": args.steps, "us_per_call": ems * 1e3, "alg_bytes": ebytes,
+                     "roofline": {"bound": "hbm", "achieved": egbs, "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": egbs / HBM_PEAK_GBS,
+                                  "traffic": load_traffic("norm_gate_kernel")}},
         "cpu_baseline": cpu,
         "source_hash": source_hash(),
     }

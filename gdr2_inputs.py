@@ -179,3 +179,20 @@ def decode_step_inputs(step: int, N: int = DECODE_N, H: int = DECODE_H, dk: int 
     gen = torch.Generator("cpu").manual_seed(seed * 100003 + step + 1)
     q, k, v, la, b, w = draw_tokens(gen, N, 1, H, dk, dv, dtype, dtype, 0.0)
     return tuple(x[:, 0].contiguous() for x in (q, k, v, la, b, w))
+
+
+# ---- output epilogue ---------------------------------------------------------------
+
+def epilogue_inputs(shape, *, dtype=torch.bfloat16, seed: int = 1005, weight: bool = True):
+    """Inputs of the output epilogue (RMSNorm, then a SiLU output gate): o of
+    ``shape`` whose rows (last axis) carry scales spread over e^-1..e^1 around
+    N(0, 1) values, the gate pre-activation z ~ N(0, 1.5^2), and a per-channel
+    fp32 weight 1 + N(0, 0.1^2) over the last axis (None when ``weight`` is
+    False)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    f32 = torch.float32
+    o = torch.randn(*shape, generator=gen, dtype=f32)
+    o = o * torch.exp(torch.rand(*shape[:-1], 1, generator=gen, dtype=f32) * 2 - 1)
+    z = 1.5 * torch.randn(*shape, generator=gen, dtype=f32)
+    wt = 1 + 0.1 * torch.randn(shape[-1], generator=gen, dtype=f32) if weight else None
+    return o.to(dtype).contiguous(), z.to(dtype).contiguous(), wt

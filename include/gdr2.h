@@ -133,6 +133,57 @@ gdr2_status gdr2_decode_step(const void *q, const void *k, const void *v,
                              float *S, void *o, int N, int H, int dk, int dv,
                              gdr2_dtype in_dtype, gdr2_dtype log_alpha_dtype, void *stream);
 
+/*
+ * Output epilogue of the Gated DeltaNet-2 block (pages, "Big-Picture
+ * Architecture" item 6 and "Gated DeltaNet-2 token mixer block" item 5: the
+ * recurrent output is RMS-normalised, then gated channel by channel by a
+ * SiLU-activated output gate):
+ *
+ *     y = o / sqrt(mean(o^2) + eps) * weight * silu(z),   silu(z) = z * sigmoid(z)
+ *
+ * with the mean over each group of `group` consecutive channels of a row.
+ * Normalising each head on its own is o viewed as [B*T*H, dv] with group = dv
+ * (weight [dv], shared by the heads), or as [B*T, H*dv] with group = dv and a
+ * per-head weight [H*dv]; group = d normalises a whole row.
+ *
+ *   o, z, y : [rows, d] contiguous in dtype (z is the gate's pre-activation).
+ *             y may alias o or z exactly (each element is read before its
+ *             output is written); partial overlaps are undefined.
+ *   weight  : fp32 [d], or NULL for ones.
+ *   group   : a multiple of 8, at most GDR2_NORM_GATE_MAX_GROUP, dividing d.
+ *   eps     : finite, >= 0.  With eps = 0 an all-zero group gives NaN.
+ * rows = 0 is a no-op (the pointers may then be NULL).  Errors as for every entry point (GDR2_E_SHAPE for a
+ * bad group or eps).  Arithmetic is fp32; y is rounded once to dtype.
+ */
+#define GDR2_NORM_GATE_MAX_GROUP 8192
+gdr2_status gdr2_norm_gate(const void *o, const void *z, const float *weight, void *y,
+                           long long rows, int d, int group, float eps, gdr2_dtype dtype,
+                           void *stream);
+
+/*
+ * gdr2_decode_step with the output epilogue fused into its store: the same
+ * state update (S is updated in place exactly as gdr2_decode_step does), but
+ * instead of o it writes
+ *
+ *     y = o / sqrt(mean(o^2) + eps) * norm_weight * silu(z)
+ *
+ * per (sequence, head) over the dv channels (the block's output RMSNorm and
+ * SiLU gate, pages "Big-Picture Architecture" item 6).  The workgroup that
+ * owns a head already holds its whole output row, so the epilogue costs one
+ * read of z and no extra pass.
+ *
+ *   z : [N, H, dv] in in_dtype; y : [N, H, dv] in in_dtype.  y may alias z
+ *       exactly; it must not alias S or another input.
+ *   norm_weight : fp32 [dv] shared by all heads, or NULL for ones.
+ *   eps : finite, >= 0 (else GDR2_E_SHAPE).
+ */
+gdr2_status gdr2_decode_step_norm_gate(const void *q, const void *k, const void *v,
+                                       const void *log_alpha, const void *b, const void *w,
+                                       float *S, const void *z, const float *norm_weight,
+                                       float eps, void *y, int N, int H, int dk, int dv,
+                                       gdr2_dtype in_dtype, gdr2_dtype log_alpha_dtype,
+                                       void *stream);
+
 /* Static description of a status code. */
 const char *gdr2_status_string(gdr2_status s);
 

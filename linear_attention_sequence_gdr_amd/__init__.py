@@ -11,6 +11,10 @@ Functions carry the C names (include/gdr2.h):
   sequences, returns ``(o, S_T)``.
 * :func:`gdr2_decode_step` -- one token for N sequences, updates ``S`` in place,
   returns ``o``.
+* :func:`gdr2_norm_gate` -- the block's output epilogue (RMSNorm, then a SiLU
+  output gate) over o, returns ``y``.
+* :func:`gdr2_decode_step_norm_gate` -- a decode step whose store applies that
+  epilogue, returns ``y``.
 * :func:`gdr2_chunk_fwd_workspace_bytes`, :func:`gdr2_status_string`,
   :func:`gdr2_last_error`, :func:`gdr2_version`.
 """
@@ -22,7 +26,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["gdr2_chunk_fwd", "gdr2_decode_step", "gdr2_chunk_fwd_workspace_bytes",
+__all__ = ["gdr2_chunk_fwd", "gdr2_decode_step", "gdr2_norm_gate", "gdr2_decode_step_norm_gate",
+           "gdr2_chunk_fwd_workspace_bytes",
            "gdr2_status_string", "gdr2_last_error", "gdr2_version", "Gdr2Error",
            "LibraryMissing", "library", "library_path", "GDR2_F32", "GDR2_BF16", "EXPORTS"]
 
@@ -30,7 +35,9 @@ GDR2_F32, GDR2_BF16 = 0, 1
 STATUS = {0: "GDR2_OK", 1: "GDR2_E_NULL", 2: "GDR2_E_SHAPE", 3: "GDR2_E_DTYPE",
           4: "GDR2_E_ALIGN", 5: "GDR2_E_UNSUPPORTED", 6: "GDR2_E_WORKSPACE", 7: "GDR2_E_LAUNCH"}
 EXPORTS = ("gdr2_chunk_fwd_workspace_bytes", "gdr2_chunk_fwd", "gdr2_decode_step",
+           "gdr2_norm_gate", "gdr2_decode_step_norm_gate",
            "gdr2_status_string", "gdr2_last_error", "gdr2_version")
+NORM_GATE_MAX_GROUP = 8192
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libgdr2.so")
@@ -63,6 +70,11 @@ def library():
         lib.gdr2_chunk_fwd.restype = i32
         lib.gdr2_decode_step.argtypes = [vp] * 8 + [i32] * 6 + [vp]
         lib.gdr2_decode_step.restype = i32
+        f32, i64 = ctypes.c_float, ctypes.c_longlong
+        lib.gdr2_norm_gate.argtypes = [vp] * 4 + [i64, i32, i32, f32, i32, vp]
+        lib.gdr2_norm_gate.restype = i32
+        lib.gdr2_decode_step_norm_gate.argtypes = [vp] * 9 + [f32, vp] + [i32] * 6 + [vp]
+        lib.gdr2_decode_step_norm_gate.restype = i32
         lib.gdr2_status_string.argtypes = [i32]
         lib.gdr2_status_string.restype = ctypes.c_char_p
         lib.gdr2_last_error.argtypes = []
@@ -195,3 +207,65 @@ def gdr2_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alph
         N, H, dk, dv, _dtype_code(q), _dtype_code(log_alpha), _stream(stream, dev))
     _check(st)
     return o
+
+
+def gdr2_norm_gate(o: torch.Tensor, z: torch.Tensor, weight: Optional[torch.Tensor] = None,
+                   eps: float = 1e-6, group: Optional[int] = None, *,
+                   y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Output epilogue y = o / sqrt(mean(o^2) + eps) * weight * silu(z), the
+    mean taken over groups of ``group`` channels of the last axis (default: the
+    whole last axis).  o, z (and y): one shape, bf16 or fp32; weight: fp32
+    [o.shape[-1]] or None.  ``y`` may be ``o`` or ``z`` (in place)."""
+    lib = library()
+    dev = o.device
+    d = o.shape[-1]
+    group = d if group is None else int(group)
+    if z.shape != o.shape or z.dtype != o.dtype:
+        raise ValueError(f"z must match o ({tuple(o.shape)}, {o.dtype}), got {tuple(z.shape)}, {z.dtype}")
+    if y is None:
+        y = torch.empty_like(o)
+    if y.shape != o.shape or y.dtype != o.dtype:
+        raise ValueError("y must match o in shape and dtype")
+    if weight is not None and (weight.dtype != torch.float32 or tuple(weight.shape) != (d,)):
+        raise ValueError(f"weight must be fp32 [{d}]")
+    rows = o.numel() // d if d else 0
+    st = lib.gdr2_norm_gate(_ptr(o, "o", dev), _ptr(z, "z", dev), _ptr(weight, "weight", dev),
+                            _ptr(y, "y", dev), rows, d, group, float(eps), _dtype_code(o),
+                            _stream(stream, dev))
+    _check(st)
+    return y
+
+
+def gdr2_decode_step_norm_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                               log_alpha: torch.Tensor, b: torch.Tensor, w: torch.Tensor,
+                               S: torch.Tensor, z: torch.Tensor,
+                               norm_weight: Optional[torch.Tensor] = None, eps: float = 1e-6, *,
+                               y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decode step (S updated in place) whose output is the epilogue
+    RMSNorm(o) * norm_weight * silu(z) over each head's dv channels.  z: [N, H,
+    dv] in q's dtype; norm_weight: fp32 [dv] or None.  Returns y [N, H, dv]."""
+    lib = library()
+    dev = q.device
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if y is None:
+        y = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    for name, t, shp in (("k", k, (N, H, dk)), ("log_alpha", log_alpha, (N, H, dk)),
+                         ("b", b, (N, H, dk)), ("v", v, (N, H, dv)), ("w", w, (N, H, dv)),
+                         ("z", z, (N, H, dv)), ("y", y, (N, H, dv)), ("S", S, (N, H, dk, dv))):
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    for name, t in (("z", z), ("y", y)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {q.dtype}")
+    if S.dtype != torch.float32:
+        raise TypeError("S must be fp32")
+    if norm_weight is not None and (norm_weight.dtype != torch.float32 or tuple(norm_weight.shape) != (dv,)):
+        raise ValueError(f"norm_weight must be fp32 [{dv}]")
+    st = lib.gdr2_decode_step_norm_gate(
+        _ptr(q, "q", dev), _ptr(k, "k", dev), _ptr(v, "v", dev), _ptr(log_alpha, "log_alpha", dev),
+        _ptr(b, "b", dev), _ptr(w, "w", dev), _ptr(S, "S", dev), _ptr(z, "z", dev),
+        _ptr(norm_weight, "norm_weight", dev), float(eps), _ptr(y, "y", dev),
+        N, H, dk, dv, _dtype_code(q), _dtype_code(log_alpha), _stream(stream, dev))
+    _check(st)
+    return y

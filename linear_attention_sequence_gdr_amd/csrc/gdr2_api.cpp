@@ -5,6 +5,7 @@
 // kernels on the caller's stream and return without synchronising.
 #include <hip/hip_runtime.h>
 
+#include <math.h>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -78,7 +79,7 @@ const char* gdr2_status_string(gdr2_status s) {
 
 const char* gdr2_last_error(void) { return g_err; }
 
-int gdr2_version(void) { return 200; }
+int gdr2_version(void) { return 300; }
 
 size_t gdr2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs,
                                       gdr2_dtype in_dtype) {
@@ -189,32 +190,95 @@ gdr2_status gdr2_chunk_fwd(const void* q, const void* k, const void* v, const vo
   return GDR2_OK;
 }
 
-gdr2_status gdr2_decode_step(const void* q, const void* k, const void* v, const void* log_alpha,
-                             const void* b, const void* w, float* S, void* o, int N, int H, int dk,
-                             int dv, gdr2_dtype in_dtype, gdr2_dtype log_alpha_dtype, void* stream) {
-  if (!q || !k || !v || !log_alpha || !b || !w || !S || !o)
-    return fail(GDR2_E_NULL, "gdr2_decode_step: q, k, v, log_alpha, b, w, S and o must be non-NULL");
+namespace {
+
+gdr2_status decode_common(const char* fn, const void* q, const void* k, const void* v,
+                          const void* log_alpha, const void* b, const void* w, float* S, void* o,
+                          const void* z, const float* nw, float eps, bool gated, int N, int H,
+                          int dk, int dv, gdr2_dtype in_dtype, gdr2_dtype log_alpha_dtype,
+                          void* stream) {
+  const char* out = gated ? "y" : "o";
+  if (!q || !k || !v || !log_alpha || !b || !w || !S || !o || (gated && !z))
+    return fail(GDR2_E_NULL, "%s: q, k, v, log_alpha, b, w, S%s and %s must be non-NULL", fn,
+                gated ? ", z" : "", out);
   if (!dtype_ok(in_dtype) || !dtype_ok(log_alpha_dtype))
-    return fail(GDR2_E_DTYPE, "gdr2_decode_step: dtype codes %d/%d are not GDR2_F32 or GDR2_BF16",
+    return fail(GDR2_E_DTYPE, "%s: dtype codes %d/%d are not GDR2_F32 or GDR2_BF16", fn,
                 (int)in_dtype, (int)log_alpha_dtype);
   if (N < 0 || H <= 0 || dk <= 0 || dv <= 0)
-    return fail(GDR2_E_SHAPE, "gdr2_decode_step: need N >= 0, H >= 1, dk, dv >= 1 (got N=%d H=%d dk=%d dv=%d)",
-                N, H, dk, dv);
+    return fail(GDR2_E_SHAPE, "%s: need N >= 0, H >= 1, dk, dv >= 1 (got N=%d H=%d dk=%d dv=%d)",
+                fn, N, H, dk, dv);
   if (!dim_ok(dk) || !dim_ok(dv))
-    return fail(GDR2_E_UNSUPPORTED, "gdr2_decode_step: dk=%d dv=%d; each must be 32, 64 or 128", dk, dv);
+    return fail(GDR2_E_UNSUPPORTED, "%s: dk=%d dv=%d; each must be 32, 64 or 128", fn, dk, dv);
   if ((long long)N * H > 0x7fffffffLL)
-    return fail(GDR2_E_SHAPE, "gdr2_decode_step: N*H = %lld is too many", (long long)N * H);
-  const void* ptrs[] = {q, k, v, log_alpha, b, w, S, o};
-  const char* names[] = {"q", "k", "v", "log_alpha", "b", "w", "S", "o"};
-  for (int i = 0; i < 8; ++i)
-    if (!aligned16(ptrs[i]))
-      return fail(GDR2_E_ALIGN, "gdr2_decode_step: %s is not 16-byte aligned", names[i]);
+    return fail(GDR2_E_SHAPE, "%s: N*H = %lld is too many", fn, (long long)N * H);
+  if (gated && !(eps >= 0.f && isfinite(eps)))
+    return fail(GDR2_E_SHAPE, "%s: eps must be finite and >= 0 (got %g)", fn, (double)eps);
+  const void* ptrs[] = {q, k, v, log_alpha, b, w, S, o, z, nw};
+  const char* names[] = {"q", "k", "v", "log_alpha", "b", "w", "S", out, "z", "norm_weight"};
+  for (int i = 0; i < 10; ++i)
+    if (ptrs[i] && !aligned16(ptrs[i]))
+      return fail(GDR2_E_ALIGN, "%s: %s is not 16-byte aligned", fn, names[i]);
   gdr2::DecodeArgs a;
   a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.b = b; a.w = w;
   a.S = S; a.o = o; a.N = N; a.H = H;
   a.la_bf16 = log_alpha_dtype == GDR2_BF16;
+  a.z = gated ? z : nullptr;
+  a.nw = gated ? nw : nullptr;
+  a.eps = gated ? eps : 0.f;
+  a.gated = gated ? 1 : 0;
   const hipError_t e = gdr2::launch_decode(a, dk, dv, in_dtype == GDR2_BF16, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "gdr2_decode_step: launch: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "%s: launch: %s", fn, hipGetErrorString(e));
+  return GDR2_OK;
+}
+
+}  // namespace
+
+gdr2_status gdr2_decode_step(const void* q, const void* k, const void* v, const void* log_alpha,
+                             const void* b, const void* w, float* S, void* o, int N, int H, int dk,
+                             int dv, gdr2_dtype in_dtype, gdr2_dtype log_alpha_dtype, void* stream) {
+  return decode_common("gdr2_decode_step", q, k, v, log_alpha, b, w, S, o, nullptr, nullptr, 0.f,
+                       false, N, H, dk, dv, in_dtype, log_alpha_dtype, stream);
+}
+
+gdr2_status gdr2_decode_step_norm_gate(const void* q, const void* k, const void* v,
+                                       const void* log_alpha, const void* b, const void* w,
+                                       float* S, const void* z, const float* norm_weight, float eps,
+                                       void* y, int N, int H, int dk, int dv, gdr2_dtype in_dtype,
+                                       gdr2_dtype log_alpha_dtype, void* stream) {
+  return decode_common("gdr2_decode_step_norm_gate", q, k, v, log_alpha, b, w, S, y, z, norm_weight,
+                       eps, true, N, H, dk, dv, in_dtype, log_alpha_dtype, stream);
+}
+
+gdr2_status gdr2_norm_gate(const void* o, const void* z, const float* weight, void* y,
+                           long long rows, int d, int group, float eps, gdr2_dtype dtype,
+                           void* stream) {
+  const char* fn = "gdr2_norm_gate";
+  if (rows > 0 && (!o || !z || !y)) return fail(GDR2_E_NULL, "%s: o, z and y must be non-NULL", fn);
+  if (!dtype_ok(dtype)) return fail(GDR2_E_DTYPE, "%s: dtype code %d is not GDR2_F32 or GDR2_BF16", fn, (int)dtype);
+  if (rows < 0 || d <= 0 || group <= 0)
+    return fail(GDR2_E_SHAPE, "%s: need rows >= 0, d >= 1, group >= 1 (got rows=%lld d=%d group=%d)", fn,
+                rows, d, group);
+  if (group % 8 != 0 || group > GDR2_NORM_GATE_MAX_GROUP || d % group != 0)
+    return fail(GDR2_E_SHAPE, "%s: group=%d must be a multiple of 8, at most %d, and divide d=%d", fn,
+                group, GDR2_NORM_GATE_MAX_GROUP, d);
+  if (!(eps >= 0.f && isfinite(eps)))
+    return fail(GDR2_E_SHAPE, "%s: eps must be finite and >= 0 (got %g)", fn, (double)eps);
+  const long long period = d / group;
+  if (rows > (1LL << 62) / d || gdr2::norm_gate_blocks(rows * period, group) > 0x7fffffffLL)
+    return fail(GDR2_E_SHAPE, "%s: rows=%lld x d=%d is too large for one launch", fn, rows, d);
+  const void* ptrs[] = {o, z, y, weight};
+  const char* names[] = {"o", "z", "y", "weight"};
+  for (int i = 0; i < 4; ++i)
+    if (ptrs[i] && !aligned16(ptrs[i]))
+      return fail(GDR2_E_ALIGN, "%s: %s is not 16-byte aligned", fn, names[i]);
+  gdr2::NormGateArgs a{};
+  a.o = o; a.z = z; a.weight = weight; a.y = y;
+  a.groups = rows * period;
+  a.group = group;
+  a.period = (int)period;
+  a.eps = eps;
+  const hipError_t e = gdr2::launch_norm_gate(a, dtype == GDR2_BF16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "%s: launch: %s", fn, hipGetErrorString(e));
   return GDR2_OK;
 }
 

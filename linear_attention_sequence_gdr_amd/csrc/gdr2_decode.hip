@@ -11,6 +11,10 @@
 // reductions come from the same pass over S (Step 5 reads S_t = S_bar + k
 // delta^T, so S_t^T q = S_bar^T q + (k^T q) delta).
 //
+// With the output epilogue on, the stored row is RMSNorm(o) * weight * silu(z)
+// instead of o (the block's output normalisation and gate), at the cost of one
+// extra read of z.
+//
 // Each lane owns 4 adjacent columns (one 16-byte load per row) of P rows, the
 // rows of a wave are interleaved so that one wave-wide load covers whole
 // contiguous state rows.  HBM-bound: 2 * dk * dv * 4 bytes of state traffic per
@@ -22,8 +26,8 @@
 
 namespace gdr2 {
 
-template <int DK, int DV, bool BF16>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+template <int DK, int DV, bool BF16, bool GATED>
+__device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   constexpr int NT = 256, NW = 4;
   constexpr int LPR = DV / 4;            // lanes per state row
   constexpr int RPI = 64 / LPR;          // rows per wave-wide instruction
@@ -50,6 +54,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 
   const size_t xk = nh * DK, xv = nh * DV;
+  // the output gate's pre-activation and the norm weight, needed only by the
+  // lanes that store
+  float zz[4] = {0.f, 0.f, 0.f, 0.f}, wt[4] = {1.f, 1.f, 1.f, 1.f};
+  if (GATED && wv == 0 && rp == 0) {
+    load4<BF16>(a.z, xv + col, zz);
+    if (a.nw) load4<false>(a.nw, col, wt);
+  }
   for (int i = tid; i < DK; i += NT) {
     const float g = a.la_bf16 ? load1<true>(a.la, xk + i) : load1<false>(a.la, xk + i);
     const float al = __expf(g);
@@ -100,7 +111,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     delta[c] = s_z[col + c] - rr;
     pq[c] = pp + s_qk * delta[c];
   }
-  if (wv == 0 && rp == 0) store4<BF16>(a.o, xv + col, pq);
+  if constexpr (!GATED) {
+    if (wv == 0 && rp == 0) store4<BF16>(a.o, xv + col, pq);
+  }
 
 #pragma unroll
   for (int p = 0; p < P; ++p) {
@@ -113,13 +126,52 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     nv.w = fmaf(al, st[p].w, kk * delta[3]);
     *reinterpret_cast<float4*>(S + (size_t)row * DV + col) = nv;
   }
+
+  if constexpr (GATED) {
+    // Output epilogue (Gated DeltaNet-2 pages, "Big-Picture Architecture" item
+    // 6), after the state stores so that it overlaps their drain.  Every
+    // aligned run of LPR lanes holds the whole output row, 4 columns per lane,
+    // so the sum of squares is an xor reduction inside that run; wave 0 alone
+    // needs it.
+    if (wv == 0) {
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ss = fmaf(pq[c], pq[c], ss);
+#pragma unroll
+      for (int off = LPR / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+      const float rn = rsqrtf(fmaf(ss, 1.f / DV, a.eps));
+      if (rp == 0) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float sig = __builtin_amdgcn_rcpf(1.f + __expf(-zz[c]));
+          pq[c] = pq[c] * rn * wt[c] * (zz[c] * sig);
+        }
+        store4<BF16>(a.o, xv + col, pq);
+      }
+    }
+  }
+}
+
+template <int DK, int DV, bool BF16>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+  decode_body<DK, DV, BF16, false>(a);
+}
+
+template <int DK, int DV, bool BF16>
+__global__ __launch_bounds__(256) void decode_norm_gate_kernel(DecodeArgs a) {
+  decode_body<DK, DV, BF16, true>(a);
 }
 
 template <int DK, int DV>
 static hipError_t launch_decode_dv(const DecodeArgs& a, bool bf16, hipStream_t stream) {
   const dim3 grid((unsigned)((size_t)a.N * a.H)), block(256);
-  if (bf16) hipLaunchKernelGGL((decode_kernel<DK, DV, true>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((decode_kernel<DK, DV, false>), grid, block, 0, stream, a);
+  if (a.gated) {
+    if (bf16) hipLaunchKernelGGL((decode_norm_gate_kernel<DK, DV, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_norm_gate_kernel<DK, DV, false>), grid, block, 0, stream, a);
+  } else {
+    if (bf16) hipLaunchKernelGGL((decode_kernel<DK, DV, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_kernel<DK, DV, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -14,6 +14,26 @@ struct DecodeArgs {
   void* o;
   int N, H;
   int la_bf16;
+  // Output epilogue applied before o is stored (gated != 0): o becomes
+  // RMSNorm(o) over dv, times nw (fp32 [dv], or NULL for ones), times silu(z).
+  const void* z;
+  const float* nw;
+  float eps;
+  int gated;
+};
+
+// Output epilogue over `groups` groups of `group` channels (a multiple of 8).
+// `period` = channels per row / group: the weight (fp32, one entry per channel
+// of a row, or NULL) is indexed by (group index % period) * group + channel.
+struct NormGateArgs {
+  const void *o, *z;
+  const float* weight;
+  void* y;
+  long long groups;
+  int group, period;
+  float eps;
+  float inv_group;  // set by launch_norm_gate
+  int lanes;        // set by launch_norm_gate
 };
 
 struct ChunkArgs {
@@ -83,6 +103,12 @@ struct StateArgs {
 hipError_t launch_two_pass(const IntraArgs& ia, const StateArgs& sa, int dk, int dv, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs& a, int dk, int dv, bool bf16, hipStream_t stream);
+
+hipError_t launch_norm_gate(NormGateArgs a, bool bf16, hipStream_t stream);
+// Lanes per group and 256-thread blocks of the epilogue launch (host-side
+// bounds checks use them).
+int norm_gate_lanes(int group);
+long long norm_gate_blocks(long long groups, int group);
 
 // Returns hipErrorInvalidValue when no kernel variant exists for the sizes.
 hipError_t launch_chunk(const ChunkArgs& a, int dk, int dv, bool bf16, hipStream_t stream);

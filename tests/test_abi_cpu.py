@@ -120,3 +120,45 @@ def test_binding_has_no_fallback(monkeypatch):
     monkeypatch.setattr(G, "_lib", None)
     with pytest.raises(G.LibraryMissing):
         G.library()
+
+
+def ng(**kw):
+    args = dict(o=A, z=A, wt=None, y=A, rows=64, d=128, group=128, eps=1e-6, dt=G.GDR2_BF16,
+                stream=None)
+    args.update(kw)
+    return G.library().gdr2_norm_gate(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=None), 1), (dict(z=None), 1), (dict(y=None), 1), (dict(dt=4), 3),
+    (dict(rows=-1), 2), (dict(d=0), 2), (dict(group=0), 2), (dict(group=12, d=24), 2),
+    (dict(group=64, d=96), 2), (dict(group=16384, d=16384), 2), (dict(eps=-1.0), 2),
+    (dict(eps=float("inf")), 2), (dict(eps=float("nan")), 2), (dict(rows=1 << 60), 2),
+    (dict(o=MIS), 4), (dict(wt=MIS), 4), (dict(y=MIS), 4),
+])
+def test_norm_gate_rejects(kw, status):
+    assert ng(**kw) == status
+    assert G.gdr2_last_error().startswith("gdr2_norm_gate")
+
+
+def test_norm_gate_empty_is_a_no_op():
+    # rows = 0 launches nothing, so fake device addresses are never touched
+    assert ng(rows=0) == 0
+    assert ng(rows=0, o=None, z=None, y=None) == 0
+
+
+def decg(**kw):
+    args = dict(q=A, k=A, v=A, la=A, b=A, w=A, S=A, z=A, nw=None, eps=1e-6, y=A, N=8, H=4,
+                dk=128, dv=128, dt=G.GDR2_BF16, ldt=G.GDR2_F32, stream=None)
+    args.update(kw)
+    return G.library().gdr2_decode_step_norm_gate(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(z=None), 1), (dict(y=None), 1), (dict(S=None), 1), (dict(dt=3), 3), (dict(N=-1), 2),
+    (dict(eps=-0.5), 2), (dict(eps=float("nan")), 2), (dict(dv=96), 5),
+    (dict(z=MIS), 4), (dict(nw=MIS), 4), (dict(y=MIS), 4),
+])
+def test_decode_norm_gate_rejects(kw, status):
+    assert decg(**kw) == status
+    assert G.gdr2_last_error().startswith("gdr2_decode_step_norm_gate")
