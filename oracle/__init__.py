@@ -10,6 +10,9 @@ with the GPU library.
   used to pin the recurrence (the two must agree to rounding).
 * :mod:`oracle.epilogue` -- the block's output epilogue, RMSNorm then a SiLU
   output gate, in fp64 numpy (pages, "Big-Picture Architecture" item 6).
+* :mod:`oracle.prologue` -- the gate prologue (Eq. 12 log-decay, Eq. 11
+  sigmoid gates, q/k L2 norm) and grouped value heads, in fp64 numpy, producing
+  the operator's inputs for :func:`fwd`.
 
 Inputs are the *stored* tensors (bf16 or fp32), converted exactly to fp64, so
 the comparison measures the kernel's arithmetic and not input quantisation.
