@@ -9,8 +9,9 @@ back to back with HIP events on the launch stream.  The same run also times D
 decode steps (256 sequences x 16 heads, fp32 state updated in place) and the
 fp64 oracle on a bounded sample of the forward workload on the host cores,
 and, outside the step, the block's output epilogue (gdr2_norm_gate over the
-forward's o) and the decode step with that epilogue fused
-(gdr2_decode_step_norm_gate).
+forward's o), the decode step with that epilogue fused
+(gdr2_decode_step_norm_gate), and the same forward from the block's projections
+with the gate prologue fused (gdr2_chunk_fwd_block).
 
 Prints one JSON line: tokens/s of the forward (whole job), its TFLOP/s and the
 HBM roofline of the forward kernel, the decode HBM GB/s with its own roofline,
@@ -104,7 +105,8 @@ def write_traffic(fetch_csv, write_csv, copy_mib, command):
             name = r["Kernel_Name"]
             if "gdr2::" not in name:
                 continue
-            key = name.split("gdr2::", 1)[1].split("<", 1)[0].split("(", 1)[0]
+            # the kernel with its template arguments: variants are kept apart
+            key = name.split("gdr2::", 1)[1].split("(", 1)[0]
             per.setdefault(key, {}).setdefault(counter, []).append(
                 float(r["Counter_Value"]) * 1024 / factor)
     for key, d in per.items():
@@ -216,7 +218,16 @@ def main():
     gbs = byts / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
     # one gdr2_chunk_fwd call = the intra-chunk pass + the state pass
-    traffic = load_traffic("intra_kernel", "state_kernel")
+    traffic = load_traffic("intra_kernel<128, 128, true, false>", "state_kernel<128, 128, 2, 4>")
+
+    # ---- the same forward from the block's projections (fused gate prologue) ------
+    bl = I.make_block(B, T, H, H, dk, dv, seed=7)
+    bargs = [x.to(dev) for x in (bl.q, bl.k, bl.v, bl.f, bl.b, bl.w, bl.a, bl.delta)]
+    del bl
+    blk = lambda: G.gdr2_chunk_fwd_block(*bargs, flags=7, o=o, S_T=ST, workspace=ws)
+    bms = time_events(blk, args.steps, args.warmup, torch)
+    bgbs = byts / (bms * 1e-3) / 1e9
+    del bargs
 
     # ---- decode: 256 sequences x 16 heads, fp32 state ---------------------------------
     S = I.decode_state().to(dev)
@@ -299,19 +310,27 @@ def main():
                    "steps": args.decode_steps, "us_per_step": dms * 1e3, "alg_bytes": dbytes,
                    "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
-                                "traffic": load_traffic("decode_kernel")},
+                                "traffic": load_traffic("decode_kernel<128, 128, false>")},
                    "norm_gate_fused": {
                        "entry": "gdr2_decode_step_norm_gate (RMSNorm over dv + SiLU gate in the store)",
                        "us_per_step": gms * 1e3, "alg_bytes": gbytes,
                        "roofline": {"bound": "hbm", "achieved": ggbs, "peak": HBM_PEAK_GBS,
                                     "unit": "GB/s", "frac": ggbs / HBM_PEAK_GBS,
-                                    "traffic": load_traffic("decode_norm_gate_kernel")}}},
+                                    "traffic": load_traffic("decode_norm_gate_kernel<128, 128, false>")}}},
+        "block": {"workload": "gdr2_chunk_fwd_block B4 T4096 H16 Hv16 dk=dv=128 from projections: "
+                              "q/k L2 norm, Eq. 12 decay from bf16 W_f x, sigmoid gates (flags 7)",
+                  "steps": args.steps, "ms_per_call": bms, "tokens_per_s": tokens / (bms * 1e-3),
+                  "alg_bytes": byts,
+                  "roofline": {"bound": "hbm", "achieved": bgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": bgbs / HBM_PEAK_GBS,
+                               "traffic": load_traffic("intra_kernel<128, 128, true, true>",
+                                                       "state_kernel<128, 128, 2, 4>")}},
         "epilogue": {"workload": "gdr2_norm_gate over the forward's o [B4 T4096 H16 128] bf16, "
                                  "RMSNorm per head (group 128) x weight x silu(z), into y",
                      "steps": args.steps, "us_per_call": ems * 1e3, "alg_bytes": ebytes,
                      "roofline": {"bound": "hbm", "achieved": egbs, "peak": HBM_PEAK_GBS,
                                   "unit": "GB/s", "frac": egbs / HBM_PEAK_GBS,
-                                  "traffic": load_traffic("norm_gate_kernel")}},
+                                  "traffic": load_traffic("norm_gate_kernel<1, true>")}},
         "cpu_baseline": cpu,
         "source_hash": source_hash(),
     }

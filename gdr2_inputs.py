@@ -196,3 +196,54 @@ def epilogue_inputs(shape, *, dtype=torch.bfloat16, seed: int = 1005, weight: bo
     z = 1.5 * torch.randn(*shape, generator=gen, dtype=f32)
     wt = 1 + 0.1 * torch.randn(shape[-1], generator=gen, dtype=f32) if weight else None
     return o.to(dtype).contiguous(), z.to(dtype).contiguous(), wt
+
+
+# ---- block inputs: projections before the gate prologue ------------------------------
+
+@dataclasses.dataclass
+class BlockWorkload:
+    """Inputs of the forward from the block's projections (all on the CPU).
+    q, k, f, b: [B, T, H, dk]; v, w: [B, T, Hv, dv]; a, delta: fp32 [H, dk]."""
+
+    name: str
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    f: torch.Tensor
+    b: torch.Tensor
+    w: torch.Tensor
+    a: torch.Tensor
+    delta: torch.Tensor
+    S0: Optional[torch.Tensor]
+    cu_seqlens: Optional[torch.Tensor]
+    seed: int
+
+
+def make_block(B: int, T: int, H: int, Hv: int, dk: int, dv: int, *, f_dtype=torch.bfloat16,
+               s0_std: float = 0.0, seqlens=None, seed: int = 0, name: str = "block") -> BlockWorkload:
+    """Raw q, k ~ N(0, 1) (not normalised), v ~ N(0, 1), pre-activations f, b,
+    w ~ N(0, 1); a = log U[1, 16] and delta = softplus^-1(dt) with dt
+    log-uniform in [1e-3, 1e-1] per (key head, channel), so that the per-token
+    decay -exp(a) * softplus(f + delta) lies mostly in [-0.3, -0.02]."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    f32 = torch.float32
+    cu = None
+    if seqlens is not None:
+        assert B == 1 and sum(seqlens) == T
+        cu = torch.zeros(len(seqlens) + 1, dtype=torch.int32)
+        cu[1:] = torch.cumsum(torch.tensor(seqlens, dtype=torch.int64), 0).to(torch.int32)
+    q = torch.randn(B, T, H, dk, generator=gen, dtype=f32)
+    k = torch.randn(B, T, H, dk, generator=gen, dtype=f32)
+    v = torch.randn(B, T, Hv, dv, generator=gen, dtype=f32)
+    f = torch.randn(B, T, H, dk, generator=gen, dtype=f32)
+    b = torch.randn(B, T, H, dk, generator=gen, dtype=f32)
+    w = torch.randn(B, T, Hv, dv, generator=gen, dtype=f32)
+    a = torch.log(1 + 15 * torch.rand(H, dk, generator=gen, dtype=f32))
+    dt = torch.exp(torch.log(torch.tensor(1e-3)) + torch.rand(H, dk, generator=gen, dtype=f32)
+                   * (torch.log(torch.tensor(1e-1)) - torch.log(torch.tensor(1e-3))))
+    delta = torch.log(torch.expm1(dt))
+    N = B if cu is None else cu.numel() - 1
+    S0 = draw_state(gen, N, Hv, dk, dv, s0_std) if s0_std > 0 else None
+    bf = torch.bfloat16
+    return BlockWorkload(name, q.to(bf), k.to(bf), v.to(bf), f.to(f_dtype), b.to(bf), w.to(bf),
+                         a.contiguous(), delta.contiguous(), S0, cu, seed)

@@ -107,9 +107,10 @@ size_t gdr2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  * matrix product takes fp32 operands.  With GDR2_BF16 the products take
  * 16-bit operands: bf16 for the decay-normalised chunk matrix, a bf16 hi/lo
  * pair for the causal score matrix, and fp16 for the bounded state-pass
- * operands (stored in that form in the workspace records).  The per-channel log-decay summed over any 32 consecutive tokens
- * of a chunk must stay above -80 (the decay normalisation is centred inside
- * each 64-token chunk); stronger decay gives undefined results.
+ * operands (stored in that form in the workspace records).  The per-channel
+ * log-decay summed over any 8 consecutive tokens must stay above -80 (the
+ * decay normalisation is centred inside each 16-token block of a chunk);
+ * stronger decay gives undefined results.
  */
 gdr2_status gdr2_chunk_fwd(const void *q, const void *k, const void *v,
                            const void *log_alpha, const void *b, const void *w,
@@ -118,6 +119,54 @@ gdr2_status gdr2_chunk_fwd(const void *q, const void *k, const void *v,
                            int B, int T, int H, int dk, int dv,
                            gdr2_dtype in_dtype, gdr2_dtype log_alpha_dtype,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Gate prologue flags of gdr2_chunk_fwd_block (Gated DeltaNet-2 pages, "Gate
+ * Parameterization", Eqs. 11-12, and the block's per-head q/k L2 norm).
+ */
+#define GDR2_PRO_QK_L2NORM 1u /* q, k <- x / sqrt(sum over dk of x^2 + qk_eps)              */
+#define GDR2_PRO_DECAY 2u     /* f is W_f x: log_alpha = -exp(a) * softplus(f + delta)      */
+#define GDR2_PRO_GATES 4u     /* b, w are W_b x, W_w x: b <- b_scale * sigmoid(b), w <- sigmoid(w) */
+
+/*
+ * The chunkwise forward from the block's projections, with grouped value heads
+ * (Gated DeltaNet-2 pages: "Gate Parameterization", Eq. 12 log-decay
+ * g = -exp(a) * softplus(W_f x + delta) and Eq. 11 gates b = sigmoid(W_b x),
+ * with the factor 2 of the negative-eigenvalue variant, and w = sigmoid(W_w x);
+ * q and k L2-normalised per head ("Big-Picture Architecture" item 1); with
+ * H_v > H value heads, the key-side q, k, g and b are repeated across each
+ * value-head group).  The selected activations run inside the intra-chunk
+ * pass on the loaded values, in fp32, so the activated tensors never reach
+ * HBM; the operator is then exactly gdr2_chunk_fwd on them.
+ *
+ *   q, k : bf16 [B, T, H, dk]          (raw when GDR2_PRO_QK_L2NORM)
+ *   f    : [B, T, H, dk] in f_dtype    (W_f x with GDR2_PRO_DECAY, else log_alpha)
+ *   b    : bf16 [B, T, H, dk]          (W_b x with GDR2_PRO_GATES, else the erase gate)
+ *   v, w : bf16 [B, T, Hv, dv]         (w is W_w x with GDR2_PRO_GATES)
+ *   decay_a, decay_bias : fp32 [H, dk], a and delta of Eq. 12 per key head
+ *         and channel (required with GDR2_PRO_DECAY, else ignored).
+ *   b_scale : 1 for the sigmoid erase gate, 2 for the negative-eigenvalue
+ *         variant (GDR2_PRO_GATES; must be finite).
+ *   qk_eps : >= 0 (GDR2_PRO_QK_L2NORM; a zero row gives NaN when it is 0).
+ *   H, Hv : key heads and value heads; Hv must be a multiple of H, and value
+ *         head h reads key head h / (Hv / H) (the group's value heads are
+ *         consecutive).
+ *   S0, S_T : fp32 [N, Hv, dk, dv] (NULL as in gdr2_chunk_fwd); o : bf16
+ *         [B, T, Hv, dv]; cu_seqlens, num_seqs as in gdr2_chunk_fwd.
+ *   workspace : at least gdr2_chunk_fwd_workspace_bytes(B, T, Hv, dk, dv,
+ *         num_seqs, GDR2_BF16) bytes.
+ * Unknown flag bits give GDR2_E_UNSUPPORTED; Hv not a multiple of H gives
+ * GDR2_E_SHAPE.  flags = 0 with Hv = H is gdr2_chunk_fwd with bf16 inputs.
+ * Precision and the decay limit are those of gdr2_chunk_fwd with GDR2_BF16,
+ * applied to the activated values.
+ */
+gdr2_status gdr2_chunk_fwd_block(const void *q, const void *k, const void *v, const void *f,
+                                 const void *b, const void *w, const float *decay_a,
+                                 const float *decay_bias, unsigned flags, float b_scale,
+                                 float qk_eps, const float *S0, void *o, float *S_T,
+                                 const int32_t *cu_seqlens, int num_seqs, int B, int T, int H,
+                                 int Hv, int dk, int dv, gdr2_dtype f_dtype, void *workspace,
+                                 size_t workspace_bytes, void *stream);
 
 /*
  * One recurrent decode step for N independent sequences (pages, Appendix C.5:

@@ -11,6 +11,9 @@ Functions carry the C names (include/gdr2.h):
   sequences, returns ``(o, S_T)``.
 * :func:`gdr2_decode_step` -- one token for N sequences, updates ``S`` in place,
   returns ``o``.
+* :func:`gdr2_chunk_fwd_block` -- the forward from the block's projections:
+  fused gate prologue (Eq. 12 decay, sigmoid gates, q/k L2 norm) and grouped
+  value heads, returns ``(o, S_T)``.
 * :func:`gdr2_norm_gate` -- the block's output epilogue (RMSNorm, then a SiLU
   output gate) over o, returns ``y``.
 * :func:`gdr2_decode_step_norm_gate` -- a decode step whose store applies that
@@ -26,7 +29,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["gdr2_chunk_fwd", "gdr2_decode_step", "gdr2_norm_gate", "gdr2_decode_step_norm_gate",
+__all__ = ["gdr2_chunk_fwd", "gdr2_chunk_fwd_block", "gdr2_decode_step", "gdr2_norm_gate",
+           "gdr2_decode_step_norm_gate", "GDR2_PRO_QK_L2NORM", "GDR2_PRO_DECAY", "GDR2_PRO_GATES",
            "gdr2_chunk_fwd_workspace_bytes",
            "gdr2_status_string", "gdr2_last_error", "gdr2_version", "Gdr2Error",
            "LibraryMissing", "library", "library_path", "GDR2_F32", "GDR2_BF16", "EXPORTS"]
@@ -34,10 +38,11 @@ __all__ = ["gdr2_chunk_fwd", "gdr2_decode_step", "gdr2_norm_gate", "gdr2_decode_
 GDR2_F32, GDR2_BF16 = 0, 1
 STATUS = {0: "GDR2_OK", 1: "GDR2_E_NULL", 2: "GDR2_E_SHAPE", 3: "GDR2_E_DTYPE",
           4: "GDR2_E_ALIGN", 5: "GDR2_E_UNSUPPORTED", 6: "GDR2_E_WORKSPACE", 7: "GDR2_E_LAUNCH"}
-EXPORTS = ("gdr2_chunk_fwd_workspace_bytes", "gdr2_chunk_fwd", "gdr2_decode_step",
+EXPORTS = ("gdr2_chunk_fwd_workspace_bytes", "gdr2_chunk_fwd", "gdr2_chunk_fwd_block", "gdr2_decode_step",
            "gdr2_norm_gate", "gdr2_decode_step_norm_gate",
            "gdr2_status_string", "gdr2_last_error", "gdr2_version")
 NORM_GATE_MAX_GROUP = 8192
+GDR2_PRO_QK_L2NORM, GDR2_PRO_DECAY, GDR2_PRO_GATES = 1, 2, 4
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libgdr2.so")
@@ -75,6 +80,9 @@ def library():
         lib.gdr2_norm_gate.restype = i32
         lib.gdr2_decode_step_norm_gate.argtypes = [vp] * 9 + [f32, vp] + [i32] * 6 + [vp]
         lib.gdr2_decode_step_norm_gate.restype = i32
+        lib.gdr2_chunk_fwd_block.argtypes = [vp] * 8 + [ctypes.c_uint, f32, f32] + [vp] * 4 + \
+            [i32] * 7 + [i32, vp, sz, vp]
+        lib.gdr2_chunk_fwd_block.restype = i32
         lib.gdr2_status_string.argtypes = [i32]
         lib.gdr2_status_string.restype = ctypes.c_char_p
         lib.gdr2_last_error.argtypes = []
@@ -269,3 +277,59 @@ def gdr2_decode_step_norm_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
         N, H, dk, dv, _dtype_code(q), _dtype_code(log_alpha), _stream(stream, dev))
     _check(st)
     return y
+
+
+def gdr2_chunk_fwd_block(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, f: torch.Tensor,
+                         b: torch.Tensor, w: torch.Tensor, decay_a: Optional[torch.Tensor] = None,
+                         decay_bias: Optional[torch.Tensor] = None, *,
+                         flags: int = GDR2_PRO_QK_L2NORM | GDR2_PRO_DECAY | GDR2_PRO_GATES,
+                         b_scale: float = 1.0, qk_eps: float = 1e-6,
+                         S0: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
+                         o: Optional[torch.Tensor] = None, S_T: Optional[torch.Tensor] = None,
+                         want_state: bool = True, workspace: Optional[torch.Tensor] = None,
+                         stream=None):
+    """Forward from the block's projections.  q, k, f, b: [B, T, H, dk]; v, w:
+    [B, T, Hv, dv] (Hv a multiple of H); all bf16 except f (bf16 or fp32).
+    ``flags`` selects the prologue steps (GDR2_PRO_*): f is W_f x under
+    GDR2_PRO_DECAY (decay_a, decay_bias: fp32 [H, dk]), b and w are W_b x and
+    W_w x under GDR2_PRO_GATES, q and k are L2-normalised under
+    GDR2_PRO_QK_L2NORM.  Returns ``(o [B, T, Hv, dv], S_T [N, Hv, dk, dv])``."""
+    lib = library()
+    dev = q.device
+    Bsz, T, H, dk = q.shape
+    Hv, dv = v.shape[-2], v.shape[-1]
+    if q.dtype != torch.bfloat16:
+        raise TypeError("gdr2_chunk_fwd_block takes bf16 q, k, v, b, w")
+    N = Bsz if cu_seqlens is None else cu_seqlens.numel() - 1
+    if o is None:
+        o = torch.empty((Bsz, T, Hv, dv), dtype=torch.bfloat16, device=dev)
+    if S_T is None and want_state:
+        S_T = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=dev)
+    ns = N if cu_seqlens is not None else 0
+    ws_bytes = gdr2_chunk_fwd_workspace_bytes(Bsz, T, Hv, dk, dv, ns, GDR2_BF16)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    for name, t, shp in (("k", k, (Bsz, T, H, dk)), ("f", f, (Bsz, T, H, dk)), ("b", b, (Bsz, T, H, dk)),
+                         ("v", v, (Bsz, T, Hv, dv)), ("w", w, (Bsz, T, Hv, dv)), ("o", o, (Bsz, T, Hv, dv))):
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+        if name != "f" and t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bf16")
+    for name, t in (("decay_a", decay_a), ("decay_bias", decay_bias)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (H, dk)):
+            raise ValueError(f"{name} must be fp32 {(H, dk)}")
+    for name, t in (("S0", S0), ("S_T", S_T)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (N, Hv, dk, dv)):
+            raise ValueError(f"{name} must be fp32 {(N, Hv, dk, dv)}")
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    st = lib.gdr2_chunk_fwd_block(
+        _ptr(q, "q", dev), _ptr(k, "k", dev), _ptr(v, "v", dev), _ptr(f, "f", dev), _ptr(b, "b", dev),
+        _ptr(w, "w", dev), _ptr(decay_a, "decay_a", dev), _ptr(decay_bias, "decay_bias", dev),
+        int(flags), float(b_scale), float(qk_eps), _ptr(S0, "S0", dev), _ptr(o, "o", dev),
+        _ptr(S_T, "S_T", dev), _ptr(cu_seqlens, "cu_seqlens", dev), ns, Bsz, T, H, Hv, dk, dv,
+        _dtype_code(f), _ptr(workspace, "workspace", dev), ws_bytes, _stream(stream, dev))
+    _check(st)
+    return o, S_T

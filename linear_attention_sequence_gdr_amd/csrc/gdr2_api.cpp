@@ -59,6 +59,51 @@ Layout two_pass_layout(int B, int T, int H, int dk, int dv, int num_seqs) {
   return l;
 }
 
+// The two-pass forward (16-bit inputs), arguments already validated: Hv value
+// heads (records, o, S0, S_T), Hk key heads (q, k, log_alpha, b).
+gdr2_status two_pass(const char* fn, const void* q, const void* k, const void* v,
+                     const void* log_alpha, const void* b, const void* w, const float* S0, void* o,
+                     float* S_T, const int32_t* cu_seqlens, int N, int B, int T, int Hk, int Hv,
+                     int dk, int dv, bool la_bf16, int pro, const float* da, const float* db,
+                     float b_scale, float qk_eps, char* ws, hipStream_t st) {
+  // intra-chunk pass over all (chunk, value head) items, then the state pass
+  const int ns = cu_seqlens ? N : 0;
+  const Layout l = two_pass_layout(B, T, Hv, dk, dv, ns);
+  int32_t* order = nullptr;
+  int32_t* cbase = nullptr;
+  int32_t* tab = nullptr;
+  if (cu_seqlens) {
+    cbase = reinterpret_cast<int32_t*>(ws + l.cbase);
+    tab = reinterpret_cast<int32_t*>(ws + l.tab);
+    if (gdr2::schedule_bytes(N)) {
+      order = reinterpret_cast<int32_t*>(ws + l.order);
+      const hipError_t e = gdr2::launch_schedule(cu_seqlens, N, T, order, st);
+      if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "%s: schedule launch: %s", fn, hipGetErrorString(e));
+    }
+    const hipError_t e = gdr2::launch_chunk_table(cu_seqlens, N, T, (int)l.cap, cbase, tab, st);
+    if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "%s: chunk table launch: %s", fn, hipGetErrorString(e));
+  }
+  gdr2::IntraArgs ia;
+  ia.q = q; ia.k = k; ia.v = v; ia.la = log_alpha; ia.b = b; ia.w = w;
+  ia.rec = ws + l.rec;
+  ia.tab = tab;
+  ia.total = cu_seqlens ? cbase + N : nullptr;
+  ia.nc = (T + 63) / 64;
+  ia.chunks = (int)l.cap;
+  ia.T = T; ia.H = Hv;
+  ia.la_bf16 = la_bf16;
+  ia.Hk = Hk; ia.grp = Hv / Hk;
+  ia.pro = pro; ia.da = da; ia.db = db; ia.b_scale = b_scale; ia.qk_eps = qk_eps;
+  gdr2::StateArgs sa;
+  sa.rec = ws + l.rec;
+  sa.S0 = S0; sa.o = o; sa.ST = S_T; sa.cu = cu_seqlens; sa.order = order; sa.cbase = cbase;
+  sa.cap = (int)l.cap;
+  sa.N = N; sa.T = T; sa.H = Hv; sa.DV = dv;
+  const hipError_t e = gdr2::launch_two_pass(ia, sa, dk, dv, st);
+  if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "%s: launch: %s", fn, hipGetErrorString(e));
+  return GDR2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -155,39 +200,62 @@ gdr2_status gdr2_chunk_fwd(const void* q, const void* k, const void* v, const vo
     return GDR2_OK;
   }
 
-  // 16-bit inputs: intra-chunk pass over all (chunk, head) items, then the state pass
-  const Layout l = two_pass_layout(B, T, H, dk, dv, ns);
-  int32_t* order = nullptr;
-  int32_t* cbase = nullptr;
-  int32_t* tab = nullptr;
+  return two_pass("gdr2_chunk_fwd", q, k, v, log_alpha, b, w, S0, o, S_T, cu_seqlens, N, B, T, H, H,
+                  dk, dv, log_alpha_dtype == GDR2_BF16, 0, nullptr, nullptr, 1.f, 0.f, ws, st);
+}
+
+gdr2_status gdr2_chunk_fwd_block(const void* q, const void* k, const void* v, const void* f,
+                                 const void* b, const void* w, const float* decay_a,
+                                 const float* decay_bias, unsigned flags, float b_scale,
+                                 float qk_eps, const float* S0, void* o, float* S_T,
+                                 const int32_t* cu_seqlens, int num_seqs, int B, int T, int H,
+                                 int Hv, int dk, int dv, gdr2_dtype f_dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  const char* fn = "gdr2_chunk_fwd_block";
+  if (!q || !k || !v || !f || !b || !w || !o)
+    return fail(GDR2_E_NULL, "%s: q, k, v, f, b, w and o must be non-NULL", fn);
+  if ((flags & GDR2_PRO_DECAY) && (!decay_a || !decay_bias))
+    return fail(GDR2_E_NULL, "%s: GDR2_PRO_DECAY needs decay_a and decay_bias", fn);
+  if (!dtype_ok(f_dtype))
+    return fail(GDR2_E_DTYPE, "%s: f dtype code %d is not GDR2_F32 or GDR2_BF16", fn, (int)f_dtype);
+  if (flags & ~(unsigned)(GDR2_PRO_QK_L2NORM | GDR2_PRO_DECAY | GDR2_PRO_GATES))
+    return fail(GDR2_E_UNSUPPORTED, "%s: unknown flag bits 0x%x", fn, flags);
+  if (B <= 0 || T < 0 || H <= 0 || Hv <= 0 || dk <= 0 || dv <= 0)
+    return fail(GDR2_E_SHAPE, "%s: need B >= 1, T >= 0, H, Hv, dk, dv >= 1 (got B=%d T=%d H=%d Hv=%d dk=%d dv=%d)",
+                fn, B, T, H, Hv, dk, dv);
+  if (Hv % H != 0)
+    return fail(GDR2_E_SHAPE, "%s: Hv=%d must be a multiple of H=%d", fn, Hv, H);
+  if (!dim_ok(dk) || !dim_ok(dv))
+    return fail(GDR2_E_UNSUPPORTED, "%s: dk=%d dv=%d; each must be 32, 64 or 128", fn, dk, dv);
+  if ((flags & GDR2_PRO_GATES) && !isfinite(b_scale))
+    return fail(GDR2_E_SHAPE, "%s: b_scale must be finite (got %g)", fn, (double)b_scale);
+  if ((flags & GDR2_PRO_QK_L2NORM) && !(qk_eps >= 0.f && isfinite(qk_eps)))
+    return fail(GDR2_E_SHAPE, "%s: qk_eps must be finite and >= 0 (got %g)", fn, (double)qk_eps);
+  int N = B;
   if (cu_seqlens) {
-    cbase = reinterpret_cast<int32_t*>(ws + l.cbase);
-    tab = reinterpret_cast<int32_t*>(ws + l.tab);
-    if (gdr2::schedule_bytes(N)) {
-      order = reinterpret_cast<int32_t*>(ws + l.order);
-      const hipError_t e = gdr2::launch_schedule(cu_seqlens, N, T, order, st);
-      if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "gdr2_chunk_fwd: schedule launch: %s", hipGetErrorString(e));
-    }
-    const hipError_t e = gdr2::launch_chunk_table(cu_seqlens, N, T, (int)l.cap, cbase, tab, st);
-    if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "gdr2_chunk_fwd: chunk table launch: %s", hipGetErrorString(e));
+    if (B != 1) return fail(GDR2_E_SHAPE, "%s: packed sequences (cu_seqlens) need B == 1, got B=%d", fn, B);
+    if (num_seqs < 1) return fail(GDR2_E_SHAPE, "%s: num_seqs must be >= 1 with cu_seqlens, got %d", fn, num_seqs);
+    N = num_seqs;
   }
-  gdr2::IntraArgs ia;
-  ia.q = q; ia.k = k; ia.v = v; ia.la = log_alpha; ia.b = b; ia.w = w;
-  ia.rec = ws + l.rec;
-  ia.tab = tab;
-  ia.total = cu_seqlens ? cbase + N : nullptr;
-  ia.nc = (T + 63) / 64;
-  ia.chunks = (int)l.cap;
-  ia.T = T; ia.H = H;
-  ia.la_bf16 = log_alpha_dtype == GDR2_BF16;
-  gdr2::StateArgs sa;
-  sa.rec = ws + l.rec;
-  sa.S0 = S0; sa.o = o; sa.ST = S_T; sa.cu = cu_seqlens; sa.order = order; sa.cbase = cbase;
-  sa.cap = (int)l.cap;
-  sa.N = N; sa.T = T; sa.H = H; sa.DV = dv;
-  const hipError_t e = gdr2::launch_two_pass(ia, sa, dk, dv, st);
-  if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "gdr2_chunk_fwd: launch: %s", hipGetErrorString(e));
-  return GDR2_OK;
+  if ((long long)N * Hv > (1LL << 26))
+    return fail(GDR2_E_SHAPE, "%s: N*Hv = %lld (sequence, head) pairs is too many", fn, (long long)N * Hv);
+  const void* ptrs[] = {q, k, v, f, b, w, o, S0, S_T, cu_seqlens, workspace, decay_a, decay_bias};
+  const char* names[] = {"q", "k", "v", "f", "b", "w", "o", "S0", "S_T", "cu_seqlens", "workspace",
+                         "decay_a", "decay_bias"};
+  for (int i = 0; i < 13; ++i)
+    if (ptrs[i] && !aligned16(ptrs[i]))
+      return fail(GDR2_E_ALIGN, "%s: %s is not 16-byte aligned", fn, names[i]);
+  const int ns = cu_seqlens ? N : 0;
+  const Layout l = two_pass_layout(B, T, Hv, dk, dv, ns);
+  if (l.cap * Hv > 0x7fffffffLL)
+    return fail(GDR2_E_SHAPE, "%s: %lld (chunk, head) items exceed 2^31 - 1", fn, l.cap * Hv);
+  const size_t need = gdr2_chunk_fwd_workspace_bytes(B, T, Hv, dk, dv, ns, GDR2_BF16);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(GDR2_E_WORKSPACE, "%s: workspace of %zu bytes needed, got %zu%s", fn, need,
+                workspace_bytes, workspace ? "" : " (NULL)");
+  return two_pass(fn, q, k, v, f, b, w, S0, o, S_T, cu_seqlens, N, B, T, H, Hv, dk, dv,
+                  f_dtype == GDR2_BF16, (int)flags, decay_a, decay_bias, b_scale, qk_eps,
+                  static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
 }
 
 namespace {

@@ -12,18 +12,22 @@
 // reads hit that XCD's L2.  Nothing is written to HBM but o and S_T.
 //
 // Per chunk, with G the fp32 cumulative log-decay from the chunk start (kept
-// in log2 units) and m = row 31 of the chunk:
+// in log2 units) and c(r) = 16*(r/16) + 7 the centre row of row r's 16-row
+// block:
 //   L   the raw q, k, g, b, v, w of the chunk come from registers filled
 //       during the previous chunk, and the next chunk's loads are issued.
-//       G by a DPP scan; centred decay factors e1 = 2^(G - G_m) and
-//       e2 = 2^(G_m - G), so no factor exceeds the decay over half a chunk;
+//       G by a DPP scan; centred decay factors e1 = 2^(G_r - G_c(r)) and
+//       e2 = 2^(G_c(r) - G_r), so no factor exceeds the decay over 8 tokens;
 //       E' = e1*b*k, K' = e2*k, Q' = e1*q, and the un-centred E = gamma*b*k,
 //       Q_g = gamma*q, K_tail = (gamma_C/gamma)*k, Z = w*v (Step 1, Eq. 20).
 //       Each thread owns consecutive rows, so the transposed copies E^T,
 //       K_tail^T and Z^T are written as vectors.
-//   P   T^T = K' E'^T and A_qk^T = K' Q'^T on MFMA (the centring cancels in
-//       every product; Step 2 and the A_qk of Eq. 24).  Computing the
-//       transposes lets each lane store 4 adjacent entries of a row.
+//   P   T^T = K' E'^T and A_qk^T = K' Q'^T on MFMA (Step 2 and the A_qk of
+//       Eq. 24).  Inside a diagonal 16x16 tile the centring cancels; an
+//       off-diagonal tile (a, b) scales K' by 2^(G_c(a) - G_c(b)) <= 1 per
+//       channel first, which restores the decay between the two centres.
+//       Computing the transposes lets each lane store 4 adjacent entries of
+//       a row.
 //   S   A = (I + T)^-1: the four 16x16 diagonal blocks by fp32 forward
 //       substitution, then the off-diagonal blocks by the block recurrence
 //       A_ab = A_aa (-sum_{b<=c<a} T_ac A_cb).
@@ -81,7 +85,8 @@ struct ChunkCfg {
   static constexpr size_t O_RT = O_ZT + (size_t)DVB * LDC * SS;     // ST [DVB][LDC] R^T
   static constexpr size_t O_S = O_RT + (size_t)DVB * LDC * SS;      // ST [2][DVB][LDK] S^T
   static constexpr size_t O_GC = O_S + (size_t)2 * DVB * LDK * SS;  // fp32 [DK] gamma_C
-  static constexpr size_t BYTES = O_GC + (size_t)DK * 4;
+  static constexpr size_t O_GCEN = O_GC + (size_t)DK * 4;           // fp32 [4][DK] block centres
+  static constexpr size_t BYTES = O_GCEN + (size_t)4 * DK * 4;
   static_assert(BYTES <= 160 * 1024, "LDS budget exceeded");
   // phase-L mapping: thread = (column group cg of EPC key channels, row group
   // rg of RPT consecutive rows); the RG row groups of a column group are
@@ -127,6 +132,7 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs p) {
   ST* RT = reinterpret_cast<ST*>(smem + Cfg::O_RT);
   ST* Sbuf = reinterpret_cast<ST*>(smem + Cfg::O_S);
   float* gC = reinterpret_cast<float*>(smem + Cfg::O_GC);
+  float* gcen = reinterpret_cast<float*>(smem + Cfg::O_GCEN);
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int m = lane & 15, g4 = lane >> 4;
@@ -289,6 +295,11 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs p) {
       for (int pr = 1; pr < RPT; ++pr)
 #pragma unroll
         for (int i = 0; i < EPC; ++i) G[pr][i] += G[pr - 1][i];
+      // Each 16-row block a is centred on its row c_a = 16a + 7, so that a
+      // centred factor spans at most 8 tokens of decay; the thread's rows all
+      // lie in block ab.  gcen[a][channel] = G at c_a lets phase P restore the
+      // decay between two block centres in the off-diagonal tiles.
+      const int ab = r0 / 16;
       float egm[EPC], egcm[EPC];
 #pragma unroll
       for (int i = 0; i < EPC; ++i) {
@@ -296,13 +307,20 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs p) {
         const float excl = seg_scan<RG>(tot) - tot;
 #pragma unroll
         for (int pr = 0; pr < RPT; ++pr) G[pr][i] += excl;
-        const float gm = __shfl(G[(CH / 2 - 1) % RPT][i], (CH / 2 - 1) / RPT, RG);
+        float gca[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) gca[a] = __shfl(G[7 % RPT][i], (16 * a + 7) / RPT, RG);
+        const float gm = ab == 0 ? gca[0] : ab == 1 ? gca[1] : ab == 2 ? gca[2] : gca[3];
         const float gc = __shfl(G[RPT - 1][i], RG - 1, RG);
         egm[i] = exp2_fast(gm);
         egcm[i] = exp2_fast(gc - gm);
-        if (rg == 0) gC[EPC * cg + i] = exp2_fast(gc);
+        if (rg == 0) {
+          gC[EPC * cg + i] = exp2_fast(gc);
 #pragma unroll
-        for (int pr = 0; pr < RPT; ++pr) G[pr][i] -= gm;  // centred: G - G_m
+          for (int a = 0; a < 4; ++a) gcen[a * DK + EPC * cg + i] = gca[a];
+        }
+#pragma unroll
+        for (int pr = 0; pr < RPT; ++pr) G[pr][i] -= gm;  // centred: G - G_(c_ab)
       }
 #pragma unroll
       for (int pr = 0; pr < RPT; ++pr) {
@@ -352,12 +370,55 @@ __global__ __launch_bounds__(NT) void chunk_fwd_kernel(ChunkArgs p) {
         if (ti < 0) break;
         int a, b;
         tri_tile(ti, a, b);
-        f32x4 acc = mma_lds<KT, DK>(zero4(), Kh + 16 * b * LDK, LDK, Qh + 16 * a * LDK, LDK);
-        if constexpr (BF16) {
-          acc = mma_lds<KT, DK>(acc, Kh + 16 * b * LDK, LDK, Ql + 16 * a * LDK, LDK);
-          acc = mma_lds<KT, DK>(acc, Kl + 16 * b * LDK, LDK, Qh + 16 * a * LDK, LDK);
+        f32x4 acc, acct;
+        if (a == b) {
+          acc = mma_lds<KT, DK>(zero4(), Kh + 16 * b * LDK, LDK, Qh + 16 * a * LDK, LDK);
+          if constexpr (BF16) {
+            acc = mma_lds<KT, DK>(acc, Kh + 16 * b * LDK, LDK, Ql + 16 * a * LDK, LDK);
+            acc = mma_lds<KT, DK>(acc, Kl + 16 * b * LDK, LDK, Qh + 16 * a * LDK, LDK);
+          }
+          acct = mma_lds<KT, DK>(zero4(), Kh + 16 * b * LDK, LDK, Ep + 16 * a * LDK, LDK);
+        } else {
+          // K' of block b is centred on c_b and E', Q' of block a on c_a: scale
+          // K' by 2^(G(c_a) - G(c_b)) <= 1 per channel before the products, as
+          // an exponent shift (the scale alone may be below the fp32 range)
+          acc = zero4();
+          acct = zero4();
+          const int ob = (16 * b + m) * LDK, oa = (16 * a + m) * LDK;
+          const float* ga = gcen + a * DK;
+          const float* gb = gcen + b * DK;
+          if constexpr (F32) {
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += 16) {
+              const int c0 = k0 + 4 * g4;
+              float4 kk = *reinterpret_cast<const float4*>(Kh + ob + c0);
+              kk.x = mul_exp2(kk.x, ga[c0] - gb[c0]);
+              kk.y = mul_exp2(kk.y, ga[c0 + 1] - gb[c0 + 1]);
+              kk.z = mul_exp2(kk.z, ga[c0 + 2] - gb[c0 + 2]);
+              kk.w = mul_exp2(kk.w, ga[c0 + 3] - gb[c0 + 3]);
+              acc = mma16(kk, *reinterpret_cast<const float4*>(Qh + oa + c0), acc);
+              acct = mma16(kk, *reinterpret_cast<const float4*>(Ep + oa + c0), acct);
+            }
+          } else {
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += 32) {
+              const int c0 = k0 + 8 * g4;
+              bf16x8 kh = *reinterpret_cast<const bf16x8*>(Kh + ob + c0);
+              bf16x8 kl = *reinterpret_cast<const bf16x8*>(Kl + ob + c0);
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                const float x = mul_exp2((float)kh[j] + (float)kl[j], ga[c0 + j] - gb[c0 + j]);
+                const float hi = bf16_round(x);
+                kh[j] = (__bf16)hi;
+                kl[j] = (__bf16)(x - hi);
+              }
+              acc = mma32(kh, *reinterpret_cast<const bf16x8*>(Qh + oa + c0), acc);
+              acc = mma32(kh, *reinterpret_cast<const bf16x8*>(Ql + oa + c0), acc);
+              acc = mma32(kl, *reinterpret_cast<const bf16x8*>(Qh + oa + c0), acc);
+              acct = mma32(kh, *reinterpret_cast<const bf16x8*>(Ep + oa + c0), acct);
+            }
+          }
         }
-        f32x4 acct = mma_lds<KT, DK>(zero4(), Kh + 16 * b * LDK, LDK, Ep + 16 * a * LDK, LDK);
         // lanes hold A_qk[16a + m][16b + 4*g4 + q] and T[16a + m][16b + 4*g4 + q]
         if (a == b) {
 #pragma unroll
@@ -536,16 +597,8 @@ bool chunk_supported(int dk, int dv, bool bf16) {
 }
 
 hipError_t launch_chunk(const ChunkArgs& a, int dk, int dv, bool bf16, hipStream_t stream) {
-  if (!chunk_supported(dk, dv, bf16)) return hipErrorInvalidValue;
-  if (bf16) {
-    // enough workgroups to cover the 256 CUs: 32-channel blocks, else 16
-    const bool wide = (long long)a.N * a.H * (dv / 32) >= 256;
-    switch (dk) {
-      case 32: return wide ? launch_variant<32, 32, false>(a, stream) : launch_variant<32, 16, false>(a, stream);
-      case 64: return wide ? launch_variant<64, 32, false>(a, stream) : launch_variant<64, 16, false>(a, stream);
-      default: return wide ? launch_variant<128, 32, false>(a, stream) : launch_variant<128, 16, false>(a, stream);
-    }
-  }
+  // 16-bit inputs take the two-pass forward (gdr2_intra.hip, gdr2_state.hip)
+  if (!chunk_supported(dk, dv, bf16) || bf16) return hipErrorInvalidValue;
   switch (dk) {
     case 32: return launch_variant<32, 16, true>(a, stream);
     default: return launch_variant<64, 16, true>(a, stream);

@@ -25,6 +25,13 @@ template <> __device__ __forceinline__ float4 cvt4<float4>(f32x4 a) {
 }
 // 2^x on the hardware exponential unit (about 1 ulp).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+// x * 2^e with the integer part of e applied as an exact exponent shift, so
+// that 2^e itself never underflows or overflows: only a result that is out of
+// range is.  (x large and 2^e below the fp32 range still give their product.)
+__device__ __forceinline__ float mul_exp2(float x, float e) {
+  const float n = floorf(e);
+  return __builtin_amdgcn_ldexpf(x * exp2_fast(e - n), (int)n);
+}
 
 template <typename V4> __device__ __forceinline__ V4 neg_cvt4(f32x4 a) {
   return cvt4<V4>(f32x4{-a[0], -a[1], -a[2], -a[3]});

@@ -79,6 +79,9 @@ size_t record_bytes(int dk, int dv);
 // Packed-sequence tables for the two-pass forward: cbase[n] = index of the
 // first chunk of sequence n (cbase[N] = total chunks), tab[2c], tab[2c+1] =
 // first token row and length of chunk c.
+// Gate prologue flags (the values of the public GDR2_PRO_* flags).
+enum { PRO_QK_L2NORM = 1, PRO_DECAY = 2, PRO_GATES = 4 };
+
 struct IntraArgs {
   const void *q, *k, *v, *la, *b, *w;
   char* rec;
@@ -86,8 +89,17 @@ struct IntraArgs {
   const int32_t* total;   // packed sequences: device total chunk count; else nullptr
   int nc;                 // chunks per sequence (equal-length sequences)
   int chunks;             // total chunks (equal-length) or an upper bound (packed)
-  int T, H;
+  int T, H;               // H: value heads (one record per chunk and value head)
   int la_bf16;
+  // Grouped value heads: q, k, la, b have Hk heads and value head h reads key
+  // head h / grp (H = Hk * grp).  The plain forward has Hk = H, grp = 1.
+  int Hk, grp;
+  // Gate prologue, applied to the loaded inputs (pro = 0: none).
+  int pro;                // PRO_* flags
+  const float* da;        // PRO_DECAY: a, fp32 [Hk][DK]
+  const float* db;        // PRO_DECAY: delta, fp32 [Hk][DK]
+  float b_scale;          // PRO_GATES: b = b_scale * sigmoid(b)
+  float qk_eps;           // PRO_QK_L2NORM: x / sqrt(sum(x^2) + qk_eps)
 };
 struct StateArgs {
   const char* rec;

@@ -8,13 +8,16 @@
 // (chunk, head) item per workgroup iteration, in a persistent grid that
 // prefetches the next item's raw inputs into registers while it works on the
 // current one.  Per item, with G the fp32 cumulative log-decay from the chunk
-// start (log2 units) and m = row 31 of the chunk:
-//   L  G by a DPP scan; centred factors e1 = 2^(G - G_m), e2 = 2^(G_m - G) so
-//      that no factor exceeds the decay over half a chunk; E' = e1*b*k,
+// start (log2 units) and c(r) = 16*(r/16) + 7 the centre row of row r's
+// 16-row block:
+//   L  G by a DPP scan; centred factors e1 = 2^(G_r - G_c(r)), e2 = 2^(G_c(r)
+//      - G_r) so that no factor exceeds the decay over 8 tokens; E' = e1*b*k,
 //      K' = e2*k, Q' = e1*q (bf16, hi/lo for K' and Q'), the un-centred
 //      E = gamma*b*k, Q_g = gamma*q, K_tail = (gamma_C/gamma)*k and Z = w*v.
-//   P  T^T = K' E'^T and A_qk^T = K' Q'^T on MFMA (the centring cancels in
-//      every product).
+//   P  T^T = K' E'^T and A_qk^T = K' Q'^T on MFMA.  Inside a diagonal 16x16
+//      tile the centring cancels; an off-diagonal tile (a, b) first scales K'
+//      by 2^(G_c(a) - G_c(b)) <= 1 per channel (and splits it into hi/lo
+//      again), which restores the decay between the two centres.
 //   S  A = (I + T)^-1: fp32 forward substitution on the four 16x16 diagonal
 //      blocks, then the block recurrence for the off-diagonal blocks.
 //   Y  Y = A E and U = A Z on MFMA.
@@ -33,7 +36,7 @@ namespace gdr2 {
 namespace {
 
 constexpr int NT = 512;  // threads per workgroup
-constexpr int NW = 8;    // wavefronts per workgroup
+constexpr int NW = 8;    // wavefronts per workgroup (the prologue's row sums read NW = 8 partials)
 
 template <int DK, int DV>
 struct IntraCfg {
@@ -56,7 +59,12 @@ struct IntraCfg {
   static constexpr size_t O_A = O_TN + (size_t)CH * LDC * 2;       // [64][LDC] A
   static constexpr int LDZ = DV + PAD;                             // rows of Z
   static constexpr size_t O_Z = O_A + (size_t)CH * LDC * 2;        // [64][LDZ] Z (row major)
-  static constexpr size_t BYTES = O_Z + (size_t)CH * LDZ * 2;
+  // per (block pair a > b, channel): 2^(G(c_a) - G(c_b)) as fp32 factor and
+  // integer exponent, float2 [6][DK]
+  static constexpr size_t O_DSC = O_Z + (size_t)CH * LDZ * 2;
+  static constexpr size_t O_NRM = O_DSC + (size_t)6 * DK * 8;      // fp32 [64][2] q, k row sums
+  static constexpr size_t O_FLAG = O_NRM + (size_t)CH * 2 * 4;     // int: an item uses block centres
+  static constexpr size_t BYTES = O_FLAG + 16;
   static_assert(BYTES <= 160 * 1024, "LDS budget exceeded");
   // key-side mapping: thread = (column group cg of EPC channels, row group rg
   // of RPT consecutive rows); the RG row groups of a column group are
@@ -83,7 +91,19 @@ __device__ __forceinline__ f16x4 lds_tr16(const _Float16* p) {
 
 }  // namespace
 
-template <int DK, int DV, bool LA16>
+// fp32 activations of the gate prologue.  softplus(x) = max(x, 0) +
+// log1p(e^-|x|), with log1p(u) = u - u^2/2 (its Taylor series) below 1e-3
+// where 1 + u would round away u.
+__device__ __forceinline__ float softplus_f(float x) {
+  const float u = __expf(-fabsf(x));
+  const float l = u < 1e-3f ? u * (1.f - 0.5f * u) : __logf(1.f + u);
+  return fmaxf(x, 0.f) + l;
+}
+__device__ __forceinline__ float sigmoid_f(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __expf(-x));
+}
+
+template <int DK, int DV, bool LA16, bool PRO>
 __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
   typedef IntraCfg<DK, DV> Cfg;
   typedef Rec<DK, DV> R;
@@ -107,6 +127,9 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
   ST* Tn = reinterpret_cast<ST*>(smem + Cfg::O_TN);
   ST* Am = reinterpret_cast<ST*>(smem + Cfg::O_A);
   ST* Zr = reinterpret_cast<ST*>(smem + Cfg::O_Z);
+  float2* dsc = reinterpret_cast<float2*>(smem + Cfg::O_DSC);
+  float* nrm = reinterpret_cast<float*>(smem + Cfg::O_NRM);
+  int* blocked = reinterpret_cast<int*>(smem + Cfg::O_FLAG);
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int m = lane & 15, g4 = lane >> 4;
@@ -116,6 +139,8 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
 
   // the strictly upper blocks of A stay zero; the products run over them
   for (int e = tid; e < CH * LDC; e += NT) Am[e] = (ST)0.f;
+  if (tid == 0) *blocked = 0;
+  for (int e = tid; e < 6 * DK; e += NT) dsc[e] = make_float2(1.f, __int_as_float(0));
 
   // item -> first token row, valid rows, head.  The values are uniform across
   // the workgroup; reading them through readfirstlane keeps them in scalar
@@ -148,7 +173,8 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
   };
 
   const int cg = tid / RG, rg = tid % RG, r0 = rg * RPT;
-  const size_t krow = (size_t)H * DK, vrow = (size_t)H * DV;
+  // key-side rows hold Hk heads (grouped value heads), value-side rows H
+  const size_t krow = (size_t)(PRO ? p.Hk : H) * DK, vrow = (size_t)H * DV;
   uint32_t koff[RPT], goff[RPT], voff[NVU];
   int vr[NVU], vc0[NVU];
 #pragma unroll
@@ -166,6 +192,19 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
 
   uint32_t rq[RPT][2], rk[RPT][2], rb[RPT][2], rgd[RPT][LW];
   uint32_t rv[NVU][VE / 2], rw[NVU][VE / 2];
+  // prologue: a and delta of this thread's 4 key channels for the next item,
+  // loaded at the end of the previous one so that they are live only across
+  // the item boundary
+  float4 rda = make_float4(0.f, 0.f, 0.f, 0.f), rdb = rda;
+  auto fetch_decay = [&](int h) {
+    if constexpr (PRO) {
+      if (p.pro & PRO_DECAY) {
+        const size_t o = (size_t)(h / p.grp) * DK + EPC * cg;
+        rda = *reinterpret_cast<const float4*>(p.da + o);
+        rdb = *reinterpret_cast<const float4*>(p.db + o);
+      }
+    }
+  };
   // Range-limited buffer loads: rows past the chunk's last valid token read
   // as zero and nothing outside the caller's tensors is touched.
   // One input tensor per batch (q, k, b, log_alpha, v, w).  A CU keeps only
@@ -174,7 +213,8 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
   // at six points of the current item (two in phase L, then one at the start
   // of each later phase).
   auto fetch = [&](long long row0, int clen, int h, int batch) {
-    const size_t kel = (size_t)row0 * krow + (size_t)h * DK, vel = (size_t)row0 * vrow + (size_t)h * DV;
+    const int hk = PRO ? h / p.grp : h;  // key head of value head h
+    const size_t kel = (size_t)row0 * krow + (size_t)hk * DK, vel = (size_t)row0 * vrow + (size_t)h * DV;
     const int kbytes = (int)(clen * krow * 2), gbytes = (int)(clen * krow * (LA16 ? 2 : 4));
     const int vbytes = (int)(clen * vrow * 2);
     if (batch <= 2) {
@@ -197,6 +237,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
   int clen, h;
   locate(order(blockIdx.x), row0, clen, h);
   for (int b = 0; b < 6; ++b) fetch(row0, clen, h, b);
+  fetch_decay(h);
   __syncthreads();
 
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
@@ -215,17 +256,84 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
       for (int pr = 0; pr < RPT; ++pr) {
         unpack4<false>(rq[pr], qv[pr]);
         unpack4<false>(rk[pr], kv[pr]);
+      }
+      // q, k L2 norm of the gate prologue: per-row scales, applied where the
+      // operand tiles are formed so that q and k can stay packed until then
+      float nq[RPT], nk[RPT];
+#pragma unroll
+      for (int pr = 0; pr < RPT; ++pr) nq[pr] = nk[pr] = 1.f;
+      if constexpr (PRO) {
+        if (p.pro & PRO_QK_L2NORM) {
+          // A token row's DK channels sit in all CG column groups: 64/RG of
+          // them per wavefront (lanes RG apart) and NW wavefronts.  Reduce
+          // inside the wavefront by xor shuffles, then across wavefronts in
+          // a fixed order through the diagonal-T buffer, which is idle during
+          // this phase: red[row][q or k][wavefront] -> nrm[row][q or k].
+          float sq[RPT], sk[RPT];
+#pragma unroll
+          for (int pr = 0; pr < RPT; ++pr) {
+            sq[pr] = 0.f;
+            sk[pr] = 0.f;
+#pragma unroll
+            for (int i = 0; i < EPC; ++i) {
+              sq[pr] = fmaf(qv[pr][i], qv[pr][i], sq[pr]);
+              sk[pr] = fmaf(kv[pr][i], kv[pr][i], sk[pr]);
+            }
+#pragma unroll
+            for (int off = RG; off < 64; off <<= 1) {
+              sq[pr] += __shfl_xor(sq[pr], off);
+              sk[pr] += __shfl_xor(sk[pr], off);
+            }
+          }
+          float* red = Tdt;
+          static_assert(CH * 2 * NW * 4 <= 4 * 16 * 16 * 4, "row sums exceed the diagonal-T buffer");
+          if (lane < RG) {
+#pragma unroll
+            for (int pr = 0; pr < RPT; ++pr) {
+              red[((r0 + pr) * 2 + 0) * NW + wv] = sq[pr];
+              red[((r0 + pr) * 2 + 1) * NW + wv] = sk[pr];
+            }
+          }
+          __syncthreads();
+          if (tid < CH * 2) {
+            const float4* r4 = reinterpret_cast<const float4*>(red + tid * NW);
+            const float4 x0 = r4[0], x1 = r4[1];
+            nrm[tid] = ((x0.x + x0.y) + (x0.z + x0.w)) + ((x1.x + x1.y) + (x1.z + x1.w));
+          }
+          __syncthreads();
+#pragma unroll
+          for (int pr = 0; pr < RPT; ++pr) {
+            const float2 t = *reinterpret_cast<const float2*>(nrm + (r0 + pr) * 2);
+            const float tq = t.x, tk = t.y;
+            // rows past the chunk's end stay zero (also with qk_eps = 0)
+            const bool live = r0 + pr < clen;
+            nq[pr] = live ? rsqrtf(tq + p.qk_eps) : 0.f;
+            nk[pr] = live ? rsqrtf(tk + p.qk_eps) : 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int pr = 0; pr < RPT; ++pr) {
         unpack4<false>(rb[pr], bv[pr]);
         unpack4<!LA16>(rgd[pr], G[pr]);
+        if constexpr (!PRO) {
 #pragma unroll
-        for (int i = 0; i < EPC; ++i) G[pr][i] *= LOG2E;
+          for (int i = 0; i < EPC; ++i) G[pr][i] *= LOG2E;
+        }
       }
 #pragma unroll
       for (int i = 0; i < NVU; ++i)
 #pragma unroll
         for (int j = 0; j < VE / 2; ++j) {
-          z[i][2 * j] = __uint_as_float(rv[i][j] << 16) * __uint_as_float(rw[i][j] << 16);
-          z[i][2 * j + 1] = __uint_as_float(rv[i][j] & 0xffff0000u) * __uint_as_float(rw[i][j] & 0xffff0000u);
+          float w0 = __uint_as_float(rw[i][j] << 16), w1 = __uint_as_float(rw[i][j] & 0xffff0000u);
+          if constexpr (PRO) {
+            if (p.pro & PRO_GATES) {  // write gate w = sigmoid(W_w x)  (Eq. 11)
+              w0 = sigmoid_f(w0);
+              w1 = sigmoid_f(w1);
+            }
+          }
+          z[i][2 * j] = __uint_as_float(rv[i][j] << 16) * w0;
+          z[i][2 * j + 1] = __uint_as_float(rv[i][j] & 0xffff0000u) * w1;
         }
       // The raw registers are free: the next item's loads go out in six
       // batches from here on.  The loads of this item are waited for
@@ -234,27 +342,93 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
       if (itn < items) fetch(nrow0, nclen, nh, 0);
 
+      if constexpr (PRO) {
+        // Gate prologue (Gated DeltaNet-2 pages, "Gate Parameterization":
+        // Eq. 12 log-decay g = -exp(a) * softplus(f + delta) and Eq. 11 erase
+        // gate b = b_scale * sigmoid(W_b x); q and k L2-normalised per head),
+        // in fp32 on the loaded values.
+        if (p.pro & PRO_DECAY) {
+          const float ea[4] = {__expf(rda.x), __expf(rda.y), __expf(rda.z), __expf(rda.w)};
+          const float dl[4] = {rdb.x, rdb.y, rdb.z, rdb.w};
+#pragma unroll
+          for (int pr = 0; pr < RPT; ++pr)
+#pragma unroll
+            for (int i = 0; i < EPC; ++i)  // rows past the chunk's end keep g = 0
+              G[pr][i] = r0 + pr < clen ? -ea[i] * softplus_f(G[pr][i] + dl[i]) : 0.f;
+        }
+        if (p.pro & PRO_GATES) {
+#pragma unroll
+          for (int pr = 0; pr < RPT; ++pr)
+#pragma unroll
+            for (int i = 0; i < EPC; ++i) bv[pr][i] = p.b_scale * sigmoid_f(bv[pr][i]);
+        }
+#pragma unroll
+        for (int pr = 0; pr < RPT; ++pr)
+#pragma unroll
+          for (int i = 0; i < EPC; ++i) G[pr][i] *= LOG2E;
+      }
+
       // fp32 cumulative log2-decay: serial inside the thread, then a scan of
       // the thread totals across the RG row groups of the column group
 #pragma unroll
       for (int pr = 1; pr < RPT; ++pr)
 #pragma unroll
         for (int i = 0; i < EPC; ++i) G[pr][i] += G[pr - 1][i];
+      // Centring.  A channel whose decay on each side of row 31 stays below
+      // 2^CLIM is centred on row 31 for the whole chunk, as one centre keeps
+      // every factor of that channel in range.  A channel with stronger decay
+      // centres each 16-row block a on its row c_a = 16a + 7 instead, so that
+      // a factor spans at most 8 tokens of decay.  The thread's rows all lie
+      // in block ab.  dsc[pair (a, b)][channel] = 2^(G(c_a) - G(c_b)) (1 for a
+      // row-31 channel, the value the table holds between items) as (factor in
+      // [1, 2), integer exponent) lets phase P
+      // restore the decay between two block centres in the off-diagonal
+      // tiles; it spans 16 tokens of decay and may lie below the fp32 range
+      // while the scaled K' (at most ~23 tokens from c_a) does not, so it is
+      // kept as an exponent shift.  The workgroup flag `blocked` tells phase
+      // P whether any channel of the item needs the scaling.
+      constexpr float CLIM = 100.f;
+      const int ab = r0 / 16;
       float egm[EPC], egcm[EPC];
+      bool blocked_t = false;
 #pragma unroll
       for (int i = 0; i < EPC; ++i) {
         const float tot = G[RPT - 1][i];
         const float excl = seg_scan<RG>(tot) - tot;
 #pragma unroll
         for (int pr = 0; pr < RPT; ++pr) G[pr][i] += excl;
-        const float gm = __shfl(G[(CH / 2 - 1) % RPT][i], (CH / 2 - 1) / RPT, RG);
+        const float g31 = __shfl(G[(CH / 2 - 1) % RPT][i], (CH / 2 - 1) / RPT, RG);
         const float gc = __shfl(G[RPT - 1][i], RG - 1, RG);
+        // G is 0 before row 0; with either sign of decay the factors of a
+        // row-31 centre stay within 2^max(|G_31|, |G_31 - G_63|)
+        const bool mild = fabsf(g31) < CLIM && fabsf(g31 - gc) < CLIM;
+        float gca[4] = {g31, g31, g31, g31};
+        if (__any(!mild)) {  // wave-uniform: the shuffles need every lane
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const float v = __shfl(G[7 % RPT][i], (16 * a + 7) / RPT, RG);
+            if (!mild) gca[a] = v;
+          }
+        }
+        const float gm = ab == 0 ? gca[0] : ab == 1 ? gca[1] : ab == 2 ? gca[2] : gca[3];
         egm[i] = exp2_fast(gm);
         egcm[i] = exp2_fast(gc - gm);
         if (rg == 0) reinterpret_cast<float*>(rec + R::GC)[EPC * cg + i] = exp2_fast(gc);
+        if (rg == 0 && !mild) {  // dsc holds 1 (factor 1, exponent 0) for every other channel
 #pragma unroll
-        for (int pr = 0; pr < RPT; ++pr) G[pr][i] -= gm;  // centred: G - G_m
+          for (int a = 1; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < a; ++b) {
+              const float dg = gca[a] - gca[b], n = floorf(dg);
+              dsc[(a * (a - 1) / 2 + b) * DK + EPC * cg + i] =
+                  make_float2(exp2_fast(dg - n), __int_as_float((int)n));
+            }
+        }
+        blocked_t = blocked_t || !mild;
+#pragma unroll
+        for (int pr = 0; pr < RPT; ++pr) G[pr][i] -= gm;  // centred
       }
+      if (blocked_t) *blocked = 1;  // every writer stores the same value
 #pragma unroll
       for (int pr = 0; pr < RPT; ++pr) {
         const int r = r0 + pr;
@@ -263,9 +437,10 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
         for (int i = 0; i < EPC; ++i) {
           const float e1 = exp2_fast(G[pr][i]);
           const float e2 = exp2_fast(-G[pr][i]);
-          ep[i] = e1 * (bv[pr][i] * kv[pr][i]);
-          const float kbv = e2 * kv[pr][i];
-          const float qp = e1 * qv[pr][i];
+          const float kk = kv[pr][i] * nk[pr], qq = qv[pr][i] * nq[pr];  // L2 norm (prologue)
+          ep[i] = e1 * (bv[pr][i] * kk);
+          const float kbv = e2 * kk;
+          const float qp = e1 * qq;
           kh[i] = bf16_round(kbv);
           kl[i] = kbv - kh[i];
           qh[i] = bf16_round(qp);
@@ -295,6 +470,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
     // and A_qk of its tile so the K' operand is read once per K step
     if (itn < items) fetch(nrow0, nclen, nh, 2);
     {
+      const bool blk = *blocked != 0;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int ti = k == 0 ? wv : (wv == 0 ? 8 : wv == 2 ? 9 : -1);
@@ -308,8 +484,29 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
           const int ob = (16 * b + m) * LDK + 8 * g4, oa = (16 * a + m) * LDK + 8 * g4;
 #pragma unroll
           for (int k0 = 0; k0 < DK; k0 += 32) {
-            const bf16x8 kh = *reinterpret_cast<const bf16x8*>(Kh + ob + k0);
-            const bf16x8 kl = *reinterpret_cast<const bf16x8*>(Kl + ob + k0);
+            bf16x8 kh = *reinterpret_cast<const bf16x8*>(Kh + ob + k0);
+            bf16x8 kl = *reinterpret_cast<const bf16x8*>(Kl + ob + k0);
+            if (a != b && blk) {
+              // K' of block b is centred on c_b and E', Q' of block a on c_a:
+              // scale K' by 2^(G(c_a) - G(c_b)) <= 1 per channel (factor, then
+              // exponent shift) and split it into hi/lo again
+              const float4* pd = reinterpret_cast<const float4*>(dsc + (a * (a - 1) / 2 + b) * DK + k0 + 8 * g4);
+#pragma unroll
+              for (int hf = 0; hf < 2; ++hf) {  // two halves of 4 channels: fewer live registers
+                const float4 d0 = pd[2 * hf], d1 = pd[2 * hf + 1];
+                const float df[4] = {d0.x, d0.z, d1.x, d1.z};
+                const int dn[4] = {__float_as_int(d0.y), __float_as_int(d0.w), __float_as_int(d1.y),
+                                   __float_as_int(d1.w)};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  const int jj = 4 * hf + j;
+                  const float x = __builtin_amdgcn_ldexpf(((float)kh[jj] + (float)kl[jj]) * df[j], dn[j]);
+                  const float hi = bf16_round(x);
+                  kh[jj] = (__bf16)hi;
+                  kl[jj] = (__bf16)(x - hi);
+                }
+              }
+            }
             const bf16x8 qh = *reinterpret_cast<const bf16x8*>(Qh + oa + k0);
             const bf16x8 ql = *reinterpret_cast<const bf16x8*>(Ql + oa + k0);
             const bf16x8 ep = *reinterpret_cast<const bf16x8*>(Ep + oa + k0);
@@ -343,6 +540,11 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
 
     // ==== phase S(i): diagonal inverses; E^T, K_tail^T, Q_g into region X ==========
     if (itn < items) fetch(nrow0, nclen, nh, 3);
+    if (*blocked) {  // uniform; phase P has read the flag and the table
+      __syncthreads();  // every thread has read the flag before it is cleared
+      for (int e = tid; e < 6 * DK; e += NT) dsc[e] = make_float2(1.f, __int_as_float(0));
+      if (tid == 0) *blocked = 0;
+    }
     {
 #pragma unroll
       for (int i = 0; i < EPC; ++i) {
@@ -463,6 +665,8 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
         *reinterpret_cast<SV4*>(rec + R::U + ((size_t)(jt * 4 + a) * 64 + lane) * 8) = cvt4<SV4>(u);
       }
     }
+    if (itn < items) fetch_decay(nh);
+    clen = nclen;  // valid rows of the next item (the prologue masks the rest)
     __syncthreads();
   }
 }
@@ -477,7 +681,7 @@ size_t record_bytes(int dk, int dv) {
   return 0;
 }
 
-template <int DK, int DV, bool LA16>
+template <int DK, int DV, bool LA16, bool PRO>
 static hipError_t launch_intra1(const IntraArgs& a, hipStream_t stream) {
   typedef IntraCfg<DK, DV> Cfg;
   const long long items = (long long)a.chunks * a.H;
@@ -487,7 +691,7 @@ static hipError_t launch_intra1(const IntraArgs& a, hipStream_t stream) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64 || !attr_set[dev]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&intra_kernel<DK, DV, LA16>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&intra_kernel<DK, DV, LA16, PRO>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::BYTES);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < 64) attr_set[dev] = true;
@@ -496,14 +700,20 @@ static hipError_t launch_intra1(const IntraArgs& a, hipStream_t stream) {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
   const long long grid = items < cus ? items : cus;  // persistent: one workgroup per CU
-  hipLaunchKernelGGL((intra_kernel<DK, DV, LA16>), dim3((unsigned)grid), dim3(NT), Cfg::BYTES, stream, a);
+  hipLaunchKernelGGL((intra_kernel<DK, DV, LA16, PRO>), dim3((unsigned)grid), dim3(NT), Cfg::BYTES, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_intra(const IntraArgs& a, int dk, int dv, hipStream_t stream) {
+  const bool pro = a.pro != 0 || a.grp != 1;
 #define GDR2_INTRA(DK, DV)                                                                  \
-  if (dk == DK && dv == DV)                                                                 \
-    return a.la_bf16 ? launch_intra1<DK, DV, true>(a, stream) : launch_intra1<DK, DV, false>(a, stream);
+  if (dk == DK && dv == DV) {                                                               \
+    if (pro)                                                                                \
+      return a.la_bf16 ? launch_intra1<DK, DV, true, true>(a, stream)                       \
+                       : launch_intra1<DK, DV, false, true>(a, stream);                     \
+    return a.la_bf16 ? launch_intra1<DK, DV, true, false>(a, stream)                        \
+                     : launch_intra1<DK, DV, false, false>(a, stream);                      \
+  }
   GDR2_INTRA(32, 32) GDR2_INTRA(32, 64) GDR2_INTRA(32, 128)
   GDR2_INTRA(64, 32) GDR2_INTRA(64, 64) GDR2_INTRA(64, 128)
   GDR2_INTRA(128, 32) GDR2_INTRA(128, 64) GDR2_INTRA(128, 128)

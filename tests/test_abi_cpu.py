@@ -162,3 +162,34 @@ def decg(**kw):
 def test_decode_norm_gate_rejects(kw, status):
     assert decg(**kw) == status
     assert G.gdr2_last_error().startswith("gdr2_decode_step_norm_gate")
+
+
+def blk(**kw):
+    args = dict(q=A, k=A, v=A, f=A, b=A, w=A, da=A, db=A, flags=7, bs=1.0, eps=1e-6, S0=None, o=A,
+                ST=None, cu=None, ns=0, B=2, T=100, H=4, Hv=8, dk=128, dv=128, fdt=G.GDR2_F32,
+                ws=None, wsb=0, stream=None)
+    args.update(kw)
+    return G.library().gdr2_chunk_fwd_block(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(f=None), 1), (dict(da=None), 1), (dict(db=None), 1),
+    (dict(fdt=9), 3), (dict(flags=8), 5), (dict(flags=0x17), 5),
+    (dict(Hv=6), 2), (dict(Hv=0), 2), (dict(H=0), 2), (dict(T=-1), 2),
+    (dict(dk=96), 5), (dict(dv=16), 5),
+    (dict(bs=float("inf")), 2), (dict(eps=-1e-6), 2), (dict(eps=float("nan")), 2),
+    (dict(cu=A, ns=2), 2), (dict(cu=A, B=1, ns=0), 2),
+    (dict(q=MIS), 4), (dict(da=MIS), 4), (dict(db=MIS), 4), (dict(o=MIS), 4),
+    (dict(), 6), (dict(ws=A, wsb=1024), 6),
+])
+def test_chunk_fwd_block_rejects(kw, status):
+    assert blk(**kw) == status
+    assert G.gdr2_last_error().startswith("gdr2_chunk_fwd_block")
+
+
+def test_chunk_fwd_block_optional_arguments():
+    # without GDR2_PRO_DECAY the decay parameters may be NULL; without the gates
+    # an infinite b_scale is ignored; both still need the workspace (status 6)
+    assert blk(da=None, db=None, flags=5) == 6
+    assert blk(flags=3, bs=float("inf")) == 6
+    assert blk(flags=6, eps=-1.0) == 6

@@ -217,6 +217,23 @@ def test_varlen_workload_sampled():
     assert torch.isfinite(o.float()).all() and torch.isfinite(ST).all()
 
 
+# ---- strong decay -------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,dk,dv", [(torch.bfloat16, 128, 128), (torch.bfloat16, 64, 32),
+                                         (torch.float32, 64, 64)])
+def test_strong_decay(dtype, dk, dv):
+    """Per-token log-decay around -5 (alpha ~ 0.007): 32 consecutive tokens sum
+    to about -180, far past the range of one centre per chunk, while any 8
+    tokens stay above -80 as the per-block centring needs."""
+    wl = I.make_forward(2, 333, 3, dk, dv, dtype=dtype, decay_shift=5.0, s0_std=0.1, seed=60)
+    g = wl.log_alpha.double().numpy()
+    c = np.concatenate([np.zeros((2, 1) + g.shape[2:]), np.cumsum(g, axis=1)], axis=1)
+    assert (c[:, 32:] - c[:, :-32]).min() < -150 and (c[:, 8:] - c[:, :-8]).min() > -80
+    o, ST = run_fwd(wl)
+    ro, rS = oracle_fwd(wl)
+    check(o, ST, ro, rS, dtype == torch.bfloat16, f"strong decay {dtype} dk={dk} dv={dv}")
+
+
 # ---- decode -------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dk,dv,dtype", [(128, 128, torch.float32), (32, 64, torch.float32),
