@@ -6,6 +6,9 @@ with the GPU library.
 
 * :func:`fwd` / :func:`decode` -- the token-by-token recurrence in fp64
   (``gdr2_oracle.c``; Gated DeltaNet-2 pages, Steps 1-5 and Eq. 10).
+* :func:`bwd` -- reverse-mode differentiation of that recurrence in fp64
+  (``gdr2_oracle_bwd.c``; the pages' gate-aware backward flow): dq, dk, dv,
+  dlog_alpha, db, dw and dS0 from dL/do and dL/dS_T.
 * :mod:`oracle.chunk_ref` -- the pages' chunkwise WY algorithm in fp64 numpy,
   used to pin the recurrence (the two must agree to rounding).
 * :mod:`oracle.epilogue` -- the block's output epilogue, RMSNorm then a SiLU
@@ -30,17 +33,26 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdr2_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "_build", "libgdr2_oracle.so")
+_BWD_SRC = os.path.join(_HERE, "gdr2_oracle_bwd.c")
+_BWD_LIB_PATH = os.path.join(_HERE, "_build", "libgdr2_oracle_bwd.so")
 _lib = None
+_bwd_lib = None
+
+
+def _gcc(src: str, out: str):
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
+                           "-Wall", "-Werror", "-o", tmp, src, "-lm"])
+    os.replace(tmp, out)
 
 
 def build(force: bool = True) -> str:
-    """Compile the C oracle with gcc (-O2, OpenMP) into oracle/_build."""
-    os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
-                               "-Wall", "-Werror", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB_PATH)
+    """Compile the C oracle (forward and backward libraries) with gcc (-O2,
+    OpenMP) into oracle/_build."""
+    for src, out in ((_SRC, _LIB_PATH), (_BWD_SRC, _BWD_LIB_PATH)):
+        if force or not os.path.exists(out):
+            _gcc(src, out)
     return _LIB_PATH
 
 
@@ -57,6 +69,26 @@ def load_library(path: str):
     lib.gdr2_oracle_decode.restype = ctypes.c_int
     lib.gdr2_oracle_max_threads.restype = ctypes.c_int
     return lib
+
+
+def load_bwd_library(path: str):
+    """Load a compiled backward oracle library and declare its C signature."""
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.gdr2_oracle_bwd.argtypes = [dp] * 6 + [ctypes.c_void_p, dp, ctypes.c_void_p] + [dp] * 6 + \
+        [ctypes.c_void_p, ctypes.POINTER(ctypes.c_longlong)] + [ctypes.c_int] * 4 + \
+        [ctypes.c_void_p, ctypes.c_int]
+    lib.gdr2_oracle_bwd.restype = ctypes.c_int
+    return lib
+
+
+def _load_bwd():
+    global _bwd_lib
+    if _bwd_lib is None:
+        if not os.path.exists(_BWD_LIB_PATH) or os.path.getmtime(_BWD_LIB_PATH) < os.path.getmtime(_BWD_SRC):
+            _gcc(_BWD_SRC, _BWD_LIB_PATH)
+        _bwd_lib = load_bwd_library(_BWD_LIB_PATH)
+    return _bwd_lib
 
 
 def _load():
@@ -134,3 +166,35 @@ def decode(q, k, v, g, b, w, S, nthreads: int = 0, lib=None):
     if rc != 0:
         raise RuntimeError("oracle decode rejected its arguments")
     return o, S
+
+
+def bwd(q, k, v, g, b, w, dO, S0=None, dST=None, cu_seqlens=None, mask=None, nthreads: int = 0,
+        lib=None):
+    """Token-by-token fp64 backward of :func:`fwd`.
+
+    Same layouts as :func:`fwd`; ``dO`` is dL/do [B, T, H, dv] and ``dST``
+    dL/dS_T [N, H, dk, dv] (None: zero).  Returns a dict with dq, dk, dg, db
+    [B, T, H, dk], dv, dw [B, T, H, dv] and dS0 [N, H, dk, dv] (fp64)."""
+    q, k, v, g, b, w, dO = (f64(x) for x in (q, k, v, g, b, w, dO))
+    Bsz, T, H, dk = q.shape
+    dv = v.shape[-1]
+    cu = (np.arange(Bsz + 1, dtype=np.int64) * T if cu_seqlens is None
+          else np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64)))
+    N = cu.size - 1
+    out = {n: np.zeros((Bsz, T, H, dk)) for n in ("dq", "dk", "dg", "db")}
+    out.update({n: np.zeros((Bsz, T, H, dv)) for n in ("dv", "dw")})
+    out["dS0"] = np.zeros((N, H, dk, dv))
+    s0 = None if S0 is None else f64(S0)
+    dst = None if dST is None else f64(dST)
+    m = None
+    if mask is not None:
+        m = np.ascontiguousarray(np.asarray(mask, dtype=np.uint8).reshape(N * H))
+    vp = lambda a: None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+    rc = (lib or _load_bwd()).gdr2_oracle_bwd(
+        _p(q), _p(k), _p(v), _p(g), _p(b), _p(w), vp(s0), _p(dO), vp(dst),
+        _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["dg"]), _p(out["db"]), _p(out["dw"]),
+        vp(out["dS0"]), cu.ctypes.data_as(ctypes.POINTER(ctypes.c_longlong)), N, H, dk, dv,
+        vp(m), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle backward rejected its arguments")
+    return out
