@@ -11,7 +11,8 @@ fp64 oracle on a bounded sample of the forward workload on the host cores,
 and, outside the step, the block's output epilogue (gdr2_norm_gate over the
 forward's o), the decode step with that epilogue fused
 (gdr2_decode_step_norm_gate), and the same forward from the block's projections
-with the gate prologue fused (gdr2_chunk_fwd_block).
+with the gate prologue fused (gdr2_chunk_fwd_block), and the backward of the
+forward (gdr2_chunk_bwd).
 
 Prints one JSON line: tokens/s of the forward (whole job), its TFLOP/s and the
 HBM roofline of the forward kernel, the decode HBM GB/s with its own roofline,
@@ -229,6 +230,19 @@ def main():
     bgbs = byts / (bms * 1e-3) / 1e9
     del bargs
 
+    # ---- backward of the same forward (dL/do, dL/dS_T -> every input gradient) ------
+    dOb = torch.randn((B, T, H, dv), generator=torch.Generator("cpu").manual_seed(8)).to(torch.bfloat16).to(dev)
+    dSTb = torch.zeros((B, H, dk, dv), dtype=torch.float32, device=dev)
+    wsb = torch.empty(G.gdr2_chunk_bwd_workspace_bytes(B, T, H, dk, dv, 0), dtype=torch.uint8, device=dev)
+    bwd = lambda: G.gdr2_chunk_bwd(*ins, dOb, None, dSTb, workspace=wsb)
+    bwd_steps = max(1, min(args.steps, 10))
+    bwms = time_events(bwd, bwd_steps, 1, torch)
+    # algorithmic bytes: q, k, log_alpha, b, v, w, dO read (bf16), dS_T read and dS0
+    # written (fp32), six fp32 input gradients written
+    bw_bytes = tokens * H * (4 * dk + 3 * dv) * 2 + 2 * B * H * dk * dv * 4 + tokens * H * (4 * dk + 2 * dv) * 4
+    bw_gbs = bw_bytes / (bwms * 1e-3) / 1e9
+    del dOb, dSTb, wsb
+
     # ---- decode: 256 sequences x 16 heads, fp32 state ---------------------------------
     S = I.decode_state().to(dev)
     pool = [[t.to(dev) for t in I.decode_step_inputs(s)] for s in range(8)]
@@ -317,6 +331,12 @@ def main():
                        "roofline": {"bound": "hbm", "achieved": ggbs, "peak": HBM_PEAK_GBS,
                                     "unit": "GB/s", "frac": ggbs / HBM_PEAK_GBS,
                                     "traffic": load_traffic("decode_norm_gate_kernel<128, 128, false>")}}},
+        "backward": {"workload": "gdr2_chunk_bwd B4 T4096 H16 dk=dv=128 bf16 inputs, fp32 gradients "
+                                 "of q, k, v, log_alpha, b, w and S0",
+                     "steps": bwd_steps, "ms_per_call": bwms, "tokens_per_s": tokens / (bwms * 1e-3),
+                     "alg_bytes": bw_bytes,
+                     "roofline": {"bound": "hbm", "achieved": bw_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": bw_gbs / HBM_PEAK_GBS, "traffic": None}},
         "block": {"workload": "gdr2_chunk_fwd_block B4 T4096 H16 Hv16 dk=dv=128 from projections: "
                               "q/k L2 norm, Eq. 12 decay from bf16 W_f x, sigmoid gates (flags 7)",
                   "steps": args.steps, "ms_per_call": bms, "tokens_per_s": tokens / (bms * 1e-3),

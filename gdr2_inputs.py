@@ -247,3 +247,14 @@ def make_block(B: int, T: int, H: int, Hv: int, dk: int, dv: int, *, f_dtype=tor
     bf = torch.bfloat16
     return BlockWorkload(name, q.to(bf), k.to(bf), v.to(bf), f.to(f_dtype), b.to(bf), w.to(bf),
                          a.contiguous(), delta.contiguous(), S0, cu, seed)
+
+
+# ---- backward: cotangents ------------------------------------------------------------
+
+def cotangents(wl: Workload, *, seed: int = 7, ds_std: float = 0.1):
+    """dL/do ~ N(0, 1) in the workload's storage dtype, shaped like o, and
+    dL/dS_T ~ N(0, ds_std^2) fp32 per sequence."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    dO = torch.randn(wl.B, wl.T, wl.H, wl.dv, generator=gen, dtype=torch.float32).to(wl.q.dtype)
+    dST = ds_std * torch.randn(wl.num_seqs, wl.H, wl.dk, wl.dv, generator=gen, dtype=torch.float32)
+    return dO.contiguous(), dST.contiguous()

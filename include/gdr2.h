@@ -121,6 +121,49 @@ gdr2_status gdr2_chunk_fwd(const void *q, const void *k, const void *v,
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Bytes of device workspace gdr2_chunk_bwd needs for these sizes (num_seqs as
+ * for gdr2_chunk_fwd).  Returns 0 for sizes gdr2_chunk_bwd would reject.  The
+ * backward keeps every intermediate of a (64-token chunk, head) in fp32:
+ * (16 * 64 * dk + 6 * 64 * dv + 7 * 64 * 64 + 2 * dk * dv + dk) * 4 bytes,
+ * rounded up to 256, per item (0.97 MB at dk = dv = 128), for
+ * B * ceil(T/64) chunks (ceil(T/64) + num_seqs with packed sequences) times H.
+ */
+size_t gdr2_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs);
+
+/*
+ * Backward of gdr2_chunk_fwd (Gated DeltaNet-2 pages, "Gate-Aware Backward
+ * Pass", Appendix B): gradients of L with respect to every input, given dL/do
+ * and dL/dS_T.  The forward quantities are recomputed from the inputs; the
+ * state pass runs again to obtain the state entering every chunk, then the
+ * state gradient runs over the chunks in reverse (the output and state
+ * paths), and every chunk forms the gate-aware WY gradients (dA with the
+ * write gate inside dU (w*v)^T and the erase gate inside dY (gamma*b*k)^T,
+ * Eqs. 64-65; dT = -tril(A^T dA A^T, -1)) and the gate and decay gradients,
+ * with dlog_alpha the reverse cumulative sum of dgamma * gamma inside each
+ * chunk.  All arithmetic is fp32.
+ *
+ *   q, k, log_alpha, b, v, w, S0, cu_seqlens, num_seqs, B, T, H, dk, dv and
+ *       the dtypes: exactly as passed to gdr2_chunk_fwd.
+ *   dO   : dL/do, [B, T, H, dv] in in_dtype.
+ *   dS_T : dL/dS_T, fp32 [N, H, dk, dv], or NULL for zero.
+ *   dq, dk, dlog_alpha, db : fp32 [B, T, H, dk];  dv, dw : fp32 [B, T, H, dv];
+ *   dS0  : fp32 [N, H, dk, dv], or NULL (not computed).  With cu_seqlens,
+ *       gradient rows outside [cu[0], cu[N]) are not written.
+ *   workspace : at least gdr2_chunk_bwd_workspace_bytes() bytes of scratch.
+ * With T == 0 the token tensors may be NULL and dS0 = dS_T (zeros without it).
+ * The centred decay factors of the chunk products need the per-channel
+ * log-decay summed over the 32 tokens on either side of a chunk's row 31 to
+ * stay above -80.
+ */
+gdr2_status gdr2_chunk_bwd(const void *q, const void *k, const void *v, const void *log_alpha,
+                           const void *b, const void *w, const float *S0, const void *dO,
+                           const float *dS_T, float *dq, float *dk, float *dv, float *dlog_alpha,
+                           float *db, float *dw, float *dS0, const int32_t *cu_seqlens,
+                           int num_seqs, int B, int T, int H, int dk_, int dv_,
+                           gdr2_dtype in_dtype, gdr2_dtype log_alpha_dtype, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/*
  * Gate prologue flags of gdr2_chunk_fwd_block (Gated DeltaNet-2 pages, "Gate
  * Parameterization", Eqs. 11-12, and the block's per-head q/k L2 norm).
  */

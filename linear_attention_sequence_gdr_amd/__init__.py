@@ -11,6 +11,8 @@ Functions carry the C names (include/gdr2.h):
   sequences, returns ``(o, S_T)``.
 * :func:`gdr2_decode_step` -- one token for N sequences, updates ``S`` in place,
   returns ``o``.
+* :func:`gdr2_chunk_bwd` -- the backward of :func:`gdr2_chunk_fwd`: fp32
+  gradients of every input from dL/do and dL/dS_T.
 * :func:`gdr2_chunk_fwd_block` -- the forward from the block's projections:
   fused gate prologue (Eq. 12 decay, sigmoid gates, q/k L2 norm) and grouped
   value heads, returns ``(o, S_T)``.
@@ -29,7 +31,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["gdr2_chunk_fwd", "gdr2_chunk_fwd_block", "gdr2_decode_step", "gdr2_norm_gate",
+__all__ = ["gdr2_chunk_fwd", "gdr2_chunk_bwd", "gdr2_chunk_bwd_workspace_bytes", "gdr2_chunk_fwd_block", "gdr2_decode_step", "gdr2_norm_gate",
            "gdr2_decode_step_norm_gate", "GDR2_PRO_QK_L2NORM", "GDR2_PRO_DECAY", "GDR2_PRO_GATES",
            "gdr2_chunk_fwd_workspace_bytes",
            "gdr2_status_string", "gdr2_last_error", "gdr2_version", "Gdr2Error",
@@ -38,7 +40,8 @@ __all__ = ["gdr2_chunk_fwd", "gdr2_chunk_fwd_block", "gdr2_decode_step", "gdr2_n
 GDR2_F32, GDR2_BF16 = 0, 1
 STATUS = {0: "GDR2_OK", 1: "GDR2_E_NULL", 2: "GDR2_E_SHAPE", 3: "GDR2_E_DTYPE",
           4: "GDR2_E_ALIGN", 5: "GDR2_E_UNSUPPORTED", 6: "GDR2_E_WORKSPACE", 7: "GDR2_E_LAUNCH"}
-EXPORTS = ("gdr2_chunk_fwd_workspace_bytes", "gdr2_chunk_fwd", "gdr2_chunk_fwd_block", "gdr2_decode_step",
+EXPORTS = ("gdr2_chunk_fwd_workspace_bytes", "gdr2_chunk_fwd", "gdr2_chunk_fwd_block",
+           "gdr2_chunk_bwd_workspace_bytes", "gdr2_chunk_bwd", "gdr2_decode_step",
            "gdr2_norm_gate", "gdr2_decode_step_norm_gate",
            "gdr2_status_string", "gdr2_last_error", "gdr2_version")
 NORM_GATE_MAX_GROUP = 8192
@@ -83,6 +86,10 @@ def library():
         lib.gdr2_chunk_fwd_block.argtypes = [vp] * 8 + [ctypes.c_uint, f32, f32] + [vp] * 4 + \
             [i32] * 7 + [i32, vp, sz, vp]
         lib.gdr2_chunk_fwd_block.restype = i32
+        lib.gdr2_chunk_bwd_workspace_bytes.argtypes = [i32] * 6
+        lib.gdr2_chunk_bwd_workspace_bytes.restype = sz
+        lib.gdr2_chunk_bwd.argtypes = [vp] * 17 + [i32] * 6 + [i32, i32, vp, sz, vp]
+        lib.gdr2_chunk_bwd.restype = i32
         lib.gdr2_status_string.argtypes = [i32]
         lib.gdr2_status_string.restype = ctypes.c_char_p
         lib.gdr2_last_error.argtypes = []
@@ -333,3 +340,57 @@ def gdr2_chunk_fwd_block(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, f: t
         _dtype_code(f), _ptr(workspace, "workspace", dev), ws_bytes, _stream(stream, dev))
     _check(st)
     return o, S_T
+
+
+def gdr2_chunk_bwd_workspace_bytes(B: int, T: int, H: int, dk: int, dv: int, num_seqs: int) -> int:
+    return int(library().gdr2_chunk_bwd_workspace_bytes(B, T, H, dk, dv, num_seqs))
+
+
+def gdr2_chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
+                   b: torch.Tensor, w: torch.Tensor, dO: torch.Tensor,
+                   S0: Optional[torch.Tensor] = None, dS_T: Optional[torch.Tensor] = None,
+                   cu_seqlens: Optional[torch.Tensor] = None, *, want_dS0: bool = True,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Backward of :func:`gdr2_chunk_fwd`.  Inputs as for the forward; dO:
+    dL/do [B, T, H, dv] in q's dtype; dS_T: fp32 [N, H, dk, dv] or None.
+    Returns a dict of fp32 gradients dq, dk, dlog_alpha, db [B, T, H, dk],
+    dv, dw [B, T, H, dv] and dS0 [N, H, dk, dv] (None unless ``want_dS0``)."""
+    lib = library()
+    dev = q.device
+    Bsz, T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = Bsz if cu_seqlens is None else cu_seqlens.numel() - 1
+    ns = N if cu_seqlens is not None else 0
+    for name, t, shp in (("k", k, (Bsz, T, H, dk)), ("log_alpha", log_alpha, (Bsz, T, H, dk)),
+                         ("b", b, (Bsz, T, H, dk)), ("v", v, (Bsz, T, H, dv)), ("w", w, (Bsz, T, H, dv)),
+                         ("dO", dO, (Bsz, T, H, dv))):
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    for name, t in (("k", k), ("v", v), ("b", b), ("w", w), ("dO", dO)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {q.dtype}")
+    for name, t in (("S0", S0), ("dS_T", dS_T)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (N, H, dk, dv)):
+            raise ValueError(f"{name} must be fp32 {(N, H, dk, dv)}")
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    f32 = torch.float32
+    # every row is written unless packed sequences leave rows outside [cu[0], cu[N])
+    alloc = torch.empty if cu_seqlens is None else torch.zeros
+    g = {n: alloc((Bsz, T, H, dk), dtype=f32, device=dev) for n in ("dq", "dk", "dlog_alpha", "db")}
+    g.update({n: alloc((Bsz, T, H, dv), dtype=f32, device=dev) for n in ("dv", "dw")})
+    g["dS0"] = torch.empty((N, H, dk, dv), dtype=f32, device=dev) if want_dS0 else None
+    ws_bytes = gdr2_chunk_bwd_workspace_bytes(Bsz, T, H, dk, dv, ns)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.gdr2_chunk_bwd(
+        _ptr(q, "q", dev), _ptr(k, "k", dev), _ptr(v, "v", dev), _ptr(log_alpha, "log_alpha", dev),
+        _ptr(b, "b", dev), _ptr(w, "w", dev), _ptr(S0, "S0", dev), _ptr(dO, "dO", dev),
+        _ptr(dS_T, "dS_T", dev), _ptr(g["dq"], "dq", dev), _ptr(g["dk"], "dk", dev),
+        _ptr(g["dv"], "dv", dev), _ptr(g["dlog_alpha"], "dlog_alpha", dev), _ptr(g["db"], "db", dev),
+        _ptr(g["dw"], "dw", dev), _ptr(g["dS0"], "dS0", dev), _ptr(cu_seqlens, "cu_seqlens", dev),
+        ns, Bsz, T, H, dk, dv, _dtype_code(q), _dtype_code(log_alpha), _ptr(workspace, "workspace", dev),
+        ws_bytes, _stream(stream, dev))
+    _check(st)
+    return g

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdr2.so")
 SOURCES = ["gdr2_api.cpp", "gdr2_chunk.hip", "gdr2_intra.hip", "gdr2_state.hip", "gdr2_decode.hip",
-           "gdr2_schedule.hip", "gdr2_epilogue.hip"]
+           "gdr2_schedule.hip", "gdr2_epilogue.hip", "gdr2_bwd.hip"]
 ARCH = os.environ.get("GDR2_OFFLOAD_ARCH", "gfx950")
 
 

@@ -260,6 +260,104 @@ gdr2_status gdr2_chunk_fwd_block(const void* q, const void* k, const void* v, co
 
 namespace {
 
+// Workspace of the backward: packed-sequence tables, then one fp32 block per
+// (chunk, head) item.
+struct BwdLayoutHost {
+  size_t cbase, tab, items, total;
+  long long cap;
+};
+BwdLayoutHost bwd_layout(int B, int T, int H, int dk, int dv, int num_seqs) {
+  BwdLayoutHost l{};
+  const long long nc = ((long long)T + 63) / 64;
+  size_t off = 0;
+  if (num_seqs > 0) {
+    l.cap = nc + num_seqs;
+    l.cbase = off;
+    off += align256(sizeof(int32_t) * ((size_t)num_seqs + 1));
+    l.tab = off;
+    off += align256(2 * sizeof(int32_t) * (size_t)l.cap);
+  } else {
+    l.cap = (long long)B * nc;
+  }
+  l.items = off;
+  l.total = off + (size_t)l.cap * (size_t)H * gdr2::bwd_item_bytes(dk, dv);
+  return l;
+}
+
+}  // namespace
+
+size_t gdr2_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs) {
+  if (B <= 0 || T < 0 || H <= 0 || !dim_ok(dk) || !dim_ok(dv) || num_seqs < 0) return 0;
+  return bwd_layout(B, T, H, dk, dv, num_seqs).total;
+}
+
+gdr2_status gdr2_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                           const void* b, const void* w, const float* S0, const void* dO,
+                           const float* dS_T, float* dq, float* dk, float* dv, float* dlog_alpha,
+                           float* db, float* dw, float* dS0, const int32_t* cu_seqlens,
+                           int num_seqs, int B, int T, int H, int dk_, int dv_, gdr2_dtype in_dtype,
+                           gdr2_dtype log_alpha_dtype, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  const char* fn = "gdr2_chunk_bwd";
+  if (T != 0 &&
+      (!q || !k || !v || !log_alpha || !b || !w || !dO || !dq || !dk || !dv || !dlog_alpha || !db || !dw))
+    return fail(GDR2_E_NULL, "%s: inputs, dO and every input gradient must be non-NULL", fn);
+  if (!dtype_ok(in_dtype) || !dtype_ok(log_alpha_dtype))
+    return fail(GDR2_E_DTYPE, "%s: dtype codes %d/%d are not GDR2_F32 or GDR2_BF16", fn, (int)in_dtype,
+                (int)log_alpha_dtype);
+  if (B <= 0 || T < 0 || H <= 0 || dk_ <= 0 || dv_ <= 0)
+    return fail(GDR2_E_SHAPE, "%s: need B >= 1, T >= 0, H >= 1, dk, dv >= 1 (got B=%d T=%d H=%d dk=%d dv=%d)",
+                fn, B, T, H, dk_, dv_);
+  if (!dim_ok(dk_) || !dim_ok(dv_))
+    return fail(GDR2_E_UNSUPPORTED, "%s: dk=%d dv=%d; each must be 32, 64 or 128", fn, dk_, dv_);
+  int N = B;
+  if (cu_seqlens) {
+    if (B != 1) return fail(GDR2_E_SHAPE, "%s: packed sequences (cu_seqlens) need B == 1, got B=%d", fn, B);
+    if (num_seqs < 1) return fail(GDR2_E_SHAPE, "%s: num_seqs must be >= 1 with cu_seqlens, got %d", fn, num_seqs);
+    N = num_seqs;
+  }
+  if ((long long)N * H > (1LL << 26))
+    return fail(GDR2_E_SHAPE, "%s: N*H = %lld (sequence, head) pairs is too many", fn, (long long)N * H);
+  const void* ptrs[] = {q, k, v, log_alpha, b, w, S0, dO, dS_T, dq, dk, dv, dlog_alpha, db, dw, dS0,
+                        cu_seqlens, workspace};
+  const char* names[] = {"q", "k", "v", "log_alpha", "b", "w", "S0", "dO", "dS_T", "dq", "dk", "dv",
+                         "dlog_alpha", "db", "dw", "dS0", "cu_seqlens", "workspace"};
+  for (int i = 0; i < 18; ++i)
+    if (ptrs[i] && !aligned16(ptrs[i]))
+      return fail(GDR2_E_ALIGN, "%s: %s is not 16-byte aligned", fn, names[i]);
+  const int ns = cu_seqlens ? N : 0;
+  const BwdLayoutHost l = bwd_layout(B, T, H, dk_, dv_, ns);
+  if (l.cap * H > 0x7fffffffLL)
+    return fail(GDR2_E_SHAPE, "%s: %lld (chunk, head) items exceed 2^31 - 1", fn, l.cap * H);
+  if (!workspace || workspace_bytes < l.total)
+    return fail(GDR2_E_WORKSPACE, "%s: workspace of %zu bytes needed, got %zu%s", fn, l.total,
+                workspace_bytes, workspace ? "" : " (NULL)");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  gdr2::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.b = b; a.w = w; a.dO = dO;
+  a.S0 = S0; a.dST = dS_T;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dlog_alpha; a.db = db; a.dw = dw; a.dS0 = dS0;
+  a.ws = reinterpret_cast<float*>(ws + l.items);
+  if (cu_seqlens) {
+    int32_t* cbase = reinterpret_cast<int32_t*>(ws + l.cbase);
+    int32_t* tab = reinterpret_cast<int32_t*>(ws + l.tab);
+    const hipError_t e = gdr2::launch_chunk_table(cu_seqlens, N, T, (int)l.cap, cbase, tab, st);
+    if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "%s: chunk table launch: %s", fn, hipGetErrorString(e));
+    a.tab = tab; a.cbase = cbase; a.total = cbase + N;
+  }
+  a.nc = (T + 63) / 64;
+  a.chunks = (int)l.cap;
+  a.N = N; a.T = T; a.H = H;
+  a.in_bf16 = in_dtype == GDR2_BF16;
+  a.la_bf16 = log_alpha_dtype == GDR2_BF16;
+  const hipError_t e = gdr2::launch_bwd(a, dk_, dv_, st);
+  if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "%s: launch: %s", fn, hipGetErrorString(e));
+  return GDR2_OK;
+}
+
+namespace {
+
 gdr2_status decode_common(const char* fn, const void* q, const void* k, const void* v,
                           const void* log_alpha, const void* b, const void* w, float* S, void* o,
                           const void* z, const float* nw, float eps, bool gated, int N, int H,

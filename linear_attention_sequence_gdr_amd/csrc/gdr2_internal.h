@@ -114,6 +114,23 @@ struct StateArgs {
 };
 hipError_t launch_two_pass(const IntraArgs& ia, const StateArgs& sa, int dk, int dv, hipStream_t stream);
 
+// ---- backward ------------------------------------------------------------------------
+// One fp32 workspace block of bwd_item_bytes() per (chunk, head) item, item =
+// chunk_index * H + head; chunk indices as in the two-pass forward.
+struct BwdArgs {
+  const void *q, *k, *v, *la, *b, *w, *dO;
+  const float *S0, *dST;
+  float *dq, *dk, *dv, *dg, *db, *dw, *dS0;
+  float* ws;
+  const int32_t* tab;     // packed sequences: per chunk (row, length); else nullptr
+  const int32_t* cbase;   // packed sequences: first chunk per sequence, [N+1]
+  const int32_t* total;   // packed sequences: cbase + N
+  int nc, chunks, N, T, H;
+  int in_bf16, la_bf16;
+};
+size_t bwd_item_bytes(int dk, int dv);
+hipError_t launch_bwd(const BwdArgs& a, int dk, int dv, hipStream_t stream);
+
 hipError_t launch_decode(const DecodeArgs& a, int dk, int dv, bool bf16, hipStream_t stream);
 
 hipError_t launch_norm_gate(NormGateArgs a, bool bf16, hipStream_t stream);

@@ -193,3 +193,33 @@ def test_chunk_fwd_block_optional_arguments():
     assert blk(da=None, db=None, flags=5) == 6
     assert blk(flags=3, bs=float("inf")) == 6
     assert blk(flags=6, eps=-1.0) == 6
+
+
+def bwdc(**kw):
+    args = dict(q=A, k=A, v=A, la=A, b=A, w=A, S0=None, dO=A, dST=None, dq=A, dk=A, dv=A, dg=A,
+                db=A, dw=A, dS0=None, cu=None, ns=0, B=2, T=100, H=4, dk_=128, dv_=128,
+                dt=G.GDR2_BF16, ldt=G.GDR2_F32, ws=None, wsb=0, stream=None)
+    args.update(kw)
+    return G.library().gdr2_chunk_bwd(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dO=None), 1), (dict(dg=None), 1), (dict(q=None), 1), (dict(dt=2), 3),
+    (dict(B=0), 2), (dict(T=-1), 2), (dict(dk_=48), 5), (dict(dv_=256), 5),
+    (dict(cu=A, ns=3), 2), (dict(cu=A, B=1, ns=0), 2),
+    (dict(dO=MIS), 4), (dict(dS0=MIS), 4), (dict(dST=MIS), 4),
+    (dict(), 6), (dict(ws=A, wsb=4096), 6),
+])
+def test_chunk_bwd_rejects(kw, status):
+    assert bwdc(**kw) == status
+    assert G.gdr2_last_error().startswith("gdr2_chunk_bwd")
+
+
+def test_chunk_bwd_workspace_query():
+    q = G.gdr2_chunk_bwd_workspace_bytes
+    item = lambda dk, dv: (16 * 64 * dk + 6 * 64 * dv + 7 * 64 * 64 + 2 * dk * dv + dk + 63) // 64 * 64 * 4
+    assert q(4, 4096, 16, 128, 128, 0) == 4 * 64 * 16 * item(128, 128)
+    assert q(2, 100, 3, 64, 32, 0) == 2 * 2 * 3 * item(64, 32)
+    a256 = lambda x: (x + 255) // 256 * 256
+    assert q(1, 100, 2, 32, 32, 5) == a256(6 * 4) + a256(2 * 4 * 7) + 7 * 2 * item(32, 32)
+    assert q(1, 100, 2, 48, 32, 0) == 0

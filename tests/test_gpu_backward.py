@@ -1,0 +1,110 @@
+"""Backward on the GPU against the fp64 backward oracle (oracle.bwd), through
+the C ABI (needs an MI355X).
+
+The backward computes in fp32 from the stored inputs (converted exactly), so
+the bar is the fp32 one: max |x - ref| / max |ref| <= 1e-4 per gradient
+tensor.  Cases span several chunks with ragged tails, all head sizes the
+library supports, packed sequences with zero- and one-token members, and the
+training shape sampled on (sequence, head) pairs the oracle computes one by
+one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdr2_inputs as I
+import oracle
+from tests import metrics as M
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+TOL = 1e-4
+NAMES = {"dq": "dq", "dk": "dk", "dv": "dv", "dlog_alpha": "dg", "db": "db", "dw": "dw"}
+
+
+def G():
+    import linear_attention_sequence_gdr_amd as g
+    return g
+
+
+def run_bwd(wl, dO, dST, **kw):
+    dev = lambda x: None if x is None else x.cuda()
+    out = G().gdr2_chunk_bwd(*(x.cuda() for x in (wl.q, wl.k, wl.v, wl.log_alpha, wl.b, wl.w)),
+                             dO.cuda(), dev(wl.S0), dev(dST), dev(wl.cu_seqlens), **kw)
+    torch.cuda.synchronize()
+    return {n: None if t is None else t.cpu() for n, t in out.items()}
+
+
+def oracle_bwd(wl, dO, dST, mask=None):
+    cu = None if wl.cu_seqlens is None else wl.cu_seqlens.numpy()
+    return oracle.bwd(wl.q, wl.k, wl.v, wl.log_alpha, wl.b, wl.w, dO, S0=wl.S0, dST=dST,
+                      cu_seqlens=cu, mask=mask)
+
+
+def check(gr, ref, what, rows=None, with_ds0=True):
+    for ours, theirs in NAMES.items():
+        x, r = M.as64(gr[ours]), ref[theirs]
+        if rows is not None:
+            x, r = rows(x), rows(r)
+        err = M.max_rel(x, r)
+        assert err <= TOL, f"{what}: {ours} {err:.3e}"
+    if with_ds0 and gr["dS0"] is not None:
+        err = M.max_rel(gr["dS0"], ref["dS0"])
+        assert err <= TOL, f"{what}: dS0 {err:.3e}"
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,dtype", [
+    (2, 150, 2, 64, 64, torch.float32),
+    (1, 200, 3, 128, 128, torch.bfloat16),
+    (2, 77, 2, 32, 64, torch.bfloat16),
+    (1, 64, 2, 128, 32, torch.float32),
+    (2, 130, 1, 64, 128, torch.bfloat16),
+])
+def test_backward_matches_oracle(B, T, H, dk, dv, dtype):
+    wl = I.make_forward(B, T, H, dk, dv, dtype=dtype, decay_shift=-2.0, erase_scale=2.0,
+                        s0_std=0.1, seed=70 + T + dk)
+    dO, dST = I.cotangents(wl, seed=71 + dv)
+    check(run_bwd(wl, dO, dST), oracle_bwd(wl, dO, dST), f"B{B} T{T} H{H} dk{dk} dv{dv} {dtype}")
+
+
+def test_backward_without_state_arguments():
+    """S0 = NULL and dS_T = NULL mean zeros; dS0 may be skipped."""
+    wl = I.make_forward(1, 100, 2, 64, 64, dtype=torch.bfloat16, decay_shift=-2.0, seed=72)
+    dO, _ = I.cotangents(wl, seed=73)
+    gr = run_bwd(wl, dO, None, want_dS0=False)
+    check(gr, oracle_bwd(wl, dO, None), "no state arguments", with_ds0=False)
+    assert gr["dS0"] is None
+
+
+def test_backward_packed_sequences():
+    lens = [1, 0, 70, 64, 129, 3, 200]
+    wl = I.make_forward(1, sum(lens), 2, 128, 128, dtype=torch.bfloat16, decay_shift=-2.0,
+                        s0_std=0.1, seqlens=lens, seed=74)
+    dO, dST = I.cotangents(wl, seed=75)
+    check(run_bwd(wl, dO, dST), oracle_bwd(wl, dO, dST), "packed sequences")
+
+
+def test_backward_empty_sequence_passes_state_gradient():
+    wl = I.make_forward(2, 0, 2, 64, 64, dtype=torch.float32, s0_std=0.1, seed=76)
+    dO, dST = I.cotangents(wl, seed=77)
+    gr = run_bwd(wl, dO, dST)
+    assert torch.equal(gr["dS0"], dST)
+
+
+def test_backward_training_shape_sampled():
+    """B4 T4096 H16 d128 bf16 (the benchmark's forward workload) with random
+    cotangents; the oracle computes 4 sampled (sequence, head) pairs."""
+    wl = I.config(1)
+    dO, dST = I.cotangents(wl, seed=78)
+    gr = run_bwd(wl, dO, dST)
+    picks = [(0, 0), (1, 7), (2, 15), (3, 4)]
+    mask = np.zeros((4, 16), bool)
+    for n, h in picks:
+        mask[n, h] = True
+    ref = oracle_bwd(wl, dO, dST, mask=mask)
+    for n, h in picks:
+        check(gr, ref, f"training shape ({n}, {h})", rows=lambda x, n=n, h=h: x[n, :, h],
+              with_ds0=False)
+        err = M.max_rel(gr["dS0"][n, h], ref["dS0"][n, h])
+        assert err <= TOL, f"dS0 ({n}, {h}) {err:.3e}"
