@@ -39,6 +39,7 @@ namespace {
 
 constexpr int BC = 64;    // chunk
 constexpr int DVB = 32;   // value channels per workgroup of the sequential passes
+constexpr int SNT = 512;  // threads per workgroup of the sequential passes
 
 template <int DK, int DV>
 struct BwdLayout {
@@ -149,45 +150,73 @@ struct BmmArgs {
 
 template <int M, int N, int K, bool TA, bool TB>
 __global__ __launch_bounds__(512) void bmm_kernel(BmmArgs p) {
-  constexpr int LD = K + 4;
-  extern __shared__ __align__(16) unsigned char smem[];
-  float* As = reinterpret_cast<float*>(smem);
-  float* Bs = As + M * LD;
+  // K is staged in slices of KC so that several workgroups fit on a CU; every
+  // global access is a 16-byte load (the item blocks, their offsets and the
+  // row strides are multiples of 4 floats)
+  constexpr int KC = 32, LD = KC + 4;
+  constexpr int TM = M / 16, TN = N / 16, TPW = (TM * TN + 7) / 8;
+  __shared__ __align__(16) float As[M * LD];
+  __shared__ __align__(16) float Bs[N * LD];
   const int item = blockIdx.x;
   if (p.total && item / p.H >= *p.total) return;
   const size_t base = (size_t)item * p.stride;
   const float* A = p.A + base;
   const float* B = p.B + base;
-  const int tid = threadIdx.x;
-  for (int e = tid; e < M * K; e += 512) {
-    if constexpr (TA) {
-      const int k = e / M, m = e - k * M;
-      As[m * LD + k] = A[(size_t)k * p.lda + m];
-    } else {
-      const int m = e / K, k = e - m * K;
-      As[m * LD + k] = A[(size_t)m * p.lda + k];
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
+  f32x4 acc[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) acc[u] = zero4();
+  for (int kc = 0; kc < K; kc += KC) {
+    for (int e = tid; e < M * KC / 4; e += 512) {
+      if constexpr (TA) {  // As[m][k] = A[k][m]: 4 consecutive m per load
+        const int k = e / (M / 4), m4 = e - k * (M / 4);
+        const float4 x = *reinterpret_cast<const float4*>(A + (size_t)(kc + k) * p.lda + 4 * m4);
+        As[(4 * m4 + 0) * LD + k] = x.x;
+        As[(4 * m4 + 1) * LD + k] = x.y;
+        As[(4 * m4 + 2) * LD + k] = x.z;
+        As[(4 * m4 + 3) * LD + k] = x.w;
+      } else {
+        const int mm = e / (KC / 4), k4 = e - mm * (KC / 4);
+        *reinterpret_cast<float4*>(As + mm * LD + 4 * k4) =
+            *reinterpret_cast<const float4*>(A + (size_t)mm * p.lda + kc + 4 * k4);
+      }
     }
-  }
-  for (int e = tid; e < N * K; e += 512) {
-    if constexpr (TB) {
-      const int n = e / K, k = e - n * K;
-      Bs[n * LD + k] = B[(size_t)n * p.ldb + k];
-    } else {
-      const int k = e / N, n = e - k * N;
-      Bs[n * LD + k] = B[(size_t)k * p.ldb + n];
+    for (int e = tid; e < N * KC / 4; e += 512) {
+      if constexpr (TB) {
+        const int n = e / (KC / 4), k4 = e - n * (KC / 4);
+        *reinterpret_cast<float4*>(Bs + n * LD + 4 * k4) =
+            *reinterpret_cast<const float4*>(B + (size_t)n * p.ldb + kc + 4 * k4);
+      } else {  // Bs[n][k] = B[k][n]: 4 consecutive n per load
+        const int k = e / (N / 4), n4 = e - k * (N / 4);
+        const float4 x = *reinterpret_cast<const float4*>(B + (size_t)(kc + k) * p.ldb + 4 * n4);
+        Bs[(4 * n4 + 0) * LD + k] = x.x;
+        Bs[(4 * n4 + 1) * LD + k] = x.y;
+        Bs[(4 * n4 + 2) * LD + k] = x.z;
+        Bs[(4 * n4 + 3) * LD + k] = x.w;
+      }
     }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int t = wv + 8 * u;
+      if (t < TM * TN) {
+        const int tm = t / TN, tn = t - tm * TN;
+        acc[u] = mma_lds<float, KC>(acc[u], As + 16 * tm * LD, LD, Bs + 16 * tn * LD, LD);
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  const int wv = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
   float* C = p.C + base;
   const float* D = p.D ? p.D + base : nullptr;
-  for (int t = wv; t < (M / 16) * (N / 16); t += 8) {
-    const int tm = t / (N / 16), tn = t - tm * (N / 16);
-    const f32x4 acc = mma_lds<float, K>(zero4(), As + 16 * tm * LD, LD, Bs + 16 * tn * LD, LD);
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int t = wv + 8 * u;
+    if (t >= TM * TN) continue;
+    const int tm = t / TN, tn = t - tm * TN;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int row = 16 * tm + 4 * g + q, col = 16 * tn + m;
-      float v = p.alpha * acc[q];
+      float v = p.alpha * acc[u][q];
       if (D) v += D[(size_t)row * p.ldc + col];
       if (p.mask && col > row + p.diag) v = 0.f;
       C[(size_t)row * p.ldc + col] = v;
@@ -218,57 +247,122 @@ __global__ __launch_bounds__(64) void bwd_inverse_kernel(BwdArgs a) {
   for (int r = 0; r < BC; ++r) W[L::A + r * BC + j] = sX[r][j];
 }
 
-// ---- sequential state pass: the state entering every chunk --------------------------
-// One workgroup per (sequence, head, 32 value channels); the state block is
-// kept transposed in LDS (S^T, the B operand of Y S).
-template <int DK, int DV>
-__global__ __launch_bounds__(256) void bwd_state_fwd_kernel(BwdArgs a) {
+// Register prefetch of one chunk's operands for the sequential passes.
+template <int DK, int DV, int NK4, int NV4>
+__device__ __forceinline__ void sf_load(const BwdArgs& a, int ci, int h, int jb, int tid,
+                                        f32x4 (&ry)[NK4], f32x4 (&rk)[NK4], f32x4 (&ru)[NV4],
+                                        f32x4& rg) {
   typedef BwdLayout<DK, DV> L;
-  constexpr int NB = DV / DVB, LK = DK + 4, LC = BC + 4;
+  const float* Wn = a.ws + ((size_t)ci * a.H + h) * L::FLOATS;
+#pragma unroll
+  for (int u = 0; u < NK4; ++u) {
+    const int e4 = tid + SNT * u;
+    ry[u] = reinterpret_cast<const f32x4*>(Wn + L::Y_)[e4];
+    rk[u] = reinterpret_cast<const f32x4*>(Wn + L::KT)[e4];
+  }
+#pragma unroll
+  for (int u = 0; u < NV4; ++u) {
+    const int e4 = tid + SNT * u, r = e4 / (DVB / 4), c4 = e4 - r * (DVB / 4);
+    ru[u] = *reinterpret_cast<const f32x4*>(Wn + L::U + (size_t)r * DV + jb * DVB + 4 * c4);
+  }
+  if (tid < DK / 4) rg = reinterpret_cast<const f32x4*>(Wn + L::GC)[tid];
+}
+
+template <int DK, int DV, int NK4, int NV4, int NC4>
+__device__ __forceinline__ void sb_load(const BwdArgs& a, int ci, int h, int jb, int tid,
+                                        f32x4 (&rq)[NK4], f32x4 (&rk)[NK4], f32x4 (&ry)[NK4],
+                                        f32x4 (&ra)[NC4], f32x4 (&ro)[NV4], f32x4& rg) {
+  typedef BwdLayout<DK, DV> L;
+  const float* Wn = a.ws + ((size_t)ci * a.H + h) * L::FLOATS;
+#pragma unroll
+  for (int u = 0; u < NK4; ++u) {
+    const int e4 = tid + SNT * u;
+    rq[u] = reinterpret_cast<const f32x4*>(Wn + L::QG)[e4];
+    rk[u] = reinterpret_cast<const f32x4*>(Wn + L::KT)[e4];
+    ry[u] = reinterpret_cast<const f32x4*>(Wn + L::Y_)[e4];
+  }
+#pragma unroll
+  for (int u = 0; u < NC4; ++u) ra[u] = reinterpret_cast<const f32x4*>(Wn + L::AQK)[tid + SNT * u];
+#pragma unroll
+  for (int u = 0; u < NV4; ++u) {
+    const int e4 = tid + SNT * u, t = e4 / (DVB / 4), c4 = e4 - t * (DVB / 4);
+    ro[u] = *reinterpret_cast<const f32x4*>(Wn + L::DO + (size_t)t * DV + jb * DVB + 4 * c4);
+  }
+  if (tid < DK / 4) rg = reinterpret_cast<const f32x4*>(Wn + L::GC)[tid];
+}
+
+// ---- sequential state pass: the state entering every chunk --------------------------
+// One workgroup of SNT threads per (sequence, head, 32 value channels); the
+// state block is
+// kept transposed in LDS (S^T, the B operand of Y S).  The next chunk's
+// operands are loaded into registers (16-byte loads) while the current chunk
+// computes.
+template <int DK, int DV>
+__global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
+  typedef BwdLayout<DK, DV> L;
+  constexpr int NB = DV / DVB, LK = DK + 4, LC = BC + 4, LV = DVB + 4;
+  constexpr int NK4 = BC * DK / 4 / SNT;   // float4 per thread of a [BC][DK] block
+  constexpr int NV4 = BC * DVB / 4 / SNT;  // float4 per thread of a [BC][DVB] block
+  static_assert(NK4 >= 1 && NV4 >= 1, "state pass tiling");
   extern __shared__ __align__(16) unsigned char smem[];
   float* sST = reinterpret_cast<float*>(smem);  // [DVB][LK]
   float* sY = sST + DVB * LK;                   // [BC][LK]
   float* sKtT = sY + BC * LK;                   // [DK][LC]
   float* sRT = sKtT + DK * LC;                  // [DVB][LC]
+  float* sU = sRT + DVB * LC;                   // [BC][LV]
+  float* sGC = sU + BC * LV;                    // [DK]
   const int jb = blockIdx.x % NB, nh = blockIdx.x / NB, n = nh / a.H, h = nh - n * a.H;
   const int c0 = a.tab ? a.cbase[n] : n * a.nc, c1 = a.tab ? a.cbase[n + 1] : (n + 1) * a.nc;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
-  for (int e = tid; e < DK * DVB; e += 256) {
+  for (int e = tid; e < DK * DVB; e += SNT) {
     const int i = e / DVB, j = e - i * DVB;
     sST[j * LK + i] = a.S0 ? a.S0[(size_t)nh * DK * DV + (size_t)i * DV + jb * DVB + j] : 0.f;
   }
-  __syncthreads();
+  f32x4 ry[NK4], rk[NK4], ru[NV4], rg = zero4();
+  if (c0 < c1) sf_load<DK, DV, NK4, NV4>(a, c0, h, jb, tid, ry, rk, ru, rg);
   for (int ci = c0; ci < c1; ++ci) {
     float* W = a.ws + ((size_t)ci * a.H + h) * L::FLOATS;
-    for (int e = tid; e < DK * DVB; e += 256) {
+#pragma unroll
+    for (int u = 0; u < NK4; ++u) {
+      const int e4 = tid + SNT * u, r = e4 / (DK / 4), i = 4 * (e4 - r * (DK / 4));
+      *reinterpret_cast<f32x4*>(sY + r * LK + i) = ry[u];
+      sKtT[(i + 0) * LC + r] = rk[u][0];
+      sKtT[(i + 1) * LC + r] = rk[u][1];
+      sKtT[(i + 2) * LC + r] = rk[u][2];
+      sKtT[(i + 3) * LC + r] = rk[u][3];
+    }
+#pragma unroll
+    for (int u = 0; u < NV4; ++u) {
+      const int e4 = tid + SNT * u, r = e4 / (DVB / 4), c4 = e4 - r * (DVB / 4);
+      *reinterpret_cast<f32x4*>(sU + r * LV + 4 * c4) = ru[u];
+    }
+    if (tid < DK / 4) *reinterpret_cast<f32x4*>(sGC + 4 * tid) = rg;
+    for (int e = tid; e < DK * DVB; e += SNT) {  // the state entering chunk ci
       const int i = e / DVB, j = e - i * DVB;
       W[L::S + (size_t)i * DV + jb * DVB + j] = sST[j * LK + i];
     }
-    for (int e = tid; e < BC * DK; e += 256) {
-      const int r = e / DK, i = e - r * DK;
-      sY[r * LK + i] = W[L::Y_ + e];
-      sKtT[i * LC + r] = W[L::KT + e];
-    }
     __syncthreads();
+    // the next chunk (the last iteration reloads the current one: no branch)
+    sf_load<DK, DV, NK4, NV4>(a, ci + 1 < c1 ? ci + 1 : ci, h, jb, tid, ry, rk, ru, rg);
     // R = U - Y S  [BC][DVB]
-    for (int t = wv; t < (BC / 16) * (DVB / 16); t += 4) {
+    for (int t = wv; t < (BC / 16) * (DVB / 16); t += SNT / 64) {
       const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
       const f32x4 acc = mma_lds<float, DK>(zero4(), sY + 16 * tm * LK, LK, sST + 16 * tn * LK, LK);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = 16 * tm + 4 * g + q, j = 16 * tn + m;
-        sRT[j * LC + r] = W[L::U + (size_t)r * DV + jb * DVB + j] - acc[q];
+        sRT[j * LC + r] = sU[r * LV + j] - acc[q];
       }
     }
     __syncthreads();
     // S <- Diag(gamma_C) S + K_tail^T R  [DK][DVB]; each lane owns its entries
-    for (int t = wv; t < (DK / 16) * (DVB / 16); t += 4) {
+    for (int t = wv; t < (DK / 16) * (DVB / 16); t += SNT / 64) {
       const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
       const f32x4 acc = mma_lds<float, BC>(zero4(), sKtT + 16 * tm * LC, LC, sRT + 16 * tn * LC, LC);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int i = 16 * tm + 4 * g + q, j = 16 * tn + m;
-        sST[j * LK + i] = W[L::GC + i] * sST[j * LK + i] + acc[q];
+        sST[j * LK + i] = sGC[i] * sST[j * LK + i] + acc[q];
       }
     }
     __syncthreads();
@@ -277,9 +371,10 @@ __global__ __launch_bounds__(256) void bwd_state_fwd_kernel(BwdArgs a) {
 
 // ---- sequential reverse pass: dS' of every chunk, dR, and dS0 ------------------------
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void bwd_state_bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
   typedef BwdLayout<DK, DV> L;
   constexpr int NB = DV / DVB, LK = DK + 4, LC = BC + 4;
+  constexpr int NK4 = BC * DK / 4 / SNT, NV4 = BC * DVB / 4 / SNT, NC4 = BC * BC / 4 / SNT;
   extern __shared__ __align__(16) unsigned char smem[];
   float* sdST = reinterpret_cast<float*>(smem);  // [DVB][LK]  dS^T
   float* sAqkT = sdST + DVB * LK;                // [BC][LC]   A_qk^T
@@ -288,37 +383,57 @@ __global__ __launch_bounds__(256) void bwd_state_bwd_kernel(BwdArgs a) {
   float* sQgT = sKt + BC * LK;                   // [DK][LC]   Q_g^T
   float* sYT = sQgT + DK * LC;                   // [DK][LC]   Y^T
   float* sdRT = sYT + DK * LC;                   // [DVB][LC]  dR^T
+  float* sGC = sdRT + DVB * LC;                  // [DK]
   const int jb = blockIdx.x % NB, nh = blockIdx.x / NB, n = nh / a.H, h = nh - n * a.H;
   const int c0 = a.tab ? a.cbase[n] : n * a.nc, c1 = a.tab ? a.cbase[n + 1] : (n + 1) * a.nc;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
-  for (int e = tid; e < DK * DVB; e += 256) {
+  for (int e = tid; e < DK * DVB; e += SNT) {
     const int i = e / DVB, j = e - i * DVB;
     sdST[j * LK + i] = a.dST ? a.dST[(size_t)nh * DK * DV + (size_t)i * DV + jb * DVB + j] : 0.f;
   }
-  __syncthreads();
+  f32x4 rq[NK4], rk[NK4], ry[NK4], ra[NC4], ro[NV4], rg = zero4();
+  if (c0 < c1) sb_load<DK, DV, NK4, NV4, NC4>(a, c1 - 1, h, jb, tid, rq, rk, ry, ra, ro, rg);
   for (int ci = c1 - 1; ci >= c0; --ci) {
     float* W = a.ws + ((size_t)ci * a.H + h) * L::FLOATS;
-    for (int e = tid; e < DK * DVB; e += 256) {
+#pragma unroll
+    for (int u = 0; u < NK4; ++u) {
+      const int e4 = tid + SNT * u, t = e4 / (DK / 4), i = 4 * (e4 - t * (DK / 4));
+      *reinterpret_cast<f32x4*>(sKt + t * LK + i) = rk[u];
+      sQgT[(i + 0) * LC + t] = rq[u][0];
+      sQgT[(i + 1) * LC + t] = rq[u][1];
+      sQgT[(i + 2) * LC + t] = rq[u][2];
+      sQgT[(i + 3) * LC + t] = rq[u][3];
+      sYT[(i + 0) * LC + t] = ry[u][0];
+      sYT[(i + 1) * LC + t] = ry[u][1];
+      sYT[(i + 2) * LC + t] = ry[u][2];
+      sYT[(i + 3) * LC + t] = ry[u][3];
+    }
+#pragma unroll
+    for (int u = 0; u < NC4; ++u) {  // A_qk[t][r..r+3] -> A_qk^T
+      const int e4 = tid + SNT * u, t = e4 / (BC / 4), r = 4 * (e4 - t * (BC / 4));
+      sAqkT[(r + 0) * LC + t] = ra[u][0];
+      sAqkT[(r + 1) * LC + t] = ra[u][1];
+      sAqkT[(r + 2) * LC + t] = ra[u][2];
+      sAqkT[(r + 3) * LC + t] = ra[u][3];
+    }
+#pragma unroll
+    for (int u = 0; u < NV4; ++u) {  // dO[t][j..j+3] -> dO^T
+      const int e4 = tid + SNT * u, t = e4 / (DVB / 4), j = 4 * (e4 - t * (DVB / 4));
+      sdOT[(j + 0) * LC + t] = ro[u][0];
+      sdOT[(j + 1) * LC + t] = ro[u][1];
+      sdOT[(j + 2) * LC + t] = ro[u][2];
+      sdOT[(j + 3) * LC + t] = ro[u][3];
+    }
+    if (tid < DK / 4) *reinterpret_cast<f32x4*>(sGC + 4 * tid) = rg;
+    for (int e = tid; e < DK * DVB; e += SNT) {  // dL/d(state leaving chunk ci)
       const int i = e / DVB, j = e - i * DVB;
       W[L::DSP + (size_t)i * DV + jb * DVB + j] = sdST[j * LK + i];
     }
-    for (int e = tid; e < BC * BC; e += 256) {
-      const int t = e / BC, r = e - t * BC;
-      sAqkT[r * LC + t] = W[L::AQK + e];
-    }
-    for (int e = tid; e < BC * DVB; e += 256) {
-      const int t = e / DVB, j = e - t * DVB;
-      sdOT[j * LC + t] = W[L::DO + (size_t)t * DV + jb * DVB + j];
-    }
-    for (int e = tid; e < BC * DK; e += 256) {
-      const int t = e / DK, i = e - t * DK;
-      sKt[t * LK + i] = W[L::KT + e];
-      sQgT[i * LC + t] = W[L::QG + e];
-      sYT[i * LC + t] = W[L::Y_ + e];
-    }
     __syncthreads();
+    // the previous chunk (the last iteration reloads the current one: no branch)
+    sb_load<DK, DV, NK4, NV4, NC4>(a, ci - 1 >= c0 ? ci - 1 : ci, h, jb, tid, rq, rk, ry, ra, ro, rg);
     // dR = A_qk^T dO + K_tail dS'  [BC][DVB]
-    for (int t = wv; t < (BC / 16) * (DVB / 16); t += 4) {
+    for (int t = wv; t < (BC / 16) * (DVB / 16); t += SNT / 64) {
       const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
       f32x4 acc = mma_lds<float, BC>(zero4(), sAqkT + 16 * tm * LC, LC, sdOT + 16 * tn * LC, LC);
       acc = mma_lds<float, DK>(acc, sKt + 16 * tm * LK, LK, sdST + 16 * tn * LK, LK);
@@ -331,20 +446,20 @@ __global__ __launch_bounds__(256) void bwd_state_bwd_kernel(BwdArgs a) {
     }
     __syncthreads();
     // dS <- Q_g^T dO + Diag(gamma_C) dS' - Y^T dR  [DK][DVB]; each lane owns its entries
-    for (int t = wv; t < (DK / 16) * (DVB / 16); t += 4) {
+    for (int t = wv; t < (DK / 16) * (DVB / 16); t += SNT / 64) {
       const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
       const f32x4 acc = mma_lds<float, BC>(zero4(), sQgT + 16 * tm * LC, LC, sdOT + 16 * tn * LC, LC);
       const f32x4 acy = mma_lds<float, BC>(zero4(), sYT + 16 * tm * LC, LC, sdRT + 16 * tn * LC, LC);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int i = 16 * tm + 4 * g + q, j = 16 * tn + m;
-        sdST[j * LK + i] = acc[q] + W[L::GC + i] * sdST[j * LK + i] - acy[q];
+        sdST[j * LK + i] = acc[q] + sGC[i] * sdST[j * LK + i] - acy[q];
       }
     }
     __syncthreads();
   }
   if (a.dS0)
-    for (int e = tid; e < DK * DVB; e += 256) {
+    for (int e = tid; e < DK * DVB; e += SNT) {
       const int i = e / DVB, j = e - i * DVB;
       a.dS0[(size_t)nh * DK * DV + (size_t)i * DV + jb * DVB + j] = sdST[j * LK + i];
     }
@@ -421,6 +536,7 @@ __global__ __launch_bounds__(256) void bwd_final_kernel(BwdArgs a) {
 template <int M, int N, int K, bool TA, bool TB>
 hipError_t bmm(const BwdArgs& a, size_t stride, size_t oa, int lda, size_t ob, int ldb, size_t oc,
                int ldc, float alpha, long long od, int mask, int diag, int items, hipStream_t st) {
+  static_assert(M % 16 == 0 && N % 16 == 0 && K % 32 == 0, "bmm tile shapes");
   BmmArgs p;
   p.A = a.ws + oa;
   p.B = a.ws + ob;
@@ -432,18 +548,7 @@ hipError_t bmm(const BwdArgs& a, size_t stride, size_t oa, int lda, size_t ob, i
   p.mask = mask; p.diag = diag;
   p.H = a.H;
   p.total = a.tab ? a.total : nullptr;
-  constexpr size_t lds = (size_t)(M + N) * (K + 4) * 4;
-  static bool attr[64] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64 || !attr[dev]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bmm_kernel<M, N, K, TA, TB>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64) attr[dev] = true;
-  }
-  hipLaunchKernelGGL((bmm_kernel<M, N, K, TA, TB>), dim3(items), dim3(512), lds, st, p);
+  hipLaunchKernelGGL((bmm_kernel<M, N, K, TA, TB>), dim3(items), dim3(512), 0, st, p);
   return hipGetLastError();
 }
 
@@ -486,8 +591,9 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   // sequential passes (with no chunks they only pass dS_T through to dS0)
   {
     constexpr int LK = DK + 4, LC = BC + 4;
-    const size_t lf = (size_t)(DVB * LK + BC * LK + DK * LC + DVB * LC) * 4;
-    const size_t lb = (size_t)(DVB * LK + BC * LC + DVB * LC + BC * LK + 2 * DK * LC + DVB * LC) * 4;
+    constexpr int LV = DVB + 4;
+    const size_t lf = (size_t)(DVB * LK + BC * LK + DK * LC + DVB * LC + BC * LV + DK) * 4;
+    const size_t lb = (size_t)(DVB * LK + BC * LC + DVB * LC + BC * LK + 2 * DK * LC + DVB * LC + DK) * 4;
     static bool attr[64] = {};
     int dev = 0;
     GDR2_CK(hipGetDevice(&dev));
@@ -497,9 +603,9 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
       if (dev >= 0 && dev < 64) attr[dev] = true;
     }
     const dim3 gs((unsigned)((size_t)a.N * a.H * (DV / DVB)));
-    hipLaunchKernelGGL((bwd_state_fwd_kernel<DK, DV>), gs, dim3(256), lf, st, a);
+    hipLaunchKernelGGL((bwd_state_fwd_kernel<DK, DV>), gs, dim3(SNT), lf, st, a);
     GDR2_CK(hipGetLastError());
-    hipLaunchKernelGGL((bwd_state_bwd_kernel<DK, DV>), gs, dim3(256), lb, st, a);
+    hipLaunchKernelGGL((bwd_state_bwd_kernel<DK, DV>), gs, dim3(SNT), lb, st, a);
     GDR2_CK(hipGetLastError());
   }
   if (items <= 0) return hipSuccess;
