@@ -30,6 +30,8 @@
 // The batched products run on fp32 MFMA (16x16x4) from LDS-staged operands.
 #include <hip/hip_runtime.h>
 
+#include <initializer_list>
+
 #include "gdr2_device.h"
 #include "gdr2_internal.h"
 
@@ -132,67 +134,71 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 
 // ---- batched fp32 products over items -----------------------------------------------
 // C[m][n] = alpha * sum_k opA(m, k) opB(k, n) (+ D[m][n]), entries with
-// n > m + diag zeroed when `mask`.  opA(m, k) = TA ? A[k][m] : A[m][k] (rows of
-// lda floats); opB(k, n) = TB ? B[n][k] : B[k][n] (rows of ldb floats).  Both
-// operands are staged into LDS K-contiguous ([M][K] and [N][K]).
-struct BmmArgs {
-  const float* A;
-  const float* B;
-  float* C;
-  const float* D;
-  size_t stride;  // floats between consecutive items (all operands)
-  int lda, ldb, ldc;
+// n > m + diag zeroed when `mask`.  opA(m, k) = A[k][m] when transposed, else
+// A[m][k] (rows of lda floats); opB(k, n) = B[n][k] when transposed, else
+// B[k][n].  Both operands are staged into LDS K-contiguous ([M][K] and [N][K]),
+// K in slices of 32 with 16-byte loads (the item blocks, their offsets and the
+// row strides are multiples of 4 floats), so several workgroups share a CU.
+// Several independent products over the items in one launch (blockIdx.y
+// selects the product; none reads another's output).  M is the chunk (64);
+// N and K (multiples of 32) and the transposes come from the job table.
+struct BmmJob {
+  size_t oa, ob, oc;  // operand offsets inside an item's block (floats)
+  long long od;       // addend offset, or -1
+  int lda, ldb, ldc, N, K, ta, tb, mask, diag;
   float alpha;
-  int mask, diag;
+};
+constexpr int MAXJOBS = 6;
+struct BmmJobs {
+  BmmJob j[MAXJOBS];
+  float* ws;
+  size_t stride;
   int H;
-  const int32_t* total;  // packed sequences: valid chunks; else nullptr
+  const int32_t* total;
 };
 
-template <int M, int N, int K, bool TA, bool TB>
-__global__ __launch_bounds__(512) void bmm_kernel(BmmArgs p) {
-  // K is staged in slices of KC so that several workgroups fit on a CU; every
-  // global access is a 16-byte load (the item blocks, their offsets and the
-  // row strides are multiples of 4 floats)
-  constexpr int KC = 32, LD = KC + 4;
-  constexpr int TM = M / 16, TN = N / 16, TPW = (TM * TN + 7) / 8;
+__global__ __launch_bounds__(512) void bmm_multi_kernel(BmmJobs P) {
+  constexpr int M = BC, KC = 32, LD = KC + 4, TM = M / 16, NMAX = 128, TPW = TM * (NMAX / 16) / 8;
   __shared__ __align__(16) float As[M * LD];
-  __shared__ __align__(16) float Bs[N * LD];
+  __shared__ __align__(16) float Bs[NMAX * LD];
   const int item = blockIdx.x;
-  if (p.total && item / p.H >= *p.total) return;
-  const size_t base = (size_t)item * p.stride;
-  const float* A = p.A + base;
-  const float* B = p.B + base;
+  if (P.total && item / P.H >= *P.total) return;
+  const BmmJob& J = P.j[blockIdx.y];
+  const int N = J.N, K = J.K, TN = N / 16;
+  const size_t base = (size_t)item * P.stride;
+  const float* A = P.ws + base + J.oa;
+  const float* B = P.ws + base + J.ob;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
   f32x4 acc[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) acc[u] = zero4();
   for (int kc = 0; kc < K; kc += KC) {
     for (int e = tid; e < M * KC / 4; e += 512) {
-      if constexpr (TA) {  // As[m][k] = A[k][m]: 4 consecutive m per load
+      if (J.ta) {
         const int k = e / (M / 4), m4 = e - k * (M / 4);
-        const float4 x = *reinterpret_cast<const float4*>(A + (size_t)(kc + k) * p.lda + 4 * m4);
-        As[(4 * m4 + 0) * LD + k] = x.x;
-        As[(4 * m4 + 1) * LD + k] = x.y;
-        As[(4 * m4 + 2) * LD + k] = x.z;
-        As[(4 * m4 + 3) * LD + k] = x.w;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(A + (size_t)(kc + k) * J.lda + 4 * m4);
+        As[(4 * m4 + 0) * LD + k] = x[0];
+        As[(4 * m4 + 1) * LD + k] = x[1];
+        As[(4 * m4 + 2) * LD + k] = x[2];
+        As[(4 * m4 + 3) * LD + k] = x[3];
       } else {
         const int mm = e / (KC / 4), k4 = e - mm * (KC / 4);
-        *reinterpret_cast<float4*>(As + mm * LD + 4 * k4) =
-            *reinterpret_cast<const float4*>(A + (size_t)mm * p.lda + kc + 4 * k4);
+        *reinterpret_cast<f32x4*>(As + mm * LD + 4 * k4) =
+            *reinterpret_cast<const f32x4*>(A + (size_t)mm * J.lda + kc + 4 * k4);
       }
     }
     for (int e = tid; e < N * KC / 4; e += 512) {
-      if constexpr (TB) {
+      if (J.tb) {
         const int n = e / (KC / 4), k4 = e - n * (KC / 4);
-        *reinterpret_cast<float4*>(Bs + n * LD + 4 * k4) =
-            *reinterpret_cast<const float4*>(B + (size_t)n * p.ldb + kc + 4 * k4);
-      } else {  // Bs[n][k] = B[k][n]: 4 consecutive n per load
+        *reinterpret_cast<f32x4*>(Bs + n * LD + 4 * k4) =
+            *reinterpret_cast<const f32x4*>(B + (size_t)n * J.ldb + kc + 4 * k4);
+      } else {
         const int k = e / (N / 4), n4 = e - k * (N / 4);
-        const float4 x = *reinterpret_cast<const float4*>(B + (size_t)(kc + k) * p.ldb + 4 * n4);
-        Bs[(4 * n4 + 0) * LD + k] = x.x;
-        Bs[(4 * n4 + 1) * LD + k] = x.y;
-        Bs[(4 * n4 + 2) * LD + k] = x.z;
-        Bs[(4 * n4 + 3) * LD + k] = x.w;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(B + (size_t)(kc + k) * J.ldb + 4 * n4);
+        Bs[(4 * n4 + 0) * LD + k] = x[0];
+        Bs[(4 * n4 + 1) * LD + k] = x[1];
+        Bs[(4 * n4 + 2) * LD + k] = x[2];
+        Bs[(4 * n4 + 3) * LD + k] = x[3];
       }
     }
     __syncthreads();
@@ -206,8 +212,8 @@ __global__ __launch_bounds__(512) void bmm_kernel(BmmArgs p) {
     }
     __syncthreads();
   }
-  float* C = p.C + base;
-  const float* D = p.D ? p.D + base : nullptr;
+  float* C = P.ws + base + J.oc;
+  const float* D = J.od >= 0 ? P.ws + base + J.od : nullptr;
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const int t = wv + 8 * u;
@@ -216,10 +222,10 @@ __global__ __launch_bounds__(512) void bmm_kernel(BmmArgs p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int row = 16 * tm + 4 * g + q, col = 16 * tn + m;
-      float v = p.alpha * acc[u][q];
-      if (D) v += D[(size_t)row * p.ldc + col];
-      if (p.mask && col > row + p.diag) v = 0.f;
-      C[(size_t)row * p.ldc + col] = v;
+      float v = J.alpha * acc[u][q];
+      if (D) v += D[(size_t)row * J.ldc + col];
+      if (J.mask && col > row + J.diag) v = 0.f;
+      C[(size_t)row * J.ldc + col] = v;
     }
   }
 }
@@ -240,7 +246,17 @@ __global__ __launch_bounds__(64) void bwd_inverse_kernel(BwdArgs a) {
     if (r == j) {
       x = 1.f;
     } else if (r > j) {
-      for (int s = j; s < r; ++s) x = fmaf(-sT[r][s], sX[s][j], x);
+      // four independent partial sums shorten the dependent FMA chain
+      float x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
+      int s = j;
+      for (; s + 3 < r; s += 4) {
+        x0 = fmaf(-sT[r][s], sX[s][j], x0);
+        x1 = fmaf(-sT[r][s + 1], sX[s + 1][j], x1);
+        x2 = fmaf(-sT[r][s + 2], sX[s + 2][j], x2);
+        x3 = fmaf(-sT[r][s + 3], sX[s + 3][j], x3);
+      }
+      for (; s < r; ++s) x0 = fmaf(-sT[r][s], sX[s][j], x0);
+      x = (x0 + x1) + (x2 + x3);
     }
     sX[r][j] = x;
   }
@@ -475,7 +491,7 @@ __global__ __launch_bounds__(256) void bwd_final_kernel(BwdArgs a) {
   if (!bwd_locate(a, ci, row0, clen)) return;
   const float* W = a.ws + (size_t)item * L::FLOATS;
   __shared__ float sdG[BC][DK];
-  __shared__ float sGm[DK], sGC[DK];
+  __shared__ float sGm[DK], sGC[DK], sRS[DK];
   const int tid = threadIdx.x;
   const size_t kr = (size_t)a.H * DK, vr = (size_t)a.H * DV;
   if (tid < DK) {
@@ -517,12 +533,28 @@ __global__ __launch_bounds__(256) void bwd_final_kernel(BwdArgs a) {
       a.dw[x] = dz * load1<BF16>(a.v, x);
     }
   }
+  // gamma_C enters the state update (Diag(gamma_C) S): the row sums of
+  // dS' * S, one wavefront per row with coalesced loads
+  {
+    const int wv = tid >> 6, lane = tid & 63;
+    for (int i0 = 4 * wv; i0 < DK; i0 += 16) {  // four rows per step: more loads in flight
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        for (int j = lane; j < DV; j += 64)
+          acc[rr] = fmaf(W[L::DSP + (size_t)(i0 + rr) * DV + j], W[L::S + (size_t)(i0 + rr) * DV + j], acc[rr]);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) acc[rr] += __shfl_xor(acc[rr], off);
+        if (lane == 0) sRS[i0 + rr] = acc[rr];
+      }
+    }
+  }
   __syncthreads();
   if (tid < DK) {
-    // gamma_C enters the state update (Diag(gamma_C) S) and every K_tail row
-    float acc = 0.f;
-    for (int j = 0; j < DV; ++j) acc = fmaf(W[L::DSP + (size_t)tid * DV + j], W[L::S + (size_t)tid * DV + j], acc);
-    acc *= W[L::GC + tid];
+    // ... and every K_tail row
+    float acc = sRS[tid] * W[L::GC + tid];
     for (int r = 0; r < BC; ++r) acc = fmaf(W[L::DKT + r * DK + tid], W[L::KT + r * DK + tid], acc);
     // dg_r = sum over rows r' >= r of dG (the decay of row r enters every
     // later cumulative sum of the chunk, and gamma_C is the last one)
@@ -533,22 +565,29 @@ __global__ __launch_bounds__(256) void bwd_final_kernel(BwdArgs a) {
   }
 }
 
-template <int M, int N, int K, bool TA, bool TB>
-hipError_t bmm(const BwdArgs& a, size_t stride, size_t oa, int lda, size_t ob, int ldb, size_t oc,
-               int ldc, float alpha, long long od, int mask, int diag, int items, hipStream_t st) {
-  static_assert(M % 16 == 0 && N % 16 == 0 && K % 32 == 0, "bmm tile shapes");
-  BmmArgs p;
-  p.A = a.ws + oa;
-  p.B = a.ws + ob;
-  p.C = a.ws + oc;
-  p.D = od >= 0 ? a.ws + od : nullptr;
-  p.stride = stride;
-  p.lda = lda; p.ldb = ldb; p.ldc = ldc;
-  p.alpha = alpha;
-  p.mask = mask; p.diag = diag;
-  p.H = a.H;
-  p.total = a.tab ? a.total : nullptr;
-  hipLaunchKernelGGL((bmm_kernel<M, N, K, TA, TB>), dim3(items), dim3(512), 0, st, p);
+BmmJob job(size_t oa, int lda, bool ta, size_t ob, int ldb, bool tb, size_t oc, int ldc, int N, int K,
+           float alpha = 1.f, long long od = -1, int mask = 0, int diag = 0) {
+  BmmJob j;
+  j.oa = oa; j.ob = ob; j.oc = oc; j.od = od;
+  j.lda = lda; j.ldb = ldb; j.ldc = ldc; j.N = N; j.K = K;
+  j.ta = ta; j.tb = tb; j.mask = mask; j.diag = diag;
+  j.alpha = alpha;
+  return j;
+}
+
+hipError_t bmm_group(const BwdArgs& a, size_t stride, int items, std::initializer_list<BmmJob> jobs,
+                     hipStream_t st) {
+  BmmJobs P{};
+  int n = 0;
+  for (const BmmJob& j : jobs) {
+    if (n >= MAXJOBS || j.N % 32 || j.K % 32 || j.N > 128) return hipErrorInvalidValue;
+    P.j[n++] = j;
+  }
+  P.ws = a.ws;
+  P.stride = stride;
+  P.H = a.H;
+  P.total = a.tab ? a.total : nullptr;
+  hipLaunchKernelGGL(bmm_multi_kernel, dim3(items, n), dim3(512), 0, st, P);
   return hipGetLastError();
 }
 
@@ -580,13 +619,13 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   }
   GDR2_CK(hipGetLastError());
   // T = tril(E' K'^T, -1), A_qk = tril(Q' K'^T, 0)  (centred factors cancel)
-  GDR2_CK((bmm<BC, BC, DK, false, true>(a, F, L::EP, DK, L::KP, DK, L::T, BC, 1.f, -1, 1, -1, items, st)));
-  GDR2_CK((bmm<BC, BC, DK, false, true>(a, F, L::QP, DK, L::KP, DK, L::AQK, BC, 1.f, -1, 1, 0, items, st)));
+  GDR2_CK(bmm_group(a, F, items, {job(L::EP, DK, 0, L::KP, DK, 1, L::T, BC, BC, DK, 1.f, -1, 1, -1),
+                                  job(L::QP, DK, 0, L::KP, DK, 1, L::AQK, BC, BC, DK, 1.f, -1, 1, 0)}, st));
   hipLaunchKernelGGL((bwd_inverse_kernel<DK, DV>), gi, dim3(64), 0, st, a);
   GDR2_CK(hipGetLastError());
   // Y = A E, U = A Z
-  GDR2_CK((bmm<BC, DK, BC, false, false>(a, F, L::A, BC, L::EB, DK, L::Y_, DK, 1.f, -1, 0, 0, items, st)));
-  GDR2_CK((bmm<BC, DV, BC, false, false>(a, F, L::A, BC, L::Z, DV, L::U, DV, 1.f, -1, 0, 0, items, st)));
+  GDR2_CK(bmm_group(a, F, items, {job(L::A, BC, 0, L::EB, DK, 0, L::Y_, DK, DK, BC),
+                                  job(L::A, BC, 0, L::Z, DV, 0, L::U, DV, DV, BC)}, st));
   }
   // sequential passes (with no chunks they only pass dS_T through to dS0)
   {
@@ -609,24 +648,27 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     GDR2_CK(hipGetLastError());
   }
   if (items <= 0) return hipSuccess;
-  // output paths
-  GDR2_CK((bmm<BC, DV, DK, false, false>(a, F, L::Y_, DK, L::S, DV, L::R, DV, -1.f, (long long)L::U, 0, 0, items, st)));
-  GDR2_CK((bmm<BC, DK, DV, false, true>(a, F, L::DO, DV, L::S, DV, L::DQG, DK, 1.f, -1, 0, 0, items, st)));
-  GDR2_CK((bmm<BC, DK, DV, false, true>(a, F, L::DR, DV, L::S, DV, L::DY, DK, -1.f, -1, 0, 0, items, st)));
-  GDR2_CK((bmm<BC, DK, DV, false, true>(a, F, L::R, DV, L::DSP, DV, L::DKT, DK, 1.f, -1, 0, 0, items, st)));
-  GDR2_CK((bmm<BC, BC, DV, false, true>(a, F, L::DO, DV, L::R, DV, L::DAQK, BC, 1.f, -1, 1, 0, items, st)));
-  // gate-aware WY inverse path (Eqs. 64-65)
-  GDR2_CK((bmm<BC, BC, DV, false, true>(a, F, L::DR, DV, L::Z, DV, L::DA, BC, 1.f, -1, 0, 0, items, st)));
-  GDR2_CK((bmm<BC, BC, DK, false, true>(a, F, L::DY, DK, L::EB, DK, L::DA, BC, 1.f, (long long)L::DA, 0, 0, items, st)));
-  GDR2_CK((bmm<BC, DV, BC, true, false>(a, F, L::A, BC, L::DR, DV, L::DZ, DV, 1.f, -1, 0, 0, items, st)));
-  GDR2_CK((bmm<BC, DK, BC, true, false>(a, F, L::A, BC, L::DY, DK, L::X1, DK, 1.f, -1, 0, 0, items, st)));
-  GDR2_CK((bmm<BC, BC, BC, true, false>(a, F, L::A, BC, L::DA, BC, L::WM, BC, 1.f, -1, 0, 0, items, st)));
-  GDR2_CK((bmm<BC, BC, BC, false, true>(a, F, L::WM, BC, L::A, BC, L::DT, BC, -1.f, -1, 1, -1, items, st)));
-  // decay-weighted products through the centred factors
-  GDR2_CK((bmm<BC, DK, BC, false, false>(a, F, L::DT, BC, L::KP, DK, L::P1, DK, 1.f, -1, 0, 0, items, st)));
-  GDR2_CK((bmm<BC, DK, BC, true, false>(a, F, L::DT, BC, L::EP, DK, L::P2, DK, 1.f, -1, 0, 0, items, st)));
-  GDR2_CK((bmm<BC, DK, BC, true, false>(a, F, L::DAQK, BC, L::QP, DK, L::P3, DK, 1.f, -1, 0, 0, items, st)));
-  GDR2_CK((bmm<BC, DK, BC, false, false>(a, F, L::DAQK, BC, L::KP, DK, L::P4, DK, 1.f, -1, 0, 0, items, st)));
+  // output paths: R = U - Y S, dQ_g = dO S^T, dY = -dR S^T
+  GDR2_CK(bmm_group(a, F, items, {job(L::Y_, DK, 0, L::S, DV, 0, L::R, DV, DV, DK, -1.f, (long long)L::U),
+                                  job(L::DO, DV, 0, L::S, DV, 1, L::DQG, DK, DK, DV),
+                                  job(L::DR, DV, 0, L::S, DV, 1, L::DY, DK, DK, DV, -1.f)}, st));
+  // dK_tail = R dS'^T, dA_qk = tril(dO R^T), dA = dR Z^T (first half of Eqs. 64-65),
+  // dZ = A^T dR, A^T dY
+  GDR2_CK(bmm_group(a, F, items, {job(L::R, DV, 0, L::DSP, DV, 1, L::DKT, DK, DK, DV),
+                                  job(L::DO, DV, 0, L::R, DV, 1, L::DAQK, BC, BC, DV, 1.f, -1, 1, 0),
+                                  job(L::DR, DV, 0, L::Z, DV, 1, L::DA, BC, BC, DV),
+                                  job(L::A, BC, 1, L::DR, DV, 0, L::DZ, DV, DV, BC),
+                                  job(L::A, BC, 1, L::DY, DK, 0, L::X1, DK, DK, BC)}, st));
+  // dA += dY E^T (second half), and the A_qk paths through the centred factors
+  GDR2_CK(bmm_group(a, F, items, {job(L::DY, DK, 0, L::EB, DK, 1, L::DA, BC, BC, DK, 1.f, (long long)L::DA),
+                                  job(L::DAQK, BC, 1, L::QP, DK, 0, L::P3, DK, DK, BC),
+                                  job(L::DAQK, BC, 0, L::KP, DK, 0, L::P4, DK, DK, BC)}, st));
+  // dT = -tril(A^T dA A^T, -1)
+  GDR2_CK(bmm_group(a, F, items, {job(L::A, BC, 1, L::DA, BC, 0, L::WM, BC, BC, BC)}, st));
+  GDR2_CK(bmm_group(a, F, items, {job(L::WM, BC, 0, L::A, BC, 1, L::DT, BC, BC, BC, -1.f, -1, 1, -1)}, st));
+  // the T paths through the centred factors
+  GDR2_CK(bmm_group(a, F, items, {job(L::DT, BC, 0, L::KP, DK, 0, L::P1, DK, DK, BC),
+                                  job(L::DT, BC, 1, L::EP, DK, 0, L::P2, DK, DK, BC)}, st));
   if (a.in_bf16) hipLaunchKernelGGL((bwd_final_kernel<DK, DV, true>), gi, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((bwd_final_kernel<DK, DV, false>), gi, dim3(256), 0, st, a);
   return hipGetLastError();
