@@ -69,7 +69,13 @@ typedef enum {
  * holds one record per (64-token chunk, head) of the intra-chunk results the
  * state pass consumes: 2*4*(dk/32) KiB + 2*(dk/16) KiB + 6 KiB + (dv/16)*2 KiB
  * + 4*dk bytes each (70.5 KiB at dk = dv = 128), for B*ceil(T/64) chunks, or
- * ceil(T/64) + num_seqs chunks with packed sequences plus small tables.  With
+ * ceil(T/64) + num_seqs chunks with packed sequences plus small tables.
+ * Without cu_seqlens, when B*H is below 64 and dk == dv, each sequence's
+ * chunks are split into P segments (a power of two, at most 16, with
+ * B*H*P <= 256 and at least 16 chunks per segment; then P is reduced to
+ * ceil(ceil(T/64) / ceil(ceil(T/64) / P))), and the workspace adds, from the
+ * next 256-byte boundary after the records, B*P*H*dk*(dk + dv) fp32 values
+ * for the segments' transfer matrices and end states.  With
  * GDR2_F32 only packed calls with more than one sequence need workspace (their
  * longest-first order).  The workspace is scratch: its contents on entry do
  * not matter and are not meaningful on return.
@@ -99,8 +105,12 @@ size_t gdr2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  * Execution: with GDR2_BF16, an intra-chunk kernel handles every (chunk,
  * head) in parallel (decay scan, chunk matrix, WY inverse and its products)
  * and writes a record per chunk to the workspace; a state kernel then walks
- * each sequence's chunks in order.  With GDR2_F32 one kernel walks the chunks
- * and does both.
+ * each sequence's chunks in order.  When the chains are split into segments
+ * (see gdr2_chunk_fwd_workspace_bytes), a transfer pass first gives every
+ * segment its affine map of the entry state (Eq. 23 composed over its
+ * chunks), an fp32 scan chains the maps, and the state pass then walks all
+ * segments at once from their true entry states.  With GDR2_F32 one kernel
+ * walks the chunks and does both.
  *
  * Precision: the cumulative log-decay, the WY solve's diagonal blocks, every
  * accumulation and the state are fp32.  With in_dtype = GDR2_F32 every

@@ -34,15 +34,20 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // Workspace of the two-pass forward (16-bit inputs): for packed sequences the
 // longest-first order, the chunk base per sequence and the chunk table, then
 // one record per (chunk, head).  Packed sequences add at most one partial
-// chunk each, so ceil(T/64) + N chunks bound the record count.
+// chunk each, so ceil(T/64) + N chunks bound the record count.  Equal-length
+// sequences with few (sequence, head) chains split each chain into P segments
+// of segc chunks; they add the segments' transfer matrices and end states.
 struct Layout {
-  size_t order, cbase, tab, rec, total;
+  size_t order, cbase, tab, rec, phi, ex, total;
   long long cap;  // chunks with a record
+  int P, segc;
 };
 Layout two_pass_layout(int B, int T, int H, int dk, int dv, int num_seqs) {
   Layout l{};
   const long long nc = ((long long)T + 63) / 64;
   size_t off = 0;
+  l.P = 1;
+  l.segc = (int)nc;
   if (num_seqs > 0) {
     l.cap = nc + num_seqs;
     l.order = off;
@@ -53,9 +58,21 @@ Layout two_pass_layout(int B, int T, int H, int dk, int dv, int num_seqs) {
     off += align256(2 * sizeof(int32_t) * (size_t)l.cap);
   } else {
     l.cap = (long long)B * nc;
+    const int P = gdr2::segments_for((long long)B * H, nc, dk, dv);
+    if (P > 1) {
+      l.segc = (int)((nc + P - 1) / P);
+      l.P = (int)((nc + l.segc - 1) / l.segc);
+    }
   }
   l.rec = off;
-  l.total = off + (size_t)l.cap * (size_t)H * gdr2::record_bytes(dk, dv);
+  off += (size_t)l.cap * (size_t)H * gdr2::record_bytes(dk, dv);
+  if (l.P > 1) {
+    const size_t chains = (size_t)B * l.P * H;
+    l.phi = align256(off);
+    l.ex = l.phi + chains * dk * dk * sizeof(float);
+    off = l.ex + chains * dk * dv * sizeof(float);
+  }
+  l.total = off;
   return l;
 }
 
@@ -99,6 +116,9 @@ gdr2_status two_pass(const char* fn, const void* q, const void* k, const void* v
   sa.S0 = S0; sa.o = o; sa.ST = S_T; sa.cu = cu_seqlens; sa.order = order; sa.cbase = cbase;
   sa.cap = (int)l.cap;
   sa.N = N; sa.T = T; sa.H = Hv; sa.DV = dv;
+  sa.P = l.P; sa.segc = l.segc;
+  sa.phi = l.P > 1 ? reinterpret_cast<float*>(ws + l.phi) : nullptr;
+  sa.ex = l.P > 1 ? reinterpret_cast<float*>(ws + l.ex) : nullptr;
   const hipError_t e = gdr2::launch_two_pass(ia, sa, dk, dv, st);
   if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "%s: launch: %s", fn, hipGetErrorString(e));
   return GDR2_OK;

@@ -111,8 +111,22 @@ struct StateArgs {
   const int32_t* cbase;   // packed sequences: first chunk per sequence; else nullptr
   int cap;                // records available (chunks); chunks past it are skipped
   int N, T, H, DV;
+  // Split chains (equal-length sequences, dk == dv, P > 1): the chunks of
+  // each sequence form P segments of segc chunks (the last may be shorter).
+  // A transfer pass gives every segment but the last its transfer matrix
+  // (phi, fp32 [N][P][H][dk][dk]) and its end state from a zero start (ex,
+  // fp32 [N][P][H][dk][dv]; segment 0 starts from S0 instead).  A scan turns
+  // ex[s] into the true end state of segment s, and the state pass then runs
+  // every segment at once, segment s > 0 starting from ex[s - 1].
+  int P, segc;
+  float* phi;
+  float* ex;
 };
 hipError_t launch_two_pass(const IntraArgs& ia, const StateArgs& sa, int dk, int dv, hipStream_t stream);
+// Segments per sequence for the state pass of `chains` equal-length
+// (sequence, value head) chains of nc chunks each (1 = no split).  It depends
+// on the shape only, so the workspace size can be computed without a device.
+int segments_for(long long chains, long long nc, int dk, int dv);
 
 // ---- backward ------------------------------------------------------------------------
 // One fp32 workspace block of bwd_item_bytes() per (chunk, head) item, item =

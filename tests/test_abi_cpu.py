@@ -102,6 +102,18 @@ def test_workspace_query():
     assert q(1, 100, 16, 128, 128, 64, G.GDR2_BF16) == \
         a256(64 * 4) + a256(65 * 4) + a256(cap * 8) + cap * 16 * rec
     assert q(2, 64, 3, 32, 64, 0, G.GDR2_BF16) == 2 * 1 * 3 * rec_bytes(32, 64)
+    # few long chains: P segments per sequence add transfer matrices and end states
+    # (B*P*H*dk*(dk+dv) fp32 from the next 256-byte boundary)
+    assert q(1, 32768, 16, 128, 128, 0, G.GDR2_BF16) == a256(512 * 16 * rec) + 16 * 16 * 128 * 256 * 4
+    assert q(1, 32768, 32, 128, 128, 0, G.GDR2_BF16) == a256(512 * 32 * rec) + 8 * 32 * 128 * 256 * 4
+    assert q(1, 32768, 1, 64, 64, 0, G.GDR2_BF16) == a256(512 * rec_bytes(64, 64)) + 16 * 64 * 128 * 4
+    # 1000 chunks, 16 segments of 63 chunks (the last 55)
+    assert q(2, 64000, 4, 32, 32, 0, G.GDR2_BF16) == \
+        a256(2 * 1000 * 4 * rec_bytes(32, 32)) + 2 * 16 * 4 * 32 * 64 * 4
+    # no split: enough chains, too short, dk != dv, or packed sequences
+    assert q(4, 32768, 16, 128, 128, 0, G.GDR2_BF16) == 4 * 512 * 16 * rec
+    assert q(1, 1024, 16, 128, 128, 0, G.GDR2_BF16) == 16 * 16 * rec
+    assert q(1, 32768, 16, 64, 128, 0, G.GDR2_BF16) == 512 * 16 * rec_bytes(64, 128)
     assert q(1, 100, 16, 48, 128, 64, G.GDR2_BF16) == 0
     assert q(0, 100, 16, 128, 128, 64, G.GDR2_BF16) == 0
 
