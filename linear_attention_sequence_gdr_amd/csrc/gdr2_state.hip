@@ -378,29 +378,33 @@ __global__ __launch_bounds__(64 * (DK / 16)) void scan_kernel(StateArgs p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) e[q] = E[(size_t)(16 * wv + 4 * g + q) * DV + j0 + m];
   };
+  // Every step issues the same loads (step indices past the last are clamped
+  // to it and their values unused), so the count of loads in flight is the
+  // same on every path and each step waits only for its own slot.
+  if (last < 1) return;
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d)
-    if (1 + d <= last) fetch(1 + d, fa[d], ea[d]);
+  for (int d = 0; d < DEPTH; ++d) fetch(min(1 + d, last), fa[d], ea[d]);
   __syncthreads();
   for (int s0 = 1; s0 <= last; s0 += DEPTH) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int s = s0 + d;
-      if (s > last) break;
-      float4 xb[NK];
+      if (s <= last) {
+        float4 xb[NK];
 #pragma unroll
-      for (int kb = 0; kb < NK; ++kb) xb[kb] = *reinterpret_cast<const float4*>(&XT[m][16 * kb + 4 * g]);
-      f32x4 part[4] = {ea[d], zero4(), zero4(), zero4()};
+        for (int kb = 0; kb < NK; ++kb) xb[kb] = *reinterpret_cast<const float4*>(&XT[m][16 * kb + 4 * g]);
+        f32x4 part[4] = {ea[d], zero4(), zero4(), zero4()};
 #pragma unroll
-      for (int kb = 0; kb < NK; ++kb) part[kb & 3] = mma16(fa[d][kb], xb[kb], part[kb & 3]);
-      const f32x4 acc = (part[0] + part[1]) + (part[2] + part[3]);
-      if (s + DEPTH <= last) fetch(s + DEPTH, fa[d], ea[d]);  // refill the slot just used
-      __syncthreads();  // every wavefront has read X_{s-1}
-      float* E = ex_of(s);
-      *reinterpret_cast<float4*>(&XT[m][16 * wv + 4 * g]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        for (int kb = 0; kb < NK; ++kb) part[kb & 3] = mma16(fa[d][kb], xb[kb], part[kb & 3]);
+        const f32x4 acc = (part[0] + part[1]) + (part[2] + part[3]);
+        __syncthreads();  // every wavefront has read X_{s-1}
+        float* E = ex_of(s);
+        *reinterpret_cast<float4*>(&XT[m][16 * wv + 4 * g]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) E[(size_t)(16 * wv + 4 * g + q) * DV + j0 + m] = acc[q];
-      __syncthreads();
+        for (int q = 0; q < 4; ++q) E[(size_t)(16 * wv + 4 * g + q) * DV + j0 + m] = acc[q];
+        __syncthreads();
+      }
+      fetch(min(s + DEPTH, last), fa[d], ea[d]);  // refill the slot just used
     }
   }
 }
