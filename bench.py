@@ -32,7 +32,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_chunk_fwd_b4_t4096_h16_d128.json")
+TRAFFIC_FILE = {"fwd": os.path.join(ROOT, "profiles", "traffic_chunk_fwd_b4_t4096_h16_d128.json"),
+                "long": os.path.join(ROOT, "profiles", "traffic_chunk_fwd_b1_t32768_h16_d128.json")}
 
 
 def fwd_algorithmic(B, T, H, dk, dv, in_bytes=2, C=64):
@@ -60,12 +61,13 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(*kernel_keys):
+def load_traffic(workload, *kernel_keys):
     """HBM bytes per launch of one kernel (summed over several kernels that
-    one call launches), from the rocprofv3 counter runs committed under
+    one call launches) of a workload ("fwd": the B4 T4096 calls, "long": the
+    long sequence), from the rocprofv3 counter runs committed under
     profiles/, only when they were taken on the current kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILE[workload]) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -80,13 +82,33 @@ def load_traffic(*kernel_keys):
     return total
 
 
+def load_call_traffic(workload, once_key, *prefixes):
+    """HBM bytes of one call that launches several kernels, some of them many
+    times: the traffic of every dispatch of the kernels whose names start with
+    one of `prefixes`, over the number of calls (the dispatches of `once_key`,
+    a kernel launched once per call)."""
+    try:
+        with open(TRAFFIC_FILE[workload]) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    ks = t.get("kernels", {})
+    if once_key not in ks:
+        return None
+    total = sum((k["fetch_bytes"] + k["write_bytes"]) * k["dispatches"]
+                for name, k in ks.items() if name.startswith(prefixes))
+    return total / ks[once_key]["dispatches"]
+
+
 def _counter_rows(path):
     import csv
     with open(path, newline="") as f:
         return list(csv.DictReader(f))
 
 
-def write_traffic(fetch_csv, write_csv, copy_mib, command):
+def write_traffic(fetch_csv, write_csv, copy_mib, command, workload="fwd"):
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
     dispatch) into HBM bytes per launch for every libgdr2 kernel.  Each counter
     is scaled by what it reads for the calibration copy (torch.neg over
@@ -107,15 +129,15 @@ def write_traffic(fetch_csv, write_csv, copy_mib, command):
             if "gdr2::" not in name:
                 continue
             # the kernel with its template arguments: variants are kept apart
-            key = name.split("gdr2::", 1)[1].split("(", 1)[0]
+            key = name.split("gdr2::", 1)[1].replace("(anonymous namespace)::", "").split("(", 1)[0]
             per.setdefault(key, {}).setdefault(counter, []).append(
                 float(r["Counter_Value"]) * 1024 / factor)
     for key, d in per.items():
         f, w = d.get("FETCH_SIZE", [0.0]), d.get("WRITE_SIZE", [0.0])
         out["kernels"][key] = {"fetch_bytes": sum(f) / len(f), "write_bytes": sum(w) / len(w),
                                "dispatches": len(f)}
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as fo:
+    os.makedirs(os.path.dirname(TRAFFIC_FILE[workload]), exist_ok=True)
+    with open(TRAFFIC_FILE[workload], "w") as fo:
         json.dump(out, fo, indent=1)
     print(json.dumps(out))
 
@@ -170,6 +192,47 @@ def cpu_baseline(wl, budget_s=12.0):
                       f"once per {H} heads"}
 
 
+def long_leg(args, torch, G, I, dev):
+    """One long sequence per head: B1 T32768 H16 d128 bf16 with S0, 16 chains of
+    512 chunks, each split into 16 segments (transfer pass, fp32 scan, state
+    pass)."""
+    lw = I.config(3)
+    ins = [x.to(dev) for x in (lw.q, lw.k, lw.v, lw.log_alpha, lw.b, lw.w)]
+    S0 = lw.S0.to(dev)
+    o = torch.empty((lw.B, lw.T, lw.H, lw.dv), dtype=torch.bfloat16, device=dev)
+    ST = torch.empty_like(S0)
+    ws = torch.empty(max(1, G.gdr2_chunk_fwd_workspace_bytes(lw.B, lw.T, lw.H, lw.dk, lw.dv, 0,
+                                                             G.GDR2_BF16)),
+                     dtype=torch.uint8, device=dev)
+    fwd = lambda: G.gdr2_chunk_fwd(*ins, S0, None, o=o, S_T=ST, workspace=ws)
+    ms = time_events(fwd, args.steps, args.warmup, torch)
+    byts, flops = fwd_algorithmic(lw.B, lw.T, lw.H, lw.dk, lw.dv)
+    byts += lw.B * lw.H * lw.dk * lw.dv * 4  # S0 read
+    gbs = byts / (ms * 1e-3) / 1e9
+    return {"workload": "gdr2_chunk_fwd B1 T32768 H16 dk=dv=128 bf16, b in [0,2], decay shift -4, "
+                        "S0 ~ N(0, 0.1): 16 chains of 512 chunks, each split into 16 segments "
+                        "(transfer pass, fp32 scan, state pass)",
+            "steps": args.steps, "ms_per_call": ms, "tokens_per_s": lw.B * lw.T / (ms * 1e-3),
+            "tflops": flops / (ms * 1e-3) / 1e12, "alg_bytes": byts,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": load_traffic("long", "intra_kernel<128, 128, true, false>",
+                                                 "state_kernel<128, 128, 8, 4, true, 2>",
+                                                 "scan_kernel<128, 128>",
+                                                 "state_kernel<128, 128, 4, 4, false, 2>")}}
+
+
+def calibration_copy(args, torch, dev):
+    if args.calibrate_copy:
+        n = args.calibrate_copy * 1024 * 1024 // 4
+        src_t = torch.randn(n, device=dev)
+        dst_t = torch.empty_like(src_t)
+        for _ in range(3):
+            torch.neg(src_t, out=dst_t)
+        torch.cuda.synchronize()
+        del src_t, dst_t
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,9 +247,15 @@ def main():
                          "rocprofv3 --pmc counter_collection.csv files")
     ap.add_argument("--traffic-command", default="",
                     help="the command that produced the counter files (recorded)")
+    ap.add_argument("--traffic-workload", choices=("fwd", "long"), default="fwd",
+                    help="which workload's kernels the counter files cover")
+    ap.add_argument("--long", choices=("on", "off", "only"), default="on",
+                    help="the long-sequence forward: in the line (on), left out (off), or "
+                         "alone in a line of its own (only; profiling its kernels apart)")
     args = ap.parse_args()
     if args.traffic:
-        write_traffic(args.traffic[0], args.traffic[1], args.calibrate_copy, args.traffic_command)
+        write_traffic(args.traffic[0], args.traffic[1], args.calibrate_copy, args.traffic_command,
+                      args.traffic_workload)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the Gated Delta Rule-2 path here has no multi-GPU "
@@ -202,6 +271,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     G.library()
+    if args.long == "only":
+        leg = long_leg(args, torch, G, I, dev)
+        calibration_copy(args, torch, dev)
+        print(json.dumps({"long_sequence": leg, "source_hash": source_hash()}), flush=True)
+        return
 
     # ---- forward: B4 T4096 H16 d128 bf16 ------------------------------------------------
     wl = I.config(1)
@@ -219,7 +293,7 @@ def main():
     gbs = byts / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
     # one gdr2_chunk_fwd call = the intra-chunk pass + the state pass
-    traffic = load_traffic("intra_kernel<128, 128, true, false>", "state_kernel<128, 128, 2, 4>")
+    traffic = load_traffic("fwd", "intra_kernel<128, 128, true, false>", "state_kernel<128, 128, 2, 4, false, 1>")
 
     # ---- the same forward from the block's projections (fused gate prologue) ------
     bl = I.make_block(B, T, H, H, dk, dv, seed=7)
@@ -282,14 +356,7 @@ def main():
     egbs = ebytes / (ems * 1e-3) / 1e9
     del z_epi, y_epi
 
-    if args.calibrate_copy:
-        n = args.calibrate_copy * 1024 * 1024 // 4
-        src_t = torch.randn(n, device=dev)
-        dst_t = torch.empty_like(src_t)
-        for _ in range(3):
-            torch.neg(src_t, out=dst_t)
-        torch.cuda.synchronize()
-        del src_t, dst_t
+    calibration_copy(args, torch, dev)
 
     cpu = None
     if not args.no_cpu:
@@ -324,33 +391,36 @@ def main():
                    "steps": args.decode_steps, "us_per_step": dms * 1e3, "alg_bytes": dbytes,
                    "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
-                                "traffic": load_traffic("decode_kernel<128, 128, false>")},
+                                "traffic": load_traffic("fwd", "decode_kernel<128, 128, false>")},
                    "norm_gate_fused": {
                        "entry": "gdr2_decode_step_norm_gate (RMSNorm over dv + SiLU gate in the store)",
                        "us_per_step": gms * 1e3, "alg_bytes": gbytes,
                        "roofline": {"bound": "hbm", "achieved": ggbs, "peak": HBM_PEAK_GBS,
                                     "unit": "GB/s", "frac": ggbs / HBM_PEAK_GBS,
-                                    "traffic": load_traffic("decode_norm_gate_kernel<128, 128, false>")}}},
+                                    "traffic": load_traffic("fwd", "decode_norm_gate_kernel<128, 128, false>")}}},
         "backward": {"workload": "gdr2_chunk_bwd B4 T4096 H16 dk=dv=128 bf16 inputs, fp32 gradients "
                                  "of q, k, v, log_alpha, b, w and S0",
                      "steps": bwd_steps, "ms_per_call": bwms, "tokens_per_s": tokens / (bwms * 1e-3),
                      "alg_bytes": bw_bytes,
                      "roofline": {"bound": "hbm", "achieved": bw_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                  "frac": bw_gbs / HBM_PEAK_GBS, "traffic": None}},
+                                  "frac": bw_gbs / HBM_PEAK_GBS,
+                                  "traffic": load_call_traffic("fwd", "bwd_state_bwd_kernel<128, 128>",
+                                                               "bwd_", "bmm_multi_kernel")}},
+        "long_sequence": long_leg(args, torch, G, I, dev) if args.long == "on" else None,
         "block": {"workload": "gdr2_chunk_fwd_block B4 T4096 H16 Hv16 dk=dv=128 from projections: "
                               "q/k L2 norm, Eq. 12 decay from bf16 W_f x, sigmoid gates (flags 7)",
                   "steps": args.steps, "ms_per_call": bms, "tokens_per_s": tokens / (bms * 1e-3),
                   "alg_bytes": byts,
                   "roofline": {"bound": "hbm", "achieved": bgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                "frac": bgbs / HBM_PEAK_GBS,
-                               "traffic": load_traffic("intra_kernel<128, 128, true, true>",
-                                                       "state_kernel<128, 128, 2, 4>")}},
+                               "traffic": load_traffic("fwd", "intra_kernel<128, 128, true, true>",
+                                                       "state_kernel<128, 128, 2, 4, false, 1>")}},
         "epilogue": {"workload": "gdr2_norm_gate over the forward's o [B4 T4096 H16 128] bf16, "
                                  "RMSNorm per head (group 128) x weight x silu(z), into y",
                      "steps": args.steps, "us_per_call": ems * 1e3, "alg_bytes": ebytes,
                      "roofline": {"bound": "hbm", "achieved": egbs, "peak": HBM_PEAK_GBS,
                                   "unit": "GB/s", "frac": egbs / HBM_PEAK_GBS,
-                                  "traffic": load_traffic("norm_gate_kernel<1, true>")}},
+                                  "traffic": load_traffic("fwd", "norm_gate_kernel<1, true>")}},
         "cpu_baseline": cpu,
         "source_hash": source_hash(),
     }
