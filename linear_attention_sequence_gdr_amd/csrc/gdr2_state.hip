@@ -455,14 +455,19 @@ static hipError_t launch_state_dv(const StateArgs& a, hipStream_t stream) {
       return hipErrorInvalidValue;
     }
   }
-  // Two compute wavefronts (32 value channels) and four producers per
-  // workgroup; with too few (sequence, head) chains to cover the CUs that
-  // way, blocks of 16 channels double the number of workgroups.
+  // With at least one (sequence, head) chain per CU the pass is bound by the
+  // total record staging, so one workgroup per chain covers every value
+  // channel (two column tiles per wavefront) and stages each record once.
+  // With fewer chains the chain length binds: two compute wavefronts (32
+  // value channels) and four producers per workgroup, or blocks of 16
+  // channels when even that leaves CUs idle.
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  if ((long long)a.N * a.H * (DV / 32) < cus) return launch_state1<DK, DV, 1, 4, false>(a, stream);
+  const long long chains = (long long)a.N * a.H;
+  if (chains >= cus) return launch_state1<DK, DV, DV / 32, 4, false, 2>(a, stream);
+  if (chains * (DV / 32) < cus) return launch_state1<DK, DV, 1, 4, false>(a, stream);
   return launch_state1<DK, DV, 2, 4, false>(a, stream);
 }
 

@@ -91,6 +91,18 @@ def test_bf16_shapes_ragged(dk, dv, H):
     check(o, ST, ro, rS, True, f"bf16 dk={dk} dv={dv} H={H}")
 
 
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64), (32, 32)])
+def test_bf16_many_chains(dk, dv):
+    """256 (sequence, head) chains, one per CU: the state pass runs one
+    workgroup per chain over every value channel (two column tiles per
+    wavefront); 150 tokens leave a ragged last chunk."""
+    wl = I.make_forward(32, 150, 8, dk, dv, dtype=torch.bfloat16, decay_shift=-2.0,
+                        s0_std=0.1, seed=23)
+    o, ST = run_fwd(wl)
+    ro, rS = oracle_fwd(wl)
+    check(o, ST, ro, rS, True, f"256 chains dk={dk} dv={dv}")
+
+
 def test_bf16_negative_eigenvalues_fp32_decay():
     wl = I.make_forward(1, 700, 4, 128, 128, dtype=torch.bfloat16, la_dtype=torch.float32,
                         decay_shift=-4.0, erase_scale=2.0, s0_std=0.1, seed=13)
