@@ -274,7 +274,10 @@ __device__ __forceinline__ void sf_load(const BwdArgs& a, int ci, int h, int jb,
   for (int u = 0; u < NK4; ++u) {
     const int e4 = tid + SNT * u;
     ry[u] = reinterpret_cast<const f32x4*>(Wn + L::Y_)[e4];
-    rk[u] = reinterpret_cast<const f32x4*>(Wn + L::KT)[e4];
+    // K_tail is stored transposed: lane = token row, so that the transposing
+    // LDS stores of a wavefront hit 64 consecutive words
+    const int t = e4 % BC, i = 4 * (e4 / BC);
+    rk[u] = *reinterpret_cast<const f32x4*>(Wn + L::KT + (size_t)t * DK + i);
   }
 #pragma unroll
   for (int u = 0; u < NV4; ++u) {
@@ -290,19 +293,24 @@ __device__ __forceinline__ void sb_load(const BwdArgs& a, int ci, int h, int jb,
                                         f32x4 (&ra)[NC4], f32x4 (&ro)[NV4], f32x4& rg) {
   typedef BwdLayout<DK, DV> L;
   const float* Wn = a.ws + ((size_t)ci * a.H + h) * L::FLOATS;
+  // Q_g, Y, A_qk and dO are stored transposed: lane = token row, so that the
+  // transposing LDS stores of a wavefront hit 64 consecutive words
 #pragma unroll
   for (int u = 0; u < NK4; ++u) {
-    const int e4 = tid + SNT * u;
-    rq[u] = reinterpret_cast<const f32x4*>(Wn + L::QG)[e4];
+    const int e4 = tid + SNT * u, t = e4 % BC, i = 4 * (e4 / BC);
+    rq[u] = *reinterpret_cast<const f32x4*>(Wn + L::QG + (size_t)t * DK + i);
     rk[u] = reinterpret_cast<const f32x4*>(Wn + L::KT)[e4];
-    ry[u] = reinterpret_cast<const f32x4*>(Wn + L::Y_)[e4];
+    ry[u] = *reinterpret_cast<const f32x4*>(Wn + L::Y_ + (size_t)t * DK + i);
   }
 #pragma unroll
-  for (int u = 0; u < NC4; ++u) ra[u] = reinterpret_cast<const f32x4*>(Wn + L::AQK)[tid + SNT * u];
+  for (int u = 0; u < NC4; ++u) {
+    const int e4 = tid + SNT * u, t = e4 % BC, r = 4 * (e4 / BC);
+    ra[u] = *reinterpret_cast<const f32x4*>(Wn + L::AQK + (size_t)t * BC + r);
+  }
 #pragma unroll
   for (int u = 0; u < NV4; ++u) {
-    const int e4 = tid + SNT * u, t = e4 / (DVB / 4), c4 = e4 - t * (DVB / 4);
-    ro[u] = *reinterpret_cast<const f32x4*>(Wn + L::DO + (size_t)t * DV + jb * DVB + 4 * c4);
+    const int e4 = tid + SNT * u, t = e4 % BC, j = 4 * (e4 / BC);
+    ro[u] = *reinterpret_cast<const f32x4*>(Wn + L::DO + (size_t)t * DV + jb * DVB + j);
   }
   if (tid < DK / 4) rg = reinterpret_cast<const f32x4*>(Wn + L::GC)[tid];
 }
@@ -342,10 +350,11 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
     for (int u = 0; u < NK4; ++u) {
       const int e4 = tid + SNT * u, r = e4 / (DK / 4), i = 4 * (e4 - r * (DK / 4));
       *reinterpret_cast<f32x4*>(sY + r * LK + i) = ry[u];
-      sKtT[(i + 0) * LC + r] = rk[u][0];
-      sKtT[(i + 1) * LC + r] = rk[u][1];
-      sKtT[(i + 2) * LC + r] = rk[u][2];
-      sKtT[(i + 3) * LC + r] = rk[u][3];
+      const int t = e4 % BC, it = 4 * (e4 / BC);  // K_tail: lane = token row (sf_load)
+      sKtT[(it + 0) * LC + t] = rk[u][0];
+      sKtT[(it + 1) * LC + t] = rk[u][1];
+      sKtT[(it + 2) * LC + t] = rk[u][2];
+      sKtT[(it + 3) * LC + t] = rk[u][3];
     }
 #pragma unroll
     for (int u = 0; u < NV4; ++u) {
@@ -413,8 +422,12 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
     float* W = a.ws + ((size_t)ci * a.H + h) * L::FLOATS;
 #pragma unroll
     for (int u = 0; u < NK4; ++u) {
-      const int e4 = tid + SNT * u, t = e4 / (DK / 4), i = 4 * (e4 - t * (DK / 4));
-      *reinterpret_cast<f32x4*>(sKt + t * LK + i) = rk[u];
+      const int e4 = tid + SNT * u;
+      {
+        const int t = e4 / (DK / 4), i = 4 * (e4 - t * (DK / 4));
+        *reinterpret_cast<f32x4*>(sKt + t * LK + i) = rk[u];
+      }
+      const int t = e4 % BC, i = 4 * (e4 / BC);  // lane = token row (sb_load)
       sQgT[(i + 0) * LC + t] = rq[u][0];
       sQgT[(i + 1) * LC + t] = rq[u][1];
       sQgT[(i + 2) * LC + t] = rq[u][2];
@@ -426,7 +439,7 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < NC4; ++u) {  // A_qk[t][r..r+3] -> A_qk^T
-      const int e4 = tid + SNT * u, t = e4 / (BC / 4), r = 4 * (e4 - t * (BC / 4));
+      const int e4 = tid + SNT * u, t = e4 % BC, r = 4 * (e4 / BC);
       sAqkT[(r + 0) * LC + t] = ra[u][0];
       sAqkT[(r + 1) * LC + t] = ra[u][1];
       sAqkT[(r + 2) * LC + t] = ra[u][2];
@@ -434,7 +447,7 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < NV4; ++u) {  // dO[t][j..j+3] -> dO^T
-      const int e4 = tid + SNT * u, t = e4 / (DVB / 4), j = 4 * (e4 - t * (DVB / 4));
+      const int e4 = tid + SNT * u, t = e4 % BC, j = 4 * (e4 / BC);
       sdOT[(j + 0) * LC + t] = ro[u][0];
       sdOT[(j + 1) * LC + t] = ro[u][1];
       sdOT[(j + 2) * LC + t] = ro[u][2];

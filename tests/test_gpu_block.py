@@ -72,6 +72,22 @@ def test_block_all_steps(B, T, H, Hv, dk, dv, fdt, bs):
     check(o, ST, ro, rS, f"B{B} T{T} H{H} Hv{Hv} dk{dk} dv{dv} {fdt} b_scale {bs}")
 
 
+def test_block_grouped_heads_split_chains():
+    """Few long chains: 1 sequence x 4 value heads of 64 chunks takes the split
+    state pass (4 segments of 16 chunks per chain, a transfer pass and a scan)
+    behind the prologue and the key-head broadcast (2 key heads, groups of 2)."""
+    B, T, H, Hv, d = 1, 4096, 2, 4, 128
+    rec = 2 * 4 * (d // 32) * 1024 + 2 * (d // 16) * 1024 + 6 * 1024 + (d // 16) * 4 * 512 + 4 * d
+    plain = B * (T // 64) * Hv * rec
+    # the workspace holds P = 4 segments' transfer matrices and end states
+    assert G().gdr2_chunk_fwd_workspace_bytes(B, T, Hv, d, d, 0, G().GDR2_BF16) == \
+        (plain + 255) // 256 * 256 + B * 4 * Hv * d * 2 * d * 4
+    wl = I.make_block(B, T, H, Hv, d, d, s0_std=0.1, seed=45)
+    o, ST = run_block(wl, b_scale=2.0)
+    ro, rS = oracle_block(wl, b_scale=2.0)
+    check(o, ST, ro, rS, "grouped heads, split chains")
+
+
 @pytest.mark.parametrize("flags", [0, 1, 2, 4, 3, 6])
 def test_block_flag_subsets(flags):
     """Each prologue step alone and in pairs; steps that are off take the
