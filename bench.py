@@ -34,6 +34,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 TRAFFIC_FILE = {"fwd": os.path.join(ROOT, "profiles", "traffic_chunk_fwd_b4_t4096_h16_d128.json"),
                 "long": os.path.join(ROOT, "profiles", "traffic_chunk_fwd_b1_t32768_h16_d128.json")}
+MFMA_FILE = {"fwd": os.path.join(ROOT, "profiles", "mfma_chunk_fwd_b4_t4096_h16_d128.json"),
+             "long": os.path.join(ROOT, "profiles", "mfma_chunk_fwd_b1_t32768_h16_d128.json")}
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32")
 
 
 def fwd_algorithmic(B, T, H, dk, dv, in_bytes=2, C=64):
@@ -100,6 +103,47 @@ def load_call_traffic(workload, once_key, *prefixes):
     total = sum((k["fetch_bytes"] + k["write_bytes"]) * k["dispatches"]
                 for name, k in ks.items() if name.startswith(prefixes))
     return total / ks[once_key]["dispatches"]
+
+
+def write_mfma(csv_path, command, workload="fwd"):
+    """Per-kernel MFMA use from one rocprofv3 --pmc run of MfmaUtil (MFMA-busy
+    cycles over active cycles and SIMDs, in percent) and the MFMA op counters
+    (units of 512 flops): the average per dispatch of every libgdr2 kernel."""
+    per = {}
+    for r in _counter_rows(csv_path):
+        name = r["Kernel_Name"]
+        if "gdr2::" not in name:
+            continue
+        key = name.split("gdr2::", 1)[1].replace("(anonymous namespace)::", "").split("(", 1)[0]
+        per.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    out = {"source_hash": source_hash(), "command": command, "kernels": {}}
+    for key, d in per.items():
+        util = d.get("MfmaUtil", [0.0])
+        flops = {c: sum(d.get(c, [0.0])) / max(1, len(d.get(c, []))) * 512 for c in MFMA_COUNTERS}
+        out["kernels"][key] = {"mfma_util_pct": sum(util) / len(util), "dispatches": len(util),
+                               "mfma_flops": sum(flops.values()),
+                               "mfma_flops_by_type": {c.rsplit("_", 1)[1]: v for c, v in flops.items()}}
+    with open(MFMA_FILE[workload], "w") as fo:
+        json.dump(out, fo, indent=1)
+    print(json.dumps(out))
+
+
+def load_mfma(workload, *kernel_keys):
+    """MFMA-busy percent per kernel and the MFMA flops one call issues (summed
+    over kernel_keys), from the committed counter run, only when it was taken
+    on the current kernel sources."""
+    try:
+        with open(MFMA_FILE[workload]) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    ks = t.get("kernels", {})
+    if any(k not in ks for k in kernel_keys):
+        return None
+    return {"util_pct": {k: ks[k]["mfma_util_pct"] for k in kernel_keys},
+            "issued_flops": sum(ks[k]["mfma_flops"] for k in kernel_keys)}
 
 
 def _counter_rows(path):
@@ -209,17 +253,22 @@ def long_leg(args, torch, G, I, dev):
     byts, flops = fwd_algorithmic(lw.B, lw.T, lw.H, lw.dk, lw.dv)
     byts += lw.B * lw.H * lw.dk * lw.dv * 4  # S0 read
     gbs = byts / (ms * 1e-3) / 1e9
+    keys = ("intra_kernel<128, 128, true, false>", "state_kernel<128, 128, 8, 4, true, 2>",
+            "scan_kernel<128, 128>", "state_kernel<128, 128, 4, 4, false, 2>")
+    mf = load_mfma("long", *keys)
+    mfma = None
+    if mf:
+        issued = mf["issued_flops"] / (ms * 1e-3) / 1e12
+        mfma = {"issued_gflop_per_call": mf["issued_flops"] / 1e9, "issued_tflops": issued,
+                "issued_frac_of_bf16_peak": issued / BF16_PEAK_TFLOPS, "busy_pct": mf["util_pct"]}
     return {"workload": "gdr2_chunk_fwd B1 T32768 H16 dk=dv=128 bf16, b in [0,2], decay shift -4, "
                         "S0 ~ N(0, 0.1): 16 chains of 512 chunks, each split into 16 segments "
                         "(transfer pass, fp32 scan, state pass)",
             "steps": args.steps, "ms_per_call": ms, "tokens_per_s": lw.B * lw.T / (ms * 1e-3),
-            "tflops": flops / (ms * 1e-3) / 1e12, "alg_bytes": byts,
+            "tflops": flops / (ms * 1e-3) / 1e12, "alg_bytes": byts, "mfma": mfma,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": load_traffic("long", "intra_kernel<128, 128, true, false>",
-                                                 "state_kernel<128, 128, 8, 4, true, 2>",
-                                                 "scan_kernel<128, 128>",
-                                                 "state_kernel<128, 128, 4, 4, false, 2>")}}
+                         "traffic": load_traffic("long", *keys)}}
 
 
 def calibration_copy(args, torch, dev):
@@ -249,6 +298,9 @@ def main():
                     help="the command that produced the counter files (recorded)")
     ap.add_argument("--traffic-workload", choices=("fwd", "long"), default="fwd",
                     help="which workload's kernels the counter files cover")
+    ap.add_argument("--mfma", metavar="CSV",
+                    help="host only: write the per-kernel MFMA table from a rocprofv3 --pmc "
+                         "MfmaUtil + SQ_INSTS_VALU_MFMA_MOPS_* counter_collection.csv")
     ap.add_argument("--long", choices=("on", "off", "only"), default="on",
                     help="the long-sequence forward: in the line (on), left out (off), or "
                          "alone in a line of its own (only; profiling its kernels apart)")
@@ -256,6 +308,9 @@ def main():
     if args.traffic:
         write_traffic(args.traffic[0], args.traffic[1], args.calibrate_copy, args.traffic_command,
                       args.traffic_workload)
+        return
+    if args.mfma:
+        write_mfma(args.mfma, args.traffic_command, args.traffic_workload)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the Gated Delta Rule-2 path here has no multi-GPU "
@@ -294,6 +349,14 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     # one gdr2_chunk_fwd call = the intra-chunk pass + the state pass
     traffic = load_traffic("fwd", "intra_kernel<128, 128, true, false>", "state_kernel<128, 128, 2, 4, false, 1>")
+    mf = load_mfma("fwd", "intra_kernel<128, 128, true, false>", "state_kernel<128, 128, 2, 4, false, 1>")
+    mfma = None
+    if mf:
+        issued = mf["issued_flops"] / (ms * 1e-3) / 1e12
+        mfma = {"issued_gflop_per_call": mf["issued_flops"] / 1e9, "issued_tflops": issued,
+                "issued_frac_of_bf16_peak": issued / BF16_PEAK_TFLOPS,
+                "busy_pct": mf["util_pct"],
+                "counters": "rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_{F16,BF16,F32}"}
 
     # ---- the same forward from the block's projections (fused gate prologue) ------
     bl = I.make_block(B, T, H, H, dk, dv, seed=7)
@@ -382,6 +445,7 @@ def main():
         "fwd_tflops_frac_of_bf16_peak": tflops / BF16_PEAK_TFLOPS,
         "fwd_alg_bytes": byts,
         "fwd_alg_flops": flops,
+        "mfma": mfma,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS,
                      "traffic": traffic,
