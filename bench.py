@@ -314,7 +314,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the Gated Delta Rule-2 path here has no multi-GPU "
-              "mode (sequences and heads shard with no exchange; see DESIGN.md). Use --gpus 1.",
+              "mode (sequences and heads shard with no exchange between GPUs). Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
