@@ -26,6 +26,7 @@
 //   prep (elementwise) -> batched products T, A_qk -> forward substitution A
 //   -> Y, U -> sequential state pass (saves the entry state of every chunk)
 //   -> sequential reverse state-gradient pass (saves dS' and dR per chunk)
+//   (the state pass also saves R = U - Y S, which it forms anyway)
 //   -> batched products of the output and WY paths -> final elementwise pass.
 // The batched products run on fp32 MFMA (16x16x4) from LDS-staged operands.
 #include <hip/hip_runtime.h>
@@ -369,14 +370,16 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
     __syncthreads();
     // the next chunk (the last iteration reloads the current one: no branch)
     sf_load<DK, DV, NK4, NV4>(a, ci + 1 < c1 ? ci + 1 : ci, h, jb, tid, ry, rk, ru, rg);
-    // R = U - Y S  [BC][DVB]
+    // R = U - Y S  [BC][DVB], kept for the output paths as well
     for (int t = wv; t < (BC / 16) * (DVB / 16); t += SNT / 64) {
       const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
       const f32x4 acc = mma_lds<float, DK>(zero4(), sY + 16 * tm * LK, LK, sST + 16 * tn * LK, LK);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = 16 * tm + 4 * g + q, j = 16 * tn + m;
-        sRT[j * LC + r] = sU[r * LV + j] - acc[q];
+        const float rv = sU[r * LV + j] - acc[q];
+        sRT[j * LC + r] = rv;
+        W[L::R + (size_t)r * DV + jb * DVB + j] = rv;
       }
     }
     __syncthreads();
@@ -661,9 +664,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     GDR2_CK(hipGetLastError());
   }
   if (items <= 0) return hipSuccess;
-  // output paths: R = U - Y S, dQ_g = dO S^T, dY = -dR S^T
-  GDR2_CK(bmm_group(a, F, items, {job(L::Y_, DK, 0, L::S, DV, 0, L::R, DV, DV, DK, -1.f, (long long)L::U),
-                                  job(L::DO, DV, 0, L::S, DV, 1, L::DQG, DK, DK, DV),
+  // output paths (R = U - Y S comes from the state pass): dQ_g = dO S^T, dY = -dR S^T
+  GDR2_CK(bmm_group(a, F, items, {job(L::DO, DV, 0, L::S, DV, 1, L::DQG, DK, DK, DV),
                                   job(L::DR, DV, 0, L::S, DV, 1, L::DY, DK, DK, DV, -1.f)}, st));
   // dK_tail = R dS'^T, dA_qk = tril(dO R^T), dA = dR Z^T (first half of Eqs. 64-65),
   // dZ = A^T dR, A^T dY
