@@ -58,7 +58,14 @@ struct StateCfg {
   static constexpr size_t O_U = R::U;                        // then this block's U tiles
   static constexpr size_t STAGE = O_U + (size_t)UT * 4 * R::TILE;
   static constexpr int NCP = (int)(STAGE / 16);              // 16-byte pieces per stage
-  static constexpr size_t BYTES = 2 * STAGE;
+  // The state pass with one column tile per wavefront (QREG) keeps Q_g out of
+  // the stage: the compute wavefronts load its fragments into registers one
+  // chunk ahead, and the stage, compacted over the gap, is triple-buffered.
+  static constexpr bool QREG = !XF && CT == 1;
+  static constexpr size_t QGS = R::KT - R::QG;               // bytes of Q_g
+  static constexpr size_t SSTR = QREG ? STAGE - QGS : STAGE; // stage stride in LDS
+  static constexpr int NBUF = QREG ? 3 : 2;
+  static constexpr size_t BYTES = NBUF * SSTR;
   static_assert(BYTES <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -81,6 +88,10 @@ __device__ __forceinline__ f16x8 join8(const f32x4& a, const f32x4& b) {
 // (LDS-bound), so each wavefront may use a whole SIMD's registers.
 // XF = false: the state pass (whole chains, packed sequences, or every segment
 // of split chains); XF = true: the transfer pass of split chains.
+// vmcnt(n) with lgkmcnt and expcnt left open (gfx9 encoding: vmcnt bits
+// [3:0] and [15:14])
+constexpr unsigned vmcnt_enc(int n) { return 0x0f70u | (unsigned)(n & 15) | ((unsigned)(n >> 4) << 14); }
+
 template <int DK, int DV, int NWV, int NP, bool XF, int CT>
 __global__ __launch_bounds__(64 * (NWV + NP), 1) void state_kernel(StateArgs p) {
   typedef StateCfg<DK, DV, NWV, NP, CT, XF> Cfg;
@@ -175,13 +186,14 @@ __global__ __launch_bounds__(64 * (NWV + NP), 1) void state_kernel(StateArgs p) 
   // CT*NWV column tiles of U (contiguous in the record).  Pieces of 16 B go
   // straight from global memory to LDS, one 1 KiB run of 64 pieces per
   // wavefront instruction, so no registers hold them in flight.  The transfer
-  // pass skips the runs of Q_g and A_qk (it forms no output).  LDS keeps the
-  // record's offsets either way.
+  // pass skips the runs of Q_g and A_qk (it forms no output) and keeps the
+  // record's offsets in LDS; the QREG state pass skips Q_g and compacts.
   constexpr int RUNS = (NCP + 63) / 64;
   constexpr int NSH = (int)(R::U / 16);  // shared pieces
   static_assert(R::QG % 1024 == 0 && R::KT % 1024 == 0 && R::AQK % 1024 == 0 && R::GC % 1024 == 0,
                 "Q_g and A_qk must occupy whole runs");
-  constexpr int QR0 = XF ? (int)(R::QG / 1024) : 0, QRN = XF ? (int)((R::KT - R::QG) / 1024) : 0;
+  constexpr bool QREG = Cfg::QREG;
+  constexpr int QR0 = (XF || QREG) ? (int)(R::QG / 1024) : 0, QRN = (XF || QREG) ? (int)((R::KT - R::QG) / 1024) : 0;
   constexpr int AR0 = XF ? (int)(R::AQK / 1024) : 0, ARN = XF ? (int)((R::GC - R::AQK) / 1024) : 0;
   constexpr int npiece = NCP;
   constexpr int nrun = (npiece + 63) / 64 - QRN - ARN;
@@ -192,22 +204,49 @@ __global__ __launch_bounds__(64 * (NWV + NP), 1) void state_kernel(StateArgs p) 
   constexpr int KPW = (RUNS - QRN - ARN + NP - 1) / NP;  // runs per producer wavefront
   auto stage_async = [&](int c, int buf) {
     const char* rec = p.rec + ((size_t)(cb + c) * H + h) * R::BYTES;
-    unsigned char* dst = smem + (size_t)buf * Cfg::STAGE;
+    unsigned char* dst = smem + (size_t)buf * Cfg::SSTR;
 #pragma unroll
     for (int k = 0; k < KPW; ++k) {
-      const int r = k * NP + (wv - NWV);  // uniform across the wavefront
-      if (r >= nrun) break;
+      int r = k * NP + (wv - NWV);  // uniform across the wavefront
+      if constexpr (QREG) {
+        // every producer issues KPW loads (the last run repeated, same bytes),
+        // so "this chunk has landed" is a fixed vmcnt
+        r = min(r, nrun - 1);
+      } else {
+        if (r >= nrun) break;
+      }
       int run = r < QR0 ? r : r + QRN;  // index among the record's runs
       if (XF && run >= AR0) run += ARN;
       const int xp = run * 64 + lane;
       const char* src = rec + (size_t)xp * 16 + (xp < NSH ? 0 : uoff);
-      if (xp < npiece) lds_dma16(src, dst + (size_t)run * 1024);
+      if (xp < npiece) lds_dma16(src, dst + (size_t)(QREG ? r : run) * 1024);
     }
   };
 
   // Producers and compute wavefronts run separate loops with one barrier per
   // chunk each, so the producers' address arithmetic is not live in the
   // compute loop.
+  if (QREG && producer) {
+    // chunk c goes to buffer c % 3, two chunks ahead: during chunk c the
+    // producers fill the buffer chunk c - 1 used, then wait until chunk c + 1
+    // has landed (chunk c + 2's loads may stay in flight)
+    static_assert(KPW < 64, "vmcnt range");
+    const int pre = min(2, nch);
+    for (int c = 0; c < pre; ++c) stage_async(c, c);
+    if (pre == 2) __builtin_amdgcn_s_waitcnt(vmcnt_enc(KPW));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+      if (c + 2 < nch) {
+        stage_async(c + 2, (c + 2) % 3);
+        __builtin_amdgcn_s_waitcnt(vmcnt_enc(KPW));
+      } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
+      }
+      __syncthreads();
+    }
+    return;
+  }
   if (producer) {
     if (nch > 0) {
       stage_async(0, 0);
@@ -224,8 +263,24 @@ __global__ __launch_bounds__(64 * (NWV + NP), 1) void state_kernel(StateArgs p) 
   }
   __syncthreads();
 
+  // operand offsets in the stage (the QREG stage lacks Q_g's bytes)
+  constexpr size_t SHIFT = QREG ? Cfg::QGS : 0;
+  constexpr size_t OK = R::KT - SHIFT, OA = R::AQK - SHIFT, OG = Cfg::O_GC - SHIFT, OU = Cfg::O_U - SHIFT;
+  // QREG: Q_g fragments of the current chunk, loaded during the previous one
+  f16x8 qreg[QREG ? 4 : 1][QREG ? NKB : 1];
+  auto load_qg = [&](int c) {
+    if constexpr (QREG) {
+      const char* rq = p.rec + ((size_t)(cb + c) * H + h) * R::BYTES + R::QG;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          qreg[a][kb] = *reinterpret_cast<const f16x8*>(rq + ((size_t)(a * NKB + kb) * 64 + lane) * 16);
+    }
+  };
+  if (nch > 0) load_qg(0);
   for (int c = 0; c < nch; ++c) {
-    const unsigned char* L = smem + (size_t)(c & 1) * Cfg::STAGE;
+    const unsigned char* L = smem + (size_t)(c % Cfg::NBUF) * Cfg::SSTR;
     const int clen = min(CH, len - c * CH);
 
     // 16-bit state operand: fragment kb = tiles 2kb, 2kb+1 (dk rows 32kb + ...)
@@ -249,7 +304,7 @@ __global__ __launch_bounds__(64 * (NWV + NP), 1) void state_kernel(StateArgs p) 
         } else {
           // this tile's U columns, relative to the block's first
           const int jt = (col0 - Cfg::DVB * jb) / 16 + ct;
-          const f16x4 u = *reinterpret_cast<const f16x4*>(L + Cfg::O_U + ((size_t)(jt * 4 + a) * 64 + lane) * 8);
+          const f16x4 u = *reinterpret_cast<const f16x4*>(L + OU + ((size_t)(jt * 4 + a) * 64 + lane) * 8);
           Rt[ct][a] = f32x4{(float)u[0], (float)u[1], (float)u[2], (float)u[3]};
         }
         O[ct][a] = zero4();
@@ -262,11 +317,15 @@ __global__ __launch_bounds__(64 * (NWV + NP), 1) void state_kernel(StateArgs p) 
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) Rt[ct][a] = mma32(yf, sf[ct][kb], Rt[ct][a]);
         if constexpr (!XF) {
-          const f16x8 qf = *reinterpret_cast<const f16x8*>(L + R::QG + ((size_t)(a * NKB + kb) * 64 + lane) * 16);
+          f16x8 qf;
+          if constexpr (QREG) qf = qreg[QREG ? a : 0][QREG ? kb : 0];
+          else qf = *reinterpret_cast<const f16x8*>(L + R::QG + ((size_t)(a * NKB + kb) * 64 + lane) * 16);
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) O[ct][a] = mma32(sf[ct][kb], qf, O[ct][a]);
         }
       }
+    // the next chunk's Q_g fragments, in flight over the rest of this chunk
+    if (QREG && c + 1 < nch) load_qg(c + 1);
     f16x8 rf[CT][2];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
@@ -279,7 +338,7 @@ __global__ __launch_bounds__(64 * (NWV + NP), 1) void state_kernel(StateArgs p) 
       f16x8 af[6];
 #pragma unroll
       for (int f = 0; f < 6; ++f)
-        af[f] = *reinterpret_cast<const f16x8*>(L + R::AQK + ((size_t)f * 64 + lane) * 16);
+        af[f] = *reinterpret_cast<const f16x8*>(L + OA + ((size_t)f * 64 + lane) * 16);
       __bf16* orow = static_cast<__bf16*>(p.o) + ((size_t)(tok0 + (long long)c * CH) * H) * DV + olane;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
@@ -301,7 +360,7 @@ __global__ __launch_bounds__(64 * (NWV + NP), 1) void state_kernel(StateArgs p) 
     // ---- S <- Diag(gamma_C) S + K_tail^T R ----
 #pragma unroll
     for (int ib = 0; ib < NIB; ++ib) {
-      const float4 gc = *reinterpret_cast<const float4*>(L + Cfg::O_GC + (size_t)(16 * ib + 4 * g4) * 4);
+      const float4 gc = *reinterpret_cast<const float4*>(L + OG + (size_t)(16 * ib + 4 * g4) * 4);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         S[ct][ib][0] *= gc.x;
@@ -314,7 +373,7 @@ __global__ __launch_bounds__(64 * (NWV + NP), 1) void state_kernel(StateArgs p) 
     for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
       for (int ib = 0; ib < NIB; ++ib) {
-        const f16x8 kf = *reinterpret_cast<const f16x8*>(L + R::KT + ((size_t)(ib * 2 + pp) * 64 + lane) * 16);
+        const f16x8 kf = *reinterpret_cast<const f16x8*>(L + OK + ((size_t)(ib * 2 + pp) * 64 + lane) * 16);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) S[ct][ib] = mma32(kf, rf[ct][pp], S[ct][ib]);
       }
