@@ -199,6 +199,26 @@ def time_events(fn, steps, warmup, torch):
     return start.elapsed_time(stop) / steps     # ms per step
 
 
+def time_cold(fn, steps, torch, flush_mib=512):
+    """Median time of single calls that each follow a write of flush_mib MiB
+    of scratch, so the 256 MB last-level cache holds none of the call's
+    inputs; the events bracket the call only."""
+    scratch = torch.empty(flush_mib * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    times = []
+    for i in range(steps + 1):
+        scratch.fill_(float(i))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        if i:
+            times.append(a.elapsed_time(b))
+    del scratch
+    times.sort()
+    return times[len(times) // 2]
+
+
 def cpu_baseline(wl, budget_s=12.0):
     """The fp64 oracle as it stands, on whole (sequence, head) chains of the
     forward workload, using every host core it is allowed.  The sample is as
@@ -289,6 +309,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="leave out the cold-cache forward timing (keeps kernel-trace averages warm)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain copy of MIB MiB (for counter calibration)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -343,6 +365,7 @@ def main():
                      dtype=torch.uint8, device=dev)
     fwd = lambda: G.gdr2_chunk_fwd(*ins, None, None, o=o, S_T=ST, workspace=ws)
     ms = time_events(fwd, args.steps, args.warmup, torch)
+    cold_ms = None if args.no_cold else time_cold(fwd, max(5, min(args.steps, 20)), torch)
     byts, flops = fwd_algorithmic(B, T, H, dk, dv)
     tokens = B * T
     gbs = byts / (ms * 1e-3) / 1e9
@@ -446,6 +469,10 @@ def main():
         "fwd_alg_bytes": byts,
         "fwd_alg_flops": flops,
         "mfma": mfma,
+        "cold_mall": None if cold_ms is None else {
+            "ms_per_call": cold_ms, "tokens_per_s": tokens / (cold_ms * 1e-3),
+            "hbm_frac": byts / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "method": "median of single calls, each after a 512 MiB scratch write"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS,
                      "traffic": traffic,

@@ -20,9 +20,12 @@
 // operands in that same K order.  All products are 16x16x32 f16 MFMAs, fed by
 // fp32 accumulators or VALU-written initial values only.
 //
-// The workgroup copies the next chunk's record into the other half of a
-// double-buffered LDS stage (direct global-to-LDS loads) while the current
-// chunk is computed.
+// Producer wavefronts copy the records of the next chunks into LDS stage
+// buffers (direct global-to-LDS loads) while the current chunk is computed.
+// With one column tile per wavefront, the compute wavefronts take Q_g's
+// fragments straight into registers, one chunk ahead, and the stage, compacted
+// over that gap, is triple-buffered (two chunks ahead); otherwise the whole
+// record is double-buffered.
 //
 // Split chains.  Eq. 23 makes each chunk an affine map of the state,
 // S -> M S + K_tail^T U with M = Diag(gamma_C) - K_tail^T Y, so a run of chunks
