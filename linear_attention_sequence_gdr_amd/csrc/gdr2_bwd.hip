@@ -22,13 +22,14 @@
 // back per row afterwards, so no 1/gamma is formed.
 //
 // Layout: every intermediate of an item is an fp32 row-major block inside the
-// workspace (BwdLayout).  The work is a chain of simple kernels:
+// workspace (BwdLayout).  The work is a chain of kernels:
 //   prep (elementwise) -> batched products T, A_qk -> forward substitution A
 //   -> Y, U -> sequential state pass (saves the entry state of every chunk)
 //   -> sequential reverse state-gradient pass (saves dS' and dR per chunk)
 //   (the state pass also saves R = U - Y S, which it forms anyway)
-//   -> batched products of the output and WY paths -> final elementwise pass.
-// The batched products run on fp32 MFMA (16x16x4) from LDS-staged operands.
+//   -> one fused kernel per item for the output and WY paths and the
+//   gradients themselves (bwd_out_kernel).
+// Every product runs on fp32 MFMA (16x16x4) from LDS-staged operands.
 #include <hip/hip_runtime.h>
 
 #include <initializer_list>
@@ -497,85 +498,310 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
     }
 }
 
-// ---- final elementwise pass: dq, dk, db, dv, dw and the reverse cumsum for dg -------
+// ---- output and WY-gradient paths, fused per item ------------------------------------
+// One workgroup per item forms, from the item's fp32 blocks (dO, R, dR, Z, A,
+// E, Q', K', E', the decay G) and the states S and dS' on either side of the
+// chunk, every remaining product and the gradients themselves:
+//   phase 1  dQ_g = dO S^T, dY = -dR S^T, dK_tail = R dS'^T,
+//            dA_qk = tril(dO R^T), dA = dR Z^T, dZ = A^T dR (-> dv, dw), and
+//            the row sums of dS' * S; the value channels stream through LDS
+//            in slices of 32, the results stay in the accumulators;
+//   phase 2  dA += dY E^T, X = A^T dY, then dA_qk^T Q' and dA_qk K';
+//   phase 3  dT = -tril(A^T dA A^T, -1);
+//   phase 4  dT K' and dT^T E';
+//   final    dq, dk, db from the accumulators (the centred factors put back
+//            per element), and dg as the reverse cumulative sum over the
+//            chunk's rows.
+// Every operand is staged K-contiguous in LDS (rows of 4 floats padding, so a
+// 16-lane group's 16-byte reads hit distinct banks); the fp32 products run on
+// 16x16x4 MFMA.  Tiles of a [64][N] result go round the eight wavefronts
+// (tile t = wave + 8u, row tile t / (N/16), column tile t % (N/16)).
+template <int DK, int DV>
+struct OutCfg {
+  static constexpr int NT = 512, NWV = 8, KC = 32, LS = KC + 4, LA = BC + 4, LKP = DK + 4;
+  static constexpr int NKT = DK / 32;  // [64][DK] tiles per wavefront
+  static constexpr int NCT = 2;        // [64][64] tiles per wavefront
+  // LDS offsets in floats.  A^T lives through phase 3; region R1 is reused.
+  static constexpr int O_AT = 0, O_R1 = O_AT + BC * LA;
+  // phase 1: slices of dO, dR, R, Z [64][KC], of S, dS' [DK][KC], dR^T [KC][64]
+  static constexpr int O_O = O_R1, O_DR = O_O + BC * LS, O_R = O_DR + BC * LS,
+                       O_Z = O_R + BC * LS, O_S = O_Z + BC * LS, O_DS = O_S + DK * LS,
+                       O_DRT = O_DS + DK * LS, E1 = O_DRT + KC * LA;
+  // phase 2a: dY [64][DK], E [64][DK], dY^T [DK][64]
+  static constexpr int O_DY = O_R1, O_EB = O_DY + BC * LKP, O_DYT = O_EB + BC * LKP,
+                       E2 = O_DYT + DK * LA;
+  // phases 2b-4: K'^T [DK][64] stays; the rest rotates behind it
+  static constexpr int O_KPT = O_R1, O_X = O_KPT + DK * LA;
+  static constexpr int O_QPT = O_X, O_AQ = O_QPT + DK * LA, O_AQT = O_AQ + BC * LA,
+                       E3 = O_AQT + BC * LA;                                  // 2b
+  static constexpr int O_DAT = O_X, O_WM = O_DAT + BC * LA, O_A = O_WM + BC * LA,
+                       E4 = O_A + BC * LA;                                    // 3
+  static constexpr int O_EPT = O_X, O_DT = O_EPT + DK * LA, O_DTT = O_DT + BC * LA,
+                       E5 = O_DTT + BC * LA;                                  // 4
+  // final: the per-element dg terms [64][DK] twice
+  static constexpr int O_U = O_R1, O_V = O_U + BC * LKP, E6 = O_V + BC * LKP;
+  static constexpr int mx(int x, int y) { return x > y ? x : y; }
+  static constexpr int O_G31 = mx(mx(mx(E1, E2), mx(E3, E4)), mx(E5, E6));
+  static constexpr int O_GCL = O_G31 + DK, FLOATS = O_GCL + DK;
+  static constexpr size_t BYTES = (size_t)FLOATS * 4;
+  static_assert(BYTES <= 160 * 1024, "LDS budget exceeded");
+  static_assert(DV % KC == 0 && DK % 32 == 0, "output pass tiling");
+};
+
 template <int DK, int DV, bool BF16>
-__global__ __launch_bounds__(256) void bwd_final_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
   typedef BwdLayout<DK, DV> L;
+  typedef OutCfg<DK, DV> C;
+  constexpr int NT = C::NT, NWV = C::NWV, KC = C::KC, LS = C::LS, LA = C::LA, LKP = C::LKP;
+  constexpr int NKT = C::NKT, NCT = C::NCT, TNK = DK / 16;
   const int item = blockIdx.x, ci = item / a.H, h = item - ci * a.H;
   long long row0;
   int clen;
   if (!bwd_locate(a, ci, row0, clen)) return;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  float* sm = reinterpret_cast<float*>(smem_raw);
   const float* W = a.ws + (size_t)item * L::FLOATS;
-  __shared__ float sdG[BC][DK];
-  __shared__ float sGm[DK], sGC[DK], sRS[DK];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
   const size_t kr = (size_t)a.H * DK, vr = (size_t)a.H * DV;
+  float* sAT = sm + C::O_AT;
+  // A^T (lane = row of A: consecutive lanes write consecutive words)
+  for (int e = tid; e < BC * BC / 4; e += NT) {
+    const int k = e % BC, c4 = e / BC;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(W + L::A + k * BC + 4 * c4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sAT[(4 * c4 + q) * LA + k] = x[q];
+  }
   if (tid < DK) {
-    sGm[tid] = W[L::G + 31 * DK + tid];
-    sGC[tid] = W[L::G + 63 * DK + tid];
+    sm[C::O_G31 + tid] = W[L::G + 31 * DK + tid];
+    sm[C::O_GCL + tid] = W[L::G + (BC - 1) * DK + tid];
+  }
+
+  // ---- phase 1 ----
+  f32x4 aQ[NKT], aY[NKT], aK[NKT], aAQ[NCT], aA[NCT];
+#pragma unroll
+  for (int u = 0; u < NKT; ++u) aQ[u] = aY[u] = aK[u] = zero4();
+#pragma unroll
+  for (int u = 0; u < NCT; ++u) aAQ[u] = aA[u] = zero4();
+  float rs = 0.f;  // sum over the value channels of dS' * S, row tid
+  float *sO = sm + C::O_O, *sDR = sm + C::O_DR, *sR = sm + C::O_R, *sZ = sm + C::O_Z;
+  float *sS = sm + C::O_S, *sDS = sm + C::O_DS, *sDRT = sm + C::O_DRT;
+  for (int j0 = 0; j0 < DV; j0 += KC) {
+    for (int e = tid; e < BC * KC / 4; e += NT) {
+      const int s = e / (KC / 4), c4 = e - s * (KC / 4);
+      const size_t x = (size_t)s * DV + j0 + 4 * c4;
+      const int o = s * LS + 4 * c4;
+      *reinterpret_cast<f32x4*>(sO + o) = *reinterpret_cast<const f32x4*>(W + L::DO + x);
+      *reinterpret_cast<f32x4*>(sR + o) = *reinterpret_cast<const f32x4*>(W + L::R + x);
+      *reinterpret_cast<f32x4*>(sZ + o) = *reinterpret_cast<const f32x4*>(W + L::Z + x);
+      const f32x4 dr = *reinterpret_cast<const f32x4*>(W + L::DR + x);
+      *reinterpret_cast<f32x4*>(sDR + o) = dr;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sDRT[(4 * c4 + q) * LA + s] = dr[q];
+    }
+    for (int e = tid; e < DK * KC / 4; e += NT) {
+      const int i = e / (KC / 4), c4 = e - i * (KC / 4);
+      const size_t x = (size_t)i * DV + j0 + 4 * c4;
+      const int o = i * LS + 4 * c4;
+      *reinterpret_cast<f32x4*>(sS + o) = *reinterpret_cast<const f32x4*>(W + L::S + x);
+      *reinterpret_cast<f32x4*>(sDS + o) = *reinterpret_cast<const f32x4*>(W + L::DSP + x);
+    }
+    __syncthreads();
+    if (tid < DK)
+#pragma unroll 8
+      for (int c = 0; c < KC; ++c) rs = fmaf(sDS[tid * LS + c], sS[tid * LS + c], rs);
+#pragma unroll
+    for (int u = 0; u < NKT; ++u) {
+      const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
+      aQ[u] = mma_lds<float, KC>(aQ[u], sO + 16 * tm * LS, LS, sS + 16 * tn * LS, LS);
+      aY[u] = mma_lds<float, KC>(aY[u], sDR + 16 * tm * LS, LS, sS + 16 * tn * LS, LS);
+      aK[u] = mma_lds<float, KC>(aK[u], sR + 16 * tm * LS, LS, sDS + 16 * tn * LS, LS);
+    }
+#pragma unroll
+    for (int u = 0; u < NCT; ++u) {
+      const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
+      if (tn <= tm) aAQ[u] = mma_lds<float, KC>(aAQ[u], sO + 16 * tm * LS, LS, sR + 16 * tn * LS, LS);
+      aA[u] = mma_lds<float, KC>(aA[u], sDR + 16 * tm * LS, LS, sZ + 16 * tn * LS, LS);
+    }
+    {  // dZ = A^T dR over this slice's 32 value channels: one [16][16] tile per wavefront
+      const int tm = wv >> 1, tn = wv & 1;
+      const f32x4 z = mma_lds<float, BC>(zero4(), sAT + 16 * tm * LA, LA, sDRT + 16 * tn * LA, LA);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 16 * tm + 4 * g + q;
+        if (r < clen) {
+          const size_t x = (size_t)(row0 + r) * vr + (size_t)h * DV + j0 + 16 * tn + m;
+          a.dv[x] = z[q] * load1<BF16>(a.w, x);
+          a.dw[x] = z[q] * load1<BF16>(a.v, x);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- phase 2a: dA += dY E^T, X = A^T dY ----
+  float *sDY = sm + C::O_DY, *sEB = sm + C::O_EB, *sDYT = sm + C::O_DYT;
+#pragma unroll
+  for (int u = 0; u < NKT; ++u) {
+    const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 16 * tm + 4 * g + q, i = 16 * tn + m;
+      const float y = -aY[u][q];
+      sDY[r * LKP + i] = y;
+      sDYT[i * LA + r] = y;
+    }
+  }
+  for (int e = tid; e < BC * DK / 4; e += NT) {
+    const int s = e / (DK / 4), i4 = e - s * (DK / 4);
+    *reinterpret_cast<f32x4*>(sEB + s * LKP + 4 * i4) =
+        *reinterpret_cast<const f32x4*>(W + L::EB + s * DK + 4 * i4);
   }
   __syncthreads();
-  for (int e = tid; e < BC * DK; e += 256) {
-    const int r = e / DK, i = e - r * DK;
-    float qv = 0.f, kv = 0.f, bv = 0.f;
-    if (r < clen) {
-      const size_t x = (size_t)(row0 + r) * kr + (size_t)h * DK + i;
-      qv = load1<BF16>(a.q, x);
-      kv = load1<BF16>(a.k, x);
-      bv = load1<BF16>(a.b, x);
-    }
-    const float G = W[L::G + e], gam = expf(G);
-    const float e1 = expf(G - sGm[i]), e2 = expf(sGm[i] - G), ktail = expf(sGC[i] - G);
-    const float dq = W[L::DQG + e] * gam + W[L::P4 + e] * e1;
-    const float dkbar = (W[L::P2 + e] + W[L::P3 + e]) * e2;   // dK_bar / gamma
-    const float deg = W[L::X1 + e] * gam + W[L::P1 + e] * e1;  // dE * gamma
-    const float dkt = W[L::DKT + e];
-    const float dk = dkbar + deg * bv + dkt * ktail;
-    const float db = deg * kv;
-    sdG[r][i] = dq * qv - dkbar * kv + db * bv - dkt * (ktail * kv);
-    if (r < clen) {
-      const size_t x = (size_t)(row0 + r) * kr + (size_t)h * DK + i;
-      a.dq[x] = dq;
-      a.dk[x] = dk;
-      a.db[x] = db;
+  f32x4 aX[NKT];
+#pragma unroll
+  for (int u = 0; u < NCT; ++u) {
+    const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
+    aA[u] = mma_lds<float, DK>(aA[u], sDY + 16 * tm * LKP, LKP, sEB + 16 * tn * LKP, LKP);
+  }
+#pragma unroll
+  for (int u = 0; u < NKT; ++u) {
+    const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
+    aX[u] = mma_lds<float, BC>(zero4(), sAT + 16 * tm * LA, LA, sDYT + 16 * tn * LA, LA);
+  }
+  __syncthreads();
+
+  // ---- phase 2b: dA_qk^T Q' and dA_qk K' ----
+  float *sKPT = sm + C::O_KPT, *sQPT = sm + C::O_QPT, *sAQ = sm + C::O_AQ, *sAQT = sm + C::O_AQT;
+#pragma unroll
+  for (int u = 0; u < NCT; ++u) {
+    const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 16 * tm + 4 * g + q, c = 16 * tn + m;
+      const float v = (tn <= tm && c <= r) ? aAQ[u][q] : 0.f;
+      sAQ[r * LA + c] = v;
+      sAQT[c * LA + r] = v;
     }
   }
-  for (int e = tid; e < BC * DV; e += 256) {
-    const int r = e / DV, j = e - r * DV;
-    if (r < clen) {
-      const size_t x = (size_t)(row0 + r) * vr + (size_t)h * DV + j;
-      const float dz = W[L::DZ + e];
-      a.dv[x] = dz * load1<BF16>(a.w, x);
-      a.dw[x] = dz * load1<BF16>(a.v, x);
+  for (int e = tid; e < BC * DK / 4; e += NT) {  // lane = token row
+    const int s = e % BC, i4 = e / BC;
+    const f32x4 qp = *reinterpret_cast<const f32x4*>(W + L::QP + s * DK + 4 * i4);
+    const f32x4 kp = *reinterpret_cast<const f32x4*>(W + L::KP + s * DK + 4 * i4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      sQPT[(4 * i4 + q) * LA + s] = qp[q];
+      sKPT[(4 * i4 + q) * LA + s] = kp[q];
     }
   }
-  // gamma_C enters the state update (Diag(gamma_C) S): the row sums of
-  // dS' * S, one wavefront per row with coalesced loads
-  {
-    const int wv = tid >> 6, lane = tid & 63;
-    for (int i0 = 4 * wv; i0 < DK; i0 += 16) {  // four rows per step: more loads in flight
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  f32x4 aP3[NKT], aP4[NKT];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        for (int j = lane; j < DV; j += 64)
-          acc[rr] = fmaf(W[L::DSP + (size_t)(i0 + rr) * DV + j], W[L::S + (size_t)(i0 + rr) * DV + j], acc[rr]);
+  for (int u = 0; u < NKT; ++u) {
+    const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
+    aP3[u] = mma_lds<float, BC>(zero4(), sAQT + 16 * tm * LA, LA, sQPT + 16 * tn * LA, LA);
+    aP4[u] = mma_lds<float, BC>(zero4(), sAQ + 16 * tm * LA, LA, sKPT + 16 * tn * LA, LA);
+  }
+  __syncthreads();
+
+  // ---- phase 3: dT = -tril(A^T dA A^T, -1) ----
+  float *sDAT = sm + C::O_DAT, *sWM = sm + C::O_WM, *sA = sm + C::O_A;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
+  for (int u = 0; u < NCT; ++u) {
+    const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) acc[rr] += __shfl_xor(acc[rr], off);
-        if (lane == 0) sRS[i0 + rr] = acc[rr];
+    for (int q = 0; q < 4; ++q) sDAT[(16 * tn + m) * LA + 16 * tm + 4 * g + q] = aA[u][q];
+  }
+  for (int e = tid; e < BC * BC / 4; e += NT) {
+    const int s = e / (BC / 4), c4 = e - s * (BC / 4);
+    *reinterpret_cast<f32x4*>(sA + s * LA + 4 * c4) = *reinterpret_cast<const f32x4*>(W + L::A + s * BC + 4 * c4);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < NCT; ++u) {
+    const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
+    const f32x4 w4 = mma_lds<float, BC>(zero4(), sAT + 16 * tm * LA, LA, sDAT + 16 * tn * LA, LA);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sWM[(16 * tm + 4 * g + q) * LA + 16 * tn + m] = w4[q];
+  }
+  __syncthreads();
+  f32x4 aT[NCT];
+#pragma unroll
+  for (int u = 0; u < NCT; ++u) {
+    const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
+    aT[u] = mma_lds<float, BC>(zero4(), sWM + 16 * tm * LA, LA, sA + 16 * tn * LA, LA);
+  }
+  __syncthreads();
+
+  // ---- phase 4: dT K' and dT^T E' ----
+  float *sEPT = sm + C::O_EPT, *sDT = sm + C::O_DT, *sDTT = sm + C::O_DTT;
+#pragma unroll
+  for (int u = 0; u < NCT; ++u) {
+    const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 16 * tm + 4 * g + q, c = 16 * tn + m;
+      const float v = c < r ? -aT[u][q] : 0.f;
+      sDT[r * LA + c] = v;
+      sDTT[c * LA + r] = v;
+    }
+  }
+  for (int e = tid; e < BC * DK / 4; e += NT) {  // lane = token row
+    const int s = e % BC, i4 = e / BC;
+    const f32x4 ep = *reinterpret_cast<const f32x4*>(W + L::EP + s * DK + 4 * i4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sEPT[(4 * i4 + q) * LA + s] = ep[q];
+  }
+  __syncthreads();
+  f32x4 aP1[NKT], aP2[NKT];
+#pragma unroll
+  for (int u = 0; u < NKT; ++u) {
+    const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
+    aP1[u] = mma_lds<float, BC>(zero4(), sDT + 16 * tm * LA, LA, sKPT + 16 * tn * LA, LA);
+    aP2[u] = mma_lds<float, BC>(zero4(), sDTT + 16 * tm * LA, LA, sEPT + 16 * tn * LA, LA);
+  }
+  __syncthreads();
+
+  // ---- final: dq, dk, db per element; dg by the reverse cumulative sum ----
+  float *sU = sm + C::O_U, *sV = sm + C::O_V;
+  const float *sG31 = sm + C::O_G31, *sGCL = sm + C::O_GCL;
+#pragma unroll
+  for (int u = 0; u < NKT; ++u) {
+    const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK, i = 16 * tn + m;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 16 * tm + 4 * g + q;
+      const size_t x = (size_t)(row0 + r) * kr + (size_t)h * DK + i;
+      float qv = 0.f, kv = 0.f, bv = 0.f;
+      if (r < clen) {
+        qv = load1<BF16>(a.q, x);
+        kv = load1<BF16>(a.k, x);
+        bv = load1<BF16>(a.b, x);
+      }
+      const float G = W[L::G + r * DK + i], gam = expf(G);
+      const float e1 = expf(G - sG31[i]), e2 = expf(sG31[i] - G), ktail = expf(sGCL[i] - G);
+      const float dq = aQ[u][q] * gam + aP4[u][q] * e1;
+      const float dkbar = (aP2[u][q] + aP3[u][q]) * e2;   // dK_bar / gamma
+      const float deg = aX[u][q] * gam + aP1[u][q] * e1;  // dE * gamma
+      const float dkt = aK[u][q];
+      const float db = deg * kv;
+      sU[r * LKP + i] = dq * qv - dkbar * kv + db * bv - dkt * (ktail * kv);
+      sV[r * LKP + i] = dkt * (ktail * kv);
+      if (r < clen) {
+        a.dq[x] = dq;
+        a.dk[x] = dkbar + deg * bv + dkt * ktail;
+        a.db[x] = db;
       }
     }
   }
   __syncthreads();
   if (tid < DK) {
-    // ... and every K_tail row
-    float acc = sRS[tid] * W[L::GC + tid];
-    for (int r = 0; r < BC; ++r) acc = fmaf(W[L::DKT + r * DK + tid], W[L::KT + r * DK + tid], acc);
+    // gamma_C enters the state update (Diag(gamma_C) S) and every K_tail row
+    float acc = rs * W[L::GC + tid];
+    for (int r = 0; r < BC; ++r) acc += sV[r * LKP + tid];
     // dg_r = sum over rows r' >= r of dG (the decay of row r enters every
     // later cumulative sum of the chunk, and gamma_C is the last one)
     for (int r = BC - 1; r >= 0; --r) {
-      acc += sdG[r][tid];
+      acc += sU[r * LKP + tid];
       if (r < clen) a.dg[(size_t)(row0 + r) * kr + (size_t)h * DK + tid] = acc;
     }
   }
@@ -664,28 +890,20 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     GDR2_CK(hipGetLastError());
   }
   if (items <= 0) return hipSuccess;
-  // output paths (R = U - Y S comes from the state pass): dQ_g = dO S^T, dY = -dR S^T
-  GDR2_CK(bmm_group(a, F, items, {job(L::DO, DV, 0, L::S, DV, 1, L::DQG, DK, DK, DV),
-                                  job(L::DR, DV, 0, L::S, DV, 1, L::DY, DK, DK, DV, -1.f)}, st));
-  // dK_tail = R dS'^T, dA_qk = tril(dO R^T), dA = dR Z^T (first half of Eqs. 64-65),
-  // dZ = A^T dR, A^T dY
-  GDR2_CK(bmm_group(a, F, items, {job(L::R, DV, 0, L::DSP, DV, 1, L::DKT, DK, DK, DV),
-                                  job(L::DO, DV, 0, L::R, DV, 1, L::DAQK, BC, BC, DV, 1.f, -1, 1, 0),
-                                  job(L::DR, DV, 0, L::Z, DV, 1, L::DA, BC, BC, DV),
-                                  job(L::A, BC, 1, L::DR, DV, 0, L::DZ, DV, DV, BC),
-                                  job(L::A, BC, 1, L::DY, DK, 0, L::X1, DK, DK, BC)}, st));
-  // dA += dY E^T (second half), and the A_qk paths through the centred factors
-  GDR2_CK(bmm_group(a, F, items, {job(L::DY, DK, 0, L::EB, DK, 1, L::DA, BC, BC, DK, 1.f, (long long)L::DA),
-                                  job(L::DAQK, BC, 1, L::QP, DK, 0, L::P3, DK, DK, BC),
-                                  job(L::DAQK, BC, 0, L::KP, DK, 0, L::P4, DK, DK, BC)}, st));
-  // dT = -tril(A^T dA A^T, -1)
-  GDR2_CK(bmm_group(a, F, items, {job(L::A, BC, 1, L::DA, BC, 0, L::WM, BC, BC, BC)}, st));
-  GDR2_CK(bmm_group(a, F, items, {job(L::WM, BC, 0, L::A, BC, 1, L::DT, BC, BC, BC, -1.f, -1, 1, -1)}, st));
-  // the T paths through the centred factors
-  GDR2_CK(bmm_group(a, F, items, {job(L::DT, BC, 0, L::KP, DK, 0, L::P1, DK, DK, BC),
-                                  job(L::DT, BC, 1, L::EP, DK, 0, L::P2, DK, DK, BC)}, st));
-  if (a.in_bf16) hipLaunchKernelGGL((bwd_final_kernel<DK, DV, true>), gi, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((bwd_final_kernel<DK, DV, false>), gi, dim3(256), 0, st, a);
+  // output paths, WY gradients and the gradients themselves, one workgroup per item
+  {
+    typedef OutCfg<DK, DV> OC;
+    static bool attr[64] = {};
+    int dev = 0;
+    GDR2_CK(hipGetDevice(&dev));
+    if (dev < 0 || dev >= 64 || !attr[dev]) {
+      GDR2_CK(set_lds(&bwd_out_kernel<DK, DV, true>, OC::BYTES));
+      GDR2_CK(set_lds(&bwd_out_kernel<DK, DV, false>, OC::BYTES));
+      if (dev >= 0 && dev < 64) attr[dev] = true;
+    }
+    if (a.in_bf16) hipLaunchKernelGGL((bwd_out_kernel<DK, DV, true>), gi, dim3(OC::NT), OC::BYTES, st, a);
+    else hipLaunchKernelGGL((bwd_out_kernel<DK, DV, false>), gi, dim3(OC::NT), OC::BYTES, st, a);
+  }
   return hipGetLastError();
 }
 
