@@ -499,9 +499,10 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
 }
 
 // ---- output and WY-gradient paths, fused per item ------------------------------------
-// One workgroup per item forms, from the item's fp32 blocks (dO, R, dR, Z, A,
-// E, Q', K', E', the decay G) and the states S and dS' on either side of the
-// chunk, every remaining product and the gradients themselves:
+// One workgroup per item forms, from the item's fp32 blocks (R, dR, A, E, Q',
+// K', E', the decay G), the inputs (dO, v, w, q, k, b) and the states S and
+// dS' on either side of the chunk, every remaining product and the gradients
+// themselves:
 //   phase 1  dQ_g = dO S^T, dY = -dR S^T, dK_tail = R dS'^T,
 //            dA_qk = tril(dO R^T), dA = dR Z^T, dZ = A^T dR (-> dv, dw), and
 //            the row sums of dS' * S; the value channels stream through LDS
@@ -511,11 +512,14 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
 //   phase 4  dT K' and dT^T E';
 //   final    dq, dk, db from the accumulators (the centred factors put back
 //            per element), and dg as the reverse cumulative sum over the
-//            chunk's rows.
-// Every operand is staged K-contiguous in LDS (rows of 4 floats padding, so a
+//            chunk's rows (row blocks summed in parallel, then scanned).
+// Every operand is staged K-contiguous in LDS (rows padded by 4 floats, so a
 // 16-lane group's 16-byte reads hit distinct banks); the fp32 products run on
 // 16x16x4 MFMA.  Tiles of a [64][N] result go round the eight wavefronts
-// (tile t = wave + 8u, row tile t / (N/16), column tile t % (N/16)).
+// (tile t = wave + 8u, row tile t / (N/16), column tile t % (N/16)).  Each
+// phase's global loads are issued into registers one phase (or one slice)
+// ahead, so they overlap the products of the phase before.  Rows past the
+// end of a sequence read a clamped (valid) row and are zeroed in registers.
 template <int DK, int DV>
 struct OutCfg {
   static constexpr int NT = 512, NWV = 8, KC = 32, LS = KC + 4, LA = BC + 4, LKP = DK + 4;
@@ -523,10 +527,11 @@ struct OutCfg {
   static constexpr int NCT = 2;        // [64][64] tiles per wavefront
   // LDS offsets in floats.  A^T lives through phase 3; region R1 is reused.
   static constexpr int O_AT = 0, O_R1 = O_AT + BC * LA;
-  // phase 1: slices of dO, dR, R, Z [64][KC], of S, dS' [DK][KC], dR^T [KC][64]
+  // phase 1: slices of dO, dR, R, Z, w, v [64][KC], of S, dS' [DK][KC], dR^T [KC][64]
   static constexpr int O_O = O_R1, O_DR = O_O + BC * LS, O_R = O_DR + BC * LS,
                        O_Z = O_R + BC * LS, O_S = O_Z + BC * LS, O_DS = O_S + DK * LS,
-                       O_DRT = O_DS + DK * LS, E1 = O_DRT + KC * LA;
+                       O_DRT = O_DS + DK * LS, O_W = O_DRT + KC * LA, O_V = O_W + BC * LS,
+                       E1 = O_V + BC * LS;
   // phase 2a: dY [64][DK], E [64][DK], dY^T [DK][64]
   static constexpr int O_DY = O_R1, O_EB = O_DY + BC * LKP, O_DYT = O_EB + BC * LKP,
                        E2 = O_DYT + DK * LA;
@@ -539,13 +544,16 @@ struct OutCfg {
   static constexpr int O_EPT = O_X, O_DT = O_EPT + DK * LA, O_DTT = O_DT + BC * LA,
                        E5 = O_DTT + BC * LA;                                  // 4
   // final: the per-element dg terms [64][DK] twice
-  static constexpr int O_U = O_R1, O_V = O_U + BC * LKP, E6 = O_V + BC * LKP;
+  static constexpr int O_U = O_R1, O_V2 = O_U + BC * LKP, E6 = O_V2 + BC * LKP;
   static constexpr int mx(int x, int y) { return x > y ? x : y; }
+  // per-channel values: G at row 31 and 63, gamma_C, the dS' * S row sums;
+  // the dg scan's row-block partial sums
   static constexpr int O_G31 = mx(mx(mx(E1, E2), mx(E3, E4)), mx(E5, E6));
-  static constexpr int O_GCL = O_G31 + DK, FLOATS = O_GCL + DK;
+  static constexpr int O_GCL = O_G31 + DK, O_GCX = O_GCL + DK, O_RS = O_GCX + DK,
+                       O_PU = O_RS + DK, O_PV = O_PU + NT, FLOATS = O_PV + NT;
   static constexpr size_t BYTES = (size_t)FLOATS * 4;
   static_assert(BYTES <= 160 * 1024, "LDS budget exceeded");
-  static_assert(DV % KC == 0 && DK % 32 == 0, "output pass tiling");
+  static_assert(DV % KC == 0 && DK % 32 == 0 && NT % DK == 0, "output pass tiling");
 };
 
 template <int DK, int DV, bool BF16>
@@ -554,19 +562,57 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
   typedef OutCfg<DK, DV> C;
   constexpr int NT = C::NT, NWV = C::NWV, KC = C::KC, LS = C::LS, LA = C::LA, LKP = C::LKP;
   constexpr int NKT = C::NKT, NCT = C::NCT, TNK = DK / 16;
+  constexpr int NS = DV / KC;                         // value slices
+  constexpr int NSK = (DK * KC / 4 + NT - 1) / NT;    // float4 of an S slice per thread
+  constexpr int NEK = BC * DK / 4 / NT;               // float4 of a [64][DK] block per thread
+  constexpr int NAA = BC * BC / 4 / NT;               // float4 of a [64][64] block per thread
   const int item = blockIdx.x, ci = item / a.H, h = item - ci * a.H;
   long long row0;
   int clen;
-  if (!bwd_locate(a, ci, row0, clen)) return;
+  if (!bwd_locate(a, ci, row0, clen) || clen <= 0) return;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   float* sm = reinterpret_cast<float*>(smem_raw);
   const float* W = a.ws + (size_t)item * L::FLOATS;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
   const size_t kr = (size_t)a.H * DK, vr = (size_t)a.H * DV;
   float* sAT = sm + C::O_AT;
+  float *sO = sm + C::O_O, *sDR = sm + C::O_DR, *sR = sm + C::O_R, *sZ = sm + C::O_Z;
+  float *sS = sm + C::O_S, *sDS = sm + C::O_DS, *sDRT = sm + C::O_DRT;
+  float *sW = sm + C::O_W, *sV = sm + C::O_V;
+
+  // value slice j0 of dO, w, v (inputs), R, dR (workspace) and S, dS' into
+  // registers: row s = tid / 8, 4 channels at 4 * (tid % 8)
+  const int ss = tid / (KC / 4), sc4 = tid - ss * (KC / 4);
+  const int ssr = ss < clen ? ss : clen - 1;
+  f32x4 pO, pR, pDR, pW, pV, pS[NSK], pDS[NSK];
+  auto slice_load = [&](int j0) {
+    const size_t xi = (size_t)(row0 + ssr) * vr + (size_t)h * DV + j0 + 4 * sc4;
+    const size_t xw = (size_t)ss * DV + j0 + 4 * sc4;
+    float t0[4], t1[4], t2[4];
+    load4<BF16>(a.dO, xi, t0);
+    load4<BF16>(a.w, xi, t1);
+    load4<BF16>(a.v, xi, t2);
+    const float z = ss < clen ? 1.f : 0.f;
+    pO = f32x4{t0[0], t0[1], t0[2], t0[3]} * z;
+    pW = f32x4{t1[0], t1[1], t1[2], t1[3]} * z;
+    pV = f32x4{t2[0], t2[1], t2[2], t2[3]} * z;
+    pR = *reinterpret_cast<const f32x4*>(W + L::R + xw);
+    pDR = *reinterpret_cast<const f32x4*>(W + L::DR + xw);
+#pragma unroll
+    for (int u = 0; u < NSK; ++u) {
+      const int e = tid + NT * u;
+      if (e < DK * KC / 4) {
+        const int i = e / (KC / 4), c4 = e - i * (KC / 4);
+        pS[u] = *reinterpret_cast<const f32x4*>(W + L::S + (size_t)i * DV + j0 + 4 * c4);
+        pDS[u] = *reinterpret_cast<const f32x4*>(W + L::DSP + (size_t)i * DV + j0 + 4 * c4);
+      }
+    }
+  };
+  slice_load(0);
   // A^T (lane = row of A: consecutive lanes write consecutive words)
-  for (int e = tid; e < BC * BC / 4; e += NT) {
-    const int k = e % BC, c4 = e / BC;
+#pragma unroll
+  for (int u = 0; u < NAA; ++u) {
+    const int e = tid + NT * u, k = e % BC, c4 = e / BC;
     const f32x4 x = *reinterpret_cast<const f32x4*>(W + L::A + k * BC + 4 * c4);
 #pragma unroll
     for (int q = 0; q < 4; ++q) sAT[(4 * c4 + q) * LA + k] = x[q];
@@ -574,38 +620,48 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
   if (tid < DK) {
     sm[C::O_G31 + tid] = W[L::G + 31 * DK + tid];
     sm[C::O_GCL + tid] = W[L::G + (BC - 1) * DK + tid];
+    sm[C::O_GCX + tid] = W[L::GC + tid];
   }
 
   // ---- phase 1 ----
-  f32x4 aQ[NKT], aY[NKT], aK[NKT], aAQ[NCT], aA[NCT];
+  f32x4 aQ[NKT], aY[NKT], aK[NKT], aAQ[NCT], aA[NCT], pEB[NEK];
 #pragma unroll
   for (int u = 0; u < NKT; ++u) aQ[u] = aY[u] = aK[u] = zero4();
 #pragma unroll
   for (int u = 0; u < NCT; ++u) aAQ[u] = aA[u] = zero4();
   float rs = 0.f;  // sum over the value channels of dS' * S, row tid
-  float *sO = sm + C::O_O, *sDR = sm + C::O_DR, *sR = sm + C::O_R, *sZ = sm + C::O_Z;
-  float *sS = sm + C::O_S, *sDS = sm + C::O_DS, *sDRT = sm + C::O_DRT;
-  for (int j0 = 0; j0 < DV; j0 += KC) {
-    for (int e = tid; e < BC * KC / 4; e += NT) {
-      const int s = e / (KC / 4), c4 = e - s * (KC / 4);
-      const size_t x = (size_t)s * DV + j0 + 4 * c4;
-      const int o = s * LS + 4 * c4;
-      *reinterpret_cast<f32x4*>(sO + o) = *reinterpret_cast<const f32x4*>(W + L::DO + x);
-      *reinterpret_cast<f32x4*>(sR + o) = *reinterpret_cast<const f32x4*>(W + L::R + x);
-      *reinterpret_cast<f32x4*>(sZ + o) = *reinterpret_cast<const f32x4*>(W + L::Z + x);
-      const f32x4 dr = *reinterpret_cast<const f32x4*>(W + L::DR + x);
-      *reinterpret_cast<f32x4*>(sDR + o) = dr;
+  for (int sl = 0; sl < NS; ++sl) {
+    const int j0 = sl * KC;
+    {
+      const int o = ss * LS + 4 * sc4;
+      *reinterpret_cast<f32x4*>(sO + o) = pO;
+      *reinterpret_cast<f32x4*>(sR + o) = pR;
+      *reinterpret_cast<f32x4*>(sDR + o) = pDR;
+      *reinterpret_cast<f32x4*>(sW + o) = pW;
+      *reinterpret_cast<f32x4*>(sV + o) = pV;
+      *reinterpret_cast<f32x4*>(sZ + o) = pW * pV;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) sDRT[(4 * c4 + q) * LA + s] = dr[q];
-    }
-    for (int e = tid; e < DK * KC / 4; e += NT) {
-      const int i = e / (KC / 4), c4 = e - i * (KC / 4);
-      const size_t x = (size_t)i * DV + j0 + 4 * c4;
-      const int o = i * LS + 4 * c4;
-      *reinterpret_cast<f32x4*>(sS + o) = *reinterpret_cast<const f32x4*>(W + L::S + x);
-      *reinterpret_cast<f32x4*>(sDS + o) = *reinterpret_cast<const f32x4*>(W + L::DSP + x);
+      for (int q = 0; q < 4; ++q) sDRT[(4 * sc4 + q) * LA + ss] = pDR[q];
+#pragma unroll
+      for (int u = 0; u < NSK; ++u) {
+        const int e = tid + NT * u;
+        if (e < DK * KC / 4) {
+          const int i = e / (KC / 4), c4 = e - i * (KC / 4);
+          *reinterpret_cast<f32x4*>(sS + i * LS + 4 * c4) = pS[u];
+          *reinterpret_cast<f32x4*>(sDS + i * LS + 4 * c4) = pDS[u];
+        }
+      }
     }
     __syncthreads();
+    if (sl + 1 < NS) {
+      slice_load(j0 + KC);
+    } else {
+#pragma unroll
+      for (int u = 0; u < NEK; ++u) {
+        const int e = tid + NT * u, s = e / (DK / 4), i4 = e - s * (DK / 4);
+        pEB[u] = *reinterpret_cast<const f32x4*>(W + L::EB + s * DK + 4 * i4);
+      }
+    }
     if (tid < DK)
 #pragma unroll 8
       for (int c = 0; c < KC; ++c) rs = fmaf(sDS[tid * LS + c], sS[tid * LS + c], rs);
@@ -627,11 +683,11 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
       const f32x4 z = mma_lds<float, BC>(zero4(), sAT + 16 * tm * LA, LA, sDRT + 16 * tn * LA, LA);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int r = 16 * tm + 4 * g + q;
+        const int r = 16 * tm + 4 * g + q, c = 16 * tn + m;
         if (r < clen) {
-          const size_t x = (size_t)(row0 + r) * vr + (size_t)h * DV + j0 + 16 * tn + m;
-          a.dv[x] = z[q] * load1<BF16>(a.w, x);
-          a.dw[x] = z[q] * load1<BF16>(a.v, x);
+          const size_t x = (size_t)(row0 + r) * vr + (size_t)h * DV + j0 + c;
+          a.dv[x] = z[q] * sW[r * LS + c];
+          a.dw[x] = z[q] * sV[r * LS + c];
         }
       }
     }
@@ -651,12 +707,19 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
       sDYT[i * LA + r] = y;
     }
   }
-  for (int e = tid; e < BC * DK / 4; e += NT) {
-    const int s = e / (DK / 4), i4 = e - s * (DK / 4);
-    *reinterpret_cast<f32x4*>(sEB + s * LKP + 4 * i4) =
-        *reinterpret_cast<const f32x4*>(W + L::EB + s * DK + 4 * i4);
+#pragma unroll
+  for (int u = 0; u < NEK; ++u) {
+    const int e = tid + NT * u, s = e / (DK / 4), i4 = e - s * (DK / 4);
+    *reinterpret_cast<f32x4*>(sEB + s * LKP + 4 * i4) = pEB[u];
   }
   __syncthreads();
+  f32x4 pQP[NEK], pKP[NEK];  // lane = token row
+#pragma unroll
+  for (int u = 0; u < NEK; ++u) {
+    const int e = tid + NT * u, s = e % BC, i4 = e / BC;
+    pQP[u] = *reinterpret_cast<const f32x4*>(W + L::QP + s * DK + 4 * i4);
+    pKP[u] = *reinterpret_cast<const f32x4*>(W + L::KP + s * DK + 4 * i4);
+  }
   f32x4 aX[NKT];
 #pragma unroll
   for (int u = 0; u < NCT; ++u) {
@@ -683,17 +746,27 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
       sAQT[c * LA + r] = v;
     }
   }
-  for (int e = tid; e < BC * DK / 4; e += NT) {  // lane = token row
-    const int s = e % BC, i4 = e / BC;
-    const f32x4 qp = *reinterpret_cast<const f32x4*>(W + L::QP + s * DK + 4 * i4);
-    const f32x4 kp = *reinterpret_cast<const f32x4*>(W + L::KP + s * DK + 4 * i4);
+#pragma unroll
+  for (int u = 0; u < NEK; ++u) {
+    const int e = tid + NT * u, s = e % BC, i4 = e / BC;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      sQPT[(4 * i4 + q) * LA + s] = qp[q];
-      sKPT[(4 * i4 + q) * LA + s] = kp[q];
+      sQPT[(4 * i4 + q) * LA + s] = pQP[u][q];
+      sKPT[(4 * i4 + q) * LA + s] = pKP[u][q];
     }
   }
   __syncthreads();
+  f32x4 pA[NAA], pEP[NEK];
+#pragma unroll
+  for (int u = 0; u < NAA; ++u) {
+    const int e = tid + NT * u, s = e / (BC / 4), c4 = e - s * (BC / 4);
+    pA[u] = *reinterpret_cast<const f32x4*>(W + L::A + s * BC + 4 * c4);
+  }
+#pragma unroll
+  for (int u = 0; u < NEK; ++u) {  // lane = token row
+    const int e = tid + NT * u, s = e % BC, i4 = e / BC;
+    pEP[u] = *reinterpret_cast<const f32x4*>(W + L::EP + s * DK + 4 * i4);
+  }
   f32x4 aP3[NKT], aP4[NKT];
 #pragma unroll
   for (int u = 0; u < NKT; ++u) {
@@ -711,9 +784,10 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) sDAT[(16 * tn + m) * LA + 16 * tm + 4 * g + q] = aA[u][q];
   }
-  for (int e = tid; e < BC * BC / 4; e += NT) {
-    const int s = e / (BC / 4), c4 = e - s * (BC / 4);
-    *reinterpret_cast<f32x4*>(sA + s * LA + 4 * c4) = *reinterpret_cast<const f32x4*>(W + L::A + s * BC + 4 * c4);
+#pragma unroll
+  for (int u = 0; u < NAA; ++u) {
+    const int e = tid + NT * u, s = e / (BC / 4), c4 = e - s * (BC / 4);
+    *reinterpret_cast<f32x4*>(sA + s * LA + 4 * c4) = pA[u];
   }
   __syncthreads();
 #pragma unroll
@@ -728,7 +802,11 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
 #pragma unroll
   for (int u = 0; u < NCT; ++u) {
     const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
-    aT[u] = mma_lds<float, BC>(zero4(), sWM + 16 * tm * LA, LA, sA + 16 * tn * LA, LA);
+    // A is unit lower triangular: column block tn of A^T has no rows past
+    // 16 (tn + 1); tiles above the diagonal are masked out below
+    aT[u] = tn <= tm ? mma_lds_k16<float, BC>(zero4(), sWM + 16 * tm * LA, LA, sA + 16 * tn * LA, LA,
+                                              16 * (tn + 1))
+                     : zero4();
   }
   __syncthreads();
 
@@ -745,13 +823,28 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
       sDTT[c * LA + r] = v;
     }
   }
-  for (int e = tid; e < BC * DK / 4; e += NT) {  // lane = token row
-    const int s = e % BC, i4 = e / BC;
-    const f32x4 ep = *reinterpret_cast<const f32x4*>(W + L::EP + s * DK + 4 * i4);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) sEPT[(4 * i4 + q) * LA + s] = ep[q];
+  for (int u = 0; u < NEK; ++u) {
+    const int e = tid + NT * u, s = e % BC, i4 = e / BC;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sEPT[(4 * i4 + q) * LA + s] = pEP[u][q];
   }
   __syncthreads();
+  // the final's per-element inputs, loaded while phase 4 computes
+  float fG[NKT][4], fq[NKT][4], fk[NKT][4], fb[NKT][4];
+#pragma unroll
+  for (int u = 0; u < NKT; ++u) {
+    const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK, i = 16 * tn + m;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 16 * tm + 4 * g + q, rr = r < clen ? r : clen - 1;
+      const size_t x = (size_t)(row0 + rr) * kr + (size_t)h * DK + i;
+      fG[u][q] = W[L::G + r * DK + i];
+      fq[u][q] = load1<BF16>(a.q, x);
+      fk[u][q] = load1<BF16>(a.k, x);
+      fb[u][q] = load1<BF16>(a.b, x);
+    }
+  }
   f32x4 aP1[NKT], aP2[NKT];
 #pragma unroll
   for (int u = 0; u < NKT; ++u) {
@@ -762,22 +855,19 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
   __syncthreads();
 
   // ---- final: dq, dk, db per element; dg by the reverse cumulative sum ----
-  float *sU = sm + C::O_U, *sV = sm + C::O_V;
-  const float *sG31 = sm + C::O_G31, *sGCL = sm + C::O_GCL;
+  float *sU = sm + C::O_U, *sV2 = sm + C::O_V2, *sRS = sm + C::O_RS;
+  float *sPU = sm + C::O_PU, *sPV = sm + C::O_PV;
+  const float *sG31 = sm + C::O_G31, *sGCL = sm + C::O_GCL, *sGCX = sm + C::O_GCX;
+  if (tid < DK) sRS[tid] = rs;
 #pragma unroll
   for (int u = 0; u < NKT; ++u) {
     const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK, i = 16 * tn + m;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = 16 * tm + 4 * g + q;
-      const size_t x = (size_t)(row0 + r) * kr + (size_t)h * DK + i;
-      float qv = 0.f, kv = 0.f, bv = 0.f;
-      if (r < clen) {
-        qv = load1<BF16>(a.q, x);
-        kv = load1<BF16>(a.k, x);
-        bv = load1<BF16>(a.b, x);
-      }
-      const float G = W[L::G + r * DK + i], gam = expf(G);
+      const bool in = r < clen;
+      const float qv = in ? fq[u][q] : 0.f, kv = in ? fk[u][q] : 0.f, bv = in ? fb[u][q] : 0.f;
+      const float G = fG[u][q], gam = expf(G);
       const float e1 = expf(G - sG31[i]), e2 = expf(sG31[i] - G), ktail = expf(sGCL[i] - G);
       const float dq = aQ[u][q] * gam + aP4[u][q] * e1;
       const float dkbar = (aP2[u][q] + aP3[u][q]) * e2;   // dK_bar / gamma
@@ -785,8 +875,9 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
       const float dkt = aK[u][q];
       const float db = deg * kv;
       sU[r * LKP + i] = dq * qv - dkbar * kv + db * bv - dkt * (ktail * kv);
-      sV[r * LKP + i] = dkt * (ktail * kv);
-      if (r < clen) {
+      sV2[r * LKP + i] = dkt * (ktail * kv);  // dK_tail * K_tail
+      if (in) {
+        const size_t x = (size_t)(row0 + r) * kr + (size_t)h * DK + i;
         a.dq[x] = dq;
         a.dk[x] = dkbar + deg * bv + dkt * ktail;
         a.db[x] = db;
@@ -794,16 +885,34 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  if (tid < DK) {
-    // gamma_C enters the state update (Diag(gamma_C) S) and every K_tail row
-    float acc = rs * W[L::GC + tid];
-    for (int r = 0; r < BC; ++r) acc += sV[r * LKP + tid];
-    // dg_r = sum over rows r' >= r of dG (the decay of row r enters every
-    // later cumulative sum of the chunk, and gamma_C is the last one)
-    for (int r = BC - 1; r >= 0; --r) {
-      acc += sU[r * LKP + tid];
-      if (r < clen) a.dg[(size_t)(row0 + r) * kr + (size_t)h * DK + tid] = acc;
+  // dg_r = gamma_C * rowsum(dS' * S) + sum over all rows of dK_tail * K_tail
+  //        + sum over rows r' >= r of the rest (the decay of row r enters every
+  //        later cumulative sum of the chunk, and gamma_C is the last one).
+  // Thread (row block rb, channel i): sums of its rows first, then its scan.
+  constexpr int NRB = NT / DK, RPB = BC / NRB;
+  const int i = tid % DK, rb = tid / DK;
+  {
+    float su = 0.f, sv = 0.f;
+#pragma unroll
+    for (int k = 0; k < RPB; ++k) {
+      su += sU[(rb * RPB + k) * LKP + i];
+      sv += sV2[(rb * RPB + k) * LKP + i];
     }
+    sPU[rb * DK + i] = su;
+    sPV[rb * DK + i] = sv;
+  }
+  __syncthreads();
+  float acc = sRS[i] * sGCX[i];
+#pragma unroll
+  for (int b = 0; b < NRB; ++b) acc += sPV[b * DK + i];
+#pragma unroll
+  for (int b = NRB - 1; b > 0; --b)
+    if (b > rb) acc += sPU[b * DK + i];
+#pragma unroll
+  for (int k = RPB - 1; k >= 0; --k) {
+    const int r = rb * RPB + k;
+    acc += sU[r * LKP + i];
+    if (r < clen) a.dg[(size_t)(row0 + r) * kr + (size_t)h * DK + i] = acc;
   }
 }
 
