@@ -337,7 +337,13 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
   float* sRT = sKtT + DK * LC;                  // [DVB][LC]
   float* sU = sRT + DVB * LC;                   // [BC][LV]
   float* sGC = sU + BC * LV;                    // [DK]
-  const int jb = blockIdx.x % NB, nh = blockIdx.x / NB, n = nh / a.H, h = nh - n * a.H;
+  // the NB value blocks of one (sequence, head) share an XCD (workgroups go
+  // round the eight XCDs in order), so their reads of the chunk blocks they
+  // all need hit that XCD's L2
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int nh = (slot / NB) * 8 + xcd, jb = slot % NB;
+  if (nh >= a.N * a.H) return;
+  const int n = nh / a.H, h = nh - n * a.H;
   const int c0 = a.tab ? a.cbase[n] : n * a.nc, c1 = a.tab ? a.cbase[n + 1] : (n + 1) * a.nc;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
   for (int e = tid; e < DK * DVB; e += SNT) {
@@ -413,7 +419,13 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
   float* sYT = sQgT + DK * LC;                   // [DK][LC]   Y^T
   float* sdRT = sYT + DK * LC;                   // [DVB][LC]  dR^T
   float* sGC = sdRT + DVB * LC;                  // [DK]
-  const int jb = blockIdx.x % NB, nh = blockIdx.x / NB, n = nh / a.H, h = nh - n * a.H;
+  // the NB value blocks of one (sequence, head) share an XCD (workgroups go
+  // round the eight XCDs in order), so their reads of the chunk blocks they
+  // all need hit that XCD's L2
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int nh = (slot / NB) * 8 + xcd, jb = slot % NB;
+  if (nh >= a.N * a.H) return;
+  const int n = nh / a.H, h = nh - n * a.H;
   const int c0 = a.tab ? a.cbase[n] : n * a.nc, c1 = a.tab ? a.cbase[n + 1] : (n + 1) * a.nc;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
   for (int e = tid; e < DK * DVB; e += SNT) {
@@ -992,7 +1004,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
       GDR2_CK(set_lds(&bwd_state_bwd_kernel<DK, DV>, lb));
       if (dev >= 0 && dev < 64) attr[dev] = true;
     }
-    const dim3 gs((unsigned)((size_t)a.N * a.H * (DV / DVB)));
+    const dim3 gs((unsigned)(((size_t)a.N * a.H + 7) / 8 * 8 * (DV / DVB)));
     hipLaunchKernelGGL((bwd_state_fwd_kernel<DK, DV>), gs, dim3(SNT), lf, st, a);
     GDR2_CK(hipGetLastError());
     hipLaunchKernelGGL((bwd_state_bwd_kernel<DK, DV>), gs, dim3(SNT), lb, st, a);
