@@ -32,8 +32,6 @@
 // Every product runs on fp32 MFMA (16x16x4) from LDS-staged operands.
 #include <hip/hip_runtime.h>
 
-#include <initializer_list>
-
 #include "gdr2_device.h"
 #include "gdr2_internal.h"
 
@@ -52,13 +50,10 @@ struct BwdLayout {
   // offsets in floats inside one item's block
   static constexpr size_t G = 0, QG = G + CK, KT = QG + CK, EB = KT + CK, EP = EB + CK,
                           KP = EP + CK, QP = KP + CK, Y_ = QP + CK;
-  static constexpr size_t Z = Y_ + CK, U = Z + CV, DO = U + CV, DR = DO + CV, R = DR + CV;
-  static constexpr size_t T = R + CV, A = T + CC, AQK = A + CC, DAQK = AQK + CC, DA = DAQK + CC,
-                          WM = DA + CC, DT = WM + CC;
-  static constexpr size_t S = DT + CC, DSP = S + KV;
-  static constexpr size_t DQG = DSP + KV, DY = DQG + CK, DKT = DY + CK, X1 = DKT + CK,
-                          P1 = X1 + CK, P2 = P1 + CK, P3 = P2 + CK, P4 = P3 + CK;
-  static constexpr size_t DZ = P4 + CK, GC = DZ + CV;
+  static constexpr size_t U = Y_ + CK, R = U + CV, DR = R + CV;
+  static constexpr size_t A = DR + CV, AQK = A + CC;
+  static constexpr size_t S = AQK + CC, DSP = S + KV;
+  static constexpr size_t GC = DSP + KV;
   static constexpr size_t FLOATS = (GC + DK + 63) / 64 * 64;
 };
 
@@ -77,192 +72,269 @@ __device__ __forceinline__ bool bwd_locate(const BwdArgs& a, int ci, long long& 
   return true;
 }
 
-// ---- prep: decay, the scaled key-side rows, Z and dO ---------------------------------
+// ---- front: decay, the scaled rows, T, A_qk, A = (I + T)^-1, Y and U per item ----------
+// One workgroup per item:
+//   phase 1  log-decay rows into LDS, q, k, b into registers; G by a column
+//            scan (row blocks scanned in parallel, then offset by the totals
+//            of the blocks above);
+//   phase 2  Q_g, K_tail, E, E', K', Q' to the workspace, E', K', Q' to LDS;
+//   phase 3  T = tril(E' K'^T, -1) and A_qk = tril(Q' K'^T) on MFMA (inside
+//            a product the centred factors cancel);
+//   phase 4  A = (I + T)^-1: forward substitution on the four diagonal 16x16
+//            blocks, then the off-diagonal blocks one block row at a time,
+//            A_ij = -A_ii sum_{k=j}^{i-1} T_ik A_kj;
+//   phase 5  Y = A E and U = A Z (Z = w * v) on MFMA, A to the workspace.
+// Rows past the end of a sequence read a clamped (valid) row and are zeroed.
+template <int DK, int DV>
+struct FrontCfg {
+  static constexpr int NT = 512, LA = BC + 4, LKP = DK + 4, LM = 20;
+  // phases 1-2: G, E', K', Q' [64][DK]
+  static constexpr int O_G = 0, O_EP = O_G + BC * LKP, O_KP = O_EP + BC * LKP,
+                       O_QP = O_KP + BC * LKP, E1 = O_QP + BC * LKP;
+  // phases 3-5: T, A, A^T [64][64], M^T [16][LM] for three wavefronts
+  static constexpr int O_T = 0, O_A = O_T + BC * LA, O_AT = O_A + BC * LA, O_M = O_AT + BC * LA,
+                       E2 = O_M + 3 * 16 * LM;
+  // phase 5: E^T [DK][64], Z^T [DV][64]
+  static constexpr int O_EBT = E2, O_ZT = O_EBT + DK * LA, E3 = O_ZT + DV * LA;
+  static constexpr int O_PS = E1 > E3 ? E1 : E3, FLOATS = O_PS + NT;
+  static constexpr size_t BYTES = (size_t)FLOATS * 4;
+  static_assert(BYTES <= 160 * 1024, "LDS budget exceeded");
+  static_assert(DK % 32 == 0 && DV % 32 == 0 && NT % DK == 0, "front pass tiling");
+};
+
 template <int DK, int DV, bool BF16, bool LA16>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512) void bwd_front_kernel(BwdArgs a) {
   typedef BwdLayout<DK, DV> L;
+  typedef FrontCfg<DK, DV> C;
+  constexpr int NT = C::NT, NWV = 8, LA = C::LA, LKP = C::LKP, LM = C::LM;
+  constexpr int NEK = BC * DK / 4 / NT;  // float4 of a [64][DK] block per thread
+  constexpr int NEV = BC * DV / 4 / NT;  // float4 of a [64][DV] block per thread
+  constexpr int NAA = BC * BC / 4 / NT;  // float4 of a [64][64] block per thread
+  constexpr int TNK = DK / 16, NKT = DK / 32, TNV = DV / 16, NVT = DV / 32;
+  constexpr int NRB = NT / DK, RPB = BC / NRB;
   const int item = blockIdx.x, ci = item / a.H, h = item - ci * a.H;
   long long row0;
   int clen;
-  if (!bwd_locate(a, ci, row0, clen)) return;
+  if (!bwd_locate(a, ci, row0, clen) || clen <= 0) return;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  float* sm = reinterpret_cast<float*>(smem_raw);
   float* W = a.ws + (size_t)item * L::FLOATS;
-  __shared__ float sG[BC][DK];
-  __shared__ float sGm[DK], sGC[DK];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
   const size_t kr = (size_t)a.H * DK, vr = (size_t)a.H * DV;
-  if (tid < DK) {
-    // cumulative log-decay from the chunk start, fp32; rows past the end add 0
-    float acc = 0.f;
-    for (int r = 0; r < BC; ++r) {
-      if (r < clen) acc += load1<LA16>(a.la, (size_t)(row0 + r) * kr + (size_t)h * DK + tid);
-      sG[r][tid] = acc;
-    }
-    sGm[tid] = sG[31][tid];
-    sGC[tid] = acc;
-    W[L::GC + tid] = expf(acc);
+
+  // ---- phase 1 ----
+  float* sG = sm + C::O_G;
+  f32x4 pq[NEK], pk[NEK], pb[NEK];
+#pragma unroll
+  for (int u = 0; u < NEK; ++u) {
+    const int e = tid + NT * u, r = e / (DK / 4), i4 = e - r * (DK / 4);
+    const int rr = r < clen ? r : clen - 1;
+    const size_t x = (size_t)(row0 + rr) * kr + (size_t)h * DK + 4 * i4;
+    const float z = r < clen ? 1.f : 0.f;
+    float t[4];
+    load4<LA16>(a.la, x, t);
+    *reinterpret_cast<f32x4*>(sG + r * LKP + 4 * i4) = f32x4{t[0], t[1], t[2], t[3]} * z;
+    load4<BF16>(a.q, x, t);
+    pq[u] = f32x4{t[0], t[1], t[2], t[3]} * z;
+    load4<BF16>(a.k, x, t);
+    pk[u] = f32x4{t[0], t[1], t[2], t[3]} * z;
+    load4<BF16>(a.b, x, t);
+    pb[u] = f32x4{t[0], t[1], t[2], t[3]} * z;
   }
   __syncthreads();
-  for (int e = tid; e < BC * DK; e += 256) {
-    const int r = e / DK, i = e - r * DK;
-    float qv = 0.f, kv = 0.f, bv = 0.f;
-    if (r < clen) {
-      const size_t x = (size_t)(row0 + r) * kr + (size_t)h * DK + i;
-      qv = load1<BF16>(a.q, x);
-      kv = load1<BF16>(a.k, x);
-      bv = load1<BF16>(a.b, x);
+  // cumulative log-decay from the chunk start, fp32 (rows past the end add 0)
+  const int si = tid % DK, rb = tid / DK;
+  float* sPS = sm + C::O_PS;
+  float run[RPB];
+  {
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < RPB; ++k) {
+      acc += sG[(rb * RPB + k) * LKP + si];
+      run[k] = acc;
     }
-    const float G = sG[r][i], gam = expf(G), e1 = expf(G - sGm[i]), e2 = expf(sGm[i] - G);
-    W[L::G + e] = G;
-    W[L::QG + e] = gam * qv;
-    W[L::KT + e] = expf(sGC[i] - G) * kv;
-    W[L::EB + e] = gam * bv * kv;
-    W[L::EP + e] = e1 * bv * kv;
-    W[L::KP + e] = e2 * kv;
-    W[L::QP + e] = e1 * qv;
+    sPS[rb * DK + si] = acc;
   }
-  for (int e = tid; e < BC * DV; e += 256) {
-    const int r = e / DV, j = e - r * DV;
-    float vv = 0.f, wv = 0.f, dov = 0.f;
-    if (r < clen) {
-      const size_t x = (size_t)(row0 + r) * vr + (size_t)h * DV + j;
-      vv = load1<BF16>(a.v, x);
-      wv = load1<BF16>(a.w, x);
-      dov = load1<BF16>(a.dO, x);
+  __syncthreads();
+  {
+    float off = 0.f;
+#pragma unroll
+    for (int b = 0; b < NRB - 1; ++b)
+      if (b < rb) off += sPS[b * DK + si];
+#pragma unroll
+    for (int k = 0; k < RPB; ++k) {
+      const int r = rb * RPB + k;
+      const float G = off + run[k];
+      sG[r * LKP + si] = G;
+      W[L::G + r * DK + si] = G;
+      if (r == BC - 1) W[L::GC + si] = expf(G);
     }
-    W[L::Z + e] = wv * vv;
-    W[L::DO + e] = dov;
   }
-}
+  __syncthreads();
 
-// ---- batched fp32 products over items -----------------------------------------------
-// C[m][n] = alpha * sum_k opA(m, k) opB(k, n) (+ D[m][n]), entries with
-// n > m + diag zeroed when `mask`.  opA(m, k) = A[k][m] when transposed, else
-// A[m][k] (rows of lda floats); opB(k, n) = B[n][k] when transposed, else
-// B[k][n].  Both operands are staged into LDS K-contiguous ([M][K] and [N][K]),
-// K in slices of 32 with 16-byte loads (the item blocks, their offsets and the
-// row strides are multiples of 4 floats), so several workgroups share a CU.
-// Several independent products over the items in one launch (blockIdx.y
-// selects the product; none reads another's output).  M is the chunk (64);
-// N and K (multiples of 32) and the transposes come from the job table.
-struct BmmJob {
-  size_t oa, ob, oc;  // operand offsets inside an item's block (floats)
-  long long od;       // addend offset, or -1
-  int lda, ldb, ldc, N, K, ta, tb, mask, diag;
-  float alpha;
-};
-constexpr int MAXJOBS = 6;
-struct BmmJobs {
-  BmmJob j[MAXJOBS];
-  float* ws;
-  size_t stride;
-  int H;
-  const int32_t* total;
-};
-
-__global__ __launch_bounds__(512) void bmm_multi_kernel(BmmJobs P) {
-  constexpr int M = BC, KC = 32, LD = KC + 4, TM = M / 16, NMAX = 128, TPW = TM * (NMAX / 16) / 8;
-  __shared__ __align__(16) float As[M * LD];
-  __shared__ __align__(16) float Bs[NMAX * LD];
-  const int item = blockIdx.x;
-  if (P.total && item / P.H >= *P.total) return;
-  const BmmJob& J = P.j[blockIdx.y];
-  const int N = J.N, K = J.K, TN = N / 16;
-  const size_t base = (size_t)item * P.stride;
-  const float* A = P.ws + base + J.oa;
-  const float* B = P.ws + base + J.ob;
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
-  f32x4 acc[TPW];
+  // ---- phase 2 ----
+  float *sEP = sm + C::O_EP, *sKP = sm + C::O_KP, *sQP = sm + C::O_QP;
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) acc[u] = zero4();
-  for (int kc = 0; kc < K; kc += KC) {
-    for (int e = tid; e < M * KC / 4; e += 512) {
-      if (J.ta) {
-        const int k = e / (M / 4), m4 = e - k * (M / 4);
-        const f32x4 x = *reinterpret_cast<const f32x4*>(A + (size_t)(kc + k) * J.lda + 4 * m4);
-        As[(4 * m4 + 0) * LD + k] = x[0];
-        As[(4 * m4 + 1) * LD + k] = x[1];
-        As[(4 * m4 + 2) * LD + k] = x[2];
-        As[(4 * m4 + 3) * LD + k] = x[3];
-      } else {
-        const int mm = e / (KC / 4), k4 = e - mm * (KC / 4);
-        *reinterpret_cast<f32x4*>(As + mm * LD + 4 * k4) =
-            *reinterpret_cast<const f32x4*>(A + (size_t)mm * J.lda + kc + 4 * k4);
-      }
-    }
-    for (int e = tid; e < N * KC / 4; e += 512) {
-      if (J.tb) {
-        const int n = e / (KC / 4), k4 = e - n * (KC / 4);
-        *reinterpret_cast<f32x4*>(Bs + n * LD + 4 * k4) =
-            *reinterpret_cast<const f32x4*>(B + (size_t)n * J.ldb + kc + 4 * k4);
-      } else {
-        const int k = e / (N / 4), n4 = e - k * (N / 4);
-        const f32x4 x = *reinterpret_cast<const f32x4*>(B + (size_t)(kc + k) * J.ldb + 4 * n4);
-        Bs[(4 * n4 + 0) * LD + k] = x[0];
-        Bs[(4 * n4 + 1) * LD + k] = x[1];
-        Bs[(4 * n4 + 2) * LD + k] = x[2];
-        Bs[(4 * n4 + 3) * LD + k] = x[3];
-      }
-    }
-    __syncthreads();
+  for (int u = 0; u < NEK; ++u) {
+    const int e = tid + NT * u, r = e / (DK / 4), i4 = e - r * (DK / 4), o = r * LKP + 4 * i4;
+    f32x4 QG, KT, EB, EP, KP, QP;
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int t = wv + 8 * u;
-      if (t < TM * TN) {
-        const int tm = t / TN, tn = t - tm * TN;
-        acc[u] = mma_lds<float, KC>(acc[u], As + 16 * tm * LD, LD, Bs + 16 * tn * LD, LD);
-      }
+    for (int c = 0; c < 4; ++c) {
+      const int i = 4 * i4 + c;
+      const float G = sG[o + c], G31 = sG[31 * LKP + i], GCl = sG[(BC - 1) * LKP + i];
+      const float gam = expf(G), e1 = expf(G - G31), e2 = expf(G31 - G);
+      const float qv = pq[u][c], kv = pk[u][c], bv = pb[u][c];
+      QG[c] = gam * qv;
+      KT[c] = expf(GCl - G) * kv;
+      EB[c] = gam * bv * kv;
+      EP[c] = e1 * bv * kv;
+      KP[c] = e2 * kv;
+      QP[c] = e1 * qv;
     }
-    __syncthreads();
+    const int wo = r * DK + 4 * i4;
+    *reinterpret_cast<f32x4*>(W + L::QG + wo) = QG;
+    *reinterpret_cast<f32x4*>(W + L::KT + wo) = KT;
+    *reinterpret_cast<f32x4*>(W + L::EB + wo) = EB;
+    *reinterpret_cast<f32x4*>(W + L::EP + wo) = EP;
+    *reinterpret_cast<f32x4*>(W + L::KP + wo) = KP;
+    *reinterpret_cast<f32x4*>(W + L::QP + wo) = QP;
+    *reinterpret_cast<f32x4*>(sEP + o) = EP;
+    *reinterpret_cast<f32x4*>(sKP + o) = KP;
+    *reinterpret_cast<f32x4*>(sQP + o) = QP;
   }
-  float* C = P.ws + base + J.oc;
-  const float* D = J.od >= 0 ? P.ws + base + J.od : nullptr;
+  // v and w for Z, loaded while the products run (lane = token row)
+  f32x4 pv[NEV], pw[NEV];
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int t = wv + 8 * u;
-    if (t >= TM * TN) continue;
-    const int tm = t / TN, tn = t - tm * TN;
+  for (int u = 0; u < NEV; ++u) {
+    const int e = tid + NT * u, s = e % BC, j4 = e / BC;
+    const int rr = s < clen ? s : clen - 1;
+    const size_t x = (size_t)(row0 + rr) * vr + (size_t)h * DV + 4 * j4;
+    const float z = s < clen ? 1.f : 0.f;
+    float t[4];
+    load4<BF16>(a.v, x, t);
+    pv[u] = f32x4{t[0], t[1], t[2], t[3]} * z;
+    load4<BF16>(a.w, x, t);
+    pw[u] = f32x4{t[0], t[1], t[2], t[3]} * z;
+  }
+  __syncthreads();
+
+  // ---- phase 3 ----
+  f32x4 aT[2], aQ[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
+    if (tn <= tm) {
+      aT[u] = mma_lds<float, DK>(zero4(), sEP + 16 * tm * LKP, LKP, sKP + 16 * tn * LKP, LKP);
+      aQ[u] = mma_lds<float, DK>(zero4(), sQP + 16 * tm * LKP, LKP, sKP + 16 * tn * LKP, LKP);
+    } else {
+      aT[u] = aQ[u] = zero4();
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int row = 16 * tm + 4 * g + q, col = 16 * tn + m;
-      float v = J.alpha * acc[u][q];
-      if (D) v += D[(size_t)row * J.ldc + col];
-      if (J.mask && col > row + J.diag) v = 0.f;
-      C[(size_t)row * J.ldc + col] = v;
+      const int r = 16 * tm + 4 * g + q, c = 16 * tn + m;
+      W[L::AQK + r * BC + c] = c <= r ? aQ[u][q] : 0.f;
     }
   }
-}
-
-// ---- A = (I + T)^-1 by forward substitution, fp32 --------------------------------------
-template <int DK, int DV>
-__global__ __launch_bounds__(64) void bwd_inverse_kernel(BwdArgs a) {
-  typedef BwdLayout<DK, DV> L;
-  const int item = blockIdx.x;
-  if (a.tab && item / a.H >= *a.total) return;
-  float* W = a.ws + (size_t)item * L::FLOATS;
-  __shared__ float sT[BC][BC + 1], sX[BC][BC + 1];
-  const int j = threadIdx.x;  // column of A
-  for (int r = 0; r < BC; ++r) sT[r][j] = W[L::T + r * BC + j];
   __syncthreads();
-  for (int r = 0; r < BC; ++r) {
-    float x = 0.f;
-    if (r == j) {
-      x = 1.f;
-    } else if (r > j) {
-      // four independent partial sums shorten the dependent FMA chain
-      float x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
-      int s = j;
-      for (; s + 3 < r; s += 4) {
-        x0 = fmaf(-sT[r][s], sX[s][j], x0);
-        x1 = fmaf(-sT[r][s + 1], sX[s + 1][j], x1);
-        x2 = fmaf(-sT[r][s + 2], sX[s + 2][j], x2);
-        x3 = fmaf(-sT[r][s + 3], sX[s + 3][j], x3);
-      }
-      for (; s < r; ++s) x0 = fmaf(-sT[r][s], sX[s][j], x0);
-      x = (x0 + x1) + (x2 + x3);
+  float *sT = sm + C::O_T, *sA = sm + C::O_A, *sAT = sm + C::O_AT;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 16 * tm + 4 * g + q, c = 16 * tn + m;
+      sT[r * LA + c] = c < r ? aT[u][q] : 0.f;
     }
-    sX[r][j] = x;
   }
-  for (int r = 0; r < BC; ++r) W[L::A + r * BC + j] = sX[r][j];
+  // A is lower triangular: zero its six blocks above the diagonal (and those of A^T)
+  for (int e = tid; e < 6 * 256; e += NT) {
+    const int blk = e >> 8, w = e & 255, rr = w >> 4, cc = w & 15;
+    const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+    const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+    sA[(16 * bi + rr) * LA + 16 * bj + cc] = 0.f;
+    sAT[(16 * bj + cc) * LA + 16 * bi + rr] = 0.f;
+  }
+  __syncthreads();
+
+  // ---- phase 4 ----
+  if (wv == 0) {  // lane = (diagonal block b, column j)
+    const int b = lane >> 4, j = lane & 15;
+    const float* Tb = sT + 16 * b * LA + 16 * b;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = r == j ? 1.f : 0.f;
+#pragma unroll
+      for (int s = 0; s < r; ++s) acc = fmaf(-Tb[r * LA + s], x[s], acc);
+      x[r] = acc;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sA[(16 * b + r) * LA + 16 * b + j] = x[r];
+      sAT[(16 * b + j) * LA + 16 * b + r] = x[r];
+    }
+  }
+  __syncthreads();
+  float* sM = sm + C::O_M;
+  for (int i = 1; i < 4; ++i) {
+    if (wv < i) {  // wavefront j = wv: M = sum_{k=j}^{i-1} T_ik A_kj, kept as M^T
+      f32x4 mm = zero4();
+      for (int k = wv; k < i; ++k)
+        mm = mma_lds<float, 16>(mm, sT + 16 * i * LA + 16 * k, LA, sAT + 16 * wv * LA + 16 * k, LA);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sM[wv * 16 * LM + m * LM + 4 * g + q] = mm[q];
+    }
+    __syncthreads();
+    if (wv < i) {  // A_ij = -A_ii M
+      const f32x4 x = mma_lds<float, 16>(zero4(), sA + 16 * i * LA + 16 * i, LA, sM + wv * 16 * LM, LM);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 4 * g + q;
+        sA[(16 * i + r) * LA + 16 * wv + m] = -x[q];
+        sAT[(16 * wv + m) * LA + 16 * i + r] = -x[q];
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- phase 5 ----
+  float *sEBT = sm + C::O_EBT, *sZT = sm + C::O_ZT;
+#pragma unroll
+  for (int u = 0; u < NAA; ++u) {
+    const int e = tid + NT * u, s = e / (BC / 4), c4 = e - s * (BC / 4);
+    *reinterpret_cast<f32x4*>(W + L::A + s * BC + 4 * c4) = *reinterpret_cast<const f32x4*>(sA + s * LA + 4 * c4);
+  }
+  // E^T (E as this workgroup wrote it in phase 2; lane = token row)
+#pragma unroll
+  for (int u = 0; u < NEK; ++u) {
+    const int e = tid + NT * u, s = e % BC, i4 = e / BC;
+    const f32x4 eb = *reinterpret_cast<const f32x4*>(W + L::EB + s * DK + 4 * i4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sEBT[(4 * i4 + q) * LA + s] = eb[q];
+  }
+#pragma unroll
+  for (int u = 0; u < NEV; ++u) {
+    const int e = tid + NT * u, s = e % BC, j4 = e / BC;
+    const f32x4 z = pw[u] * pv[u];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sZT[(4 * j4 + q) * LA + s] = z[q];
+  }
+  __syncthreads();
+  // A is lower triangular: row block tm needs the first 16 (tm + 1) columns only
+#pragma unroll
+  for (int u = 0; u < NKT; ++u) {
+    const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
+    const f32x4 y = mma_lds_k16<float, BC>(zero4(), sA + 16 * tm * LA, LA, sEBT + 16 * tn * LA, LA, 16 * (tm + 1));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) W[L::Y_ + (16 * tm + 4 * g + q) * DK + 16 * tn + m] = y[q];
+  }
+#pragma unroll
+  for (int u = 0; u < NVT; ++u) {
+    const int t = wv + NWV * u, tm = t / TNV, tn = t - tm * TNV;
+    const f32x4 y = mma_lds_k16<float, BC>(zero4(), sA + 16 * tm * LA, LA, sZT + 16 * tn * LA, LA, 16 * (tm + 1));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) W[L::U + (16 * tm + 4 * g + q) * DV + 16 * tn + m] = y[q];
+  }
 }
 
 // Register prefetch of one chunk's operands for the sequential passes.
@@ -289,7 +361,7 @@ __device__ __forceinline__ void sf_load(const BwdArgs& a, int ci, int h, int jb,
   if (tid < DK / 4) rg = reinterpret_cast<const f32x4*>(Wn + L::GC)[tid];
 }
 
-template <int DK, int DV, int NK4, int NV4, int NC4>
+template <int DK, int DV, int NK4, int NV4, int NC4, bool BF16>
 __device__ __forceinline__ void sb_load(const BwdArgs& a, int ci, int h, int jb, int tid,
                                         f32x4 (&rq)[NK4], f32x4 (&rk)[NK4], f32x4 (&ry)[NK4],
                                         f32x4 (&ra)[NC4], f32x4 (&ro)[NV4], f32x4& rg) {
@@ -309,10 +381,17 @@ __device__ __forceinline__ void sb_load(const BwdArgs& a, int ci, int h, int jb,
     const int e4 = tid + SNT * u, t = e4 % BC, r = 4 * (e4 / BC);
     ra[u] = *reinterpret_cast<const f32x4*>(Wn + L::AQK + (size_t)t * BC + r);
   }
+  // dO straight from the input (rows past the end: a clamped row, zeroed)
+  long long row0 = 0;
+  int clen = 0;
+  bwd_locate(a, ci, row0, clen);
 #pragma unroll
   for (int u = 0; u < NV4; ++u) {
     const int e4 = tid + SNT * u, t = e4 % BC, j = 4 * (e4 / BC);
-    ro[u] = *reinterpret_cast<const f32x4*>(Wn + L::DO + (size_t)t * DV + jb * DVB + j);
+    const int tt = t < clen ? t : clen - 1;
+    float x[4];
+    load4<BF16>(a.dO, (size_t)(row0 + tt) * a.H * DV + (size_t)h * DV + jb * DVB + j, x);
+    ro[u] = f32x4{x[0], x[1], x[2], x[3]} * (t < clen ? 1.f : 0.f);
   }
   if (tid < DK / 4) rg = reinterpret_cast<const f32x4*>(Wn + L::GC)[tid];
 }
@@ -405,7 +484,7 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
 }
 
 // ---- sequential reverse pass: dS' of every chunk, dR, and dS0 ------------------------
-template <int DK, int DV>
+template <int DK, int DV, bool BF16>
 __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
   typedef BwdLayout<DK, DV> L;
   constexpr int NB = DV / DVB, LK = DK + 4, LC = BC + 4;
@@ -433,7 +512,7 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
     sdST[j * LK + i] = a.dST ? a.dST[(size_t)nh * DK * DV + (size_t)i * DV + jb * DVB + j] : 0.f;
   }
   f32x4 rq[NK4], rk[NK4], ry[NK4], ra[NC4], ro[NV4], rg = zero4();
-  if (c0 < c1) sb_load<DK, DV, NK4, NV4, NC4>(a, c1 - 1, h, jb, tid, rq, rk, ry, ra, ro, rg);
+  if (c0 < c1) sb_load<DK, DV, NK4, NV4, NC4, BF16>(a, c1 - 1, h, jb, tid, rq, rk, ry, ra, ro, rg);
   for (int ci = c1 - 1; ci >= c0; --ci) {
     float* W = a.ws + ((size_t)ci * a.H + h) * L::FLOATS;
 #pragma unroll
@@ -476,7 +555,7 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
     }
     __syncthreads();
     // the previous chunk (the last iteration reloads the current one: no branch)
-    sb_load<DK, DV, NK4, NV4, NC4>(a, ci - 1 >= c0 ? ci - 1 : ci, h, jb, tid, rq, rk, ry, ra, ro, rg);
+    sb_load<DK, DV, NK4, NV4, NC4, BF16>(a, ci - 1 >= c0 ? ci - 1 : ci, h, jb, tid, rq, rk, ry, ra, ro, rg);
     // dR = A_qk^T dO + K_tail dS'  [BC][DVB]
     for (int t = wv; t < (BC / 16) * (DVB / 16); t += SNT / 64) {
       const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
@@ -928,32 +1007,6 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
   }
 }
 
-BmmJob job(size_t oa, int lda, bool ta, size_t ob, int ldb, bool tb, size_t oc, int ldc, int N, int K,
-           float alpha = 1.f, long long od = -1, int mask = 0, int diag = 0) {
-  BmmJob j;
-  j.oa = oa; j.ob = ob; j.oc = oc; j.od = od;
-  j.lda = lda; j.ldb = ldb; j.ldc = ldc; j.N = N; j.K = K;
-  j.ta = ta; j.tb = tb; j.mask = mask; j.diag = diag;
-  j.alpha = alpha;
-  return j;
-}
-
-hipError_t bmm_group(const BwdArgs& a, size_t stride, int items, std::initializer_list<BmmJob> jobs,
-                     hipStream_t st) {
-  BmmJobs P{};
-  int n = 0;
-  for (const BmmJob& j : jobs) {
-    if (n >= MAXJOBS || j.N % 32 || j.K % 32 || j.N > 128) return hipErrorInvalidValue;
-    P.j[n++] = j;
-  }
-  P.ws = a.ws;
-  P.stride = stride;
-  P.H = a.H;
-  P.total = a.tab ? a.total : nullptr;
-  hipLaunchKernelGGL(bmm_multi_kernel, dim3(items, n), dim3(512), 0, st, P);
-  return hipGetLastError();
-}
-
 template <typename Kern>
 hipError_t set_lds(Kern k, size_t bytes) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -968,27 +1021,28 @@ hipError_t set_lds(Kern k, size_t bytes) {
 
 template <int DK, int DV>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
-  typedef BwdLayout<DK, DV> L;
   const int items = a.chunks * a.H;
-  const size_t F = L::FLOATS;
   const dim3 gi(items > 0 ? items : 1);
-  if (items > 0) {
-  if (a.in_bf16) {
-    if (a.la_bf16) hipLaunchKernelGGL((bwd_prep_kernel<DK, DV, true, true>), gi, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((bwd_prep_kernel<DK, DV, true, false>), gi, dim3(256), 0, st, a);
-  } else {
-    if (a.la_bf16) hipLaunchKernelGGL((bwd_prep_kernel<DK, DV, false, true>), gi, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((bwd_prep_kernel<DK, DV, false, false>), gi, dim3(256), 0, st, a);
-  }
-  GDR2_CK(hipGetLastError());
-  // T = tril(E' K'^T, -1), A_qk = tril(Q' K'^T, 0)  (centred factors cancel)
-  GDR2_CK(bmm_group(a, F, items, {job(L::EP, DK, 0, L::KP, DK, 1, L::T, BC, BC, DK, 1.f, -1, 1, -1),
-                                  job(L::QP, DK, 0, L::KP, DK, 1, L::AQK, BC, BC, DK, 1.f, -1, 1, 0)}, st));
-  hipLaunchKernelGGL((bwd_inverse_kernel<DK, DV>), gi, dim3(64), 0, st, a);
-  GDR2_CK(hipGetLastError());
-  // Y = A E, U = A Z
-  GDR2_CK(bmm_group(a, F, items, {job(L::A, BC, 0, L::EB, DK, 0, L::Y_, DK, DK, BC),
-                                  job(L::A, BC, 0, L::Z, DV, 0, L::U, DV, DV, BC)}, st));
+  if (items > 0) {  // decay, scaled rows, T, A_qk, A, Y and U
+    typedef FrontCfg<DK, DV> FC;
+    static bool attr[64] = {};
+    int dev = 0;
+    GDR2_CK(hipGetDevice(&dev));
+    if (dev < 0 || dev >= 64 || !attr[dev]) {
+      GDR2_CK(set_lds(&bwd_front_kernel<DK, DV, true, true>, FC::BYTES));
+      GDR2_CK(set_lds(&bwd_front_kernel<DK, DV, true, false>, FC::BYTES));
+      GDR2_CK(set_lds(&bwd_front_kernel<DK, DV, false, true>, FC::BYTES));
+      GDR2_CK(set_lds(&bwd_front_kernel<DK, DV, false, false>, FC::BYTES));
+      if (dev >= 0 && dev < 64) attr[dev] = true;
+    }
+    if (a.in_bf16) {
+      if (a.la_bf16) hipLaunchKernelGGL((bwd_front_kernel<DK, DV, true, true>), gi, dim3(FC::NT), FC::BYTES, st, a);
+      else hipLaunchKernelGGL((bwd_front_kernel<DK, DV, true, false>), gi, dim3(FC::NT), FC::BYTES, st, a);
+    } else {
+      if (a.la_bf16) hipLaunchKernelGGL((bwd_front_kernel<DK, DV, false, true>), gi, dim3(FC::NT), FC::BYTES, st, a);
+      else hipLaunchKernelGGL((bwd_front_kernel<DK, DV, false, false>), gi, dim3(FC::NT), FC::BYTES, st, a);
+    }
+    GDR2_CK(hipGetLastError());
   }
   // sequential passes (with no chunks they only pass dS_T through to dS0)
   {
@@ -1001,13 +1055,15 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     GDR2_CK(hipGetDevice(&dev));
     if (dev < 0 || dev >= 64 || !attr[dev]) {
       GDR2_CK(set_lds(&bwd_state_fwd_kernel<DK, DV>, lf));
-      GDR2_CK(set_lds(&bwd_state_bwd_kernel<DK, DV>, lb));
+      GDR2_CK(set_lds(&bwd_state_bwd_kernel<DK, DV, true>, lb));
+      GDR2_CK(set_lds(&bwd_state_bwd_kernel<DK, DV, false>, lb));
       if (dev >= 0 && dev < 64) attr[dev] = true;
     }
     const dim3 gs((unsigned)(((size_t)a.N * a.H + 7) / 8 * 8 * (DV / DVB)));
     hipLaunchKernelGGL((bwd_state_fwd_kernel<DK, DV>), gs, dim3(SNT), lf, st, a);
     GDR2_CK(hipGetLastError());
-    hipLaunchKernelGGL((bwd_state_bwd_kernel<DK, DV>), gs, dim3(SNT), lb, st, a);
+    if (a.in_bf16) hipLaunchKernelGGL((bwd_state_bwd_kernel<DK, DV, true>), gs, dim3(SNT), lb, st, a);
+    else hipLaunchKernelGGL((bwd_state_bwd_kernel<DK, DV, false>), gs, dim3(SNT), lb, st, a);
     GDR2_CK(hipGetLastError());
   }
   if (items <= 0) return hipSuccess;
