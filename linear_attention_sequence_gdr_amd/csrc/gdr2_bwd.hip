@@ -667,6 +667,15 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
   const size_t kr = (size_t)a.H * DK, vr = (size_t)a.H * DV;
   float* sAT = sm + C::O_AT;
+  // Products with a triangular left factor over the chunk's 64 rows, for row
+  // tile tm: a lower-triangular factor has no columns past 16 (tm + 1), an
+  // upper-triangular one none before 16 tm (A, dA_qk, dT and their transposes)
+  auto mm_lo = [&](const float* X, const float* Bt, int tm) {
+    return mma_lds_k16<float, BC>(zero4(), X, LA, Bt, LA, 16 * (tm + 1));
+  };
+  auto mm_hi = [&](const float* X, const float* Bt, int tm) {
+    return mma_lds_k16<float, BC>(zero4(), X + 16 * tm, LA, Bt + 16 * tm, LA, BC - 16 * tm);
+  };
   float *sO = sm + C::O_O, *sDR = sm + C::O_DR, *sR = sm + C::O_R, *sZ = sm + C::O_Z;
   float *sS = sm + C::O_S, *sDS = sm + C::O_DS, *sDRT = sm + C::O_DRT;
   float *sW = sm + C::O_W, *sV = sm + C::O_V;
@@ -771,7 +780,7 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
     }
     {  // dZ = A^T dR over this slice's 32 value channels: one [16][16] tile per wavefront
       const int tm = wv >> 1, tn = wv & 1;
-      const f32x4 z = mma_lds<float, BC>(zero4(), sAT + 16 * tm * LA, LA, sDRT + 16 * tn * LA, LA);
+      const f32x4 z = mm_hi(sAT + 16 * tm * LA, sDRT + 16 * tn * LA, tm);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = 16 * tm + 4 * g + q, c = 16 * tn + m;
@@ -820,7 +829,7 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
 #pragma unroll
   for (int u = 0; u < NKT; ++u) {
     const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
-    aX[u] = mma_lds<float, BC>(zero4(), sAT + 16 * tm * LA, LA, sDYT + 16 * tn * LA, LA);
+    aX[u] = mm_hi(sAT + 16 * tm * LA, sDYT + 16 * tn * LA, tm);
   }
   __syncthreads();
 
@@ -862,8 +871,8 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
 #pragma unroll
   for (int u = 0; u < NKT; ++u) {
     const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
-    aP3[u] = mma_lds<float, BC>(zero4(), sAQT + 16 * tm * LA, LA, sQPT + 16 * tn * LA, LA);
-    aP4[u] = mma_lds<float, BC>(zero4(), sAQ + 16 * tm * LA, LA, sKPT + 16 * tn * LA, LA);
+    aP3[u] = mm_hi(sAQT + 16 * tm * LA, sQPT + 16 * tn * LA, tm);
+    aP4[u] = mm_lo(sAQ + 16 * tm * LA, sKPT + 16 * tn * LA, tm);
   }
   __syncthreads();
 
@@ -884,7 +893,7 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
 #pragma unroll
   for (int u = 0; u < NCT; ++u) {
     const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
-    const f32x4 w4 = mma_lds<float, BC>(zero4(), sAT + 16 * tm * LA, LA, sDAT + 16 * tn * LA, LA);
+    const f32x4 w4 = mm_hi(sAT + 16 * tm * LA, sDAT + 16 * tn * LA, tm);
 #pragma unroll
     for (int q = 0; q < 4; ++q) sWM[(16 * tm + 4 * g + q) * LA + 16 * tn + m] = w4[q];
   }
@@ -895,9 +904,7 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
     const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
     // A is unit lower triangular: column block tn of A^T has no rows past
     // 16 (tn + 1); tiles above the diagonal are masked out below
-    aT[u] = tn <= tm ? mma_lds_k16<float, BC>(zero4(), sWM + 16 * tm * LA, LA, sA + 16 * tn * LA, LA,
-                                              16 * (tn + 1))
-                     : zero4();
+    aT[u] = tn <= tm ? mm_lo(sWM + 16 * tm * LA, sA + 16 * tn * LA, tn) : zero4();
   }
   __syncthreads();
 
@@ -940,8 +947,8 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
 #pragma unroll
   for (int u = 0; u < NKT; ++u) {
     const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
-    aP1[u] = mma_lds<float, BC>(zero4(), sDT + 16 * tm * LA, LA, sKPT + 16 * tn * LA, LA);
-    aP2[u] = mma_lds<float, BC>(zero4(), sDTT + 16 * tm * LA, LA, sEPT + 16 * tn * LA, LA);
+    aP1[u] = mm_lo(sDT + 16 * tm * LA, sKPT + 16 * tn * LA, tm);
+    aP2[u] = mm_hi(sDTT + 16 * tm * LA, sEPT + 16 * tn * LA, tm);
   }
   __syncthreads();
 
