@@ -348,10 +348,7 @@ __device__ __forceinline__ void sf_load(const BwdArgs& a, int ci, int h, int jb,
   for (int u = 0; u < NK4; ++u) {
     const int e4 = tid + SNT * u;
     ry[u] = reinterpret_cast<const f32x4*>(Wn + L::Y_)[e4];
-    // K_tail is stored transposed: lane = token row, so that the transposing
-    // LDS stores of a wavefront hit 64 consecutive words
-    const int t = e4 % BC, i = 4 * (e4 / BC);
-    rk[u] = *reinterpret_cast<const f32x4*>(Wn + L::KT + (size_t)t * DK + i);
+    rk[u] = reinterpret_cast<const f32x4*>(Wn + L::KT)[e4];
   }
 #pragma unroll
   for (int u = 0; u < NV4; ++u) {
@@ -367,27 +364,23 @@ __device__ __forceinline__ void sb_load(const BwdArgs& a, int ci, int h, int jb,
                                         f32x4 (&ra)[NC4], f32x4 (&ro)[NV4], f32x4& rg) {
   typedef BwdLayout<DK, DV> L;
   const float* Wn = a.ws + ((size_t)ci * a.H + h) * L::FLOATS;
-  // Q_g, Y, A_qk and dO are stored transposed: lane = token row, so that the
-  // transposing LDS stores of a wavefront hit 64 consecutive words
+  // row-major blocks, 16-byte loads in address order
 #pragma unroll
   for (int u = 0; u < NK4; ++u) {
-    const int e4 = tid + SNT * u, t = e4 % BC, i = 4 * (e4 / BC);
-    rq[u] = *reinterpret_cast<const f32x4*>(Wn + L::QG + (size_t)t * DK + i);
+    const int e4 = tid + SNT * u;
+    rq[u] = reinterpret_cast<const f32x4*>(Wn + L::QG)[e4];
     rk[u] = reinterpret_cast<const f32x4*>(Wn + L::KT)[e4];
-    ry[u] = *reinterpret_cast<const f32x4*>(Wn + L::Y_ + (size_t)t * DK + i);
+    ry[u] = reinterpret_cast<const f32x4*>(Wn + L::Y_)[e4];
   }
 #pragma unroll
-  for (int u = 0; u < NC4; ++u) {
-    const int e4 = tid + SNT * u, t = e4 % BC, r = 4 * (e4 / BC);
-    ra[u] = *reinterpret_cast<const f32x4*>(Wn + L::AQK + (size_t)t * BC + r);
-  }
+  for (int u = 0; u < NC4; ++u) ra[u] = reinterpret_cast<const f32x4*>(Wn + L::AQK)[tid + SNT * u];
   // dO straight from the input (rows past the end: a clamped row, zeroed)
   long long row0 = 0;
   int clen = 0;
   bwd_locate(a, ci, row0, clen);
 #pragma unroll
   for (int u = 0; u < NV4; ++u) {
-    const int e4 = tid + SNT * u, t = e4 % BC, j = 4 * (e4 / BC);
+    const int e4 = tid + SNT * u, t = e4 / (DVB / 4), j = 4 * (e4 - t * (DVB / 4));
     const int tt = t < clen ? t : clen - 1;
     float x[4];
     load4<BF16>(a.dO, (size_t)(row0 + tt) * a.H * DV + (size_t)h * DV + jb * DVB + j, x);
@@ -399,7 +392,7 @@ __device__ __forceinline__ void sb_load(const BwdArgs& a, int ci, int h, int jb,
 // ---- sequential state pass: the state entering every chunk --------------------------
 // One workgroup of SNT threads per (sequence, head, 32 value channels); the
 // state block is
-// kept transposed in LDS (S^T, the B operand of Y S).  The next chunk's
+// kept transposed in LDS (S^T, the B operand of Y S).  The next two chunks'
 // operands are loaded into registers (16-byte loads) while the current chunk
 // computes.
 template <int DK, int DV>
@@ -412,8 +405,8 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* sST = reinterpret_cast<float*>(smem);  // [DVB][LK]
   float* sY = sST + DVB * LK;                   // [BC][LK]
-  float* sKtT = sY + BC * LK;                   // [DK][LC]
-  float* sRT = sKtT + DK * LC;                  // [DVB][LC]
+  float* sKt = sY + BC * LK;                    // [BC][LK]
+  float* sRT = sKt + BC * LK;                   // [DVB][LC]
   float* sU = sRT + DVB * LC;                   // [BC][LV]
   float* sGC = sU + BC * LV;                    // [DK]
   // the NB value blocks of one (sequence, head) share an XCD (workgroups go
@@ -429,19 +422,18 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
     const int i = e / DVB, j = e - i * DVB;
     sST[j * LK + i] = a.S0 ? a.S0[(size_t)nh * DK * DV + (size_t)i * DV + jb * DVB + j] : 0.f;
   }
-  f32x4 ry[NK4], rk[NK4], ru[NV4], rg = zero4();
-  if (c0 < c1) sf_load<DK, DV, NK4, NV4>(a, c0, h, jb, tid, ry, rk, ru, rg);
-  for (int ci = c0; ci < c1; ++ci) {
+  // two register sets in turn: chunks ci + 1 and ci + 2 are in flight while chunk ci computes
+  f32x4 ry0[NK4], rk0[NK4], ru0[NV4], rg0 = zero4();
+  f32x4 ry1[NK4], rk1[NK4], ru1[NV4], rg1 = zero4();
+  if (c0 < c1) sf_load<DK, DV, NK4, NV4>(a, c0, h, jb, tid, ry0, rk0, ru0, rg0);
+  if (c0 + 1 < c1) sf_load<DK, DV, NK4, NV4>(a, c0 + 1, h, jb, tid, ry1, rk1, ru1, rg1);
+  auto step = [&](const int ci, f32x4 (&ry)[NK4], f32x4 (&rk)[NK4], f32x4 (&ru)[NV4], f32x4& rg) {
     float* W = a.ws + ((size_t)ci * a.H + h) * L::FLOATS;
 #pragma unroll
     for (int u = 0; u < NK4; ++u) {
       const int e4 = tid + SNT * u, r = e4 / (DK / 4), i = 4 * (e4 - r * (DK / 4));
       *reinterpret_cast<f32x4*>(sY + r * LK + i) = ry[u];
-      const int t = e4 % BC, it = 4 * (e4 / BC);  // K_tail: lane = token row (sf_load)
-      sKtT[(it + 0) * LC + t] = rk[u][0];
-      sKtT[(it + 1) * LC + t] = rk[u][1];
-      sKtT[(it + 2) * LC + t] = rk[u][2];
-      sKtT[(it + 3) * LC + t] = rk[u][3];
+      *reinterpret_cast<f32x4*>(sKt + r * LK + i) = rk[u];
     }
 #pragma unroll
     for (int u = 0; u < NV4; ++u) {
@@ -454,8 +446,9 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
       W[L::S + (size_t)i * DV + jb * DVB + j] = sST[j * LK + i];
     }
     __syncthreads();
-    // the next chunk (the last iteration reloads the current one: no branch)
-    sf_load<DK, DV, NK4, NV4>(a, ci + 1 < c1 ? ci + 1 : ci, h, jb, tid, ry, rk, ru, rg);
+    // the chunk after next into the registers just stored (near the end the
+    // current chunk is reloaded instead: no branch)
+    sf_load<DK, DV, NK4, NV4>(a, ci + 2 < c1 ? ci + 2 : ci, h, jb, tid, ry, rk, ru, rg);
     // R = U - Y S  [BC][DVB], kept for the output paths as well
     for (int t = wv; t < (BC / 16) * (DVB / 16); t += SNT / 64) {
       const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
@@ -472,7 +465,8 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
     // S <- Diag(gamma_C) S + K_tail^T R  [DK][DVB]; each lane owns its entries
     for (int t = wv; t < (DK / 16) * (DVB / 16); t += SNT / 64) {
       const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
-      const f32x4 acc = mma_lds<float, BC>(zero4(), sKtT + 16 * tm * LC, LC, sRT + 16 * tn * LC, LC);
+      // K_tail^T as the left factor: K_tail read K-major from its row-major block
+      const f32x4 acc = mma_lds_f32<BC, true, false>(zero4(), sKt + 16 * tm, LK, sRT + 16 * tn * LC, LC);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int i = 16 * tm + 4 * g + q, j = 16 * tn + m;
@@ -480,7 +474,13 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
+  };
+  int ci = c0;
+  for (; ci + 1 < c1; ci += 2) {
+    step(ci, ry0, rk0, ru0, rg0);
+    step(ci + 1, ry1, rk1, ru1, rg1);
   }
+  if (ci < c1) step(ci, ry0, rk0, ru0, rg0);
 }
 
 // ---- sequential reverse pass: dS' of every chunk, dR, and dS0 ------------------------
@@ -490,13 +490,14 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
   constexpr int NB = DV / DVB, LK = DK + 4, LC = BC + 4;
   constexpr int NK4 = BC * DK / 4 / SNT, NV4 = BC * DVB / 4 / SNT, NC4 = BC * BC / 4 / SNT;
   extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int LV = DVB + 4;
   float* sdST = reinterpret_cast<float*>(smem);  // [DVB][LK]  dS^T
-  float* sAqkT = sdST + DVB * LK;                // [BC][LC]   A_qk^T
-  float* sdOT = sAqkT + BC * LC;                 // [DVB][LC]  dO^T
-  float* sKt = sdOT + DVB * LC;                  // [BC][LK]   K_tail
-  float* sQgT = sKt + BC * LK;                   // [DK][LC]   Q_g^T
-  float* sYT = sQgT + DK * LC;                   // [DK][LC]   Y^T
-  float* sdRT = sYT + DK * LC;                   // [DVB][LC]  dR^T
+  float* sAqk = sdST + DVB * LK;                 // [BC][LC]   A_qk
+  float* sdO = sAqk + BC * LC;                   // [BC][LV]   dO
+  float* sKt = sdO + BC * LV;                    // [BC][LK]   K_tail
+  float* sQg = sKt + BC * LK;                    // [BC][LK]   Q_g
+  float* sY = sQg + BC * LK;                     // [BC][LK]   Y
+  float* sdRT = sY + BC * LK;                    // [DVB][LC]  dR^T
   float* sGC = sdRT + DVB * LC;                  // [DK]
   // the NB value blocks of one (sequence, head) share an XCD (workgroups go
   // round the eight XCDs in order), so their reads of the chunk blocks they
@@ -517,36 +518,20 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
     float* W = a.ws + ((size_t)ci * a.H + h) * L::FLOATS;
 #pragma unroll
     for (int u = 0; u < NK4; ++u) {
-      const int e4 = tid + SNT * u;
-      {
-        const int t = e4 / (DK / 4), i = 4 * (e4 - t * (DK / 4));
-        *reinterpret_cast<f32x4*>(sKt + t * LK + i) = rk[u];
-      }
-      const int t = e4 % BC, i = 4 * (e4 / BC);  // lane = token row (sb_load)
-      sQgT[(i + 0) * LC + t] = rq[u][0];
-      sQgT[(i + 1) * LC + t] = rq[u][1];
-      sQgT[(i + 2) * LC + t] = rq[u][2];
-      sQgT[(i + 3) * LC + t] = rq[u][3];
-      sYT[(i + 0) * LC + t] = ry[u][0];
-      sYT[(i + 1) * LC + t] = ry[u][1];
-      sYT[(i + 2) * LC + t] = ry[u][2];
-      sYT[(i + 3) * LC + t] = ry[u][3];
+      const int e4 = tid + SNT * u, t = e4 / (DK / 4), i = 4 * (e4 - t * (DK / 4));
+      *reinterpret_cast<f32x4*>(sKt + t * LK + i) = rk[u];
+      *reinterpret_cast<f32x4*>(sQg + t * LK + i) = rq[u];
+      *reinterpret_cast<f32x4*>(sY + t * LK + i) = ry[u];
     }
 #pragma unroll
-    for (int u = 0; u < NC4; ++u) {  // A_qk[t][r..r+3] -> A_qk^T
-      const int e4 = tid + SNT * u, t = e4 % BC, r = 4 * (e4 / BC);
-      sAqkT[(r + 0) * LC + t] = ra[u][0];
-      sAqkT[(r + 1) * LC + t] = ra[u][1];
-      sAqkT[(r + 2) * LC + t] = ra[u][2];
-      sAqkT[(r + 3) * LC + t] = ra[u][3];
+    for (int u = 0; u < NC4; ++u) {
+      const int e4 = tid + SNT * u, t = e4 / (BC / 4), r = 4 * (e4 - t * (BC / 4));
+      *reinterpret_cast<f32x4*>(sAqk + t * LC + r) = ra[u];
     }
 #pragma unroll
-    for (int u = 0; u < NV4; ++u) {  // dO[t][j..j+3] -> dO^T
-      const int e4 = tid + SNT * u, t = e4 % BC, j = 4 * (e4 / BC);
-      sdOT[(j + 0) * LC + t] = ro[u][0];
-      sdOT[(j + 1) * LC + t] = ro[u][1];
-      sdOT[(j + 2) * LC + t] = ro[u][2];
-      sdOT[(j + 3) * LC + t] = ro[u][3];
+    for (int u = 0; u < NV4; ++u) {
+      const int e4 = tid + SNT * u, t = e4 / (DVB / 4), j = 4 * (e4 - t * (DVB / 4));
+      *reinterpret_cast<f32x4*>(sdO + t * LV + j) = ro[u];
     }
     if (tid < DK / 4) *reinterpret_cast<f32x4*>(sGC + 4 * tid) = rg;
     for (int e = tid; e < DK * DVB; e += SNT) {  // dL/d(state leaving chunk ci)
@@ -559,7 +544,8 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
     // dR = A_qk^T dO + K_tail dS'  [BC][DVB]
     for (int t = wv; t < (BC / 16) * (DVB / 16); t += SNT / 64) {
       const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
-      f32x4 acc = mma_lds<float, BC>(zero4(), sAqkT + 16 * tm * LC, LC, sdOT + 16 * tn * LC, LC);
+      // A_qk^T and dO both read K-major from their row-major blocks
+      f32x4 acc = mma_lds_f32<BC, true, true>(zero4(), sAqk + 16 * tm, LC, sdO + 16 * tn, LV);
       acc = mma_lds<float, DK>(acc, sKt + 16 * tm * LK, LK, sdST + 16 * tn * LK, LK);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -572,8 +558,8 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
     // dS <- Q_g^T dO + Diag(gamma_C) dS' - Y^T dR  [DK][DVB]; each lane owns its entries
     for (int t = wv; t < (DK / 16) * (DVB / 16); t += SNT / 64) {
       const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
-      const f32x4 acc = mma_lds<float, BC>(zero4(), sQgT + 16 * tm * LC, LC, sdOT + 16 * tn * LC, LC);
-      const f32x4 acy = mma_lds<float, BC>(zero4(), sYT + 16 * tm * LC, LC, sdRT + 16 * tn * LC, LC);
+      const f32x4 acc = mma_lds_f32<BC, true, true>(zero4(), sQg + 16 * tm, LK, sdO + 16 * tn, LV);
+      const f32x4 acy = mma_lds_f32<BC, true, false>(zero4(), sY + 16 * tm, LK, sdRT + 16 * tn * LC, LC);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int i = 16 * tm + 4 * g + q, j = 16 * tn + m;
@@ -1055,8 +1041,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   {
     constexpr int LK = DK + 4, LC = BC + 4;
     constexpr int LV = DVB + 4;
-    const size_t lf = (size_t)(DVB * LK + BC * LK + DK * LC + DVB * LC + BC * LV + DK) * 4;
-    const size_t lb = (size_t)(DVB * LK + BC * LC + DVB * LC + BC * LK + 2 * DK * LC + DVB * LC + DK) * 4;
+    const size_t lf = (size_t)(DVB * LK + 2 * BC * LK + DVB * LC + BC * LV + DK) * 4;
+    const size_t lb = (size_t)(DVB * LK + BC * LC + BC * (DVB + 4) + 3 * BC * LK + DVB * LC + DK) * 4;
     static bool attr[64] = {};
     int dev = 0;
     GDR2_CK(hipGetDevice(&dev));

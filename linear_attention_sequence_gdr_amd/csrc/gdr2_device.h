@@ -157,6 +157,38 @@ __device__ __forceinline__ f32x4 mma_lds_k16(f32x4 acc, const E* A, int lda, con
   return acc;
 }
 
+// acc += A[16 x K] * B[K x 16] in fp32 from LDS, each operand either
+// K-contiguous as in mma_lds (A row m at A + m*lda, B column n at B + n*ldb)
+// or K-major (TA: A element (m, k) at A + k*lda + m; TB: B element (k, n) at
+// B + k*ldb + n).  A K-major operand takes four 4-byte reads per K = 16
+// block; within a 16-lane group they hit consecutive words.
+template <int K, bool TA, bool TB>
+__device__ __forceinline__ f32x4 mma_lds_f32(f32x4 acc, const float* A, int lda, const float* B, int ldb) {
+  static_assert(K % 16 == 0, "K must be a multiple of 16");
+  const int m = lane_id() & 15, g = lane_id() >> 4;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    float av[4], bv[4];
+    if constexpr (TA) {
+      const float* a = A + (k0 + 4 * g) * lda + m;
+      av[0] = a[0]; av[1] = a[lda]; av[2] = a[2 * lda]; av[3] = a[3 * lda];
+    } else {
+      const float4 x = *reinterpret_cast<const float4*>(A + m * lda + k0 + 4 * g);
+      av[0] = x.x; av[1] = x.y; av[2] = x.z; av[3] = x.w;
+    }
+    if constexpr (TB) {
+      const float* b = B + (k0 + 4 * g) * ldb + m;
+      bv[0] = b[0]; bv[1] = b[ldb]; bv[2] = b[2 * ldb]; bv[3] = b[3 * ldb];
+    } else {
+      const float4 x = *reinterpret_cast<const float4*>(B + m * ldb + k0 + 4 * g);
+      bv[0] = x.x; bv[1] = x.y; bv[2] = x.z; bv[3] = x.w;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bv[q], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 }  // namespace gdr2
