@@ -94,8 +94,9 @@ struct FrontCfg {
   // phases 3-5: T, A, A^T [64][64], M^T [16][LM] for three wavefronts
   static constexpr int O_T = 0, O_A = O_T + BC * LA, O_AT = O_A + BC * LA, O_M = O_AT + BC * LA,
                        E2 = O_M + 3 * 16 * LM;
-  // phase 5: E^T [DK][64], Z^T [DV][64]
-  static constexpr int O_EBT = E2, O_ZT = O_EBT + DK * LA, E3 = O_ZT + DV * LA;
+  // phase 5: E [64][DK], Z [64][DV] (row-major, read K-major)
+  static constexpr int LZ = DV + 4;
+  static constexpr int O_EB = E2, O_Z = O_EB + BC * LKP, E3 = O_Z + BC * LZ;
   static constexpr int O_PS = E1 > E3 ? E1 : E3, FLOATS = O_PS + NT;
   static constexpr size_t BYTES = (size_t)FLOATS * 4;
   static_assert(BYTES <= 160 * 1024, "LDS budget exceeded");
@@ -202,11 +203,11 @@ __global__ __launch_bounds__(512) void bwd_front_kernel(BwdArgs a) {
     *reinterpret_cast<f32x4*>(sKP + o) = KP;
     *reinterpret_cast<f32x4*>(sQP + o) = QP;
   }
-  // v and w for Z, loaded while the products run (lane = token row)
+  // v and w for Z, loaded while the products run
   f32x4 pv[NEV], pw[NEV];
 #pragma unroll
   for (int u = 0; u < NEV; ++u) {
-    const int e = tid + NT * u, s = e % BC, j4 = e / BC;
+    const int e = tid + NT * u, s = e / (DV / 4), j4 = e - s * (DV / 4);
     const int rr = s < clen ? s : clen - 1;
     const size_t x = (size_t)(row0 + rr) * vr + (size_t)h * DV + 4 * j4;
     const float z = s < clen ? 1.f : 0.f;
@@ -298,40 +299,36 @@ __global__ __launch_bounds__(512) void bwd_front_kernel(BwdArgs a) {
   }
 
   // ---- phase 5 ----
-  float *sEBT = sm + C::O_EBT, *sZT = sm + C::O_ZT;
+  float *sEB = sm + C::O_EB, *sZ = sm + C::O_Z;
 #pragma unroll
   for (int u = 0; u < NAA; ++u) {
     const int e = tid + NT * u, s = e / (BC / 4), c4 = e - s * (BC / 4);
     *reinterpret_cast<f32x4*>(W + L::A + s * BC + 4 * c4) = *reinterpret_cast<const f32x4*>(sA + s * LA + 4 * c4);
   }
-  // E^T (E as this workgroup wrote it in phase 2; lane = token row)
+  // E as this workgroup wrote it in phase 2, and Z = w * v
 #pragma unroll
   for (int u = 0; u < NEK; ++u) {
-    const int e = tid + NT * u, s = e % BC, i4 = e / BC;
-    const f32x4 eb = *reinterpret_cast<const f32x4*>(W + L::EB + s * DK + 4 * i4);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) sEBT[(4 * i4 + q) * LA + s] = eb[q];
+    const int e = tid + NT * u, s = e / (DK / 4), i4 = e - s * (DK / 4);
+    *reinterpret_cast<f32x4*>(sEB + s * LKP + 4 * i4) = reinterpret_cast<const f32x4*>(W + L::EB)[e];
   }
 #pragma unroll
   for (int u = 0; u < NEV; ++u) {
-    const int e = tid + NT * u, s = e % BC, j4 = e / BC;
-    const f32x4 z = pw[u] * pv[u];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) sZT[(4 * j4 + q) * LA + s] = z[q];
+    const int e = tid + NT * u, s = e / (DV / 4), j4 = e - s * (DV / 4);
+    *reinterpret_cast<f32x4*>(sZ + s * C::LZ + 4 * j4) = pw[u] * pv[u];
   }
   __syncthreads();
   // A is lower triangular: row block tm needs the first 16 (tm + 1) columns only
 #pragma unroll
   for (int u = 0; u < NKT; ++u) {
     const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
-    const f32x4 y = mma_lds_k16<float, BC>(zero4(), sA + 16 * tm * LA, LA, sEBT + 16 * tn * LA, LA, 16 * (tm + 1));
+    const f32x4 y = mma_lds_f32<BC, false, true>(zero4(), sA + 16 * tm * LA, LA, sEB + 16 * tn, LKP, 16 * (tm + 1));
 #pragma unroll
     for (int q = 0; q < 4; ++q) W[L::Y_ + (16 * tm + 4 * g + q) * DK + 16 * tn + m] = y[q];
   }
 #pragma unroll
   for (int u = 0; u < NVT; ++u) {
     const int t = wv + NWV * u, tm = t / TNV, tn = t - tm * TNV;
-    const f32x4 y = mma_lds_k16<float, BC>(zero4(), sA + 16 * tm * LA, LA, sZT + 16 * tn * LA, LA, 16 * (tm + 1));
+    const f32x4 y = mma_lds_f32<BC, false, true>(zero4(), sA + 16 * tm * LA, LA, sZ + 16 * tn, C::LZ, 16 * (tm + 1));
 #pragma unroll
     for (int q = 0; q < 4; ++q) W[L::U + (16 * tm + 4 * g + q) * DV + 16 * tn + m] = y[q];
   }
@@ -590,9 +587,10 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
 //   final    dq, dk, db from the accumulators (the centred factors put back
 //            per element), and dg as the reverse cumulative sum over the
 //            chunk's rows (row blocks summed in parallel, then scanned).
-// Every operand is staged K-contiguous in LDS (rows padded by 4 floats, so a
-// 16-lane group's 16-byte reads hit distinct banks); the fp32 products run on
-// 16x16x4 MFMA.  Tiles of a [64][N] result go round the eight wavefronts
+// Operands are staged in LDS from 16-byte loads in address order, rows padded
+// by 4 floats, and read either K-contiguous (16-byte reads) or K-major (four
+// 4-byte reads per K = 16 block); a 16-lane group's reads hit distinct banks
+// either way.  The fp32 products run on 16x16x4 MFMA.  Tiles of a [64][N] result go round the eight wavefronts
 // (tile t = wave + 8u, row tile t / (N/16), column tile t % (N/16)).  Each
 // phase's global loads are issued into registers one phase (or one slice)
 // ahead, so they overlap the products of the phase before.  Rows past the
@@ -602,8 +600,9 @@ struct OutCfg {
   static constexpr int NT = 512, NWV = 8, KC = 32, LS = KC + 4, LA = BC + 4, LKP = DK + 4;
   static constexpr int NKT = DK / 32;  // [64][DK] tiles per wavefront
   static constexpr int NCT = 2;        // [64][64] tiles per wavefront
-  // LDS offsets in floats.  A^T lives through phase 3; region R1 is reused.
-  static constexpr int O_AT = 0, O_R1 = O_AT + BC * LA;
+  // LDS offsets in floats.  A (row-major) lives through phase 3; region R1
+  // is reused.
+  static constexpr int O_A = 0, O_R1 = O_A + BC * LA;
   // phase 1: slices of dO, dR, R, Z, w, v [64][KC], of S, dS' [DK][KC], dR^T [KC][64]
   static constexpr int O_O = O_R1, O_DR = O_O + BC * LS, O_R = O_DR + BC * LS,
                        O_Z = O_R + BC * LS, O_S = O_Z + BC * LS, O_DS = O_S + DK * LS,
@@ -612,13 +611,12 @@ struct OutCfg {
   // phase 2a: dY [64][DK], E [64][DK], dY^T [DK][64]
   static constexpr int O_DY = O_R1, O_EB = O_DY + BC * LKP, O_DYT = O_EB + BC * LKP,
                        E2 = O_DYT + DK * LA;
-  // phases 2b-4: K'^T [DK][64] stays; the rest rotates behind it
-  static constexpr int O_KPT = O_R1, O_X = O_KPT + DK * LA;
-  static constexpr int O_QPT = O_X, O_AQ = O_QPT + DK * LA, O_AQT = O_AQ + BC * LA,
+  // phases 2b-4: K' [64][DK] stays; the rest rotates behind it
+  static constexpr int O_KP = O_R1, O_X = O_KP + BC * LKP;
+  static constexpr int O_QP = O_X, O_AQ = O_QP + BC * LKP, O_AQT = O_AQ + BC * LA,
                        E3 = O_AQT + BC * LA;                                  // 2b
-  static constexpr int O_DAT = O_X, O_WM = O_DAT + BC * LA, O_A = O_WM + BC * LA,
-                       E4 = O_A + BC * LA;                                    // 3
-  static constexpr int O_EPT = O_X, O_DT = O_EPT + DK * LA, O_DTT = O_DT + BC * LA,
+  static constexpr int O_DAT = O_X, O_WM = O_DAT + BC * LA, E4 = O_WM + BC * LA;  // 3
+  static constexpr int O_EP = O_X, O_DT = O_EP + BC * LKP, O_DTT = O_DT + BC * LA,
                        E5 = O_DTT + BC * LA;                                  // 4
   // final: the per-element dg terms [64][DK] twice
   static constexpr int O_U = O_R1, O_V2 = O_U + BC * LKP, E6 = O_V2 + BC * LKP;
@@ -652,16 +650,12 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
   const float* W = a.ws + (size_t)item * L::FLOATS;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
   const size_t kr = (size_t)a.H * DK, vr = (size_t)a.H * DV;
-  float* sAT = sm + C::O_AT;
-  // Products with a triangular left factor over the chunk's 64 rows, for row
-  // tile tm: a lower-triangular factor has no columns past 16 (tm + 1), an
-  // upper-triangular one none before 16 tm (A, dA_qk, dT and their transposes)
-  auto mm_lo = [&](const float* X, const float* Bt, int tm) {
-    return mma_lds_k16<float, BC>(zero4(), X, LA, Bt, LA, 16 * (tm + 1));
-  };
-  auto mm_hi = [&](const float* X, const float* Bt, int tm) {
-    return mma_lds_k16<float, BC>(zero4(), X + 16 * tm, LA, Bt + 16 * tm, LA, BC - 16 * tm);
-  };
+  float* sA = sm + C::O_A;
+  // Products with a triangular left factor over the chunk's 64 rows run over
+  // its nonzero K range only, for row tile tm: a lower-triangular factor has
+  // no columns past 16 (tm + 1), an upper-triangular one none before 16 tm
+  // (A, dA_qk, dT and their transposes).  A^T and the right factors Q', K',
+  // E' are read K-major from row-major blocks.
   float *sO = sm + C::O_O, *sDR = sm + C::O_DR, *sR = sm + C::O_R, *sZ = sm + C::O_Z;
   float *sS = sm + C::O_S, *sDS = sm + C::O_DS, *sDRT = sm + C::O_DRT;
   float *sW = sm + C::O_W, *sV = sm + C::O_V;
@@ -695,13 +689,10 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
     }
   };
   slice_load(0);
-  // A^T (lane = row of A: consecutive lanes write consecutive words)
 #pragma unroll
   for (int u = 0; u < NAA; ++u) {
-    const int e = tid + NT * u, k = e % BC, c4 = e / BC;
-    const f32x4 x = *reinterpret_cast<const f32x4*>(W + L::A + k * BC + 4 * c4);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) sAT[(4 * c4 + q) * LA + k] = x[q];
+    const int e = tid + NT * u, s = e / (BC / 4), c4 = e - s * (BC / 4);
+    *reinterpret_cast<f32x4*>(sA + s * LA + 4 * c4) = *reinterpret_cast<const f32x4*>(W + L::A + s * BC + 4 * c4);
   }
   if (tid < DK) {
     sm[C::O_G31 + tid] = W[L::G + 31 * DK + tid];
@@ -766,7 +757,8 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
     }
     {  // dZ = A^T dR over this slice's 32 value channels: one [16][16] tile per wavefront
       const int tm = wv >> 1, tn = wv & 1;
-      const f32x4 z = mm_hi(sAT + 16 * tm * LA, sDRT + 16 * tn * LA, tm);
+      const f32x4 z = mma_lds_f32<BC, true, false>(zero4(), sA + 16 * tm * LA + 16 * tm, LA,
+                                                   sDRT + 16 * tn * LA + 16 * tm, LA, BC - 16 * tm);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = 16 * tm + 4 * g + q, c = 16 * tn + m;
@@ -799,12 +791,12 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
     *reinterpret_cast<f32x4*>(sEB + s * LKP + 4 * i4) = pEB[u];
   }
   __syncthreads();
-  f32x4 pQP[NEK], pKP[NEK];  // lane = token row
+  f32x4 pQP[NEK], pKP[NEK];
 #pragma unroll
   for (int u = 0; u < NEK; ++u) {
-    const int e = tid + NT * u, s = e % BC, i4 = e / BC;
-    pQP[u] = *reinterpret_cast<const f32x4*>(W + L::QP + s * DK + 4 * i4);
-    pKP[u] = *reinterpret_cast<const f32x4*>(W + L::KP + s * DK + 4 * i4);
+    const int e = tid + NT * u;
+    pQP[u] = reinterpret_cast<const f32x4*>(W + L::QP)[e];
+    pKP[u] = reinterpret_cast<const f32x4*>(W + L::KP)[e];
   }
   f32x4 aX[NKT];
 #pragma unroll
@@ -815,12 +807,13 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
 #pragma unroll
   for (int u = 0; u < NKT; ++u) {
     const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
-    aX[u] = mm_hi(sAT + 16 * tm * LA, sDYT + 16 * tn * LA, tm);
+    aX[u] = mma_lds_f32<BC, true, false>(zero4(), sA + 16 * tm * LA + 16 * tm, LA,
+                                         sDYT + 16 * tn * LA + 16 * tm, LA, BC - 16 * tm);
   }
   __syncthreads();
 
   // ---- phase 2b: dA_qk^T Q' and dA_qk K' ----
-  float *sKPT = sm + C::O_KPT, *sQPT = sm + C::O_QPT, *sAQ = sm + C::O_AQ, *sAQT = sm + C::O_AQT;
+  float *sKP = sm + C::O_KP, *sQP = sm + C::O_QP, *sAQ = sm + C::O_AQ, *sAQT = sm + C::O_AQT;
 #pragma unroll
   for (int u = 0; u < NCT; ++u) {
     const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
@@ -834,52 +827,38 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int u = 0; u < NEK; ++u) {
-    const int e = tid + NT * u, s = e % BC, i4 = e / BC;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      sQPT[(4 * i4 + q) * LA + s] = pQP[u][q];
-      sKPT[(4 * i4 + q) * LA + s] = pKP[u][q];
-    }
+    const int e = tid + NT * u, s = e / (DK / 4), i4 = e - s * (DK / 4);
+    *reinterpret_cast<f32x4*>(sQP + s * LKP + 4 * i4) = pQP[u];
+    *reinterpret_cast<f32x4*>(sKP + s * LKP + 4 * i4) = pKP[u];
   }
   __syncthreads();
-  f32x4 pA[NAA], pEP[NEK];
+  f32x4 pEP[NEK];
 #pragma unroll
-  for (int u = 0; u < NAA; ++u) {
-    const int e = tid + NT * u, s = e / (BC / 4), c4 = e - s * (BC / 4);
-    pA[u] = *reinterpret_cast<const f32x4*>(W + L::A + s * BC + 4 * c4);
-  }
-#pragma unroll
-  for (int u = 0; u < NEK; ++u) {  // lane = token row
-    const int e = tid + NT * u, s = e % BC, i4 = e / BC;
-    pEP[u] = *reinterpret_cast<const f32x4*>(W + L::EP + s * DK + 4 * i4);
-  }
+  for (int u = 0; u < NEK; ++u) pEP[u] = reinterpret_cast<const f32x4*>(W + L::EP)[tid + NT * u];
   f32x4 aP3[NKT], aP4[NKT];
 #pragma unroll
   for (int u = 0; u < NKT; ++u) {
     const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
-    aP3[u] = mm_hi(sAQT + 16 * tm * LA, sQPT + 16 * tn * LA, tm);
-    aP4[u] = mm_lo(sAQ + 16 * tm * LA, sKPT + 16 * tn * LA, tm);
+    aP3[u] = mma_lds_f32<BC, false, true>(zero4(), sAQT + 16 * tm * LA + 16 * tm, LA,
+                                          sQP + 16 * tm * LKP + 16 * tn, LKP, BC - 16 * tm);
+    aP4[u] = mma_lds_f32<BC, false, true>(zero4(), sAQ + 16 * tm * LA, LA, sKP + 16 * tn, LKP, 16 * (tm + 1));
   }
   __syncthreads();
 
   // ---- phase 3: dT = -tril(A^T dA A^T, -1) ----
-  float *sDAT = sm + C::O_DAT, *sWM = sm + C::O_WM, *sA = sm + C::O_A;
+  float *sDAT = sm + C::O_DAT, *sWM = sm + C::O_WM;
 #pragma unroll
   for (int u = 0; u < NCT; ++u) {
     const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
 #pragma unroll
     for (int q = 0; q < 4; ++q) sDAT[(16 * tn + m) * LA + 16 * tm + 4 * g + q] = aA[u][q];
   }
-#pragma unroll
-  for (int u = 0; u < NAA; ++u) {
-    const int e = tid + NT * u, s = e / (BC / 4), c4 = e - s * (BC / 4);
-    *reinterpret_cast<f32x4*>(sA + s * LA + 4 * c4) = pA[u];
-  }
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < NCT; ++u) {
     const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
-    const f32x4 w4 = mm_hi(sAT + 16 * tm * LA, sDAT + 16 * tn * LA, tm);
+    const f32x4 w4 = mma_lds_f32<BC, true, false>(zero4(), sA + 16 * tm * LA + 16 * tm, LA,
+                                                  sDAT + 16 * tn * LA + 16 * tm, LA, BC - 16 * tm);
 #pragma unroll
     for (int q = 0; q < 4; ++q) sWM[(16 * tm + 4 * g + q) * LA + 16 * tn + m] = w4[q];
   }
@@ -890,12 +869,14 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
     const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
     // A is unit lower triangular: column block tn of A^T has no rows past
     // 16 (tn + 1); tiles above the diagonal are masked out below
-    aT[u] = tn <= tm ? mm_lo(sWM + 16 * tm * LA, sA + 16 * tn * LA, tn) : zero4();
+    aT[u] = tn <= tm ? mma_lds_f32<BC, false, false>(zero4(), sWM + 16 * tm * LA, LA, sA + 16 * tn * LA, LA,
+                                                     16 * (tn + 1))
+                     : zero4();
   }
   __syncthreads();
 
   // ---- phase 4: dT K' and dT^T E' ----
-  float *sEPT = sm + C::O_EPT, *sDT = sm + C::O_DT, *sDTT = sm + C::O_DTT;
+  float *sEP = sm + C::O_EP, *sDT = sm + C::O_DT, *sDTT = sm + C::O_DTT;
 #pragma unroll
   for (int u = 0; u < NCT; ++u) {
     const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
@@ -909,9 +890,8 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int u = 0; u < NEK; ++u) {
-    const int e = tid + NT * u, s = e % BC, i4 = e / BC;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) sEPT[(4 * i4 + q) * LA + s] = pEP[u][q];
+    const int e = tid + NT * u, s = e / (DK / 4), i4 = e - s * (DK / 4);
+    *reinterpret_cast<f32x4*>(sEP + s * LKP + 4 * i4) = pEP[u];
   }
   __syncthreads();
   // the final's per-element inputs, loaded while phase 4 computes
@@ -933,8 +913,9 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
 #pragma unroll
   for (int u = 0; u < NKT; ++u) {
     const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
-    aP1[u] = mm_lo(sDT + 16 * tm * LA, sKPT + 16 * tn * LA, tm);
-    aP2[u] = mm_hi(sDTT + 16 * tm * LA, sEPT + 16 * tn * LA, tm);
+    aP1[u] = mma_lds_f32<BC, false, true>(zero4(), sDT + 16 * tm * LA, LA, sKP + 16 * tn, LKP, 16 * (tm + 1));
+    aP2[u] = mma_lds_f32<BC, false, true>(zero4(), sDTT + 16 * tm * LA + 16 * tm, LA,
+                                          sEP + 16 * tm * LKP + 16 * tn, LKP, BC - 16 * tm);
   }
   __syncthreads();
 

@@ -161,13 +161,16 @@ __device__ __forceinline__ f32x4 mma_lds_k16(f32x4 acc, const E* A, int lda, con
 // K-contiguous as in mma_lds (A row m at A + m*lda, B column n at B + n*ldb)
 // or K-major (TA: A element (m, k) at A + k*lda + m; TB: B element (k, n) at
 // B + k*ldb + n).  A K-major operand takes four 4-byte reads per K = 16
-// block; within a 16-lane group they hit consecutive words.
+// block; within a 16-lane group they hit consecutive words.  kn (a multiple
+// of 16, at most K, the same across the wavefront) cuts K short.
 template <int K, bool TA, bool TB>
-__device__ __forceinline__ f32x4 mma_lds_f32(f32x4 acc, const float* A, int lda, const float* B, int ldb) {
+__device__ __forceinline__ f32x4 mma_lds_f32(f32x4 acc, const float* A, int lda, const float* B, int ldb,
+                                             int kn = K) {
   static_assert(K % 16 == 0, "K must be a multiple of 16");
   const int m = lane_id() & 15, g = lane_id() >> 4;
 #pragma unroll
   for (int k0 = 0; k0 < K; k0 += 16) {
+    if (k0 >= kn) break;
     float av[4], bv[4];
     if constexpr (TA) {
       const float* a = A + (k0 + 4 * g) * lda + m;
