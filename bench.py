@@ -495,8 +495,8 @@ def main():
                      "alg_bytes": bw_bytes,
                      "roofline": {"bound": "hbm", "achieved": bw_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": bw_gbs / HBM_PEAK_GBS,
-                                  "traffic": load_call_traffic("fwd", "bwd_state_bwd_kernel<128, 128>",
-                                                               "bwd_", "bmm_multi_kernel")}},
+                                  "traffic": load_call_traffic("fwd", "bwd_state_fwd_kernel<128, 128>",
+                                                               "bwd_")}},
         "long_sequence": long_leg(args, torch, G, I, dev) if args.long == "on" else None,
         "block": {"workload": "gdr2_chunk_fwd_block B4 T4096 H16 Hv16 dk=dv=128 from projections: "
                               "q/k L2 norm, Eq. 12 decay from bf16 W_f x, sigmoid gates (flags 7)",
