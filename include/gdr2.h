@@ -134,8 +134,8 @@ gdr2_status gdr2_chunk_fwd(const void *q, const void *k, const void *v,
  * Bytes of device workspace gdr2_chunk_bwd needs for these sizes (num_seqs as
  * for gdr2_chunk_fwd).  Returns 0 for sizes gdr2_chunk_bwd would reject.  The
  * backward keeps the intermediates its passes hand on, per (64-token chunk,
- * head), in fp32: (8 * 64 * dk + 3 * 64 * dv + 2 * 64 * 64 + 2 * dk * dv + dk)
- * * 4 bytes, rounded up to 256, per item (0.52 MB at dk = dv = 128), for
+ * head), in fp32: (4 * 64 * dk + 3 * 64 * dv + 2 * 64 * 64 + 2 * dk * dv + dk)
+ * * 4 bytes, rounded up to 256, per item (0.39 MB at dk = dv = 128), for
  * B * ceil(T/64) chunks (ceil(T/64) + num_seqs with packed sequences) times H.
  */
 size_t gdr2_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs);

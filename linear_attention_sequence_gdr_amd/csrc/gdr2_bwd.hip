@@ -48,8 +48,7 @@ struct BwdLayout {
   static constexpr size_t CK = (size_t)BC * DK, CV = (size_t)BC * DV, CC = (size_t)BC * BC,
                           KV = (size_t)DK * DV;
   // offsets in floats inside one item's block
-  static constexpr size_t G = 0, QG = G + CK, KT = QG + CK, EB = KT + CK, EP = EB + CK,
-                          KP = EP + CK, QP = KP + CK, Y_ = QP + CK;
+  static constexpr size_t G = 0, QG = G + CK, KT = QG + CK, Y_ = KT + CK;
   static constexpr size_t U = Y_ + CK, R = U + CV, DR = R + CV;
   static constexpr size_t A = DR + CV, AQK = A + CC;
   static constexpr size_t S = AQK + CC, DSP = S + KV;
@@ -77,7 +76,8 @@ __device__ __forceinline__ bool bwd_locate(const BwdArgs& a, int ci, long long& 
 //   phase 1  log-decay rows into LDS, q, k, b into registers; G by a column
 //            scan (row blocks scanned in parallel, then offset by the totals
 //            of the blocks above);
-//   phase 2  Q_g, K_tail, E, E', K', Q' to the workspace, E', K', Q' to LDS;
+//   phase 2  Q_g and K_tail to the workspace, E', K', Q' to LDS (E and the
+//            centred rows are not stored: the output pass forms them again);
 //   phase 3  T = tril(E' K'^T, -1) and A_qk = tril(Q' K'^T) on MFMA (inside
 //            a product the centred factors cancel);
 //   phase 4  A = (I + T)^-1: forward substitution on the four diagonal 16x16
@@ -175,19 +175,20 @@ __global__ __launch_bounds__(512) void bwd_front_kernel(BwdArgs a) {
 
   // ---- phase 2 ----
   float *sEP = sm + C::O_EP, *sKP = sm + C::O_KP, *sQP = sm + C::O_QP;
+  f32x4 pg[NEK];  // G of this thread's units, for E in phase 5
 #pragma unroll
   for (int u = 0; u < NEK; ++u) {
     const int e = tid + NT * u, r = e / (DK / 4), i4 = e - r * (DK / 4), o = r * LKP + 4 * i4;
-    f32x4 QG, KT, EB, EP, KP, QP;
+    f32x4 QG, KT, EP, KP, QP;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int i = 4 * i4 + c;
       const float G = sG[o + c], G31 = sG[31 * LKP + i], GCl = sG[(BC - 1) * LKP + i];
       const float gam = expf(G), e1 = expf(G - G31), e2 = expf(G31 - G);
       const float qv = pq[u][c], kv = pk[u][c], bv = pb[u][c];
+      pg[u][c] = G;
       QG[c] = gam * qv;
       KT[c] = expf(GCl - G) * kv;
-      EB[c] = gam * bv * kv;
       EP[c] = e1 * bv * kv;
       KP[c] = e2 * kv;
       QP[c] = e1 * qv;
@@ -195,10 +196,6 @@ __global__ __launch_bounds__(512) void bwd_front_kernel(BwdArgs a) {
     const int wo = r * DK + 4 * i4;
     *reinterpret_cast<f32x4*>(W + L::QG + wo) = QG;
     *reinterpret_cast<f32x4*>(W + L::KT + wo) = KT;
-    *reinterpret_cast<f32x4*>(W + L::EB + wo) = EB;
-    *reinterpret_cast<f32x4*>(W + L::EP + wo) = EP;
-    *reinterpret_cast<f32x4*>(W + L::KP + wo) = KP;
-    *reinterpret_cast<f32x4*>(W + L::QP + wo) = QP;
     *reinterpret_cast<f32x4*>(sEP + o) = EP;
     *reinterpret_cast<f32x4*>(sKP + o) = KP;
     *reinterpret_cast<f32x4*>(sQP + o) = QP;
@@ -305,11 +302,14 @@ __global__ __launch_bounds__(512) void bwd_front_kernel(BwdArgs a) {
     const int e = tid + NT * u, s = e / (BC / 4), c4 = e - s * (BC / 4);
     *reinterpret_cast<f32x4*>(W + L::A + s * BC + 4 * c4) = *reinterpret_cast<const f32x4*>(sA + s * LA + 4 * c4);
   }
-  // E as this workgroup wrote it in phase 2, and Z = w * v
+  // E = gamma * b * k from the registers of phase 1-2, and Z = w * v
 #pragma unroll
   for (int u = 0; u < NEK; ++u) {
     const int e = tid + NT * u, s = e / (DK / 4), i4 = e - s * (DK / 4);
-    *reinterpret_cast<f32x4*>(sEB + s * LKP + 4 * i4) = reinterpret_cast<const f32x4*>(W + L::EB)[e];
+    f32x4 eb;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) eb[c] = expf(pg[u][c]) * pb[u][c] * pk[u][c];
+    *reinterpret_cast<f32x4*>(sEB + s * LKP + 4 * i4) = eb;
   }
 #pragma unroll
   for (int u = 0; u < NEV; ++u) {
@@ -616,14 +616,14 @@ struct OutCfg {
   static constexpr int O_QP = O_X, O_AQ = O_QP + BC * LKP, O_AQT = O_AQ + BC * LA,
                        E3 = O_AQT + BC * LA;                                  // 2b
   static constexpr int O_DAT = O_X, O_WM = O_DAT + BC * LA, E4 = O_WM + BC * LA;  // 3
-  static constexpr int O_EP = O_X, O_DT = O_EP + BC * LKP, O_DTT = O_DT + BC * LA,
-                       E5 = O_DTT + BC * LA;                                  // 4
+  static constexpr int O_DT = O_X, O_DTT = O_DT + BC * LA, E5 = O_DTT + BC * LA;  // 4
   // final: the per-element dg terms [64][DK] twice
   static constexpr int O_U = O_R1, O_V2 = O_U + BC * LKP, E6 = O_V2 + BC * LKP;
   static constexpr int mx(int x, int y) { return x > y ? x : y; }
-  // per-channel values: G at row 31 and 63, gamma_C, the dS' * S row sums;
-  // the dg scan's row-block partial sums
-  static constexpr int O_G31 = mx(mx(mx(E1, E2), mx(E3, E4)), mx(E5, E6));
+  // E' [64][DK] from phase 2a to phase 4; per-channel values: G at row 31
+  // and 63, gamma_C, the dS' * S row sums; the dg scan's row-block partial sums
+  static constexpr int O_EP = mx(mx(mx(E1, E2), mx(E3, E4)), mx(E5, E6));
+  static constexpr int O_G31 = O_EP + BC * LKP;
   static constexpr int O_GCL = O_G31 + DK, O_GCX = O_GCL + DK, O_RS = O_GCX + DK,
                        O_PU = O_RS + DK, O_PV = O_PU + NT, FLOATS = O_PV + NT;
   static constexpr size_t BYTES = (size_t)FLOATS * 4;
@@ -701,7 +701,8 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
   }
 
   // ---- phase 1 ----
-  f32x4 aQ[NKT], aY[NKT], aK[NKT], aAQ[NCT], aA[NCT], pEB[NEK];
+  f32x4 aQ[NKT], aY[NKT], aK[NKT], aAQ[NCT], aA[NCT];
+  f32x4 pG[NEK], pK[NEK], pB[NEK];  // G, k, b of row-major units: E, E', K', Q' are formed again
 #pragma unroll
   for (int u = 0; u < NKT; ++u) aQ[u] = aY[u] = aK[u] = zero4();
 #pragma unroll
@@ -730,15 +731,7 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
-    if (sl + 1 < NS) {
-      slice_load(j0 + KC);
-    } else {
-#pragma unroll
-      for (int u = 0; u < NEK; ++u) {
-        const int e = tid + NT * u, s = e / (DK / 4), i4 = e - s * (DK / 4);
-        pEB[u] = *reinterpret_cast<const f32x4*>(W + L::EB + s * DK + 4 * i4);
-      }
-    }
+    if (sl + 1 < NS) slice_load(j0 + KC);
     if (tid < DK)
 #pragma unroll 8
       for (int c = 0; c < KC; ++c) rs = fmaf(sDS[tid * LS + c], sS[tid * LS + c], rs);
@@ -773,6 +766,20 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
   }
 
   // ---- phase 2a: dA += dY E^T, X = A^T dY ----
+  // G, k and b for E and E' (issued before dY goes to LDS)
+#pragma unroll
+  for (int u = 0; u < NEK; ++u) {
+    const int e = tid + NT * u, s = e / (DK / 4), i4 = e - s * (DK / 4);
+    const int sr = s < clen ? s : clen - 1;
+    const size_t x = (size_t)(row0 + sr) * kr + (size_t)h * DK + 4 * i4;
+    const float z = s < clen ? 1.f : 0.f;
+    float t[4];
+    pG[u] = reinterpret_cast<const f32x4*>(W + L::G)[e];
+    load4<BF16>(a.k, x, t);
+    pK[u] = f32x4{t[0], t[1], t[2], t[3]} * z;
+    load4<BF16>(a.b, x, t);
+    pB[u] = f32x4{t[0], t[1], t[2], t[3]} * z;
+  }
   float *sDY = sm + C::O_DY, *sEB = sm + C::O_EB, *sDYT = sm + C::O_DYT;
 #pragma unroll
   for (int u = 0; u < NKT; ++u) {
@@ -785,18 +792,31 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
       sDYT[i * LA + r] = y;
     }
   }
+  // E = gamma b k and E' = e1 b k (the forms of the front pass, same order
+  // of operations), e1 = exp(G - G_31)
+  float* sEP = sm + C::O_EP;
+#pragma unroll
+  for (int u = 0; u < NEK; ++u) {
+    const int e = tid + NT * u, s = e / (DK / 4), i4 = e - s * (DK / 4), o = s * LKP + 4 * i4;
+    f32x4 eb, ep;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float G = pG[u][c], gam = expf(G), e1 = expf(G - sm[C::O_G31 + 4 * i4 + c]);
+      eb[c] = gam * pB[u][c] * pK[u][c];
+      ep[c] = e1 * pB[u][c] * pK[u][c];
+    }
+    *reinterpret_cast<f32x4*>(sEB + o) = eb;
+    *reinterpret_cast<f32x4*>(sEP + o) = ep;
+  }
+  __syncthreads();
+  f32x4 pQ[NEK];
 #pragma unroll
   for (int u = 0; u < NEK; ++u) {
     const int e = tid + NT * u, s = e / (DK / 4), i4 = e - s * (DK / 4);
-    *reinterpret_cast<f32x4*>(sEB + s * LKP + 4 * i4) = pEB[u];
-  }
-  __syncthreads();
-  f32x4 pQP[NEK], pKP[NEK];
-#pragma unroll
-  for (int u = 0; u < NEK; ++u) {
-    const int e = tid + NT * u;
-    pQP[u] = reinterpret_cast<const f32x4*>(W + L::QP)[e];
-    pKP[u] = reinterpret_cast<const f32x4*>(W + L::KP)[e];
+    const int sr = s < clen ? s : clen - 1;
+    float t[4];
+    load4<BF16>(a.q, (size_t)(row0 + sr) * kr + (size_t)h * DK + 4 * i4, t);
+    pQ[u] = f32x4{t[0], t[1], t[2], t[3]} * (s < clen ? 1.f : 0.f);
   }
   f32x4 aX[NKT];
 #pragma unroll
@@ -825,16 +845,21 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
       sAQT[c * LA + r] = v;
     }
   }
+  // Q' = e1 q and K' = e2 k, e2 = exp(G_31 - G)
 #pragma unroll
   for (int u = 0; u < NEK; ++u) {
     const int e = tid + NT * u, s = e / (DK / 4), i4 = e - s * (DK / 4);
-    *reinterpret_cast<f32x4*>(sQP + s * LKP + 4 * i4) = pQP[u];
-    *reinterpret_cast<f32x4*>(sKP + s * LKP + 4 * i4) = pKP[u];
+    f32x4 qp, kp;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float G = pG[u][c], G31 = sm[C::O_G31 + 4 * i4 + c];
+      qp[c] = expf(G - G31) * pQ[u][c];
+      kp[c] = expf(G31 - G) * pK[u][c];
+    }
+    *reinterpret_cast<f32x4*>(sQP + s * LKP + 4 * i4) = qp;
+    *reinterpret_cast<f32x4*>(sKP + s * LKP + 4 * i4) = kp;
   }
   __syncthreads();
-  f32x4 pEP[NEK];
-#pragma unroll
-  for (int u = 0; u < NEK; ++u) pEP[u] = reinterpret_cast<const f32x4*>(W + L::EP)[tid + NT * u];
   f32x4 aP3[NKT], aP4[NKT];
 #pragma unroll
   for (int u = 0; u < NKT; ++u) {
@@ -876,7 +901,7 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
   __syncthreads();
 
   // ---- phase 4: dT K' and dT^T E' ----
-  float *sEP = sm + C::O_EP, *sDT = sm + C::O_DT, *sDTT = sm + C::O_DTT;
+  float *sDT = sm + C::O_DT, *sDTT = sm + C::O_DTT;
 #pragma unroll
   for (int u = 0; u < NCT; ++u) {
     const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
@@ -887,11 +912,6 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
       sDT[r * LA + c] = v;
       sDTT[c * LA + r] = v;
     }
-  }
-#pragma unroll
-  for (int u = 0; u < NEK; ++u) {
-    const int e = tid + NT * u, s = e / (DK / 4), i4 = e - s * (DK / 4);
-    *reinterpret_cast<f32x4*>(sEP + s * LKP + 4 * i4) = pEP[u];
   }
   __syncthreads();
   // the final's per-element inputs, loaded while phase 4 computes

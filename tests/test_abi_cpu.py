@@ -229,7 +229,7 @@ def test_chunk_bwd_rejects(kw, status):
 
 def test_chunk_bwd_workspace_query():
     q = G.gdr2_chunk_bwd_workspace_bytes
-    item = lambda dk, dv: (8 * 64 * dk + 3 * 64 * dv + 2 * 64 * 64 + 2 * dk * dv + dk + 63) // 64 * 64 * 4
+    item = lambda dk, dv: (4 * 64 * dk + 3 * 64 * dv + 2 * 64 * 64 + 2 * dk * dv + dk + 63) // 64 * 64 * 4
     assert q(4, 4096, 16, 128, 128, 0) == 4 * 64 * 16 * item(128, 128)
     assert q(2, 100, 3, 64, 32, 0) == 2 * 2 * 3 * item(64, 32)
     a256 = lambda x: (x + 255) // 256 * 256
