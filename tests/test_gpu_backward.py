@@ -68,6 +68,16 @@ def test_backward_matches_oracle(B, T, H, dk, dv, dtype):
     check(run_bwd(wl, dO, dST), oracle_bwd(wl, dO, dST), f"B{B} T{T} H{H} dk{dk} dv{dv} {dtype}")
 
 
+@pytest.mark.parametrize("dtype,la_dtype", [(torch.bfloat16, torch.float32), (torch.float32, torch.bfloat16)])
+def test_backward_log_alpha_in_its_own_dtype(dtype, la_dtype):
+    """log_alpha in a dtype of its own: fp32 log-decay with bf16 activations, and
+    the reverse (the front pass reads each in its own width)."""
+    wl = I.make_forward(2, 130, 2, 64, 64, dtype=dtype, la_dtype=la_dtype, decay_shift=-2.0,
+                        erase_scale=2.0, s0_std=0.1, seed=76)
+    dO, dST = I.cotangents(wl, seed=77)
+    check(run_bwd(wl, dO, dST), oracle_bwd(wl, dO, dST), f"{dtype} with log_alpha {la_dtype}")
+
+
 def test_backward_without_state_arguments():
     """S0 = NULL and dS_T = NULL mean zeros; dS0 may be skipped."""
     wl = I.make_forward(1, 100, 2, 64, 64, dtype=torch.bfloat16, decay_shift=-2.0, seed=72)
