@@ -2,7 +2,7 @@
 
 The oracle's C sources and tests/oracle_sanitize_driver.c are compiled with
 gcc under AddressSanitizer and UndefinedBehaviorSanitizer (leak checks on),
-and the driver exercises every option of the oracle's interface: packed
+and that C program exercises every option of the oracle's interface: packed
 sequences with a zero-length one, NULL S0 / S_T / dS_T / dS0, a (sequence,
 head) mask, decode run token by token against the forward (to 1e-12), and the
 backward.  Any sanitizer report fails the test.
