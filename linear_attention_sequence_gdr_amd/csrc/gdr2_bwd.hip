@@ -21,14 +21,16 @@
 // chunk's row 31 (e1 = exp(G - G_31), e2 = exp(G_31 - G)) with the scale put
 // back per row afterwards, so no 1/gamma is formed.
 //
-// Layout: every intermediate of an item is an fp32 row-major block inside the
-// workspace (BwdLayout).  The work is a chain of kernels:
-//   prep (elementwise) -> batched products T, A_qk -> forward substitution A
-//   -> Y, U -> sequential state pass (saves the entry state of every chunk)
-//   -> sequential reverse state-gradient pass (saves dS' and dR per chunk)
-//   (the state pass also saves R = U - Y S, which it forms anyway)
-//   -> one fused kernel per item for the output and WY paths and the
-//   gradients themselves (bwd_out_kernel).
+// Layout: what one kernel hands to the next is an fp32 row-major block per
+// item inside the workspace (BwdLayout: G, Q_g, K_tail, Y, U, R, dR, A, A_qk,
+// the entering state S, dS' and gamma_C).  Four kernels run:
+//   bwd_front_kernel      per item: G, the scaled rows, T and A_qk, A, Y, U;
+//   bwd_state_fwd_kernel  per chain, chunks in order: S entering each chunk
+//                         and R = U - Y S;
+//   bwd_state_bwd_kernel  per chain, chunks in reverse: dS' and dR, and dS0;
+//   bwd_out_kernel        per item: every output-path and WY-gradient product
+//                         and the gradients themselves (E, E', K', Q' are
+//                         formed again from G, q, k, b rather than stored).
 // Every product runs on fp32 MFMA (16x16x4) from LDS-staged operands.
 #include <hip/hip_runtime.h>
 
@@ -334,7 +336,8 @@ __global__ __launch_bounds__(512) void bwd_front_kernel(BwdArgs a) {
   }
 }
 
-// Register prefetch of one chunk's operands for the sequential passes.
+// Register prefetch of one chunk's operands for the sequential passes
+// (16-byte loads in address order, into row-major LDS blocks).
 template <int DK, int DV, int NK4, int NV4>
 __device__ __forceinline__ void sf_load(const BwdArgs& a, int ci, int h, int jb, int tid,
                                         f32x4 (&ry)[NK4], f32x4 (&rk)[NK4], f32x4 (&ru)[NV4],
@@ -388,10 +391,9 @@ __device__ __forceinline__ void sb_load(const BwdArgs& a, int ci, int h, int jb,
 
 // ---- sequential state pass: the state entering every chunk --------------------------
 // One workgroup of SNT threads per (sequence, head, 32 value channels); the
-// state block is
-// kept transposed in LDS (S^T, the B operand of Y S).  The next two chunks'
-// operands are loaded into registers (16-byte loads) while the current chunk
-// computes.
+// state block is kept transposed in LDS (S^T, the B operand of Y S).  The
+// next two chunks' operands are loaded into registers (16-byte loads in
+// address order) while the current chunk computes.
 template <int DK, int DV>
 __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
   typedef BwdLayout<DK, DV> L;
@@ -573,10 +575,10 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
 }
 
 // ---- output and WY-gradient paths, fused per item ------------------------------------
-// One workgroup per item forms, from the item's fp32 blocks (R, dR, A, E, Q',
-// K', E', the decay G), the inputs (dO, v, w, q, k, b) and the states S and
-// dS' on either side of the chunk, every remaining product and the gradients
-// themselves:
+// One workgroup per item forms, from the item's fp32 blocks (R, dR, A, the
+// decay G), the inputs (dO, v, w, q, k, b) and the states S and dS' on either
+// side of the chunk, every remaining product and the gradients themselves.
+// E, E' (phase 2a) and Q', K' (phase 2b) are formed again from G, q, k, b:
 //   phase 1  dQ_g = dO S^T, dY = -dR S^T, dK_tail = R dS'^T,
 //            dA_qk = tril(dO R^T), dA = dR Z^T, dZ = A^T dR (-> dv, dw), and
 //            the row sums of dS' * S; the value channels stream through LDS
@@ -590,8 +592,9 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
 // Operands are staged in LDS from 16-byte loads in address order, rows padded
 // by 4 floats, and read either K-contiguous (16-byte reads) or K-major (four
 // 4-byte reads per K = 16 block); a 16-lane group's reads hit distinct banks
-// either way.  The fp32 products run on 16x16x4 MFMA.  Tiles of a [64][N] result go round the eight wavefronts
-// (tile t = wave + 8u, row tile t / (N/16), column tile t % (N/16)).  Each
+// either way.  The fp32 products run on 16x16x4 MFMA.  Tiles of a [64][N]
+// result go round the eight wavefronts (tile t = wave + 8u, row tile
+// t / (N/16), column tile t % (N/16)).  Each
 // phase's global loads are issued into registers one phase (or one slice)
 // ahead, so they overlap the products of the phase before.  Rows past the
 // end of a sequence read a clamped (valid) row and are zeroed in registers.
