@@ -33,7 +33,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 TRAFFIC_FILE = {"fwd": os.path.join(ROOT, "profiles", "traffic_chunk_fwd_b4_t4096_h16_d128.json"),
-                "long": os.path.join(ROOT, "profiles", "traffic_chunk_fwd_b1_t32768_h16_d128.json")}
+                "long": os.path.join(ROOT, "profiles", "traffic_chunk_fwd_b1_t32768_h16_d128.json"),
+                "varlen": os.path.join(ROOT, "profiles", "traffic_chunk_fwd_varlen64_h16_d128.json")}
 MFMA_FILE = {"fwd": os.path.join(ROOT, "profiles", "mfma_chunk_fwd_b4_t4096_h16_d128.json"),
              "long": os.path.join(ROOT, "profiles", "mfma_chunk_fwd_b1_t32768_h16_d128.json")}
 MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32")
@@ -291,6 +292,105 @@ def long_leg(args, torch, G, I, dev):
                          "traffic": load_traffic("long", *keys)}}
 
 
+def ceilings(torch, dev):
+    """Measured ceilings beside the published peaks: a copy of 1 GiB into
+    another 1 GiB (read and write streams at once), a read-only stream over
+    2 GiB (both far beyond the 256 MB last-level cache), and back-to-back
+    16x16x32 bf16 and f16 MFMAs from registers on every CU.  Each is the best
+    of five launches timed with HIP events on torch's current stream."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "linear_attention_sequence_gdr_amd", "libgdr2_ceiling.so"))
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int
+    lib.gdr2_ceiling_copy.argtypes = [vp, vp, i64, i32, vp]
+    lib.gdr2_ceiling_read.argtypes = [vp, vp, i64, i32, vp]
+    lib.gdr2_ceiling_mfma.argtypes = [vp, i32, i32, i32, vp]
+    for f in (lib.gdr2_ceiling_copy, lib.gdr2_ceiling_read, lib.gdr2_ceiling_mfma):
+        f.restype = i32
+    st = torch.cuda.current_stream(dev).cuda_stream
+
+    def best(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            rc = fn()
+            b.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"ceiling kernel launch failed ({rc})")
+            t.append(a.elapsed_time(b))
+        return min(t) * 1e-3
+
+    gib = 1 << 30
+    src = torch.empty(2 * gib, dtype=torch.uint8, device=dev)
+    dst = torch.empty(gib, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    red = torch.empty(256 * 64, dtype=torch.int32, device=dev)
+    blocks = 256 * 64
+    tc = best(lambda: lib.gdr2_ceiling_copy(src.data_ptr(), dst.data_ptr(), gib // 16, blocks, st))
+    tr = best(lambda: lib.gdr2_ceiling_read(src.data_ptr(), red.data_ptr(), 2 * gib // 16, blocks, st))
+    del src, dst, red
+    mb, iters = 256 * 8, 4000
+    out = torch.empty(mb * 256, dtype=torch.float32, device=dev)
+    flops = mb * 4 * iters * 8 * 16 * 16 * 32 * 2
+    tb = best(lambda: lib.gdr2_ceiling_mfma(out.data_ptr(), mb, iters, 0, st))
+    th = best(lambda: lib.gdr2_ceiling_mfma(out.data_ptr(), mb, iters, 1, st))
+    del out
+    return {"hbm_copy_GBs": 2 * gib / tc / 1e9, "hbm_read_GBs": 2 * gib / tr / 1e9,
+            "mfma_bf16_TFLOPs": flops / tb / 1e12, "mfma_f16_TFLOPs": flops / th / 1e12,
+            "published": {"hbm_GBs": HBM_PEAK_GBS, "mfma_bf16_TFLOPs": BF16_PEAK_TFLOPS},
+            "method": "copy 1 GiB -> 1 GiB and read 2 GiB with 16-byte vector loads; 16x16x32 "
+                      "MFMAs, 8 independent chains per wavefront, 2048 workgroups of 4 "
+                      "wavefronts; best of 5, HIP events"}
+
+
+def cpu_single_thread(wl):
+    """The oracle on one (sequence, head) chain of the forward workload on one
+    thread: a per-core figure."""
+    import numpy as np
+    import oracle
+    m = np.zeros((1, wl.H), bool)
+    m[0, 0] = True
+    q, k, v, g, b, w = (oracle.f64(x[:1]) for x in (wl.q, wl.k, wl.v, wl.log_alpha, wl.b, wl.w))
+    oracle.fwd(q[:, :64], k[:, :64], v[:, :64], g[:, :64], b[:, :64], w[:, :64], mask=m, nthreads=1)
+    t0 = time.perf_counter()
+    oracle.fwd(q, k, v, g, b, w, mask=m, nthreads=1)
+    dt = time.perf_counter() - t0
+    return {"value": wl.T / dt, "unit": "head-tokens/s", "cores": 1,
+            "sample": f"1 (sequence, head) chain x {wl.T} tokens, fp64 token-by-token, {dt:.2f} s"}
+
+
+def varlen_leg(args, torch, G, I, dev):
+    """64 packed sequences of U[1, 8192] tokens (about 262K tokens), H16 d128
+    bf16, each with its own S0 and S_T."""
+    vw = I.config(4)
+    ins = [x.to(dev) for x in (vw.q, vw.k, vw.v, vw.log_alpha, vw.b, vw.w)]
+    S0, cu = vw.S0.to(dev), vw.cu_seqlens.to(dev)
+    N, T, H, dk, dv = vw.num_seqs, vw.T, vw.H, vw.dk, vw.dv
+    o = torch.empty((1, T, H, dv), dtype=torch.bfloat16, device=dev)
+    ST = torch.empty_like(S0)
+    ws = torch.empty(max(1, G.gdr2_chunk_fwd_workspace_bytes(1, T, H, dk, dv, N, G.GDR2_BF16)),
+                     dtype=torch.uint8, device=dev)
+    fwd = lambda: G.gdr2_chunk_fwd(*ins, S0, cu, o=o, S_T=ST, workspace=ws)
+    steps = max(3, min(args.steps, 10))
+    ms = time_events(fwd, steps, 2, torch)
+    byts, flops = fwd_algorithmic(1, T, H, dk, dv)
+    byts += N * H * dk * dv * 4 - H * dk * dv * 4  # S0 read and N final states (not 1)
+    gbs = byts / (ms * 1e-3) / 1e9
+    del ins, S0, cu, o, ST, ws
+    return {"workload": f"gdr2_chunk_fwd, {N} packed sequences of U[1, 8192] tokens ({T} tokens), "
+                        "H16 dk=dv=128 bf16, per-sequence S0 ~ N(0, 0.1), decay shift -2",
+            "steps": steps, "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),
+            "tflops": flops / (ms * 1e-3) / 1e12, "alg_bytes": byts,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": load_call_traffic("varlen", "intra_kernel<128, 128, true, false>",
+                                                      "intra_kernel", "state_kernel", "schedule",
+                                                      "chunk_table")}}
+
+
 def calibration_copy(args, torch, dev):
     if args.calibrate_copy:
         n = args.calibrate_copy * 1024 * 1024 // 4
@@ -309,6 +409,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true", help="leave out the packed-sequence forward")
+    ap.add_argument("--no-ceilings", action="store_true", help="leave out the measured ceilings")
     ap.add_argument("--no-cold", action="store_true",
                     help="leave out the cold-cache forward timing (keeps kernel-trace averages warm)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -318,7 +420,7 @@ def main():
                          "rocprofv3 --pmc counter_collection.csv files")
     ap.add_argument("--traffic-command", default="",
                     help="the command that produced the counter files (recorded)")
-    ap.add_argument("--traffic-workload", choices=("fwd", "long"), default="fwd",
+    ap.add_argument("--traffic-workload", choices=("fwd", "long", "varlen"), default="fwd",
                     help="which workload's kernels the counter files cover")
     ap.add_argument("--mfma", metavar="CSV",
                     help="host only: write the per-kernel MFMA table from a rocprofv3 --pmc "
@@ -417,6 +519,21 @@ def main():
     Nd, Hd, D = I.DECODE_N, I.DECODE_H, I.DECODE_D
     dbytes = Nd * Hd * (2 * D * D * 4 + 6 * D * 4 + D * 4)
     dgbs = dbytes / (dms * 1e-3) / 1e9
+    # the same step from a cold last-level cache: single steps, each after a
+    # 512 MiB scratch write
+    dcold_ms = time_cold(dec, 20, torch)
+    # steady state over two states of 256 MiB each, used in turn: each step
+    # reads the state the previous step did not touch, and 512 MiB of states
+    # exceed the 256 MB last-level cache
+    S2 = S.clone()
+    states = (S, S2)
+
+    def dec_alt():
+        x = pool[it[0] % len(pool)]
+        G.gdr2_decode_step(*x, states[it[0] & 1], o=od)
+        it[0] += 1
+    dalt_ms = time_events(dec_alt, args.decode_steps, 6, torch)
+    del S2
 
     # the same decode step with the output epilogue fused into its store
     zd = torch.randn((Nd, Hd, D), generator=torch.Generator("cpu").manual_seed(5)).to(dev)
@@ -442,11 +559,17 @@ def main():
     egbs = ebytes / (ems * 1e-3) / 1e9
     del z_epi, y_epi
 
+    # ---- 64 packed sequences (about 262K tokens) ---------------------------------------
+    varlen = varlen_leg(args, torch, G, I, dev) if not args.no_varlen else None
+
+    ceil = None if args.no_ceilings else ceilings(torch, dev)
+
     calibration_copy(args, torch, dev)
 
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(wl)
+        cpu["single_thread"] = cpu_single_thread(wl)
 
     line = {
         "metric": "GDR-2 fwd tokens/s + TFLOP/s (H16,d128,T4K); decode HBM GB/s",
@@ -459,11 +582,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16 in, fp16/bf16 MFMA, fp32 acc",
         "data": "synthetic",
         "config": {"workload": "gdr2_chunk_fwd B4 T4096 H16 dk=dv=128, bf16 q/k/v/b/w/log_alpha, "
                                "fp32 state, S0=0, chunk 64",
-                   "global_batch": B, "seq_len": T, "heads": H, "dk": dk, "dv": dv},
+                   "global_batch": B, "seq_len": T, "heads": H, "dk": dk, "dv": dv,
+                   "arithmetic": "inputs and o bf16; decay sum, WY diagonal solve, every "
+                                 "accumulation and the state fp32; chunk matrix T on bf16 MFMA, "
+                                 "causal scores on bf16 hi/lo pairs, state-pass products on fp16 "
+                                 "MFMA"},
         "fwd_tflops": tflops,
         "fwd_tflops_frac_of_bf16_peak": tflops / BF16_PEAK_TFLOPS,
         "fwd_alg_bytes": byts,
@@ -483,6 +610,13 @@ def main():
                    "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
                                 "traffic": load_traffic("fwd", "decode_kernel<128, 128, false>")},
+                   "cold": {"us_per_step": dcold_ms * 1e3,
+                            "frac": dbytes / (dcold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                            "method": "median of 20 single steps, each after a 512 MiB scratch write"},
+                   "two_states": {"us_per_step": dalt_ms * 1e3,
+                                  "frac": dbytes / (dalt_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                  "method": "back-to-back steps alternating between two 256 MiB "
+                                            "states (512 MiB, beyond the 256 MB last-level cache)"},
                    "norm_gate_fused": {
                        "entry": "gdr2_decode_step_norm_gate (RMSNorm over dv + SiLU gate in the store)",
                        "us_per_step": gms * 1e3, "alg_bytes": gbytes,
@@ -512,6 +646,8 @@ def main():
                      "roofline": {"bound": "hbm", "achieved": egbs, "peak": HBM_PEAK_GBS,
                                   "unit": "GB/s", "frac": egbs / HBM_PEAK_GBS,
                                   "traffic": load_traffic("fwd", "norm_gate_kernel<1, true>")}},
+        "varlen": varlen,
+        "ceilings": ceil,
         "cpu_baseline": cpu,
         "source_hash": source_hash(),
     }

@@ -26,8 +26,10 @@
  *     in fp32 (pages, Appendix D.1).
  *   - Calls are stream ordered and asynchronous: they enqueue kernels on
  *     `stream` (a hipStream_t; NULL is the null stream) and return without
- *     synchronising.  They are reentrant; the library has no global mutable
- *     state besides a thread-local error string.
+ *     synchronising.  They are reentrant: the only global mutable state is a
+ *     thread-local error string and, per kernel and device, an atomic flag
+ *     recording that its LDS limit has been raised (setting it twice is
+ *     harmless).
  *   - Every argument error is detected on the host before any device call:
  *     nothing is written, the status is returned and gdr2_last_error()
  *     describes it.  A failed launch returns GDR2_E_LAUNCH.
@@ -75,10 +77,11 @@ typedef enum {
  * B*H*P <= 256 and at least 16 chunks per segment; then P is reduced to
  * ceil(ceil(T/64) / ceil(ceil(T/64) / P))), and the workspace adds, from the
  * next 256-byte boundary after the records, B*P*H*dk*(dk + dv) fp32 values
- * for the segments' transfer matrices and end states.  With
- * GDR2_F32 only packed calls with more than one sequence need workspace (their
- * longest-first order).  The workspace is scratch: its contents on entry do
- * not matter and are not meaningful on return.
+ * for the segments' transfer matrices and end states.  With GDR2_F32 the
+ * forward runs on the fp32 blocks of the backward's front pass and needs
+ * exactly gdr2_chunk_bwd_workspace_bytes(B, T, H, dk, dv, num_seqs) bytes.
+ * The workspace is scratch: its contents on entry do not matter and are not
+ * meaningful on return.
  */
 size_t gdr2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs,
                                       gdr2_dtype in_dtype);
@@ -109,18 +112,30 @@ size_t gdr2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  * (see gdr2_chunk_fwd_workspace_bytes), a transfer pass first gives every
  * segment its affine map of the entry state (Eq. 23 composed over its
  * chunks), an fp32 scan chains the maps, and the state pass then walks all
- * segments at once from their true entry states.  With GDR2_F32 one kernel
- * walks the chunks and does both.
+ * segments at once from their true entry states.  With GDR2_F32 a front
+ * kernel forms every (chunk, head)'s decay, chunk matrices, WY inverse and its
+ * products in fp32 (the first pass of gdr2_chunk_bwd), and a sequential
+ * kernel per (sequence, head, 32 value channels) forms o and S_T from them.
  *
  * Precision: the cumulative log-decay, the WY solve's diagonal blocks, every
  * accumulation and the state are fp32.  With in_dtype = GDR2_F32 every
  * matrix product takes fp32 operands.  With GDR2_BF16 the products take
  * 16-bit operands: bf16 for the decay-normalised chunk matrix, a bf16 hi/lo
- * pair for the causal score matrix, and fp16 for the bounded state-pass
- * operands (stored in that form in the workspace records).  The per-channel
- * log-decay summed over any 8 consecutive tokens must stay above -80 (the
- * decay normalisation is centred inside each 16-token block of a chunk);
- * stronger decay gives undefined results.
+ * pair for the causal score matrix, and fp16 for the state-pass operands
+ * (stored in that form in the workspace records): the state, the chunk's
+ * write targets U = A (w * v) and residuals R, and the decay-scaled q, k, b k,
+ * which are at most |q|, |k|, |b k|.  The state-pass values must therefore
+ * stay inside the fp16 range (|S|, |U|, |R| < 65504; with unit-norm keys and
+ * b, w in [0, 2] that is |v| and |S0| below about 1e4); beyond it they become
+ * +-inf.
+ *
+ * Decay: any log_alpha <= 0 is computed as given.  The 16-bit products use
+ * decay factors normalised on one row per chunk, or per 16-token block when
+ * the chunk's decay is stronger; a chunk whose decay even those factors
+ * cannot carry (a factor beyond 2^112) is flagged and formed again, entry by
+ * entry with the exact decay, by the same kernel after its other chunks (about
+ * three times the cost of an ordinary chunk).  The fp32 path uses one row per
+ * chunk and the same exact path beyond e^80.
  */
 gdr2_status gdr2_chunk_fwd(const void *q, const void *k, const void *v,
                            const void *log_alpha, const void *b, const void *w,
@@ -129,6 +144,23 @@ gdr2_status gdr2_chunk_fwd(const void *q, const void *k, const void *v,
                            int B, int T, int H, int dk, int dv,
                            gdr2_dtype in_dtype, gdr2_dtype log_alpha_dtype,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gdr2_chunk_fwd with the output o stored in fp32 whatever in_dtype (the same
+ * passage and the same arithmetic; with in_dtype = GDR2_F32 it is exactly
+ * gdr2_chunk_fwd).  o : fp32 [B, T, H, dv].  For 16-bit inputs this keeps the
+ * output's fp32 accumulation instead of rounding it to bf16: a bf16 store of
+ * an exact value is off by up to 2^-8 of its magnitude, which for outputs
+ * many times the RMS exceeds an error bound taken relative to the RMS.  Every
+ * other argument, the workspace and the errors are those of gdr2_chunk_fwd.
+ */
+gdr2_status gdr2_chunk_fwd_f32_out(const void *q, const void *k, const void *v,
+                                   const void *log_alpha, const void *b, const void *w,
+                                   const float *S0, float *o, float *S_T,
+                                   const int32_t *cu_seqlens, int num_seqs,
+                                   int B, int T, int H, int dk, int dv,
+                                   gdr2_dtype in_dtype, gdr2_dtype log_alpha_dtype,
+                                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Bytes of device workspace gdr2_chunk_bwd needs for these sizes (num_seqs as
@@ -161,9 +193,12 @@ size_t gdr2_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  *       gradient rows outside [cu[0], cu[N]) are not written.
  *   workspace : at least gdr2_chunk_bwd_workspace_bytes() bytes of scratch.
  * With T == 0 the token tensors may be NULL and dS0 = dS_T (zeros without it).
- * The centred decay factors of the chunk products need the per-channel
- * log-decay summed over the 32 tokens on either side of a chunk's row 31 to
- * stay above -80.
+ * Any log_alpha <= 0 is handled: the decay-weighted chunk products use factors
+ * normalised on a chunk's row 31, and a chunk where some channel's decay moves
+ * more than 80 nats from that row forms them entry by entry with the exact
+ * decay instead.  The decay gradient sums each of its terms once (no term is
+ * added and taken away again), so it keeps its relative precision when the
+ * decay is strong and the gradient itself is small.
  */
 gdr2_status gdr2_chunk_bwd(const void *q, const void *k, const void *v, const void *log_alpha,
                            const void *b, const void *w, const float *S0, const void *dO,
@@ -210,8 +245,8 @@ gdr2_status gdr2_chunk_bwd(const void *q, const void *k, const void *v, const vo
  *         num_seqs, GDR2_BF16) bytes.
  * Unknown flag bits give GDR2_E_UNSUPPORTED; Hv not a multiple of H gives
  * GDR2_E_SHAPE.  flags = 0 with Hv = H is gdr2_chunk_fwd with bf16 inputs.
- * Precision and the decay limit are those of gdr2_chunk_fwd with GDR2_BF16,
- * applied to the activated values.
+ * Precision and the handling of strong decay are those of gdr2_chunk_fwd
+ * with GDR2_BF16, applied to the activated values.
  */
 gdr2_status gdr2_chunk_fwd_block(const void *q, const void *k, const void *v, const void *f,
                                  const void *b, const void *w, const float *decay_a,

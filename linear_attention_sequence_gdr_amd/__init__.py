@@ -40,7 +40,8 @@ __all__ = ["gdr2_chunk_fwd", "gdr2_chunk_bwd", "gdr2_chunk_bwd_workspace_bytes",
 GDR2_F32, GDR2_BF16 = 0, 1
 STATUS = {0: "GDR2_OK", 1: "GDR2_E_NULL", 2: "GDR2_E_SHAPE", 3: "GDR2_E_DTYPE",
           4: "GDR2_E_ALIGN", 5: "GDR2_E_UNSUPPORTED", 6: "GDR2_E_WORKSPACE", 7: "GDR2_E_LAUNCH"}
-EXPORTS = ("gdr2_chunk_fwd_workspace_bytes", "gdr2_chunk_fwd", "gdr2_chunk_fwd_block",
+EXPORTS = ("gdr2_chunk_fwd_workspace_bytes", "gdr2_chunk_fwd", "gdr2_chunk_fwd_f32_out",
+           "gdr2_chunk_fwd_block",
            "gdr2_chunk_bwd_workspace_bytes", "gdr2_chunk_bwd", "gdr2_decode_step",
            "gdr2_norm_gate", "gdr2_decode_step_norm_gate",
            "gdr2_status_string", "gdr2_last_error", "gdr2_version")
@@ -76,6 +77,8 @@ def library():
         lib.gdr2_chunk_fwd_workspace_bytes.restype = sz
         lib.gdr2_chunk_fwd.argtypes = [vp] * 10 + [i32] * 6 + [i32, i32, vp, sz, vp]
         lib.gdr2_chunk_fwd.restype = i32
+        lib.gdr2_chunk_fwd_f32_out.argtypes = lib.gdr2_chunk_fwd.argtypes
+        lib.gdr2_chunk_fwd_f32_out.restype = i32
         lib.gdr2_decode_step.argtypes = [vp] * 8 + [i32] * 6 + [vp]
         lib.gdr2_decode_step.restype = i32
         f32, i64 = ctypes.c_float, ctypes.c_longlong
@@ -132,10 +135,30 @@ def _ptr(t: Optional[torch.Tensor], name: str, device) -> Optional[int]:
     return t.data_ptr()
 
 
-def _stream(stream, device) -> int:
+def _device(x: torch.Tensor, name: str):
+    """The device of the leading tensor of a call, which must be a GPU tensor
+    (checked before any stream or device query)."""
+    if not x.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return x.device
+
+
+def _torch_stream(stream, device):
+    """The stream the kernels are enqueued on, as a torch stream: torch's current
+    stream on ``device`` when ``stream`` is None, a torch stream as given, or a
+    raw hipStream_t handle wrapped as an external stream.  Every call makes it
+    current while it allocates its outputs and workspace (and fills any zeros),
+    so those tensors belong to that stream: the caching allocator hands their
+    memory to later work only in stream order after the kernels that use it."""
     if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def _stream(s) -> int:
+    return int(s.cuda_stream)
 
 
 def _check(status: int):
@@ -152,19 +175,34 @@ def gdr2_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha:
                    b: torch.Tensor, w: torch.Tensor, S0: Optional[torch.Tensor] = None,
                    cu_seqlens: Optional[torch.Tensor] = None, *, o: Optional[torch.Tensor] = None,
                    S_T: Optional[torch.Tensor] = None, want_state: bool = True,
-                   workspace: Optional[torch.Tensor] = None, stream=None):
+                   workspace: Optional[torch.Tensor] = None, stream=None,
+                   o_dtype: Optional[torch.dtype] = None):
     """Chunkwise forward.  q, k, log_alpha, b: [B, T, H, dk]; v, w: [B, T, H, dv];
     S0: fp32 [N, H, dk, dv] or None; cu_seqlens: int32 [N+1] (B == 1) or None.
-    ``o``/``S_T``/``workspace`` may be passed to avoid allocation.  Returns
-    ``(o, S_T)`` (S_T is None when ``want_state`` is False and none is given)."""
+    ``o``/``S_T``/``workspace`` may be passed to avoid allocation.  ``o`` has
+    q's dtype by default; an fp32 ``o`` (or ``o_dtype=torch.float32``) with
+    bf16 inputs calls gdr2_chunk_fwd_f32_out.  Returns ``(o, S_T)`` (S_T is
+    None when ``want_state`` is False and none is given)."""
     lib = library()
-    dev = q.device
+    dev = _device(q, "q")
+    s = _torch_stream(stream, dev)
+    with torch.cuda.stream(s):
+        return _chunk_fwd(lib, dev, s, q, k, v, log_alpha, b, w, S0, cu_seqlens, o, S_T, want_state,
+                          workspace, o_dtype)
+
+
+def _chunk_fwd(lib, dev, s, q, k, v, log_alpha, b, w, S0, cu_seqlens, o, S_T, want_state, workspace,
+               o_dtype):
     Bsz, T, H, dk = q.shape
     dv = v.shape[-1]
     in_dt = _dtype_code(q)
     N = Bsz if cu_seqlens is None else cu_seqlens.numel() - 1
+    if o_dtype is None:
+        o_dtype = q.dtype if o is None else o.dtype
+    if o_dtype not in (q.dtype, torch.float32):
+        raise TypeError(f"o_dtype must be {q.dtype} or torch.float32, got {o_dtype}")
     if o is None:
-        o = torch.empty((Bsz, T, H, dv), dtype=q.dtype, device=dev)
+        o = torch.empty((Bsz, T, H, dv), dtype=o_dtype, device=dev)
     if S_T is None and want_state:
         S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     ws_bytes = gdr2_chunk_fwd_workspace_bytes(Bsz, T, H, dk, dv,
@@ -174,7 +212,7 @@ def gdr2_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha:
     if workspace is not None:
         ws_bytes = workspace.numel() * workspace.element_size()
     for name, t, want in (("k", k, q.dtype), ("v", v, q.dtype), ("b", b, q.dtype), ("w", w, q.dtype),
-                          ("o", o, q.dtype)):
+                          ("o", o, o_dtype)):
         if t.dtype != want:
             raise TypeError(f"{name} has dtype {t.dtype}, expected {want}")
     for name, t in (("k", k), ("log_alpha", log_alpha), ("b", b)):
@@ -188,12 +226,13 @@ def gdr2_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha:
             raise ValueError(f"{name} must be fp32 {(N, H, dk, dv)}")
     if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
-    st = lib.gdr2_chunk_fwd(
+    entry = lib.gdr2_chunk_fwd if o_dtype == q.dtype else lib.gdr2_chunk_fwd_f32_out
+    st = entry(
         _ptr(q, "q", dev), _ptr(k, "k", dev), _ptr(v, "v", dev), _ptr(log_alpha, "log_alpha", dev),
         _ptr(b, "b", dev), _ptr(w, "w", dev), _ptr(S0, "S0", dev), _ptr(o, "o", dev),
         _ptr(S_T, "S_T", dev), _ptr(cu_seqlens, "cu_seqlens", dev), N if cu_seqlens is not None else 0,
         Bsz, T, H, dk, dv, in_dt, _dtype_code(log_alpha), _ptr(workspace, "workspace", dev),
-        ws_bytes, _stream(stream, dev))
+        ws_bytes, _stream(s))
     _check(st)
     return o, S_T
 
@@ -204,11 +243,13 @@ def gdr2_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alph
     """One decode step.  q, k, log_alpha, b: [N, H, dk]; v, w: [N, H, dv];
     S: fp32 [N, H, dk, dv] updated in place.  Returns o [N, H, dv]."""
     lib = library()
-    dev = q.device
+    dev = _device(q, "q")
     N, H, dk = q.shape
     dv = v.shape[-1]
+    s = _torch_stream(stream, dev)
     if o is None:
-        o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+        with torch.cuda.stream(s):
+            o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
     for name, t, shp in (("k", k, (N, H, dk)), ("log_alpha", log_alpha, (N, H, dk)),
                          ("b", b, (N, H, dk)), ("v", v, (N, H, dv)), ("w", w, (N, H, dv)),
                          ("o", o, (N, H, dv)), ("S", S, (N, H, dk, dv))):
@@ -219,7 +260,7 @@ def gdr2_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alph
     st = lib.gdr2_decode_step(
         _ptr(q, "q", dev), _ptr(k, "k", dev), _ptr(v, "v", dev), _ptr(log_alpha, "log_alpha", dev),
         _ptr(b, "b", dev), _ptr(w, "w", dev), _ptr(S, "S", dev), _ptr(o, "o", dev),
-        N, H, dk, dv, _dtype_code(q), _dtype_code(log_alpha), _stream(stream, dev))
+        N, H, dk, dv, _dtype_code(q), _dtype_code(log_alpha), _stream(s))
     _check(st)
     return o
 
@@ -232,13 +273,15 @@ def gdr2_norm_gate(o: torch.Tensor, z: torch.Tensor, weight: Optional[torch.Tens
     whole last axis).  o, z (and y): one shape, bf16 or fp32; weight: fp32
     [o.shape[-1]] or None.  ``y`` may be ``o`` or ``z`` (in place)."""
     lib = library()
-    dev = o.device
+    dev = _device(o, "o")
     d = o.shape[-1]
     group = d if group is None else int(group)
     if z.shape != o.shape or z.dtype != o.dtype:
         raise ValueError(f"z must match o ({tuple(o.shape)}, {o.dtype}), got {tuple(z.shape)}, {z.dtype}")
+    s = _torch_stream(stream, dev)
     if y is None:
-        y = torch.empty_like(o)
+        with torch.cuda.stream(s):
+            y = torch.empty_like(o)
     if y.shape != o.shape or y.dtype != o.dtype:
         raise ValueError("y must match o in shape and dtype")
     if weight is not None and (weight.dtype != torch.float32 or tuple(weight.shape) != (d,)):
@@ -246,7 +289,7 @@ def gdr2_norm_gate(o: torch.Tensor, z: torch.Tensor, weight: Optional[torch.Tens
     rows = o.numel() // d if d else 0
     st = lib.gdr2_norm_gate(_ptr(o, "o", dev), _ptr(z, "z", dev), _ptr(weight, "weight", dev),
                             _ptr(y, "y", dev), rows, d, group, float(eps), _dtype_code(o),
-                            _stream(stream, dev))
+                            _stream(s))
     _check(st)
     return y
 
@@ -260,11 +303,13 @@ def gdr2_decode_step_norm_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     RMSNorm(o) * norm_weight * silu(z) over each head's dv channels.  z: [N, H,
     dv] in q's dtype; norm_weight: fp32 [dv] or None.  Returns y [N, H, dv]."""
     lib = library()
-    dev = q.device
+    dev = _device(q, "q")
     N, H, dk = q.shape
     dv = v.shape[-1]
+    s = _torch_stream(stream, dev)
     if y is None:
-        y = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+        with torch.cuda.stream(s):
+            y = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
     for name, t, shp in (("k", k, (N, H, dk)), ("log_alpha", log_alpha, (N, H, dk)),
                          ("b", b, (N, H, dk)), ("v", v, (N, H, dv)), ("w", w, (N, H, dv)),
                          ("z", z, (N, H, dv)), ("y", y, (N, H, dv)), ("S", S, (N, H, dk, dv))):
@@ -281,7 +326,7 @@ def gdr2_decode_step_norm_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
         _ptr(q, "q", dev), _ptr(k, "k", dev), _ptr(v, "v", dev), _ptr(log_alpha, "log_alpha", dev),
         _ptr(b, "b", dev), _ptr(w, "w", dev), _ptr(S, "S", dev), _ptr(z, "z", dev),
         _ptr(norm_weight, "norm_weight", dev), float(eps), _ptr(y, "y", dev),
-        N, H, dk, dv, _dtype_code(q), _dtype_code(log_alpha), _stream(stream, dev))
+        N, H, dk, dv, _dtype_code(q), _dtype_code(log_alpha), _stream(s))
     _check(st)
     return y
 
@@ -302,11 +347,19 @@ def gdr2_chunk_fwd_block(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, f: t
     W_w x under GDR2_PRO_GATES, q and k are L2-normalised under
     GDR2_PRO_QK_L2NORM.  Returns ``(o [B, T, Hv, dv], S_T [N, Hv, dk, dv])``."""
     lib = library()
-    dev = q.device
-    Bsz, T, H, dk = q.shape
-    Hv, dv = v.shape[-2], v.shape[-1]
+    dev = _device(q, "q")
     if q.dtype != torch.bfloat16:
         raise TypeError("gdr2_chunk_fwd_block takes bf16 q, k, v, b, w")
+    s = _torch_stream(stream, dev)
+    with torch.cuda.stream(s):
+        return _chunk_fwd_block(lib, dev, s, q, k, v, f, b, w, decay_a, decay_bias, flags, b_scale,
+                                qk_eps, S0, cu_seqlens, o, S_T, want_state, workspace)
+
+
+def _chunk_fwd_block(lib, dev, s, q, k, v, f, b, w, decay_a, decay_bias, flags, b_scale, qk_eps, S0,
+                     cu_seqlens, o, S_T, want_state, workspace):
+    Bsz, T, H, dk = q.shape
+    Hv, dv = v.shape[-2], v.shape[-1]
     N = Bsz if cu_seqlens is None else cu_seqlens.numel() - 1
     if o is None:
         o = torch.empty((Bsz, T, Hv, dv), dtype=torch.bfloat16, device=dev)
@@ -337,7 +390,7 @@ def gdr2_chunk_fwd_block(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, f: t
         _ptr(w, "w", dev), _ptr(decay_a, "decay_a", dev), _ptr(decay_bias, "decay_bias", dev),
         int(flags), float(b_scale), float(qk_eps), _ptr(S0, "S0", dev), _ptr(o, "o", dev),
         _ptr(S_T, "S_T", dev), _ptr(cu_seqlens, "cu_seqlens", dev), ns, Bsz, T, H, Hv, dk, dv,
-        _dtype_code(f), _ptr(workspace, "workspace", dev), ws_bytes, _stream(stream, dev))
+        _dtype_code(f), _ptr(workspace, "workspace", dev), ws_bytes, _stream(s))
     _check(st)
     return o, S_T
 
@@ -356,7 +409,14 @@ def gdr2_chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha:
     Returns a dict of fp32 gradients dq, dk, dlog_alpha, db [B, T, H, dk],
     dv, dw [B, T, H, dv] and dS0 [N, H, dk, dv] (None unless ``want_dS0``)."""
     lib = library()
-    dev = q.device
+    dev = _device(q, "q")
+    s = _torch_stream(stream, dev)
+    with torch.cuda.stream(s):
+        return _chunk_bwd(lib, dev, s, q, k, v, log_alpha, b, w, dO, S0, dS_T, cu_seqlens, want_dS0,
+                          workspace)
+
+
+def _chunk_bwd(lib, dev, s, q, k, v, log_alpha, b, w, dO, S0, dS_T, cu_seqlens, want_dS0, workspace):
     Bsz, T, H, dk = q.shape
     dv = v.shape[-1]
     N = Bsz if cu_seqlens is None else cu_seqlens.numel() - 1
@@ -391,6 +451,6 @@ def gdr2_chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha:
         _ptr(g["dv"], "dv", dev), _ptr(g["dlog_alpha"], "dlog_alpha", dev), _ptr(g["db"], "db", dev),
         _ptr(g["dw"], "dw", dev), _ptr(g["dS0"], "dS0", dev), _ptr(cu_seqlens, "cu_seqlens", dev),
         ns, Bsz, T, H, dk, dv, _dtype_code(q), _dtype_code(log_alpha), _ptr(workspace, "workspace", dev),
-        ws_bytes, _stream(stream, dev))
+        ws_bytes, _stream(s))
     _check(st)
     return g

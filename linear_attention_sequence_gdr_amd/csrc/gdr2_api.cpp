@@ -38,7 +38,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // sequences with few (sequence, head) chains split each chain into P segments
 // of segc chunks; they add the segments' transfer matrices and end states.
 struct Layout {
-  size_t order, cbase, tab, rec, phi, ex, total;
+  size_t order, cbase, tab, rec, phi, ex, sflag, total;
   long long cap;  // chunks with a record
   int P, segc;
 };
@@ -72,7 +72,34 @@ Layout two_pass_layout(int B, int T, int H, int dk, int dv, int num_seqs) {
     l.ex = l.phi + chains * dk * dk * sizeof(float);
     off = l.ex + chains * dk * dv * sizeof(float);
   }
+  // one int per record: its chunk needed the exact-decay path
+  l.sflag = align256(off);
+  off = l.sflag + (size_t)l.cap * (size_t)H * sizeof(int32_t);
   l.total = off;
+  return l;
+}
+
+// Workspace of the backward: packed-sequence tables, then one fp32 block per
+// (chunk, head) item.
+struct BwdLayoutHost {
+  size_t cbase, tab, items, total;
+  long long cap;
+};
+BwdLayoutHost bwd_layout(int B, int T, int H, int dk, int dv, int num_seqs) {
+  BwdLayoutHost l{};
+  const long long nc = ((long long)T + 63) / 64;
+  size_t off = 0;
+  if (num_seqs > 0) {
+    l.cap = nc + num_seqs;
+    l.cbase = off;
+    off += align256(sizeof(int32_t) * ((size_t)num_seqs + 1));
+    l.tab = off;
+    off += align256(2 * sizeof(int32_t) * (size_t)l.cap);
+  } else {
+    l.cap = (long long)B * nc;
+  }
+  l.items = off;
+  l.total = off + (size_t)l.cap * (size_t)H * gdr2::bwd_item_bytes(dk, dv);
   return l;
 }
 
@@ -82,7 +109,7 @@ gdr2_status two_pass(const char* fn, const void* q, const void* k, const void* v
                      const void* log_alpha, const void* b, const void* w, const float* S0, void* o,
                      float* S_T, const int32_t* cu_seqlens, int N, int B, int T, int Hk, int Hv,
                      int dk, int dv, bool la_bf16, int pro, const float* da, const float* db,
-                     float b_scale, float qk_eps, char* ws, hipStream_t st) {
+                     float b_scale, float qk_eps, bool o_f32, char* ws, hipStream_t st) {
   // intra-chunk pass over all (chunk, value head) items, then the state pass
   const int ns = cu_seqlens ? N : 0;
   const Layout l = two_pass_layout(B, T, Hv, dk, dv, ns);
@@ -103,6 +130,7 @@ gdr2_status two_pass(const char* fn, const void* q, const void* k, const void* v
   gdr2::IntraArgs ia;
   ia.q = q; ia.k = k; ia.v = v; ia.la = log_alpha; ia.b = b; ia.w = w;
   ia.rec = ws + l.rec;
+  ia.sflag = reinterpret_cast<int*>(ws + l.sflag);
   ia.tab = tab;
   ia.total = cu_seqlens ? cbase + N : nullptr;
   ia.nc = (T + 63) / 64;
@@ -113,7 +141,7 @@ gdr2_status two_pass(const char* fn, const void* q, const void* k, const void* v
   ia.pro = pro; ia.da = da; ia.db = db; ia.b_scale = b_scale; ia.qk_eps = qk_eps;
   gdr2::StateArgs sa;
   sa.rec = ws + l.rec;
-  sa.S0 = S0; sa.o = o; sa.ST = S_T; sa.cu = cu_seqlens; sa.order = order; sa.cbase = cbase;
+  sa.S0 = S0; sa.o = o; sa.o_f32 = o_f32 ? 1 : 0; sa.ST = S_T; sa.cu = cu_seqlens; sa.order = order; sa.cbase = cbase;
   sa.cap = (int)l.cap;
   sa.N = N; sa.T = T; sa.H = Hv; sa.DV = dv;
   sa.P = l.P; sa.segc = l.segc;
@@ -151,77 +179,113 @@ size_t gdr2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
   if (B <= 0 || T < 0 || H <= 0 || !dim_ok(dk) || !dim_ok(dv) || num_seqs < 0 ||
       !dtype_ok(in_dtype))
     return 0;
-  if (in_dtype == GDR2_F32) {
-    const size_t s = gdr2::schedule_bytes(num_seqs);
-    return s ? align256(s) : 0;
-  }
+  if (in_dtype == GDR2_F32) return bwd_layout(B, T, H, dk, dv, num_seqs).total;
   const Layout l = two_pass_layout(B, T, H, dk, dv, num_seqs);
   return l.total;
 }
+
+}  // extern "C"
+
+namespace {
+
+// gdr2_chunk_fwd and gdr2_chunk_fwd_f32_out: o in in_dtype, or fp32 (o_f32).
+gdr2_status chunk_fwd_common(const char* fn, const void* q, const void* k, const void* v,
+                             const void* log_alpha, const void* b, const void* w, const float* S0,
+                             void* o, float* S_T, const int32_t* cu_seqlens, int num_seqs, int B,
+                             int T, int H, int dk, int dv, gdr2_dtype in_dtype,
+                             gdr2_dtype log_alpha_dtype, bool o_f32, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !log_alpha || !b || !w || !o)
+    return fail(GDR2_E_NULL, "%s: q, k, v, log_alpha, b, w and o must be non-NULL", fn);
+  if (!dtype_ok(in_dtype) || !dtype_ok(log_alpha_dtype))
+    return fail(GDR2_E_DTYPE, "%s: dtype codes %d/%d are not GDR2_F32 or GDR2_BF16", fn,
+                (int)in_dtype, (int)log_alpha_dtype);
+  if (B <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0)
+    return fail(GDR2_E_SHAPE, "%s: need B >= 1, T >= 0, H >= 1, dk, dv >= 1 (got B=%d T=%d H=%d dk=%d dv=%d)",
+                fn, B, T, H, dk, dv);
+  if (!dim_ok(dk) || !dim_ok(dv))
+    return fail(GDR2_E_UNSUPPORTED, "%s: dk=%d dv=%d; each must be 32, 64 or 128", fn, dk, dv);
+  const bool bf16 = in_dtype == GDR2_BF16;
+  int N = B;
+  if (cu_seqlens) {
+    if (B != 1)
+      return fail(GDR2_E_SHAPE, "%s: packed sequences (cu_seqlens) need B == 1, got B=%d", fn, B);
+    if (num_seqs < 1)
+      return fail(GDR2_E_SHAPE, "%s: num_seqs must be >= 1 with cu_seqlens, got %d", fn, num_seqs);
+    N = num_seqs;
+  }
+  if ((long long)N * H > (1LL << 26))
+    return fail(GDR2_E_SHAPE, "%s: N*H = %lld (sequence, head) pairs is too many", fn, (long long)N * H);
+  const void* ptrs[] = {q, k, v, log_alpha, b, w, o, S0, S_T, cu_seqlens, workspace};
+  const char* names[] = {"q", "k", "v", "log_alpha", "b", "w", "o", "S0", "S_T", "cu_seqlens", "workspace"};
+  for (int i = 0; i < 11; ++i)
+    if (ptrs[i] && !aligned16(ptrs[i]))
+      return fail(GDR2_E_ALIGN, "%s: %s is not 16-byte aligned", fn, names[i]);
+  const int ns = cu_seqlens ? N : 0;
+  const long long items =
+      bf16 ? two_pass_layout(B, T, H, dk, dv, ns).cap * H : bwd_layout(B, T, H, dk, dv, ns).cap * H;
+  if (items > 0x7fffffffLL)
+    return fail(GDR2_E_SHAPE, "%s: %lld (chunk, head) items exceed 2^31 - 1", fn, items);
+  const size_t need = gdr2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, ns, in_dtype);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(GDR2_E_WORKSPACE, "%s: workspace of %zu bytes needed, got %zu%s", fn, need,
+                workspace_bytes, workspace ? "" : " (NULL)");
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if (!bf16) {
+    // fp32 inputs: the fp32 front pass per (chunk, head), then the sequential
+    // pass per (sequence, head, 32 value channels) that forms o and S_T
+    const BwdLayoutHost l = bwd_layout(B, T, H, dk, dv, ns);
+    gdr2::BwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.b = b; a.w = w;
+    a.S0 = S0; a.o = static_cast<float*>(o); a.ST = S_T;
+    a.ws = reinterpret_cast<float*>(ws + l.items);
+    if (cu_seqlens) {
+      int32_t* cbase = reinterpret_cast<int32_t*>(ws + l.cbase);
+      int32_t* tab = reinterpret_cast<int32_t*>(ws + l.tab);
+      const hipError_t e = gdr2::launch_chunk_table(cu_seqlens, N, T, (int)l.cap, cbase, tab, st);
+      if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "%s: chunk table launch: %s", fn, hipGetErrorString(e));
+      a.tab = tab; a.cbase = cbase; a.total = cbase + N;
+    }
+    a.nc = (T + 63) / 64;
+    a.chunks = (int)l.cap;
+    a.N = N; a.T = T; a.H = H;
+    a.in_bf16 = 0;
+    a.la_bf16 = log_alpha_dtype == GDR2_BF16;
+    const hipError_t e = gdr2::launch_fwd32(a, dk, dv, st);
+    if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "%s: launch: %s", fn, hipGetErrorString(e));
+    return GDR2_OK;
+  }
+
+  return two_pass(fn, q, k, v, log_alpha, b, w, S0, o, S_T, cu_seqlens, N, B, T, H, H, dk, dv,
+                  log_alpha_dtype == GDR2_BF16, 0, nullptr, nullptr, 1.f, 0.f, o_f32, ws, st);
+}
+
+}  // namespace
+
+extern "C" {
 
 gdr2_status gdr2_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
                            const void* b, const void* w, const float* S0, void* o, float* S_T,
                            const int32_t* cu_seqlens, int num_seqs, int B, int T, int H, int dk,
                            int dv, gdr2_dtype in_dtype, gdr2_dtype log_alpha_dtype,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !log_alpha || !b || !w || !o)
-    return fail(GDR2_E_NULL, "gdr2_chunk_fwd: q, k, v, log_alpha, b, w and o must be non-NULL");
-  if (!dtype_ok(in_dtype) || !dtype_ok(log_alpha_dtype))
-    return fail(GDR2_E_DTYPE, "gdr2_chunk_fwd: dtype codes %d/%d are not GDR2_F32 or GDR2_BF16",
-                (int)in_dtype, (int)log_alpha_dtype);
-  if (B <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0)
-    return fail(GDR2_E_SHAPE, "gdr2_chunk_fwd: need B >= 1, T >= 0, H >= 1, dk, dv >= 1 (got B=%d T=%d H=%d dk=%d dv=%d)",
-                B, T, H, dk, dv);
-  if (!dim_ok(dk) || !dim_ok(dv))
-    return fail(GDR2_E_UNSUPPORTED, "gdr2_chunk_fwd: dk=%d dv=%d; each must be 32, 64 or 128", dk, dv);
-  const bool bf16 = in_dtype == GDR2_BF16;
-  if (!gdr2::chunk_supported(dk, dv, bf16))
-    return fail(GDR2_E_UNSUPPORTED, "gdr2_chunk_fwd: fp32 inputs support dk of 32 or 64 (got dk=%d)", dk);
-  int N = B;
-  if (cu_seqlens) {
-    if (B != 1)
-      return fail(GDR2_E_SHAPE, "gdr2_chunk_fwd: packed sequences (cu_seqlens) need B == 1, got B=%d", B);
-    if (num_seqs < 1)
-      return fail(GDR2_E_SHAPE, "gdr2_chunk_fwd: num_seqs must be >= 1 with cu_seqlens, got %d", num_seqs);
-    N = num_seqs;
-  }
-  if ((long long)N * H > (1LL << 26))
-    return fail(GDR2_E_SHAPE, "gdr2_chunk_fwd: N*H = %lld (sequence, head) pairs is too many", (long long)N * H);
-  const void* ptrs[] = {q, k, v, log_alpha, b, w, o, S0, S_T, cu_seqlens, workspace};
-  const char* names[] = {"q", "k", "v", "log_alpha", "b", "w", "o", "S0", "S_T", "cu_seqlens", "workspace"};
-  for (int i = 0; i < 11; ++i)
-    if (ptrs[i] && !aligned16(ptrs[i]))
-      return fail(GDR2_E_ALIGN, "gdr2_chunk_fwd: %s is not 16-byte aligned", names[i]);
-  const int ns = cu_seqlens ? N : 0;
-  if (bf16 && two_pass_layout(B, T, H, dk, dv, ns).cap * H > 0x7fffffffLL)
-    return fail(GDR2_E_SHAPE, "gdr2_chunk_fwd: %lld (chunk, head) items exceed 2^31 - 1",
-                two_pass_layout(B, T, H, dk, dv, ns).cap * H);
-  const size_t need = gdr2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, ns, in_dtype);
-  if (need && (!workspace || workspace_bytes < need))
-    return fail(GDR2_E_WORKSPACE, "gdr2_chunk_fwd: workspace of %zu bytes needed, got %zu%s", need,
-                workspace_bytes, workspace ? "" : " (NULL)");
+  return chunk_fwd_common("gdr2_chunk_fwd", q, k, v, log_alpha, b, w, S0, o, S_T, cu_seqlens,
+                          num_seqs, B, T, H, dk, dv, in_dtype, log_alpha_dtype,
+                          in_dtype == GDR2_F32, workspace, workspace_bytes, stream);
+}
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  if (!bf16) {
-    // fp32 inputs: single fused kernel per (sequence, head, value block)
-    int32_t* order = need ? reinterpret_cast<int32_t*>(ws) : nullptr;
-    if (order) {
-      const hipError_t e = gdr2::launch_schedule(cu_seqlens, N, T, order, st);
-      if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "gdr2_chunk_fwd: schedule launch: %s", hipGetErrorString(e));
-    }
-    gdr2::ChunkArgs a;
-    a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.b = b; a.w = w;
-    a.S0 = S0; a.o = o; a.ST = S_T; a.cu = cu_seqlens; a.order = order;
-    a.N = N; a.T = T; a.H = H; a.DV = dv;
-    a.la_bf16 = log_alpha_dtype == GDR2_BF16;
-    const hipError_t e = gdr2::launch_chunk(a, dk, dv, bf16, st);
-    if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "gdr2_chunk_fwd: launch: %s", hipGetErrorString(e));
-    return GDR2_OK;
-  }
-
-  return two_pass("gdr2_chunk_fwd", q, k, v, log_alpha, b, w, S0, o, S_T, cu_seqlens, N, B, T, H, H,
-                  dk, dv, log_alpha_dtype == GDR2_BF16, 0, nullptr, nullptr, 1.f, 0.f, ws, st);
+gdr2_status gdr2_chunk_fwd_f32_out(const void* q, const void* k, const void* v,
+                                   const void* log_alpha, const void* b, const void* w,
+                                   const float* S0, float* o, float* S_T,
+                                   const int32_t* cu_seqlens, int num_seqs, int B, int T, int H,
+                                   int dk, int dv, gdr2_dtype in_dtype,
+                                   gdr2_dtype log_alpha_dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return chunk_fwd_common("gdr2_chunk_fwd_f32_out", q, k, v, log_alpha, b, w, S0, o, S_T,
+                          cu_seqlens, num_seqs, B, T, H, dk, dv, in_dtype, log_alpha_dtype, true,
+                          workspace, workspace_bytes, stream);
 }
 
 gdr2_status gdr2_chunk_fwd_block(const void* q, const void* k, const void* v, const void* f,
@@ -274,37 +338,10 @@ gdr2_status gdr2_chunk_fwd_block(const void* q, const void* k, const void* v, co
     return fail(GDR2_E_WORKSPACE, "%s: workspace of %zu bytes needed, got %zu%s", fn, need,
                 workspace_bytes, workspace ? "" : " (NULL)");
   return two_pass(fn, q, k, v, f, b, w, S0, o, S_T, cu_seqlens, N, B, T, H, Hv, dk, dv,
-                  f_dtype == GDR2_BF16, (int)flags, decay_a, decay_bias, b_scale, qk_eps,
+                  f_dtype == GDR2_BF16, (int)flags, decay_a, decay_bias, b_scale, qk_eps, false,
                   static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
 }
 
-namespace {
-
-// Workspace of the backward: packed-sequence tables, then one fp32 block per
-// (chunk, head) item.
-struct BwdLayoutHost {
-  size_t cbase, tab, items, total;
-  long long cap;
-};
-BwdLayoutHost bwd_layout(int B, int T, int H, int dk, int dv, int num_seqs) {
-  BwdLayoutHost l{};
-  const long long nc = ((long long)T + 63) / 64;
-  size_t off = 0;
-  if (num_seqs > 0) {
-    l.cap = nc + num_seqs;
-    l.cbase = off;
-    off += align256(sizeof(int32_t) * ((size_t)num_seqs + 1));
-    l.tab = off;
-    off += align256(2 * sizeof(int32_t) * (size_t)l.cap);
-  } else {
-    l.cap = (long long)B * nc;
-  }
-  l.items = off;
-  l.total = off + (size_t)l.cap * (size_t)H * gdr2::bwd_item_bytes(dk, dv);
-  return l;
-}
-
-}  // namespace
 
 size_t gdr2_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs) {
   if (B <= 0 || T < 0 || H <= 0 || !dim_ok(dk) || !dim_ok(dv) || num_seqs < 0) return 0;

@@ -73,6 +73,66 @@ __device__ __forceinline__ bool bwd_locate(const BwdArgs& a, int ci, long long& 
   return true;
 }
 
+// Factors centred on one row stay inside [e^-SLIM, e^SLIM] (nats); a chunk
+// that needs more takes the exact path.
+constexpr float BWD_SLIM = 80.f;
+
+// Exact decay-weighted chunk products for one 16x16 tile in C layout: lane
+// (m, g) gets, for q < 4, the sum over channels i of
+//     X[r + q][i] * K[c][i] * exp(G[r + q][i] - G[c][i])
+// with r = r0 (= 16 tm + 4 g), c = c0 (= 16 tn + m), from row-major [64][LD]
+// LDS blocks.  Entries with c > r + q are formed too (and masked by the
+// caller), so the exponent is not clamped.
+template <int DK, int LD>
+__device__ __forceinline__ f32x4 decay_product(const float* X, const float* K, const float* G, int r0,
+                                               int c0) {
+  f32x4 acc = zero4();
+  const float* gc = G + c0 * LD;
+  const float* kc = K + c0 * LD;
+#pragma unroll 2
+  for (int i = 0; i < DK; i += 4) {
+    const float4 g4 = *reinterpret_cast<const float4*>(gc + i);
+    const float4 k4 = *reinterpret_cast<const float4*>(kc + i);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 gr = *reinterpret_cast<const float4*>(G + (r0 + q) * LD + i);
+      const float4 xr = *reinterpret_cast<const float4*>(X + (r0 + q) * LD + i);
+      acc[q] = fmaf(xr.x * k4.x, __expf(gr.x - g4.x), acc[q]);
+      acc[q] = fmaf(xr.y * k4.y, __expf(gr.y - g4.y), acc[q]);
+      acc[q] = fmaf(xr.z * k4.z, __expf(gr.z - g4.z), acc[q]);
+      acc[q] = fmaf(xr.w * k4.w, __expf(gr.w - g4.w), acc[q]);
+    }
+  }
+  return acc;
+}
+
+// Exact decay-weighted products of the backward's strong chunks, for one
+// 16x16 tile in C layout: lane (m, g) gets, for q < 4 and x = x0 + q
+// (x0 = 16 tm + 4 g) and channel c,
+//   ROW:  sum over t <= x of M[x][t] * X[t][c] * exp(G[x][c] - G[t][c])
+//   !ROW: sum over t >= x of M[x][t] * X[t][c] * exp(G[t][c] - G[x][c])
+// over t in [t0, t1), M row-major with stride LDM, X and G row-major with
+// stride LDX.  Terms outside the triangle are discarded by a select, so an
+// overflowing exponent there never reaches the sum.
+template <int LDM, int LDX, bool ROW>
+__device__ __forceinline__ f32x4 decay_tri(const float* M, const float* X, const float* G, int x0, int c,
+                                           int t0, int t1) {
+  f32x4 acc = zero4();
+  float gx[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) gx[q] = G[(x0 + q) * LDX + c];
+  for (int t = t0; t < t1; ++t) {
+    const float xt = X[t * LDX + c], gt = G[t * LDX + c];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float term = M[(x0 + q) * LDM + t] * xt * __expf(ROW ? gx[q] - gt : gt - gx[q]);
+      const bool in = ROW ? t <= x0 + q : t >= x0 + q;
+      acc[q] = in ? acc[q] + term : acc[q];
+    }
+  }
+  return acc;
+}
+
 // ---- front: decay, the scaled rows, T, A_qk, A = (I + T)^-1, Y and U per item ----------
 // One workgroup per item:
 //   phase 1  log-decay rows into LDS, q, k, b into registers; G by a column
@@ -105,7 +165,8 @@ struct FrontCfg {
   static_assert(DK % 32 == 0 && DV % 32 == 0 && NT % DK == 0, "front pass tiling");
 };
 
-template <int DK, int DV, bool BF16, bool LA16>
+// FWD: the front pass of the fp32 forward, which needs neither G nor A later.
+template <int DK, int DV, bool BF16, bool LA16, bool FWD>
 __global__ __launch_bounds__(512) void bwd_front_kernel(BwdArgs a) {
   typedef BwdLayout<DK, DV> L;
   typedef FrontCfg<DK, DV> C;
@@ -169,13 +230,26 @@ __global__ __launch_bounds__(512) void bwd_front_kernel(BwdArgs a) {
       const int r = rb * RPB + k;
       const float G = off + run[k];
       sG[r * LKP + si] = G;
-      W[L::G + r * DK + si] = G;
+      if constexpr (!FWD) W[L::G + r * DK + si] = G;
       if (r == BC - 1) W[L::GC + si] = expf(G);
     }
   }
   __syncthreads();
 
   // ---- phase 2 ----
+  // A chunk whose decay moves some channel more than SLIM nats away from row
+  // 31 would take centred factors outside the fp32 range: it is "strong", and
+  // its T and A_qk are formed entry by entry with the exact decay instead
+  // (phase 3), from the raw rows b k, k and q.
+  bool strong_t = false;
+#pragma unroll
+  for (int u = 0; u < NEK; ++u) {
+    const int e = tid + NT * u, r = e / (DK / 4), i4 = e - r * (DK / 4);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      strong_t = strong_t || fabsf(sG[r * LKP + 4 * i4 + c] - sG[31 * LKP + 4 * i4 + c]) > BWD_SLIM;
+  }
+  const bool strong = __syncthreads_or(strong_t) != 0;
   float *sEP = sm + C::O_EP, *sKP = sm + C::O_KP, *sQP = sm + C::O_QP;
   f32x4 pg[NEK];  // G of this thread's units, for E in phase 5
 #pragma unroll
@@ -186,7 +260,8 @@ __global__ __launch_bounds__(512) void bwd_front_kernel(BwdArgs a) {
     for (int c = 0; c < 4; ++c) {
       const int i = 4 * i4 + c;
       const float G = sG[o + c], G31 = sG[31 * LKP + i], GCl = sG[(BC - 1) * LKP + i];
-      const float gam = expf(G), e1 = expf(G - G31), e2 = expf(G31 - G);
+      const float gam = expf(G);
+      const float e1 = strong ? 1.f : expf(G - G31), e2 = strong ? 1.f : expf(G31 - G);
       const float qv = pq[u][c], kv = pk[u][c], bv = pb[u][c];
       pg[u][c] = G;
       QG[c] = gam * qv;
@@ -224,8 +299,13 @@ __global__ __launch_bounds__(512) void bwd_front_kernel(BwdArgs a) {
   for (int u = 0; u < 2; ++u) {
     const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
     if (tn <= tm) {
-      aT[u] = mma_lds<float, DK>(zero4(), sEP + 16 * tm * LKP, LKP, sKP + 16 * tn * LKP, LKP);
-      aQ[u] = mma_lds<float, DK>(zero4(), sQP + 16 * tm * LKP, LKP, sKP + 16 * tn * LKP, LKP);
+      if (strong) {
+        aT[u] = decay_product<DK, LKP>(sEP, sKP, sG, 16 * tm + 4 * g, 16 * tn + m);
+        aQ[u] = decay_product<DK, LKP>(sQP, sKP, sG, 16 * tm + 4 * g, 16 * tn + m);
+      } else {
+        aT[u] = mma_lds<float, DK>(zero4(), sEP + 16 * tm * LKP, LKP, sKP + 16 * tn * LKP, LKP);
+        aQ[u] = mma_lds<float, DK>(zero4(), sQP + 16 * tm * LKP, LKP, sKP + 16 * tn * LKP, LKP);
+      }
     } else {
       aT[u] = aQ[u] = zero4();
     }
@@ -302,7 +382,8 @@ __global__ __launch_bounds__(512) void bwd_front_kernel(BwdArgs a) {
 #pragma unroll
   for (int u = 0; u < NAA; ++u) {
     const int e = tid + NT * u, s = e / (BC / 4), c4 = e - s * (BC / 4);
-    *reinterpret_cast<f32x4*>(W + L::A + s * BC + 4 * c4) = *reinterpret_cast<const f32x4*>(sA + s * LA + 4 * c4);
+    if constexpr (!FWD)
+      *reinterpret_cast<f32x4*>(W + L::A + s * BC + 4 * c4) = *reinterpret_cast<const f32x4*>(sA + s * LA + 4 * c4);
   }
   // E = gamma * b * k from the registers of phase 1-2, and Z = w * v
 #pragma unroll
@@ -338,10 +419,11 @@ __global__ __launch_bounds__(512) void bwd_front_kernel(BwdArgs a) {
 
 // Register prefetch of one chunk's operands for the sequential passes
 // (16-byte loads in address order, into row-major LDS blocks).
-template <int DK, int DV, int NK4, int NV4>
+// With FWD (the fp32 forward) Q_g and A_qk come too, for the output.
+template <int DK, int DV, int NK4, int NV4, int NC4, bool FWD>
 __device__ __forceinline__ void sf_load(const BwdArgs& a, int ci, int h, int jb, int tid,
                                         f32x4 (&ry)[NK4], f32x4 (&rk)[NK4], f32x4 (&ru)[NV4],
-                                        f32x4& rg) {
+                                        f32x4& rg, f32x4 (&rq)[NK4], f32x4 (&ra)[NC4]) {
   typedef BwdLayout<DK, DV> L;
   const float* Wn = a.ws + ((size_t)ci * a.H + h) * L::FLOATS;
 #pragma unroll
@@ -349,6 +431,11 @@ __device__ __forceinline__ void sf_load(const BwdArgs& a, int ci, int h, int jb,
     const int e4 = tid + SNT * u;
     ry[u] = reinterpret_cast<const f32x4*>(Wn + L::Y_)[e4];
     rk[u] = reinterpret_cast<const f32x4*>(Wn + L::KT)[e4];
+    if constexpr (FWD) rq[u] = reinterpret_cast<const f32x4*>(Wn + L::QG)[e4];
+  }
+  if constexpr (FWD) {
+#pragma unroll
+    for (int u = 0; u < NC4; ++u) ra[u] = reinterpret_cast<const f32x4*>(Wn + L::AQK)[tid + SNT * u];
   }
 #pragma unroll
   for (int u = 0; u < NV4; ++u) {
@@ -394,13 +481,18 @@ __device__ __forceinline__ void sb_load(const BwdArgs& a, int ci, int h, int jb,
 // state block is kept transposed in LDS (S^T, the B operand of Y S).  The
 // next two chunks' operands are loaded into registers (16-byte loads in
 // address order) while the current chunk computes.
-template <int DK, int DV>
+// FWD = false (the backward): saves the state entering every chunk and
+// R = U - Y S to the workspace.  FWD = true (the fp32 forward, Eqs. 23-24):
+// writes o = Q_g S + A_qk R for every chunk and the final state instead.
+template <int DK, int DV, bool FWD>
 __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
   typedef BwdLayout<DK, DV> L;
   constexpr int NB = DV / DVB, LK = DK + 4, LC = BC + 4, LV = DVB + 4;
   constexpr int NK4 = BC * DK / 4 / SNT;   // float4 per thread of a [BC][DK] block
   constexpr int NV4 = BC * DVB / 4 / SNT;  // float4 per thread of a [BC][DVB] block
+  constexpr int NC4 = FWD ? BC * BC / 4 / SNT : 1;  // float4 per thread of A_qk
   static_assert(NK4 >= 1 && NV4 >= 1, "state pass tiling");
+  static_assert(!FWD || (BC / 16) * (DVB / 16) == SNT / 64, "one output tile per wavefront");
   extern __shared__ __align__(16) unsigned char smem[];
   float* sST = reinterpret_cast<float*>(smem);  // [DVB][LK]
   float* sY = sST + DVB * LK;                   // [BC][LK]
@@ -408,6 +500,8 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
   float* sRT = sKt + BC * LK;                   // [DVB][LC]
   float* sU = sRT + DVB * LC;                   // [BC][LV]
   float* sGC = sU + BC * LV;                    // [DK]
+  float* sQg = sGC + DK;                        // FWD: [BC][LK]
+  float* sAq = sQg + BC * LK;                   // FWD: [BC][LC]
   // the NB value blocks of one (sequence, head) share an XCD (workgroups go
   // round the eight XCDs in order), so their reads of the chunk blocks they
   // all need hit that XCD's L2
@@ -422,17 +516,26 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
     sST[j * LK + i] = a.S0 ? a.S0[(size_t)nh * DK * DV + (size_t)i * DV + jb * DVB + j] : 0.f;
   }
   // two register sets in turn: chunks ci + 1 and ci + 2 are in flight while chunk ci computes
-  f32x4 ry0[NK4], rk0[NK4], ru0[NV4], rg0 = zero4();
-  f32x4 ry1[NK4], rk1[NK4], ru1[NV4], rg1 = zero4();
-  if (c0 < c1) sf_load<DK, DV, NK4, NV4>(a, c0, h, jb, tid, ry0, rk0, ru0, rg0);
-  if (c0 + 1 < c1) sf_load<DK, DV, NK4, NV4>(a, c0 + 1, h, jb, tid, ry1, rk1, ru1, rg1);
-  auto step = [&](const int ci, f32x4 (&ry)[NK4], f32x4 (&rk)[NK4], f32x4 (&ru)[NV4], f32x4& rg) {
-    float* W = a.ws + ((size_t)ci * a.H + h) * L::FLOATS;
+  f32x4 ry0[NK4], rk0[NK4], ru0[NV4], rg0 = zero4(), rq0[NK4], ra0[NC4];
+  f32x4 ry1[NK4], rk1[NK4], ru1[NV4], rg1 = zero4(), rq1[NK4], ra1[NC4];
+  if (c0 < c1) sf_load<DK, DV, NK4, NV4, NC4, FWD>(a, c0, h, jb, tid, ry0, rk0, ru0, rg0, rq0, ra0);
+  if (c0 + 1 < c1) sf_load<DK, DV, NK4, NV4, NC4, FWD>(a, c0 + 1, h, jb, tid, ry1, rk1, ru1, rg1, rq1, ra1);
+  auto step = [&](const int ci, f32x4 (&ry)[NK4], f32x4 (&rk)[NK4], f32x4 (&ru)[NV4], f32x4& rg,
+                  f32x4 (&rq)[NK4], f32x4 (&ra)[NC4]) {
+    [[maybe_unused]] float* W = a.ws + ((size_t)ci * a.H + h) * L::FLOATS;
 #pragma unroll
     for (int u = 0; u < NK4; ++u) {
       const int e4 = tid + SNT * u, r = e4 / (DK / 4), i = 4 * (e4 - r * (DK / 4));
       *reinterpret_cast<f32x4*>(sY + r * LK + i) = ry[u];
       *reinterpret_cast<f32x4*>(sKt + r * LK + i) = rk[u];
+      if constexpr (FWD) *reinterpret_cast<f32x4*>(sQg + r * LK + i) = rq[u];
+    }
+    if constexpr (FWD) {
+#pragma unroll
+      for (int u = 0; u < NC4; ++u) {
+        const int e4 = tid + SNT * u, r = e4 / (BC / 4), c4 = e4 - r * (BC / 4);
+        *reinterpret_cast<f32x4*>(sAq + r * LC + 4 * c4) = ra[u];
+      }
     }
 #pragma unroll
     for (int u = 0; u < NV4; ++u) {
@@ -440,27 +543,46 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
       *reinterpret_cast<f32x4*>(sU + r * LV + 4 * c4) = ru[u];
     }
     if (tid < DK / 4) *reinterpret_cast<f32x4*>(sGC + 4 * tid) = rg;
-    for (int e = tid; e < DK * DVB; e += SNT) {  // the state entering chunk ci
-      const int i = e / DVB, j = e - i * DVB;
-      W[L::S + (size_t)i * DV + jb * DVB + j] = sST[j * LK + i];
+    if constexpr (!FWD) {
+      for (int e = tid; e < DK * DVB; e += SNT) {  // the state entering chunk ci
+        const int i = e / DVB, j = e - i * DVB;
+        W[L::S + (size_t)i * DV + jb * DVB + j] = sST[j * LK + i];
+      }
     }
     __syncthreads();
     // the chunk after next into the registers just stored (near the end the
     // current chunk is reloaded instead: no branch)
-    sf_load<DK, DV, NK4, NV4>(a, ci + 2 < c1 ? ci + 2 : ci, h, jb, tid, ry, rk, ru, rg);
-    // R = U - Y S  [BC][DVB], kept for the output paths as well
+    sf_load<DK, DV, NK4, NV4, NC4, FWD>(a, ci + 2 < c1 ? ci + 2 : ci, h, jb, tid, ry, rk, ru, rg, rq, ra);
+    // R = U - Y S  [BC][DVB], kept for the output paths as well; the forward
+    // also forms Q_g S (same tile, from the state entering the chunk)
+    f32x4 ao = zero4();
     for (int t = wv; t < (BC / 16) * (DVB / 16); t += SNT / 64) {
       const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
       const f32x4 acc = mma_lds<float, DK>(zero4(), sY + 16 * tm * LK, LK, sST + 16 * tn * LK, LK);
+      if constexpr (FWD) ao = mma_lds<float, DK>(zero4(), sQg + 16 * tm * LK, LK, sST + 16 * tn * LK, LK);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = 16 * tm + 4 * g + q, j = 16 * tn + m;
         const float rv = sU[r * LV + j] - acc[q];
         sRT[j * LC + r] = rv;
-        W[L::R + (size_t)r * DV + jb * DVB + j] = rv;
+        if constexpr (!FWD) W[L::R + (size_t)r * DV + jb * DVB + j] = rv;
       }
     }
     __syncthreads();
+    if constexpr (FWD) {
+      // o = Q_g S + A_qk R (Eq. 24); A_qk is lower triangular, so row tile
+      // tm needs the first 16 (tm + 1) tokens of R only
+      const int tm = wv / (DVB / 16), tn = wv - tm * (DVB / 16);
+      ao = mma_lds_f32<BC, false, false>(ao, sAq + 16 * tm * LC, LC, sRT + 16 * tn * LC, LC, 16 * (tm + 1));
+      long long row0 = 0;
+      int clen = 0;
+      bwd_locate(a, ci, row0, clen);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 16 * tm + 4 * g + q;
+        if (r < clen) a.o[(size_t)(row0 + r) * a.H * DV + (size_t)h * DV + jb * DVB + 16 * tn + m] = ao[q];
+      }
+    }
     // S <- Diag(gamma_C) S + K_tail^T R  [DK][DVB]; each lane owns its entries
     for (int t = wv; t < (DK / 16) * (DVB / 16); t += SNT / 64) {
       const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
@@ -476,10 +598,18 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
   };
   int ci = c0;
   for (; ci + 1 < c1; ci += 2) {
-    step(ci, ry0, rk0, ru0, rg0);
-    step(ci + 1, ry1, rk1, ru1, rg1);
+    step(ci, ry0, rk0, ru0, rg0, rq0, ra0);
+    step(ci + 1, ry1, rk1, ru1, rg1, rq1, ra1);
   }
-  if (ci < c1) step(ci, ry0, rk0, ru0, rg0);
+  if (ci < c1) step(ci, ry0, rk0, ru0, rg0, rq0, ra0);
+  if constexpr (FWD) {
+    // the state after the sequence's last token (S0 itself for an empty one)
+    if (a.ST)
+      for (int e = tid; e < DK * DVB; e += SNT) {
+        const int i = e / DVB, j = e - i * DVB;
+        a.ST[(size_t)nh * DK * DV + (size_t)i * DV + jb * DVB + j] = sST[j * LK + i];
+      }
+  }
 }
 
 // ---- sequential reverse pass: dS' of every chunk, dR, and dS0 ------------------------
@@ -626,9 +756,13 @@ struct OutCfg {
   // E' [64][DK] from phase 2a to phase 4; per-channel values: G at row 31
   // and 63, gamma_C, the dS' * S row sums; the dg scan's row-block partial sums
   static constexpr int O_EP = mx(mx(mx(E1, E2), mx(E3, E4)), mx(E5, E6));
+  // strong chunks (see BWD_SLIM): G [64][DK] takes E''s place from phase 2a to
+  // phase 4, and b k [64][DK] sits behind phase 4's dT and dT^T
+  static constexpr int O_BK = E5;
+  static_assert(O_BK + BC * LKP <= O_EP, "b k block overlaps E'");
   static constexpr int O_G31 = O_EP + BC * LKP;
   static constexpr int O_GCL = O_G31 + DK, O_GCX = O_GCL + DK, O_RS = O_GCX + DK,
-                       O_PU = O_RS + DK, O_PV = O_PU + NT, FLOATS = O_PV + NT;
+                       O_PU = O_RS + DK, O_PV = O_PU + NT, O_DQK = O_PV + NT, FLOATS = O_DQK + BC;
   static constexpr size_t BYTES = (size_t)FLOATS * 4;
   static_assert(BYTES <= 160 * 1024, "LDS budget exceeded");
   static_assert(DV % KC == 0 && DK % 32 == 0 && NT % DK == 0, "output pass tiling");
@@ -795,6 +929,17 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
       sDYT[i * LA + r] = y;
     }
   }
+  // a strong chunk (the front pass's test on the same values) forms its
+  // decay-weighted products exactly, with G in E''s place
+  bool strong_t = false;
+#pragma unroll
+  for (int u = 0; u < NEK; ++u) {
+    const int e = tid + NT * u, i4 = e % (DK / 4);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      strong_t = strong_t || fabsf(pG[u][c] - sm[C::O_G31 + 4 * i4 + c]) > BWD_SLIM;
+  }
+  const bool strong = __syncthreads_or(strong_t) != 0;
   // E = gamma b k and E' = e1 b k (the forms of the front pass, same order
   // of operations), e1 = exp(G - G_31)
   float* sEP = sm + C::O_EP;
@@ -806,7 +951,7 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
     for (int c = 0; c < 4; ++c) {
       const float G = pG[u][c], gam = expf(G), e1 = expf(G - sm[C::O_G31 + 4 * i4 + c]);
       eb[c] = gam * pB[u][c] * pK[u][c];
-      ep[c] = e1 * pB[u][c] * pK[u][c];
+      ep[c] = strong ? G : e1 * pB[u][c] * pK[u][c];
     }
     *reinterpret_cast<f32x4*>(sEB + o) = eb;
     *reinterpret_cast<f32x4*>(sEP + o) = ep;
@@ -843,9 +988,12 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = 16 * tm + 4 * g + q, c = 16 * tn + m;
-      const float v = (tn <= tm && c <= r) ? aAQ[u][q] : 0.f;
+      // strictly lower: the diagonal of dA_qk is kept apart (sDQK), so that
+      // its two equal and opposite terms in dg never meet in a sum
+      const float v = (tn <= tm && c < r) ? aAQ[u][q] : 0.f;
       sAQ[r * LA + c] = v;
       sAQT[c * LA + r] = v;
+      if (c == r) sm[C::O_DQK + r] = aAQ[u][q];
     }
   }
   // Q' = e1 q and K' = e2 k, e2 = exp(G_31 - G)
@@ -856,8 +1004,8 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float G = pG[u][c], G31 = sm[C::O_G31 + 4 * i4 + c];
-      qp[c] = expf(G - G31) * pQ[u][c];
-      kp[c] = expf(G31 - G) * pK[u][c];
+      qp[c] = strong ? pQ[u][c] : expf(G - G31) * pQ[u][c];
+      kp[c] = strong ? pK[u][c] : expf(G31 - G) * pK[u][c];
     }
     *reinterpret_cast<f32x4*>(sQP + s * LKP + 4 * i4) = qp;
     *reinterpret_cast<f32x4*>(sKP + s * LKP + 4 * i4) = kp;
@@ -867,9 +1015,15 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
 #pragma unroll
   for (int u = 0; u < NKT; ++u) {
     const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
-    aP3[u] = mma_lds_f32<BC, false, true>(zero4(), sAQT + 16 * tm * LA + 16 * tm, LA,
-                                          sQP + 16 * tm * LKP + 16 * tn, LKP, BC - 16 * tm);
-    aP4[u] = mma_lds_f32<BC, false, true>(zero4(), sAQ + 16 * tm * LA, LA, sKP + 16 * tn, LKP, 16 * (tm + 1));
+    if (strong) {  // sEP holds G
+      aP3[u] = decay_tri<LA, LKP, false>(sAQT, sQP, sEP, 16 * tm + 4 * g, 16 * tn + m, 16 * tm, BC);
+      aP4[u] = decay_tri<LA, LKP, true>(sAQ, sKP, sEP, 16 * tm + 4 * g, 16 * tn + m, 0, 16 * (tm + 1));
+    } else {
+      aP3[u] = mma_lds_f32<BC, false, true>(zero4(), sAQT + 16 * tm * LA + 16 * tm, LA,
+                                            sQP + 16 * tm * LKP + 16 * tn, LKP, BC - 16 * tm);
+      aP4[u] = mma_lds_f32<BC, false, true>(zero4(), sAQ + 16 * tm * LA, LA, sKP + 16 * tn, LKP,
+                                            16 * (tm + 1));
+    }
   }
   __syncthreads();
 
@@ -933,12 +1087,33 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
     }
   }
   f32x4 aP1[NKT], aP2[NKT];
+  if (strong) {
+    // b k of the tile's own elements into its block behind dT and dT^T
+    float* sBK = sm + C::O_BK;
 #pragma unroll
-  for (int u = 0; u < NKT; ++u) {
-    const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
-    aP1[u] = mma_lds_f32<BC, false, true>(zero4(), sDT + 16 * tm * LA, LA, sKP + 16 * tn, LKP, 16 * (tm + 1));
-    aP2[u] = mma_lds_f32<BC, false, true>(zero4(), sDTT + 16 * tm * LA + 16 * tm, LA,
-                                          sEP + 16 * tm * LKP + 16 * tn, LKP, BC - 16 * tm);
+    for (int u = 0; u < NKT; ++u) {
+      const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK, i = 16 * tn + m;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 16 * tm + 4 * g + q;
+        sBK[r * LKP + i] = r < clen ? fb[u][q] * fk[u][q] : 0.f;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NKT; ++u) {
+      const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
+      aP1[u] = decay_tri<LA, LKP, true>(sDT, sKP, sEP, 16 * tm + 4 * g, 16 * tn + m, 0, 16 * (tm + 1));
+      aP2[u] = decay_tri<LA, LKP, false>(sDTT, sBK, sEP, 16 * tm + 4 * g, 16 * tn + m, 16 * tm, BC);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < NKT; ++u) {
+      const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
+      aP1[u] = mma_lds_f32<BC, false, true>(zero4(), sDT + 16 * tm * LA, LA, sKP + 16 * tn, LKP, 16 * (tm + 1));
+      aP2[u] = mma_lds_f32<BC, false, true>(zero4(), sDTT + 16 * tm * LA + 16 * tm, LA,
+                                            sEP + 16 * tm * LKP + 16 * tn, LKP, BC - 16 * tm);
+    }
   }
   __syncthreads();
 
@@ -956,27 +1131,35 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
       const bool in = r < clen;
       const float qv = in ? fq[u][q] : 0.f, kv = in ? fk[u][q] : 0.f, bv = in ? fb[u][q] : 0.f;
       const float G = fG[u][q], gam = expf(G);
-      const float e1 = expf(G - sG31[i]), e2 = expf(sG31[i] - G), ktail = expf(sGCL[i] - G);
-      const float dq = aQ[u][q] * gam + aP4[u][q] * e1;
-      const float dkbar = (aP2[u][q] + aP3[u][q]) * e2;   // dK_bar / gamma
+      // a strong chunk's products carry the whole decay already
+      const float e1 = strong ? 1.f : expf(G - sG31[i]), e2 = strong ? 1.f : expf(sG31[i] - G);
+      const float ktail = expf(sGCL[i] - G);
+      // off the diagonal of dA_qk, then its diagonal entry (decay 1)
+      const float dqo = aQ[u][q] * gam + aP4[u][q] * e1;
+      const float dkbo = (aP2[u][q] + aP3[u][q]) * e2;    // dK_bar / gamma
+      const float dd = sm[C::O_DQK + r];
       const float deg = aX[u][q] * gam + aP1[u][q] * e1;  // dE * gamma
       const float dkt = aK[u][q];
       const float db = deg * kv;
-      sU[r * LKP + i] = dq * qv - dkbar * kv + db * bv - dkt * (ktail * kv);
+      // the decay gradient of row r's own factors (the diagonal of A_qk has none)
+      sU[r * LKP + i] = dqo * qv - dkbo * kv + db * bv;
       sV2[r * LKP + i] = dkt * (ktail * kv);  // dK_tail * K_tail
       if (in) {
         const size_t x = (size_t)(row0 + r) * kr + (size_t)h * DK + i;
-        a.dq[x] = dq;
-        a.dk[x] = dkbar + deg * bv + dkt * ktail;
+        a.dq[x] = dqo + dd * kv;
+        a.dk[x] = dkbo + dd * qv + deg * bv + dkt * ktail;
         a.db[x] = db;
       }
     }
   }
   __syncthreads();
-  // dg_r = gamma_C * rowsum(dS' * S) + sum over all rows of dK_tail * K_tail
-  //        + sum over rows r' >= r of the rest (the decay of row r enters every
-  //        later cumulative sum of the chunk, and gamma_C is the last one).
-  // Thread (row block rb, channel i): sums of its rows first, then its scan.
+  // The decay of row r enters the cumulative sums of rows r' >= r, gamma_C
+  // (the last one) among them, and K_tail of row r' is gamma_C / gamma_r':
+  //   dg_r = gamma_C * rowsum(dS' * S) + sum over r' < r of dK_tail * K_tail
+  //          + sum over r' >= r of the rest.
+  // Each sum runs over its own rows only, so no term is added and then taken
+  // away again (under strong decay those terms dwarf dg itself).
+  // Thread (row block rb, channel i): sums of its rows first, then its scans.
   constexpr int NRB = NT / DK, RPB = BC / NRB;
   const int i = tid % DK, rb = tid / DK;
   {
@@ -990,24 +1173,29 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
     sPV[rb * DK + i] = sv;
   }
   __syncthreads();
-  float acc = sRS[i] * sGCX[i];
+  float base = sRS[i] * sGCX[i];
 #pragma unroll
-  for (int b = 0; b < NRB; ++b) acc += sPV[b * DK + i];
+  for (int b = 0; b < NRB; ++b) {
+    if (b < rb) base += sPV[b * DK + i];
+    if (b > rb) base += sPU[b * DK + i];
+  }
+  {  // the K_tail prefix of each row, in place
+    float pv = 0.f;
 #pragma unroll
-  for (int b = NRB - 1; b > 0; --b)
-    if (b > rb) acc += sPU[b * DK + i];
+    for (int k = 0; k < RPB; ++k) {
+      const int r = rb * RPB + k;
+      const float x = sV2[r * LKP + i];
+      sV2[r * LKP + i] = pv;
+      pv += x;
+    }
+  }
+  float su = 0.f;
 #pragma unroll
   for (int k = RPB - 1; k >= 0; --k) {
     const int r = rb * RPB + k;
-    acc += sU[r * LKP + i];
-    if (r < clen) a.dg[(size_t)(row0 + r) * kr + (size_t)h * DK + i] = acc;
+    su += sU[r * LKP + i];
+    if (r < clen) a.dg[(size_t)(row0 + r) * kr + (size_t)h * DK + i] = base + sV2[r * LKP + i] + su;
   }
-}
-
-template <typename Kern>
-hipError_t set_lds(Kern k, size_t bytes) {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)bytes);
 }
 
 #define GDR2_CK(x)                       \
@@ -1016,68 +1204,92 @@ hipError_t set_lds(Kern k, size_t bytes) {
     if (e_ != hipSuccess) return e_;     \
   } while (0)
 
+// Raises the dynamic LDS limit of a kernel once per device (race-free flags).
+#define GDR2_LDS(kernel, bytes)                                                    \
+  do {                                                                             \
+    static std::atomic<bool> done_[64];                                            \
+    GDR2_CK(lds_opt_in(reinterpret_cast<const void*>(&kernel), (bytes), done_));   \
+  } while (0)
+
+template <int DK, int DV, bool FWD>
+hipError_t launch_front(const BwdArgs& a, dim3 gi, hipStream_t st) {
+  typedef FrontCfg<DK, DV> FC;
+  if (a.in_bf16) {
+    if (a.la_bf16) {
+      GDR2_LDS((bwd_front_kernel<DK, DV, true, true, FWD>), FC::BYTES);
+      hipLaunchKernelGGL((bwd_front_kernel<DK, DV, true, true, FWD>), gi, dim3(FC::NT), FC::BYTES, st, a);
+    } else {
+      GDR2_LDS((bwd_front_kernel<DK, DV, true, false, FWD>), FC::BYTES);
+      hipLaunchKernelGGL((bwd_front_kernel<DK, DV, true, false, FWD>), gi, dim3(FC::NT), FC::BYTES, st, a);
+    }
+  } else {
+    if (a.la_bf16) {
+      GDR2_LDS((bwd_front_kernel<DK, DV, false, true, FWD>), FC::BYTES);
+      hipLaunchKernelGGL((bwd_front_kernel<DK, DV, false, true, FWD>), gi, dim3(FC::NT), FC::BYTES, st, a);
+    } else {
+      GDR2_LDS((bwd_front_kernel<DK, DV, false, false, FWD>), FC::BYTES);
+      hipLaunchKernelGGL((bwd_front_kernel<DK, DV, false, false, FWD>), gi, dim3(FC::NT), FC::BYTES, st, a);
+    }
+  }
+  return hipGetLastError();
+}
+
+// LDS of the sequential forward pass (FWD adds Q_g and A_qk)
+template <int DK, bool FWD>
+constexpr size_t state_fwd_lds() {
+  constexpr int LK = DK + 4, LC = BC + 4, LV = DVB + 4;
+  return (size_t)(DVB * LK + 2 * BC * LK + DVB * LC + BC * LV + DK + (FWD ? BC * LK + BC * LC : 0)) * 4;
+}
+
 template <int DK, int DV>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   const int items = a.chunks * a.H;
   const dim3 gi(items > 0 ? items : 1);
-  if (items > 0) {  // decay, scaled rows, T, A_qk, A, Y and U
-    typedef FrontCfg<DK, DV> FC;
-    static bool attr[64] = {};
-    int dev = 0;
-    GDR2_CK(hipGetDevice(&dev));
-    if (dev < 0 || dev >= 64 || !attr[dev]) {
-      GDR2_CK(set_lds(&bwd_front_kernel<DK, DV, true, true>, FC::BYTES));
-      GDR2_CK(set_lds(&bwd_front_kernel<DK, DV, true, false>, FC::BYTES));
-      GDR2_CK(set_lds(&bwd_front_kernel<DK, DV, false, true>, FC::BYTES));
-      GDR2_CK(set_lds(&bwd_front_kernel<DK, DV, false, false>, FC::BYTES));
-      if (dev >= 0 && dev < 64) attr[dev] = true;
-    }
-    if (a.in_bf16) {
-      if (a.la_bf16) hipLaunchKernelGGL((bwd_front_kernel<DK, DV, true, true>), gi, dim3(FC::NT), FC::BYTES, st, a);
-      else hipLaunchKernelGGL((bwd_front_kernel<DK, DV, true, false>), gi, dim3(FC::NT), FC::BYTES, st, a);
-    } else {
-      if (a.la_bf16) hipLaunchKernelGGL((bwd_front_kernel<DK, DV, false, true>), gi, dim3(FC::NT), FC::BYTES, st, a);
-      else hipLaunchKernelGGL((bwd_front_kernel<DK, DV, false, false>), gi, dim3(FC::NT), FC::BYTES, st, a);
-    }
-    GDR2_CK(hipGetLastError());
-  }
+  if (items > 0) GDR2_CK((launch_front<DK, DV, false>(a, gi, st)));  // decay, T, A_qk, A, Y and U
   // sequential passes (with no chunks they only pass dS_T through to dS0)
   {
     constexpr int LK = DK + 4, LC = BC + 4;
-    constexpr int LV = DVB + 4;
-    const size_t lf = (size_t)(DVB * LK + 2 * BC * LK + DVB * LC + BC * LV + DK) * 4;
+    constexpr size_t lf = state_fwd_lds<DK, false>();
     const size_t lb = (size_t)(DVB * LK + BC * LC + BC * (DVB + 4) + 3 * BC * LK + DVB * LC + DK) * 4;
-    static bool attr[64] = {};
-    int dev = 0;
-    GDR2_CK(hipGetDevice(&dev));
-    if (dev < 0 || dev >= 64 || !attr[dev]) {
-      GDR2_CK(set_lds(&bwd_state_fwd_kernel<DK, DV>, lf));
-      GDR2_CK(set_lds(&bwd_state_bwd_kernel<DK, DV, true>, lb));
-      GDR2_CK(set_lds(&bwd_state_bwd_kernel<DK, DV, false>, lb));
-      if (dev >= 0 && dev < 64) attr[dev] = true;
-    }
+    GDR2_LDS((bwd_state_fwd_kernel<DK, DV, false>), lf);
     const dim3 gs((unsigned)(((size_t)a.N * a.H + 7) / 8 * 8 * (DV / DVB)));
-    hipLaunchKernelGGL((bwd_state_fwd_kernel<DK, DV>), gs, dim3(SNT), lf, st, a);
+    hipLaunchKernelGGL((bwd_state_fwd_kernel<DK, DV, false>), gs, dim3(SNT), lf, st, a);
     GDR2_CK(hipGetLastError());
-    if (a.in_bf16) hipLaunchKernelGGL((bwd_state_bwd_kernel<DK, DV, true>), gs, dim3(SNT), lb, st, a);
-    else hipLaunchKernelGGL((bwd_state_bwd_kernel<DK, DV, false>), gs, dim3(SNT), lb, st, a);
+    if (a.in_bf16) {
+      GDR2_LDS((bwd_state_bwd_kernel<DK, DV, true>), lb);
+      hipLaunchKernelGGL((bwd_state_bwd_kernel<DK, DV, true>), gs, dim3(SNT), lb, st, a);
+    } else {
+      GDR2_LDS((bwd_state_bwd_kernel<DK, DV, false>), lb);
+      hipLaunchKernelGGL((bwd_state_bwd_kernel<DK, DV, false>), gs, dim3(SNT), lb, st, a);
+    }
     GDR2_CK(hipGetLastError());
   }
   if (items <= 0) return hipSuccess;
   // output paths, WY gradients and the gradients themselves, one workgroup per item
   {
     typedef OutCfg<DK, DV> OC;
-    static bool attr[64] = {};
-    int dev = 0;
-    GDR2_CK(hipGetDevice(&dev));
-    if (dev < 0 || dev >= 64 || !attr[dev]) {
-      GDR2_CK(set_lds(&bwd_out_kernel<DK, DV, true>, OC::BYTES));
-      GDR2_CK(set_lds(&bwd_out_kernel<DK, DV, false>, OC::BYTES));
-      if (dev >= 0 && dev < 64) attr[dev] = true;
+    if (a.in_bf16) {
+      GDR2_LDS((bwd_out_kernel<DK, DV, true>), OC::BYTES);
+      hipLaunchKernelGGL((bwd_out_kernel<DK, DV, true>), gi, dim3(OC::NT), OC::BYTES, st, a);
+    } else {
+      GDR2_LDS((bwd_out_kernel<DK, DV, false>), OC::BYTES);
+      hipLaunchKernelGGL((bwd_out_kernel<DK, DV, false>), gi, dim3(OC::NT), OC::BYTES, st, a);
     }
-    if (a.in_bf16) hipLaunchKernelGGL((bwd_out_kernel<DK, DV, true>), gi, dim3(OC::NT), OC::BYTES, st, a);
-    else hipLaunchKernelGGL((bwd_out_kernel<DK, DV, false>), gi, dim3(OC::NT), OC::BYTES, st, a);
   }
+  return hipGetLastError();
+}
+
+// The fp32 forward: the front pass (decay, T, A_qk, A, Y, U per item) and the
+// sequential pass that forms o and the final state.
+template <int DK, int DV>
+hipError_t launch_fwd32_t(const BwdArgs& a, hipStream_t st) {
+  const int items = a.chunks * a.H;
+  if (items > 0) GDR2_CK((launch_front<DK, DV, true>(a, dim3(items), st)));
+  constexpr size_t lf = state_fwd_lds<DK, true>();
+  static_assert(lf <= 160 * 1024, "LDS budget exceeded");
+  GDR2_LDS((bwd_state_fwd_kernel<DK, DV, true>), lf);
+  const dim3 gs((unsigned)(((size_t)a.N * a.H + 7) / 8 * 8 * (DV / DVB)));
+  hipLaunchKernelGGL((bwd_state_fwd_kernel<DK, DV, true>), gs, dim3(SNT), lf, st, a);
   return hipGetLastError();
 }
 
@@ -1091,6 +1303,16 @@ size_t bwd_item_bytes(int dk, int dv) {
   GDR2_BI(128, 32) GDR2_BI(128, 64) GDR2_BI(128, 128)
 #undef GDR2_BI
   return 0;
+}
+
+hipError_t launch_fwd32(const BwdArgs& a, int dk, int dv, hipStream_t st) {
+#define GDR2_FW(DK, DV) \
+  if (dk == DK && dv == DV) return launch_fwd32_t<DK, DV>(a, st);
+  GDR2_FW(32, 32) GDR2_FW(32, 64) GDR2_FW(32, 128)
+  GDR2_FW(64, 32) GDR2_FW(64, 64) GDR2_FW(64, 128)
+  GDR2_FW(128, 32) GDR2_FW(128, 64) GDR2_FW(128, 128)
+#undef GDR2_FW
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int dk, int dv, hipStream_t st) {

@@ -6,7 +6,25 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace gdr2 {
+
+// Raises `kernel`'s dynamic LDS limit to `bytes` on the current device the
+// first time it is launched there.  `done` is that kernel's own per-device
+// flag array (64 devices; others set the attribute on every call).  The flags
+// are atomic: first calls from several threads may each set the attribute,
+// which is idempotent, but never race on a flag.
+inline hipError_t lds_opt_in(const void* kernel, size_t bytes, std::atomic<bool>* done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool slot = dev >= 0 && dev < 64;
+  if (slot && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess && slot) done[dev].store(true, std::memory_order_release);
+  return e;
+}
 
 struct DecodeArgs {
   const void *q, *k, *v, *la, *b, *w;
@@ -34,17 +52,6 @@ struct NormGateArgs {
   float eps;
   float inv_group;  // set by launch_norm_gate
   int lanes;        // set by launch_norm_gate
-};
-
-struct ChunkArgs {
-  const void *q, *k, *v, *la, *b, *w;
-  const float* S0;
-  void* o;
-  float* ST;
-  const int32_t* cu;      // device [N+1] or nullptr
-  const int32_t* order;   // device [N] schedule (longest first) or nullptr
-  int N, T, H, DV;
-  int la_bf16;
 };
 
 // ---- two-pass chunkwise forward (16-bit inputs) ------------------------------------
@@ -85,6 +92,7 @@ enum { PRO_QK_L2NORM = 1, PRO_DECAY = 2, PRO_GATES = 4 };
 struct IntraArgs {
   const void *q, *k, *v, *la, *b, *w;
   char* rec;
+  int* sflag;             // per record: 1 when its chunk's decay needs the exact path
   const int32_t* tab;     // packed sequences: per chunk (row, length); else nullptr
   const int32_t* total;   // packed sequences: device total chunk count; else nullptr
   int nc;                 // chunks per sequence (equal-length sequences)
@@ -104,7 +112,8 @@ struct IntraArgs {
 struct StateArgs {
   const char* rec;
   const float* S0;
-  void* o;
+  void* o;                // bf16, or fp32 when o_f32
+  int o_f32;
   float* ST;
   const int32_t* cu;      // device [N+1] or nullptr
   const int32_t* order;   // longest-first schedule or nullptr
@@ -135,6 +144,7 @@ struct BwdArgs {
   const void *q, *k, *v, *la, *b, *w, *dO;
   const float *S0, *dST;
   float *dq, *dk, *dv, *dg, *db, *dw, *dS0;
+  float *o, *ST;          // the fp32 forward's outputs (launch_fwd32); unused by the backward
   float* ws;
   const int32_t* tab;     // packed sequences: per chunk (row, length); else nullptr
   const int32_t* cbase;   // packed sequences: first chunk per sequence, [N+1]
@@ -144,6 +154,10 @@ struct BwdArgs {
 };
 size_t bwd_item_bytes(int dk, int dv);
 hipError_t launch_bwd(const BwdArgs& a, int dk, int dv, hipStream_t stream);
+// The forward for fp32 inputs, on the backward's fp32 front pass and the
+// forward variant of its sequential state pass: q..w, S0, o (fp32), ST, the
+// packed-sequence tables and the workspace as for the backward.
+hipError_t launch_fwd32(const BwdArgs& a, int dk, int dv, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs& a, int dk, int dv, bool bf16, hipStream_t stream);
 
@@ -153,9 +167,6 @@ hipError_t launch_norm_gate(NormGateArgs a, bool bf16, hipStream_t stream);
 int norm_gate_lanes(int group);
 long long norm_gate_blocks(long long groups, int group);
 
-// Returns hipErrorInvalidValue when no kernel variant exists for the sizes.
-hipError_t launch_chunk(const ChunkArgs& a, int dk, int dv, bool bf16, hipStream_t stream);
-bool chunk_supported(int dk, int dv, bool bf16);
 
 // Schedule: a permutation of the N packed sequences, longest first, written
 // into `order` (device int32 [N]) from cu_seqlens.  `scratch` holds N int32.

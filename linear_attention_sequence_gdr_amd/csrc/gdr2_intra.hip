@@ -63,9 +63,18 @@ struct IntraCfg {
   // integer exponent, float2 [6][DK]
   static constexpr size_t O_DSC = O_Z + (size_t)CH * LDZ * 2;
   static constexpr size_t O_NRM = O_DSC + (size_t)6 * DK * 8;      // fp32 [64][2] q, k row sums
-  static constexpr size_t O_FLAG = O_NRM + (size_t)CH * 2 * 4;     // int: an item uses block centres
+  static constexpr size_t O_SCL = O_NRM + (size_t)CH * 2 * 4;      // fp32 [64][2] q, k row scales
+  static constexpr size_t O_FLAG = O_SCL + (size_t)CH * 2 * 4;     // ints: block centres, strong item
   static constexpr size_t BYTES = O_FLAG + 16;
   static_assert(BYTES <= 160 * 1024, "LDS budget exceeded");
+  // region X of a strong item in phase P: the uncentred G (fp32 [64][LDG]) and
+  // the raw k, q (bf16) and activated b (fp16) rows, [64][LDK] each
+  static constexpr int LDG = DK + 4;
+  static constexpr size_t O_SG = 0;
+  static constexpr size_t O_SK = O_SG + (size_t)CH * LDG * 4;
+  static constexpr size_t O_SQ = O_SK + SZK;
+  static constexpr size_t O_SB = O_SQ + SZK;
+  static_assert(O_SB + SZK <= X, "strong-item rows exceed region X");
   // key-side mapping: thread = (column group cg of EPC channels, row group rg
   // of RPT consecutive rows); the RG row groups of a column group are
   // consecutive lanes of one wavefront
@@ -89,6 +98,54 @@ __device__ __forceinline__ f16x4 lds_tr16(const _Float16* p) {
   return __builtin_bit_cast(f16x4, v);
 }
 
+// Exact chunk-matrix tile of a strong item (decay that centred factors cannot
+// carry): lane (m, g4) gets, for q < 4, row r = r0 + m and column s = s0 + q
+// (s0 = 16 b + 4 g4), in the layout of the MFMA path,
+//   aq[q] = nq_r nk_s sum_c q[r][c] k[s][c] 2^(G[r][c] - G[s][c])        (A_qk)
+//   at[q] = nk_r nk_s sum_c b[r][c] k[r][c] k[s][c] 2^(G[r][c] - G[s][c]) (T)
+// from the rows staged in region X (G in log2 units) and the per-row L2
+// scales (nq, nk) in scl.  Entries above the diagonal are formed too and
+// masked by the caller.
+template <int DK, int LDG, int LDK>
+__device__ __forceinline__ void strong_tile(const float* SG, const __bf16* SK, const __bf16* SQ,
+                                            const _Float16* SB, const float* scl, int r, int s0,
+                                            f32x4& aq, f32x4& at) {
+  typedef __attribute__((ext_vector_type(4))) __bf16 b4;
+  typedef __attribute__((ext_vector_type(4))) _Float16 h4;
+  aq = zero4();
+  at = zero4();
+#pragma unroll 1
+  for (int c = 0; c < DK; c += 4) {
+    const float4 gr = *reinterpret_cast<const float4*>(SG + r * LDG + c);
+    const b4 kr = *reinterpret_cast<const b4*>(SK + r * LDK + c);
+    const b4 qr = *reinterpret_cast<const b4*>(SQ + r * LDK + c);
+    const h4 br = *reinterpret_cast<const h4*>(SB + r * LDK + c);
+    const float bk[4] = {(float)br[0] * (float)kr[0], (float)br[1] * (float)kr[1],
+                         (float)br[2] * (float)kr[2], (float)br[3] * (float)kr[3]};
+    const float qq[4] = {(float)qr[0], (float)qr[1], (float)qr[2], (float)qr[3]};
+    const float g[4] = {gr.x, gr.y, gr.z, gr.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 gs = *reinterpret_cast<const float4*>(SG + (s0 + q) * LDG + c);
+      const b4 ks = *reinterpret_cast<const b4*>(SK + (s0 + q) * LDK + c);
+      const float gsv[4] = {gs.x, gs.y, gs.z, gs.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x = (float)ks[j] * exp2_fast(g[j] - gsv[j]);
+        aq[q] = fmaf(qq[j], x, aq[q]);
+        at[q] = fmaf(bk[j], x, at[q]);
+      }
+    }
+  }
+  const float2 sr = *reinterpret_cast<const float2*>(scl + 2 * r);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float nks = scl[2 * (s0 + q) + 1];
+    aq[q] *= sr.x * nks;
+    at[q] *= sr.y * nks;
+  }
+}
+
 }  // namespace
 
 // fp32 activations of the gate prologue.  softplus(x) = max(x, 0) +
@@ -103,7 +160,133 @@ __device__ __forceinline__ float sigmoid_f(float x) {
   return __builtin_amdgcn_rcpf(1.f + __expf(-x));
 }
 
+// Stages a strong item's rows in region X for the exact products of phase P
+// (strong_tile): the uncentred cumulative log2-decay G (fp32), the raw k and
+// q rows (bf16) and the erase gate b (fp16, activated under the prologue),
+// read again from the inputs of token rows [row0, row0 + clen) of value head
+// h's key head; rows past the end get zero q, k and log-decay.  Thread tid
+// owns channel tid % DK and a group of consecutive rows; the group totals of
+// the decay scan meet in the diagonal-T buffer, free until the tiles.
 template <int DK, int DV, bool LA16, bool PRO>
+__device__ __forceinline__ void strong_stage(const IntraArgs& p, long long row0, int clen, int h) {
+  typedef IntraCfg<DK, DV> Cfg;
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int NGR = NT / DK, RPG = CH / NGR, LDK = Cfg::LDK, LDG = Cfg::LDG;
+  float* SG = reinterpret_cast<float*>(smem + Cfg::O_SG);
+  __bf16* SK = reinterpret_cast<__bf16*>(smem + Cfg::O_SK);
+  __bf16* SQ = reinterpret_cast<__bf16*>(smem + Cfg::O_SQ);
+  _Float16* SB = reinterpret_cast<_Float16*>(smem + Cfg::O_SB);
+  float* part = reinterpret_cast<float*>(smem + Cfg::O_TD);
+  const int tid = threadIdx.x, c = tid % DK, gr = tid / DK;
+  const int hk = PRO ? h / p.grp : h;
+  const size_t krow = (size_t)(PRO ? p.Hk : p.H) * DK;
+  float ea = 0.f, dl = 0.f;
+  if constexpr (PRO) {
+    if (p.pro & PRO_DECAY) {
+      ea = __expf(p.da[(size_t)hk * DK + c]);
+      dl = p.db[(size_t)hk * DK + c];
+    }
+  }
+  float acc = 0.f;
+#pragma unroll 2
+  for (int j = 0; j < RPG; ++j) {
+    const int r = gr * RPG + j;
+    float gv = 0.f, kv = 0.f, qv = 0.f, bv = 0.f;
+    if (r < clen) {
+      const size_t x = (size_t)(row0 + r) * krow + (size_t)hk * DK + c;
+      gv = load1<LA16>(p.la, x);
+      kv = load1<true>(p.k, x);
+      qv = load1<true>(p.q, x);
+      bv = load1<true>(p.b, x);
+      if constexpr (PRO) {
+        if (p.pro & PRO_DECAY) gv = -ea * softplus_f(gv + dl);
+        if (p.pro & PRO_GATES) bv = p.b_scale * sigmoid_f(bv);
+      }
+    }
+    acc += gv * LOG2E;
+    SG[r * LDG + c] = acc;  // the group's own partial sum; offset below
+    SK[r * LDK + c] = (__bf16)kv;
+    SQ[r * LDK + c] = (__bf16)qv;
+    SB[r * LDK + c] = (_Float16)bv;
+  }
+  part[gr * DK + c] = acc;
+  // Z = w * v rows (the write gate activated under the prologue)
+  _Float16* Zr = reinterpret_cast<_Float16*>(smem + Cfg::O_Z);
+  const size_t vrow = (size_t)p.H * DV;
+  for (int e = tid; e < CH * DV; e += NT) {
+    const int r = e / DV, j = e - r * DV;
+    float z = 0.f;
+    if (r < clen) {
+      const size_t x = (size_t)(row0 + r) * vrow + (size_t)h * DV + j;
+      float wv = load1<true>(p.w, x);
+      if constexpr (PRO) {
+        if (p.pro & PRO_GATES) wv = sigmoid_f(wv);
+      }
+      z = load1<true>(p.v, x) * wv;
+    }
+    Zr[r * Cfg::LDZ + j] = (_Float16)z;
+  }
+  __syncthreads();
+  float off = 0.f;
+#pragma unroll
+  for (int q = 0; q < NGR - 1; ++q)
+    if (q < gr) off += part[q * DK + c];
+#pragma unroll 4
+  for (int j = 0; j < RPG; ++j) SG[(gr * RPG + j) * LDG + c] += off;
+  // per-row scales of the q, k L2 norm (1 without it; 0 past the end)
+  float* scl = reinterpret_cast<float*>(smem + Cfg::O_SCL);
+  if (tid < 2 * CH) {
+    const int r = tid >> 1, which = tid & 1;
+    float sc = 1.f;
+    if constexpr (PRO) {
+      if (p.pro & PRO_QK_L2NORM) {
+        const __bf16* row = (which ? SK : SQ) + r * LDK;
+        float ss = 0.f;
+        for (int cc = 0; cc < DK; ++cc) ss = fmaf((float)row[cc], (float)row[cc], ss);
+        sc = r < clen ? rsqrtf(ss + p.qk_eps) : 0.f;
+      }
+    }
+    scl[2 * r + which] = sc;
+  }
+}
+
+// Stores one lower tile (a, b) of phase P, lane layout of the MFMA products
+// (acc: A_qk[16a + m][16b + 4 g4 + q], acct: T likewise): the diagonal blocks
+// of T transposed in fp32 (Tdt), -T of the off-diagonal blocks in fp16 (Tn),
+// and A_qk as record fragments.
+template <int DK, int DV>
+__device__ __forceinline__ void tile_store(int a, int b, f32x4 acc, f32x4 acct, char* rec) {
+  typedef IntraCfg<DK, DV> Cfg;
+  typedef Rec<DK, DV> R;
+  typedef _Float16 ST;
+  typedef f16x4 SV4;
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* Tdt = reinterpret_cast<float*>(smem + Cfg::O_TD);
+  ST* Tn = reinterpret_cast<ST*>(smem + Cfg::O_TN);
+  const int lane = lane_id(), m = lane & 15, g4 = lane >> 4;
+  if (a == b) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = (4 * g4 + q <= m) ? acc[q] : 0.f;
+    // diagonal blocks of T transposed, fp32: Tdt[a][s][r] = T[r][s], s < r
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Tdt[(a * 16 + 4 * g4 + q) * 16 + m] = (4 * g4 + q < m) ? acct[q] : 0.f;
+  } else {
+    *reinterpret_cast<SV4*>(Tn + (16 * a + m) * Cfg::LDC + 16 * b + 4 * g4) = neg_cvt4<SV4>(acct);
+  }
+  // A_qk fragment (a, p = b/2) half b&1, lane (m, g4); the upper halves of
+  // fragments (0, 0) and (2, 1) are zero
+  const int f = a < 2 ? a : 2 * a - 2 + (b >> 1);
+  char* dst = rec + R::AQK + ((size_t)f * 64 + lane) * 16;
+  *reinterpret_cast<SV4*>(dst + 8 * (b & 1)) = cvt4<SV4>(acc);
+  if (a == b && (a & 1) == 0) *reinterpret_cast<SV4*>(dst + 8) = SV4{(ST)0.f, (ST)0.f, (ST)0.f, (ST)0.f};
+}
+
+// MODE 0: every item, then again the strong ones this workgroup met; MODE 1:
+// every item, strong ones only flagged; MODE 2: the flagged items only (the
+// second launch after MODE 1).  Variants whose main loop is near the register
+// limit take MODE 1 and 2, so that the exact path's registers never weigh on
+// their main loop.
+template <int DK, int DV, bool LA16, bool PRO, int MODE>
 __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
   typedef IntraCfg<DK, DV> Cfg;
   typedef Rec<DK, DV> R;
@@ -130,6 +313,8 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
   float2* dsc = reinterpret_cast<float2*>(smem + Cfg::O_DSC);
   float* nrm = reinterpret_cast<float*>(smem + Cfg::O_NRM);
   int* blocked = reinterpret_cast<int*>(smem + Cfg::O_FLAG);
+  int* strongf = blocked + 1;
+  float* scl = reinterpret_cast<float*>(smem + Cfg::O_SCL);
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int m = lane & 15, g4 = lane >> 4;
@@ -139,7 +324,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
 
   // the strictly upper blocks of A stay zero; the products run over them
   for (int e = tid; e < CH * LDC; e += NT) Am[e] = (ST)0.f;
-  if (tid == 0) *blocked = 0;
+  if (tid == 0) *blocked = *strongf = 0;
   for (int e = tid; e < 6 * DK; e += NT) dsc[e] = make_float2(1.f, __int_as_float(0));
 
   // item -> first token row, valid rows, head.  The values are uniform across
@@ -233,6 +418,116 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
     }
   };
 
+  // ---- phases S and Y, shared by the main loop and the strong items' loop -----
+  // S(i): wave a < 4 inverts I + T_aa (diagonal blocks of A)
+  auto inv_diag = [&]() __attribute__((always_inline)) {
+      if (wv < 4) {
+      // wave a inverts I + T_aa: lane 4*cc + part holds rows 4*part .. 4*part+3
+      // of column cc and runs a right-looking fp32 forward substitution over
+      // the columns s of T_aa; row s of column cc is broadcast in its quad
+      const int a = wv, cc = lane >> 2, part = lane & 3;
+      const float4* Tc = reinterpret_cast<const float4*>(Tdt + a * 256);
+      // all 15 column pieces first, so the substitution chain waits on no LDS read
+      float4 tcol[15];
+#pragma unroll
+      for (int s = 0; s < 15; ++s) tcol[s] = Tc[s * 4 + part];
+      float xs[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xs[j] = (4 * part + j == cc) ? 1.f : 0.f;
+#pragma unroll
+      for (int s = 0; s < 15; ++s) {
+        const float4 col = tcol[s];
+        const float xv = quad_bcast(xs[s & 3], s >> 2);
+        // T[r][s] is zero for r <= s, so finished rows are left unchanged
+        xs[0] = fmaf(-col.x, xv, xs[0]);
+        xs[1] = fmaf(-col.y, xv, xs[1]);
+        xs[2] = fmaf(-col.z, xv, xs[2]);
+        xs[3] = fmaf(-col.w, xv, xs[3]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Am[(16 * a + 4 * part + j) * LDC + 16 * a + cc] = (ST)xs[j];
+    }
+  };
+  // S(ii): the off-diagonal blocks of A; the Q_g and K_tail fragments into the record
+  auto phase_s2 = [&](char* rec, bool copy_fragments) __attribute__((always_inline)) {
+    if (wv == 3) wy_column<0, ST, SV4, LDC>(Tn, Am);
+    else if (wv == 2) wy_column<1, ST, SV4, LDC>(Tn, Am);
+    else if (wv == 1) wy_column<2, ST, SV4, LDC>(Tn, Am);
+    else if (copy_fragments) {
+      // waves 0, 4..7 copy the Q_g and K_tail fragments, complete since phase
+      // S(i), while the others solve (16-byte pieces, 1 KiB per instruction)
+      constexpr int NQG = 4 * R::NKB, NF = NQG + 2 * R::NIB;
+      const int w5 = wv == 0 ? 0 : wv - 3;  // 0..4
+      for (int f = w5; f < NF; f += 5) {
+        const ST* src;
+        char* dst;
+        if (f < NQG) {
+          const int a = f / R::NKB, kb = f % R::NKB;
+          src = Qg + (16 * a + m) * LDK + 32 * kb + 4 * g4;
+          dst = rec + R::QG + (size_t)f * R::FRAG;
+        } else {
+          const int ff = f - NQG, ib = ff >> 1, pp = ff & 1;
+          src = KtT + (16 * ib + m) * LDC + 32 * pp + 4 * g4;
+          dst = rec + R::KT + (size_t)ff * R::FRAG;
+        }
+        const SV4 lo = *reinterpret_cast<const SV4*>(src);
+        const SV4 hi = *reinterpret_cast<const SV4*>(src + 16);
+        *reinterpret_cast<f16x8*>(dst + lane * 16) =
+            f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    }
+  };
+  // Y: -Y and U into the record
+  auto phase_y = [&](char* rec) __attribute__((always_inline)) {
+    {
+      // -Y fragments (a, kb): wave -> kb = wv / 2 and row blocks {wv & 1, 3 - (wv & 1)}
+      const int kb = wv >> 1;
+      if (kb < R::NKB) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int a = s == 0 ? (wv & 1) : 3 - (wv & 1);
+          f32x4 y0, y1;
+          if (a < 2) {
+            y0 = mma_lds<ST, 32>(zero4(), EhT + 32 * kb * LDC, LDC, Am + 16 * a * LDC, LDC);
+            y1 = mma_lds<ST, 32>(zero4(), EhT + (32 * kb + 16) * LDC, LDC, Am + 16 * a * LDC, LDC);
+          } else {
+            y0 = mma_lds<ST, 64>(zero4(), EhT + 32 * kb * LDC, LDC, Am + 16 * a * LDC, LDC);
+            y1 = mma_lds<ST, 64>(zero4(), EhT + (32 * kb + 16) * LDC, LDC, Am + 16 * a * LDC, LDC);
+          }
+          // lane holds Y[16a + m][32kb + 4*g4 + q] (y0) and Y[16a + m][32kb + 16 + 4*g4 + q] (y1)
+          *reinterpret_cast<f16x8*>(rec + R::YN + ((size_t)(a * R::NKB + kb) * 64 + lane) * 16) =
+              f16x8{(ST)-y0[0], (ST)-y0[1], (ST)-y0[2], (ST)-y0[3],
+                    (ST)-y1[0], (ST)-y1[1], (ST)-y1[2], (ST)-y1[3]};
+        }
+      }
+      // U tiles (jt, a): U = A Z over tokens.  K position 8*g4 + j of a 32-token
+      // step p is token 32p + 4*g4 + j (j < 4) or 32p + 16 + 4*g4 + j - 4; the
+      // A operand reads those columns of row 16a + m of A, and the Z operand
+      // comes from row-major Z through the LDS transpose read (lane s of a
+      // 16-lane group points at 4 channels of one token row; lane m then holds
+      // channel m of 4 consecutive token rows)
+      for (int t = wv; t < 4 * R::NJT; t += NW) {
+        const int a = t / R::NJT, jt = t % R::NJT;
+        f32x4 u = zero4();
+        const int s = m;  // source lane inside the 16-lane group
+        for (int pp = 0; pp <= (a >> 1); ++pp) {
+          const ST* arow = Am + (16 * a + m) * LDC + 32 * pp + 4 * g4;
+          const f16x4 a0 = *reinterpret_cast<const f16x4*>(arow);
+          const f16x4 a1 = *reinterpret_cast<const f16x4*>(arow + 16);
+          const ST* z0 = Zr + (32 * pp + 4 * g4 + (s >> 2)) * Cfg::LDZ + 16 * jt + 4 * (s & 3);
+          const f16x4 b0 = lds_tr16(z0);
+          const f16x4 b1 = lds_tr16(z0 + 16 * Cfg::LDZ);
+          u = mma32(f16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]},
+                    f16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]}, u);
+        }
+        // lane holds U[16a + 4*g4 + q][16jt + m]
+        *reinterpret_cast<SV4*>(rec + R::U + ((size_t)(jt * 4 + a) * 64 + lane) * 8) = cvt4<SV4>(u);
+      }
+    }
+  };
+
+  int nstrong = 0;  // strong items this workgroup met (the same in every thread)
+  if constexpr (MODE != 2) {
   long long row0;
   int clen, h;
   locate(order(blockIdx.x), row0, clen, h);
@@ -245,7 +540,8 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
     long long nrow0 = 0;
     int nclen = 0, nh = 0;
     if (itn < items) locate(order(itn), nrow0, nclen, nh);
-    char* rec = p.rec + (size_t)order(it) * R::BYTES;
+    const int ri = order(it);  // record index
+    char* rec = p.rec + (size_t)ri * R::BYTES;
 
     // ================= phase L: decay scan and operand tiles ====================
     SV4 eh[RPT], qg[RPT], kt[RPT];
@@ -429,6 +725,19 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
         for (int pr = 0; pr < RPT; ++pr) G[pr][i] -= gm;  // centred
       }
       if (blocked_t) *blocked = 1;  // every writer stores the same value
+      // A strong item has some centred factor beyond 2^SLIM: decay that even
+      // the per-block centres cannot carry in 16-bit operands.  This pass
+      // still runs it (with out-of-range factors and a record that means
+      // nothing); the item is flagged, and the workgroup forms its record
+      // again after its last item, from the inputs, with the exact decay.
+      constexpr float SLIM = 112.f;
+      bool strong_t = false;
+#pragma unroll
+      for (int pr = 0; pr < RPT; ++pr)
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) strong_t = strong_t || fabsf(G[pr][i]) > SLIM;
+      if (strong_t) *strongf = 1;  // every writer stores the same value
+      {
 #pragma unroll
       for (int pr = 0; pr < RPT; ++pr) {
         const int r = r0 + pr;
@@ -454,6 +763,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
         st4<KT>(Kl + r * LDK + EPC * cg, kl);
         st4<KT>(Qh + r * LDK + EPC * cg, qh);
         st4<KT>(Ql + r * LDK + EPC * cg, ql);
+      }
       }
       if (itn < items) fetch(nrow0, nclen, nh, 1);
       // Z row major: each unit is VE consecutive channels of one row
@@ -516,34 +826,20 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
             acc = mma32(kl, qh, acc);
           }
         }
-        // lanes hold A_qk[16a + m][16b + 4*g4 + q] and T[16a + m][16b + 4*g4 + q]
-        if (a == b) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[q] = (4 * g4 + q <= m) ? acc[q] : 0.f;
-          // diagonal blocks of T transposed, fp32: Tdt[a][s][r] = T[r][s], s < r
-#pragma unroll
-          for (int q = 0; q < 4; ++q) Tdt[(a * 16 + 4 * g4 + q) * 16 + m] = (4 * g4 + q < m) ? acct[q] : 0.f;
-        } else {
-          *reinterpret_cast<SV4*>(Tn + (16 * a + m) * LDC + 16 * b + 4 * g4) = neg_cvt4<SV4>(acct);
-        }
-        // A_qk fragment (a, p = b/2) half b&1, lane (m, g4); the upper halves of
-        // fragments (0, 0) and (2, 1) are zero
-        {
-          const int f = a < 2 ? a : 2 * a - 2 + (b >> 1);
-          char* dst = rec + R::AQK + ((size_t)f * 64 + lane) * 16;
-          *reinterpret_cast<SV4*>(dst + 8 * (b & 1)) = cvt4<SV4>(acc);
-          if (a == b && (a & 1) == 0) *reinterpret_cast<SV4*>(dst + 8) = SV4{(ST)0.f, (ST)0.f, (ST)0.f, (ST)0.f};
-        }
+        tile_store<DK, DV>(a, b, acc, acct, rec);
       }
     }
     __syncthreads();
 
     // ==== phase S(i): diagonal inverses; E^T, K_tail^T, Q_g into region X ==========
     if (itn < items) fetch(nrow0, nclen, nh, 3);
-    if (*blocked) {  // uniform; phase P has read the flag and the table
-      __syncthreads();  // every thread has read the flag before it is cleared
+    const bool strong = *strongf != 0;  // uniform
+    if (tid == 0) p.sflag[ri] = strong ? 1 : 0;
+    nstrong += strong ? 1 : 0;
+    if (*blocked || strong) {  // uniform; phase P has read the flags and the table
+      __syncthreads();  // every thread has read the flags before they are cleared
       for (int e = tid; e < 6 * DK; e += NT) dsc[e] = make_float2(1.f, __int_as_float(0));
-      if (tid == 0) *blocked = 0;
+      if (tid == 0) *blocked = *strongf = 0;
     }
     {
 #pragma unroll
@@ -559,115 +855,120 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
       }
 #pragma unroll
       for (int pr = 0; pr < RPT; ++pr) *reinterpret_cast<SV4*>(Qg + (r0 + pr) * LDK + EPC * cg) = qg[pr];
-      if (wv < 4) {
-        // wave a inverts I + T_aa: lane 4*cc + part holds rows 4*part .. 4*part+3
-        // of column cc and runs a right-looking fp32 forward substitution over
-        // the columns s of T_aa; row s of column cc is broadcast in its quad
-        const int a = wv, cc = lane >> 2, part = lane & 3;
-        const float4* Tc = reinterpret_cast<const float4*>(Tdt + a * 256);
-        // all 15 column pieces first, so the substitution chain waits on no LDS read
-        float4 tcol[15];
-#pragma unroll
-        for (int s = 0; s < 15; ++s) tcol[s] = Tc[s * 4 + part];
-        float xs[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xs[j] = (4 * part + j == cc) ? 1.f : 0.f;
-#pragma unroll
-        for (int s = 0; s < 15; ++s) {
-          const float4 col = tcol[s];
-          const float xv = quad_bcast(xs[s & 3], s >> 2);
-          // T[r][s] is zero for r <= s, so finished rows are left unchanged
-          xs[0] = fmaf(-col.x, xv, xs[0]);
-          xs[1] = fmaf(-col.y, xv, xs[1]);
-          xs[2] = fmaf(-col.z, xv, xs[2]);
-          xs[3] = fmaf(-col.w, xv, xs[3]);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Am[(16 * a + 4 * part + j) * LDC + 16 * a + cc] = (ST)xs[j];
-      }
+      inv_diag();
     }
     __syncthreads();
 
     // ==== phase S(ii): off-diagonal blocks of A ===================================
     if (itn < items) fetch(nrow0, nclen, nh, 4);
-    if (wv == 3) wy_column<0, ST, SV4, LDC>(Tn, Am);
-    else if (wv == 2) wy_column<1, ST, SV4, LDC>(Tn, Am);
-    else if (wv == 1) wy_column<2, ST, SV4, LDC>(Tn, Am);
-    else {
-      // waves 0, 4..7 copy the Q_g and K_tail fragments, complete since phase
-      // S(i), while the others solve (16-byte pieces, 1 KiB per instruction)
-      constexpr int NQG = 4 * R::NKB, NF = NQG + 2 * R::NIB;
-      const int w5 = wv == 0 ? 0 : wv - 3;  // 0..4
-      for (int f = w5; f < NF; f += 5) {
-        const ST* src;
-        char* dst;
-        if (f < NQG) {
-          const int a = f / R::NKB, kb = f % R::NKB;
-          src = Qg + (16 * a + m) * LDK + 32 * kb + 4 * g4;
-          dst = rec + R::QG + (size_t)f * R::FRAG;
-        } else {
-          const int ff = f - NQG, ib = ff >> 1, pp = ff & 1;
-          src = KtT + (16 * ib + m) * LDC + 32 * pp + 4 * g4;
-          dst = rec + R::KT + (size_t)ff * R::FRAG;
-        }
-        const SV4 lo = *reinterpret_cast<const SV4*>(src);
-        const SV4 hi = *reinterpret_cast<const SV4*>(src + 16);
-        *reinterpret_cast<f16x8*>(dst + lane * 16) =
-            f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-    }
+    phase_s2(rec, true);
     __syncthreads();
 
     // ==== phase Y: -Y and U into the record ======================================
     if (itn < items) fetch(nrow0, nclen, nh, 5);
-    {
-      // -Y fragments (a, kb): wave -> kb = wv / 2 and row blocks {wv & 1, 3 - (wv & 1)}
-      const int kb = wv >> 1;
-      if (kb < R::NKB) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int a = s == 0 ? (wv & 1) : 3 - (wv & 1);
-          f32x4 y0, y1;
-          if (a < 2) {
-            y0 = mma_lds<ST, 32>(zero4(), EhT + 32 * kb * LDC, LDC, Am + 16 * a * LDC, LDC);
-            y1 = mma_lds<ST, 32>(zero4(), EhT + (32 * kb + 16) * LDC, LDC, Am + 16 * a * LDC, LDC);
-          } else {
-            y0 = mma_lds<ST, 64>(zero4(), EhT + 32 * kb * LDC, LDC, Am + 16 * a * LDC, LDC);
-            y1 = mma_lds<ST, 64>(zero4(), EhT + (32 * kb + 16) * LDC, LDC, Am + 16 * a * LDC, LDC);
-          }
-          // lane holds Y[16a + m][32kb + 4*g4 + q] (y0) and Y[16a + m][32kb + 16 + 4*g4 + q] (y1)
-          *reinterpret_cast<f16x8*>(rec + R::YN + ((size_t)(a * R::NKB + kb) * 64 + lane) * 16) =
-              f16x8{(ST)-y0[0], (ST)-y0[1], (ST)-y0[2], (ST)-y0[3],
-                    (ST)-y1[0], (ST)-y1[1], (ST)-y1[2], (ST)-y1[3]};
-        }
-      }
-      // U tiles (jt, a): U = A Z over tokens.  K position 8*g4 + j of a 32-token
-      // step p is token 32p + 4*g4 + j (j < 4) or 32p + 16 + 4*g4 + j - 4; the
-      // A operand reads those columns of row 16a + m of A, and the Z operand
-      // comes from row-major Z through the LDS transpose read (lane s of a
-      // 16-lane group points at 4 channels of one token row; lane m then holds
-      // channel m of 4 consecutive token rows)
-      for (int t = wv; t < 4 * R::NJT; t += NW) {
-        const int a = t / R::NJT, jt = t % R::NJT;
-        f32x4 u = zero4();
-        const int s = m;  // source lane inside the 16-lane group
-        for (int pp = 0; pp <= (a >> 1); ++pp) {
-          const ST* arow = Am + (16 * a + m) * LDC + 32 * pp + 4 * g4;
-          const f16x4 a0 = *reinterpret_cast<const f16x4*>(arow);
-          const f16x4 a1 = *reinterpret_cast<const f16x4*>(arow + 16);
-          const ST* z0 = Zr + (32 * pp + 4 * g4 + (s >> 2)) * Cfg::LDZ + 16 * jt + 4 * (s & 3);
-          const f16x4 b0 = lds_tr16(z0);
-          const f16x4 b1 = lds_tr16(z0 + 16 * Cfg::LDZ);
-          u = mma32(f16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]},
-                    f16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]}, u);
-        }
-        // lane holds U[16a + 4*g4 + q][16jt + m]
-        *reinterpret_cast<SV4*>(rec + R::U + ((size_t)(jt * 4 + a) * 64 + lane) * 8) = cvt4<SV4>(u);
-      }
-    }
+    phase_y(rec);
     if (itn < items) fetch_decay(nh);
     clen = nclen;  // valid rows of the next item (the prologue masks the rest)
     __syncthreads();
+  }
+  }  // MODE != 2
+
+  // ==== strong items, again: exact decay from the inputs ===========================
+  // Every item of this workgroup that the main loop flagged (its flag was
+  // written by this workgroup, before a barrier) is staged again from the
+  // inputs; T and A_qk are formed entry by entry with the exact decay, E,
+  // K_tail and Q_g from the uncentred G, and phases S and Y run as above.
+  auto strong_item = [&](int ri) __attribute__((always_inline)) {
+    long long frow0;
+    int fclen, fh;
+    locate(ri, frow0, fclen, fh);
+    char* rec = p.rec + (size_t)ri * R::BYTES;
+    strong_stage<DK, DV, LA16, PRO>(p, frow0, fclen, fh);
+    __syncthreads();
+    {
+      const float* SG = reinterpret_cast<const float*>(smem + Cfg::O_SG);
+      const KT* SK = reinterpret_cast<const KT*>(smem + Cfg::O_SK);
+      const KT* SQ = reinterpret_cast<const KT*>(smem + Cfg::O_SQ);
+      const ST* SB = reinterpret_cast<const ST*>(smem + Cfg::O_SB);
+      for (int k = 0; k < 2; ++k) {
+        const int ti = k == 0 ? wv : (wv == 0 ? 8 : wv == 2 ? 9 : -1);
+        if (ti < 0) break;
+        int a, b;
+        tri_tile(ti, a, b);
+        f32x4 acc, acct;
+        strong_tile<DK, Cfg::LDG, LDK>(SG, SK, SQ, SB, scl, 16 * a + m, 16 * b + 4 * g4, acc, acct);
+        tile_store<DK, DV>(a, b, acc, acct, rec);
+      }
+      // this thread's rows and channels (the phase-L layout) of Q_g = gamma q
+      // and K_tail = (gamma_C / gamma) k go straight into their record
+      // fragments; E = gamma b k waits in registers for region X
+      float fe[RPT][EPC], kcol[EPC][RPT];
+#pragma unroll
+      for (int pr = 0; pr < RPT; ++pr) {
+        const int r = r0 + pr;
+        const float2 sc = *reinterpret_cast<const float2*>(scl + 2 * r);
+        float qrow[EPC];
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) {
+          const int c = EPC * cg + i;
+          const float gr = SG[r * Cfg::LDG + c], gam = exp2_fast(gr);
+          const float kk = (float)SK[r * LDK + c] * sc.y;
+          fe[pr][i] = gam * ((float)SB[r * LDK + c] * kk);
+          qrow[i] = gam * ((float)SQ[r * LDK + c] * sc.x);
+          kcol[i][pr] = exp2_fast(SG[(CH - 1) * Cfg::LDG + c] - gr) * kk;
+        }
+        // Q_g fragment (a, kb), lane (m, g4): channels 32 kb + 4 g4 + [0, 4)
+        // (first half) or 32 kb + 16 + 4 g4 + [0, 4) (second half) of row 16 a + m
+        const int c0 = EPC * cg, kb = c0 / 32, w = c0 % 32, half = w / 16, g4q = (w % 16) / 4;
+        char* dq = rec + R::QG + ((size_t)((r / 16) * R::NKB + kb) * 64 + 16 * g4q + (r % 16)) * 16 + 8 * half;
+        *reinterpret_cast<SV4*>(dq) = SV4{(ST)qrow[0], (ST)qrow[1], (ST)qrow[2], (ST)qrow[3]};
+      }
+      // K_tail fragment (ib, p), lane (m, g4): tokens 32 p + 4 g4 + [0, 4) (first
+      // half) or 32 p + 16 + 4 g4 + [0, 4) (second half) of channel 16 ib + m;
+      // this thread's RPT rows (RPT <= 4, aligned) are RPT of those 4 tokens
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) {
+        const int c = EPC * cg + i, pp = r0 / 32, w = r0 % 32, half = w / 16, g4k = (w % 16) / 4;
+        ST* dk = reinterpret_cast<ST*>(rec + R::KT + ((size_t)((c / 16) * 2 + pp) * 64 + 16 * g4k + (c % 16)) * 16 +
+                                       8 * half);
+        stn<ST, RPT>(dk + r0 % 4, kcol[i]);
+      }
+      __syncthreads();  // the staged rows are read; region X takes E^T
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) {
+        float col[RPT];
+#pragma unroll
+        for (int pr = 0; pr < RPT; ++pr) col[pr] = fe[pr][i];
+        stn<ST, RPT>(EhT + (EPC * cg + i) * LDC + r0, col);
+      }
+      inv_diag();
+    }
+    __syncthreads();
+    phase_s2(rec, false);
+    __syncthreads();
+    phase_y(rec);
+    __syncthreads();
+  };
+  if constexpr (MODE == 0) {
+    for (int it = blockIdx.x; nstrong > 0 && it < items; it += gridDim.x) {
+      const int ri = order(it);
+      if (p.sflag[ri] == 0) continue;  // uniform
+      --nstrong;
+      strong_item(ri);
+    }
+  }
+  if constexpr (MODE == 2) {
+    // the flags of NT of this workgroup's items at a time, one per thread
+    for (int base = blockIdx.x; base < items; base += gridDim.x * NT) {
+      const int mine = base + tid * gridDim.x;
+      if (__syncthreads_or(mine < items && p.sflag[order(mine)] != 0) == 0) continue;
+      for (int j = 0; j < NT; ++j) {
+        const int it = base + j * gridDim.x;
+        if (it >= items) break;
+        const int ri = order(it);
+        if (p.sflag[ri] != 0) strong_item(ri);  // uniform
+      }
+    }
   }
 }
 
@@ -681,27 +982,38 @@ size_t record_bytes(int dk, int dv) {
   return 0;
 }
 
+template <int DK, int DV, bool LA16, bool PRO, int MODE>
+static hipError_t launch_intra_mode(const IntraArgs& a, long long grid, hipStream_t stream) {
+  typedef IntraCfg<DK, DV> Cfg;
+  static std::atomic<bool> lds_set[64];
+  const hipError_t e =
+      lds_opt_in(reinterpret_cast<const void*>(&intra_kernel<DK, DV, LA16, PRO, MODE>), Cfg::BYTES, lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((intra_kernel<DK, DV, LA16, PRO, MODE>), dim3((unsigned)grid), dim3(NT), Cfg::BYTES, stream,
+                     a);
+  return hipGetLastError();
+}
+
 template <int DK, int DV, bool LA16, bool PRO>
 static hipError_t launch_intra1(const IntraArgs& a, hipStream_t stream) {
-  typedef IntraCfg<DK, DV> Cfg;
   const long long items = (long long)a.chunks * a.H;
   if (items <= 0) return hipSuccess;
-  static bool attr_set[64] = {};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64 || !attr_set[dev]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&intra_kernel<DK, DV, LA16, PRO>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::BYTES);
-    if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64) attr_set[dev] = true;
-  }
   int cus = 256;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
   const long long grid = items < cus ? items : cus;  // persistent: one workgroup per CU
-  hipLaunchKernelGGL((intra_kernel<DK, DV, LA16, PRO>), dim3((unsigned)grid), dim3(NT), Cfg::BYTES, stream, a);
-  return hipGetLastError();
+  // the variants whose main loop is lightest keep the exact path in the same
+  // launch; the others run it as a second launch
+  if constexpr (LA16 && !PRO) {
+    return launch_intra_mode<DK, DV, LA16, PRO, 0>(a, grid, stream);
+  } else {
+    e = launch_intra_mode<DK, DV, LA16, PRO, 1>(a, grid, stream);
+    if (e != hipSuccess) return e;
+    return launch_intra_mode<DK, DV, LA16, PRO, 2>(a, grid, stream);
+  }
 }
 
 hipError_t launch_intra(const IntraArgs& a, int dk, int dv, hipStream_t stream) {

@@ -342,7 +342,7 @@ __global__ __launch_bounds__(64 * (NWV + NP), 1) void state_kernel(StateArgs p) 
 #pragma unroll
       for (int f = 0; f < 6; ++f)
         af[f] = *reinterpret_cast<const f16x8*>(L + OA + ((size_t)f * 64 + lane) * 16);
-      __bf16* orow = static_cast<__bf16*>(p.o) + ((size_t)(tok0 + (long long)c * CH) * H) * DV + olane;
+      const size_t obase = ((size_t)(tok0 + (long long)c * CH) * H) * DV + olane;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         // A_qk tile (a, p) exists for p <= a / 2; index a for a < 2, 2a - 2 + p above
@@ -354,9 +354,15 @@ __global__ __launch_bounds__(64 * (NWV + NP), 1) void state_kernel(StateArgs p) 
         O[ct][3] = mma32(rf[ct][1], af[5], O[ct][3]);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
-          if (16 * a + m < clen)
-            *reinterpret_cast<bf16x4*>(orow + (size_t)16 * a * H * DV + 16 * ct) =
-                bf16x4{(__bf16)O[ct][a][0], (__bf16)O[ct][a][1], (__bf16)O[ct][a][2], (__bf16)O[ct][a][3]};
+          if (16 * a + m < clen) {
+            const size_t oi = obase + (size_t)16 * a * H * DV + 16 * ct;
+            if (p.o_f32)  // uniform: fp32 output rows
+              *reinterpret_cast<float4*>(static_cast<float*>(p.o) + oi) =
+                  make_float4(O[ct][a][0], O[ct][a][1], O[ct][a][2], O[ct][a][3]);
+            else
+              *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.o) + oi) =
+                  bf16x4{(__bf16)O[ct][a][0], (__bf16)O[ct][a][1], (__bf16)O[ct][a][2], (__bf16)O[ct][a][3]};
+          }
       }
     }
 
@@ -481,16 +487,10 @@ static hipError_t launch_state1(const StateArgs& a, hipStream_t stream) {
   const long long grid = (pairs + 7) / 8 * 8 * NB;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  static bool attr_set[64] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  static std::atomic<bool> lds_set[64];
+  const hipError_t e =
+      lds_opt_in(reinterpret_cast<const void*>(&state_kernel<DK, DV, NWV, NP, XF, CT>), Cfg::BYTES, lds_set);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64 || !attr_set[dev]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&state_kernel<DK, DV, NWV, NP, XF, CT>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::BYTES);
-    if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64) attr_set[dev] = true;
-  }
   hipLaunchKernelGGL((state_kernel<DK, DV, NWV, NP, XF, CT>), dim3((unsigned)grid), dim3(Cfg::NTH), Cfg::BYTES,
                      stream, a);
   return hipGetLastError();

@@ -153,11 +153,16 @@ def fwd(q, k, v, g, b, w, S0=None, cu_seqlens=None, mask=None, nthreads: int = 0
     return o, ST
 
 
-def decode(q, k, v, g, b, w, S, nthreads: int = 0, lib=None):
-    """One fp64 decode step.  Inputs [N, H, d]; S [N, H, dk, dv] (not modified).
-    Returns (o [N, H, dv], S_new)."""
+def decode(q, k, v, g, b, w, S, nthreads: int = 0, lib=None, inplace: bool = False):
+    """One fp64 decode step.  Inputs [N, H, d]; S [N, H, dk, dv].  Returns
+    (o [N, H, dv], S_new).  S is not modified unless ``inplace``, which needs a
+    C-contiguous float64 numpy S and updates it (S_new is then S itself)."""
     q, k, v, g, b, w = (f64(x) for x in (q, k, v, g, b, w))
-    S = f64(S).copy()
+    if inplace:
+        if not (isinstance(S, np.ndarray) and S.dtype == np.float64 and S.flags.c_contiguous):
+            raise TypeError("inplace decode needs a C-contiguous float64 numpy state")
+    else:
+        S = f64(S).copy()
     N, H, dk = q.shape
     dv = v.shape[-1]
     o = np.zeros((N, H, dv), dtype=np.float64)

@@ -62,7 +62,7 @@ def dec(**kw):
     (dict(q=None), 1), (dict(o=None), 1), (dict(la=None), 1),
     (dict(dt=7), 3), (dict(ldt=-1), 3),
     (dict(B=0), 2), (dict(T=-1), 2), (dict(H=0), 2), (dict(dk=0), 2),
-    (dict(dk=48), 5), (dict(dv=256), 5), (dict(dt=G.GDR2_F32, dk=128), 5),
+    (dict(dk=48), 5), (dict(dv=256), 5), (dict(dt=G.GDR2_F32, dk=128), 6),
     (dict(cu=A, ns=3), 2), (dict(cu=A, B=1, ns=0), 2),
     (dict(q=MIS), 4), (dict(S0=MIS), 4), (dict(cu=MIS, B=1, ns=3), 4),
     (dict(cu=A, B=1, ns=3), 6), (dict(cu=A, B=1, ns=3, ws=A, wsb=8), 6),
@@ -84,11 +84,15 @@ def test_decode_rejects(kw, status):
 def test_workspace_query():
     q = G.gdr2_chunk_fwd_workspace_bytes
     a256 = lambda x: (x + 255) // 256 * 256
-    # fp32 inputs: only the longest-first order of more than one packed sequence
-    assert q(1, 100, 16, 64, 64, 0, G.GDR2_F32) == 0
-    assert q(1, 100, 16, 64, 64, 1, G.GDR2_F32) == 0
-    assert q(1, 100, 16, 64, 64, 64, G.GDR2_F32) == 256
-    assert q(1, 100, 16, 64, 64, 100, G.GDR2_F32) == 512
+    # fp32 inputs: the fp32 blocks of the backward's front pass, per (chunk, head)
+    # (include/gdr2.h: gdr2_chunk_bwd_workspace_bytes), plus packed-sequence tables
+    qb = G.gdr2_chunk_bwd_workspace_bytes
+    for dk, dv in ((64, 64), (128, 128), (32, 128)):
+        item = a256((4 * 64 * dk + 3 * 64 * dv + 2 * 64 * 64 + 2 * dk * dv + dk) * 4)
+        assert q(1, 100, 16, dk, dv, 0, G.GDR2_F32) == qb(1, 100, 16, dk, dv, 0) == 2 * 16 * item
+        assert q(2, 300, 3, dk, dv, 0, G.GDR2_F32) == 2 * 5 * 3 * item
+        assert q(1, 100, 16, dk, dv, 64, G.GDR2_F32) == qb(1, 100, 16, dk, dv, 64) == \
+            a256(65 * 4) + a256(66 * 8) + 66 * 16 * item
     # 16-bit inputs: one record per (chunk, head), plus the packed-sequence tables
     # record of the intra-chunk pass (include/gdr2.h): fp16 fragments -Y and Q_g
     # (4*dk/32 KiB each), K_tail (2*dk/16 KiB), A_qk (6 KiB), U (dv/16*4 tiles of
@@ -96,24 +100,30 @@ def test_workspace_query():
     def rec_bytes(dk, dv):
         return 2 * 4 * (dk // 32) * 1024 + 2 * (dk // 16) * 1024 + 6 * 1024 + (dv // 16) * 4 * 512 + 4 * dk
     rec = rec_bytes(128, 128)
-    assert q(4, 4096, 16, 128, 128, 0, G.GDR2_BF16) == 4 * 64 * 16 * rec
-    assert q(1, 100, 16, 128, 128, 0, G.GDR2_BF16) == 2 * 16 * rec
+    # then, from the next 256-byte boundary, one int per record: its chunk took
+    # the exact-decay path
+    fl = lambda before, recs: a256(before) + recs * 4
+    assert q(4, 4096, 16, 128, 128, 0, G.GDR2_BF16) == fl(4 * 64 * 16 * rec, 4 * 64 * 16)
+    assert q(1, 100, 16, 128, 128, 0, G.GDR2_BF16) == fl(2 * 16 * rec, 2 * 16)
     cap = 2 + 64
     assert q(1, 100, 16, 128, 128, 64, G.GDR2_BF16) == \
-        a256(64 * 4) + a256(65 * 4) + a256(cap * 8) + cap * 16 * rec
-    assert q(2, 64, 3, 32, 64, 0, G.GDR2_BF16) == 2 * 1 * 3 * rec_bytes(32, 64)
+        fl(a256(64 * 4) + a256(65 * 4) + a256(cap * 8) + cap * 16 * rec, cap * 16)
+    assert q(2, 64, 3, 32, 64, 0, G.GDR2_BF16) == fl(2 * 1 * 3 * rec_bytes(32, 64), 2 * 3)
     # few long chains: P segments per sequence add transfer matrices and end states
     # (B*P*H*dk*(dk+dv) fp32 from the next 256-byte boundary)
-    assert q(1, 32768, 16, 128, 128, 0, G.GDR2_BF16) == a256(512 * 16 * rec) + 16 * 16 * 128 * 256 * 4
-    assert q(1, 32768, 32, 128, 128, 0, G.GDR2_BF16) == a256(512 * 32 * rec) + 8 * 32 * 128 * 256 * 4
-    assert q(1, 32768, 1, 64, 64, 0, G.GDR2_BF16) == a256(512 * rec_bytes(64, 64)) + 16 * 64 * 128 * 4
+    assert q(1, 32768, 16, 128, 128, 0, G.GDR2_BF16) == \
+        fl(a256(512 * 16 * rec) + 16 * 16 * 128 * 256 * 4, 512 * 16)
+    assert q(1, 32768, 32, 128, 128, 0, G.GDR2_BF16) == \
+        fl(a256(512 * 32 * rec) + 8 * 32 * 128 * 256 * 4, 512 * 32)
+    assert q(1, 32768, 1, 64, 64, 0, G.GDR2_BF16) == \
+        fl(a256(512 * rec_bytes(64, 64)) + 16 * 64 * 128 * 4, 512)
     # 1000 chunks, 16 segments of 63 chunks (the last 55)
     assert q(2, 64000, 4, 32, 32, 0, G.GDR2_BF16) == \
-        a256(2 * 1000 * 4 * rec_bytes(32, 32)) + 2 * 16 * 4 * 32 * 64 * 4
+        fl(a256(2 * 1000 * 4 * rec_bytes(32, 32)) + 2 * 16 * 4 * 32 * 64 * 4, 2 * 1000 * 4)
     # no split: enough chains, too short, dk != dv, or packed sequences
-    assert q(4, 32768, 16, 128, 128, 0, G.GDR2_BF16) == 4 * 512 * 16 * rec
-    assert q(1, 1024, 16, 128, 128, 0, G.GDR2_BF16) == 16 * 16 * rec
-    assert q(1, 32768, 16, 64, 128, 0, G.GDR2_BF16) == 512 * 16 * rec_bytes(64, 128)
+    assert q(4, 32768, 16, 128, 128, 0, G.GDR2_BF16) == fl(4 * 512 * 16 * rec, 4 * 512 * 16)
+    assert q(1, 1024, 16, 128, 128, 0, G.GDR2_BF16) == fl(16 * 16 * rec, 16 * 16)
+    assert q(1, 32768, 16, 64, 128, 0, G.GDR2_BF16) == fl(512 * 16 * rec_bytes(64, 128), 512 * 16)
     assert q(1, 100, 16, 48, 128, 64, G.GDR2_BF16) == 0
     assert q(0, 100, 16, 128, 128, 64, G.GDR2_BF16) == 0
 

@@ -5,8 +5,7 @@ The backward computes in fp32 from the stored inputs (converted exactly), so
 the bar is the fp32 one: max |x - ref| / max |ref| <= 1e-4 per gradient
 tensor.  Cases span several chunks with ragged tails, all head sizes the
 library supports, packed sequences with zero- and one-token members, and the
-training shape sampled on (sequence, head) pairs the oracle computes one by
-one.
+training shape on every (sequence, head) chain.
 """
 import numpy as np
 import pytest
@@ -43,15 +42,17 @@ def oracle_bwd(wl, dO, dST, mask=None):
 
 
 def check(gr, ref, what, rows=None, with_ds0=True):
+    errs = {}
     for ours, theirs in NAMES.items():
         x, r = M.as64(gr[ours]), ref[theirs]
         if rows is not None:
             x, r = rows(x), rows(r)
-        err = M.max_rel(x, r)
-        assert err <= TOL, f"{what}: {ours} {err:.3e}"
+        errs[ours] = M.max_rel(x, r)
     if with_ds0 and gr["dS0"] is not None:
-        err = M.max_rel(gr["dS0"], ref["dS0"])
-        assert err <= TOL, f"{what}: dS0 {err:.3e}"
+        errs["dS0"] = M.max_rel(gr["dS0"], ref["dS0"])
+    M.record(what, **errs)
+    bad = {n: e for n, e in errs.items() if not e <= TOL}
+    assert not bad, f"{what}: " + ", ".join(f"{n} {e:.3e}" for n, e in bad.items())
 
 
 @pytest.mark.parametrize("B,T,H,dk,dv,dtype", [
@@ -102,19 +103,10 @@ def test_backward_empty_sequence_passes_state_gradient():
     assert torch.equal(gr["dS0"], dST)
 
 
-def test_backward_training_shape_sampled():
+def test_backward_training_shape():
     """B4 T4096 H16 d128 bf16 (the benchmark's forward workload) with random
-    cotangents; the oracle computes 4 sampled (sequence, head) pairs."""
+    cotangents, against the oracle on every (sequence, head) chain."""
     wl = I.config(1)
     dO, dST = I.cotangents(wl, seed=78)
     gr = run_bwd(wl, dO, dST)
-    picks = [(0, 0), (1, 7), (2, 15), (3, 4)]
-    mask = np.zeros((4, 16), bool)
-    for n, h in picks:
-        mask[n, h] = True
-    ref = oracle_bwd(wl, dO, dST, mask=mask)
-    for n, h in picks:
-        check(gr, ref, f"training shape ({n}, {h})", rows=lambda x, n=n, h=h: x[n, :, h],
-              with_ds0=False)
-        err = M.max_rel(gr["dS0"][n, h], ref["dS0"][n, h])
-        assert err <= TOL, f"dS0 ({n}, {h}) {err:.3e}"
+    check(gr, oracle_bwd(wl, dO, dST), "backward training shape, all chains")

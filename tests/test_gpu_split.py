@@ -52,12 +52,14 @@ def rec_bytes(dk, dv):
 
 def assert_split(B, T, H, dk, P):
     """The workspace the library asks for has the transfer matrices and end
-    states of P segments per chain exactly when P > 1."""
+    states of P segments per chain exactly when P > 1 (then one int per record
+    for the exact-decay flags)."""
     nc = (T + 63) // 64
     rec = B * nc * H * rec_bytes(dk, dk)
     extra = 0 if P == 1 else B * P * H * dk * 2 * dk * 4
     base = (rec + 255) // 256 * 256 if P > 1 else rec
-    assert G().gdr2_chunk_fwd_workspace_bytes(B, T, H, dk, dk, 0, G().GDR2_BF16) == base + extra
+    total = (base + extra + 255) // 256 * 256 + B * nc * H * 4
+    assert G().gdr2_chunk_fwd_workspace_bytes(B, T, H, dk, dk, 0, G().GDR2_BF16) == total
 
 
 def run(wl, **kw):
