@@ -27,9 +27,9 @@
  *   - Calls are stream ordered and asynchronous: they enqueue kernels on
  *     `stream` (a hipStream_t; NULL is the null stream) and return without
  *     synchronising.  They are reentrant: the only global mutable state is a
- *     thread-local error string and, per kernel and device, an atomic flag
+ *     thread-local error string, per kernel and device an atomic flag
  *     recording that its LDS limit has been raised (setting it twice is
- *     harmless).
+ *     harmless), and the static scratch of gdr2_chunk_fwd_noalloc.
  *   - Every argument error is detected on the host before any device call:
  *     nothing is written, the status is returned and gdr2_last_error()
  *     describes it.  A failed launch returns GDR2_E_LAUNCH.
@@ -161,6 +161,28 @@ gdr2_status gdr2_chunk_fwd_f32_out(const void *q, const void *k, const void *v,
                                    int B, int T, int H, int dk, int dv,
                                    gdr2_dtype in_dtype, gdr2_dtype log_alpha_dtype,
                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gdr2_chunk_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments without a workspace, and the same results.  The
+ * workspace is a static device array of GDR2_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per device it runs on, held until the process ends; the call
+ * allocates nothing (no hipMalloc, no library allocation).  Sizes whose
+ * workspace (gdr2_chunk_fwd_workspace_bytes) exceeds that array give
+ * GDR2_E_WORKSPACE: at dk = dv = 128 with bf16 inputs, about 3,600
+ * (64-token chunk, head) items, e.g. B = 3, T = 4096, H = 16.  Every call on
+ * one device shares its array, so calls that overlap on one device (other
+ * streams, other threads) race and give undefined results; calls in stream
+ * order on one stream do not.
+ */
+#define GDR2_NOALLOC_SCRATCH_BYTES (256u << 20)
+gdr2_status gdr2_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                                   const void *log_alpha, const void *b, const void *w,
+                                   const float *S0, void *o, float *S_T,
+                                   const int32_t *cu_seqlens, int num_seqs,
+                                   int B, int T, int H, int dk, int dv,
+                                   gdr2_dtype in_dtype, gdr2_dtype log_alpha_dtype, void *stream);
 
 /*
  * Bytes of device workspace gdr2_chunk_bwd needs for these sizes (num_seqs as

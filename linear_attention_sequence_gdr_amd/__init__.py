@@ -31,7 +31,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["gdr2_chunk_fwd", "gdr2_chunk_bwd", "gdr2_chunk_bwd_workspace_bytes", "gdr2_chunk_fwd_block", "gdr2_decode_step", "gdr2_norm_gate",
+__all__ = ["gdr2_chunk_fwd", "gdr2_chunk_fwd_noalloc", "gdr2_chunk_bwd", "gdr2_chunk_bwd_workspace_bytes", "gdr2_chunk_fwd_block", "gdr2_decode_step", "gdr2_norm_gate",
            "gdr2_decode_step_norm_gate", "GDR2_PRO_QK_L2NORM", "GDR2_PRO_DECAY", "GDR2_PRO_GATES",
            "gdr2_chunk_fwd_workspace_bytes",
            "gdr2_status_string", "gdr2_last_error", "gdr2_version", "Gdr2Error",
@@ -41,6 +41,7 @@ GDR2_F32, GDR2_BF16 = 0, 1
 STATUS = {0: "GDR2_OK", 1: "GDR2_E_NULL", 2: "GDR2_E_SHAPE", 3: "GDR2_E_DTYPE",
           4: "GDR2_E_ALIGN", 5: "GDR2_E_UNSUPPORTED", 6: "GDR2_E_WORKSPACE", 7: "GDR2_E_LAUNCH"}
 EXPORTS = ("gdr2_chunk_fwd_workspace_bytes", "gdr2_chunk_fwd", "gdr2_chunk_fwd_f32_out",
+           "gdr2_chunk_fwd_noalloc",
            "gdr2_chunk_fwd_block",
            "gdr2_chunk_bwd_workspace_bytes", "gdr2_chunk_bwd", "gdr2_decode_step",
            "gdr2_norm_gate", "gdr2_decode_step_norm_gate",
@@ -79,6 +80,8 @@ def library():
         lib.gdr2_chunk_fwd.restype = i32
         lib.gdr2_chunk_fwd_f32_out.argtypes = lib.gdr2_chunk_fwd.argtypes
         lib.gdr2_chunk_fwd_f32_out.restype = i32
+        lib.gdr2_chunk_fwd_noalloc.argtypes = [vp] * 10 + [i32] * 6 + [i32, i32, vp]
+        lib.gdr2_chunk_fwd_noalloc.restype = i32
         lib.gdr2_decode_step.argtypes = [vp] * 8 + [i32] * 6 + [vp]
         lib.gdr2_decode_step.restype = i32
         f32, i64 = ctypes.c_float, ctypes.c_longlong
@@ -233,6 +236,44 @@ def _chunk_fwd(lib, dev, s, q, k, v, log_alpha, b, w, S0, cu_seqlens, o, S_T, wa
         _ptr(S_T, "S_T", dev), _ptr(cu_seqlens, "cu_seqlens", dev), N if cu_seqlens is not None else 0,
         Bsz, T, H, dk, dv, in_dt, _dtype_code(log_alpha), _ptr(workspace, "workspace", dev),
         ws_bytes, _stream(s))
+    _check(st)
+    return o, S_T
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20
+
+
+def gdr2_chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
+                           b: torch.Tensor, w: torch.Tensor, S0: Optional[torch.Tensor],
+                           cu_seqlens: Optional[torch.Tensor], o: torch.Tensor,
+                           S_T: Optional[torch.Tensor], stream=None):
+    """gdr2_chunk_fwd on the library's static scratch: the caller passes every
+    output (o in q's dtype, S_T fp32 or None) and nothing is allocated, by
+    this binding or the library.  Returns ``(o, S_T)``."""
+    lib = library()
+    dev = _device(q, "q")
+    s = _torch_stream(stream, dev)
+    Bsz, T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = Bsz if cu_seqlens is None else cu_seqlens.numel() - 1
+    for name, t in (("k", k), ("v", v), ("b", b), ("w", w), ("o", o)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {q.dtype}")
+    for name, t, shp in (("k", k, (Bsz, T, H, dk)), ("log_alpha", log_alpha, (Bsz, T, H, dk)),
+                         ("b", b, (Bsz, T, H, dk)), ("v", v, (Bsz, T, H, dv)), ("w", w, (Bsz, T, H, dv)),
+                         ("o", o, (Bsz, T, H, dv))):
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    for name, t in (("S0", S0), ("S_T", S_T)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (N, H, dk, dv)):
+            raise ValueError(f"{name} must be fp32 {(N, H, dk, dv)}")
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    st = lib.gdr2_chunk_fwd_noalloc(
+        _ptr(q, "q", dev), _ptr(k, "k", dev), _ptr(v, "v", dev), _ptr(log_alpha, "log_alpha", dev),
+        _ptr(b, "b", dev), _ptr(w, "w", dev), _ptr(S0, "S0", dev), _ptr(o, "o", dev),
+        _ptr(S_T, "S_T", dev), _ptr(cu_seqlens, "cu_seqlens", dev), N if cu_seqlens is not None else 0,
+        Bsz, T, H, dk, dv, _dtype_code(q), _dtype_code(log_alpha), _stream(s))
     _check(st)
     return o, S_T
 

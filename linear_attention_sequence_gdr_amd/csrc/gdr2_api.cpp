@@ -10,8 +10,16 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "gdr2.h"
 #include "gdr2_internal.h"
+
+// Workspace of gdr2_chunk_fwd_noalloc: one static array per device that the
+// library runs on, held until the process ends.  Host code never uses this
+// name as an address (on the host it only stands for the symbol): the device
+// address comes from hipGetSymbolAddress, once per device (scratch_address).
+static __device__ __align__(256) unsigned char scratch[GDR2_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -189,12 +197,13 @@ size_t gdr2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
 namespace {
 
 // gdr2_chunk_fwd and gdr2_chunk_fwd_f32_out: o in in_dtype, or fp32 (o_f32).
+// dry_run: validate every argument but the workspace, and return.
 gdr2_status chunk_fwd_common(const char* fn, const void* q, const void* k, const void* v,
                              const void* log_alpha, const void* b, const void* w, const float* S0,
                              void* o, float* S_T, const int32_t* cu_seqlens, int num_seqs, int B,
                              int T, int H, int dk, int dv, gdr2_dtype in_dtype,
                              gdr2_dtype log_alpha_dtype, bool o_f32, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+                             size_t workspace_bytes, void* stream, bool dry_run = false) {
   if (!q || !k || !v || !log_alpha || !b || !w || !o)
     return fail(GDR2_E_NULL, "%s: q, k, v, log_alpha, b, w and o must be non-NULL", fn);
   if (!dtype_ok(in_dtype) || !dtype_ok(log_alpha_dtype))
@@ -226,6 +235,7 @@ gdr2_status chunk_fwd_common(const char* fn, const void* q, const void* k, const
       bf16 ? two_pass_layout(B, T, H, dk, dv, ns).cap * H : bwd_layout(B, T, H, dk, dv, ns).cap * H;
   if (items > 0x7fffffffLL)
     return fail(GDR2_E_SHAPE, "%s: %lld (chunk, head) items exceed 2^31 - 1", fn, items);
+  if (dry_run) return GDR2_OK;
   const size_t need = gdr2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, ns, in_dtype);
   if (need && (!workspace || workspace_bytes < need))
     return fail(GDR2_E_WORKSPACE, "%s: workspace of %zu bytes needed, got %zu%s", fn, need,
@@ -262,9 +272,55 @@ gdr2_status chunk_fwd_common(const char* fn, const void* q, const void* k, const
                   log_alpha_dtype == GDR2_BF16, 0, nullptr, nullptr, 1.f, 0.f, o_f32, ws, st);
 }
 
+// The device address of this device's static scratch, looked up once per
+// device with that device current (each device holds its own copy).
+constexpr int SCRATCH_DEVICES = 64;
+std::once_flag g_scratch_once[SCRATCH_DEVICES];
+void* g_scratch_addr[SCRATCH_DEVICES];
+hipError_t g_scratch_err[SCRATCH_DEVICES];
+
+hipError_t scratch_address(void** addr) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= SCRATCH_DEVICES) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_addr[dev], HIP_SYMBOL(scratch));
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *addr = g_scratch_addr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
+
+gdr2_status gdr2_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                   const void* log_alpha, const void* b, const void* w,
+                                   const float* S0, void* o, float* S_T,
+                                   const int32_t* cu_seqlens, int num_seqs, int B, int T, int H,
+                                   int dk, int dv, gdr2_dtype in_dtype,
+                                   gdr2_dtype log_alpha_dtype, void* stream) {
+  const char* fn = "gdr2_chunk_fwd_noalloc";
+  gdr2_status st = chunk_fwd_common(fn, q, k, v, log_alpha, b, w, S0, o, S_T, cu_seqlens, num_seqs,
+                                    B, T, H, dk, dv, in_dtype, log_alpha_dtype, in_dtype == GDR2_F32,
+                                    nullptr, 0, stream, true);
+  if (st != GDR2_OK) return st;
+  const size_t need = gdr2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, cu_seqlens ? num_seqs : 0, in_dtype);
+  if (need > (size_t)GDR2_NOALLOC_SCRATCH_BYTES)
+    return fail(GDR2_E_WORKSPACE,
+                "%s: these sizes need %zu bytes of workspace, more than the %zu bytes of static "
+                "scratch (use gdr2_chunk_fwd with a workspace)",
+                fn, need, (size_t)GDR2_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess)
+    return fail(GDR2_E_LAUNCH, "%s: address of the static scratch: %s", fn, hipGetErrorString(e));
+  return chunk_fwd_common(fn, q, k, v, log_alpha, b, w, S0, o, S_T, cu_seqlens, num_seqs, B, T, H, dk,
+                          dv, in_dtype, log_alpha_dtype, in_dtype == GDR2_F32, ws,
+                          (size_t)GDR2_NOALLOC_SCRATCH_BYTES, stream);
+}
 
 gdr2_status gdr2_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
                            const void* b, const void* w, const float* S0, void* o, float* S_T,

@@ -245,3 +245,33 @@ def test_chunk_bwd_workspace_query():
     a256 = lambda x: (x + 255) // 256 * 256
     assert q(1, 100, 2, 32, 32, 5) == a256(6 * 4) + a256(2 * 4 * 7) + 7 * 2 * item(32, 32)
     assert q(1, 100, 2, 48, 32, 0) == 0
+
+
+def noalloc(**kw):
+    args = dict(q=A, k=A, v=A, la=A, b=A, w=A, S0=None, o=A, ST=None, cu=None, ns=0, B=2, T=100,
+                H=4, dk=128, dv=128, dt=G.GDR2_BF16, ldt=G.GDR2_BF16, stream=None)
+    args.update(kw)
+    return G.library().gdr2_chunk_fwd_noalloc(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(dt=7), 3), (dict(B=0), 2), (dict(dk=48), 5), (dict(q=MIS), 4),
+    (dict(cu=A, ns=3), 2),
+    # B4 T4096 H16 d128 needs about 296 MB of workspace, more than the 256 MiB scratch
+    (dict(B=4, T=4096, H=16), 6),
+    (dict(B=1, T=64 * 1200, H=16, dt=G.GDR2_F32, ldt=G.GDR2_F32), 6),
+])
+def test_noalloc_rejects_on_the_host(kw, status):
+    """Argument errors, and sizes whose workspace exceeds the static scratch,
+    are refused before any device call (no GPU here)."""
+    assert noalloc(**kw) == status
+    assert G.gdr2_last_error().startswith("gdr2_chunk_fwd_noalloc")
+
+
+def test_noalloc_limit_matches_the_workspace_query():
+    q = G.gdr2_chunk_fwd_workspace_bytes
+    assert q(3, 4096, 16, 128, 128, 0, G.GDR2_BF16) <= G.NOALLOC_SCRATCH_BYTES
+    assert q(4, 4096, 16, 128, 128, 0, G.GDR2_BF16) > G.NOALLOC_SCRATCH_BYTES
+    hdr = open(HEADER).read()
+    assert "#define GDR2_NOALLOC_SCRATCH_BYTES (256u << 20)" in hdr
+    assert G.NOALLOC_SCRATCH_BYTES == 256 << 20
