@@ -38,6 +38,8 @@ TRAFFIC_FILE = {"fwd": os.path.join(ROOT, "profiles", "traffic_chunk_fwd_b4_t409
 MFMA_FILE = {"fwd": os.path.join(ROOT, "profiles", "mfma_chunk_fwd_b4_t4096_h16_d128.json"),
              "long": os.path.join(ROOT, "profiles", "mfma_chunk_fwd_b1_t32768_h16_d128.json")}
 MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32")
+# the kernels of one B4 T4096 H16 d128 bf16 gdr2_chunk_fwd call
+FWD_KERNELS = ("intra_kernel<128, 128, true, false, 0>", "state_kernel<128, 128, 2, 4, false, 1>")
 
 
 def fwd_algorithmic(B, T, H, dk, dv, in_bytes=2, C=64):
@@ -274,7 +276,7 @@ def long_leg(args, torch, G, I, dev):
     byts, flops = fwd_algorithmic(lw.B, lw.T, lw.H, lw.dk, lw.dv)
     byts += lw.B * lw.H * lw.dk * lw.dv * 4  # S0 read
     gbs = byts / (ms * 1e-3) / 1e9
-    keys = ("intra_kernel<128, 128, true, false>", "state_kernel<128, 128, 8, 4, true, 2>",
+    keys = ("intra_kernel<128, 128, true, false, 0>", "state_kernel<128, 128, 8, 4, true, 2>",
             "scan_kernel<128, 128>", "state_kernel<128, 128, 4, 4, false, 2>")
     mf = load_mfma("long", *keys)
     mfma = None
@@ -386,7 +388,7 @@ def varlen_leg(args, torch, G, I, dev):
             "tflops": flops / (ms * 1e-3) / 1e12, "alg_bytes": byts,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": load_call_traffic("varlen", "intra_kernel<128, 128, true, false>",
+                         "traffic": load_call_traffic("varlen", "intra_kernel<128, 128, true, false, 0>",
                                                       "intra_kernel", "state_kernel", "schedule",
                                                       "chunk_table")}}
 
@@ -409,7 +411,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-varlen", action="store_true", help="leave out the packed-sequence forward")
+    ap.add_argument("--varlen", choices=("on", "off", "only"), default="on",
+                    help="the packed-sequence forward: in the line (on), left out (off), or alone "
+                         "in a line of its own (only; profiling its kernels apart)")
     ap.add_argument("--no-ceilings", action="store_true", help="leave out the measured ceilings")
     ap.add_argument("--no-cold", action="store_true",
                     help="leave out the cold-cache forward timing (keeps kernel-trace averages warm)")
@@ -455,6 +459,11 @@ def main():
         calibration_copy(args, torch, dev)
         print(json.dumps({"long_sequence": leg, "source_hash": source_hash()}), flush=True)
         return
+    if args.varlen == "only":
+        leg = varlen_leg(args, torch, G, I, dev)
+        calibration_copy(args, torch, dev)
+        print(json.dumps({"varlen": leg, "source_hash": source_hash()}), flush=True)
+        return
 
     # ---- forward: B4 T4096 H16 d128 bf16 ------------------------------------------------
     wl = I.config(1)
@@ -473,8 +482,8 @@ def main():
     gbs = byts / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
     # one gdr2_chunk_fwd call = the intra-chunk pass + the state pass
-    traffic = load_traffic("fwd", "intra_kernel<128, 128, true, false>", "state_kernel<128, 128, 2, 4, false, 1>")
-    mf = load_mfma("fwd", "intra_kernel<128, 128, true, false>", "state_kernel<128, 128, 2, 4, false, 1>")
+    traffic = load_traffic("fwd", *FWD_KERNELS)
+    mf = load_mfma("fwd", *FWD_KERNELS)
     mfma = None
     if mf:
         issued = mf["issued_flops"] / (ms * 1e-3) / 1e12
@@ -560,7 +569,7 @@ def main():
     del z_epi, y_epi
 
     # ---- 64 packed sequences (about 262K tokens) ---------------------------------------
-    varlen = varlen_leg(args, torch, G, I, dev) if not args.no_varlen else None
+    varlen = varlen_leg(args, torch, G, I, dev) if args.varlen == "on" else None
 
     ceil = None if args.no_ceilings else ceilings(torch, dev)
 
@@ -629,7 +638,7 @@ def main():
                      "alg_bytes": bw_bytes,
                      "roofline": {"bound": "hbm", "achieved": bw_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": bw_gbs / HBM_PEAK_GBS,
-                                  "traffic": load_call_traffic("fwd", "bwd_state_fwd_kernel<128, 128>",
+                                  "traffic": load_call_traffic("fwd", "bwd_state_fwd_kernel<128, 128, false>",
                                                                "bwd_")}},
         "long_sequence": long_leg(args, torch, G, I, dev) if args.long == "on" else None,
         "block": {"workload": "gdr2_chunk_fwd_block B4 T4096 H16 Hv16 dk=dv=128 from projections: "
@@ -638,7 +647,8 @@ def main():
                   "alg_bytes": byts,
                   "roofline": {"bound": "hbm", "achieved": bgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                "frac": bgbs / HBM_PEAK_GBS,
-                               "traffic": load_traffic("fwd", "intra_kernel<128, 128, true, true>",
+                               "traffic": load_traffic("fwd", "intra_kernel<128, 128, true, true, 1>",
+                                                       "intra_kernel<128, 128, true, true, 2>",
                                                        "state_kernel<128, 128, 2, 4, false, 1>")}},
         "epilogue": {"workload": "gdr2_norm_gate over the forward's o [B4 T4096 H16 128] bf16, "
                                  "RMSNorm per head (group 128) x weight x silu(z), into y",
