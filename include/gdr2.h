@@ -127,7 +127,7 @@ size_t gdr2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  * which are at most |q|, |k|, |b k|.  The state-pass values must therefore
  * stay inside the fp16 range (|S|, |U|, |R| < 65504; with unit-norm keys and
  * b, w in [0, 2] that is |v| and |S0| below about 1e4); beyond it they become
- * +-inf.
+ * +-inf and o and S_T come out non-finite.  The fp32 path has no such bound.
  *
  * Decay: any log_alpha <= 0 is computed as given.  The 16-bit products use
  * decay factors normalised on one row per chunk, or per 16-token block when
