@@ -34,7 +34,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 TRAFFIC_FILE = {"fwd": os.path.join(ROOT, "profiles", "traffic_chunk_fwd_b4_t4096_h16_d128.json"),
                 "long": os.path.join(ROOT, "profiles", "traffic_chunk_fwd_b1_t32768_h16_d128.json"),
-                "varlen": os.path.join(ROOT, "profiles", "traffic_chunk_fwd_varlen64_h16_d128.json")}
+                "varlen": os.path.join(ROOT, "profiles", "traffic_chunk_fwd_varlen64_h16_d128.json"),
+                "packed_long": os.path.join(ROOT, "profiles", "traffic_chunk_fwd_packed_long32k_h16_d128.json")}
 MFMA_FILE = {"fwd": os.path.join(ROOT, "profiles", "mfma_chunk_fwd_b4_t4096_h16_d128.json"),
              "long": os.path.join(ROOT, "profiles", "mfma_chunk_fwd_b1_t32768_h16_d128.json")}
 MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32")
@@ -393,6 +394,36 @@ def varlen_leg(args, torch, G, I, dev):
                                                       "chunk_table")}}
 
 
+def packed_long_leg(args, torch, G, I, dev):
+    """One 32K-token sequence among 63 short ones, packed: the device plan
+    splits the long sequence into segments."""
+    vw = I.packed_long()
+    ins = [x.to(dev) for x in (vw.q, vw.k, vw.v, vw.log_alpha, vw.b, vw.w)]
+    S0, cu = vw.S0.to(dev), vw.cu_seqlens.to(dev)
+    N, T, H, dk, dv = vw.num_seqs, vw.T, vw.H, vw.dk, vw.dv
+    o = torch.empty((1, T, H, dv), dtype=torch.bfloat16, device=dev)
+    ST = torch.empty_like(S0)
+    ws = torch.empty(max(1, G.gdr2_chunk_fwd_workspace_bytes(1, T, H, dk, dv, N, G.GDR2_BF16)),
+                     dtype=torch.uint8, device=dev)
+    fwd = lambda: G.gdr2_chunk_fwd(*ins, S0, cu, o=o, S_T=ST, workspace=ws)
+    steps = max(3, min(args.steps, 20))
+    ms = time_events(fwd, steps, 2, torch)
+    byts, flops = fwd_algorithmic(1, T, H, dk, dv)
+    byts += N * H * dk * dv * 4 - H * dk * dv * 4  # S0 read and N final states (not 1)
+    gbs = byts / (ms * 1e-3) / 1e9
+    del ins, S0, cu, o, ST, ws
+    return {"workload": f"gdr2_chunk_fwd, one 32768-token sequence among 63 of U[1, 512] tokens "
+                        f"({T} tokens, {N} packed sequences), H16 dk=dv=128 bf16, per-sequence S0 ~ N(0, 0.1), "
+                        "decay shift -2; the long sequence is split into segments on the device",
+            "steps": steps, "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),
+            "tflops": flops / (ms * 1e-3) / 1e12, "alg_bytes": byts,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": load_call_traffic("packed_long", "intra_kernel<128, 128, true, false, 0>",
+                                                      "intra_kernel", "state_kernel", "scan_kernel",
+                                                      "schedule", "chunk_table", "segment_plan")}}
+
+
 def calibration_copy(args, torch, dev):
     if args.calibrate_copy:
         n = args.calibrate_copy * 1024 * 1024 // 4
@@ -424,7 +455,9 @@ def main():
                          "rocprofv3 --pmc counter_collection.csv files")
     ap.add_argument("--traffic-command", default="",
                     help="the command that produced the counter files (recorded)")
-    ap.add_argument("--traffic-workload", choices=("fwd", "long", "varlen"), default="fwd",
+    ap.add_argument("--packed-long", choices=("on", "off", "only"), default="on",
+                    help="the leg with one 32K-token sequence among 63 short ones (only: that leg alone)")
+    ap.add_argument("--traffic-workload", choices=("fwd", "long", "varlen", "packed_long"), default="fwd",
                     help="which workload's kernels the counter files cover")
     ap.add_argument("--mfma", metavar="CSV",
                     help="host only: write the per-kernel MFMA table from a rocprofv3 --pmc "
@@ -463,6 +496,11 @@ def main():
         leg = varlen_leg(args, torch, G, I, dev)
         calibration_copy(args, torch, dev)
         print(json.dumps({"varlen": leg, "source_hash": source_hash()}), flush=True)
+        return
+    if args.packed_long == "only":
+        leg = packed_long_leg(args, torch, G, I, dev)
+        calibration_copy(args, torch, dev)
+        print(json.dumps({"packed_long": leg, "source_hash": source_hash()}), flush=True)
         return
 
     # ---- forward: B4 T4096 H16 d128 bf16 ------------------------------------------------
@@ -570,6 +608,7 @@ def main():
 
     # ---- 64 packed sequences (about 262K tokens) ---------------------------------------
     varlen = varlen_leg(args, torch, G, I, dev) if args.varlen == "on" else None
+    packed_long = packed_long_leg(args, torch, G, I, dev) if args.packed_long == "on" else None
 
     ceil = None if args.no_ceilings else ceilings(torch, dev)
 
@@ -657,6 +696,7 @@ def main():
                                   "unit": "GB/s", "frac": egbs / HBM_PEAK_GBS,
                                   "traffic": load_traffic("fwd", "norm_gate_kernel<1, true>")}},
         "varlen": varlen,
+        "packed_long": packed_long,
         "ceilings": ceil,
         "cpu_baseline": cpu,
         "source_hash": source_hash(),

@@ -161,6 +161,17 @@ def config(index: int, *, variant: str = "none") -> Workload:
     raise ValueError(f"no forward workload for config {index}")
 
 
+def packed_long(seed: int = 1010) -> Workload:
+    """One 32,768-token sequence among 63 short ones of U[1, 512] tokens (the
+    long one at index 20), packed by cu_seqlens, H16 dk=dv=128 bf16, gates as
+    in config 1, per-sequence S0 ~ N(0, 0.1)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    lens = torch.randint(1, 513, (64,), generator=gen).tolist()
+    lens[20] = 32768
+    return make_forward(1, sum(lens), 16, 128, 128, dtype=torch.bfloat16, decay_shift=-2.0,
+                        s0_std=0.1, seqlens=lens, seed=seed, name="packed-long")
+
+
 # ---- decode (config 2) -------------------------------------------------------------
 
 DECODE_N, DECODE_H, DECODE_D, DECODE_STEPS = 256, 16, 128, 512

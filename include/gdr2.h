@@ -77,7 +77,15 @@ typedef enum {
  * B*H*P <= 256 and at least 16 chunks per segment; then P is reduced to
  * ceil(ceil(T/64) / ceil(ceil(T/64) / P))), and the workspace adds, from the
  * next 256-byte boundary after the records, B*P*H*dk*(dk + dv) fp32 values
- * for the segments' transfer matrices and end states.  With GDR2_F32 the
+ * for the segments' transfer matrices and end states.  With cu_seqlens, dk ==
+ * dv and more than 32 chunks in all (ceil(T/64) > 32), long sequences may be
+ * split too, as a plan built on the device from cu_seqlens decides: the
+ * tables gain the plan (16 bytes per segment and 8 per sequence, each from a
+ * 256-byte boundary, then 256 bytes), for at most nsmax = num_seqs +
+ * (ceil(T/64) + num_seqs) / 32 segments, and the records are followed, from
+ * the next 256-byte boundary, by nsmax*H*dk*(dk + dv) fp32 values.  Last, from
+ * the next 256-byte boundary, comes one int32 per record (its chunk took the
+ * exact strong-decay path).  With GDR2_F32 the
  * forward runs on the fp32 blocks of the backward's front pass and needs
  * exactly gdr2_chunk_bwd_workspace_bytes(B, T, H, dk, dv, num_seqs) bytes.
  * The workspace is scratch: its contents on entry do not matter and are not
@@ -112,7 +120,12 @@ size_t gdr2_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  * (see gdr2_chunk_fwd_workspace_bytes), a transfer pass first gives every
  * segment its affine map of the entry state (Eq. 23 composed over its
  * chunks), an fp32 scan chains the maps, and the state pass then walks all
- * segments at once from their true entry states.  With GDR2_F32 a front
+ * segments at once from their true entry states.  Packed sequences are
+ * planned one by one on the device: a sequence of nc chunks gets ceil(nc / L)
+ * segments of balanced length, where L is the largest of 32 chunks, the
+ * chunks times heads per compute unit, and sqrt(2 x the longest sequence's
+ * chunks), so a long sequence among short ones no longer sets the call's
+ * length.  With GDR2_F32 a front
  * kernel forms every (chunk, head)'s decay, chunk matrices, WY inverse and its
  * products in fp32 (the first pass of gdr2_chunk_bwd), and a sequential
  * kernel per (sequence, head, 32 value channels) forms o and S_T from them.

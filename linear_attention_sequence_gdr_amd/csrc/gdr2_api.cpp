@@ -45,10 +45,16 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // chunk each, so ceil(T/64) + N chunks bound the record count.  Equal-length
 // sequences with few (sequence, head) chains split each chain into P segments
 // of segc chunks; they add the segments' transfer matrices and end states.
+// Packed sequences with dk == dv and more than PSEG_MIN chunks in all may be
+// split too, as the segment plan built on the device decides: they add the
+// plan (per segment 4 ints, per sequence 2, and the count) and transfer
+// matrices and end states for its largest possible number of segments,
+// nsmax = N + cap / PSEG_MIN.
 struct Layout {
-  size_t order, cbase, tab, rec, phi, ex, sflag, total;
+  size_t order, cbase, tab, seg, sq, nseg, rec, phi, ex, sflag, total;
   long long cap;  // chunks with a record
   int P, segc;
+  int nsmax;      // split packed sequences: segment capacity (0: never split)
 };
 Layout two_pass_layout(int B, int T, int H, int dk, int dv, int num_seqs) {
   Layout l{};
@@ -64,6 +70,15 @@ Layout two_pass_layout(int B, int T, int H, int dk, int dv, int num_seqs) {
     off += align256(sizeof(int32_t) * ((size_t)num_seqs + 1));
     l.tab = off;
     off += align256(2 * sizeof(int32_t) * (size_t)l.cap);
+    if (dk == dv && nc > gdr2::PSEG_MIN) {
+      l.nsmax = (int)(num_seqs + l.cap / gdr2::PSEG_MIN);
+      l.seg = off;
+      off += align256(4 * sizeof(int32_t) * (size_t)l.nsmax);
+      l.sq = off;
+      off += align256(2 * sizeof(int32_t) * (size_t)num_seqs);
+      l.nseg = off;
+      off += 256;
+    }
   } else {
     l.cap = (long long)B * nc;
     const int P = gdr2::segments_for((long long)B * H, nc, dk, dv);
@@ -74,8 +89,8 @@ Layout two_pass_layout(int B, int T, int H, int dk, int dv, int num_seqs) {
   }
   l.rec = off;
   off += (size_t)l.cap * (size_t)H * gdr2::record_bytes(dk, dv);
-  if (l.P > 1) {
-    const size_t chains = (size_t)B * l.P * H;
+  if (l.P > 1 || l.nsmax > 0) {
+    const size_t chains = l.nsmax > 0 ? (size_t)l.nsmax * H : (size_t)B * l.P * H;
     l.phi = align256(off);
     l.ex = l.phi + chains * dk * dk * sizeof(float);
     off = l.ex + chains * dk * dv * sizeof(float);
@@ -134,6 +149,17 @@ gdr2_status two_pass(const char* fn, const void* q, const void* k, const void* v
     }
     const hipError_t e = gdr2::launch_chunk_table(cu_seqlens, N, T, (int)l.cap, cbase, tab, st);
     if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "%s: chunk table launch: %s", fn, hipGetErrorString(e));
+    if (l.nsmax > 0) {
+      // the segment plan balances the longest segment against the work per CU
+      int dev = 0, cus = 256;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+      const hipError_t ep = gdr2::launch_segment_plan(
+          cu_seqlens, N, T, order, cbase, Hv, cus, l.nsmax, reinterpret_cast<int32_t*>(ws + l.seg),
+          reinterpret_cast<int32_t*>(ws + l.sq), reinterpret_cast<int32_t*>(ws + l.nseg), st);
+      if (ep != hipSuccess) return fail(GDR2_E_LAUNCH, "%s: segment plan launch: %s", fn, hipGetErrorString(ep));
+    }
   }
   gdr2::IntraArgs ia;
   ia.q = q; ia.k = k; ia.v = v; ia.la = log_alpha; ia.b = b; ia.w = w;
@@ -153,8 +179,13 @@ gdr2_status two_pass(const char* fn, const void* q, const void* k, const void* v
   sa.cap = (int)l.cap;
   sa.N = N; sa.T = T; sa.H = Hv; sa.DV = dv;
   sa.P = l.P; sa.segc = l.segc;
-  sa.phi = l.P > 1 ? reinterpret_cast<float*>(ws + l.phi) : nullptr;
-  sa.ex = l.P > 1 ? reinterpret_cast<float*>(ws + l.ex) : nullptr;
+  const bool split = l.P > 1 || l.nsmax > 0;
+  sa.phi = split ? reinterpret_cast<float*>(ws + l.phi) : nullptr;
+  sa.ex = split ? reinterpret_cast<float*>(ws + l.ex) : nullptr;
+  sa.seg = l.nsmax > 0 ? reinterpret_cast<const int32_t*>(ws + l.seg) : nullptr;
+  sa.sq = l.nsmax > 0 ? reinterpret_cast<const int32_t*>(ws + l.sq) : nullptr;
+  sa.nseg = l.nsmax > 0 ? reinterpret_cast<const int32_t*>(ws + l.nseg) : nullptr;
+  sa.nsmax = l.nsmax;
   const hipError_t e = gdr2::launch_two_pass(ia, sa, dk, dv, st);
   if (e != hipSuccess) return fail(GDR2_E_LAUNCH, "%s: launch: %s", fn, hipGetErrorString(e));
   return GDR2_OK;

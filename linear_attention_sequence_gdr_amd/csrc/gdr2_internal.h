@@ -130,6 +130,15 @@ struct StateArgs {
   int P, segc;
   float* phi;
   float* ex;
+  // Split packed sequences (cu set, seg set): sequence n's chunks form sq[2n+1]
+  // segments with global ids sq[2n] + [0, sq[2n+1]), numbered in schedule
+  // order; segment g (g < *nseg <= nsmax) is seg[4g..4g+3] = (sequence, first
+  // chunk within the sequence, chunks, the sequence's first segment id).  phi
+  // and ex are then [nsmax][H][..], indexed by (segment id, head).
+  const int32_t* seg;
+  const int32_t* sq;
+  const int32_t* nseg;
+  int nsmax;
 };
 hipError_t launch_two_pass(const IntraArgs& ia, const StateArgs& sa, int dk, int dv, hipStream_t stream);
 // Segments per sequence for the state pass of `chains` equal-length
@@ -176,5 +185,14 @@ size_t schedule_bytes(int N);
 hipError_t launch_chunk_table(const int32_t* cu, int N, int T, int cap, int32_t* cbase, int32_t* tab,
                               hipStream_t stream);
 constexpr int SCHED_MAX = 4096;  // sequences the longest-first sort handles
+// Segment plan of packed sequences for the split state pass (StateArgs::seg):
+// sequence n of nc_n chunks gets P_n = ceil(nc_n / L) segments of balanced
+// length, L = max(PSEG_MIN, ceil(total chunks * H / slots), ceil(sqrt(2 * the
+// longest nc_n))); reads cbase[N] (the chunk total) from the chunk table and
+// `order` (or the identity when NULL).  At most N + cap / PSEG_MIN segments.
+constexpr int PSEG_MIN = 32;
+hipError_t launch_segment_plan(const int32_t* cu, int N, int T, const int32_t* order, const int32_t* cbase,
+                               int H, int slots, int nsmax, int32_t* seg, int32_t* sq, int32_t* nseg,
+                               hipStream_t stream);
 
 }  // namespace gdr2

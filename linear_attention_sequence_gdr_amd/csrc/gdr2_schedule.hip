@@ -97,6 +97,92 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* cu, in
   if (t == 0) cbase[N] = carry_s;
 }
 
+// Segment plan of packed sequences for the split state pass (one workgroup).
+// Each sequence's chain of nc_n chunks is cut into P_n = ceil(nc_n / L)
+// segments of ceil(nc_n / P_n) chunks (the last shorter), where L balances
+// the longest segment against the work per CU (total chunks x heads over the
+// CUs), is at least PSEG_MIN chunks, and at least sqrt(2 x the longest chain)
+// so that the scan over one sequence's segments stays short next to them.
+// Segment ids follow the schedule order, so a sequence's segments are
+// consecutive and the longest sequences' segments come first.  Ids at or past
+// nsmax (only reachable by inputs that break the cu_seqlens contract) are not
+// written; *nseg is the number of segments, at most nsmax.
+__global__ __launch_bounds__(1024) void segment_plan_kernel(const int32_t* cu, int N, int T, const int32_t* order,
+                                                           const int32_t* cbase, int H, int slots, int nsmax,
+                                                           int32_t* seg, int32_t* sq, int32_t* nseg) {
+  __shared__ int part[1024];
+  __shared__ int carry_s, maxc_s, L_s;
+  const int t = threadIdx.x;
+  auto chunks_of = [&](int n) {
+    int s = cu[n], e = cu[n + 1];
+    s = s < 0 ? 0 : (s > T ? T : s);
+    e = e < s ? s : (e > T ? T : e);
+    return (e - s + 63) / 64;
+  };
+  if (t == 0) {
+    carry_s = 0;
+    maxc_s = 0;
+  }
+  __syncthreads();
+  int mx = 0;
+  for (int n = t; n < N; n += 1024) mx = max(mx, chunks_of(n));
+  atomicMax(&maxc_s, mx);
+  __syncthreads();
+  if (t == 0) {
+    const long long work = ((long long)cbase[N] * H + slots - 1) / slots;
+    long long L = work > PSEG_MIN ? work : PSEG_MIN;
+    const long long r = (long long)ceilf(sqrtf(2.f * (float)maxc_s));
+    L = L > r ? L : r;
+    L_s = (int)(L < 0x7fffffffLL ? L : 0x7fffffffLL);
+  }
+  __syncthreads();
+  const int L = L_s;
+  for (int base = 0; base < N; base += 1024) {
+    const int i = base + t;
+    int n = 0, nc = 0, P = 0;
+    if (i < N) {
+      n = order ? order[i] : i;
+      nc = chunks_of(n);
+      P = nc > L ? (nc + L - 1) / L : 1;
+    }
+    part[t] = P;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+      const int v = t >= d ? part[t - d] : 0;
+      __syncthreads();
+      part[t] += v;
+      __syncthreads();
+    }
+    const long long first = (long long)carry_s + part[t] - P;
+    if (i < N) {
+      const int f = (int)(first < nsmax ? first : nsmax);
+      sq[2 * n] = f;
+      sq[2 * n + 1] = first + P <= nsmax ? P : nsmax - f;
+      const int sc = (nc + P - 1) / P;  // chunks per segment; every segment gets at least one when P > 1
+      for (int j = 0; j < P && first + j < nsmax; ++j) {
+        const int g = (int)first + j;
+        seg[4 * g] = n;
+        seg[4 * g + 1] = j * sc;
+        seg[4 * g + 2] = min(sc, nc - j * sc);
+        seg[4 * g + 3] = f;
+      }
+    }
+    __syncthreads();
+    if (t == 1023) carry_s = (int)min((long long)carry_s + part[1023], (long long)nsmax);
+    __syncthreads();
+  }
+  if (t == 0) *nseg = carry_s;
+}
+
+hipError_t launch_segment_plan(const int32_t* cu, int N, int T, const int32_t* order, const int32_t* cbase,
+                               int H, int slots, int nsmax, int32_t* seg, int32_t* sq, int32_t* nseg,
+                               hipStream_t stream) {
+  if (N <= 0 || nsmax <= 0 || H <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(segment_plan_kernel, dim3(1), dim3(1024), 0, stream, cu, N, T, order, cbase, H,
+                     slots > 0 ? slots : 1, nsmax, seg, sq, nseg);
+  return hipGetLastError();
+}
+
 hipError_t launch_chunk_table(const int32_t* cu, int N, int T, int cap, int32_t* cbase, int32_t* tab,
                               hipStream_t stream) {
   if (N <= 0) return hipSuccess;

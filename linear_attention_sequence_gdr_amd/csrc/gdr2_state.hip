@@ -116,34 +116,58 @@ __global__ __launch_bounds__(64 * (NWV + NP), 1) void state_kernel(StateArgs p) 
   const int pair = (slot / NB) * 8 + xcd;
   const int jb = slot % NB;
   const int H = p.H;
-  const int SP = XF ? p.P - 1 : p.P;  // segments per sequence in this pass
-  if (pair >= p.N * SP * H) return;
   const int h = pair % H;
-  const int seg = (pair / H) % SP;
-  const int n = p.order ? p.order[pair / H] : pair / (H * SP);
-  // transfer pass: this wavefront runs columns of the identity (segment 0
-  // forms a transfer matrix too, unused: it starts from S0)
-  const bool ident = XF && 16 * CT * wv < DK;
+  // this chain's sequence n, its segment seg of nseg, and the slot sh of
+  // (sequence, segment, head) in phi and ex
+  int n, seg, nseg;
+  size_t sh;
   long long tok0;
   int len, cb;
-  if (p.cu) {
+  if (p.seg) {
+    // split packed sequences: chain = (segment id, head), every segment id of
+    // the plan in both passes; the transfer pass skips each sequence's last
+    const int g = pair / H;
+    if (pair >= p.nsmax * H || g >= *p.nseg) return;
+    n = p.seg[4 * g];
+    seg = g - p.seg[4 * g + 3];
+    nseg = p.sq[2 * n + 1];
+    if (XF && seg == nseg - 1) return;
+    sh = (size_t)g * H + h;
     int s = p.cu[n], e = p.cu[n + 1];
     s = s < 0 ? 0 : (s > p.T ? p.T : s);
     e = e < s ? s : (e > p.T ? p.T : e);
-    tok0 = s;
-    len = e - s;
-    cb = p.cbase[n];
+    const int c0 = p.seg[4 * g + 1];
+    tok0 = (long long)s + (long long)c0 * CH;
+    len = max(0, min(e - s - c0 * CH, p.seg[4 * g + 2] * CH));
+    cb = p.cbase[n] + c0;
   } else {
-    // segc is the whole sequence's chunk count when chains are not split
-    const int c0 = seg * p.segc;
-    tok0 = (long long)n * p.T + (long long)c0 * CH;
-    len = max(0, min(p.T - c0 * CH, p.segc * CH));
-    cb = n * ((p.T + CH - 1) / CH) + c0;
+    const int SP = XF ? p.P - 1 : p.P;  // segments per sequence in this pass
+    if (pair >= p.N * SP * H) return;
+    seg = (pair / H) % SP;
+    n = p.order ? p.order[pair / H] : pair / (H * SP);
+    nseg = p.P;
+    sh = ((size_t)n * p.P + seg) * H + h;
+    if (p.cu) {
+      int s = p.cu[n], e = p.cu[n + 1];
+      s = s < 0 ? 0 : (s > p.T ? p.T : s);
+      e = e < s ? s : (e > p.T ? p.T : e);
+      tok0 = s;
+      len = e - s;
+      cb = p.cbase[n];
+    } else {
+      // segc is the whole sequence's chunk count when chains are not split
+      const int c0 = seg * p.segc;
+      tok0 = (long long)n * p.T + (long long)c0 * CH;
+      len = max(0, min(p.T - c0 * CH, p.segc * CH));
+      cb = n * ((p.T + CH - 1) / CH) + c0;
+    }
   }
+  // transfer pass: this wavefront runs columns of the identity (segment 0
+  // forms a transfer matrix too, unused: it starts from S0)
+  const bool ident = XF && 16 * CT * wv < DK;
   int nch = (len + CH - 1) / CH;
   if (cb + nch > p.cap) nch = max(0, p.cap - cb);  // only inputs that break the cu_seqlens contract
   const size_t nh = (size_t)n * H + h;
-  const size_t sh = ((size_t)n * p.P + seg) * H + h;  // (sequence, segment, head)
   const bool producer = wv >= NWV;
   // this wavefront's first column (of the identity, or a value channel); its
   // tile ct covers columns col0 + 16*ct + [0, 16)
@@ -154,12 +178,12 @@ __global__ __launch_bounds__(64 * (NWV + NP), 1) void state_kernel(StateArgs p) 
   // S_T may alias S0, and with split chains the last segment writes S_T while
   // segment 0 of the same launch starts: the transfer pass keeps a copy of S0
   // in the spare slot ex[P - 1] for the state pass to start segment 0 from.
-  float* s0copy = p.P > 1 ? p.ex + (sh + (size_t)(p.P - 1 - seg) * H) * (size_t)(DK * DV) : nullptr;
+  float* s0copy = nseg > 1 ? p.ex + (sh + (size_t)(nseg - 1 - seg) * H) * (size_t)(DK * DV) : nullptr;
   const float* sin = nullptr;  // entry state, [DK][DV] row-major
   if (XF) {
     if (!ident && seg == 0 && p.S0) sin = p.S0 + nh * (size_t)(DK * DV);
   } else if (seg == 0) {
-    if (p.S0) sin = p.P > 1 ? s0copy : p.S0 + nh * (size_t)(DK * DV);
+    if (p.S0) sin = nseg > 1 ? s0copy : p.S0 + nh * (size_t)(DK * DV);
   } else {
     sin = p.ex + (sh - H) * (size_t)(DK * DV);  // the end state of segment seg - 1
   }
@@ -395,7 +419,7 @@ __global__ __launch_bounds__(64 * (NWV + NP), 1) void state_kernel(StateArgs p) 
   if (XF) {
     sout = ident ? p.phi + sh * (size_t)(DK * DK) : p.ex + sh * (size_t)(DK * DV);
     ld = ident ? DK : DV;
-  } else if (p.ST && seg == SP - 1) {
+  } else if (p.ST && seg == nseg - 1) {
     sout = p.ST + nh * (size_t)(DK * DV);
   }
   if (sout) {
@@ -429,8 +453,12 @@ __global__ __launch_bounds__(64 * (DK / 16)) void scan_kernel(StateArgs p) {
   const int nh = (slot / NJ) * 8 + xcd, j0 = 16 * (slot % NJ);
   const int n = nh / p.H, h = nh % p.H;
   if (n >= p.N) return;
-  const int last = p.P - 2;                       // steps s = 1 .. last
-  const size_t base = (size_t)n * p.P * p.H + h;  // (n, segment 0, h)
+  // (n, segment 0, h) and the segment count: fixed per sequence, or from the
+  // plan of split packed sequences
+  const int P = p.seg ? p.sq[2 * n + 1] : p.P;
+  const size_t base = p.seg ? (size_t)p.sq[2 * n] * p.H + h : (size_t)n * p.P * p.H + h;
+  const int last = P - 2;  // steps s = 1 .. last
+  if (last < 1) return;
   const float* x0 = p.ex + base * (size_t)(DK * DV);
   for (int i = tid; i < DK * 16; i += 64 * NK) XT[i & 15][i >> 4] = x0[(size_t)(i >> 4) * DV + j0 + (i & 15)];
 
@@ -449,7 +477,6 @@ __global__ __launch_bounds__(64 * (DK / 16)) void scan_kernel(StateArgs p) {
   // Every step issues the same loads (step indices past the last are clamped
   // to it and their values unused), so the count of loads in flight is the
   // same on every path and each step waits only for its own slot.
-  if (last < 1) return;
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) fetch(min(1 + d, last), fa[d], ea[d]);
   __syncthreads();
@@ -483,7 +510,7 @@ template <int DK, int DV, int NWV, int NP, bool XF, int CT = 1>
 static hipError_t launch_state1(const StateArgs& a, hipStream_t stream) {
   typedef StateCfg<DK, DV, NWV, NP, CT, XF> Cfg;
   constexpr int NB = XF ? 1 : DV / Cfg::DVB;
-  const long long pairs = (long long)a.N * (XF ? a.P - 1 : a.P) * a.H;
+  const long long pairs = a.seg ? (long long)a.nsmax * a.H : (long long)a.N * (XF ? a.P - 1 : a.P) * a.H;
   const long long grid = (pairs + 7) / 8 * 8 * NB;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -498,7 +525,7 @@ static hipError_t launch_state1(const StateArgs& a, hipStream_t stream) {
 
 template <int DK, int DV>
 static hipError_t launch_state_dv(const StateArgs& a, hipStream_t stream) {
-  if (a.P > 1) {
+  if (a.P > 1 || a.seg) {
     // split chains: one workgroup per segment covers every column, so the
     // shared part of each record is staged once per segment; two column tiles
     // per wavefront halve the LDS reads of the shared operands
@@ -506,8 +533,11 @@ static hipError_t launch_state_dv(const StateArgs& a, hipStream_t stream) {
       constexpr int NW = DV / 32;
       hipError_t e = launch_state1<DK, DV, 2 * NW, 4, true, 2>(a, stream);
       if (e != hipSuccess) return e;
-      if (a.P > 2) {
+      // split packed sequences: the plan on the device decides which
+      // sequences have segments to chain, so the scan always runs
+      if (a.P > 2 || a.seg) {
         const long long grid = ((long long)a.N * a.H + 7) / 8 * 8 * (DV / 16);
+        if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
         hipLaunchKernelGGL((scan_kernel<DK, DV>), dim3((unsigned)grid), dim3(64 * (DK / 16)), 0, stream, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;

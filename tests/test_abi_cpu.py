@@ -120,7 +120,30 @@ def test_workspace_query():
     # 1000 chunks, 16 segments of 63 chunks (the last 55)
     assert q(2, 64000, 4, 32, 32, 0, G.GDR2_BF16) == \
         fl(a256(2 * 1000 * 4 * rec_bytes(32, 32)) + 2 * 16 * 4 * 32 * 64 * 4, 2 * 1000 * 4)
-    # no split: enough chains, too short, dk != dv, or packed sequences
+    # packed sequences with dk == dv and more than 32 chunks in all may be split
+    # by the plan built on the device: after the chunk table come the plan (4
+    # ints per segment, 2 per sequence, then 256 B for the count) for at most
+    # nsmax = N + cap // 32 segments, and after the records the transfer
+    # matrices and end states of nsmax * H (segment, head) chains
+    def packed(T, N, H, d):
+        cap = (T + 63) // 64 + N
+        nsmax = N + cap // 32
+        head = (a256(N * 4) if 1 < N <= 4096 else 0) + a256((N + 1) * 4) + a256(cap * 8)
+        head += a256(nsmax * 16) + a256(N * 8) + 256
+        recs = head + cap * H * rec_bytes(d, d)
+        return fl(a256(recs) + nsmax * H * d * 2 * d * 4, cap * H)
+    assert q(1, 32768 + 63 * 256, 16, 128, 128, 64, G.GDR2_BF16) == packed(32768 + 63 * 256, 64, 16, 128)
+    assert q(1, 267139, 16, 128, 128, 64, G.GDR2_BF16) == packed(267139, 64, 16, 128)
+    assert q(1, 5000, 3, 32, 32, 1, G.GDR2_BF16) == packed(5000, 1, 3, 32)
+    # 32 chunks or fewer in all: never split, no plan
+    cap = 32 + 5
+    assert q(1, 2048, 4, 128, 128, 5, G.GDR2_BF16) == \
+        fl(a256(5 * 4) + a256(6 * 4) + a256(cap * 8) + cap * 4 * rec, cap * 4)
+    # dk != dv: never split
+    cap = 80 + 3
+    assert q(1, 80 * 64, 2, 64, 128, 3, G.GDR2_BF16) == \
+        fl(a256(3 * 4) + a256(4 * 4) + a256(cap * 8) + cap * 2 * rec_bytes(64, 128), cap * 2)
+    # no split: enough chains, too short, dk != dv
     assert q(4, 32768, 16, 128, 128, 0, G.GDR2_BF16) == fl(4 * 512 * 16 * rec, 4 * 512 * 16)
     assert q(1, 1024, 16, 128, 128, 0, G.GDR2_BF16) == fl(16 * 16 * rec, 16 * 16)
     assert q(1, 32768, 16, 64, 128, 0, G.GDR2_BF16) == fl(512 * 16 * rec_bytes(64, 128), 512 * 16)
