@@ -53,11 +53,15 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* cu, int N
 // chunk counts, one block of 1024 sequences at a time with a running carry),
 // cbase[N] the number of chunks, clamped to the capacity `cap` of the table
 // and of the record buffer; tab[2c], tab[2c+1] are chunk c's first token row
-// and length.  Entries at or past `cap` are never written (only inputs that
-// break the cu_seqlens contract can reach them).
+// and length.  The chunks of a block of sequences are written by all threads
+// at once (thread t takes chunks t, t + 1024, ... and finds its sequence by a
+// binary search over the block's prefix sums), so one long sequence does not
+// serialise the table.  Entries at or past `cap` are never written (only
+// inputs that break the cu_seqlens contract can reach them).
 __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* cu, int N, int T, int cap,
                                                           int32_t* cbase, int32_t* tab) {
   __shared__ int part[1024];
+  __shared__ int st[1024], ln[1024];
   __shared__ int carry_s;
   const int t = threadIdx.x;
   if (t == 0) carry_s = 0;
@@ -74,6 +78,8 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* cu, in
     }
     const int nc = (len + 63) / 64;
     part[t] = nc;
+    st[t] = s;
+    ln[t] = len;
     __syncthreads();
     for (int d = 1; d < 1024; d <<= 1) {
       const int v = t >= d ? part[t - d] : 0;
@@ -83,12 +89,21 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* cu, in
     }
     const long long carry = carry_s;
     const long long first = carry + part[t] - nc;
-    if (n < N) {
-      cbase[n] = (int32_t)(first < cap ? first : cap);
-      for (int c = 0; c < nc && first + c < cap; ++c) {
-        tab[2 * (first + c)] = s + 64 * c;
-        tab[2 * (first + c) + 1] = min(64, len - 64 * c);
+    if (n < N) cbase[n] = (int32_t)(first < cap ? first : cap);
+    // chunk j of this block (j < part[1023]) belongs to the sequence i with
+    // part[i - 1] <= j < part[i]
+    const int nb = part[1023];
+    for (int j = t; j < nb && carry + j < cap; j += 1024) {
+      int lo = 0, hi = 1023;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (part[mid] > j) hi = mid;
+        else lo = mid + 1;
       }
+      const int c = j - (part[lo] - (ln[lo] + 63) / 64);  // chunk within sequence lo
+      const long long x = carry + j;
+      tab[2 * x] = st[lo] + 64 * c;
+      tab[2 * x + 1] = min(64, ln[lo] - 64 * c);
     }
     __syncthreads();
     if (t == 1023) carry_s = (int)min(carry + part[1023], (long long)cap);
