@@ -203,6 +203,18 @@ def time_events(fn, steps, warmup, torch):
     return start.elapsed_time(stop) / steps     # ms per step
 
 
+def settle(fn, torch, seconds=0.25):
+    """Untimed back-to-back calls for about `seconds`: the first milliseconds
+    of a process run at lower clocks, which the warm-up steps alone do not
+    always cover."""
+    import time
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+
+
 def time_cold(fn, steps, torch, flush_mib=512):
     """Median time of single calls that each follow a write of flush_mib MiB
     of scratch, so the 256 MB last-level cache holds none of the call's
@@ -513,6 +525,7 @@ def main():
     ws = torch.empty(max(1, G.gdr2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, 0, G.GDR2_BF16)),
                      dtype=torch.uint8, device=dev)
     fwd = lambda: G.gdr2_chunk_fwd(*ins, None, None, o=o, S_T=ST, workspace=ws)
+    settle(fwd, torch)
     ms = time_events(fwd, args.steps, args.warmup, torch)
     cold_ms = None if args.no_cold else time_cold(fwd, max(5, min(args.steps, 20)), torch)
     byts, flops = fwd_algorithmic(B, T, H, dk, dv)
