@@ -48,9 +48,19 @@
 extern "C" {
 #endif
 
-typedef enum { GDR2_F32 = 0, GDR2_BF16 = 1 } gdr2_dtype;
+/* Both enumerations are int-sized in C and C++ alike.  C++ gets the int
+ * underlying type spelled out so that every int a C caller passes (an unknown
+ * dtype code, say, which the entry points reject) is a valid value of the
+ * parameter's type rather than undefined behaviour. */
+#ifdef __cplusplus
+#define GDR2_ENUM_BASE : int
+#else
+#define GDR2_ENUM_BASE
+#endif
 
-typedef enum {
+typedef enum GDR2_ENUM_BASE { GDR2_F32 = 0, GDR2_BF16 = 1 } gdr2_dtype;
+
+typedef enum GDR2_ENUM_BASE {
     GDR2_OK = 0,
     GDR2_E_NULL = 1,        /* a required pointer is NULL */
     GDR2_E_SHAPE = 2,       /* a size is negative, zero where it must not be, or inconsistent */
