@@ -40,7 +40,7 @@ MFMA_FILE = {"fwd": os.path.join(ROOT, "profiles", "mfma_chunk_fwd_b4_t4096_h16_
              "long": os.path.join(ROOT, "profiles", "mfma_chunk_fwd_b1_t32768_h16_d128.json")}
 MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32")
 # the kernels of one B4 T4096 H16 d128 bf16 gdr2_chunk_fwd call
-FWD_KERNELS = ("intra_kernel<128, 128, true, false, 0>", "state_kernel<128, 128, 2, 4, false, 1>")
+FWD_KERNELS = ("intra_kernel<128, 128, true, 0, 0>", "state_kernel<128, 128, 2, 4, false, 1>")
 
 
 def fwd_algorithmic(B, T, H, dk, dv, in_bytes=2, C=64):
@@ -289,7 +289,7 @@ def long_leg(args, torch, G, I, dev):
     byts, flops = fwd_algorithmic(lw.B, lw.T, lw.H, lw.dk, lw.dv)
     byts += lw.B * lw.H * lw.dk * lw.dv * 4  # S0 read
     gbs = byts / (ms * 1e-3) / 1e9
-    keys = ("intra_kernel<128, 128, true, false, 0>", "state_kernel<128, 128, 8, 4, true, 2>",
+    keys = ("intra_kernel<128, 128, true, 0, 0>", "state_kernel<128, 128, 8, 4, true, 2>",
             "scan_kernel<128, 128>", "state_kernel<128, 128, 4, 4, false, 2>")
     mf = load_mfma("long", *keys)
     mfma = None
@@ -401,7 +401,7 @@ def varlen_leg(args, torch, G, I, dev):
             "tflops": flops / (ms * 1e-3) / 1e12, "alg_bytes": byts,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": load_call_traffic("varlen", "intra_kernel<128, 128, true, false, 0>",
+                         "traffic": load_call_traffic("varlen", "intra_kernel<128, 128, true, 0, 0>",
                                                       "intra_kernel", "state_kernel", "schedule",
                                                       "chunk_table")}}
 
@@ -431,7 +431,7 @@ def packed_long_leg(args, torch, G, I, dev):
             "tflops": flops / (ms * 1e-3) / 1e12, "alg_bytes": byts,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": load_call_traffic("packed_long", "intra_kernel<128, 128, true, false, 0>",
+                         "traffic": load_call_traffic("packed_long", "intra_kernel<128, 128, true, 0, 0>",
                                                       "intra_kernel", "state_kernel", "scan_kernel",
                                                       "schedule", "chunk_table", "segment_plan")}}
 
@@ -699,8 +699,8 @@ def main():
                   "alg_bytes": byts,
                   "roofline": {"bound": "hbm", "achieved": bgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                "frac": bgbs / HBM_PEAK_GBS,
-                               "traffic": load_traffic("fwd", "intra_kernel<128, 128, true, true, 1>",
-                                                       "intra_kernel<128, 128, true, true, 2>",
+                               "traffic": load_traffic("fwd", "intra_kernel<128, 128, true, 7, 1>",
+                                                       "intra_kernel<128, 128, true, 8, 2>",
                                                        "state_kernel<128, 128, 2, 4, false, 1>")}},
         "epilogue": {"workload": "gdr2_norm_gate over the forward's o [B4 T4096 H16 128] bf16, "
                                  "RMSNorm per head (group 128) x weight x silu(z), into y",

@@ -160,6 +160,20 @@ __device__ __forceinline__ float sigmoid_f(float x) {
   return __builtin_amdgcn_rcpf(1.f + __expf(-x));
 }
 
+// Gate-prologue steps of an instantiation: PRO = 0 runs none, PRO_ALL all
+// three with the choice fixed at compile time, PRO_ANY the steps the call's
+// flags select, read at run time.  The all-steps case is the usual one, and
+// fixing it at compile time keeps the registers of the branches it never
+// skips from weighing on the rest of the item (its main loop spills 8 bytes
+// per lane instead of 56).
+constexpr int PRO_ALL = PRO_QK_L2NORM | PRO_DECAY | PRO_GATES;
+constexpr int PRO_ANY = 8;
+template <int PRO>
+__device__ __forceinline__ bool pro_step(const IntraArgs& p, int step) {
+  if constexpr (PRO == PRO_ANY) return (p.pro & step) != 0;
+  else return (PRO & step) != 0;
+}
+
 // Stages a strong item's rows in region X for the exact products of phase P
 // (strong_tile): the uncentred cumulative log2-decay G (fp32), the raw k and
 // q rows (bf16) and the erase gate b (fp16, activated under the prologue),
@@ -167,7 +181,7 @@ __device__ __forceinline__ float sigmoid_f(float x) {
 // h's key head; rows past the end get zero q, k and log-decay.  Thread tid
 // owns channel tid % DK and a group of consecutive rows; the group totals of
 // the decay scan meet in the diagonal-T buffer, free until the tiles.
-template <int DK, int DV, bool LA16, bool PRO>
+template <int DK, int DV, bool LA16, int PRO>
 __device__ __forceinline__ void strong_stage(const IntraArgs& p, long long row0, int clen, int h) {
   typedef IntraCfg<DK, DV> Cfg;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -178,11 +192,11 @@ __device__ __forceinline__ void strong_stage(const IntraArgs& p, long long row0,
   _Float16* SB = reinterpret_cast<_Float16*>(smem + Cfg::O_SB);
   float* part = reinterpret_cast<float*>(smem + Cfg::O_TD);
   const int tid = threadIdx.x, c = tid % DK, gr = tid / DK;
-  const int hk = PRO ? h / p.grp : h;
-  const size_t krow = (size_t)(PRO ? p.Hk : p.H) * DK;
+  const int hk = PRO != 0 ? h / p.grp : h;
+  const size_t krow = (size_t)(PRO != 0 ? p.Hk : p.H) * DK;
   float ea = 0.f, dl = 0.f;
-  if constexpr (PRO) {
-    if (p.pro & PRO_DECAY) {
+  if constexpr (PRO != 0) {
+    if (pro_step<PRO>(p, PRO_DECAY)) {
       ea = __expf(p.da[(size_t)hk * DK + c]);
       dl = p.db[(size_t)hk * DK + c];
     }
@@ -198,9 +212,9 @@ __device__ __forceinline__ void strong_stage(const IntraArgs& p, long long row0,
       kv = load1<true>(p.k, x);
       qv = load1<true>(p.q, x);
       bv = load1<true>(p.b, x);
-      if constexpr (PRO) {
-        if (p.pro & PRO_DECAY) gv = -ea * softplus_f(gv + dl);
-        if (p.pro & PRO_GATES) bv = p.b_scale * sigmoid_f(bv);
+      if constexpr (PRO != 0) {
+        if (pro_step<PRO>(p, PRO_DECAY)) gv = -ea * softplus_f(gv + dl);
+        if (pro_step<PRO>(p, PRO_GATES)) bv = p.b_scale * sigmoid_f(bv);
       }
     }
     acc += gv * LOG2E;
@@ -219,8 +233,8 @@ __device__ __forceinline__ void strong_stage(const IntraArgs& p, long long row0,
     if (r < clen) {
       const size_t x = (size_t)(row0 + r) * vrow + (size_t)h * DV + j;
       float wv = load1<true>(p.w, x);
-      if constexpr (PRO) {
-        if (p.pro & PRO_GATES) wv = sigmoid_f(wv);
+      if constexpr (PRO != 0) {
+        if (pro_step<PRO>(p, PRO_GATES)) wv = sigmoid_f(wv);
       }
       z = load1<true>(p.v, x) * wv;
     }
@@ -238,8 +252,8 @@ __device__ __forceinline__ void strong_stage(const IntraArgs& p, long long row0,
   if (tid < 2 * CH) {
     const int r = tid >> 1, which = tid & 1;
     float sc = 1.f;
-    if constexpr (PRO) {
-      if (p.pro & PRO_QK_L2NORM) {
+    if constexpr (PRO != 0) {
+      if (pro_step<PRO>(p, PRO_QK_L2NORM)) {
         const __bf16* row = (which ? SK : SQ) + r * LDK;
         float ss = 0.f;
         for (int cc = 0; cc < DK; ++cc) ss = fmaf((float)row[cc], (float)row[cc], ss);
@@ -286,7 +300,7 @@ __device__ __forceinline__ void tile_store(int a, int b, f32x4 acc, f32x4 acct, 
 // second launch after MODE 1).  Variants whose main loop is near the register
 // limit take MODE 1 and 2, so that the exact path's registers never weigh on
 // their main loop.
-template <int DK, int DV, bool LA16, bool PRO, int MODE>
+template <int DK, int DV, bool LA16, int PRO, int MODE>
 __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
   typedef IntraCfg<DK, DV> Cfg;
   typedef Rec<DK, DV> R;
@@ -359,7 +373,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
 
   const int cg = tid / RG, rg = tid % RG, r0 = rg * RPT;
   // key-side rows hold Hk heads (grouped value heads), value-side rows H
-  const size_t krow = (size_t)(PRO ? p.Hk : H) * DK, vrow = (size_t)H * DV;
+  const size_t krow = (size_t)(PRO != 0 ? p.Hk : H) * DK, vrow = (size_t)H * DV;
   uint32_t koff[RPT], goff[RPT], voff[NVU];
   int vr[NVU], vc0[NVU];
 #pragma unroll
@@ -382,8 +396,8 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
   // the item boundary
   float4 rda = make_float4(0.f, 0.f, 0.f, 0.f), rdb = rda;
   auto fetch_decay = [&](int h) {
-    if constexpr (PRO) {
-      if (p.pro & PRO_DECAY) {
+    if constexpr (PRO != 0) {
+      if (pro_step<PRO>(p, PRO_DECAY)) {
         const size_t o = (size_t)(h / p.grp) * DK + EPC * cg;
         rda = *reinterpret_cast<const float4*>(p.da + o);
         rdb = *reinterpret_cast<const float4*>(p.db + o);
@@ -398,7 +412,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
   // at six points of the current item (two in phase L, then one at the start
   // of each later phase).
   auto fetch = [&](long long row0, int clen, int h, int batch) {
-    const int hk = PRO ? h / p.grp : h;  // key head of value head h
+    const int hk = PRO != 0 ? h / p.grp : h;  // key head of value head h
     const size_t kel = (size_t)row0 * krow + (size_t)hk * DK, vel = (size_t)row0 * vrow + (size_t)h * DV;
     const int kbytes = (int)(clen * krow * 2), gbytes = (int)(clen * krow * (LA16 ? 2 : 4));
     const int vbytes = (int)(clen * vrow * 2);
@@ -558,8 +572,8 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
       float nq[RPT], nk[RPT];
 #pragma unroll
       for (int pr = 0; pr < RPT; ++pr) nq[pr] = nk[pr] = 1.f;
-      if constexpr (PRO) {
-        if (p.pro & PRO_QK_L2NORM) {
+      if constexpr (PRO != 0) {
+        if (pro_step<PRO>(p, PRO_QK_L2NORM)) {
           // A token row's DK channels sit in all CG column groups: 64/RG of
           // them per wavefront (lanes RG apart) and NW wavefronts.  Reduce
           // inside the wavefront by xor shuffles, then across wavefronts in
@@ -612,7 +626,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
       for (int pr = 0; pr < RPT; ++pr) {
         unpack4<false>(rb[pr], bv[pr]);
         unpack4<!LA16>(rgd[pr], G[pr]);
-        if constexpr (!PRO) {
+        if constexpr (PRO == 0) {
 #pragma unroll
           for (int i = 0; i < EPC; ++i) G[pr][i] *= LOG2E;
         }
@@ -622,8 +636,8 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
 #pragma unroll
         for (int j = 0; j < VE / 2; ++j) {
           float w0 = __uint_as_float(rw[i][j] << 16), w1 = __uint_as_float(rw[i][j] & 0xffff0000u);
-          if constexpr (PRO) {
-            if (p.pro & PRO_GATES) {  // write gate w = sigmoid(W_w x)  (Eq. 11)
+          if constexpr (PRO != 0) {
+            if (pro_step<PRO>(p, PRO_GATES)) {  // write gate w = sigmoid(W_w x)  (Eq. 11)
               w0 = sigmoid_f(w0);
               w1 = sigmoid_f(w1);
             }
@@ -638,12 +652,12 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
       if (itn < items) fetch(nrow0, nclen, nh, 0);
 
-      if constexpr (PRO) {
+      if constexpr (PRO != 0) {
         // Gate prologue (Gated DeltaNet-2 pages, "Gate Parameterization":
         // Eq. 12 log-decay g = -exp(a) * softplus(f + delta) and Eq. 11 erase
         // gate b = b_scale * sigmoid(W_b x); q and k L2-normalised per head),
         // in fp32 on the loaded values.
-        if (p.pro & PRO_DECAY) {
+        if (pro_step<PRO>(p, PRO_DECAY)) {
           const float ea[4] = {__expf(rda.x), __expf(rda.y), __expf(rda.z), __expf(rda.w)};
           const float dl[4] = {rdb.x, rdb.y, rdb.z, rdb.w};
 #pragma unroll
@@ -652,7 +666,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
             for (int i = 0; i < EPC; ++i)  // rows past the chunk's end keep g = 0
               G[pr][i] = r0 + pr < clen ? -ea[i] * softplus_f(G[pr][i] + dl[i]) : 0.f;
         }
-        if (p.pro & PRO_GATES) {
+        if (pro_step<PRO>(p, PRO_GATES)) {
 #pragma unroll
           for (int pr = 0; pr < RPT; ++pr)
 #pragma unroll
@@ -982,7 +996,7 @@ size_t record_bytes(int dk, int dv) {
   return 0;
 }
 
-template <int DK, int DV, bool LA16, bool PRO, int MODE>
+template <int DK, int DV, bool LA16, int PRO, int MODE>
 static hipError_t launch_intra_mode(const IntraArgs& a, long long grid, hipStream_t stream) {
   typedef IntraCfg<DK, DV> Cfg;
   static std::atomic<bool> lds_set[64];
@@ -994,7 +1008,7 @@ static hipError_t launch_intra_mode(const IntraArgs& a, long long grid, hipStrea
   return hipGetLastError();
 }
 
-template <int DK, int DV, bool LA16, bool PRO>
+template <int DK, int DV, bool LA16, int PRO>
 static hipError_t launch_intra1(const IntraArgs& a, hipStream_t stream) {
   const long long items = (long long)a.chunks * a.H;
   if (items <= 0) return hipSuccess;
@@ -1007,24 +1021,31 @@ static hipError_t launch_intra1(const IntraArgs& a, hipStream_t stream) {
   const long long grid = items < cus ? items : cus;  // persistent: one workgroup per CU
   // the variants whose main loop is lightest keep the exact path in the same
   // launch; the others run it as a second launch
-  if constexpr (LA16 && !PRO) {
+  if constexpr (LA16 && PRO == 0) {
     return launch_intra_mode<DK, DV, LA16, PRO, 0>(a, grid, stream);
   } else {
     e = launch_intra_mode<DK, DV, LA16, PRO, 1>(a, grid, stream);
     if (e != hipSuccess) return e;
-    return launch_intra_mode<DK, DV, LA16, PRO, 2>(a, grid, stream);
+    // the second launch reads the flags at run time: one instantiation serves
+    // every prologue choice
+    return launch_intra_mode<DK, DV, LA16, PRO == 0 ? 0 : PRO_ANY, 2>(a, grid, stream);
   }
 }
 
 hipError_t launch_intra(const IntraArgs& a, int dk, int dv, hipStream_t stream) {
+  // the prologue variants (also for grouped value heads without a prologue
+  // step): all three steps fixed at compile time, or any choice at run time
   const bool pro = a.pro != 0 || a.grp != 1;
 #define GDR2_INTRA(DK, DV)                                                                  \
   if (dk == DK && dv == DV) {                                                               \
+    if (pro && a.pro == PRO_ALL)                                                            \
+      return a.la_bf16 ? launch_intra1<DK, DV, true, PRO_ALL>(a, stream)                    \
+                       : launch_intra1<DK, DV, false, PRO_ALL>(a, stream);                  \
     if (pro)                                                                                \
-      return a.la_bf16 ? launch_intra1<DK, DV, true, true>(a, stream)                       \
-                       : launch_intra1<DK, DV, false, true>(a, stream);                     \
-    return a.la_bf16 ? launch_intra1<DK, DV, true, false>(a, stream)                        \
-                     : launch_intra1<DK, DV, false, false>(a, stream);                      \
+      return a.la_bf16 ? launch_intra1<DK, DV, true, PRO_ANY>(a, stream)                    \
+                       : launch_intra1<DK, DV, false, PRO_ANY>(a, stream);                  \
+    return a.la_bf16 ? launch_intra1<DK, DV, true, 0>(a, stream)                            \
+                     : launch_intra1<DK, DV, false, 0>(a, stream);                          \
   }
   GDR2_INTRA(32, 32) GDR2_INTRA(32, 64) GDR2_INTRA(32, 128)
   GDR2_INTRA(64, 32) GDR2_INTRA(64, 64) GDR2_INTRA(64, 128)
