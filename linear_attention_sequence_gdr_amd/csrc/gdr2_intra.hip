@@ -192,8 +192,8 @@ __device__ __forceinline__ void strong_stage(const IntraArgs& p, long long row0,
   _Float16* SB = reinterpret_cast<_Float16*>(smem + Cfg::O_SB);
   float* part = reinterpret_cast<float*>(smem + Cfg::O_TD);
   const int tid = threadIdx.x, c = tid % DK, gr = tid / DK;
-  const int hk = PRO != 0 ? h / p.grp : h;
-  const size_t krow = (size_t)(PRO != 0 ? p.Hk : p.H) * DK;
+  const int hk = h / p.grp;  // key head of value head h (grp = 1 without grouping)
+  const size_t krow = (size_t)p.Hk * DK;
   float ea = 0.f, dl = 0.f;
   if constexpr (PRO != 0) {
     if (pro_step<PRO>(p, PRO_DECAY)) {
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
 
   const int cg = tid / RG, rg = tid % RG, r0 = rg * RPT;
   // key-side rows hold Hk heads (grouped value heads), value-side rows H
-  const size_t krow = (size_t)(PRO != 0 ? p.Hk : H) * DK, vrow = (size_t)H * DV;
+  const size_t krow = (size_t)p.Hk * DK, vrow = (size_t)H * DV;
   uint32_t koff[RPT], goff[RPT], voff[NVU];
   int vr[NVU], vc0[NVU];
 #pragma unroll
@@ -412,7 +412,7 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs p) {
   // at six points of the current item (two in phase L, then one at the start
   // of each later phase).
   auto fetch = [&](long long row0, int clen, int h, int batch) {
-    const int hk = PRO != 0 ? h / p.grp : h;  // key head of value head h
+    const int hk = h / p.grp;  // key head of value head h (grp = 1 without grouping)
     const size_t kel = (size_t)row0 * krow + (size_t)hk * DK, vel = (size_t)row0 * vrow + (size_t)h * DV;
     const int kbytes = (int)(clen * krow * 2), gbytes = (int)(clen * krow * (LA16 ? 2 : 4));
     const int vbytes = (int)(clen * vrow * 2);
@@ -1033,9 +1033,10 @@ static hipError_t launch_intra1(const IntraArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_intra(const IntraArgs& a, int dk, int dv, hipStream_t stream) {
-  // the prologue variants (also for grouped value heads without a prologue
-  // step): all three steps fixed at compile time, or any choice at run time
-  const bool pro = a.pro != 0 || a.grp != 1;
+  // the prologue variants: all three steps fixed at compile time, or any
+  // other choice read at run time; grouped value heads need no variant of
+  // their own (every variant reads key head h / grp)
+  const bool pro = a.pro != 0;
 #define GDR2_INTRA(DK, DV)                                                                  \
   if (dk == DK && dv == DV) {                                                               \
     if (pro && a.pro == PRO_ALL)                                                            \
