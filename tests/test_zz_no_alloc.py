@@ -65,6 +65,25 @@ def test_noalloc_strong_decay_items_then_plain():
     assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
 
 
+def test_noalloc_packed_split_then_unsplit():
+    """Packed sequences whose long member the device plan splits (the plan and
+    the segment maps live in the scratch), then a smaller packed call that
+    splits nothing, on the same scratch."""
+    lens = [7000, 30, 0, 2500]
+    wl = I.make_forward(1, sum(lens), 2, 128, 128, dtype=torch.bfloat16, decay_shift=-2.0, s0_std=0.1,
+                        seqlens=lens, seed=135)
+    o, S, o_ref, S_ref = both(wl)
+    assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
+    ro, rS = oracle.fwd(wl.q, wl.k, wl.v, wl.log_alpha, wl.b, wl.w, S0=wl.S0,
+                        cu_seqlens=wl.cu_seqlens.numpy())
+    assert M.bf16_excess(o, ro) <= 2e-2 and M.rms_err(S, rS) <= 2e-2
+    lens = [300, 1, 900]
+    wl = I.make_forward(1, sum(lens), 2, 128, 128, dtype=torch.bfloat16, decay_shift=-2.0, s0_std=0.1,
+                        seqlens=lens, seed=136)
+    o, S, o_ref, S_ref = both(wl)
+    assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
+
+
 def test_noalloc_refuses_oversize_before_any_launch():
     wl = I.make_forward(4, 64, 16, 128, 128, dtype=torch.bfloat16, seed=134)
     x = torch.zeros(4, 4096, 16, 128, dtype=torch.bfloat16, device="cuda")
