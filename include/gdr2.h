@@ -213,7 +213,9 @@ gdr2_status gdr2_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
  * backward keeps the intermediates its passes hand on, per (64-token chunk,
  * head), in fp32: (4 * 64 * dk + 3 * 64 * dv + 2 * 64 * 64 + 2 * dk * dv + dk)
  * * 4 bytes, rounded up to 256, per item (0.39 MB at dk = dv = 128), for
- * B * ceil(T/64) chunks (ceil(T/64) + num_seqs with packed sequences) times H.
+ * B * ceil(T/64) chunks (ceil(T/64) + num_seqs with packed sequences) times H,
+ * then from the next 256-byte boundary one int per item, which records whether
+ * its chunk's decay needs the exact-decay path.
  */
 size_t gdr2_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs);
 

@@ -103,9 +103,10 @@ Layout two_pass_layout(int B, int T, int H, int dk, int dv, int num_seqs) {
 }
 
 // Workspace of the backward: packed-sequence tables, then one fp32 block per
-// (chunk, head) item.
+// (chunk, head) item, then from the next 256-byte boundary one int per item
+// (its chunk took the exact-decay path).
 struct BwdLayoutHost {
-  size_t cbase, tab, items, total;
+  size_t cbase, tab, items, sflag, total;
   long long cap;
 };
 BwdLayoutHost bwd_layout(int B, int T, int H, int dk, int dv, int num_seqs) {
@@ -122,7 +123,9 @@ BwdLayoutHost bwd_layout(int B, int T, int H, int dk, int dv, int num_seqs) {
     l.cap = (long long)B * nc;
   }
   l.items = off;
-  l.total = off + (size_t)l.cap * (size_t)H * gdr2::bwd_item_bytes(dk, dv);
+  off += (size_t)l.cap * (size_t)H * gdr2::bwd_item_bytes(dk, dv);
+  l.sflag = align256(off);
+  l.total = l.sflag + (size_t)l.cap * (size_t)H * sizeof(int32_t);
   return l;
 }
 
@@ -282,6 +285,7 @@ gdr2_status chunk_fwd_common(const char* fn, const void* q, const void* k, const
     a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.b = b; a.w = w;
     a.S0 = S0; a.o = static_cast<float*>(o); a.ST = S_T;
     a.ws = reinterpret_cast<float*>(ws + l.items);
+    a.sflag = reinterpret_cast<int*>(ws + l.sflag);
     if (cu_seqlens) {
       int32_t* cbase = reinterpret_cast<int32_t*>(ws + l.cbase);
       int32_t* tab = reinterpret_cast<int32_t*>(ws + l.tab);
@@ -483,6 +487,7 @@ gdr2_status gdr2_chunk_bwd(const void* q, const void* k, const void* v, const vo
   a.S0 = S0; a.dST = dS_T;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dlog_alpha; a.db = db; a.dw = dw; a.dS0 = dS0;
   a.ws = reinterpret_cast<float*>(ws + l.items);
+  a.sflag = reinterpret_cast<int*>(ws + l.sflag);
   if (cu_seqlens) {
     int32_t* cbase = reinterpret_cast<int32_t*>(ws + l.cbase);
     int32_t* tab = reinterpret_cast<int32_t*>(ws + l.tab);

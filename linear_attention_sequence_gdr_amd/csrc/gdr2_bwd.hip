@@ -165,9 +165,14 @@ struct FrontCfg {
   static_assert(DK % 32 == 0 && DV % 32 == 0 && NT % DK == 0, "front pass tiling");
 };
 
-// FWD: the front pass of the fp32 forward, which needs neither G nor A later.
-template <int DK, int DV, bool BF16, bool LA16, bool FWD>
-__global__ __launch_bounds__(512) void bwd_front_kernel(BwdArgs a) {
+// One item of the front pass.  FWD: the front pass of the fp32 forward, which
+// needs neither G nor A later.  SM = 0: the main launch, whose code has no
+// exact-decay path: a strong chunk (see BWD_SLIM) is only flagged in
+// a.sflag and left for SM = 1, the launch that forms the flagged chunks with
+// the exact decay.  Keeping the exact path out of the main launch keeps its
+// registers out of the common case.
+template <int DK, int DV, bool BF16, bool LA16, bool FWD, int SM>
+__device__ __forceinline__ void front_item(const BwdArgs& a, const int item) {
   typedef BwdLayout<DK, DV> L;
   typedef FrontCfg<DK, DV> C;
   constexpr int NT = C::NT, NWV = 8, LA = C::LA, LKP = C::LKP, LM = C::LM;
@@ -176,7 +181,7 @@ __global__ __launch_bounds__(512) void bwd_front_kernel(BwdArgs a) {
   constexpr int NAA = BC * BC / 4 / NT;  // float4 of a [64][64] block per thread
   constexpr int TNK = DK / 16, NKT = DK / 32, TNV = DV / 16, NVT = DV / 32;
   constexpr int NRB = NT / DK, RPB = BC / NRB;
-  const int item = blockIdx.x, ci = item / a.H, h = item - ci * a.H;
+  const int ci = item / a.H, h = item - ci * a.H;
   long long row0;
   int clen;
   if (!bwd_locate(a, ci, row0, clen) || clen <= 0) return;
@@ -249,7 +254,12 @@ __global__ __launch_bounds__(512) void bwd_front_kernel(BwdArgs a) {
     for (int c = 0; c < 4; ++c)
       strong_t = strong_t || fabsf(sG[r * LKP + 4 * i4 + c] - sG[31 * LKP + 4 * i4 + c]) > BWD_SLIM;
   }
-  const bool strong = __syncthreads_or(strong_t) != 0;
+  const bool flagged = __syncthreads_or(strong_t) != 0;
+  if constexpr (SM == 0) {
+    if (tid == 0) a.sflag[item] = flagged ? 1 : 0;  // every item of the main launch writes its flag
+    if (flagged) return;                            // uniform: the strong launch forms this chunk
+  }
+  constexpr bool strong = SM == 1;
   float *sEP = sm + C::O_EP, *sKP = sm + C::O_KP, *sQP = sm + C::O_QP;
   f32x4 pg[NEK];  // G of this thread's units, for E in phase 5
 #pragma unroll
@@ -415,6 +425,24 @@ __global__ __launch_bounds__(512) void bwd_front_kernel(BwdArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) W[L::U + (16 * tm + 4 * g + q) * DV + 16 * tn + m] = y[q];
   }
+}
+
+// The front pass: one workgroup per item; strong chunks are flagged only.
+template <int DK, int DV, bool BF16, bool LA16, bool FWD>
+__global__ __launch_bounds__(512) void bwd_front_kernel(BwdArgs a) {
+  front_item<DK, DV, BF16, LA16, FWD, 0>(a, blockIdx.x);
+}
+
+// The strong chunks the main launch flagged, with the exact decay: one
+// workgroup per item, which leaves at once unless its item is flagged.  The
+// main launch sets the flag of every item inside the sequences; a stale flag
+// of an item outside them (a packed call's spare chunks) sends its workgroup
+// into front_item, which leaves at once too.  (A grid-stride loop here would
+// keep values live across items and spill.)
+template <int DK, int DV, bool BF16, bool LA16, bool FWD>
+__global__ __launch_bounds__(512) void bwd_front_strong_kernel(BwdArgs a) {
+  if (a.sflag[blockIdx.x] == 0) return;  // uniform
+  front_item<DK, DV, BF16, LA16, FWD, 1>(a, blockIdx.x);
 }
 
 // Register prefetch of one chunk's operands for the sequential passes
@@ -768,8 +796,11 @@ struct OutCfg {
   static_assert(DV % KC == 0 && DK % 32 == 0 && NT % DK == 0, "output pass tiling");
 };
 
-template <int DK, int DV, bool BF16>
-__global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
+// One item of the output pass.  SM = 0: the main launch, without the exact
+// decay path; it leaves the chunks the front pass flagged strong.  SM = 1:
+// a flagged chunk, with the exact decay.
+template <int DK, int DV, bool BF16, int SM>
+__device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
   typedef BwdLayout<DK, DV> L;
   typedef OutCfg<DK, DV> C;
   constexpr int NT = C::NT, NWV = C::NWV, KC = C::KC, LS = C::LS, LA = C::LA, LKP = C::LKP;
@@ -778,10 +809,14 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
   constexpr int NSK = (DK * KC / 4 + NT - 1) / NT;    // float4 of an S slice per thread
   constexpr int NEK = BC * DK / 4 / NT;               // float4 of a [64][DK] block per thread
   constexpr int NAA = BC * BC / 4 / NT;               // float4 of a [64][64] block per thread
-  const int item = blockIdx.x, ci = item / a.H, h = item - ci * a.H;
+  const int ci = item / a.H, h = item - ci * a.H;
   long long row0;
   int clen;
   if (!bwd_locate(a, ci, row0, clen) || clen <= 0) return;
+  // the front pass flagged this item's chunk strong (the same test on the
+  // same G): it is the strong launch's
+  if constexpr (SM == 0)
+    if (a.sflag[item] != 0) return;  // uniform
   extern __shared__ __align__(16) unsigned char smem_raw[];
   float* sm = reinterpret_cast<float*>(smem_raw);
   const float* W = a.ws + (size_t)item * L::FLOATS;
@@ -929,17 +964,9 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
       sDYT[i * LA + r] = y;
     }
   }
-  // a strong chunk (the front pass's test on the same values) forms its
-  // decay-weighted products exactly, with G in E''s place
-  bool strong_t = false;
-#pragma unroll
-  for (int u = 0; u < NEK; ++u) {
-    const int e = tid + NT * u, i4 = e % (DK / 4);
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      strong_t = strong_t || fabsf(pG[u][c] - sm[C::O_G31 + 4 * i4 + c]) > BWD_SLIM;
-  }
-  const bool strong = __syncthreads_or(strong_t) != 0;
+  // a strong chunk (flagged by the front pass) forms its decay-weighted
+  // products exactly, with G in E''s place
+  constexpr bool strong = SM == 1;
   // E = gamma b k and E' = e1 b k (the forms of the front pass, same order
   // of operations), e1 = exp(G - G_31)
   float* sEP = sm + C::O_EP;
@@ -1198,6 +1225,20 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
   }
 }
 
+// The output pass: one workgroup per item, the flagged chunks left out.
+template <int DK, int DV, bool BF16>
+__global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
+  out_item<DK, DV, BF16, 0>(a, blockIdx.x);
+}
+
+// The flagged chunks of the output pass, one workgroup per item as in
+// bwd_front_strong_kernel.
+template <int DK, int DV, bool BF16>
+__global__ __launch_bounds__(512) void bwd_out_strong_kernel(BwdArgs a) {
+  if (a.sflag[blockIdx.x] == 0) return;  // uniform
+  out_item<DK, DV, BF16, 1>(a, blockIdx.x);
+}
+
 #define GDR2_CK(x)                       \
   do {                                   \
     const hipError_t e_ = (x);           \
@@ -1211,27 +1252,25 @@ __global__ __launch_bounds__(512) void bwd_out_kernel(BwdArgs a) {
     GDR2_CK(lds_opt_in(reinterpret_cast<const void*>(&kernel), (bytes), done_));   \
   } while (0)
 
+template <int DK, int DV, bool BF16, bool LA16, bool FWD>
+hipError_t launch_front_t(const BwdArgs& a, dim3 gi, hipStream_t st) {
+  typedef FrontCfg<DK, DV> FC;
+  GDR2_LDS((bwd_front_kernel<DK, DV, BF16, LA16, FWD>), FC::BYTES);
+  hipLaunchKernelGGL((bwd_front_kernel<DK, DV, BF16, LA16, FWD>), gi, dim3(FC::NT), FC::BYTES, st, a);
+  GDR2_CK(hipGetLastError());
+  GDR2_LDS((bwd_front_strong_kernel<DK, DV, BF16, LA16, FWD>), FC::BYTES);
+  hipLaunchKernelGGL((bwd_front_strong_kernel<DK, DV, BF16, LA16, FWD>), gi, dim3(FC::NT), FC::BYTES, st, a);
+  return hipGetLastError();
+}
+
+// The front pass, then its strong chunks.
 template <int DK, int DV, bool FWD>
 hipError_t launch_front(const BwdArgs& a, dim3 gi, hipStream_t st) {
-  typedef FrontCfg<DK, DV> FC;
-  if (a.in_bf16) {
-    if (a.la_bf16) {
-      GDR2_LDS((bwd_front_kernel<DK, DV, true, true, FWD>), FC::BYTES);
-      hipLaunchKernelGGL((bwd_front_kernel<DK, DV, true, true, FWD>), gi, dim3(FC::NT), FC::BYTES, st, a);
-    } else {
-      GDR2_LDS((bwd_front_kernel<DK, DV, true, false, FWD>), FC::BYTES);
-      hipLaunchKernelGGL((bwd_front_kernel<DK, DV, true, false, FWD>), gi, dim3(FC::NT), FC::BYTES, st, a);
-    }
-  } else {
-    if (a.la_bf16) {
-      GDR2_LDS((bwd_front_kernel<DK, DV, false, true, FWD>), FC::BYTES);
-      hipLaunchKernelGGL((bwd_front_kernel<DK, DV, false, true, FWD>), gi, dim3(FC::NT), FC::BYTES, st, a);
-    } else {
-      GDR2_LDS((bwd_front_kernel<DK, DV, false, false, FWD>), FC::BYTES);
-      hipLaunchKernelGGL((bwd_front_kernel<DK, DV, false, false, FWD>), gi, dim3(FC::NT), FC::BYTES, st, a);
-    }
-  }
-  return hipGetLastError();
+  if (a.in_bf16)
+    return a.la_bf16 ? launch_front_t<DK, DV, true, true, FWD>(a, gi, st)
+                     : launch_front_t<DK, DV, true, false, FWD>(a, gi, st);
+  return a.la_bf16 ? launch_front_t<DK, DV, false, true, FWD>(a, gi, st)
+                   : launch_front_t<DK, DV, false, false, FWD>(a, gi, st);
 }
 
 // LDS of the sequential forward pass (FWD adds Q_g and A_qk)
@@ -1265,15 +1304,24 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     GDR2_CK(hipGetLastError());
   }
   if (items <= 0) return hipSuccess;
-  // output paths, WY gradients and the gradients themselves, one workgroup per item
+  // output paths, WY gradients and the gradients themselves, one workgroup per
+  // item, then the strong chunks
   {
     typedef OutCfg<DK, DV> OC;
     if (a.in_bf16) {
       GDR2_LDS((bwd_out_kernel<DK, DV, true>), OC::BYTES);
       hipLaunchKernelGGL((bwd_out_kernel<DK, DV, true>), gi, dim3(OC::NT), OC::BYTES, st, a);
+      GDR2_CK(hipGetLastError());
+      GDR2_LDS((bwd_out_strong_kernel<DK, DV, true>), OC::BYTES);
+      hipLaunchKernelGGL((bwd_out_strong_kernel<DK, DV, true>), gi, dim3(OC::NT), OC::BYTES, st,
+                         a);
     } else {
       GDR2_LDS((bwd_out_kernel<DK, DV, false>), OC::BYTES);
       hipLaunchKernelGGL((bwd_out_kernel<DK, DV, false>), gi, dim3(OC::NT), OC::BYTES, st, a);
+      GDR2_CK(hipGetLastError());
+      GDR2_LDS((bwd_out_strong_kernel<DK, DV, false>), OC::BYTES);
+      hipLaunchKernelGGL((bwd_out_strong_kernel<DK, DV, false>), gi, dim3(OC::NT), OC::BYTES, st,
+                         a);
     }
   }
   return hipGetLastError();

@@ -155,6 +155,7 @@ struct BwdArgs {
   float *dq, *dk, *dv, *dg, *db, *dw, *dS0;
   float *o, *ST;          // the fp32 forward's outputs (launch_fwd32); unused by the backward
   float* ws;
+  int* sflag;             // per item: its chunk took the exact-decay path (written by the front pass)
   const int32_t* tab;     // packed sequences: per chunk (row, length); else nullptr
   const int32_t* cbase;   // packed sequences: first chunk per sequence, [N+1]
   const int32_t* total;   // packed sequences: cbase + N

@@ -85,14 +85,16 @@ def test_workspace_query():
     q = G.gdr2_chunk_fwd_workspace_bytes
     a256 = lambda x: (x + 255) // 256 * 256
     # fp32 inputs: the fp32 blocks of the backward's front pass, per (chunk, head)
-    # (include/gdr2.h: gdr2_chunk_bwd_workspace_bytes), plus packed-sequence tables
+    # (include/gdr2.h: gdr2_chunk_bwd_workspace_bytes), plus packed-sequence tables,
+    # then from the next 256-byte boundary one int per item (its exact-decay flag)
     qb = G.gdr2_chunk_bwd_workspace_bytes
     for dk, dv in ((64, 64), (128, 128), (32, 128)):
         item = a256((4 * 64 * dk + 3 * 64 * dv + 2 * 64 * 64 + 2 * dk * dv + dk) * 4)
-        assert q(1, 100, 16, dk, dv, 0, G.GDR2_F32) == qb(1, 100, 16, dk, dv, 0) == 2 * 16 * item
-        assert q(2, 300, 3, dk, dv, 0, G.GDR2_F32) == 2 * 5 * 3 * item
+        assert q(1, 100, 16, dk, dv, 0, G.GDR2_F32) == qb(1, 100, 16, dk, dv, 0) == \
+            2 * 16 * item + 2 * 16 * 4
+        assert q(2, 300, 3, dk, dv, 0, G.GDR2_F32) == 2 * 5 * 3 * item + 2 * 5 * 3 * 4
         assert q(1, 100, 16, dk, dv, 64, G.GDR2_F32) == qb(1, 100, 16, dk, dv, 64) == \
-            a256(65 * 4) + a256(66 * 8) + 66 * 16 * item
+            a256(65 * 4) + a256(66 * 8) + 66 * 16 * item + 66 * 16 * 4
     # 16-bit inputs: one record per (chunk, head), plus the packed-sequence tables
     # record of the intra-chunk pass (include/gdr2.h): fp16 fragments -Y and Q_g
     # (4*dk/32 KiB each), K_tail (2*dk/16 KiB), A_qk (6 KiB), U (dv/16*4 tiles of
@@ -263,10 +265,11 @@ def test_chunk_bwd_rejects(kw, status):
 def test_chunk_bwd_workspace_query():
     q = G.gdr2_chunk_bwd_workspace_bytes
     item = lambda dk, dv: (4 * 64 * dk + 3 * 64 * dv + 2 * 64 * 64 + 2 * dk * dv + dk + 63) // 64 * 64 * 4
-    assert q(4, 4096, 16, 128, 128, 0) == 4 * 64 * 16 * item(128, 128)
-    assert q(2, 100, 3, 64, 32, 0) == 2 * 2 * 3 * item(64, 32)
     a256 = lambda x: (x + 255) // 256 * 256
-    assert q(1, 100, 2, 32, 32, 5) == a256(6 * 4) + a256(2 * 4 * 7) + 7 * 2 * item(32, 32)
+    # the fp32 blocks, then from the next 256-byte boundary one int per item
+    assert q(4, 4096, 16, 128, 128, 0) == 4 * 64 * 16 * item(128, 128) + 4 * 64 * 16 * 4
+    assert q(2, 100, 3, 64, 32, 0) == 2 * 2 * 3 * item(64, 32) + 2 * 2 * 3 * 4
+    assert q(1, 100, 2, 32, 32, 5) == a256(6 * 4) + a256(2 * 4 * 7) + 7 * 2 * item(32, 32) + 7 * 2 * 4
     assert q(1, 100, 2, 48, 32, 0) == 0
 
 
