@@ -77,6 +77,22 @@ __device__ __forceinline__ bool bwd_locate(const BwdArgs& a, int ci, long long& 
 // that needs more takes the exact path.
 constexpr float BWD_SLIM = 80.f;
 
+// e^x for the decay factors, as 2^(x log2 e) on the hardware exp2.  The
+// product x log2 e is carried as its rounded value h plus a residual l: one
+// FMA gives the rounding error of x * L2E exactly, a second adds x times the
+// part of log2 e below fp32 (L2E_LO).  Then 2^(h + l) = 2^h (1 + l ln 2) up to
+// terms in l^2, with |l| <= 2^-24 |h|.  The result is within about two ulp
+// of e^x for |x| < 88 (six instructions against fourteen for expf); results
+// below 2^-126 may flush to zero, and an overflowing 2^h stays +inf.
+__device__ __forceinline__ float exp_dec(float x) {
+  constexpr float L2E = 1.44269502162933349609375f;  // log2(e) rounded to fp32
+  constexpr float L2E_LO = 1.925963033500011e-08f;    // log2(e) - L2E
+  constexpr float LN2 = 0.693147180559945309f;
+  const float h = x * L2E;
+  const float l = fmaf(x, L2E_LO, fmaf(x, L2E, -h));
+  return __builtin_amdgcn_exp2f(h) * fmaf(l, LN2, 1.f);
+}
+
 // Exact decay-weighted chunk products for one 16x16 tile in C layout: lane
 // (m, g) gets, for q < 4, the sum over channels i of
 //     X[r + q][i] * K[c][i] * exp(G[r + q][i] - G[c][i])
@@ -97,10 +113,10 @@ __device__ __forceinline__ f32x4 decay_product(const float* X, const float* K, c
     for (int q = 0; q < 4; ++q) {
       const float4 gr = *reinterpret_cast<const float4*>(G + (r0 + q) * LD + i);
       const float4 xr = *reinterpret_cast<const float4*>(X + (r0 + q) * LD + i);
-      acc[q] = fmaf(xr.x * k4.x, __expf(gr.x - g4.x), acc[q]);
-      acc[q] = fmaf(xr.y * k4.y, __expf(gr.y - g4.y), acc[q]);
-      acc[q] = fmaf(xr.z * k4.z, __expf(gr.z - g4.z), acc[q]);
-      acc[q] = fmaf(xr.w * k4.w, __expf(gr.w - g4.w), acc[q]);
+      acc[q] = fmaf(xr.x * k4.x, exp_dec(gr.x - g4.x), acc[q]);
+      acc[q] = fmaf(xr.y * k4.y, exp_dec(gr.y - g4.y), acc[q]);
+      acc[q] = fmaf(xr.z * k4.z, exp_dec(gr.z - g4.z), acc[q]);
+      acc[q] = fmaf(xr.w * k4.w, exp_dec(gr.w - g4.w), acc[q]);
     }
   }
   return acc;
@@ -125,7 +141,7 @@ __device__ __forceinline__ f32x4 decay_tri(const float* M, const float* X, const
     const float xt = X[t * LDX + c], gt = G[t * LDX + c];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float term = M[(x0 + q) * LDM + t] * xt * __expf(ROW ? gx[q] - gt : gt - gx[q]);
+      const float term = M[(x0 + q) * LDM + t] * xt * exp_dec(ROW ? gx[q] - gt : gt - gx[q]);
       const bool in = ROW ? t <= x0 + q : t >= x0 + q;
       acc[q] = in ? acc[q] + term : acc[q];
     }
@@ -236,7 +252,7 @@ __device__ __forceinline__ void front_item(const BwdArgs& a, const int item) {
       const float G = off + run[k];
       sG[r * LKP + si] = G;
       if constexpr (!FWD) W[L::G + r * DK + si] = G;
-      if (r == BC - 1) W[L::GC + si] = expf(G);
+      if (r == BC - 1) W[L::GC + si] = exp_dec(G);
     }
   }
   __syncthreads();
@@ -270,12 +286,12 @@ __device__ __forceinline__ void front_item(const BwdArgs& a, const int item) {
     for (int c = 0; c < 4; ++c) {
       const int i = 4 * i4 + c;
       const float G = sG[o + c], G31 = sG[31 * LKP + i], GCl = sG[(BC - 1) * LKP + i];
-      const float gam = expf(G);
-      const float e1 = strong ? 1.f : expf(G - G31), e2 = strong ? 1.f : expf(G31 - G);
+      const float gam = exp_dec(G);
+      const float e1 = strong ? 1.f : exp_dec(G - G31), e2 = strong ? 1.f : exp_dec(G31 - G);
       const float qv = pq[u][c], kv = pk[u][c], bv = pb[u][c];
       pg[u][c] = G;
       QG[c] = gam * qv;
-      KT[c] = expf(GCl - G) * kv;
+      KT[c] = exp_dec(GCl - G) * kv;
       EP[c] = e1 * bv * kv;
       KP[c] = e2 * kv;
       QP[c] = e1 * qv;
@@ -401,7 +417,7 @@ __device__ __forceinline__ void front_item(const BwdArgs& a, const int item) {
     const int e = tid + NT * u, s = e / (DK / 4), i4 = e - s * (DK / 4);
     f32x4 eb;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) eb[c] = expf(pg[u][c]) * pb[u][c] * pk[u][c];
+    for (int c = 0; c < 4; ++c) eb[c] = exp_dec(pg[u][c]) * pb[u][c] * pk[u][c];
     *reinterpret_cast<f32x4*>(sEB + s * LKP + 4 * i4) = eb;
   }
 #pragma unroll
@@ -976,7 +992,7 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
     f32x4 eb, ep;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const float G = pG[u][c], gam = expf(G), e1 = expf(G - sm[C::O_G31 + 4 * i4 + c]);
+      const float G = pG[u][c], gam = exp_dec(G), e1 = exp_dec(G - sm[C::O_G31 + 4 * i4 + c]);
       eb[c] = gam * pB[u][c] * pK[u][c];
       ep[c] = strong ? G : e1 * pB[u][c] * pK[u][c];
     }
@@ -1031,8 +1047,8 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float G = pG[u][c], G31 = sm[C::O_G31 + 4 * i4 + c];
-      qp[c] = strong ? pQ[u][c] : expf(G - G31) * pQ[u][c];
-      kp[c] = strong ? pK[u][c] : expf(G31 - G) * pK[u][c];
+      qp[c] = strong ? pQ[u][c] : exp_dec(G - G31) * pQ[u][c];
+      kp[c] = strong ? pK[u][c] : exp_dec(G31 - G) * pK[u][c];
     }
     *reinterpret_cast<f32x4*>(sQP + s * LKP + 4 * i4) = qp;
     *reinterpret_cast<f32x4*>(sKP + s * LKP + 4 * i4) = kp;
@@ -1157,10 +1173,10 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
       const int r = 16 * tm + 4 * g + q;
       const bool in = r < clen;
       const float qv = in ? fq[u][q] : 0.f, kv = in ? fk[u][q] : 0.f, bv = in ? fb[u][q] : 0.f;
-      const float G = fG[u][q], gam = expf(G);
+      const float G = fG[u][q], gam = exp_dec(G);
       // a strong chunk's products carry the whole decay already
-      const float e1 = strong ? 1.f : expf(G - sG31[i]), e2 = strong ? 1.f : expf(sG31[i] - G);
-      const float ktail = expf(sGCL[i] - G);
+      const float e1 = strong ? 1.f : exp_dec(G - sG31[i]), e2 = strong ? 1.f : exp_dec(sG31[i] - G);
+      const float ktail = exp_dec(sGCL[i] - G);
       // off the diagonal of dA_qk, then its diagonal entry (decay 1)
       const float dqo = aQ[u][q] * gam + aP4[u][q] * e1;
       const float dkbo = (aP2[u][q] + aP3[u][q]) * e2;    // dK_bar / gamma
