@@ -73,6 +73,19 @@ __device__ __forceinline__ bool bwd_locate(const BwdArgs& a, int ci, long long& 
   return true;
 }
 
+// Two or three independent fp32 MFMA accumulator chains advanced by one
+// K = 4 step each, in one place so that their issue interleaves.
+__device__ __forceinline__ void mfma2(f32x4& c0, float a0, float b0, f32x4& c1, float a1, float b1) {
+  c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, c0, 0, 0, 0);
+  c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, c1, 0, 0, 0);
+}
+__device__ __forceinline__ void mfma3(f32x4& c0, float a0, float b0, f32x4& c1, float a1, float b1, f32x4& c2,
+                                      float a2, float b2) {
+  c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, c0, 0, 0, 0);
+  c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, c1, 0, 0, 0);
+  c2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, b2, c2, 0, 0, 0);
+}
+
 // Factors centred on one row stay inside [e^-SLIM, e^SLIM] (nats); a chunk
 // that needs more takes the exact path.
 constexpr float BWD_SLIM = 80.f;
@@ -923,18 +936,54 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
     if (tid < DK)
 #pragma unroll 8
       for (int c = 0; c < KC; ++c) rs = fmaf(sDS[tid * LS + c], sS[tid * LS + c], rs);
+    {
+      // aQ += dO S'^T, aY += dR S'^T, aK += R dS'^T over this slice: the
+      // wavefront's column block tn is the same for every u, so its S' and
+      // dS' fragments are read once; per K step the three products run as
+      // independent accumulator chains, interleaved (the same K order per
+      // tile as one chain at a time)
+      const int tn = wv % TNK;
+      float4 fS[KC / 16], fD[KC / 16];
 #pragma unroll
-    for (int u = 0; u < NKT; ++u) {
-      const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
-      aQ[u] = mma_lds<float, KC>(aQ[u], sO + 16 * tm * LS, LS, sS + 16 * tn * LS, LS);
-      aY[u] = mma_lds<float, KC>(aY[u], sDR + 16 * tm * LS, LS, sS + 16 * tn * LS, LS);
-      aK[u] = mma_lds<float, KC>(aK[u], sR + 16 * tm * LS, LS, sDS + 16 * tn * LS, LS);
+      for (int k = 0; k < KC / 16; ++k) {
+        fS[k] = *reinterpret_cast<const float4*>(sS + (16 * tn + m) * LS + 16 * k + 4 * g);
+        fD[k] = *reinterpret_cast<const float4*>(sDS + (16 * tn + m) * LS + 16 * k + 4 * g);
+      }
+#pragma unroll
+      for (int u = 0; u < NKT; ++u) {
+        const int ro = (16 * ((wv + NWV * u) / TNK) + m) * LS + 4 * g;
+#pragma unroll
+        for (int k = 0; k < KC / 16; ++k) {
+          const float4 o = *reinterpret_cast<const float4*>(sO + ro + 16 * k);
+          const float4 d = *reinterpret_cast<const float4*>(sDR + ro + 16 * k);
+          const float4 r = *reinterpret_cast<const float4*>(sR + ro + 16 * k);
+          mfma3(aQ[u], o.x, fS[k].x, aY[u], d.x, fS[k].x, aK[u], r.x, fD[k].x);
+          mfma3(aQ[u], o.y, fS[k].y, aY[u], d.y, fS[k].y, aK[u], r.y, fD[k].y);
+          mfma3(aQ[u], o.z, fS[k].z, aY[u], d.z, fS[k].z, aK[u], r.z, fD[k].z);
+          mfma3(aQ[u], o.w, fS[k].w, aY[u], d.w, fS[k].w, aK[u], r.w, fD[k].w);
+        }
+      }
     }
 #pragma unroll
     for (int u = 0; u < NCT; ++u) {
+      // aAQ += dO R^T (lower tiles) and aA += dR Z^T, interleaved likewise
       const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
-      if (tn <= tm) aAQ[u] = mma_lds<float, KC>(aAQ[u], sO + 16 * tm * LS, LS, sR + 16 * tn * LS, LS);
-      aA[u] = mma_lds<float, KC>(aA[u], sDR + 16 * tm * LS, LS, sZ + 16 * tn * LS, LS);
+      const int ra = (16 * tm + m) * LS + 4 * g, rb = (16 * tn + m) * LS + 4 * g;
+      if (tn <= tm) {
+#pragma unroll
+        for (int k = 0; k < KC / 16; ++k) {
+          const float4 o = *reinterpret_cast<const float4*>(sO + ra + 16 * k);
+          const float4 r = *reinterpret_cast<const float4*>(sR + rb + 16 * k);
+          const float4 d = *reinterpret_cast<const float4*>(sDR + ra + 16 * k);
+          const float4 z = *reinterpret_cast<const float4*>(sZ + rb + 16 * k);
+          mfma2(aAQ[u], o.x, r.x, aA[u], d.x, z.x);
+          mfma2(aAQ[u], o.y, r.y, aA[u], d.y, z.y);
+          mfma2(aAQ[u], o.z, r.z, aA[u], d.z, z.z);
+          mfma2(aAQ[u], o.w, r.w, aA[u], d.w, z.w);
+        }
+      } else {
+        aA[u] = mma_lds<float, KC>(aA[u], sDR + 16 * tm * LS, LS, sZ + 16 * tn * LS, LS);
+      }
     }
     {  // dZ = A^T dR over this slice's 32 value channels: one [16][16] tile per wavefront
       const int tm = wv >> 1, tn = wv & 1;
