@@ -86,6 +86,41 @@ __device__ __forceinline__ void mfma3(f32x4& c0, float a0, float b0, f32x4& c1, 
   c2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, b2, c2, 0, 0, 0);
 }
 
+// acc = A[16 x K] * B[K x 16], both operands K-contiguous in LDS (A row m at
+// A + m*lda, B column n at Bt + n*ldb), with the K = 16 blocks dealt in turn
+// to NA accumulators, independent chains summed at the end: a chain NA times
+// shorter for a product that has no other chain beside it.
+template <int K, int NA>
+__device__ __forceinline__ f32x4 mma_lds_split(const float* A, int lda, const float* Bt, int ldb) {
+  static_assert(K % (16 * NA) == 0, "K blocks per accumulator");
+  const int m = lane_id() & 15, g = lane_id() >> 4;
+  const float* a = A + m * lda + 4 * g;
+  const float* b = Bt + m * ldb + 4 * g;
+  f32x4 c[NA];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) c[j] = zero4();
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 16 * NA) {
+    float4 av[NA], bv[NA];
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      av[j] = *reinterpret_cast<const float4*>(a + k0 + 16 * j);
+      bv[j] = *reinterpret_cast<const float4*>(b + k0 + 16 * j);
+    }
+#pragma unroll
+    for (int j = 0; j < NA; ++j) c[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j].x, bv[j].x, c[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NA; ++j) c[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j].y, bv[j].y, c[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NA; ++j) c[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j].z, bv[j].z, c[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NA; ++j) c[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j].w, bv[j].w, c[j], 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 1; j < NA; ++j) c[0] += c[j];
+  return c[0];
+}
+
 // Factors centred on one row stay inside [e^-SLIM, e^SLIM] (nats); a chunk
 // that needs more takes the exact path.
 constexpr float BWD_SLIM = 80.f;
@@ -615,7 +650,11 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
     f32x4 ao = zero4();
     for (int t = wv; t < (BC / 16) * (DVB / 16); t += SNT / 64) {
       const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
-      const f32x4 acc = mma_lds<float, DK>(zero4(), sY + 16 * tm * LK, LK, sST + 16 * tn * LK, LK);
+      // one tile per wavefront: Y S as two chains over alternate K blocks
+      // (the forward, at its register limit with Q_g and A_qk, keeps one)
+      f32x4 acc;
+      if constexpr (FWD) acc = mma_lds<float, DK>(zero4(), sY + 16 * tm * LK, LK, sST + 16 * tn * LK, LK);
+      else acc = mma_lds_split<DK, 2>(sY + 16 * tm * LK, LK, sST + 16 * tn * LK, LK);
       if constexpr (FWD) ao = mma_lds<float, DK>(zero4(), sQg + 16 * tm * LK, LK, sST + 16 * tn * LK, LK);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -641,14 +680,39 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
       }
     }
     // S <- Diag(gamma_C) S + K_tail^T R  [DK][DVB]; each lane owns its entries
-    for (int t = wv; t < (DK / 16) * (DVB / 16); t += SNT / 64) {
-      const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
-      // K_tail^T as the left factor: K_tail read K-major from its row-major block
-      const f32x4 acc = mma_lds_f32<BC, true, false>(zero4(), sKt + 16 * tm, LK, sRT + 16 * tn * LC, LC);
+    constexpr int NSU = (DK / 16) * (DVB / 16);
+    if constexpr (!FWD && NSU == 2 * (SNT / 64)) {
+      // two tiles per wavefront, t = wv and wv + 8, in one column block tn:
+      // one R^T fragment per K step serves both chains, interleaved (each
+      // in ascending K, as one chain at a time)
+      const int tn = wv % (DVB / 16), tm0 = wv / (DVB / 16), tm1 = tm0 + (SNT / 64) / (DVB / 16);
+      f32x4 c0 = zero4(), c1 = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < BC; k0 += 16) {
+        const float4 rb = *reinterpret_cast<const float4*>(sRT + (16 * tn + m) * LC + k0 + 4 * g);
+        const float* x0 = sKt + (k0 + 4 * g) * LK + 16 * tm0 + m;  // K_tail read K-major
+        const float* x1 = x0 + 16 * (tm1 - tm0);
+        mfma2(c0, x0[0], rb.x, c1, x1[0], rb.x);
+        mfma2(c0, x0[LK], rb.y, c1, x1[LK], rb.y);
+        mfma2(c0, x0[2 * LK], rb.z, c1, x1[2 * LK], rb.z);
+        mfma2(c0, x0[3 * LK], rb.w, c1, x1[3 * LK], rb.w);
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int i = 16 * tm + 4 * g + q, j = 16 * tn + m;
-        sST[j * LK + i] = sGC[i] * sST[j * LK + i] + acc[q];
+        const int i0 = 16 * tm0 + 4 * g + q, i1 = 16 * tm1 + 4 * g + q, j = 16 * tn + m;
+        sST[j * LK + i0] = sGC[i0] * sST[j * LK + i0] + c0[q];
+        sST[j * LK + i1] = sGC[i1] * sST[j * LK + i1] + c1[q];
+      }
+    } else {
+      for (int t = wv; t < NSU; t += SNT / 64) {
+        const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
+        // K_tail^T as the left factor: K_tail read K-major from its row-major block
+        const f32x4 acc = mma_lds_f32<BC, true, false>(zero4(), sKt + 16 * tm, LK, sRT + 16 * tn * LC, LC);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = 16 * tm + 4 * g + q, j = 16 * tn + m;
+          sST[j * LK + i] = sGC[i] * sST[j * LK + i] + acc[q];
+        }
       }
     }
     __syncthreads();
@@ -731,8 +795,10 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
     for (int t = wv; t < (BC / 16) * (DVB / 16); t += SNT / 64) {
       const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
       // A_qk^T and dO both read K-major from their row-major blocks
+      // (the two products as separate chains, the second over alternate K
+      // blocks, summed at the end)
       f32x4 acc = mma_lds_f32<BC, true, true>(zero4(), sAqk + 16 * tm, LC, sdO + 16 * tn, LV);
-      acc = mma_lds<float, DK>(acc, sKt + 16 * tm * LK, LK, sdST + 16 * tn * LK, LK);
+      acc += mma_lds_split<DK, 2>(sKt + 16 * tm * LK, LK, sdST + 16 * tn * LK, LK);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = 16 * tm + 4 * g + q, j = 16 * tn + m;
@@ -742,14 +808,44 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
     }
     __syncthreads();
     // dS <- Q_g^T dO + Diag(gamma_C) dS' - Y^T dR  [DK][DVB]; each lane owns its entries
-    for (int t = wv; t < (DK / 16) * (DVB / 16); t += SNT / 64) {
-      const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
-      const f32x4 acc = mma_lds_f32<BC, true, true>(zero4(), sQg + 16 * tm, LK, sdO + 16 * tn, LV);
-      const f32x4 acy = mma_lds_f32<BC, true, false>(zero4(), sY + 16 * tm, LK, sdRT + 16 * tn * LC, LC);
+    constexpr int NSU = (DK / 16) * (DVB / 16);
+    if constexpr (NSU == 2 * (SNT / 64)) {
+      // two tiles per wavefront (t = wv and wv + 8) in one column block tn:
+      // the dO and dR^T fragments of a K step serve four chains, interleaved
+      // (each in ascending K, as one chain at a time)
+      const int tn = wv % (DVB / 16), tm0 = wv / (DVB / 16), tm1 = tm0 + (SNT / 64) / (DVB / 16);
+      f32x4 q0 = zero4(), q1 = zero4(), y0 = zero4(), y1 = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < BC; k0 += 16) {
+        const float* o = sdO + (k0 + 4 * g) * LV + 16 * tn + m;  // dO read K-major
+        const float4 rb = *reinterpret_cast<const float4*>(sdRT + (16 * tn + m) * LC + k0 + 4 * g);
+        const float* xq = sQg + (k0 + 4 * g) * LK + 16 * tm0 + m;  // Q_g, Y read K-major
+        const float* xy = sY + (k0 + 4 * g) * LK + 16 * tm0 + m;
+        const int d1 = 16 * (tm1 - tm0);
+        const float ob[4] = {o[0], o[LV], o[2 * LV], o[3 * LV]};
+        const float rv[4] = {rb.x, rb.y, rb.z, rb.w};
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          mfma2(q0, xq[qq * LK], ob[qq], q1, xq[qq * LK + d1], ob[qq]);
+          mfma2(y0, xy[qq * LK], rv[qq], y1, xy[qq * LK + d1], rv[qq]);
+        }
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int i = 16 * tm + 4 * g + q, j = 16 * tn + m;
-        sdST[j * LK + i] = acc[q] + sGC[i] * sdST[j * LK + i] - acy[q];
+        const int i0 = 16 * tm0 + 4 * g + q, i1 = 16 * tm1 + 4 * g + q, j = 16 * tn + m;
+        sdST[j * LK + i0] = q0[q] + sGC[i0] * sdST[j * LK + i0] - y0[q];
+        sdST[j * LK + i1] = q1[q] + sGC[i1] * sdST[j * LK + i1] - y1[q];
+      }
+    } else {
+      for (int t = wv; t < NSU; t += SNT / 64) {
+        const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
+        const f32x4 acc = mma_lds_f32<BC, true, true>(zero4(), sQg + 16 * tm, LK, sdO + 16 * tn, LV);
+        const f32x4 acy = mma_lds_f32<BC, true, false>(zero4(), sY + 16 * tm, LK, sdRT + 16 * tn * LC, LC);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = 16 * tm + 4 * g + q, j = 16 * tn + m;
+          sdST[j * LK + i] = acc[q] + sGC[i] * sdST[j * LK + i] - acy[q];
+        }
       }
     }
     __syncthreads();
