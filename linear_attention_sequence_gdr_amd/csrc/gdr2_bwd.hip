@@ -642,9 +642,6 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
-    // the chunk after next into the registers just stored (near the end the
-    // current chunk is reloaded instead: no branch)
-    sf_load<DK, DV, NK4, NV4, NC4, FWD>(a, ci + 2 < c1 ? ci + 2 : ci, h, jb, tid, ry, rk, ru, rg, rq, ra);
     // R = U - Y S  [BC][DVB], kept for the output paths as well; the forward
     // also forms Q_g S (same tile, from the state entering the chunk)
     f32x4 ao = zero4();
@@ -679,6 +676,10 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
         if (r < clen) a.o[(size_t)(row0 + r) * a.H * DV + (size_t)h * DV + jb * DVB + 16 * tn + m] = ao[q];
       }
     }
+    // the chunk after next into the registers stored above (near the end the
+    // current chunk is reloaded instead: no branch); issued here, after R,
+    // so that R's products start at once
+    sf_load<DK, DV, NK4, NV4, NC4, FWD>(a, ci + 2 < c1 ? ci + 2 : ci, h, jb, tid, ry, rk, ru, rg, rq, ra);
     // S <- Diag(gamma_C) S + K_tail^T R  [DK][DVB]; each lane owns its entries
     constexpr int NSU = (DK / 16) * (DVB / 16);
     if constexpr (!FWD && NSU == 2 * (SNT / 64)) {
@@ -789,8 +790,6 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
       W[L::DSP + (size_t)i * DV + jb * DVB + j] = sdST[j * LK + i];
     }
     __syncthreads();
-    // the previous chunk (the last iteration reloads the current one: no branch)
-    sb_load<DK, DV, NK4, NV4, NC4, BF16>(a, ci - 1 >= c0 ? ci - 1 : ci, h, jb, tid, rq, rk, ry, ra, ro, rg);
     // dR = A_qk^T dO + K_tail dS'  [BC][DVB]
     for (int t = wv; t < (BC / 16) * (DVB / 16); t += SNT / 64) {
       const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
@@ -807,6 +806,10 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
+    // the previous chunk into the registers stored above (the last iteration
+    // reloads the current one: no branch); issued here, after dR, so that
+    // dR's products start at once
+    sb_load<DK, DV, NK4, NV4, NC4, BF16>(a, ci - 1 >= c0 ? ci - 1 : ci, h, jb, tid, rq, rk, ry, ra, ro, rg);
     // dS <- Q_g^T dO + Diag(gamma_C) dS' - Y^T dR  [DK][DVB]; each lane owns its entries
     constexpr int NSU = (DK / 16) * (DVB / 16);
     if constexpr (NSU == 2 * (SNT / 64)) {
