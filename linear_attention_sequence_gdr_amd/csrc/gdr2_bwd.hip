@@ -1031,7 +1031,6 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
       }
     }
     __syncthreads();
-    if (sl + 1 < NS) slice_load(j0 + KC);
     if (tid < DK)
 #pragma unroll 8
       for (int c = 0; c < KC; ++c) rs = fmaf(sDS[tid * LS + c], sS[tid * LS + c], rs);
@@ -1063,6 +1062,9 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
         }
       }
     }
+    // the next slice into the registers stored above, issued after the first
+    // products so that they start at once
+    if (sl + 1 < NS) slice_load(j0 + KC);
 #pragma unroll
     for (int u = 0; u < NCT; ++u) {
       // aAQ += dO R^T (lower tiles) and aA += dR Z^T, interleaved likewise
