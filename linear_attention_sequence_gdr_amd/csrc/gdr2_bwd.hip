@@ -211,6 +211,45 @@ __device__ __forceinline__ f32x4 decay_tri(const float* M, const float* X, const
 //            A_ij = -A_ii sum_{k=j}^{i-1} T_ik A_kj;
 //   phase 5  Y = A E and U = A Z (Z = w * v) on MFMA, A to the workspace.
 // Rows past the end of a sequence read a clamped (valid) row and are zeroed.
+// X = A B over the 64 rows of a chunk: A lower triangular [64][64] and B
+// [64][16 TN], both row-major in LDS (strides LA, LB), B read K-major.  The
+// NU tiles of one wavefront (t = wv + 8u: row tile t / TN, column tile
+// t % TN, the same for every u since TN divides 8) run together: at each K
+// step one B fragment serves every tile whose range still runs (row tile tm
+// needs K < 16 (tm + 1)), and each tile accumulates in ascending K.  X goes
+// to global memory with row stride ldx.
+template <int NU, int TN, int LA, int LB>
+__device__ __forceinline__ void tri_rows(const float* sA, const float* sB, int wv, int m, int g, float* X,
+                                         int ldx) {
+  static_assert(8 % TN == 0, "the column tile is the same for every u");
+  const int tn = wv % TN;
+  f32x4 acc[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) acc[u] = zero4();
+#pragma unroll
+  for (int k0 = 0; k0 < BC; k0 += 16) {
+    const float* bp = sB + (k0 + 4 * g) * LB + 16 * tn + m;  // B read K-major
+    const float b0 = bp[0], b1 = bp[LB], b2 = bp[2 * LB], b3 = bp[3 * LB];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int tm = (wv + 8 * u) / TN;
+      if (k0 < 16 * (tm + 1)) {  // uniform
+        const float4 x = *reinterpret_cast<const float4*>(sA + (16 * tm + m) * LA + k0 + 4 * g);
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.x, b0, acc[u], 0, 0, 0);
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.y, b1, acc[u], 0, 0, 0);
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.z, b2, acc[u], 0, 0, 0);
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.w, b3, acc[u], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int tm = (wv + 8 * u) / TN;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) X[(size_t)(16 * tm + 4 * g + q) * ldx + 16 * tn + m] = acc[u][q];
+  }
+}
+
 template <int DK, int DV>
 struct FrontCfg {
   static constexpr int NT = 512, LA = BC + 4, LKP = DK + 4, LM = 20;
@@ -368,37 +407,78 @@ __device__ __forceinline__ void front_item(const BwdArgs& a, const int item) {
   __syncthreads();
 
   // ---- phase 3 ----
+  // T and A_qk are lower triangular: only the ten 16x16 tiles on and below
+  // the diagonal are formed.  Tile p (row-wise, p < 10) goes to wavefront
+  // p % 8, so that the two wavefronts of each SIMD (w and w + 4) share at
+  // most three of them; the six tiles above the diagonal are zero.
+  const auto low_tile = [](int p, int& tm, int& tn) {
+    tm = (p >= 1) + (p >= 3) + (p >= 6);
+    tn = p - tm * (tm + 1) / 2;
+  };
   f32x4 aT[2], aQ[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
-    if (tn <= tm) {
+    const int p = wv + NWV * u;
+    aT[u] = aQ[u] = zero4();
+    if (p < 10) {  // uniform
+      int tm, tn;
+      low_tile(p, tm, tn);
       if (strong) {
         aT[u] = decay_product<DK, LKP>(sEP, sKP, sG, 16 * tm + 4 * g, 16 * tn + m);
         aQ[u] = decay_product<DK, LKP>(sQP, sKP, sG, 16 * tm + 4 * g, 16 * tn + m);
       } else {
-        aT[u] = mma_lds<float, DK>(zero4(), sEP + 16 * tm * LKP, LKP, sKP + 16 * tn * LKP, LKP);
-        aQ[u] = mma_lds<float, DK>(zero4(), sQP + 16 * tm * LKP, LKP, sKP + 16 * tn * LKP, LKP);
-      }
-    } else {
-      aT[u] = aQ[u] = zero4();
-    }
+        // the two products share K''s fragments: two chains, interleaved
+        const float* e = sEP + (16 * tm + m) * LKP + 4 * g;
+        const float* qp = sQP + (16 * tm + m) * LKP + 4 * g;
+        const float* kp = sKP + (16 * tn + m) * LKP + 4 * g;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = 16 * tm + 4 * g + q, c = 16 * tn + m;
-      W[L::AQK + r * BC + c] = c <= r ? aQ[u][q] : 0.f;
+        for (int k0 = 0; k0 < DK; k0 += 16) {
+          const float4 x = *reinterpret_cast<const float4*>(e + k0);
+          const float4 y = *reinterpret_cast<const float4*>(qp + k0);
+          const float4 z = *reinterpret_cast<const float4*>(kp + k0);
+          mfma2(aT[u], x.x, z.x, aQ[u], y.x, z.x);
+          mfma2(aT[u], x.y, z.y, aQ[u], y.y, z.y);
+          mfma2(aT[u], x.z, z.z, aQ[u], y.z, z.z);
+          mfma2(aT[u], x.w, z.w, aQ[u], y.w, z.w);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 16 * tm + 4 * g + q, c = 16 * tn + m;
+        W[L::AQK + r * BC + c] = c <= r ? aQ[u][q] : 0.f;
+      }
     }
+  }
+  const auto up_tile = [](int p, int& tm, int& tn) {  // p < 6, row-wise above the diagonal
+    tm = (p >= 3) + (p >= 5);
+    tn = p - (tm == 0 ? 0 : (tm == 1 ? 3 : 5)) + tm + 1;
+  };
+  if (wv >= 2) {  // the upper tiles of A_qk, one per wavefront 2-7
+    int tm, tn;
+    up_tile(wv - 2, tm, tn);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) W[L::AQK + (16 * tm + 4 * g + q) * BC + 16 * tn + m] = 0.f;
   }
   __syncthreads();
   float *sT = sm + C::O_T, *sA = sm + C::O_A, *sAT = sm + C::O_AT;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
+    const int p = wv + NWV * u;
+    if (p < 10) {
+      int tm, tn;
+      low_tile(p, tm, tn);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = 16 * tm + 4 * g + q, c = 16 * tn + m;
-      sT[r * LA + c] = c < r ? aT[u][q] : 0.f;
+      for (int q = 0; q < 4; ++q) {
+        const int r = 16 * tm + 4 * g + q, c = 16 * tn + m;
+        sT[r * LA + c] = c < r ? aT[u][q] : 0.f;
+      }
     }
+  }
+  if (wv >= 2) {
+    int tm, tn;
+    up_tile(wv - 2, tm, tn);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sT[(16 * tm + 4 * g + q) * LA + 16 * tn + m] = 0.f;
   }
   // A is lower triangular: zero its six blocks above the diagonal (and those of A^T)
   for (int e = tid; e < 6 * 256; e += NT) {
@@ -475,20 +555,12 @@ __device__ __forceinline__ void front_item(const BwdArgs& a, const int item) {
   }
   __syncthreads();
   // A is lower triangular: row block tm needs the first 16 (tm + 1) columns only
-#pragma unroll
-  for (int u = 0; u < NKT; ++u) {
-    const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
-    const f32x4 y = mma_lds_f32<BC, false, true>(zero4(), sA + 16 * tm * LA, LA, sEB + 16 * tn, LKP, 16 * (tm + 1));
-#pragma unroll
-    for (int q = 0; q < 4; ++q) W[L::Y_ + (16 * tm + 4 * g + q) * DK + 16 * tn + m] = y[q];
-  }
-#pragma unroll
-  for (int u = 0; u < NVT; ++u) {
-    const int t = wv + NWV * u, tm = t / TNV, tn = t - tm * TNV;
-    const f32x4 y = mma_lds_f32<BC, false, true>(zero4(), sA + 16 * tm * LA, LA, sZ + 16 * tn, C::LZ, 16 * (tm + 1));
-#pragma unroll
-    for (int q = 0; q < 4; ++q) W[L::U + (16 * tm + 4 * g + q) * DV + 16 * tn + m] = y[q];
-  }
+  // Y = A E and U = A Z: a wavefront's tiles (t = wv + 8u) share the column
+  // block of E (of Z), so at each K step one fragment of it serves every
+  // tile whose range (A is lower triangular: K < 16 (tm + 1)) still runs;
+  // each tile accumulates in ascending K
+  tri_rows<NKT, TNK, LA, LKP>(sA, sEB, wv, m, g, W + L::Y_, DK);
+  tri_rows<NVT, TNV, LA, C::LZ>(sA, sZ, wv, m, g, W + L::U, DV);
 }
 
 // The front pass: one workgroup per item; strong chunks are flagged only.
