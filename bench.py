@@ -558,6 +558,7 @@ def main():
     wsb = torch.empty(G.gdr2_chunk_bwd_workspace_bytes(B, T, H, dk, dv, 0), dtype=torch.uint8, device=dev)
     bwd = lambda: G.gdr2_chunk_bwd(*ins, dOb, None, dSTb, workspace=wsb)
     bwd_steps = max(1, min(args.steps, 10))
+    settle(bwd, torch, 0.25)
     bwms = time_events(bwd, bwd_steps, 3, torch)
     # algorithmic bytes: q, k, log_alpha, b, v, w, dO read (bf16), dS_T read and dS0
     # written (fp32), six fp32 input gradients written
