@@ -73,17 +73,11 @@ __device__ __forceinline__ bool bwd_locate(const BwdArgs& a, int ci, long long& 
   return true;
 }
 
-// Two or three independent fp32 MFMA accumulator chains advanced by one
-// K = 4 step each, in one place so that their issue interleaves.
+// Two independent fp32 MFMA accumulator chains advanced by one K = 4 step
+// each, in one place so that their issue interleaves.
 __device__ __forceinline__ void mfma2(f32x4& c0, float a0, float b0, f32x4& c1, float a1, float b1) {
   c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, c0, 0, 0, 0);
   c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, c1, 0, 0, 0);
-}
-__device__ __forceinline__ void mfma3(f32x4& c0, float a0, float b0, f32x4& c1, float a1, float b1, f32x4& c2,
-                                      float a2, float b2) {
-  c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, c0, 0, 0, 0);
-  c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, c1, 0, 0, 0);
-  c2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, b2, c2, 0, 0, 0);
 }
 
 // acc = A[16 x K] * B[K x 16], both operands K-contiguous in LDS (A row m at
@@ -806,6 +800,190 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
   }
 }
 
+// LDS plan of bwd_state_fwd3_kernel (byte offsets).  The fp32 state S^T is
+// the master copy; its bf16 hi/lo halves, those of Y, K_tail and R^T feed the
+// products.  Row pitches keep the 16-lane groups' reads on distinct banks:
+// DK + 8 and BC + 8 halves for rows read along K, DK + 16 for K_tail, which
+// is read down its columns by the transposing read.
+template <int DK>
+struct StateF3Cfg {
+  static constexpr int LK = DK + 4, LV = DVB + 4;  // fp32 S^T, U
+  static constexpr int LSB = DK + 8, LTB = DK + 16, LRB = BC + 8;
+  static constexpr size_t O_ST = 0;
+  static constexpr size_t O_SH = O_ST + (size_t)DVB * LK * 4, O_SL = O_SH + (size_t)DVB * LSB * 2;
+  static constexpr size_t O_YH = O_SL + (size_t)DVB * LSB * 2, O_YL = O_YH + (size_t)BC * LSB * 2;
+  static constexpr size_t O_KH = O_YL + (size_t)BC * LSB * 2, O_KL = O_KH + (size_t)BC * LTB * 2;
+  static constexpr size_t O_RH = O_KL + (size_t)BC * LTB * 2, O_RL = O_RH + (size_t)DVB * LRB * 2;
+  static constexpr size_t O_U = O_RL + (size_t)DVB * LRB * 2;
+  static constexpr size_t O_GC = O_U + (size_t)BC * LV * 4;
+  static constexpr size_t BYTES = O_GC + (size_t)DK * 4;
+  static_assert(BYTES <= 160 * 1024, "LDS budget exceeded");
+  static_assert(O_SH % 16 == 0 && O_YH % 16 == 0 && O_KH % 16 == 0 && O_RH % 16 == 0 &&
+                    O_U % 16 == 0 && O_GC % 16 == 0,
+                "16-byte aligned regions");
+};
+
+// ---- sequential state pass of the backward, products as three bf16 products ----------
+// The same pass as bwd_state_fwd_kernel<.., false> (the state entering every
+// chunk and R = U - Y S, saved for the output paths), with R = U - Y S and
+// S <- Diag(gamma_C) S + K_tail^T R on 16x16x32 bf16 MFMA over hi/lo halves
+// (mma3x): the chunk step's dependent chain is twelve instructions per tile
+// instead of 32 fp32 ones.  Y and K_tail are split as they are staged, R where
+// it is formed and S where the update writes it; the fp32 S stays the master
+// copy that the update scales and the workspace receives.
+template <int DK, int DV>
+__global__ __launch_bounds__(SNT, 1) void bwd_state_fwd3_kernel(BwdArgs a) {
+  typedef BwdLayout<DK, DV> L;
+  typedef StateF3Cfg<DK> C;
+  constexpr int NB = DV / DVB, LK = C::LK, LV = C::LV, LSB = C::LSB, LTB = C::LTB, LRB = C::LRB;
+  constexpr int NK4 = BC * DK / 4 / SNT;   // float4 per thread of a [BC][DK] block
+  constexpr int NV4 = BC * DVB / 4 / SNT;  // float4 per thread of a [BC][DVB] block
+  constexpr int NKB = DK / 32;             // K = 32 blocks of Y S
+  static_assert(NK4 >= 1 && NV4 >= 1, "state pass tiling");
+  static_assert((BC / 16) * (DVB / 16) == SNT / 64, "one R tile per wavefront");
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* sST = reinterpret_cast<float*>(smem + C::O_ST);  // [DVB][LK] fp32 S^T
+  __bf16* sSh = reinterpret_cast<__bf16*>(smem + C::O_SH);  // [DVB][LSB] S^T halves
+  __bf16* sSl = reinterpret_cast<__bf16*>(smem + C::O_SL);
+  __bf16* sYh = reinterpret_cast<__bf16*>(smem + C::O_YH);  // [BC][LSB] Y halves
+  __bf16* sYl = reinterpret_cast<__bf16*>(smem + C::O_YL);
+  __bf16* sKh = reinterpret_cast<__bf16*>(smem + C::O_KH);  // [BC][LTB] K_tail halves
+  __bf16* sKl = reinterpret_cast<__bf16*>(smem + C::O_KL);
+  __bf16* sRh = reinterpret_cast<__bf16*>(smem + C::O_RH);  // [DVB][LRB] R^T halves
+  __bf16* sRl = reinterpret_cast<__bf16*>(smem + C::O_RL);
+  float* sU = reinterpret_cast<float*>(smem + C::O_U);     // [BC][LV]
+  float* sGC = reinterpret_cast<float*>(smem + C::O_GC);   // [DK]
+  // the NB value blocks of one (sequence, head) share an XCD (workgroups go
+  // round the eight XCDs in order), so their reads of the chunk blocks they
+  // all need hit that XCD's L2
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int nh = (slot / NB) * 8 + xcd, jb = slot % NB;
+  if (nh >= a.N * a.H) return;
+  const int n = nh / a.H, h = nh - n * a.H;
+  const int c0 = a.tab ? a.cbase[n] : n * a.nc, c1 = a.tab ? a.cbase[n + 1] : (n + 1) * a.nc;
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
+  // S0 block: thread e4 takes 4 consecutive key channels i of value column j
+  for (int e4 = tid; e4 < DK * DVB / 4; e4 += SNT) {
+    const int j = e4 / (DK / 4), i = 4 * (e4 - j * (DK / 4));
+    f32x4 s = zero4();
+    if (a.S0) {
+      const float* src = a.S0 + (size_t)nh * DK * DV + (size_t)i * DV + jb * DVB + j;
+      s = f32x4{src[0], src[DV], src[2 * DV], src[3 * DV]};
+    }
+    *reinterpret_cast<f32x4*>(sST + j * LK + i) = s;
+    bf16x4 hi, lo;
+    split_bf16(s, hi, lo);
+    *reinterpret_cast<bf16x4*>(sSh + j * LSB + i) = hi;
+    *reinterpret_cast<bf16x4*>(sSl + j * LSB + i) = lo;
+  }
+  __syncthreads();  // the first chunk step saves S0 in another thread mapping
+  // two register sets in turn: chunks ci + 1 and ci + 2 are in flight while chunk ci computes
+  f32x4 ry0[NK4], rk0[NK4], ru0[NV4], rg0 = zero4(), rq0[NK4], ra0[1];
+  f32x4 ry1[NK4], rk1[NK4], ru1[NV4], rg1 = zero4(), rq1[NK4], ra1[1];
+  if (c0 < c1) sf_load<DK, DV, NK4, NV4, 1, false>(a, c0, h, jb, tid, ry0, rk0, ru0, rg0, rq0, ra0);
+  if (c0 + 1 < c1) sf_load<DK, DV, NK4, NV4, 1, false>(a, c0 + 1, h, jb, tid, ry1, rk1, ru1, rg1, rq1, ra1);
+  auto step = [&](const int ci, f32x4 (&ry)[NK4], f32x4 (&rk)[NK4], f32x4 (&ru)[NV4], f32x4& rg,
+                  f32x4 (&rq)[NK4], f32x4 (&ra)[1]) {
+    float* W = a.ws + ((size_t)ci * a.H + h) * L::FLOATS;
+#pragma unroll
+    for (int u = 0; u < NK4; ++u) {
+      const int e4 = tid + SNT * u, r = e4 / (DK / 4), i = 4 * (e4 - r * (DK / 4));
+      bf16x4 hi, lo;
+      split_bf16(ry[u], hi, lo);
+      *reinterpret_cast<bf16x4*>(sYh + r * LSB + i) = hi;
+      *reinterpret_cast<bf16x4*>(sYl + r * LSB + i) = lo;
+      split_bf16(rk[u], hi, lo);
+      *reinterpret_cast<bf16x4*>(sKh + r * LTB + i) = hi;
+      *reinterpret_cast<bf16x4*>(sKl + r * LTB + i) = lo;
+    }
+#pragma unroll
+    for (int u = 0; u < NV4; ++u) {
+      const int e4 = tid + SNT * u, r = e4 / (DVB / 4), c4 = e4 - r * (DVB / 4);
+      *reinterpret_cast<f32x4*>(sU + r * LV + 4 * c4) = ru[u];
+    }
+    if (tid < DK / 4) *reinterpret_cast<f32x4*>(sGC + 4 * tid) = rg;
+    for (int e = tid; e < DK * DVB; e += SNT) {  // the state entering chunk ci
+      const int i = e / DVB, j = e - i * DVB;
+      W[L::S + (size_t)i * DV + jb * DVB + j] = sST[j * LK + i];
+    }
+    __syncthreads();
+    {
+      // R = U - Y S, one [16][16] tile per wavefront: Y rows and S^T rows
+      // both run along K; alternate K blocks go to two chains
+      const int tm = wv / (DVB / 16), tn = wv - tm * (DVB / 16);
+      f32x4 acc0 = zero4(), acc1 = zero4();
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int k0 = 32 * kb;
+        const bf16x8 ah = frag_krow(sYh, LSB, k0, 16 * tm), al = frag_krow(sYl, LSB, k0, 16 * tm);
+        const bf16x8 bh = frag_krow(sSh, LSB, k0, 16 * tn), bl = frag_krow(sSl, LSB, k0, 16 * tn);
+        if (kb & 1) acc1 = mma3x(ah, al, bh, bl, acc1);
+        else acc0 = mma3x(ah, al, bh, bl, acc0);
+      }
+      const f32x4 acc = acc0 + acc1;
+      f32x4 rv;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 16 * tm + 4 * g + q, j = 16 * tn + m;
+        rv[q] = sU[r * LV + j] - acc[q];
+        W[L::R + (size_t)r * DV + jb * DVB + j] = rv[q];
+      }
+      bf16x4 hi, lo;
+      split_bf16(rv, hi, lo);
+      *reinterpret_cast<bf16x4*>(sRh + (16 * tn + m) * LRB + 16 * tm + 4 * g) = hi;
+      *reinterpret_cast<bf16x4*>(sRl + (16 * tn + m) * LRB + 16 * tm + 4 * g) = lo;
+    }
+    __syncthreads();
+    // the chunk after next into the registers stored above (near the end the
+    // current chunk is reloaded instead: no branch); issued here, after R,
+    // so that R's products start at once
+    sf_load<DK, DV, NK4, NV4, 1, false>(a, ci + 2 < c1 ? ci + 2 : ci, h, jb, tid, ry, rk, ru, rg, rq, ra);
+    // S <- Diag(gamma_C) S + K_tail^T R  [DK][DVB]; each lane owns its entries.
+    // K_tail^T comes down the columns of the row-major K_tail (transposing
+    // reads), R^T rows run along K.
+    // The tiles t = wv + 8u of a wavefront share the column block tn, so one
+    // pair of R^T fragments per K block serves every chain, interleaved.
+    constexpr int NSU = (DK / 16) * (DVB / 16), NPW = (NSU + SNT / 64 - 1) / (SNT / 64);
+    const int tn = wv % (DVB / 16), j = 16 * tn + m;
+    f32x4 acc[NPW];
+#pragma unroll
+    for (int u = 0; u < NPW; ++u) acc[u] = zero4();
+#pragma unroll
+    for (int k0 = 0; k0 < BC; k0 += 32) {
+      const bf16x8 bh = frag_krow(sRh, LRB, k0, 16 * tn), bl = frag_krow(sRl, LRB, k0, 16 * tn);
+#pragma unroll
+      for (int u = 0; u < NPW; ++u) {
+        const int tm = (wv + (SNT / 64) * u) / (DVB / 16);
+        if (tm < DK / 16) {  // uniform per wavefront
+          const bf16x8 ah = frag_kmajor(sKh, LTB, k0, 16 * tm), al = frag_kmajor(sKl, LTB, k0, 16 * tm);
+          acc[u] = mma3x(ah, al, bh, bl, acc[u]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NPW; ++u) {
+      const int tm = (wv + (SNT / 64) * u) / (DVB / 16), i = 16 * tm + 4 * g;
+      if (tm < DK / 16) {
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(sST + j * LK + i);
+        const f32x4 gc = *reinterpret_cast<const f32x4*>(sGC + i);
+        const f32x4 s = gc * s0 + acc[u];
+        *reinterpret_cast<f32x4*>(sST + j * LK + i) = s;
+        bf16x4 hi, lo;
+        split_bf16(s, hi, lo);
+        *reinterpret_cast<bf16x4*>(sSh + j * LSB + i) = hi;
+        *reinterpret_cast<bf16x4*>(sSl + j * LSB + i) = lo;
+      }
+    }
+    __syncthreads();
+  };
+  int ci = c0;
+  for (; ci + 1 < c1; ci += 2) {
+    step(ci, ry0, rk0, ru0, rg0, rq0, ra0);
+    step(ci + 1, ry1, rk1, ru1, rg1, rq1, ra1);
+  }
+  if (ci < c1) step(ci, ry0, rk0, ru0, rg0, rq0, ra0);
+}
+
 // ---- sequential reverse pass: dS' of every chunk, dR, and dS0 ------------------------
 template <int DK, int DV, bool BF16>
 __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
@@ -1079,17 +1257,37 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
   for (int u = 0; u < NKT; ++u) aQ[u] = aY[u] = aK[u] = zero4();
 #pragma unroll
   for (int u = 0; u < NCT; ++u) aAQ[u] = aA[u] = zero4();
-  float rs = 0.f;  // sum over the value channels of dS' * S, row tid
+  // Row sums over the value channels of dS' * S: each thread sums the entries
+  // it stages (row (tid + NT u) / 8, 4 channels per slice); the 8 threads of a
+  // row, consecutive lanes, are combined after the last slice.
+  float rsp[NSK];
+#pragma unroll
+  for (int u = 0; u < NSK; ++u) rsp[u] = 0.f;
+  // The products of this phase take their operands as bf16 hi/lo halves
+  // (mma3x), split once as they are staged: a row of a [.][KC] slice holds
+  // its KC hi halves, then its KC lo halves (pitch LH halves, the bytes of
+  // the fp32 row it replaces).
+  constexpr int LH = 2 * LS;
+  static_assert(KC == 32 && LH % 8 == 0, "one K = 32 block per slice, 16-byte aligned rows");
+  __bf16 *bO = reinterpret_cast<__bf16*>(sO), *bDR = reinterpret_cast<__bf16*>(sDR);
+  __bf16 *bR = reinterpret_cast<__bf16*>(sR), *bZ = reinterpret_cast<__bf16*>(sZ);
+  __bf16 *bS = reinterpret_cast<__bf16*>(sS), *bDS = reinterpret_cast<__bf16*>(sDS);
+  auto st_split = [&](__bf16* base, int row, int c, const f32x4& x) {
+    bf16x4 hi, lo;
+    split_bf16(x, hi, lo);
+    *reinterpret_cast<bf16x4*>(base + row * LH + c) = hi;
+    *reinterpret_cast<bf16x4*>(base + row * LH + KC + c) = lo;
+  };
   for (int sl = 0; sl < NS; ++sl) {
     const int j0 = sl * KC;
     {
       const int o = ss * LS + 4 * sc4;
-      *reinterpret_cast<f32x4*>(sO + o) = pO;
-      *reinterpret_cast<f32x4*>(sR + o) = pR;
-      *reinterpret_cast<f32x4*>(sDR + o) = pDR;
+      st_split(bO, ss, 4 * sc4, pO);
+      st_split(bR, ss, 4 * sc4, pR);
+      st_split(bDR, ss, 4 * sc4, pDR);
+      st_split(bZ, ss, 4 * sc4, pW * pV);
       *reinterpret_cast<f32x4*>(sW + o) = pW;
       *reinterpret_cast<f32x4*>(sV + o) = pV;
-      *reinterpret_cast<f32x4*>(sZ + o) = pW * pV;
 #pragma unroll
       for (int q = 0; q < 4; ++q) sDRT[(4 * sc4 + q) * LA + ss] = pDR[q];
 #pragma unroll
@@ -1097,41 +1295,37 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
         const int e = tid + NT * u;
         if (e < DK * KC / 4) {
           const int i = e / (KC / 4), c4 = e - i * (KC / 4);
-          *reinterpret_cast<f32x4*>(sS + i * LS + 4 * c4) = pS[u];
-          *reinterpret_cast<f32x4*>(sDS + i * LS + 4 * c4) = pDS[u];
+          st_split(bS, i, 4 * c4, pS[u]);
+          st_split(bDS, i, 4 * c4, pDS[u]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) rsp[u] = fmaf(pDS[u][q], pS[u][q], rsp[u]);
         }
       }
     }
     __syncthreads();
-    if (tid < DK)
-#pragma unroll 8
-      for (int c = 0; c < KC; ++c) rs = fmaf(sDS[tid * LS + c], sS[tid * LS + c], rs);
     {
-      // aQ += dO S'^T, aY += dR S'^T, aK += R dS'^T over this slice: the
-      // wavefront's column block tn is the same for every u, so its S' and
-      // dS' fragments are read once; per K step the three products run as
-      // independent accumulator chains, interleaved (the same K order per
-      // tile as one chain at a time)
+      // aQ += dO S^T, aY += dR S^T, aK += R dS'^T over this slice (one K = 32
+      // block): the wavefront's column block tn is the same for every u, so
+      // its S and dS' fragments are read once; the three products run as
+      // independent accumulator chains, interleaved
       const int tn = wv % TNK;
-      float4 fS[KC / 16], fD[KC / 16];
-#pragma unroll
-      for (int k = 0; k < KC / 16; ++k) {
-        fS[k] = *reinterpret_cast<const float4*>(sS + (16 * tn + m) * LS + 16 * k + 4 * g);
-        fD[k] = *reinterpret_cast<const float4*>(sDS + (16 * tn + m) * LS + 16 * k + 4 * g);
-      }
+      const bf16x8 sh = frag_krow(bS, LH, 0, 16 * tn), sl2 = frag_krow(bS, LH, KC, 16 * tn);
+      const bf16x8 dh = frag_krow(bDS, LH, 0, 16 * tn), dl = frag_krow(bDS, LH, KC, 16 * tn);
 #pragma unroll
       for (int u = 0; u < NKT; ++u) {
-        const int ro = (16 * ((wv + NWV * u) / TNK) + m) * LS + 4 * g;
-#pragma unroll
-        for (int k = 0; k < KC / 16; ++k) {
-          const float4 o = *reinterpret_cast<const float4*>(sO + ro + 16 * k);
-          const float4 d = *reinterpret_cast<const float4*>(sDR + ro + 16 * k);
-          const float4 r = *reinterpret_cast<const float4*>(sR + ro + 16 * k);
-          mfma3(aQ[u], o.x, fS[k].x, aY[u], d.x, fS[k].x, aK[u], r.x, fD[k].x);
-          mfma3(aQ[u], o.y, fS[k].y, aY[u], d.y, fS[k].y, aK[u], r.y, fD[k].y);
-          mfma3(aQ[u], o.z, fS[k].z, aY[u], d.z, fS[k].z, aK[u], r.z, fD[k].z);
-          mfma3(aQ[u], o.w, fS[k].w, aY[u], d.w, fS[k].w, aK[u], r.w, fD[k].w);
-        }
+        const int r0 = 16 * ((wv + NWV * u) / TNK);
+        const bf16x8 oh = frag_krow(bO, LH, 0, r0), ol = frag_krow(bO, LH, KC, r0);
+        const bf16x8 yh = frag_krow(bDR, LH, 0, r0), yl = frag_krow(bDR, LH, KC, r0);
+        const bf16x8 rh = frag_krow(bR, LH, 0, r0), rl = frag_krow(bR, LH, KC, r0);
+        aQ[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ol, sh, aQ[u], 0, 0, 0);
+        aY[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yl, sh, aY[u], 0, 0, 0);
+        aK[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rl, dh, aK[u], 0, 0, 0);
+        aQ[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oh, sl2, aQ[u], 0, 0, 0);
+        aY[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yh, sl2, aY[u], 0, 0, 0);
+        aK[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rh, dl, aK[u], 0, 0, 0);
+        aQ[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oh, sh, aQ[u], 0, 0, 0);
+        aY[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yh, sh, aY[u], 0, 0, 0);
+        aK[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rh, dh, aK[u], 0, 0, 0);
       }
     }
     // the next slice into the registers stored above, issued after the first
@@ -1141,21 +1335,19 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
     for (int u = 0; u < NCT; ++u) {
       // aAQ += dO R^T (lower tiles) and aA += dR Z^T, interleaved likewise
       const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
-      const int ra = (16 * tm + m) * LS + 4 * g, rb = (16 * tn + m) * LS + 4 * g;
+      const bf16x8 yh = frag_krow(bDR, LH, 0, 16 * tm), yl = frag_krow(bDR, LH, KC, 16 * tm);
+      const bf16x8 zh = frag_krow(bZ, LH, 0, 16 * tn), zl = frag_krow(bZ, LH, KC, 16 * tn);
       if (tn <= tm) {
-#pragma unroll
-        for (int k = 0; k < KC / 16; ++k) {
-          const float4 o = *reinterpret_cast<const float4*>(sO + ra + 16 * k);
-          const float4 r = *reinterpret_cast<const float4*>(sR + rb + 16 * k);
-          const float4 d = *reinterpret_cast<const float4*>(sDR + ra + 16 * k);
-          const float4 z = *reinterpret_cast<const float4*>(sZ + rb + 16 * k);
-          mfma2(aAQ[u], o.x, r.x, aA[u], d.x, z.x);
-          mfma2(aAQ[u], o.y, r.y, aA[u], d.y, z.y);
-          mfma2(aAQ[u], o.z, r.z, aA[u], d.z, z.z);
-          mfma2(aAQ[u], o.w, r.w, aA[u], d.w, z.w);
-        }
+        const bf16x8 oh = frag_krow(bO, LH, 0, 16 * tm), ol = frag_krow(bO, LH, KC, 16 * tm);
+        const bf16x8 rh = frag_krow(bR, LH, 0, 16 * tn), rl = frag_krow(bR, LH, KC, 16 * tn);
+        aAQ[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ol, rh, aAQ[u], 0, 0, 0);
+        aA[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yl, zh, aA[u], 0, 0, 0);
+        aAQ[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oh, rl, aAQ[u], 0, 0, 0);
+        aA[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yh, zl, aA[u], 0, 0, 0);
+        aAQ[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oh, rh, aAQ[u], 0, 0, 0);
+        aA[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yh, zh, aA[u], 0, 0, 0);
       } else {
-        aA[u] = mma_lds<float, KC>(aA[u], sDR + 16 * tm * LS, LS, sZ + 16 * tn * LS, LS);
+        aA[u] = mma3x(yh, yl, zh, zl, aA[u]);
       }
     }
     {  // dZ = A^T dR over this slice's 32 value channels: one [16][16] tile per wavefront
@@ -1173,6 +1365,18 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
       }
     }
     __syncthreads();
+  }
+
+  // row sums of dS' * S: combine the 8 lanes of each row (sRS is read in the
+  // final phase, after several barriers)
+#pragma unroll
+  for (int u = 0; u < NSK; ++u) {
+    float x = rsp[u];
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    const int e = tid + NT * u;
+    if (e < DK * KC / 4 && (e & (KC / 4 - 1)) == 0) sm[C::O_RS + e / (KC / 4)] = x;
   }
 
   // ---- phase 2a: dA += dY E^T, X = A^T dY ----
@@ -1235,7 +1439,8 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
 #pragma unroll
   for (int u = 0; u < NCT; ++u) {
     const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
-    aA[u] = mma_lds<float, DK>(aA[u], sDY + 16 * tm * LKP, LKP, sEB + 16 * tn * LKP, LKP);
+    // a chain of its own, added to the bf16 chain of phase 1 (one MFMA shape per chain)
+    aA[u] += mma_lds<float, DK>(zero4(), sDY + 16 * tm * LKP, LKP, sEB + 16 * tn * LKP, LKP);
   }
 #pragma unroll
   for (int u = 0; u < NKT; ++u) {
@@ -1386,7 +1591,6 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
   float *sU = sm + C::O_U, *sV2 = sm + C::O_V2, *sRS = sm + C::O_RS;
   float *sPU = sm + C::O_PU, *sPV = sm + C::O_PV;
   const float *sG31 = sm + C::O_G31, *sGCL = sm + C::O_GCL, *sGCX = sm + C::O_GCX;
-  if (tid < DK) sRS[tid] = rs;
 #pragma unroll
   for (int u = 0; u < NKT; ++u) {
     const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK, i = 16 * tn + m;
@@ -1526,11 +1730,11 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   // sequential passes (with no chunks they only pass dS_T through to dS0)
   {
     constexpr int LK = DK + 4, LC = BC + 4;
-    constexpr size_t lf = state_fwd_lds<DK, false>();
+    constexpr size_t lf = StateF3Cfg<DK>::BYTES;
     const size_t lb = (size_t)(DVB * LK + BC * LC + BC * (DVB + 4) + 3 * BC * LK + DVB * LC + DK) * 4;
-    GDR2_LDS((bwd_state_fwd_kernel<DK, DV, false>), lf);
+    GDR2_LDS((bwd_state_fwd3_kernel<DK, DV>), lf);
     const dim3 gs((unsigned)(((size_t)a.N * a.H + 7) / 8 * 8 * (DV / DVB)));
-    hipLaunchKernelGGL((bwd_state_fwd_kernel<DK, DV, false>), gs, dim3(SNT), lf, st, a);
+    hipLaunchKernelGGL((bwd_state_fwd3_kernel<DK, DV>), gs, dim3(SNT), lf, st, a);
     GDR2_CK(hipGetLastError());
     if (a.in_bf16) {
       GDR2_LDS((bwd_state_bwd_kernel<DK, DV, true>), lb);

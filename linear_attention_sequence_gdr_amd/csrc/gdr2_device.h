@@ -194,4 +194,62 @@ __device__ __forceinline__ f32x4 mma_lds_f32(f32x4 acc, const float* A, int lda,
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// ---- fp32 products as three bf16 products ---------------------------------------------
+// x = hi + lo + e with hi = bf16(x), lo = bf16(x - hi) (both rounded to
+// nearest), so |e| <= 2^-18 |x|.  A product a b then runs as hi_a hi_b +
+// hi_a lo_b + lo_a hi_b on bf16 MFMA with fp32 accumulation; the dropped
+// lo_a lo_b and the split residuals leave at most about 3 * 2^-18 |a b| per
+// term, against 2^-24 for an fp32 product.  One 16x16x32 step of three
+// instructions replaces eight 16x16x4 fp32 steps at a sixteenth of the issue
+// cost each.
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+
+__device__ __forceinline__ void split_bf16(const f32x4& x, bf16x4& hi, bf16x4& lo) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    hi[q] = (__bf16)x[q];
+    lo[q] = (__bf16)(x[q] - (float)hi[q]);
+  }
+}
+
+// acc += A B over one K = 32 block, from the hi/lo halves of both operands
+// (smallest terms first).
+__device__ __forceinline__ f32x4 mma3x(const bf16x8& ah, const bf16x8& al, const bf16x8& bh,
+                                       const bf16x8& bl, f32x4 acc) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+}
+
+// Transposing LDS read of 16-bit data (gfx950 ds_read_b64_tr_b16): within
+// each 16-lane group, lane t receives elements t, t + 16, t + 32 and t + 48
+// of the 64 elements that the group's lanes address (4 consecutive elements
+// per lane, in lane order).  With lane s of the group pointing at elements
+// 4 (s % 4) .. 4 (s % 4) + 3 of row s / 4 of a row-major block, lane t gets
+// column t of those 4 rows: a K-major operand fragment from a row-major block.
+__device__ __forceinline__ bf16x4 lds_tr16_bf16(const __bf16* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(__attribute__((address_space(3))) void*)p);
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// The 16x16x32 operand fragment of lane (m, g) for a factor whose K index
+// runs down the rows of a row-major bf16 block X (leading dimension ld):
+// elements X[k0 + 8g + e][c0 + m], e < 8, as two transposing reads.
+__device__ __forceinline__ bf16x8 frag_kmajor(const __bf16* X, int ld, int k0, int c0) {
+  const int m = lane_id() & 15, g = lane_id() >> 4;
+  const __bf16* p = X + (k0 + 8 * g + (m >> 2)) * ld + c0 + 4 * (m & 3);
+  const bf16x4 x0 = lds_tr16_bf16(p);
+  const bf16x4 x1 = lds_tr16_bf16(p + 4 * ld);
+  return bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+}
+
+// The fragment of lane (m, g) for a factor whose K index runs along the rows
+// of X: elements X[c0 + m][k0 + 8g + e], e < 8, one 16-byte read.
+__device__ __forceinline__ bf16x8 frag_krow(const __bf16* X, int ld, int k0, int c0) {
+  const int m = lane_id() & 15, g = lane_id() >> 4;
+  return *reinterpret_cast<const bf16x8*>(X + (c0 + m) * ld + k0 + 8 * g);
+}
+
 }  // namespace gdr2
