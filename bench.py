@@ -691,7 +691,7 @@ def main():
                      "alg_bytes": bw_bytes,
                      "roofline": {"bound": "hbm", "achieved": bw_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": bw_gbs / HBM_PEAK_GBS,
-                                  "traffic": load_call_traffic("fwd", "bwd_state_fwd_kernel<128, 128, false>",
+                                  "traffic": load_call_traffic("fwd", "bwd_state_fwd3_kernel<128, 128>",
                                                                "bwd_")}},
         "long_sequence": long_leg(args, torch, G, I, dev) if args.long == "on" else None,
         "block": {"workload": "gdr2_chunk_fwd_block B4 T4096 H16 Hv16 dk=dv=128 from projections: "

@@ -25,13 +25,18 @@
 // item inside the workspace (BwdLayout: G, Q_g, K_tail, Y, U, R, dR, A, A_qk,
 // the entering state S, dS' and gamma_C).  Four kernels run:
 //   bwd_front_kernel      per item: G, the scaled rows, T and A_qk, A, Y, U;
-//   bwd_state_fwd_kernel  per chain, chunks in order: S entering each chunk
+//   bwd_state_fwd3_kernel per chain, chunks in order: S entering each chunk
 //                         and R = U - Y S;
-//   bwd_state_bwd_kernel  per chain, chunks in reverse: dS' and dR, and dS0;
+//   bwd_state_bwd3_kernel per chain, chunks in reverse: dS' and dR, and dS0;
 //   bwd_out_kernel        per item: every output-path and WY-gradient product
 //                         and the gradients themselves (E, E', K', Q' are
 //                         formed again from G, q, k, b rather than stored).
-// Every product runs on fp32 MFMA (16x16x4) from LDS-staged operands.
+// The products run from LDS-staged operands with fp32 accumulation: on fp32
+// MFMA (16x16x4) in the front pass and in phases 2-4 of the output pass; in
+// the two sequential passes and the output pass's value-slice phase as three
+// bf16 MFMAs over hi/lo operand halves (mma3x, about 2^-16 of each term).
+// The fp32 forward (fwd32_state_kernel after the front pass) keeps fp32
+// products throughout.
 #include <hip/hip_runtime.h>
 
 #include "gdr2_device.h"
@@ -78,41 +83,6 @@ __device__ __forceinline__ bool bwd_locate(const BwdArgs& a, int ci, long long& 
 __device__ __forceinline__ void mfma2(f32x4& c0, float a0, float b0, f32x4& c1, float a1, float b1) {
   c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, c0, 0, 0, 0);
   c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, c1, 0, 0, 0);
-}
-
-// acc = A[16 x K] * B[K x 16], both operands K-contiguous in LDS (A row m at
-// A + m*lda, B column n at Bt + n*ldb), with the K = 16 blocks dealt in turn
-// to NA accumulators, independent chains summed at the end: a chain NA times
-// shorter for a product that has no other chain beside it.
-template <int K, int NA>
-__device__ __forceinline__ f32x4 mma_lds_split(const float* A, int lda, const float* Bt, int ldb) {
-  static_assert(K % (16 * NA) == 0, "K blocks per accumulator");
-  const int m = lane_id() & 15, g = lane_id() >> 4;
-  const float* a = A + m * lda + 4 * g;
-  const float* b = Bt + m * ldb + 4 * g;
-  f32x4 c[NA];
-#pragma unroll
-  for (int j = 0; j < NA; ++j) c[j] = zero4();
-#pragma unroll
-  for (int k0 = 0; k0 < K; k0 += 16 * NA) {
-    float4 av[NA], bv[NA];
-#pragma unroll
-    for (int j = 0; j < NA; ++j) {
-      av[j] = *reinterpret_cast<const float4*>(a + k0 + 16 * j);
-      bv[j] = *reinterpret_cast<const float4*>(b + k0 + 16 * j);
-    }
-#pragma unroll
-    for (int j = 0; j < NA; ++j) c[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j].x, bv[j].x, c[j], 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < NA; ++j) c[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j].y, bv[j].y, c[j], 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < NA; ++j) c[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j].z, bv[j].z, c[j], 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < NA; ++j) c[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j].w, bv[j].w, c[j], 0, 0, 0);
-  }
-#pragma unroll
-  for (int j = 1; j < NA; ++j) c[0] += c[j];
-  return c[0];
 }
 
 // Factors centred on one row stay inside [e^-SLIM, e^SLIM] (nats); a chunk
@@ -634,23 +604,22 @@ __device__ __forceinline__ void sb_load(const BwdArgs& a, int ci, int h, int jb,
   if (tid < DK / 4) rg = reinterpret_cast<const f32x4*>(Wn + L::GC)[tid];
 }
 
-// ---- sequential state pass: the state entering every chunk --------------------------
+// ---- sequential state pass of the fp32 forward (Eqs. 23-24) ------------------------
 // One workgroup of SNT threads per (sequence, head, 32 value channels); the
 // state block is kept transposed in LDS (S^T, the B operand of Y S).  The
 // next two chunks' operands are loaded into registers (16-byte loads in
-// address order) while the current chunk computes.
-// FWD = false (the backward): saves the state entering every chunk and
-// R = U - Y S to the workspace.  FWD = true (the fp32 forward, Eqs. 23-24):
-// writes o = Q_g S + A_qk R for every chunk and the final state instead.
-template <int DK, int DV, bool FWD>
-__global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
-  typedef BwdLayout<DK, DV> L;
+// address order) while the current chunk computes.  Per chunk: R = U - Y S,
+// o = Q_g S + A_qk R, S <- Diag(gamma_C) S + K_tail^T R, all on fp32 MFMA;
+// the final state after the last chunk.
+template <int DK, int DV>
+__global__ __launch_bounds__(SNT, 1) void fwd32_state_kernel(BwdArgs a) {
+  constexpr bool FWD = true;
   constexpr int NB = DV / DVB, LK = DK + 4, LC = BC + 4, LV = DVB + 4;
   constexpr int NK4 = BC * DK / 4 / SNT;   // float4 per thread of a [BC][DK] block
   constexpr int NV4 = BC * DVB / 4 / SNT;  // float4 per thread of a [BC][DVB] block
-  constexpr int NC4 = FWD ? BC * BC / 4 / SNT : 1;  // float4 per thread of A_qk
+  constexpr int NC4 = BC * BC / 4 / SNT;   // float4 per thread of A_qk
   static_assert(NK4 >= 1 && NV4 >= 1, "state pass tiling");
-  static_assert(!FWD || (BC / 16) * (DVB / 16) == SNT / 64, "one output tile per wavefront");
+  static_assert((BC / 16) * (DVB / 16) == SNT / 64, "one output tile per wavefront");
   extern __shared__ __align__(16) unsigned char smem[];
   float* sST = reinterpret_cast<float*>(smem);  // [DVB][LK]
   float* sY = sST + DVB * LK;                   // [BC][LK]
@@ -658,8 +627,8 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
   float* sRT = sKt + BC * LK;                   // [DVB][LC]
   float* sU = sRT + DVB * LC;                   // [BC][LV]
   float* sGC = sU + BC * LV;                    // [DK]
-  float* sQg = sGC + DK;                        // FWD: [BC][LK]
-  float* sAq = sQg + BC * LK;                   // FWD: [BC][LC]
+  float* sQg = sGC + DK;                        // [BC][LK]
+  float* sAq = sQg + BC * LK;                   // [BC][LC]
   // the NB value blocks of one (sequence, head) share an XCD (workgroups go
   // round the eight XCDs in order), so their reads of the chunk blocks they
   // all need hit that XCD's L2
@@ -680,20 +649,17 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
   if (c0 + 1 < c1) sf_load<DK, DV, NK4, NV4, NC4, FWD>(a, c0 + 1, h, jb, tid, ry1, rk1, ru1, rg1, rq1, ra1);
   auto step = [&](const int ci, f32x4 (&ry)[NK4], f32x4 (&rk)[NK4], f32x4 (&ru)[NV4], f32x4& rg,
                   f32x4 (&rq)[NK4], f32x4 (&ra)[NC4]) {
-    [[maybe_unused]] float* W = a.ws + ((size_t)ci * a.H + h) * L::FLOATS;
 #pragma unroll
     for (int u = 0; u < NK4; ++u) {
       const int e4 = tid + SNT * u, r = e4 / (DK / 4), i = 4 * (e4 - r * (DK / 4));
       *reinterpret_cast<f32x4*>(sY + r * LK + i) = ry[u];
       *reinterpret_cast<f32x4*>(sKt + r * LK + i) = rk[u];
-      if constexpr (FWD) *reinterpret_cast<f32x4*>(sQg + r * LK + i) = rq[u];
+      *reinterpret_cast<f32x4*>(sQg + r * LK + i) = rq[u];
     }
-    if constexpr (FWD) {
 #pragma unroll
-      for (int u = 0; u < NC4; ++u) {
-        const int e4 = tid + SNT * u, r = e4 / (BC / 4), c4 = e4 - r * (BC / 4);
-        *reinterpret_cast<f32x4*>(sAq + r * LC + 4 * c4) = ra[u];
-      }
+    for (int u = 0; u < NC4; ++u) {
+      const int e4 = tid + SNT * u, r = e4 / (BC / 4), c4 = e4 - r * (BC / 4);
+      *reinterpret_cast<f32x4*>(sAq + r * LC + 4 * c4) = ra[u];
     }
 #pragma unroll
     for (int u = 0; u < NV4; ++u) {
@@ -701,34 +667,22 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
       *reinterpret_cast<f32x4*>(sU + r * LV + 4 * c4) = ru[u];
     }
     if (tid < DK / 4) *reinterpret_cast<f32x4*>(sGC + 4 * tid) = rg;
-    if constexpr (!FWD) {
-      for (int e = tid; e < DK * DVB; e += SNT) {  // the state entering chunk ci
-        const int i = e / DVB, j = e - i * DVB;
-        W[L::S + (size_t)i * DV + jb * DVB + j] = sST[j * LK + i];
-      }
-    }
     __syncthreads();
-    // R = U - Y S  [BC][DVB], kept for the output paths as well; the forward
-    // also forms Q_g S (same tile, from the state entering the chunk)
+    // R = U - Y S  [BC][DVB] and Q_g S (same tile, from the state entering the chunk)
     f32x4 ao = zero4();
     for (int t = wv; t < (BC / 16) * (DVB / 16); t += SNT / 64) {
       const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
-      // one tile per wavefront: Y S as two chains over alternate K blocks
-      // (the forward, at its register limit with Q_g and A_qk, keeps one)
-      f32x4 acc;
-      if constexpr (FWD) acc = mma_lds<float, DK>(zero4(), sY + 16 * tm * LK, LK, sST + 16 * tn * LK, LK);
-      else acc = mma_lds_split<DK, 2>(sY + 16 * tm * LK, LK, sST + 16 * tn * LK, LK);
-      if constexpr (FWD) ao = mma_lds<float, DK>(zero4(), sQg + 16 * tm * LK, LK, sST + 16 * tn * LK, LK);
+      const f32x4 acc = mma_lds<float, DK>(zero4(), sY + 16 * tm * LK, LK, sST + 16 * tn * LK, LK);
+      ao = mma_lds<float, DK>(zero4(), sQg + 16 * tm * LK, LK, sST + 16 * tn * LK, LK);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = 16 * tm + 4 * g + q, j = 16 * tn + m;
         const float rv = sU[r * LV + j] - acc[q];
         sRT[j * LC + r] = rv;
-        if constexpr (!FWD) W[L::R + (size_t)r * DV + jb * DVB + j] = rv;
       }
     }
     __syncthreads();
-    if constexpr (FWD) {
+    {
       // o = Q_g S + A_qk R (Eq. 24); A_qk is lower triangular, so row tile
       // tm needs the first 16 (tm + 1) tokens of R only
       const int tm = wv / (DVB / 16), tn = wv - tm * (DVB / 16);
@@ -748,29 +702,7 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
     sf_load<DK, DV, NK4, NV4, NC4, FWD>(a, ci + 2 < c1 ? ci + 2 : ci, h, jb, tid, ry, rk, ru, rg, rq, ra);
     // S <- Diag(gamma_C) S + K_tail^T R  [DK][DVB]; each lane owns its entries
     constexpr int NSU = (DK / 16) * (DVB / 16);
-    if constexpr (!FWD && NSU == 2 * (SNT / 64)) {
-      // two tiles per wavefront, t = wv and wv + 8, in one column block tn:
-      // one R^T fragment per K step serves both chains, interleaved (each
-      // in ascending K, as one chain at a time)
-      const int tn = wv % (DVB / 16), tm0 = wv / (DVB / 16), tm1 = tm0 + (SNT / 64) / (DVB / 16);
-      f32x4 c0 = zero4(), c1 = zero4();
-#pragma unroll
-      for (int k0 = 0; k0 < BC; k0 += 16) {
-        const float4 rb = *reinterpret_cast<const float4*>(sRT + (16 * tn + m) * LC + k0 + 4 * g);
-        const float* x0 = sKt + (k0 + 4 * g) * LK + 16 * tm0 + m;  // K_tail read K-major
-        const float* x1 = x0 + 16 * (tm1 - tm0);
-        mfma2(c0, x0[0], rb.x, c1, x1[0], rb.x);
-        mfma2(c0, x0[LK], rb.y, c1, x1[LK], rb.y);
-        mfma2(c0, x0[2 * LK], rb.z, c1, x1[2 * LK], rb.z);
-        mfma2(c0, x0[3 * LK], rb.w, c1, x1[3 * LK], rb.w);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int i0 = 16 * tm0 + 4 * g + q, i1 = 16 * tm1 + 4 * g + q, j = 16 * tn + m;
-        sST[j * LK + i0] = sGC[i0] * sST[j * LK + i0] + c0[q];
-        sST[j * LK + i1] = sGC[i1] * sST[j * LK + i1] + c1[q];
-      }
-    } else {
+    {
       for (int t = wv; t < NSU; t += SNT / 64) {
         const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
         // K_tail^T as the left factor: K_tail read K-major from its row-major block
@@ -790,14 +722,12 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd_kernel(BwdArgs a) {
     step(ci + 1, ry1, rk1, ru1, rg1, rq1, ra1);
   }
   if (ci < c1) step(ci, ry0, rk0, ru0, rg0, rq0, ra0);
-  if constexpr (FWD) {
-    // the state after the sequence's last token (S0 itself for an empty one)
-    if (a.ST)
-      for (int e = tid; e < DK * DVB; e += SNT) {
-        const int i = e / DVB, j = e - i * DVB;
-        a.ST[(size_t)nh * DK * DV + (size_t)i * DV + jb * DVB + j] = sST[j * LK + i];
-      }
-  }
+  // the state after the sequence's last token (S0 itself for an empty one)
+  if (a.ST)
+    for (int e = tid; e < DK * DVB; e += SNT) {
+      const int i = e / DVB, j = e - i * DVB;
+      a.ST[(size_t)nh * DK * DV + (size_t)i * DV + jb * DVB + j] = sST[j * LK + i];
+    }
 }
 
 // LDS plan of bwd_state_fwd3_kernel (byte offsets).  The fp32 state S^T is
@@ -824,8 +754,8 @@ struct StateF3Cfg {
 };
 
 // ---- sequential state pass of the backward, products as three bf16 products ----------
-// The same pass as bwd_state_fwd_kernel<.., false> (the state entering every
-// chunk and R = U - Y S, saved for the output paths), with R = U - Y S and
+// The state entering every chunk and R = U - Y S, saved for the output
+// paths, with R = U - Y S and
 // S <- Diag(gamma_C) S + K_tail^T R on 16x16x32 bf16 MFMA over hi/lo halves
 // (mma3x): the chunk step's dependent chain is twelve instructions per tile
 // instead of 32 fp32 ones.  Y and K_tail are split as they are staged, R where
@@ -984,22 +914,67 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_fwd3_kernel(BwdArgs a) {
   if (ci < c1) step(ci, ry0, rk0, ru0, rg0, rq0, ra0);
 }
 
-// ---- sequential reverse pass: dS' of every chunk, dR, and dS0 ------------------------
+// LDS plan of bwd_state_bwd3_kernel (byte offsets): the fp32 dS'^T master,
+// and bf16 hi/lo halves of dS'^T, A_qk, dO, Q_g, -dR^T and one region X that
+// holds K_tail for dR and then Y for the state gradient.  Blocks read down
+// their columns (transposing reads: A_qk, dO, Q_g, Y) have pitches whose four
+// rows per 16-lane group land on distinct banks; blocks read along rows
+// (K_tail, dS'^T, -dR^T) pitches of 4 words mod 64.
+template <int DK>
+struct StateB3Cfg {
+  static constexpr int LK = DK + 4;  // fp32 dS'^T
+  static constexpr int LSB = DK + 8, LAB = BC + 16, LOB = DVB + 16, LTB = DK + 16, LRB = BC + 8;
+  static constexpr size_t O_DST = 0;
+  static constexpr size_t O_DSH = O_DST + (size_t)DVB * LK * 4, O_DSL = O_DSH + (size_t)DVB * LSB * 2;
+  static constexpr size_t O_AH = O_DSL + (size_t)DVB * LSB * 2, O_AL = O_AH + (size_t)BC * LAB * 2;
+  static constexpr size_t O_OH = O_AL + (size_t)BC * LAB * 2, O_OL = O_OH + (size_t)BC * LOB * 2;
+  static constexpr size_t O_QH = O_OL + (size_t)BC * LOB * 2, O_QL = O_QH + (size_t)BC * LTB * 2;
+  static constexpr size_t O_XH = O_QL + (size_t)BC * LTB * 2, O_XL = O_XH + (size_t)BC * LSB * 2;
+  static constexpr size_t O_RH = O_XL + (size_t)BC * LSB * 2, O_RL = O_RH + (size_t)DVB * LRB * 2;
+  static constexpr size_t O_GC = O_RL + (size_t)DVB * LRB * 2;
+  static constexpr size_t BYTES = O_GC + (size_t)DK * 4;
+  static_assert(BYTES <= 160 * 1024, "LDS budget exceeded");
+  static_assert(O_DSH % 16 == 0 && O_AH % 16 == 0 && O_OH % 16 == 0 && O_QH % 16 == 0 &&
+                    O_XH % 16 == 0 && O_RH % 16 == 0 && O_GC % 16 == 0,
+                "16-byte aligned regions");
+};
+
+// ---- sequential reverse pass, products as three bf16 products ----------------------
+// dS' and dR of every chunk, and dS0, with every product on 16x16x32 bf16 MFMA over hi/lo halves (mma3x).  A
+// chunk step, chunks in reverse:
+//   stage Q_g, A_qk, dO, K_tail (split as they are stored), save dS';
+//   dR = A_qk^T dO + K_tail dS' (one tile per wavefront), and Q_g^T dO into
+//   the state-gradient accumulators (two tiles per wavefront, same dO
+//   fragments); -dR^T split into LDS;
+//   stage Y over K_tail, then issue the previous chunk's loads;
+//   dS <- (Q_g^T dO - Y^T dR) + Diag(gamma_C) dS', the fp32 master and its
+//   halves written by the lanes that own the entries.
 template <int DK, int DV, bool BF16>
-__global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(SNT, 1) void bwd_state_bwd3_kernel(BwdArgs a) {
   typedef BwdLayout<DK, DV> L;
-  constexpr int NB = DV / DVB, LK = DK + 4, LC = BC + 4;
+  typedef StateB3Cfg<DK> C;
+  constexpr int NB = DV / DVB, LK = C::LK, LSB = C::LSB, LAB = C::LAB, LOB = C::LOB, LTB = C::LTB,
+                LRB = C::LRB;
   constexpr int NK4 = BC * DK / 4 / SNT, NV4 = BC * DVB / 4 / SNT, NC4 = BC * BC / 4 / SNT;
+  constexpr int NKB = DK / 32;  // K = 32 blocks of K_tail dS'
+  constexpr int NSU = (DK / 16) * (DVB / 16), NPW = (NSU + SNT / 64 - 1) / (SNT / 64);
+  static_assert(NK4 >= 1 && NV4 >= 1 && NC4 >= 1, "state pass tiling");
+  static_assert((BC / 16) * (DVB / 16) == SNT / 64, "one dR tile per wavefront");
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int LV = DVB + 4;
-  float* sdST = reinterpret_cast<float*>(smem);  // [DVB][LK]  dS^T
-  float* sAqk = sdST + DVB * LK;                 // [BC][LC]   A_qk
-  float* sdO = sAqk + BC * LC;                   // [BC][LV]   dO
-  float* sKt = sdO + BC * LV;                    // [BC][LK]   K_tail
-  float* sQg = sKt + BC * LK;                    // [BC][LK]   Q_g
-  float* sY = sQg + BC * LK;                     // [BC][LK]   Y
-  float* sdRT = sY + BC * LK;                    // [DVB][LC]  dR^T
-  float* sGC = sdRT + DVB * LC;                  // [DK]
+  float* sdST = reinterpret_cast<float*>(smem + C::O_DST);  // [DVB][LK] fp32 dS'^T
+  __bf16* sDh = reinterpret_cast<__bf16*>(smem + C::O_DSH);  // [DVB][LSB] dS'^T halves
+  __bf16* sDl = reinterpret_cast<__bf16*>(smem + C::O_DSL);
+  __bf16* sAh = reinterpret_cast<__bf16*>(smem + C::O_AH);   // [BC][LAB] A_qk halves
+  __bf16* sAl = reinterpret_cast<__bf16*>(smem + C::O_AL);
+  __bf16* sOh = reinterpret_cast<__bf16*>(smem + C::O_OH);   // [BC][LOB] dO halves
+  __bf16* sOl = reinterpret_cast<__bf16*>(smem + C::O_OL);
+  __bf16* sQh = reinterpret_cast<__bf16*>(smem + C::O_QH);   // [BC][LTB] Q_g halves
+  __bf16* sQl = reinterpret_cast<__bf16*>(smem + C::O_QL);
+  __bf16* sXh = reinterpret_cast<__bf16*>(smem + C::O_XH);   // [BC][LSB] K_tail, then Y
+  __bf16* sXl = reinterpret_cast<__bf16*>(smem + C::O_XL);
+  __bf16* sRh = reinterpret_cast<__bf16*>(smem + C::O_RH);   // [DVB][LRB] -dR^T halves
+  __bf16* sRl = reinterpret_cast<__bf16*>(smem + C::O_RL);
+  float* sGC = reinterpret_cast<float*>(smem + C::O_GC);     // [DK]
   // the NB value blocks of one (sequence, head) share an XCD (workgroups go
   // round the eight XCDs in order), so their reads of the chunk blocks they
   // all need hit that XCD's L2
@@ -1009,10 +984,28 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
   const int n = nh / a.H, h = nh - n * a.H;
   const int c0 = a.tab ? a.cbase[n] : n * a.nc, c1 = a.tab ? a.cbase[n + 1] : (n + 1) * a.nc;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
-  for (int e = tid; e < DK * DVB; e += SNT) {
-    const int i = e / DVB, j = e - i * DVB;
-    sdST[j * LK + i] = a.dST ? a.dST[(size_t)nh * DK * DV + (size_t)i * DV + jb * DVB + j] : 0.f;
+  // dS_T block: thread e4 takes 4 consecutive key channels i of value column j
+  for (int e4 = tid; e4 < DK * DVB / 4; e4 += SNT) {
+    const int j = e4 / (DK / 4), i = 4 * (e4 - j * (DK / 4));
+    f32x4 s = zero4();
+    if (a.dST) {
+      const float* src = a.dST + (size_t)nh * DK * DV + (size_t)i * DV + jb * DVB + j;
+      s = f32x4{src[0], src[DV], src[2 * DV], src[3 * DV]};
+    }
+    *reinterpret_cast<f32x4*>(sdST + j * LK + i) = s;
+    bf16x4 hi, lo;
+    split_bf16(s, hi, lo);
+    *reinterpret_cast<bf16x4*>(sDh + j * LSB + i) = hi;
+    *reinterpret_cast<bf16x4*>(sDl + j * LSB + i) = lo;
   }
+  __syncthreads();  // the first chunk step saves dS' in another thread mapping
+  auto st_split = [](__bf16* hb, __bf16* lb, int off, const f32x4& x) {
+    bf16x4 hi, lo;
+    split_bf16(x, hi, lo);
+    *reinterpret_cast<bf16x4*>(hb + off) = hi;
+    *reinterpret_cast<bf16x4*>(lb + off) = lo;
+  };
+  const int tn = wv % (DVB / 16);  // column block of every tile of this wavefront
   f32x4 rq[NK4], rk[NK4], ry[NK4], ra[NC4], ro[NV4], rg = zero4();
   if (c0 < c1) sb_load<DK, DV, NK4, NV4, NC4, BF16>(a, c1 - 1, h, jb, tid, rq, rk, ry, ra, ro, rg);
   for (int ci = c1 - 1; ci >= c0; --ci) {
@@ -1020,19 +1013,18 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
 #pragma unroll
     for (int u = 0; u < NK4; ++u) {
       const int e4 = tid + SNT * u, t = e4 / (DK / 4), i = 4 * (e4 - t * (DK / 4));
-      *reinterpret_cast<f32x4*>(sKt + t * LK + i) = rk[u];
-      *reinterpret_cast<f32x4*>(sQg + t * LK + i) = rq[u];
-      *reinterpret_cast<f32x4*>(sY + t * LK + i) = ry[u];
+      st_split(sXh, sXl, t * LSB + i, rk[u]);
+      st_split(sQh, sQl, t * LTB + i, rq[u]);
     }
 #pragma unroll
     for (int u = 0; u < NC4; ++u) {
       const int e4 = tid + SNT * u, t = e4 / (BC / 4), r = 4 * (e4 - t * (BC / 4));
-      *reinterpret_cast<f32x4*>(sAqk + t * LC + r) = ra[u];
+      st_split(sAh, sAl, t * LAB + r, ra[u]);
     }
 #pragma unroll
     for (int u = 0; u < NV4; ++u) {
       const int e4 = tid + SNT * u, t = e4 / (DVB / 4), j = 4 * (e4 - t * (DVB / 4));
-      *reinterpret_cast<f32x4*>(sdO + t * LV + j) = ro[u];
+      st_split(sOh, sOl, t * LOB + j, ro[u]);
     }
     if (tid < DK / 4) *reinterpret_cast<f32x4*>(sGC + 4 * tid) = rg;
     for (int e = tid; e < DK * DVB; e += SNT) {  // dL/d(state leaving chunk ci)
@@ -1040,65 +1032,86 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd_kernel(BwdArgs a) {
       W[L::DSP + (size_t)i * DV + jb * DVB + j] = sdST[j * LK + i];
     }
     __syncthreads();
-    // dR = A_qk^T dO + K_tail dS'  [BC][DVB]
-    for (int t = wv; t < (BC / 16) * (DVB / 16); t += SNT / 64) {
-      const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
-      // A_qk^T and dO both read K-major from their row-major blocks
-      // (the two products as separate chains, the second over alternate K
-      // blocks, summed at the end)
-      f32x4 acc = mma_lds_f32<BC, true, true>(zero4(), sAqk + 16 * tm, LC, sdO + 16 * tn, LV);
-      acc += mma_lds_split<DK, 2>(sKt + 16 * tm * LK, LK, sdST + 16 * tn * LK, LK);
+    // dO fragments (K = the chunk's tokens) shared by every product below
+    bf16x8 oh[2], ol[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      oh[kb] = frag_kmajor(sOh, LOB, 32 * kb, 16 * tn);
+      ol[kb] = frag_kmajor(sOl, LOB, 32 * kb, 16 * tn);
+    }
+    // Q_g^T dO, the first part of the state gradient (tiles t = wv + 8u)
+    f32x4 ds[NPW];
+#pragma unroll
+    for (int u = 0; u < NPW; ++u) {
+      ds[u] = zero4();
+      const int tm = (wv + (SNT / 64) * u) / (DVB / 16);
+      if (tm < DK / 16) {  // uniform per wavefront
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 qh = frag_kmajor(sQh, LTB, 32 * kb, 16 * tm), ql = frag_kmajor(sQl, LTB, 32 * kb, 16 * tm);
+          ds[u] = mma3x(qh, ql, oh[kb], ol[kb], ds[u]);
+        }
+      }
+    }
+    {
+      // dR = A_qk^T dO + K_tail dS', one tile per wavefront, as two chains.
+      // A_qk is lower triangular: A_qk^T rows 16 tm.. need tokens from 16 tm
+      // on, so the first K block is zero for tm >= 2.
+      const int tm = wv / (DVB / 16);
+      f32x4 acc0 = zero4(), acc1 = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (kb == 0 && tm >= 2) continue;  // uniform per wavefront
+        const bf16x8 ah = frag_kmajor(sAh, LAB, 32 * kb, 16 * tm), al = frag_kmajor(sAl, LAB, 32 * kb, 16 * tm);
+        acc0 = mma3x(ah, al, oh[kb], ol[kb], acc0);
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 kh = frag_krow(sXh, LSB, 32 * kb, 16 * tm), kl = frag_krow(sXl, LSB, 32 * kb, 16 * tm);
+        const bf16x8 dh = frag_krow(sDh, LSB, 32 * kb, 16 * tn), dl = frag_krow(sDl, LSB, 32 * kb, 16 * tn);
+        acc1 = mma3x(kh, kl, dh, dl, acc1);
+      }
+      const f32x4 acc = acc0 + acc1;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = 16 * tm + 4 * g + q, j = 16 * tn + m;
         W[L::DR + (size_t)r * DV + jb * DVB + j] = acc[q];
-        sdRT[j * LC + r] = acc[q];
       }
+      st_split(sRh, sRl, (16 * tn + m) * LRB + 16 * tm + 4 * g, -acc);
     }
     __syncthreads();
-    // the previous chunk into the registers stored above (the last iteration
-    // reloads the current one: no branch); issued here, after dR, so that
-    // dR's products start at once
+    // Y over K_tail (every read of K_tail is done), then the previous chunk
+    // into the registers just stored (the last iteration reloads the current
+    // one: no branch)
+#pragma unroll
+    for (int u = 0; u < NK4; ++u) {
+      const int e4 = tid + SNT * u, t = e4 / (DK / 4), i = 4 * (e4 - t * (DK / 4));
+      st_split(sXh, sXl, t * LSB + i, ry[u]);
+    }
     sb_load<DK, DV, NK4, NV4, NC4, BF16>(a, ci - 1 >= c0 ? ci - 1 : ci, h, jb, tid, rq, rk, ry, ra, ro, rg);
-    // dS <- Q_g^T dO + Diag(gamma_C) dS' - Y^T dR  [DK][DVB]; each lane owns its entries
-    constexpr int NSU = (DK / 16) * (DVB / 16);
-    if constexpr (NSU == 2 * (SNT / 64)) {
-      // two tiles per wavefront (t = wv and wv + 8) in one column block tn:
-      // the dO and dR^T fragments of a K step serve four chains, interleaved
-      // (each in ascending K, as one chain at a time)
-      const int tn = wv % (DVB / 16), tm0 = wv / (DVB / 16), tm1 = tm0 + (SNT / 64) / (DVB / 16);
-      f32x4 q0 = zero4(), q1 = zero4(), y0 = zero4(), y1 = zero4();
+    __syncthreads();
+    // dS <- Q_g^T dO - Y^T dR + Diag(gamma_C) dS'; each lane owns its entries
 #pragma unroll
-      for (int k0 = 0; k0 < BC; k0 += 16) {
-        const float* o = sdO + (k0 + 4 * g) * LV + 16 * tn + m;  // dO read K-major
-        const float4 rb = *reinterpret_cast<const float4*>(sdRT + (16 * tn + m) * LC + k0 + 4 * g);
-        const float* xq = sQg + (k0 + 4 * g) * LK + 16 * tm0 + m;  // Q_g, Y read K-major
-        const float* xy = sY + (k0 + 4 * g) * LK + 16 * tm0 + m;
-        const int d1 = 16 * (tm1 - tm0);
-        const float ob[4] = {o[0], o[LV], o[2 * LV], o[3 * LV]};
-        const float rv[4] = {rb.x, rb.y, rb.z, rb.w};
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 rh = frag_krow(sRh, LRB, 32 * kb, 16 * tn), rl = frag_krow(sRl, LRB, 32 * kb, 16 * tn);
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          mfma2(q0, xq[qq * LK], ob[qq], q1, xq[qq * LK + d1], ob[qq]);
-          mfma2(y0, xy[qq * LK], rv[qq], y1, xy[qq * LK + d1], rv[qq]);
+      for (int u = 0; u < NPW; ++u) {
+        const int tm = (wv + (SNT / 64) * u) / (DVB / 16);
+        if (tm < DK / 16) {
+          const bf16x8 yh = frag_kmajor(sXh, LSB, 32 * kb, 16 * tm), yl = frag_kmajor(sXl, LSB, 32 * kb, 16 * tm);
+          ds[u] = mma3x(yh, yl, rh, rl, ds[u]);
         }
       }
+    }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int i0 = 16 * tm0 + 4 * g + q, i1 = 16 * tm1 + 4 * g + q, j = 16 * tn + m;
-        sdST[j * LK + i0] = q0[q] + sGC[i0] * sdST[j * LK + i0] - y0[q];
-        sdST[j * LK + i1] = q1[q] + sGC[i1] * sdST[j * LK + i1] - y1[q];
-      }
-    } else {
-      for (int t = wv; t < NSU; t += SNT / 64) {
-        const int tm = t / (DVB / 16), tn = t - tm * (DVB / 16);
-        const f32x4 acc = mma_lds_f32<BC, true, true>(zero4(), sQg + 16 * tm, LK, sdO + 16 * tn, LV);
-        const f32x4 acy = mma_lds_f32<BC, true, false>(zero4(), sY + 16 * tm, LK, sdRT + 16 * tn * LC, LC);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int i = 16 * tm + 4 * g + q, j = 16 * tn + m;
-          sdST[j * LK + i] = acc[q] + sGC[i] * sdST[j * LK + i] - acy[q];
-        }
+    for (int u = 0; u < NPW; ++u) {
+      const int tm = (wv + (SNT / 64) * u) / (DVB / 16), i = 16 * tm + 4 * g, j = 16 * tn + m;
+      if (tm < DK / 16) {
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(sdST + j * LK + i);
+        const f32x4 gc = *reinterpret_cast<const f32x4*>(sGC + i);
+        const f32x4 d = ds[u] + gc * d0;
+        *reinterpret_cast<f32x4*>(sdST + j * LK + i) = d;
+        st_split(sDh, sDl, j * LSB + i, d);
       }
     }
     __syncthreads();
@@ -1729,19 +1742,18 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   if (items > 0) GDR2_CK((launch_front<DK, DV, false>(a, gi, st)));  // decay, T, A_qk, A, Y and U
   // sequential passes (with no chunks they only pass dS_T through to dS0)
   {
-    constexpr int LK = DK + 4, LC = BC + 4;
     constexpr size_t lf = StateF3Cfg<DK>::BYTES;
-    const size_t lb = (size_t)(DVB * LK + BC * LC + BC * (DVB + 4) + 3 * BC * LK + DVB * LC + DK) * 4;
+    constexpr size_t lb = StateB3Cfg<DK>::BYTES;
     GDR2_LDS((bwd_state_fwd3_kernel<DK, DV>), lf);
     const dim3 gs((unsigned)(((size_t)a.N * a.H + 7) / 8 * 8 * (DV / DVB)));
     hipLaunchKernelGGL((bwd_state_fwd3_kernel<DK, DV>), gs, dim3(SNT), lf, st, a);
     GDR2_CK(hipGetLastError());
     if (a.in_bf16) {
-      GDR2_LDS((bwd_state_bwd_kernel<DK, DV, true>), lb);
-      hipLaunchKernelGGL((bwd_state_bwd_kernel<DK, DV, true>), gs, dim3(SNT), lb, st, a);
+      GDR2_LDS((bwd_state_bwd3_kernel<DK, DV, true>), lb);
+      hipLaunchKernelGGL((bwd_state_bwd3_kernel<DK, DV, true>), gs, dim3(SNT), lb, st, a);
     } else {
-      GDR2_LDS((bwd_state_bwd_kernel<DK, DV, false>), lb);
-      hipLaunchKernelGGL((bwd_state_bwd_kernel<DK, DV, false>), gs, dim3(SNT), lb, st, a);
+      GDR2_LDS((bwd_state_bwd3_kernel<DK, DV, false>), lb);
+      hipLaunchKernelGGL((bwd_state_bwd3_kernel<DK, DV, false>), gs, dim3(SNT), lb, st, a);
     }
     GDR2_CK(hipGetLastError());
   }
@@ -1777,9 +1789,9 @@ hipError_t launch_fwd32_t(const BwdArgs& a, hipStream_t st) {
   if (items > 0) GDR2_CK((launch_front<DK, DV, true>(a, dim3(items), st)));
   constexpr size_t lf = state_fwd_lds<DK, true>();
   static_assert(lf <= 160 * 1024, "LDS budget exceeded");
-  GDR2_LDS((bwd_state_fwd_kernel<DK, DV, true>), lf);
+  GDR2_LDS((fwd32_state_kernel<DK, DV>), lf);
   const dim3 gs((unsigned)(((size_t)a.N * a.H + 7) / 8 * 8 * (DV / DVB)));
-  hipLaunchKernelGGL((bwd_state_fwd_kernel<DK, DV, true>), gs, dim3(SNT), lf, st, a);
+  hipLaunchKernelGGL((fwd32_state_kernel<DK, DV>), gs, dim3(SNT), lf, st, a);
   return hipGetLastError();
 }
 
