@@ -328,6 +328,12 @@ __device__ __forceinline__ void front_item(const BwdArgs& a, const int item) {
   }
   constexpr bool strong = SM == 1;
   float *sEP = sm + C::O_EP, *sKP = sm + C::O_KP, *sQP = sm + C::O_QP;
+  // The backward's main launch multiplies E', K' and Q' (phase 3 only) as
+  // bf16 hi/lo halves (mma3x); the fp32 forward and the strong launch keep
+  // fp32 operands.
+  constexpr bool SPLIT = !FWD && SM == 0;
+  __bf16 *bEP = reinterpret_cast<__bf16*>(sEP), *bKP = reinterpret_cast<__bf16*>(sKP),
+         *bQP = reinterpret_cast<__bf16*>(sQP);
   f32x4 pg[NEK];  // G of this thread's units, for E in phase 5
 #pragma unroll
   for (int u = 0; u < NEK; ++u) {
@@ -350,9 +356,24 @@ __device__ __forceinline__ void front_item(const BwdArgs& a, const int item) {
     const int wo = r * DK + 4 * i4;
     *reinterpret_cast<f32x4*>(W + L::QG + wo) = QG;
     *reinterpret_cast<f32x4*>(W + L::KT + wo) = KT;
-    *reinterpret_cast<f32x4*>(sEP + o) = EP;
-    *reinterpret_cast<f32x4*>(sKP + o) = KP;
-    *reinterpret_cast<f32x4*>(sQP + o) = QP;
+    if constexpr (SPLIT) {
+      // hi halves of row r at [0, DK), lo halves at [DK, 2 DK): the bytes of the fp32 row
+      const int ob = r * (2 * LKP) + 4 * i4;
+      bf16x4 hi, lo;
+      split_bf16(EP, hi, lo);
+      *reinterpret_cast<bf16x4*>(bEP + ob) = hi;
+      *reinterpret_cast<bf16x4*>(bEP + ob + DK) = lo;
+      split_bf16(KP, hi, lo);
+      *reinterpret_cast<bf16x4*>(bKP + ob) = hi;
+      *reinterpret_cast<bf16x4*>(bKP + ob + DK) = lo;
+      split_bf16(QP, hi, lo);
+      *reinterpret_cast<bf16x4*>(bQP + ob) = hi;
+      *reinterpret_cast<bf16x4*>(bQP + ob + DK) = lo;
+    } else {
+      *reinterpret_cast<f32x4*>(sEP + o) = EP;
+      *reinterpret_cast<f32x4*>(sKP + o) = KP;
+      *reinterpret_cast<f32x4*>(sQP + o) = QP;
+    }
   }
   // v and w for Z, loaded while the products run
   f32x4 pv[NEV], pw[NEV];
@@ -387,7 +408,22 @@ __device__ __forceinline__ void front_item(const BwdArgs& a, const int item) {
     if (p < 10) {  // uniform
       int tm, tn;
       low_tile(p, tm, tn);
-      if (strong) {
+      if constexpr (SPLIT) {
+        // the two products share K''s fragments: two chains, interleaved
+        constexpr int LH = 2 * LKP;
+#pragma unroll
+        for (int k0 = 0; k0 < DK; k0 += 32) {
+          const bf16x8 kh = frag_krow(bKP, LH, k0, 16 * tn), kl = frag_krow(bKP, LH, DK + k0, 16 * tn);
+          const bf16x8 eh = frag_krow(bEP, LH, k0, 16 * tm), el = frag_krow(bEP, LH, DK + k0, 16 * tm);
+          const bf16x8 qh = frag_krow(bQP, LH, k0, 16 * tm), ql = frag_krow(bQP, LH, DK + k0, 16 * tm);
+          aT[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(el, kh, aT[u], 0, 0, 0);
+          aQ[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql, kh, aQ[u], 0, 0, 0);
+          aT[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(eh, kl, aT[u], 0, 0, 0);
+          aQ[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, kl, aQ[u], 0, 0, 0);
+          aT[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(eh, kh, aT[u], 0, 0, 0);
+          aQ[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, kh, aQ[u], 0, 0, 0);
+        }
+      } else if (strong) {
         aT[u] = decay_product<DK, LKP>(sEP, sKP, sG, 16 * tm + 4 * g, 16 * tn + m);
         aQ[u] = decay_product<DK, LKP>(sQP, sKP, sG, 16 * tm + 4 * g, 16 * tn + m);
       } else {
@@ -1147,6 +1183,26 @@ __global__ __launch_bounds__(SNT, 1) void bwd_state_bwd3_kernel(BwdArgs a) {
 // phase's global loads are issued into registers one phase (or one slice)
 // ahead, so they overlap the products of the phase before.  Rows past the
 // end of a sequence read a clamped (valid) row and are zeroed in registers.
+// One [16][16] tile of M X for a triangular M over the chunk's 64 tokens,
+// from bf16 hi/lo halves: M row-major with its 64 hi then 64 lo halves per row
+// (pitch LHA), X a [64][DK] block whose rows are tokens, read down its columns
+// (pitch LH, hi halves at column c, lo at DK + c).  Rows 16 tm.. of M are zero
+// before token 16 tm when UPPER (M strictly upper triangular), or from token
+// 16 (tm + 1) on otherwise, so only the K = 32 blocks that can be nonzero run.
+template <int LHA, int LH, bool UPPER>
+__device__ __forceinline__ f32x4 tri3x(const float* M, const float* X, int tm, int tn) {
+  constexpr int DK = (LH - 8) / 2;
+  const __bf16 *bm = reinterpret_cast<const __bf16*>(M), *bx = reinterpret_cast<const __bf16*>(X);
+  f32x4 acc = zero4();
+#pragma unroll
+  for (int k0 = 0; k0 < BC; k0 += 32) {
+    if (UPPER ? k0 + 32 <= 16 * tm : k0 >= 16 * (tm + 1)) continue;  // uniform
+    acc = mma3x(frag_krow(bm, LHA, k0, 16 * tm), frag_krow(bm, LHA, BC + k0, 16 * tm),
+                frag_kmajor(bx, LH, k0, 16 * tn), frag_kmajor(bx, LH, k0, DK + 16 * tn), acc);
+  }
+  return acc;
+}
+
 template <int DK, int DV>
 struct OutCfg {
   static constexpr int NT = 512, NWV = 8, KC = 32, LS = KC + 4, LA = BC + 4, LKP = DK + 4;
@@ -1408,6 +1464,29 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
     pB[u] = f32x4{t[0], t[1], t[2], t[3]} * z;
   }
   float *sDY = sm + C::O_DY, *sEB = sm + C::O_EB, *sDYT = sm + C::O_DYT;
+  // a strong chunk (flagged by the front pass) forms its decay-weighted
+  // products exactly, with G in E''s place
+  constexpr bool strong = SM == 1;
+  // The main launch multiplies dY, E, E', Q', K', dA_qk and dT (phases 2a,
+  // 2b and 4) as bf16 hi/lo halves (mma3x): a [64][DK] block keeps a row's
+  // DK hi halves, then its DK lo halves (pitch LHK), a [64][64] block its 64
+  // hi then 64 lo halves (pitch LHA), in the bytes of the fp32 rows.  The
+  // products with A (X = A^T dY, phase 3) and the strong launch stay fp32.
+  constexpr bool SPLIT = SM == 0;
+  constexpr int LHK = 2 * LKP, LHA = 2 * LA;
+  auto st_h = [](float* base, int ld, int off, int row, int col, float x) {
+    __bf16* b = reinterpret_cast<__bf16*>(base) + row * ld + col;
+    const __bf16 hi = (__bf16)x;
+    b[0] = hi;
+    b[off] = (__bf16)(x - (float)hi);
+  };
+  auto st_h4 = [](float* base, int ld, int off, int row, int col, const f32x4& x) {
+    __bf16* b = reinterpret_cast<__bf16*>(base) + row * ld + col;
+    bf16x4 hi, lo;
+    split_bf16(x, hi, lo);
+    *reinterpret_cast<bf16x4*>(b) = hi;
+    *reinterpret_cast<bf16x4*>(b + off) = lo;
+  };
 #pragma unroll
   for (int u = 0; u < NKT; ++u) {
     const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
@@ -1415,13 +1494,11 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
     for (int q = 0; q < 4; ++q) {
       const int r = 16 * tm + 4 * g + q, i = 16 * tn + m;
       const float y = -aY[u][q];
-      sDY[r * LKP + i] = y;
+      if constexpr (SPLIT) st_h(sDY, LHK, DK, r, i, y);
+      else sDY[r * LKP + i] = y;
       sDYT[i * LA + r] = y;
     }
   }
-  // a strong chunk (flagged by the front pass) forms its decay-weighted
-  // products exactly, with G in E''s place
-  constexpr bool strong = SM == 1;
   // E = gamma b k and E' = e1 b k (the forms of the front pass, same order
   // of operations), e1 = exp(G - G_31)
   float* sEP = sm + C::O_EP;
@@ -1435,8 +1512,13 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
       eb[c] = gam * pB[u][c] * pK[u][c];
       ep[c] = strong ? G : e1 * pB[u][c] * pK[u][c];
     }
-    *reinterpret_cast<f32x4*>(sEB + o) = eb;
-    *reinterpret_cast<f32x4*>(sEP + o) = ep;
+    if constexpr (SPLIT) {
+      st_h4(sEB, LHK, DK, s, 4 * i4, eb);
+      st_h4(sEP, LHK, DK, s, 4 * i4, ep);
+    } else {
+      *reinterpret_cast<f32x4*>(sEB + o) = eb;
+      *reinterpret_cast<f32x4*>(sEP + o) = ep;
+    }
   }
   __syncthreads();
   f32x4 pQ[NEK];
@@ -1452,8 +1534,16 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
 #pragma unroll
   for (int u = 0; u < NCT; ++u) {
     const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
-    // a chain of its own, added to the bf16 chain of phase 1 (one MFMA shape per chain)
-    aA[u] += mma_lds<float, DK>(zero4(), sDY + 16 * tm * LKP, LKP, sEB + 16 * tn * LKP, LKP);
+    if constexpr (SPLIT) {
+      const __bf16 *bY = reinterpret_cast<const __bf16*>(sDY), *bE = reinterpret_cast<const __bf16*>(sEB);
+#pragma unroll
+      for (int k0 = 0; k0 < DK; k0 += 32)
+        aA[u] = mma3x(frag_krow(bY, LHK, k0, 16 * tm), frag_krow(bY, LHK, DK + k0, 16 * tm),
+                      frag_krow(bE, LHK, k0, 16 * tn), frag_krow(bE, LHK, DK + k0, 16 * tn), aA[u]);
+    } else {
+      // a chain of its own, added to the bf16 chain of phase 1 (one MFMA shape per chain)
+      aA[u] += mma_lds<float, DK>(zero4(), sDY + 16 * tm * LKP, LKP, sEB + 16 * tn * LKP, LKP);
+    }
   }
 #pragma unroll
   for (int u = 0; u < NKT; ++u) {
@@ -1474,8 +1564,13 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
       // strictly lower: the diagonal of dA_qk is kept apart (sDQK), so that
       // its two equal and opposite terms in dg never meet in a sum
       const float v = (tn <= tm && c < r) ? aAQ[u][q] : 0.f;
-      sAQ[r * LA + c] = v;
-      sAQT[c * LA + r] = v;
+      if constexpr (SPLIT) {
+        st_h(sAQ, LHA, BC, r, c, v);
+        st_h(sAQT, LHA, BC, c, r, v);
+      } else {
+        sAQ[r * LA + c] = v;
+        sAQT[c * LA + r] = v;
+      }
       if (c == r) sm[C::O_DQK + r] = aAQ[u][q];
     }
   }
@@ -1490,22 +1585,25 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
       qp[c] = strong ? pQ[u][c] : exp_dec(G - G31) * pQ[u][c];
       kp[c] = strong ? pK[u][c] : exp_dec(G31 - G) * pK[u][c];
     }
-    *reinterpret_cast<f32x4*>(sQP + s * LKP + 4 * i4) = qp;
-    *reinterpret_cast<f32x4*>(sKP + s * LKP + 4 * i4) = kp;
+    if constexpr (SPLIT) {
+      st_h4(sQP, LHK, DK, s, 4 * i4, qp);
+      st_h4(sKP, LHK, DK, s, 4 * i4, kp);
+    } else {
+      *reinterpret_cast<f32x4*>(sQP + s * LKP + 4 * i4) = qp;
+      *reinterpret_cast<f32x4*>(sKP + s * LKP + 4 * i4) = kp;
+    }
   }
   __syncthreads();
   f32x4 aP3[NKT], aP4[NKT];
 #pragma unroll
   for (int u = 0; u < NKT; ++u) {
     const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
-    if (strong) {  // sEP holds G
+    if constexpr (SPLIT) {
+      aP3[u] = tri3x<LHA, LHK, true>(sAQT, sQP, tm, tn);
+      aP4[u] = tri3x<LHA, LHK, false>(sAQ, sKP, tm, tn);
+    } else {  // the strong launch: sEP holds G
       aP3[u] = decay_tri<LA, LKP, false>(sAQT, sQP, sEP, 16 * tm + 4 * g, 16 * tn + m, 16 * tm, BC);
       aP4[u] = decay_tri<LA, LKP, true>(sAQ, sKP, sEP, 16 * tm + 4 * g, 16 * tn + m, 0, 16 * (tm + 1));
-    } else {
-      aP3[u] = mma_lds_f32<BC, false, true>(zero4(), sAQT + 16 * tm * LA + 16 * tm, LA,
-                                            sQP + 16 * tm * LKP + 16 * tn, LKP, BC - 16 * tm);
-      aP4[u] = mma_lds_f32<BC, false, true>(zero4(), sAQ + 16 * tm * LA, LA, sKP + 16 * tn, LKP,
-                                            16 * (tm + 1));
     }
   }
   __syncthreads();
@@ -1549,8 +1647,13 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
     for (int q = 0; q < 4; ++q) {
       const int r = 16 * tm + 4 * g + q, c = 16 * tn + m;
       const float v = c < r ? -aT[u][q] : 0.f;
-      sDT[r * LA + c] = v;
-      sDTT[c * LA + r] = v;
+      if constexpr (SPLIT) {
+        st_h(sDT, LHA, BC, r, c, v);
+        st_h(sDTT, LHA, BC, c, r, v);
+      } else {
+        sDT[r * LA + c] = v;
+        sDTT[c * LA + r] = v;
+      }
     }
   }
   __syncthreads();
@@ -1593,9 +1696,8 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
 #pragma unroll
     for (int u = 0; u < NKT; ++u) {
       const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
-      aP1[u] = mma_lds_f32<BC, false, true>(zero4(), sDT + 16 * tm * LA, LA, sKP + 16 * tn, LKP, 16 * (tm + 1));
-      aP2[u] = mma_lds_f32<BC, false, true>(zero4(), sDTT + 16 * tm * LA + 16 * tm, LA,
-                                            sEP + 16 * tm * LKP + 16 * tn, LKP, BC - 16 * tm);
+      aP1[u] = tri3x<LHA, LHK, false>(sDT, sKP, tm, tn);
+      aP2[u] = tri3x<LHA, LHK, true>(sDTT, sEP, tm, tn);
     }
   }
   __syncthreads();
