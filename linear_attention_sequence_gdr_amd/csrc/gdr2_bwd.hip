@@ -1203,6 +1203,24 @@ __device__ __forceinline__ f32x4 tri3x(const float* M, const float* X, int tm, i
   return acc;
 }
 
+// One [16][16] tile of A^T X over the chunk's 64 tokens, from bf16 hi/lo
+// halves (pitch LHA: a row's 64 hi then 64 lo halves): A row-major and lower
+// triangular (its transpose read down the columns), X given transposed (row
+// n of XT holds X[.][n] along the tokens).  Rows 16 tm.. of A^T are zero
+// before token 16 tm, so a K = 32 block wholly before it is skipped.
+template <int LHA>
+__device__ __forceinline__ f32x4 at3x(const float* A, const float* XT, int tm, int tn) {
+  const __bf16 *ba = reinterpret_cast<const __bf16*>(A), *bx = reinterpret_cast<const __bf16*>(XT);
+  f32x4 acc = zero4();
+#pragma unroll
+  for (int k0 = 0; k0 < BC; k0 += 32) {
+    if (k0 + 32 <= 16 * tm) continue;  // uniform
+    acc = mma3x(frag_kmajor(ba, LHA, k0, 16 * tm), frag_kmajor(ba, LHA, k0, BC + 16 * tm),
+                frag_krow(bx, LHA, k0, 16 * tn), frag_krow(bx, LHA, BC + k0, 16 * tn), acc);
+  }
+  return acc;
+}
+
 template <int DK, int DV>
 struct OutCfg {
   static constexpr int NT = 512, NWV = 8, KC = 32, LS = KC + 4, LA = BC + 4, LKP = DK + 4;
@@ -1270,6 +1288,26 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
   const size_t kr = (size_t)a.H * DK, vr = (size_t)a.H * DV;
   float* sA = sm + C::O_A;
+  // The main launch multiplies every block but the value slices' fp32 copies
+  // (sW, sV) as bf16 hi/lo halves (mma3x): a [64][DK] block keeps a row's DK
+  // hi halves, then its DK lo halves (pitch LHK), a [.][64] block its 64 hi
+  // then 64 lo halves (pitch LHA), in the bytes of the fp32 rows.  The strong
+  // launch keeps fp32 blocks and products.
+  constexpr bool SPLIT = SM == 0;
+  constexpr int LHK = 2 * LKP, LHA = 2 * LA;
+  auto st_h = [](float* base, int ld, int off, int row, int col, float x) {
+    __bf16* b = reinterpret_cast<__bf16*>(base) + row * ld + col;
+    const __bf16 hi = (__bf16)x;
+    b[0] = hi;
+    b[off] = (__bf16)(x - (float)hi);
+  };
+  auto st_h4 = [](float* base, int ld, int off, int row, int col, const f32x4& x) {
+    __bf16* b = reinterpret_cast<__bf16*>(base) + row * ld + col;
+    bf16x4 hi, lo;
+    split_bf16(x, hi, lo);
+    *reinterpret_cast<bf16x4*>(b) = hi;
+    *reinterpret_cast<bf16x4*>(b + off) = lo;
+  };
   // Products with a triangular left factor over the chunk's 64 rows run over
   // its nonzero K range only, for row tile tm: a lower-triangular factor has
   // no columns past 16 (tm + 1), an upper-triangular one none before 16 tm
@@ -1311,7 +1349,9 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
 #pragma unroll
   for (int u = 0; u < NAA; ++u) {
     const int e = tid + NT * u, s = e / (BC / 4), c4 = e - s * (BC / 4);
-    *reinterpret_cast<f32x4*>(sA + s * LA + 4 * c4) = *reinterpret_cast<const f32x4*>(W + L::A + s * BC + 4 * c4);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(W + L::A + s * BC + 4 * c4);
+    if constexpr (SPLIT) st_h4(sA, LHA, BC, s, 4 * c4, x);
+    else *reinterpret_cast<f32x4*>(sA + s * LA + 4 * c4) = x;
   }
   if (tid < DK) {
     sm[C::O_G31 + tid] = W[L::G + 31 * DK + tid];
@@ -1358,7 +1398,10 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
       *reinterpret_cast<f32x4*>(sW + o) = pW;
       *reinterpret_cast<f32x4*>(sV + o) = pV;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) sDRT[(4 * sc4 + q) * LA + ss] = pDR[q];
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (SPLIT) st_h(sDRT, LHA, BC, 4 * sc4 + q, ss, pDR[q]);
+        else sDRT[(4 * sc4 + q) * LA + ss] = pDR[q];
+      }
 #pragma unroll
       for (int u = 0; u < NSK; ++u) {
         const int e = tid + NT * u;
@@ -1421,8 +1464,10 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
     }
     {  // dZ = A^T dR over this slice's 32 value channels: one [16][16] tile per wavefront
       const int tm = wv >> 1, tn = wv & 1;
-      const f32x4 z = mma_lds_f32<BC, true, false>(zero4(), sA + 16 * tm * LA + 16 * tm, LA,
-                                                   sDRT + 16 * tn * LA + 16 * tm, LA, BC - 16 * tm);
+      f32x4 z;
+      if constexpr (SPLIT) z = at3x<LHA>(sA, sDRT, tm, tn);
+      else z = mma_lds_f32<BC, true, false>(zero4(), sA + 16 * tm * LA + 16 * tm, LA,
+                                            sDRT + 16 * tn * LA + 16 * tm, LA, BC - 16 * tm);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = 16 * tm + 4 * g + q, c = 16 * tn + m;
@@ -1467,26 +1512,6 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
   // a strong chunk (flagged by the front pass) forms its decay-weighted
   // products exactly, with G in E''s place
   constexpr bool strong = SM == 1;
-  // The main launch multiplies dY, E, E', Q', K', dA_qk and dT (phases 2a,
-  // 2b and 4) as bf16 hi/lo halves (mma3x): a [64][DK] block keeps a row's
-  // DK hi halves, then its DK lo halves (pitch LHK), a [64][64] block its 64
-  // hi then 64 lo halves (pitch LHA), in the bytes of the fp32 rows.  The
-  // products with A (X = A^T dY, phase 3) and the strong launch stay fp32.
-  constexpr bool SPLIT = SM == 0;
-  constexpr int LHK = 2 * LKP, LHA = 2 * LA;
-  auto st_h = [](float* base, int ld, int off, int row, int col, float x) {
-    __bf16* b = reinterpret_cast<__bf16*>(base) + row * ld + col;
-    const __bf16 hi = (__bf16)x;
-    b[0] = hi;
-    b[off] = (__bf16)(x - (float)hi);
-  };
-  auto st_h4 = [](float* base, int ld, int off, int row, int col, const f32x4& x) {
-    __bf16* b = reinterpret_cast<__bf16*>(base) + row * ld + col;
-    bf16x4 hi, lo;
-    split_bf16(x, hi, lo);
-    *reinterpret_cast<bf16x4*>(b) = hi;
-    *reinterpret_cast<bf16x4*>(b + off) = lo;
-  };
 #pragma unroll
   for (int u = 0; u < NKT; ++u) {
     const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
@@ -1496,7 +1521,8 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
       const float y = -aY[u][q];
       if constexpr (SPLIT) st_h(sDY, LHK, DK, r, i, y);
       else sDY[r * LKP + i] = y;
-      sDYT[i * LA + r] = y;
+      if constexpr (SPLIT) st_h(sDYT, LHA, BC, i, r, y);
+      else sDYT[i * LA + r] = y;
     }
   }
   // E = gamma b k and E' = e1 b k (the forms of the front pass, same order
@@ -1548,8 +1574,9 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
 #pragma unroll
   for (int u = 0; u < NKT; ++u) {
     const int t = wv + NWV * u, tm = t / TNK, tn = t - tm * TNK;
-    aX[u] = mma_lds_f32<BC, true, false>(zero4(), sA + 16 * tm * LA + 16 * tm, LA,
-                                         sDYT + 16 * tn * LA + 16 * tm, LA, BC - 16 * tm);
+    if constexpr (SPLIT) aX[u] = at3x<LHA>(sA, sDYT, tm, tn);
+    else aX[u] = mma_lds_f32<BC, true, false>(zero4(), sA + 16 * tm * LA + 16 * tm, LA,
+                                              sDYT + 16 * tn * LA + 16 * tm, LA, BC - 16 * tm);
   }
   __syncthreads();
 
@@ -1614,16 +1641,24 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
   for (int u = 0; u < NCT; ++u) {
     const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) sDAT[(16 * tn + m) * LA + 16 * tm + 4 * g + q] = aA[u][q];
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (SPLIT) st_h(sDAT, LHA, BC, 16 * tn + m, 16 * tm + 4 * g + q, aA[u][q]);
+      else sDAT[(16 * tn + m) * LA + 16 * tm + 4 * g + q] = aA[u][q];
+    }
   }
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < NCT; ++u) {
     const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
-    const f32x4 w4 = mma_lds_f32<BC, true, false>(zero4(), sA + 16 * tm * LA + 16 * tm, LA,
-                                                  sDAT + 16 * tn * LA + 16 * tm, LA, BC - 16 * tm);
+    f32x4 w4;
+    if constexpr (SPLIT) w4 = at3x<LHA>(sA, sDAT, tm, tn);
+    else w4 = mma_lds_f32<BC, true, false>(zero4(), sA + 16 * tm * LA + 16 * tm, LA,
+                                           sDAT + 16 * tn * LA + 16 * tm, LA, BC - 16 * tm);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) sWM[(16 * tm + 4 * g + q) * LA + 16 * tn + m] = w4[q];
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (SPLIT) st_h(sWM, LHA, BC, 16 * tm + 4 * g + q, 16 * tn + m, w4[q]);
+      else sWM[(16 * tm + 4 * g + q) * LA + 16 * tn + m] = w4[q];
+    }
   }
   __syncthreads();
   f32x4 aT[NCT];
@@ -1632,9 +1667,21 @@ __device__ __forceinline__ void out_item(const BwdArgs& a, const int item) {
     const int t = wv + NWV * u, tm = t >> 2, tn = t & 3;
     // A is unit lower triangular: column block tn of A^T has no rows past
     // 16 (tn + 1); tiles above the diagonal are masked out below
-    aT[u] = tn <= tm ? mma_lds_f32<BC, false, false>(zero4(), sWM + 16 * tm * LA, LA, sA + 16 * tn * LA, LA,
+    if constexpr (SPLIT) {
+      aT[u] = zero4();
+      if (tn <= tm) {  // uniform
+        const __bf16 *bw = reinterpret_cast<const __bf16*>(sWM), *ba = reinterpret_cast<const __bf16*>(sA);
+#pragma unroll
+        for (int k0 = 0; k0 < BC; k0 += 32)
+          if (k0 < 16 * (tn + 1))
+            aT[u] = mma3x(frag_krow(bw, LHA, k0, 16 * tm), frag_krow(bw, LHA, BC + k0, 16 * tm),
+                          frag_krow(ba, LHA, k0, 16 * tn), frag_krow(ba, LHA, BC + k0, 16 * tn), aT[u]);
+      }
+    } else {
+      aT[u] = tn <= tm ? mma_lds_f32<BC, false, false>(zero4(), sWM + 16 * tm * LA, LA, sA + 16 * tn * LA, LA,
                                                      16 * (tn + 1))
                      : zero4();
+    }
   }
   __syncthreads();
 
