@@ -31,12 +31,12 @@
 //   bwd_out_kernel        per item: every output-path and WY-gradient product
 //                         and the gradients themselves (E, E', K', Q' are
 //                         formed again from G, q, k, b rather than stored).
-// The products run from LDS-staged operands with fp32 accumulation: on fp32
-// MFMA (16x16x4) in the front pass and in phases 2-4 of the output pass; in
-// the two sequential passes and the output pass's value-slice phase as three
-// bf16 MFMAs over hi/lo operand halves (mma3x, about 2^-16 of each term).
-// The fp32 forward (fwd32_state_kernel after the front pass) keeps fp32
-// products throughout.
+// The products run from LDS-staged operands with fp32 accumulation.  In the
+// main launches of the backward they run as three bf16 MFMAs over hi/lo
+// operand halves (mma3x, about 2^-16 of each term), except the front pass's
+// WY inverse and Y = A E, U = A Z, which stay on fp32 MFMA (16x16x4).  The
+// launches that form strongly decaying chunks, and the fp32 forward (the
+// front pass, then fwd32_state_kernel), keep fp32 products throughout.
 #include <hip/hip_runtime.h>
 
 #include "gdr2_device.h"
