@@ -103,6 +103,26 @@ def test_backward_empty_sequence_passes_state_gradient():
     assert torch.equal(gr["dS0"], dST)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_backward_cotangent_scaling_is_exact(dtype):
+    """The gradients are linear in (dL/do, dL/dS_T), and every product of the
+    backward has one factor that carries the cotangents and one that does not.
+    Scaling both cotangents by 2^a therefore scales every gradient by exactly
+    2^a, bit for bit, as long as nothing overflows or leaves the normal range:
+    the bf16 hi/lo split of an operand commutes with a power-of-two scale, so
+    the three-product path has the range of fp32.  Checked at a = 64 and -40
+    (gradients near 1e19 and 1e-12 times their unscaled size)."""
+    wl = I.make_forward(1, 200, 2, 128, 128, dtype=dtype, s0_std=0.1, seed=79)
+    dO, dST = I.cotangents(wl, seed=80)
+    base = run_bwd(wl, dO, dST)
+    for a in (64, -40):
+        f = 2.0 ** a
+        gr = run_bwd(wl, (dO.float() * f).to(dO.dtype), dST * f)
+        for n in ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dS0"):
+            assert torch.isfinite(gr[n]).all(), (a, n)
+            assert torch.equal(gr[n], base[n] * f), (a, n, (gr[n] - base[n] * f).abs().max().item())
+
+
 def test_backward_training_shape():
     """B4 T4096 H16 d128 bf16 (the benchmark's forward workload) with random
     cotangents, against the oracle on every (sequence, head) chain."""
