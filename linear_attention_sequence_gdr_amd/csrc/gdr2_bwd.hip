@@ -214,6 +214,34 @@ __device__ __forceinline__ void tri_rows(const float* sA, const float* sB, int w
   }
 }
 
+// tri_rows from bf16 hi/lo halves (mma3x): A with a row's 64 hi then 64 lo
+// halves (pitch LHA), B with a row's NB hi then NB lo halves (pitch LHB),
+// read down its columns; K = 32 blocks past A's triangle are skipped.
+template <int NU, int TN, int LHA, int LHB, int NB>
+__device__ __forceinline__ void tri_rows3(const __bf16* bA, const __bf16* bB, int wv, float* X, int ldx) {
+  static_assert(8 % TN == 0, "the column tile is the same for every u");
+  const int tn = wv % TN, m = lane_id() & 15, g = lane_id() >> 4;
+  f32x4 acc[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) acc[u] = zero4();
+#pragma unroll
+  for (int k0 = 0; k0 < BC; k0 += 32) {
+    const bf16x8 bh = frag_kmajor(bB, LHB, k0, 16 * tn), bl = frag_kmajor(bB, LHB, k0, NB + 16 * tn);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int tm = (wv + 8 * u) / TN;
+      if (k0 < 16 * (tm + 1))  // uniform
+        acc[u] = mma3x(frag_krow(bA, LHA, k0, 16 * tm), frag_krow(bA, LHA, BC + k0, 16 * tm), bh, bl, acc[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int tm = (wv + 8 * u) / TN;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) X[(size_t)(16 * tm + 4 * g + q) * ldx + 16 * tn + m] = acc[u][q];
+  }
+}
+
 template <int DK, int DV>
 struct FrontCfg {
   static constexpr int NT = 512, LA = BC + 4, LKP = DK + 4, LM = 20;
@@ -225,7 +253,9 @@ struct FrontCfg {
                        E2 = O_M + 3 * 16 * LM;
   // phase 5: E [64][DK], Z [64][DV] (row-major, read K-major)
   static constexpr int LZ = DV + 4;
-  static constexpr int O_EB = E2, O_Z = O_EB + BC * LKP, E3 = O_Z + BC * LZ;
+  static constexpr int O_EB = E2, O_Z = O_EB + BC * LKP, O_AS = O_Z + BC * LZ;
+  // the backward's main launch: A as bf16 hi/lo halves, 64 hi then 64 lo per row
+  static constexpr int E3 = O_AS + BC * LA;
   static constexpr int O_PS = E1 > E3 ? E1 : E3, FLOATS = O_PS + NT;
   static constexpr size_t BYTES = (size_t)FLOATS * 4;
   static_assert(BYTES <= 160 * 1024, "LDS budget exceeded");
@@ -533,11 +563,23 @@ __device__ __forceinline__ void front_item(const BwdArgs& a, const int item) {
 
   // ---- phase 5 ----
   float *sEB = sm + C::O_EB, *sZ = sm + C::O_Z;
+  // The backward's main launch runs Y and U on hi/lo halves too: A's into a
+  // region of their own (A itself stays fp32 for the workspace), E's and Z's
+  // in the bytes of their fp32 rows (hi halves first, pitch twice the fp32
+  // one).
+  __bf16 *bAS = reinterpret_cast<__bf16*>(sm + C::O_AS), *bEB = reinterpret_cast<__bf16*>(sEB),
+         *bZ = reinterpret_cast<__bf16*>(sZ);
 #pragma unroll
   for (int u = 0; u < NAA; ++u) {
     const int e = tid + NT * u, s = e / (BC / 4), c4 = e - s * (BC / 4);
-    if constexpr (!FWD)
-      *reinterpret_cast<f32x4*>(W + L::A + s * BC + 4 * c4) = *reinterpret_cast<const f32x4*>(sA + s * LA + 4 * c4);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(sA + s * LA + 4 * c4);
+    if constexpr (!FWD) *reinterpret_cast<f32x4*>(W + L::A + s * BC + 4 * c4) = x;
+    if constexpr (SPLIT) {
+      bf16x4 hi, lo;
+      split_bf16(x, hi, lo);
+      *reinterpret_cast<bf16x4*>(bAS + s * (2 * LA) + 4 * c4) = hi;
+      *reinterpret_cast<bf16x4*>(bAS + s * (2 * LA) + BC + 4 * c4) = lo;
+    }
   }
   // E = gamma * b * k from the registers of phase 1-2, and Z = w * v
 #pragma unroll
@@ -546,12 +588,26 @@ __device__ __forceinline__ void front_item(const BwdArgs& a, const int item) {
     f32x4 eb;
 #pragma unroll
     for (int c = 0; c < 4; ++c) eb[c] = exp_dec(pg[u][c]) * pb[u][c] * pk[u][c];
-    *reinterpret_cast<f32x4*>(sEB + s * LKP + 4 * i4) = eb;
+    if constexpr (SPLIT) {
+      bf16x4 hi, lo;
+      split_bf16(eb, hi, lo);
+      *reinterpret_cast<bf16x4*>(bEB + s * (2 * LKP) + 4 * i4) = hi;
+      *reinterpret_cast<bf16x4*>(bEB + s * (2 * LKP) + DK + 4 * i4) = lo;
+    } else {
+      *reinterpret_cast<f32x4*>(sEB + s * LKP + 4 * i4) = eb;
+    }
   }
 #pragma unroll
   for (int u = 0; u < NEV; ++u) {
     const int e = tid + NT * u, s = e / (DV / 4), j4 = e - s * (DV / 4);
-    *reinterpret_cast<f32x4*>(sZ + s * C::LZ + 4 * j4) = pw[u] * pv[u];
+    if constexpr (SPLIT) {
+      bf16x4 hi, lo;
+      split_bf16(pw[u] * pv[u], hi, lo);
+      *reinterpret_cast<bf16x4*>(bZ + s * (2 * C::LZ) + 4 * j4) = hi;
+      *reinterpret_cast<bf16x4*>(bZ + s * (2 * C::LZ) + DV + 4 * j4) = lo;
+    } else {
+      *reinterpret_cast<f32x4*>(sZ + s * C::LZ + 4 * j4) = pw[u] * pv[u];
+    }
   }
   __syncthreads();
   // A is lower triangular: row block tm needs the first 16 (tm + 1) columns only
@@ -559,8 +615,13 @@ __device__ __forceinline__ void front_item(const BwdArgs& a, const int item) {
   // block of E (of Z), so at each K step one fragment of it serves every
   // tile whose range (A is lower triangular: K < 16 (tm + 1)) still runs;
   // each tile accumulates in ascending K
-  tri_rows<NKT, TNK, LA, LKP>(sA, sEB, wv, m, g, W + L::Y_, DK);
-  tri_rows<NVT, TNV, LA, C::LZ>(sA, sZ, wv, m, g, W + L::U, DV);
+  if constexpr (SPLIT) {
+    tri_rows3<NKT, TNK, 2 * LA, 2 * LKP, DK>(bAS, bEB, wv, W + L::Y_, DK);
+    tri_rows3<NVT, TNV, 2 * LA, 2 * C::LZ, DV>(bAS, bZ, wv, W + L::U, DV);
+  } else {
+    tri_rows<NKT, TNK, LA, LKP>(sA, sEB, wv, m, g, W + L::Y_, DK);
+    tri_rows<NVT, TNV, LA, C::LZ>(sA, sZ, wv, m, g, W + L::U, DV);
+  }
 }
 
 // The front pass: one workgroup per item; strong chunks are flagged only.
