@@ -231,10 +231,10 @@ size_t gdr2_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n
  * with dlog_alpha the reverse cumulative sum of dgamma * gamma inside each
  * chunk.  Everything is stored and accumulated in fp32.  Most products run
  * as three bf16 MFMA products on a hi/lo split of each fp32 operand (about
- * 2^-16 of each term); the WY inverse and Y = A E, U = A Z run on fp32 MFMA.
- * The gradients meet a max error of 1e-4 relative to each tensor's largest
- * value (measured 3e-6 to 1.3e-5 at B4 T4096 H16 d128, at most 1.4e-5 over
- * the tested inputs).
+ * 2^-16 of each term); the WY inverse runs in fp32 (forward substitution and
+ * fp32 MFMA).  The gradients meet a max error of 1e-4 relative to each
+ * tensor's largest value (measured 3e-6 to 1.3e-5 at B4 T4096 H16 d128, at
+ * most 1.6e-5 over the tested inputs).
  *
  *   q, k, log_alpha, b, v, w, S0, cu_seqlens, num_seqs, B, T, H, dk, dv and
  *       the dtypes: exactly as passed to gdr2_chunk_fwd.

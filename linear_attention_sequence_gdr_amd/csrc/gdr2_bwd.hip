@@ -34,7 +34,7 @@
 // The products run from LDS-staged operands with fp32 accumulation.  In the
 // main launches of the backward they run as three bf16 MFMAs over hi/lo
 // operand halves (mma3x, about 2^-16 of each term), except the front pass's
-// WY inverse and Y = A E, U = A Z, which stay on fp32 MFMA (16x16x4).  The
+// WY inverse, which stays on fp32 (forward substitution and fp32 MFMA).  The
 // launches that form strongly decaying chunks, and the fp32 forward (the
 // front pass, then fwd32_state_kernel), keep fp32 products throughout.
 #include <hip/hip_runtime.h>
